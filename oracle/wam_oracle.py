@@ -1,0 +1,487 @@
+"""Oracle for KV-cached action denoising: plain, slow, CPU-only.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
+(the C-ABI library and its Python binding) never calls it, and this module
+imports nothing from that path: it shares only the seeded input generator
+(``kv_cached_flow_amd.inputs``/``configs``), which holds no arithmetic of the
+method.
+
+Written in plain PyTorch CPU ops (a matmul, a softmax, ``erf`` serve as
+library steps), float64 for the fp32 workload C0 and float32 for the bf16
+workloads, on the same (bf16-rounded) inputs the GPU path consumes; nothing is
+rounded here.  Every function states the passage of the pages it follows.  The
+pages are:
+
+* "Long-WAM 源码精读" (yeyulingfeng.com), sections 03-04;
+* "Fast-WAM 精读" (alicepotter4869.xyz), sections 四, 五 and 七;
+* "Long-WAM: Scaling the Context of World-Action Models | Summary"
+  (greeksharifa.github.io), sections 3.1, 3.2, 4.2 and appendix B.2;
+* "世界模型之Faster-WAM详解" (171host.com), sections 3.1-3.4.
+
+Pins: every function here is checked by ``tests/test_oracle_pins.py`` against
+closed forms, library routines, special cases or brute force.  The composite
+network output (``run_chunk``) has no numeric example on the pages: it is
+pinned through its parts and through the structural identities (joint
+sequence == cached path, cached history == recompute, padding invariance),
+not against printed values.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+RMS_EPS = 1e-6
+
+# --------------------------------------------------------------------------
+# Schedules and the flow path
+# --------------------------------------------------------------------------
+
+
+def phi(u: float, shift: float) -> float:
+    """Time-shift map applied to the uniform grid u in [0, 1].
+
+    The Long-WAM code close-reading (section 04, 对照一) names ``_phi(u, shift)``
+    without defining it.  Reading adopted: the usual flow-matching shift
+    s*u / (1 + (s-1)*u), which is the identity for s = 1 (every workload here);
+    the endpoints are pinned to 0 and 1 exactly.
+    """
+    if u == 0.0:
+        return 0.0
+    if u == 1.0:
+        return 1.0
+    if shift == 1.0:
+        return u
+    return shift * u / (1.0 + (shift - 1.0) * u)
+
+
+def schedule(steps: int, sigma_end: float, shift: float = 1.0) -> np.ndarray:
+    """Noise levels sigma_0 .. sigma_steps, computed in float64, stored float32.
+
+    Long-WAM code close-reading, section 04 (对照一): a uniform grid from 1 to 0
+    with steps+1 points, mapped through ``_phi``, re-calibrated so that the
+    first level is pure noise and the last is exactly sigma* (0.9 for the IDM
+    video steps).  Reading: sigma_k = sigma_end + (1 - sigma_end) * phi(1 - k/steps).
+    Action steps use sigma_end = 0 (1 -> 0, "Fast-WAM" page section 七).
+    sigma_end is taken as a float64 number (0.9, not its float32 rounding).
+    """
+    if steps < 1:
+        raise ValueError("steps must be >= 1")
+    se = float(sigma_end)
+    out = []
+    for k in range(steps + 1):
+        u = 1.0 - k / steps
+        out.append(se + (1.0 - se) * phi(u, shift))
+    return np.asarray(out, dtype=np.float64).astype(np.float32)
+
+
+def flow_point(x0, eps, sigma):
+    """Point on the flow path x_sigma = (1 - sigma) x + sigma eps (Long-WAM
+    close-reading section 03; Fast-WAM page section 五 step 5)."""
+    return (1.0 - sigma) * x0 + sigma * eps
+
+
+def flow_velocity(x0, eps):
+    """Velocity target u = eps - x (Long-WAM close-reading section 03)."""
+    return eps - x0
+
+
+def euler_step(x, v, sigma, sigma_next):
+    """One Euler step of dx/dsigma = u from sigma to sigma_next.
+
+    The pages only say the scheduler "updates the latent" after each pass
+    (Fast-WAM page section 七.2).  Since d x_sigma / d sigma = eps - x = u on the
+    linear path, the step is x + (sigma_next - sigma) * v.
+    """
+    return x + (float(sigma_next) - float(sigma)) * v
+
+
+def integrate(x_init, sigmas: Sequence[float], velocity: Callable):
+    """Run Euler over a schedule; ``velocity(x, k, sigma_k)`` returns v-hat.
+    Returns the final state and the list of v-hat per step."""
+    x = x_init
+    vs = []
+    for k in range(len(sigmas) - 1):
+        v = velocity(x, k, float(sigmas[k]))
+        vs.append(v)
+        x = euler_step(x, v, sigmas[k], sigmas[k + 1])
+    return x, vs
+
+
+# --------------------------------------------------------------------------
+# Layer pieces
+# --------------------------------------------------------------------------
+
+
+def time_embedding(sigma: float, D: int, dtype=torch.float64) -> torch.Tensor:
+    """Sinusoidal embedding of the flow time, added to every token.
+
+    The pages do not give the conditioning form (they speak of per-token noise
+    levels, "Faster-WAM" page section 3.4).  Reading: t = 1000*sigma,
+    w_i = 10000^(-i/(D/2)), emb = [cos(t w_0..), sin(t w_0..)], in float64.
+    """
+    t = 1000.0 * float(sigma)
+    half = D // 2
+    i = torch.arange(half, dtype=torch.float64)
+    w = torch.pow(torch.tensor(10000.0, dtype=torch.float64), -i / half)
+    a = t * w
+    return torch.cat([torch.cos(a), torch.sin(a)]).to(dtype)
+
+
+def rmsnorm(x: torch.Tensor, g: torch.Tensor) -> torch.Tensor:
+    """RMSNorm(x; g) = x * (mean(x^2) + eps)^(-1/2) * g, eps = 1e-6 (the
+    pages give no normalisation details; a pre-norm block is the reading)."""
+    return x * torch.rsqrt((x * x).mean(dim=-1, keepdim=True) + RMS_EPS) * g
+
+
+def gelu(x: torch.Tensor) -> torch.Tensor:
+    """Exact GELU, 0.5 x (1 + erf(x / sqrt 2)) (the workload's "GELU MLP")."""
+    return 0.5 * x * (1.0 + torch.erf(x / math.sqrt(2.0)))
+
+
+MaskFn = Callable[[int, int], torch.Tensor]
+
+
+def attention(q, k, v, allow: Optional[MaskFn] = None, q_chunk: int = 1024):
+    """Scaled dot-product attention, one head at a time in a batch.
+
+    q [nq, Hh, dh], k/v [nk, Hh, dh]; ``allow(q0, q1)`` returns the boolean
+    visibility of keys for query rows q0..q1 (None: every key visible).
+    s_ij = q_i.k_j / sqrt(dh) over visible keys, p = softmax_j(s),
+    o_i = sum_j p_ij v_j.  A row with no visible key returns zeros (only
+    padding rows, whose outputs nobody reads, can be in that case).
+    Query rows are processed in chunks only to bound memory.
+    """
+    nq, Hh, dh = q.shape
+    scale = 1.0 / math.sqrt(dh)
+    kh = k.permute(1, 2, 0)          # [Hh, dh, nk]
+    vh = v.permute(1, 0, 2)          # [Hh, nk, dh]
+    out = torch.empty_like(q)
+    for q0 in range(0, nq, q_chunk):
+        q1 = min(nq, q0 + q_chunk)
+        qh = q[q0:q1].permute(1, 0, 2)                    # [Hh, qc, dh]
+        s = torch.matmul(qh, kh) * scale                  # [Hh, qc, nk]
+        if allow is not None:
+            m = allow(q0, q1)                             # [qc, nk]
+            s = s.masked_fill(~m.unsqueeze(0), float("-inf"))
+            empty = ~m.any(dim=1)
+            if bool(empty.any()):
+                s[:, empty, :] = 0.0
+            p = torch.softmax(s, dim=-1)
+            if bool(empty.any()):
+                p[:, empty, :] = 0.0
+        else:
+            p = torch.softmax(s, dim=-1)
+        out[q0:q1] = torch.matmul(p, vh).permute(1, 0, 2)
+    return out
+
+
+def layer(X, w: dict, Hh: int, ctx: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+          allow: Optional[MaskFn] = None, kv_only: bool = False):
+    """One expert layer on token states X [n, D] with attention context ctx.
+
+    Keys and values are [ctx ; this layer's own K, V] ("Fast-WAM" page
+    section 七.2: K = [K_video ; K_action], V likewise).  Block:
+      Y = RMSNorm(X; g1); Q, K, V = Y Wq^T, Y Wk^T, Y Wv^T (split into heads);
+      X += concat(attn) Wo^T;  X += GELU(RMSNorm(X; g2) W1^T) W2^T.
+    No biases.  Returns (X_out, K, V); K, V are this layer's cache rows.
+    With ``kv_only`` only K, V are produced (X_out is None).
+    """
+    n, D = X.shape
+    dh = D // Hh
+    Y = rmsnorm(X, w["g1"])
+    qkv = Y @ w["wqkv"].T
+    Q = qkv[:, :D].reshape(n, Hh, dh)
+    K = qkv[:, D:2 * D].reshape(n, Hh, dh)
+    V = qkv[:, 2 * D:].reshape(n, Hh, dh)
+    if kv_only:
+        return None, K, V
+    if ctx is not None:
+        Kall = torch.cat([ctx[0], K], dim=0)
+        Vall = torch.cat([ctx[1], V], dim=0)
+    else:
+        Kall, Vall = K, V
+    O = attention(Q, Kall, Vall, allow)
+    X = X + O.reshape(n, D) @ w["wo"].T
+    X = X + gelu(rmsnorm(X, w["g2"]) @ w["w1"].T) @ w["w2"].T
+    return X, K, V
+
+
+def head(X, g_out, w_out):
+    """Velocity head v-hat = RMSNorm(X_L; g_out) W_out^T."""
+    return rmsnorm(X, g_out) @ w_out.T
+
+
+def embed(x, w_in, sigma: float, D: int):
+    """Token embedding X = x W_in^T + emb(sigma) (the action expert maps each
+    action step to the hidden width with one linear layer, "Fast-WAM" page
+    section 四.3; the video side is the same form on latent channels)."""
+    return x @ w_in.T + time_embedding(sigma, D, x.dtype)
+
+
+# --------------------------------------------------------------------------
+# Masks
+# --------------------------------------------------------------------------
+
+
+def video_visible(frame_q: torch.Tensor, frame_k: torch.Tensor,
+                  block: torch.Tensor, valid: torch.Tensor) -> torch.Tensor:
+    """Visibility of video key tokens for video query tokens.
+
+    A video query reads its own and earlier temporal blocks ("Long-WAM ...
+    Summary" page, section 3.2; Faster-WAM page section 3.1: future slots read
+    the anchor and each other, the anchor does not read future slots), and
+    never a padded frame (appendix B.2: padding is masked).  Video rows never
+    see action tokens: no action column exists in any video pass.
+    allow(q, k) = valid(f(k)) and block(f(k)) <= block(f(q)).
+    """
+    bq = block[frame_q].unsqueeze(1)
+    bk = block[frame_k].unsqueeze(0)
+    return (bk <= bq) & valid[frame_k].unsqueeze(0).bool()
+
+
+# --------------------------------------------------------------------------
+# Experts
+# --------------------------------------------------------------------------
+
+
+def to_torch_expert(w: dict, dtype) -> dict:
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dtype)
+    return {"w_in": t(w["w_in"]), "g_out": t(w["g_out"]), "w_out": t(w["w_out"]),
+            "layers": [{k: t(v) for k, v in lw.items()} for lw in w["layers"]]}
+
+
+def oracle_dtype(cfg) -> torch.dtype:
+    return torch.float64 if cfg.dtype == "f32" else torch.float32
+
+
+def video_prefill(cfg, vw: dict, hist_b, valid_b, eps_v_b, drop_padded: bool = True):
+    """Video expert for one episode: history prefill, imagine, cache pass.
+
+    * History/anchor tokens at sigma = 0 run through the L layers with
+      block-causal attention; each layer's K, V are kept (Fast-WAM page
+      section 七.1, ``prefill_video_cache``; Long-WAM Summary section 3.2).
+    * Imagine (V >= 1): future latents start from noise and take V Euler steps
+      to sigma* = 0.9, keys = [history cache ; future] under the same block
+      rule; they are never decoded (Long-WAM close-reading sections 03-04;
+      Summary section 3.2).
+    * Cache pass: the future latents at sigma* (or, with V = 0, the noise at
+      video time 1, Faster-WAM page section 3.1) run once more and their
+      per-layer K, V are appended to the cache.  The last layer only needs K, V.
+
+    ``drop_padded`` leaves padded history frames out of the token list; with
+    False they are kept as tokens and masked as keys (the result on valid
+    rows is the same, a pinned identity).
+    Returns (cache: list of (K, V) [T, Hh, dh] per layer over the valid rows
+             in frame order, z: [Ff*P, Cv], frames: frame index per cache row).
+    """
+    dt = vw["w_in"].dtype
+    P, Fh, Ff, D, Hh, L = cfg.P, cfg.Fh, cfg.Ff, cfg.D, cfg.Hh, len(vw["layers"])
+    hist_frames = [f for f in range(Fh) if (valid_b[f] or not drop_padded)]
+    fut_frames = [Fh + j for j in range(Ff)]
+    block = torch.tensor(cfg.frame_block, dtype=torch.int64)
+    valid = torch.tensor(list(valid_b) + [1] * Ff, dtype=torch.int64)
+    fh = torch.tensor(hist_frames, dtype=torch.int64).repeat_interleave(P)
+    ff = torch.tensor(fut_frames, dtype=torch.int64).repeat_interleave(P)
+    fall = torch.cat([fh, ff])
+
+    hist_tok = torch.from_numpy(np.ascontiguousarray(hist_b[hist_frames])).to(dt).reshape(-1, cfg.Cv)
+    mask_h = lambda q0, q1: video_visible(fh[q0:q1], fh, block, valid)
+    mask_f = lambda q0, q1: video_visible(ff[q0:q1], fall, block, valid)
+
+    cache_h = []
+    if len(hist_frames):
+        X = embed(hist_tok, vw["w_in"], 0.0, D)
+        for l, lw in enumerate(vw["layers"]):
+            X, K, V = layer(X, lw, Hh, None, mask_h, kv_only=(l == L - 1))
+            cache_h.append((K, V))
+    else:
+        empty = torch.zeros((0, Hh, D // Hh), dtype=dt)
+        cache_h = [(empty, empty)] * L
+
+    z = torch.from_numpy(np.ascontiguousarray(eps_v_b)).to(dt).reshape(-1, cfg.Cv)
+    if cfg.V >= 1:
+        sig = schedule(cfg.V, cfg.sigma_star, cfg.shift)
+
+        def vel(zc, k, s):
+            X = embed(zc, vw["w_in"], s, D)
+            for l, lw in enumerate(vw["layers"]):
+                X, _, _ = layer(X, lw, Hh, cache_h[l], mask_f)
+            return head(X, vw["g_out"], vw["w_out"])
+
+        z, _ = integrate(z, sig, vel)
+        sigma_f = float(sig[-1])
+    else:
+        sigma_f = 1.0
+
+    cache = []
+    keep = valid[fall].bool()          # the cache holds valid rows only
+    X = embed(z, vw["w_in"], sigma_f, D)
+    for l, lw in enumerate(vw["layers"]):
+        X, K, V = layer(X, lw, Hh, cache_h[l], mask_f, kv_only=(l == L - 1))
+        cache.append((torch.cat([cache_h[l][0], K])[keep], torch.cat([cache_h[l][1], V])[keep]))
+    return cache, z, fall[keep]
+
+
+def fusion_weights(logits_row, count: int) -> np.ndarray:
+    """Softmax-normalised fusion weights of one interval, in float64
+    (Faster-WAM page section 3.3: W^fuse is softmax-normalised)."""
+    x = np.asarray(logits_row[:count], dtype=np.float64)
+    m = np.max(x)
+    e = np.exp(x - m)
+    return e / e.sum()
+
+
+def fuse_interval(cache: List[Tuple[torch.Tensor, torch.Tensor]], fuse, logits):
+    """Interval KV-Fusion: (K_bar, V_bar)_m = sum_{j in I_m} W_{m,j} (K_j, V_j).
+
+    Faster-WAM page section 3.3.  One scalar weight per (m, j), shared by K
+    and V, all heads and all tokens; the fused pair has one layer's length.
+    """
+    out = []
+    for m, (s, c) in enumerate(fuse):
+        w = fusion_weights(logits[m], c)
+        Kb = sum(float(w[j]) * cache[s + j][0] for j in range(c))
+        Vb = sum(float(w[j]) * cache[s + j][1] for j in range(c))
+        out.append((Kb, Vb))
+    return out
+
+
+def action_velocity(cfg, aw: dict, kv_read: List[Optional[Tuple]], a, sigma: float):
+    """One pass of the action expert at flow time sigma: v-hat for the chunk.
+
+    Per layer the 32 action queries attend over [video K/V read by this layer ;
+    the chunk's own K/V], or over the chunk alone where the layer reads
+    nothing (SparseMoT, Faster-WAM page section 3.2); no mask among action
+    tokens (Long-WAM Summary section 3.2: the entire noisy chunk is visible).
+    """
+    X = embed(a, aw["w_in"], sigma, cfg.D)
+    for l, lw in enumerate(aw["layers"]):
+        X, _, _ = layer(X, lw, cfg.Hh, kv_read[l], None)
+    return head(X, aw["g_out"], aw["w_out"])
+
+
+def denoise(cfg, aw: dict, kv_read, eps_a_b):
+    """N Euler steps of the action flow from noise at t=1 to t=0, re-reading
+    the same video K/V at every step (Fast-WAM page section 七.2-七.3)."""
+    t = schedule(cfg.N, 0.0, cfg.shift)
+    a = torch.from_numpy(np.ascontiguousarray(eps_a_b)).to(aw["w_in"].dtype)
+    return integrate(a, t, lambda x, k, s: action_velocity(cfg, aw, kv_read, x, s))
+
+
+def read_layers(cfg, cache, fused):
+    """The K/V each action layer reads: cache[l] (dense MoT pairing, Fast-WAM
+    page section 四.4), fused pair m at interaction layers, nothing elsewhere."""
+    src = fused if cfg.fuse else cache
+    return [None if r < 0 else src[r] for r in cfg.read_map]
+
+
+def run_chunk(cfg, inp: dict, dtype=None, drop_padded: bool = True,
+              cache_sampler: Optional[Callable] = None, keep_cache: bool = False):
+    """Whole chunk per episode: prefill -> (fuse) -> N action steps.
+
+    Returns actions [B, H, A] (numpy float64), z [B, Ff*P, Cv], v-hat per
+    step [N, B, H, A]; with ``keep_cache`` also the cache per episode (valid
+    rows, in frame order) and the fused pairs.  ``cache_sampler(b, cache,
+    fused)`` is called per episode before the cache is dropped.
+    """
+    dt = dtype or oracle_dtype(cfg)
+    vw = to_torch_expert(inp["video"], dt)
+    aw = to_torch_expert(inp["action"], dt)
+    acts, zs, vhs, caches, fuseds = [], [], [], [], []
+    for b in range(cfg.B):
+        cache, z, _ = video_prefill(cfg, vw, inp["hist"][b], inp["hist_valid"][b],
+                                    inp["eps_v"][b], drop_padded)
+        fused = fuse_interval(cache, cfg.fuse, inp["fuse_logits"]) if cfg.fuse else None
+        a, vh = denoise(cfg, aw, read_layers(cfg, cache, fused), inp["eps_a"][b])
+        if cache_sampler is not None:
+            cache_sampler(b, cache, fused)
+        acts.append(a.double().numpy())
+        zs.append(z.double().numpy())
+        vhs.append(np.stack([v.double().numpy() for v in vh]))
+        if keep_cache:
+            caches.append(cache)
+            fuseds.append(fused)
+    out = {"actions": np.stack(acts), "z": np.stack(zs),
+           "vhat": np.stack(vhs, axis=1)}
+    if keep_cache:
+        out["cache"] = caches
+        out["fused"] = fuseds
+    return out
+
+
+# --------------------------------------------------------------------------
+# Uncached references used by the structural pins
+# --------------------------------------------------------------------------
+
+
+def joint_mot_step(cfg, vw: dict, aw: dict, video_tok, video_sigma, video_frames,
+                   frame_valid, a, t: float):
+    """One pass of the two experts over ONE joint sequence [video ; action],
+    with no cache: each row uses its expert's weights, one attention over the
+    union with an explicit mask where video rows see video columns by the
+    block rule and never action columns, and action rows see every valid
+    video column and every action column (Long-WAM Summary section 3.2's
+    asymmetric interface; Fast-WAM page section 四.4 layer pairing).
+
+    video_tok [Nv, Cv] at per-row levels video_sigma [Nv]; a [H, A] at t.
+    Returns (v-hat of the action rows, per-layer video (K, V)).
+    """
+    D, Hh = cfg.D, cfg.Hh
+    dh = D // Hh
+    dt = vw["w_in"].dtype
+    Nv, H = video_tok.shape[0], a.shape[0]
+    Xv = video_tok @ vw["w_in"].T + torch.stack(
+        [time_embedding(float(s), D, dt) for s in video_sigma])
+    Xa = embed(a, aw["w_in"], t, D)
+    block = torch.tensor(cfg.frame_block, dtype=torch.int64)
+    valid = torch.as_tensor(frame_valid, dtype=torch.int64)
+    vv = video_visible(video_frames, video_frames, block, valid)
+    full = torch.zeros((Nv + H, Nv + H), dtype=torch.bool)
+    full[:Nv, :Nv] = vv
+    full[Nv:, :Nv] = valid[video_frames].bool().unsqueeze(0)
+    full[Nv:, Nv:] = True
+    kv = []
+    for lv, la in zip(vw["layers"], aw["layers"]):
+        Yv, Ya = rmsnorm(Xv, lv["g1"]), rmsnorm(Xa, la["g1"])
+        qv, qa = Yv @ lv["wqkv"].T, Ya @ la["wqkv"].T
+        Q = torch.cat([qv[:, :D], qa[:, :D]]).reshape(-1, Hh, dh)
+        K = torch.cat([qv[:, D:2 * D], qa[:, D:2 * D]]).reshape(-1, Hh, dh)
+        V = torch.cat([qv[:, 2 * D:], qa[:, 2 * D:]]).reshape(-1, Hh, dh)
+        kv.append((K[:Nv], V[:Nv]))
+        O = attention(Q, K, V, lambda q0, q1: full[q0:q1]).reshape(-1, D)
+        Xv = Xv + O[:Nv] @ lv["wo"].T
+        Xa = Xa + O[Nv:] @ la["wo"].T
+        Xv = Xv + gelu(rmsnorm(Xv, lv["g2"]) @ lv["w1"].T) @ lv["w2"].T
+        Xa = Xa + gelu(rmsnorm(Xa, la["g2"]) @ la["w1"].T) @ la["w2"].T
+    return head(Xa, aw["g_out"], aw["w_out"]), kv
+
+
+def imagine_recompute(cfg, vw: dict, hist_b, valid_b, eps_v_b):
+    """Imagine without a history cache: at every video step the whole
+    [history ; future] sequence runs through the layers (history at sigma=0).
+    Returns z after V steps.  Equal to ``video_prefill``'s z because history
+    rows never see future columns (block causality)."""
+    dt = vw["w_in"].dtype
+    P, Fh, Ff, D, Hh = cfg.P, cfg.Fh, cfg.Ff, cfg.D, cfg.Hh
+    hist_frames = [f for f in range(Fh) if valid_b[f]]
+    frames = torch.tensor(hist_frames + [Fh + j for j in range(Ff)]).repeat_interleave(P)
+    block = torch.tensor(cfg.frame_block, dtype=torch.int64)
+    valid = torch.tensor(list(valid_b) + [1] * Ff, dtype=torch.int64)
+    nh = len(hist_frames) * P
+    hist_tok = torch.from_numpy(np.ascontiguousarray(hist_b[hist_frames])).to(dt).reshape(-1, cfg.Cv)
+    sig = schedule(cfg.V, cfg.sigma_star, cfg.shift)
+    mask = lambda q0, q1: video_visible(frames[q0:q1], frames, block, valid)
+
+    def vel(zc, k, s):
+        X = torch.cat([embed(hist_tok, vw["w_in"], 0.0, D), embed(zc, vw["w_in"], s, D)])
+        for lw in vw["layers"]:
+            X, _, _ = layer(X, lw, Hh, None, mask)
+        return head(X[nh:], vw["g_out"], vw["w_out"])
+
+    z0 = torch.from_numpy(np.ascontiguousarray(eps_v_b)).to(dt).reshape(-1, cfg.Cv)
+    z, _ = integrate(z0, sig, vel)
+    return z

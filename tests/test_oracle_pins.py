@@ -1,0 +1,425 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these tests re-types an oracle formula: each compares against a
+closed form, a library routine, a special case, an identity that a mistake
+(dropped term, wrong sign or index, transposed operand) would break, or brute
+force on tiny inputs.
+"""
+import math
+import struct
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from kv_cached_flow_amd import configs, inputs
+from oracle import wam_oracle as O
+
+f64 = torch.float64
+
+
+def bits(x):
+    return struct.unpack("<I", struct.pack("<f", float(x)))[0]
+
+
+# ---------------------------------------------------------------- schedules
+@pytest.mark.parametrize("V", [1, 2, 4, 7])
+def test_video_schedule_endpoints(V):
+    # Long-WAM close-reading section 04: start is pure noise, end exactly sigma*=0.9
+    s = O.schedule(V, 0.9)
+    assert s.dtype == np.float32 and len(s) == V + 1
+    assert bits(s[0]) == bits(1.0)
+    assert bits(s[-1]) == 0x3F666666
+    assert np.all(np.diff(s.astype(np.float64)) < 0)
+
+
+def test_video_schedule_v4_values():
+    s = O.schedule(4, 0.9)
+    want = np.array([1.0, 0.975, 0.95, 0.925, 0.9], dtype=np.float32)
+    assert np.array_equal(s.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 10])
+@pytest.mark.parametrize("shift", [1.0, 3.0, 0.5])
+def test_action_schedule(N, shift):
+    t = O.schedule(N, 0.0, shift)
+    assert t[0] == 1.0 and t[-1] == 0.0
+    assert np.all(np.diff(t.astype(np.float64)) < 0)
+    if shift == 1.0:
+        assert np.allclose(t, np.linspace(1, 0, N + 1), atol=1e-7)
+
+
+def test_shift_map_closed_form():
+    # shift s maps u=1/2 to s/(1+s): a textbook value of the shift map
+    for s in (0.5, 2.0, 3.0, 5.0):
+        assert abs(O.phi(0.5, s) - s / (1 + s)) < 1e-15
+
+
+# ---------------------------------------------------------------- flow / Euler
+def _sched(n, seed):
+    r = np.random.default_rng(seed)
+    x = np.sort(r.uniform(0, 1, n - 1))[::-1]
+    return np.concatenate([[1.0], x, [0.0]])
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_euler_exact_velocity_lands_on_data(seed):
+    # The path is linear in sigma, so Euler with the exact velocity eps - x0 is
+    # exact at every node: x_k = (1 - t_k) x0 + t_k eps for ANY schedule.
+    r = np.random.default_rng(100 + seed)
+    x0 = torch.tensor(r.standard_normal((32, 14)), dtype=f64)
+    eps = torch.tensor(r.standard_normal((32, 14)), dtype=f64)
+    ts = _sched(2 + seed * 3, seed)
+    states = []
+
+    def vel(x, k, s):
+        states.append((x.clone(), ts[k]))
+        return eps - x0
+
+    xN, vs = O.integrate(eps, ts, vel)
+    assert torch.max(torch.abs(xN - x0)) < 1e-13
+    for x, t in states:
+        assert torch.max(torch.abs(x - ((1 - t) * x0 + t * eps))) < 1e-13
+    assert len(vs) == len(ts) - 1
+
+
+def test_euler_constant_velocity():
+    # x_N = x_0 + (t_N - t_0) v = eps - v for the action schedule 1 -> 0
+    r = np.random.default_rng(3)
+    eps = torch.tensor(r.standard_normal((8, 3)), dtype=f64)
+    v = torch.tensor(r.standard_normal((8, 3)), dtype=f64)
+    xN, _ = O.integrate(eps, O.schedule(10, 0.0), lambda x, k, s: v)
+    assert torch.max(torch.abs(xN - (eps - v))) < 1e-13
+
+
+def test_flow_velocity_is_path_derivative():
+    r = np.random.default_rng(4)
+    x0 = torch.tensor(r.standard_normal(50), dtype=f64)
+    eps = torch.tensor(r.standard_normal(50), dtype=f64)
+    s, h = 0.37, 1e-6
+    fd = (O.flow_point(x0, eps, s + h) - O.flow_point(x0, eps, s - h)) / (2 * h)
+    assert torch.max(torch.abs(fd - O.flow_velocity(x0, eps))) < 1e-8
+    assert torch.equal(O.flow_point(x0, eps, 0.0), x0)
+    assert torch.equal(O.flow_point(x0, eps, 1.0), eps)
+
+
+# ---------------------------------------------------------------- layer pieces
+def test_time_embedding_structure():
+    D = 64
+    e0 = O.time_embedding(0.0, D)
+    assert torch.equal(e0, torch.cat([torch.ones(32, dtype=f64), torch.zeros(32, dtype=f64)]))
+    e = O.time_embedding(0.731, D)
+    # each frequency is a point on the unit circle; lowest frequency is 1 rad per unit t
+    assert torch.max(torch.abs(e[:32] ** 2 + e[32:] ** 2 - 1)) < 1e-14
+    assert abs(e[0].item() - math.cos(731.0)) < 1e-12
+    assert abs(e[32].item() - math.sin(731.0)) < 1e-12
+    # frequencies decrease geometrically by 10000^(1/32) per index
+    tt = 1000 * 0.731
+    w1 = math.atan2(e[33].item(), e[1].item())
+    assert abs(math.remainder(w1 - tt * 10000 ** (-1 / 32), 2 * math.pi)) < 1e-9
+
+
+def test_rmsnorm_vs_library():
+    r = np.random.default_rng(5)
+    x = torch.tensor(r.standard_normal((7, 96)), dtype=f64)
+    g = torch.tensor(1 + 0.1 * r.standard_normal(96), dtype=f64)
+    ref = F.rms_norm(x, (96,), g, eps=1e-6)
+    assert torch.max(torch.abs(O.rmsnorm(x, g) - ref)) < 1e-14
+    y = O.rmsnorm(x, torch.ones(96, dtype=f64))
+    assert torch.max(torch.abs((y * y).mean(-1) - 1)) < 1e-5
+
+
+def test_gelu_vs_library():
+    x = torch.linspace(-8, 8, 1001, dtype=f64)
+    assert torch.max(torch.abs(O.gelu(x) - F.gelu(x))) < 1e-15
+    assert torch.max(torch.abs(O.gelu(x) - O.gelu(-x) - x)) < 1e-14
+
+
+def _qkv(r, nq, nk, Hh, dh):
+    q = torch.tensor(r.standard_normal((nq, Hh, dh)), dtype=f64)
+    k = torch.tensor(r.standard_normal((nk, Hh, dh)), dtype=f64)
+    v = torch.tensor(r.standard_normal((nk, Hh, dh)), dtype=f64)
+    return q, k, v
+
+
+def _sdpa(q, k, v, mask=None):
+    o = F.scaled_dot_product_attention(q.permute(1, 0, 2), k.permute(1, 0, 2),
+                                       v.permute(1, 0, 2), attn_mask=mask)
+    return o.permute(1, 0, 2)
+
+
+def test_attention_vs_library_unmasked_and_masked():
+    r = np.random.default_rng(6)
+    q, k, v = _qkv(r, 13, 29, 3, 16)
+    assert torch.max(torch.abs(O.attention(q, k, v) - _sdpa(q, k, v))) < 1e-13
+    m = torch.tensor(r.uniform(size=(13, 29)) < 0.6)
+    m[:, 0] = True
+    got = O.attention(q, k, v, lambda a, b: m[a:b], q_chunk=4)
+    assert torch.max(torch.abs(got - _sdpa(q, k, v, m))) < 1e-13
+
+
+def test_attention_single_key_returns_value():
+    r = np.random.default_rng(7)
+    q, k, v = _qkv(r, 5, 9, 2, 8)
+    m = torch.zeros((5, 9), dtype=torch.bool)
+    m[:, 4] = True
+    got = O.attention(q, k, v, lambda a, b: m[a:b])
+    assert torch.equal(got, v[4].unsqueeze(0).expand(5, -1, -1))
+
+
+def test_attention_zero_query_is_mean_of_visible():
+    r = np.random.default_rng(8)
+    _, k, v = _qkv(r, 1, 16, 2, 8)
+    q = torch.zeros((3, 2, 8), dtype=f64)
+    m = torch.zeros((3, 16), dtype=torch.bool)
+    m[0, :4] = True
+    m[1, :8] = True
+    m[2, :] = True
+    got = O.attention(q, k, v, lambda a, b: m[a:b])
+    for i, n in enumerate((4, 8, 16)):
+        assert torch.max(torch.abs(got[i] - v[:n].mean(0))) < 1e-15
+
+
+def test_attention_key_permutation_invariance():
+    r = np.random.default_rng(9)
+    q, k, v = _qkv(r, 6, 21, 2, 8)
+    perm = torch.tensor(r.permutation(21))
+    a = O.attention(q, k, v)
+    b = O.attention(q, k[perm], v[perm])
+    assert torch.max(torch.abs(a - b)) < 1e-14
+
+
+def _rand_layer(r, D, Fm, std=0.2):
+    t = lambda *s: torch.tensor(r.standard_normal(s) * std, dtype=f64)
+    return {"g1": 1 + t(D), "wqkv": t(3 * D, D), "wo": t(D, D), "g2": 1 + t(D),
+            "w1": t(Fm, D), "w2": t(D, Fm)}
+
+
+def _library_layer(X, w, Hh, ctx, mask):
+    # Same block built from torch library routines (rms_norm, linear, SDPA, gelu).
+    n, D = X.shape
+    dh = D // Hh
+    Y = F.rms_norm(X, (D,), w["g1"], eps=1e-6)
+    q, k, v = F.linear(Y, w["wqkv"]).split(D, dim=1)
+    q, k, v = (t.reshape(n, Hh, dh) for t in (q, k, v))
+    if ctx is not None:
+        k = torch.cat([ctx[0], k])
+        v = torch.cat([ctx[1], v])
+    o = _sdpa(q, k, v, mask).reshape(n, D)
+    X = X + F.linear(o, w["wo"])
+    h = F.gelu(F.linear(F.rms_norm(X, (D,), w["g2"], eps=1e-6), w["w1"]))
+    return X + F.linear(h, w["w2"])
+
+
+def test_layer_vs_library_composition():
+    r = np.random.default_rng(10)
+    D, Hh, Fm, n, nc = 48, 3, 80, 11, 17
+    w = _rand_layer(r, D, Fm)
+    X = torch.tensor(r.standard_normal((n, D)), dtype=f64)
+    ctx = (torch.tensor(r.standard_normal((nc, Hh, 16)), dtype=f64),
+           torch.tensor(r.standard_normal((nc, Hh, 16)), dtype=f64))
+    m = torch.tensor(r.uniform(size=(n, nc + n)) < 0.7)
+    m[:, -1] = True
+    got, K, V = O.layer(X, w, Hh, ctx, lambda a, b: m[a:b])
+    ref = _library_layer(X, w, Hh, ctx, m)
+    assert torch.max(torch.abs(got - ref)) < 1e-12
+    _, K2, V2 = O.layer(X, w, Hh, ctx, None, kv_only=True)
+    assert torch.equal(K, K2) and torch.equal(V, V2)
+
+
+def test_layer_zero_output_projections_is_identity():
+    r = np.random.default_rng(11)
+    w = _rand_layer(r, 32, 64)
+    w["wo"].zero_()
+    w["w2"].zero_()
+    X = torch.tensor(r.standard_normal((5, 32)), dtype=f64)
+    got, _, _ = O.layer(X, w, 2)
+    assert torch.equal(got, X)
+
+
+# ---------------------------------------------------------------- masks
+def _brute_visible(frames_q, frames_k, block, valid):
+    # Rule of Long-WAM Summary 3.2 / Faster-WAM 3.1 enumerated pair by pair.
+    out = np.zeros((len(frames_q), len(frames_k)), dtype=bool)
+    for i, fq in enumerate(frames_q):
+        for j, fk in enumerate(frames_k):
+            earlier_or_same = block[fk] <= block[fq]
+            out[i, j] = bool(valid[fk]) and earlier_or_same
+    return out
+
+
+def test_block_causal_per_frame_counts():
+    # one frame per block: a query in frame f sees exactly frames 0..f
+    P, Fn = 3, 6
+    block = torch.arange(Fn)
+    valid = torch.ones(Fn, dtype=torch.int64)
+    fr = torch.arange(Fn).repeat_interleave(P)
+    m = O.video_visible(fr, fr, block, valid)
+    for i in range(Fn * P):
+        f = i // P
+        assert m[i].sum().item() == (f + 1) * P
+        assert bool(m[i, : (f + 1) * P].all())
+
+
+def test_anchor_future_rule():
+    # Faster-WAM 3.1: anchor (block 0) never reads future slots; future slots
+    # read the anchor and each other.
+    P = 4
+    block = torch.tensor([0] + [1] * 8)
+    valid = torch.ones(9, dtype=torch.int64)
+    fr = torch.arange(9).repeat_interleave(P)
+    m = O.video_visible(fr, fr, block, valid)
+    assert bool(m[:P, :P].all()) and not bool(m[:P, P:].any())
+    assert bool(m[P:, :].all())
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_video_mask_brute_force_ragged(seed):
+    r = np.random.default_rng(50 + seed)
+    Fn = int(r.integers(2, 7))
+    P = int(r.integers(1, 6))
+    block = np.sort(r.integers(0, Fn, Fn))
+    valid = (r.uniform(size=Fn) < 0.7).astype(np.int64)
+    valid[-1] = 1
+    fr = np.repeat(np.arange(Fn), P)
+    got = O.video_visible(torch.tensor(fr), torch.tensor(fr), torch.tensor(block),
+                          torch.tensor(valid)).numpy()
+    assert np.array_equal(got, _brute_visible(fr, fr, block, valid))
+
+
+# ---------------------------------------------------------------- fusion
+def _layers(r, n, T=6, Hh=2, dh=4):
+    return [(torch.tensor(r.standard_normal((T, Hh, dh)), dtype=torch.float32),
+             torch.tensor(r.standard_normal((T, Hh, dh)), dtype=torch.float32))
+            for _ in range(n)]
+
+
+def test_fusion_one_hot_is_exact_layer():
+    r = np.random.default_rng(12)
+    cache = _layers(r, 8)
+    logits = np.full((2, 4), -np.inf, dtype=np.float32)
+    logits[0, 2] = 0.0
+    logits[1, 1] = 3.5
+    fused = O.fuse_interval(cache, ((0, 4), (4, 4)), logits)
+    assert torch.equal(fused[0][0], cache[2][0]) and torch.equal(fused[0][1], cache[2][1])
+    assert torch.equal(fused[1][0], cache[5][0]) and torch.equal(fused[1][1], cache[5][1])
+
+
+def test_fusion_identical_layers_and_weights():
+    r = np.random.default_rng(13)
+    one = _layers(r, 1)[0]
+    cache = [(one[0].double(), one[1].double())] * 4
+    logits = r.standard_normal((1, 4)).astype(np.float32)
+    fused = O.fuse_interval(cache, ((0, 4),), logits)
+    assert torch.max(torch.abs(fused[0][0] - cache[0][0])) < 1e-14
+    w = O.fusion_weights(logits[0], 4)
+    assert abs(w.sum() - 1) < 1e-15 and np.all(w > 0)
+    # softmax is invariant to a common logit offset and ordered like the logits
+    w2 = O.fusion_weights(logits[0].astype(np.float64) + 7.0, 4)
+    assert np.max(np.abs(w - w2)) < 1e-14
+    assert np.array_equal(np.argsort(w), np.argsort(logits[0]))
+
+
+def test_sparse_mot_tables_partition():
+    read_map, fuse = configs.sparse_mot_tables(30, 4)
+    assert [j for j, m in enumerate(read_map) if m >= 0] == [3, 7, 11, 15, 19, 23, 27, 29]
+    covered = [s + i for s, c in fuse for i in range(c)]
+    assert covered == list(range(30)) and len(fuse) == 8
+
+
+# ---------------------------------------------------------------- structural
+def _tiny(**kw):
+    base = dict(dtype="f32", L=2, D=32, Hh=2, dh=16, Fm=48, Cv=6, A=3, H=5, B=1,
+                P=3, Fh=3, Ff=2, frame_block=(0, 1, 2, 3, 4), pad_frames=1, V=2,
+                N=2, w_std=0.2, qk_std=0.2, read_map=(0, 1), seed=21)
+    base.update(kw)
+    return configs.small("T", **base)
+
+
+def test_joint_sequence_equals_cached_path():
+    # Asymmetric mask => caching is exact: one joint [video ; action] pass with
+    # the explicit mask reproduces the cache rows and the first action v-hat.
+    cfg = _tiny()
+    inp = inputs.generate(cfg, threads=1)
+    vw = O.to_torch_expert(inp["video"], f64)
+    aw = O.to_torch_expert(inp["action"], f64)
+    cache, z, frames = O.video_prefill(cfg, vw, inp["hist"][0], inp["hist_valid"][0], inp["eps_v"][0])
+    t0 = float(O.schedule(cfg.N, 0.0)[0])
+    a = torch.tensor(inp["eps_a"][0], dtype=f64)
+    v_cached = O.action_velocity(cfg, aw, O.read_layers(cfg, cache, None), a, t0)
+
+    valid_frames = [f for f in range(cfg.Fh) if inp["hist_valid"][0][f]]
+    hist_tok = torch.tensor(inp["hist"][0][valid_frames], dtype=f64).reshape(-1, cfg.Cv)
+    vtok = torch.cat([hist_tok, z])
+    sig_f = float(O.schedule(cfg.V, cfg.sigma_star)[-1])
+    vsig = [0.0] * hist_tok.shape[0] + [sig_f] * z.shape[0]
+    fvalid = list(inp["hist_valid"][0]) + [1] * cfg.Ff
+    v_joint, kv = O.joint_mot_step(cfg, vw, aw, vtok, vsig, frames, fvalid, a, t0)
+    assert torch.max(torch.abs(v_joint - v_cached)) < 1e-12
+    for (Kc, Vc), (Kj, Vj) in zip(cache, kv):
+        assert torch.max(torch.abs(Kc - Kj)) < 1e-12
+        assert torch.max(torch.abs(Vc - Vj)) < 1e-12
+
+
+def test_cached_history_equals_recompute():
+    cfg = _tiny()
+    inp = inputs.generate(cfg, threads=1)
+    vw = O.to_torch_expert(inp["video"], f64)
+    _, z, _ = O.video_prefill(cfg, vw, inp["hist"][0], inp["hist_valid"][0], inp["eps_v"][0])
+    z2 = O.imagine_recompute(cfg, vw, inp["hist"][0], inp["hist_valid"][0], inp["eps_v"][0])
+    assert torch.max(torch.abs(z - z2)) < 1e-12
+    # and the imagined latents did move away from the noise
+    assert torch.max(torch.abs(z - torch.tensor(inp["eps_v"][0], dtype=f64).reshape(z.shape))) > 1e-3
+
+
+def test_padding_invariance_and_dropping():
+    cfg = _tiny()
+    inp = inputs.generate(cfg, threads=1)
+    ref = O.run_chunk(cfg, inp, drop_padded=True)
+    kept = O.run_chunk(cfg, inp, drop_padded=False)
+    assert np.max(np.abs(ref["actions"] - kept["actions"])) < 1e-12
+    inp2 = dict(inp)
+    inp2["hist"] = inp["hist"].copy()
+    inp2["hist"][0, 0] = 123.0   # contents of the padded frame
+    kept2 = O.run_chunk(cfg, inp2, drop_padded=False)
+    assert np.array_equal(kept["actions"], kept2["actions"])
+    # a valid frame does matter
+    inp3 = dict(inp)
+    inp3["hist"] = inp["hist"].copy()
+    inp3["hist"][0, 1] += 1.0
+    assert np.max(np.abs(O.run_chunk(cfg, inp3)["actions"] - ref["actions"])) > 1e-6
+
+
+def test_batch_independence():
+    cfg2 = _tiny(B=2)
+    inp2 = inputs.generate(cfg2, threads=1)
+    both = O.run_chunk(cfg2, inp2)
+    for b in range(2):
+        one = {k: (v[b:b + 1] if k in ("hist", "hist_valid", "eps_v", "eps_a") else v)
+               for k, v in inp2.items()}
+        single = O.run_chunk(_tiny(B=1), one)
+        assert np.array_equal(both["actions"][b], single["actions"][0])
+
+
+def test_sparse_one_hot_stride_one_equals_dense():
+    # Stride-1 SparseMoT with one-hot weights on the own layer == dense MoT.
+    dense = _tiny(V=0)
+    sparse = _tiny(V=0, fuse=((0, 1), (1, 1)))
+    inp = inputs.generate(dense, threads=1)
+    inp_s = dict(inp)
+    inp_s["fuse_logits"] = np.zeros((2, 1), dtype=np.float32)
+    a = O.run_chunk(dense, inp)["actions"]
+    b = O.run_chunk(sparse, inp_s)["actions"]
+    assert np.array_equal(a, b)
+
+
+def test_action_only_layers_ignore_video():
+    # A layer with read_map = -1 must not depend on the cache at all.
+    cfg = _tiny(read_map=(-1, -1))
+    inp = inputs.generate(cfg, threads=1)
+    a1 = O.run_chunk(cfg, inp)["actions"]
+    inp2 = dict(inp)
+    inp2["hist"] = inp["hist"] * 3.0
+    inp2["eps_v"] = inp["eps_v"] * -1.0
+    assert np.array_equal(a1, O.run_chunk(cfg, inp2)["actions"])
