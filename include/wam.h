@@ -1,0 +1,251 @@
+/*
+ * wam.h -- C-ABI of the KV-cached action-denoising library (libwam.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (the "Long-WAM", "Fast-WAM" and "Faster-WAM" pages):
+ *   1. a video expert fills a per-layer K/V cache once, with block-causal
+ *      attention over history latents and future latents that are partially
+ *      denoised to sigma* ("Long-WAM: Scaling the Context of World-Action
+ *      Models | Summary", section 3.2; Long-WAM code close-reading, section 04);
+ *   2. Faster-WAM's Interval KV-Fusion may collapse each depth interval of
+ *      video layers into one softmax-weighted K/V pair ("世界模型之Faster-WAM详解",
+ *      section 3.3);
+ *   3. an action expert runs N flow-matching Euler steps over a 32-token
+ *      action chunk; at every step the action queries attend over
+ *      [video cache ; action K/V] and video tokens never read actions
+ *      ("Fast-WAM 精读", section 七; Long-WAM Summary, section 3.2).
+ *
+ * Conventions (all calls):
+ *   - Every buffer is owned by the caller.  The library never allocates or
+ *     frees device memory inside these calls; scratch comes from the caller's
+ *     workspace ``ws`` (size from the matching *_workspace_bytes call).
+ *   - Device pointers must be 16-byte aligned and contiguous in the layouts
+ *     stated below.  Host arrays are read before the call returns.
+ *   - Work is enqueued asynchronously on ``stream`` (a hipStream_t passed as
+ *     void*, NULL = default stream).  Argument errors are detected on the host
+ *     before anything is enqueued; the call then returns a negative status and
+ *     enqueues nothing.  ``wam_last_error()`` gives a message (thread-local).
+ *   - Matrices are out-major: W[out_features][in_features] (y = x W^T).
+ *   - dtype WAM_BF16: weight matrices, latent tokens, noise and K/V are bf16;
+ *     residual stream, softmax, accumulators, latents and actions are fp32.
+ *     dtype WAM_F32: everything fp32.  RMSNorm gains are always fp32.
+ *   - Results are deterministic: identical inputs give bitwise-identical
+ *     outputs (no floating-point atomics; split reductions merge in a fixed
+ *     order).  Calls on disjoint buffers and workspaces may run concurrently.
+ */
+#ifndef WAM_H
+#define WAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WAM_ABI_VERSION 1
+#define WAM_MAX_FRAMES 256   /* latent frames per episode (history + future) */
+#define WAM_MAX_BATCH 64     /* episodes per call */
+#define WAM_MAX_FUSE 32      /* fused pairs per wam_fuse_interval_kv call */
+#define WAM_MAX_INTERVAL 8   /* layers per fusion interval */
+#define WAM_MAX_STEPS 64     /* Euler steps per call */
+
+enum {
+  WAM_OK = 0,
+  WAM_E_ARG = -1,        /* null pointer, bad enum, out-of-range scalar */
+  WAM_E_SHAPE = -2,      /* inconsistent or unsupported dimensions */
+  WAM_E_DTYPE = -3,      /* dtype mismatch between arguments */
+  WAM_E_ALIGN = -4,      /* device pointer not 16-byte aligned */
+  WAM_E_WORKSPACE = -5,  /* workspace missing or too small */
+  WAM_E_HIP = -6         /* a HIP runtime call failed (see wam_last_error) */
+};
+
+enum { WAM_F32 = 0, WAM_BF16 = 1 };
+
+/* Shapes shared by both experts (layer count, heads and head dim must match
+ * so that video layer i pairs with action layer i, "Fast-WAM 精读" section 四.4). */
+typedef struct {
+  int L;      /* layers per expert */
+  int D;      /* hidden width; D == Hh * dh */
+  int Hh;     /* attention heads */
+  int dh;     /* head dim; must be 64 */
+  int Fm;     /* MLP inner width */
+  int Cv;     /* channels per video latent token */
+  int A;      /* action dims per action token */
+  int H;      /* action tokens per chunk; must be 32 */
+  int P;      /* tokens per latent frame */
+  int dtype;  /* WAM_F32 or WAM_BF16 */
+} wam_dims;
+
+/* One layer: Y = RMSNorm(X; g1); [Q K V] = Y Wqkv^T; X += Attn Wo^T;
+ * X += GELU(RMSNorm(X; g2) W1^T) W2^T.  No biases.  RMSNorm eps = 1e-6. */
+typedef struct {
+  const float* g1;   /* [D] fp32 */
+  const void* wqkv;  /* [3D][D]; rows 0..D-1 = Wq, D..2D-1 = Wk, 2D..3D-1 = Wv */
+  const void* wo;    /* [D][D] */
+  const float* g2;   /* [D] fp32 */
+  const void* w1;    /* [Fm][D] */
+  const void* w2;    /* [D][Fm] */
+} wam_layer_w;
+
+/* An expert: X = x W_in^T + emb(sigma); layers; v = RMSNorm(X; g_out) W_out^T.
+ * emb(sigma) = [cos(t w_i), sin(t w_i)], t = 1000 sigma, w_i = 10000^(-i/(D/2)).
+ * C = Cv for the video expert, A for the action expert. */
+typedef struct {
+  const void* w_in;            /* [D][C] */
+  const float* g_out;          /* [D] fp32 */
+  const void* w_out;           /* [C][D] */
+  const wam_layer_w* layers;   /* host array of n_layers */
+  int n_layers;
+} wam_expert_w;
+
+/* Per-layer K/V cache of B episodes.
+ *   k: [n_layers][B][Hh][cap][dh]   (token-major within a head)
+ *   v: [n_layers][B][Hh][dh][cap]   (transposed: tokens contiguous)
+ * Rows 0..len[b]-1 of episode b are valid: the valid history frames in frame
+ * order, then the future frames.  cap must be a multiple of 64. */
+typedef struct {
+  void* k;
+  void* v;
+  int n_layers, B, Hh, dh, cap, dtype;
+  int32_t* len;                /* host [B] */
+} wam_kv;
+
+/* ---------------------------------------------------------------------------
+ * wam_prefill_video_cache -- the video expert's side of one chunk
+ * ("prefill_video_cache", Fast-WAM 精读 section 七.1; imagine-then-cache,
+ * Long-WAM code close-reading section 04 and Summary section 3.2; one-shot
+ * future at video time 1, Faster-WAM section 3.1).
+ *
+ * Per episode b:
+ *   - history frames with hist_valid[b][f] != 0 (all if hist_valid is NULL)
+ *     are embedded at sigma = 0 and run through the L layers; a query token
+ *     of frame f sees key tokens of valid frames g with
+ *     frame_block[g] <= frame_block[f]; each layer's K, V are stored;
+ *   - video_steps >= 1: future latents z start at fut_noise and take
+ *     video_steps Euler steps over sigma_k = sigma_star + (1 - sigma_star) *
+ *     phi(1 - k/video_steps), phi(u) = s u / (1 + (s-1) u) with s = shift,
+ *     attending to [history cache ; future] under the same block rule; then
+ *     one more pass at sigma_star stores the future K, V;
+ *   - video_steps == 0: one pass of the noise at sigma = 1 stores the future
+ *     K, V.  Ff == 0: history only.
+ * The last layer of a caching pass computes K, V only.
+ *
+ *   hist       device [B][Fh][P][Cv] dtype     history / anchor latents
+ *   hist_valid host [B][Fh] uint8 or NULL
+ *   fut_noise  device [B][Ff][P][Cv] dtype     (may be NULL iff Ff == 0)
+ *   frame_block host [Fh + Ff] int32, non-decreasing
+ *   cache      device k/v per wam_kv; n_layers == L; cache->len (host) is written
+ *   fut_latents_out device [B][Ff][P][Cv] fp32 or NULL: z after the video steps
+ * Errors: WAM_E_SHAPE if a frame table is not monotone, an episode has no
+ * token at all, or cap is too small.
+ * ------------------------------------------------------------------------- */
+size_t wam_prefill_workspace_bytes(const wam_dims* d, int B, int Fh, int Ff);
+int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video,
+                            const void* hist, const uint8_t* hist_valid, int B, int Fh,
+                            const void* fut_noise, int Ff, const int32_t* frame_block,
+                            int video_steps, double sigma_star, double shift,
+                            wam_kv* cache, float* fut_latents_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * wam_fuse_interval_kv -- Interval KV-Fusion ("世界模型之Faster-WAM详解",
+ * section 3.3): for m < M,
+ *   (Kbar_m, Vbar_m) = sum_{j < count[m]} w_{m,j} (K_{start[m]+j}, V_{start[m]+j}),
+ *   w_m = softmax(logits[m*logits_stride + 0 .. count[m]-1])   (host, float64;
+ *   -INFINITY gives an exact 0 weight).
+ * One scalar per (m, j) for K and V, all heads and tokens; fp32 accumulation,
+ * output rounded once to the cache dtype.  The fused pair has one layer's
+ * length.  dst->n_layers >= M; dst->len is set to src->len.
+ * ------------------------------------------------------------------------- */
+int wam_fuse_interval_kv(const wam_kv* src, int M, const int32_t* start,
+                         const int32_t* count, const float* logits, int logits_stride,
+                         wam_kv* dst, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * wam_action_layer -- one action-expert layer on the chunk, in place
+ * (forward_action_with_video_cache for one layer): the B*H action queries of
+ * episode b attend over [kv layer kv_layer of episode b ; the chunk's own H
+ * keys], or over the chunk alone when kv is NULL (SparseMoT action-only
+ * layers, Faster-WAM section 3.2).  No mask among action tokens.
+ *   x  device [B][H][D] fp32, updated in place.
+ * ------------------------------------------------------------------------- */
+size_t wam_action_workspace_bytes(const wam_dims* d, int B, const wam_kv* kv);
+int wam_action_layer(const wam_dims* d, const wam_layer_w* w, float* x,
+                     const wam_kv* kv, int kv_layer, int B,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * wam_flow_euler_step -- x <- x + (sigma_next - sigma) * v, elementwise fp32
+ * (the flow path x_sigma = (1-sigma) x + sigma eps has velocity eps - x, Long-WAM
+ * code close-reading section 03).  n >= 0; x and v device fp32.
+ * ------------------------------------------------------------------------- */
+int wam_flow_euler_step(float* x, const float* v, int64_t n, float sigma,
+                        float sigma_next, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * wam_denoise_chunk -- N Euler steps of the action flow from t=1 to t=0 over
+ * t_k = phi(1 - k/N), re-reading the cached video K/V at every step
+ * ("Fast-WAM 精读" section 七.2-七.3).  Step k: X = a W_in^T + emb(t_k); layer l
+ * reads kv layer read_map[l] (or nothing if read_map[l] < 0); v = head(X);
+ * a += (t_{k+1} - t_k) v.
+ *   read_map   host [L] int32
+ *   eps        device [B][H][A] fp32   initial noise
+ *   actions_out device [B][H][A] fp32
+ *   vhat_out   device [N][B][H][A] fp32 or NULL
+ * kv may be NULL only if every read_map entry is negative.
+ * ------------------------------------------------------------------------- */
+size_t wam_denoise_workspace_bytes(const wam_dims* d, int B, const wam_kv* kv);
+int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_kv* kv,
+                      const int32_t* read_map, const float* eps, int B, int N,
+                      double shift, float* actions_out, float* vhat_out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Auxiliary calls.
+ * ------------------------------------------------------------------------- */
+int wam_abi_version(void);
+const char* wam_status_str(int status);
+const char* wam_last_error(void);
+
+/* sigma_k = sigma_end + (1 - sigma_end) * phi(1 - k/steps), k = 0..steps,
+ * computed in float64 and rounded to float32 (host only; out has steps+1). */
+int wam_schedule(int steps, double sigma_end, double shift, float* out);
+
+/* Host-side frame table of one episode: compacted frames (valid history in
+ * order, then future), and for each compacted frame i the end (exclusive,
+ * in tokens) of the key prefix its queries see.  src_frame/kend: host
+ * [WAM_MAX_FRAMES].  Returns the number of compacted frames or < 0. */
+int wam_frame_table(const int32_t* frame_block, const uint8_t* valid, int Fh, int Ff,
+                    int P, int32_t* src_frame, int32_t* kend);
+
+/* Visibility matrix evaluated on the GPU by the same predicate the attention
+ * kernels use: vis[q][k] (uncompacted tokens, F = Fh + Ff frames of P) is 1
+ * iff both tokens are valid and k is visible to q.  vis: device [F*P][F*P]. */
+int wam_debug_visibility(const int32_t* frame_block, const uint8_t* valid, int Fh, int Ff,
+                         int P, uint8_t* vis, void* stream);
+
+/* Kernel-level attention entries (the kernels the calls above use).
+ * Action attention: q [B][Hh][H][dh], ka [B][Hh][H][dh], va [B][Hh][dh][H]
+ * (the chunk's own keys; NULL with n_act = 0 to leave them out), cache layer
+ * kc [B][Hh][cap][dh], vc [B][Hh][dh][cap] with len[b] (host) rows, or
+ * kc = vc = NULL.  out [B][H][Hh*dh] dtype.  splits_hint > 0 forces the
+ * number of key splits per (episode, head) (0 = automatic).
+ * ws: wam_action_workspace_bytes of a matching dims. */
+int wam_attention_action(int dtype, int B, int Hh, int dh, int H, const void* q,
+                         const void* ka, const void* va, int n_act,
+                         const void* kc, const void* vc, int cap, const int32_t* len,
+                         void* out, int splits_hint, void* ws, size_t ws_bytes, void* stream);
+
+/* Block-causal prefill attention for rows row0..row0+nq-1 of one episode's
+ * cache layer: q [Hh][nq][dh], kc [Hh][cap][dh], vc [Hh][dh][cap];
+ * query row r (cache position row0 + r) sees cache rows 0..kend[(row0+r)/P]-1
+ * (kend from wam_frame_table).  out [nq][Hh*dh] dtype. */
+int wam_attention_prefill(int dtype, int Hh, int dh, int nq, int row0, int P,
+                          const int32_t* kend, int n_frames, const void* q,
+                          const void* kc, const void* vc, int cap, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WAM_H */

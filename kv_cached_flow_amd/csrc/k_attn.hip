@@ -1,0 +1,630 @@
+// Attention kernels.
+//
+//  * attn_prefill  block-causal video attention (flash style): bf16 MFMA
+//    (v_mfma_f32_16x16x32_bf16) with K and V^T tiles staged in LDS, fp32
+//    online softmax in the log2 domain.  A query in cache row r sees cache
+//    rows [0, kend(r)) (own and earlier temporal blocks; padded frames are
+//    compacted out of the cache).
+//  * attn_action   32 action queries per (episode, head) over [cache ; own
+//    keys]: split-K over the cache tokens, K and V^T streamed straight from
+//    HBM into MFMA operands with 16-byte loads, per-wave online softmax, a
+//    fixed-order merge inside the workgroup and a fixed-order merge of the
+//    splits in a second kernel.  The chunk's own keys are one more split.
+//
+// Both compute S^T = K Q^T so that a lane owns one query column: row maxima
+// and sums are per-lane plus two cross-lane steps.  Key rows are permuted
+// inside each 32-key window so that the S^T output layout is exactly the
+// B-operand layout of the P V MFMA (no data movement between the two):
+// in window w, S subtile 2w row r is key 8*(r/4) + r%4, subtile 2w+1 row r is
+// key 8*(r/4) + 4 + r%4, so lane group g ends up holding keys 8g..8g+7.
+//
+// fp32 variants (one thread per query, plain FMA) serve the fp32 workload.
+#include <algorithm>
+
+#include "wam_internal.h"
+
+namespace wam {
+
+#define LOG2E 1.4426950408889634f
+
+__device__ inline float wave_max16x4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+__device__ inline float wave_sum16x4(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__device__ inline bf16x8 pack8(const float* p) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; i++) r[i] = (short)f2bf(p[i]);
+  return r;
+}
+
+// key index (0..63) inside a 64-key tile of S^T subtile `sub` (0..3), row r (0..15)
+__device__ inline int perm_key(int sub, int r) {
+  return 32 * (sub >> 1) + 8 * (r >> 2) + (r & 3) + 4 * (sub & 1);
+}
+
+// ====================================================================== prefill
+namespace pf {
+constexpr int QW = 32, NW = 4, QT = QW * NW;  // queries per wave / per workgroup
+constexpr int KT = 64;                        // keys per tile
+constexpr int LD = 64 + 8;                    // LDS row stride (bf16)
+}
+
+__global__ __launch_bounds__(256) void attn_prefill_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+    bf16_t* __restrict__ out, int nq, int row0, int cap, int Hh, FrameTab tab, float sl2) {
+  using namespace pf;
+  __shared__ __attribute__((aligned(16))) bf16_t sK[KT * LD];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[64 * LD];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int h = blockIdx.y;
+  const int ntq = (nq + QT - 1) / QT;
+  const int qt = ntq - 1 - blockIdx.x;  // heaviest (latest) query tiles first
+  const int q0 = qt * QT;
+  const int qlast = min(q0 + QT, nq) - 1;
+  const int kend_min = kend_of_row(tab, row0 + q0);
+  const int kend_max = kend_of_row(tab, row0 + qlast);
+  const bf16_t* kh = kc + (long long)h * cap * 64;
+  const bf16_t* vh = vc + (long long)h * 64 * cap;
+
+  // this lane's two query columns and their key ends
+  int kq[2];
+  bf16x8 qf[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const int qi = q0 + w * QW + 16 * t + c16;
+    const bool ok = qi < nq;
+    kq[t] = ok ? kend_of_row(tab, row0 + qi) : kend_max;
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+      if (ok)
+        qf[t][s] = *(const bf16x8*)(q + ((long long)h * nq + qi) * 64 + 32 * s + 8 * g);
+      else
+        qf[t][s] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  floatx4 o[4][2];
+#pragma unroll
+  for (int d = 0; d < 4; d++)
+#pragma unroll
+    for (int t = 0; t < 2; t++) o[d][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+
+  // register staging of the next K / V^T tile (2 chunks of 16 B each per thread)
+  u32x4 rk[2], rv[2];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int c = tid + 256 * i;
+      const int row = c >> 3, ch = c & 7;
+      const int key = kt + row;
+      rk[i] = (key < kend_max) ? *(const u32x4*)(kh + (long long)key * 64 + ch * 8)
+                               : u32x4{0u, 0u, 0u, 0u};
+      const int k0 = kt + ch * 8;  // V^T: row = head dim, 8 keys
+      if (k0 + 8 <= kend_max) {
+        rv[i] = *(const u32x4*)(vh + (long long)row * cap + k0);
+      } else if (k0 < kend_max) {
+        u32x4 x = *(const u32x4*)(vh + (long long)row * cap + k0);
+        bf16_t* e = (bf16_t*)&x;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+          if (k0 + j >= kend_max) e[j] = 0;
+        rv[i] = x;
+      } else {
+        rv[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  gload(0);
+  for (int kt = 0; kt < kend_max; kt += KT) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int c = tid + 256 * i;
+      const int row = c >> 3, ch = c & 7;
+      *(u32x4*)(sK + row * LD + ch * 8) = rk[i];
+      *(u32x4*)(sV + row * LD + ch * 8) = rv[i];
+    }
+    __syncthreads();
+    if (kt + KT < kend_max) gload(kt + KT);
+
+    floatx4 sacc[4][2];
+#pragma unroll
+    for (int sub = 0; sub < 4; sub++) {
+#pragma unroll
+      for (int t = 0; t < 2; t++) sacc[sub][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int kr = perm_key(sub, c16);
+#pragma unroll
+      for (int s = 0; s < 2; s++) {
+        bf16x8 a = *(const bf16x8*)(sK + kr * LD + 32 * s + 8 * g);
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+          sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[t][s], sacc[sub][t], 0, 0, 0);
+      }
+    }
+    const bool need_mask = (kt + KT > kend_min);
+    bf16x8 pf[2][2];  // [window][q tile]
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      float sv[4][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < 4; sub++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          float x = sacc[sub][t][r] * sl2;
+          if (need_mask) {
+            const int key = kt + 32 * (sub >> 1) + 8 * g + 4 * (sub & 1) + r;
+            if (key >= kq[t]) x = -INFINITY;
+          }
+          sv[sub][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = wave_max16x4(mx);
+      const float mnew = fmaxf(mrun[t], mx);
+      const float alpha = __builtin_amdgcn_exp2f(mrun[t] - mnew);
+      mrun[t] = mnew;
+      float ls = 0.f;
+      float p[4][4];
+#pragma unroll
+      for (int sub = 0; sub < 4; sub++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          p[sub][r] = __builtin_amdgcn_exp2f(sv[sub][r] - mnew);
+          ls += p[sub][r];
+        }
+      lrun[t] = lrun[t] * alpha + ls;
+#pragma unroll
+      for (int d = 0; d < 4; d++) o[d][t] *= alpha;
+#pragma unroll
+      for (int wd = 0; wd < 2; wd++) {
+        float pw[8] = {p[2 * wd][0], p[2 * wd][1], p[2 * wd][2], p[2 * wd][3],
+                       p[2 * wd + 1][0], p[2 * wd + 1][1], p[2 * wd + 1][2], p[2 * wd + 1][3]};
+        pf[wd][t] = pack8(pw);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+#pragma unroll
+      for (int wd = 0; wd < 2; wd++) {
+        bf16x8 a = *(const bf16x8*)(sV + (16 * d + c16) * LD + 32 * wd + 8 * g);
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+          o[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[wd][t], o[d][t], 0, 0, 0);
+      }
+  }
+  const int D = Hh * 64;
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const float l = wave_sum16x4(lrun[t]);
+    const int qi = q0 + w * QW + 16 * t + c16;
+    if (qi >= nq) continue;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      bf16_t v4[4];
+#pragma unroll
+      for (int r = 0; r < 4; r++) v4[r] = f2bf(o[d][t][r] * inv);
+      *(uint2*)(out + (long long)qi * D + h * 64 + 16 * d + 4 * g) = *(uint2*)v4;
+    }
+  }
+}
+
+// fp32: one thread per (query, head)
+__global__ __launch_bounds__(64) void attn_prefill_f32_kernel(const float* __restrict__ q,
+                                                              const float* __restrict__ kc,
+                                                              const float* __restrict__ vc,
+                                                              float* __restrict__ out, int nq,
+                                                              int row0, int cap, int Hh,
+                                                              FrameTab tab, float scale) {
+  const int h = blockIdx.y;
+  const int qi = blockIdx.x * 64 + threadIdx.x;
+  if (qi >= nq) return;
+  const float* qr = q + ((long long)h * nq + qi) * 64;
+  const float* kh = kc + (long long)h * cap * 64;
+  const float* vh = vc + (long long)h * 64 * cap;
+  float qv[64], o[64];
+#pragma unroll
+  for (int d = 0; d < 64; d++) { qv[d] = qr[d]; o[d] = 0.f; }
+  const int kend = kend_of_row(tab, row0 + qi);
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j < kend; j++) {
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < 64; d++) s = fmaf(qv[d], kh[(long long)j * 64 + d], s);
+    s *= scale;
+    const float mn = fmaxf(m, s);
+    const float a = expf(m - mn), p = expf(s - mn);
+    l = l * a + p;
+#pragma unroll
+    for (int d = 0; d < 64; d++) o[d] = fmaf(p, vh[(long long)d * cap + j], o[d] * a);
+    m = mn;
+  }
+  const float inv = 1.0f / l;
+  float* orow = out + (long long)qi * Hh * 64 + h * 64;
+#pragma unroll
+  for (int d = 0; d < 64; d++) orow[d] = o[d] * inv;
+}
+
+hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int nq, int row0, const FrameTab& tab,
+                        const void* q, const void* kc, const void* vc, int cap, void* out) {
+  if (nq <= 0) return hipSuccess;
+  if (dt == WAM_BF16) {
+    dim3 grid((nq + pf::QT - 1) / pf::QT, Hh);
+    hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, (const bf16_t*)q,
+                       (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)out, nq, row0, cap, Hh,
+                       tab, 0.125f * LOG2E);
+  } else {
+    dim3 grid((nq + 63) / 64, Hh);
+    hipLaunchKernelGGL(attn_prefill_f32_kernel, grid, dim3(64), 0, s, (const float*)q,
+                       (const float*)kc, (const float*)vc, (float*)out, nq, row0, cap, Hh, tab,
+                       0.125f);
+  }
+  return hipGetLastError();
+}
+
+// ====================================================================== action
+namespace act {
+constexpr int H = 32;   // queries per (episode, head)
+constexpr int KT = 64;  // keys per wave tile
+}
+
+struct ActGeom {
+  int B, Hh, cap, n_act, kc_chunk, S;  // S = splits per (b, h) incl. the own-key split
+  ActLens lens;
+};
+
+// Split (b, h, s): cache keys [s*kc_chunk, min(len, (s+1)*kc_chunk)) for s < ncs(b),
+// the chunk's own keys for s == ncs(b).  Writes the split's (m, l, o) in the
+// log2 domain: m [32], l [32], o [32][64] (unnormalised).
+__global__ __launch_bounds__(256) void attn_action_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ ka, const bf16_t* __restrict__ va,
+    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, ActGeom G,
+    float* __restrict__ part, float sl2) {
+  using namespace act;
+  __shared__ float sm[4][H], sl[4][H];
+  __shared__ float so[4][H][65];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int len = G.lens.len[b];
+  const int ncs = (kc != nullptr) ? (len + G.kc_chunk - 1) / G.kc_chunk : 0;
+  const bool own = (s == ncs);
+  if (s > ncs || (own && G.n_act == 0)) return;
+  const bf16_t* kb;
+  const bf16_t* vb;
+  int key0, key1, vld;
+  if (!own) {
+    kb = kc + ((long long)b * G.Hh + h) * G.cap * 64;
+    vb = vc + ((long long)b * G.Hh + h) * 64 * G.cap;
+    key0 = s * G.kc_chunk;
+    key1 = min(len, key0 + G.kc_chunk);
+    vld = G.cap;
+  } else {
+    kb = ka + ((long long)b * G.Hh + h) * H * 64;
+    vb = va + ((long long)b * G.Hh + h) * 64 * H;
+    key0 = 0;
+    key1 = G.n_act;
+    vld = H;
+  }
+  // queries: B operand of S^T = K Q^T
+  bf16x8 qf[2][2];
+  const bf16_t* qb = q + ((long long)b * G.Hh + h) * H * 64;
+#pragma unroll
+  for (int t = 0; t < 2; t++)
+#pragma unroll
+    for (int ss = 0; ss < 2; ss++)
+      qf[t][ss] = *(const bf16x8*)(qb + (16 * t + c16) * 64 + 32 * ss + 8 * g);
+
+  floatx4 o[4][2];
+#pragma unroll
+  for (int d = 0; d < 4; d++)
+#pragma unroll
+    for (int t = 0; t < 2; t++) o[d][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+
+  for (int kt = key0 + w * KT; kt < key1; kt += 4 * KT) {
+    // ---- loads: K rows (A of S^T) and V^T rows (A of P V), zero past key1
+    bf16x8 ak[4][2], av[4][2];
+#pragma unroll
+    for (int sub = 0; sub < 4; sub++) {
+      const int key = kt + perm_key(sub, c16);
+#pragma unroll
+      for (int ss = 0; ss < 2; ss++)
+        ak[sub][ss] = (key < key1) ? *(const bf16x8*)(kb + (long long)key * 64 + 32 * ss + 8 * g)
+                                   : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+#pragma unroll
+      for (int wd = 0; wd < 2; wd++) {
+        const int k0 = kt + 32 * wd + 8 * g;
+        const bf16_t* src = vb + (long long)(16 * d + c16) * vld + k0;
+        if (k0 + 8 <= key1) {
+          av[d][wd] = *(const bf16x8*)src;
+        } else if (k0 < key1) {
+          bf16x8 x = *(const bf16x8*)src;
+#pragma unroll
+          for (int j = 0; j < 8; j++)
+            if (k0 + j >= key1) x[j] = 0;
+          av[d][wd] = x;
+        } else {
+          av[d][wd] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+      }
+    // ---- S^T
+    floatx4 sacc[4][2];
+#pragma unroll
+    for (int sub = 0; sub < 4; sub++)
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        sacc[sub][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ss = 0; ss < 2; ss++)
+          sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[sub][ss], qf[t][ss], sacc[sub][t], 0, 0, 0);
+      }
+    const bool need_mask = (kt + KT > key1);
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      float sv[4][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < 4; sub++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          float x = sacc[sub][t][r] * sl2;
+          if (need_mask && kt + 32 * (sub >> 1) + 8 * g + 4 * (sub & 1) + r >= key1) x = -INFINITY;
+          sv[sub][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = wave_max16x4(mx);
+      const float mnew = fmaxf(mrun[t], mx);
+      const float alpha = __builtin_amdgcn_exp2f(mrun[t] - mnew);
+      mrun[t] = mnew;
+      float ls = 0.f, p[4][4];
+#pragma unroll
+      for (int sub = 0; sub < 4; sub++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          p[sub][r] = __builtin_amdgcn_exp2f(sv[sub][r] - mnew);
+          ls += p[sub][r];
+        }
+      lrun[t] = lrun[t] * alpha + ls;
+#pragma unroll
+      for (int d = 0; d < 4; d++) o[d][t] *= alpha;
+#pragma unroll
+      for (int wd = 0; wd < 2; wd++) {
+        float pw[8] = {p[2 * wd][0], p[2 * wd][1], p[2 * wd][2], p[2 * wd][3],
+                       p[2 * wd + 1][0], p[2 * wd + 1][1], p[2 * wd + 1][2], p[2 * wd + 1][3]};
+        pf[wd][t] = pack8(pw);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+#pragma unroll
+      for (int wd = 0; wd < 2; wd++)
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+          o[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[d][wd], pf[wd][t], o[d][t], 0, 0, 0);
+  }
+  // ---- per-wave state to LDS (waves without keys hold m = -inf, l = 0, o = 0)
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const float l = wave_sum16x4(lrun[t]);
+    const int qi = 16 * t + c16;
+    if (g == 0) {
+      sm[w][qi] = mrun[t];
+      sl[w][qi] = l;
+    }
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) so[w][qi][16 * d + 4 * g + r] = o[d][t][r];
+  }
+  __syncthreads();
+  // ---- merge the 4 waves in a fixed order, write the split's partial
+  const long long pidx = (((long long)b * G.Hh + h) * G.S + s);
+  float* pm = part + pidx * H;
+  float* pl = part + (long long)G.B * G.Hh * G.S * H + pidx * H;
+  float* po = part + 2ll * G.B * G.Hh * G.S * H + pidx * H * 64;
+  for (int i = tid; i < H * 64; i += 256) {
+    const int qi = i >> 6, d = i & 63;
+    float M = sm[0][qi];
+#pragma unroll
+    for (int ww = 1; ww < 4; ww++) M = fmaxf(M, sm[ww][qi]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ww++) {
+      const float f = (sm[ww][qi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[ww][qi] - M);
+      L += sl[ww][qi] * f;
+      O += so[ww][qi][d] * f;
+    }
+    po[qi * 64 + d] = O;
+    if (d == 0) {
+      pm[qi] = M;
+      pl[qi] = L;
+    }
+  }
+}
+
+// Merge splits 0..S_b-1 of (b, h) in order; out[b*32 + q][h*64 + d].
+template <typename TO>
+__global__ __launch_bounds__(256) void attn_action_merge_kernel(const float* __restrict__ part,
+                                                                ActGeom G, TO* __restrict__ out) {
+  using namespace act;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int len = G.lens.len[b];
+  const int ncs = G.kc_chunk > 0 ? (len + G.kc_chunk - 1) / G.kc_chunk : 0;
+  const int ns = ncs + (G.n_act > 0 ? 1 : 0);
+  const long long base = ((long long)b * G.Hh + h) * G.S;
+  const float* pm = part + base * H;
+  const float* pl = part + (long long)G.B * G.Hh * G.S * H + base * H;
+  const float* po = part + 2ll * G.B * G.Hh * G.S * H + base * H * 64;
+  for (int i = threadIdx.x; i < H * 64; i += 256) {
+    const int qi = i >> 6, d = i & 63;
+    float M = -INFINITY;
+    for (int sp = 0; sp < ns; sp++) M = fmaxf(M, pm[sp * H + qi]);
+    float L = 0.f, O = 0.f;
+    for (int sp = 0; sp < ns; sp++) {
+      const float f = __builtin_amdgcn_exp2f(pm[sp * H + qi] - M);
+      L += pl[sp * H + qi] * f;
+      O += po[((long long)sp * H + qi) * 64 + d] * f;
+    }
+    out[((long long)b * H + qi) * G.Hh * 64 + h * 64 + d] = from_f<TO>(O / L);
+  }
+}
+
+// fp32: one thread per (episode, head, query)
+__global__ __launch_bounds__(64) void attn_action_f32_kernel(const float* __restrict__ q,
+                                                             const float* __restrict__ ka,
+                                                             const float* __restrict__ va,
+                                                             const float* __restrict__ kc,
+                                                             const float* __restrict__ vc,
+                                                             ActGeom G, float* __restrict__ out,
+                                                             float scale) {
+  using namespace act;
+  const int h = blockIdx.x, b = blockIdx.y, qi = threadIdx.x;
+  if (qi >= H) return;
+  const float* qr = q + (((long long)b * G.Hh + h) * H + qi) * 64;
+  float qv[64], o[64];
+#pragma unroll
+  for (int d = 0; d < 64; d++) { qv[d] = qr[d]; o[d] = 0.f; }
+  float m = -INFINITY, l = 0.f;
+  for (int part = 0; part < 2; part++) {
+    const float* kb;
+    const float* vb;
+    int n, ld;
+    if (part == 0) {
+      if (!kc) continue;
+      kb = kc + ((long long)b * G.Hh + h) * G.cap * 64;
+      vb = vc + ((long long)b * G.Hh + h) * 64 * G.cap;
+      n = G.lens.len[b];
+      ld = G.cap;
+    } else {
+      kb = ka + ((long long)b * G.Hh + h) * H * 64;
+      vb = va + ((long long)b * G.Hh + h) * 64 * H;
+      n = G.n_act;
+      ld = H;
+    }
+    for (int j = 0; j < n; j++) {
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < 64; d++) s = fmaf(qv[d], kb[(long long)j * 64 + d], s);
+      s *= scale;
+      const float mn = fmaxf(m, s);
+      const float a = expf(m - mn), p = expf(s - mn);
+      l = l * a + p;
+#pragma unroll
+      for (int d = 0; d < 64; d++) o[d] = fmaf(p, vb[(long long)d * ld + j], o[d] * a);
+      m = mn;
+    }
+  }
+  const float inv = 1.0f / l;
+  float* orow = out + ((long long)b * H + qi) * G.Hh * 64 + h * 64;
+#pragma unroll
+  for (int d = 0; d < 64; d++) orow[d] = o[d] * inv;
+}
+
+static int action_chunk(int B, int Hh, int max_len, int splits_hint) {
+  if (max_len <= 0) return 0;
+  int splits = splits_hint > 0 ? splits_hint : (512 + B * Hh - 1) / (B * Hh);
+  if (splits < 1) splits = 1;
+  int kc = (max_len + splits - 1) / splits;
+  kc = (kc + act::KT - 1) / act::KT * act::KT;
+  if (splits_hint <= 0 && kc < 4 * act::KT) kc = 4 * act::KT;
+  return kc;
+}
+
+// Upper bound of the split count for any length <= max_len (monotone in
+// max_len, so a workspace sized for a capacity fits every shorter cache).
+size_t attn_action_scratch_bytes(int B, int Hh, int H, int max_len, int splits_hint) {
+  int S = 1;
+  if (max_len > 0) {
+    if (splits_hint > 0) {
+      int kc = action_chunk(B, Hh, max_len, splits_hint);
+      S = (max_len + kc - 1) / kc + 1;
+    } else {
+      int splits = (512 + B * Hh - 1) / (B * Hh);
+      S = std::min((max_len + 4 * act::KT - 1) / (4 * act::KT), splits + 1) + 1;
+    }
+  }
+  return (size_t)B * Hh * S * H * (64 + 2) * sizeof(float);
+}
+
+hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* q,
+                       const void* ka, const void* va, int n_act, const void* kc,
+                       const void* vc, int cap, const ActLens& lens, void* out,
+                       int splits_hint, void* scratch, size_t scratch_bytes) {
+  if (H != act::H) return hipErrorInvalidValue;
+  ActGeom G;
+  G.B = B;
+  G.Hh = Hh;
+  G.cap = cap;
+  G.n_act = n_act;
+  G.lens = lens;
+  int max_len = 0;
+  if (kc)
+    for (int b = 0; b < B; b++) max_len = max(max_len, lens.len[b]);
+  if (!kc)
+    for (int b = 0; b < B; b++) G.lens.len[b] = 0;
+  if (dt == WAM_F32) {
+    G.kc_chunk = 0;
+    G.S = 0;
+    hipLaunchKernelGGL(attn_action_f32_kernel, dim3(Hh, B), dim3(64), 0, s, (const float*)q,
+                       (const float*)ka, (const float*)va, (const float*)kc, (const float*)vc,
+                       G, (float*)out, 0.125f);
+    return hipGetLastError();
+  }
+  G.kc_chunk = action_chunk(B, Hh, max_len, splits_hint);
+  G.S = (G.kc_chunk > 0 ? (max_len + G.kc_chunk - 1) / G.kc_chunk : 0) + 1;
+  if (scratch_bytes < (size_t)B * Hh * G.S * H * 66 * sizeof(float)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_action_kernel, dim3(G.S, Hh, B), dim3(256), 0, s, (const bf16_t*)q,
+                     (const bf16_t*)ka, (const bf16_t*)va, (const bf16_t*)kc, (const bf16_t*)vc,
+                     G, (float*)scratch, 0.125f * LOG2E);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_action_merge_kernel<bf16_t>, dim3(Hh, B), dim3(256), 0, s,
+                     (const float*)scratch, G, (bf16_t*)out);
+  return hipGetLastError();
+}
+
+// ====================================================================== debug
+struct FrameComp {
+  int F, P;
+  int comp[WAM_MAX_FRAMES];
+};
+
+__global__ void visibility_kernel(FrameTab tab, FrameComp fc, uint8_t* __restrict__ vis) {
+  const long long n = (long long)fc.F * fc.P;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n * n;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int qt = (int)(i / n), kt = (int)(i % n);
+    const int cq = fc.comp[qt / fc.P], ck = fc.comp[kt / fc.P];
+    uint8_t v = 0;
+    if (cq >= 0 && ck >= 0) v = visible(tab, cq * fc.P + qt % fc.P, ck * fc.P + kt % fc.P) ? 1 : 0;
+    vis[i] = v;
+  }
+}
+
+hipError_t debug_visibility(hipStream_t s, const FrameTab& tab, const int* comp_of_frame,
+                            int F, uint8_t* vis) {
+  FrameComp fc;
+  fc.F = F;
+  fc.P = tab.P;
+  for (int f = 0; f < F; f++) fc.comp[f] = comp_of_frame[f];
+  long long n = (long long)F * tab.P;
+  long long blocks = (n * n + 255) / 256;
+  if (blocks > 65535) blocks = 65535;
+  hipLaunchKernelGGL(visibility_kernel, dim3((unsigned)blocks), dim3(256), 0, s, tab, fc, vis);
+  return hipGetLastError();
+}
+
+}  // namespace wam

@@ -1,0 +1,235 @@
+// Elementwise and row-wise kernels: RMSNorm, token embedding (+ time
+// embedding), Euler update, dtype conversion, Interval KV-Fusion.
+#include "wam_internal.h"
+
+namespace wam {
+
+// ------------------------------------------------------------ RMSNorm
+// One wavefront per row: y = x * (mean(x^2) + 1e-6)^(-1/2) * g.
+template <typename TO>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
+                                                      const float* __restrict__ g,
+                                                      TO* __restrict__ y, int M, int D) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float* xr = x + (long long)row * D;
+  float ss = 0.f;
+  for (int i = lane * 4; i < D; i += 256) {
+    float4 v = *(const float4*)(xr + i);
+    ss = fmaf(v.x, v.x, ss);
+    ss = fmaf(v.y, v.y, ss);
+    ss = fmaf(v.z, v.z, ss);
+    ss = fmaf(v.w, v.w, ss);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const float r = 1.0f / sqrtf(ss / (float)D + 1e-6f);
+  TO* yr = y + (long long)row * D;
+  for (int i = lane * 4; i < D; i += 256) {
+    float4 v = *(const float4*)(xr + i);
+    float4 gg = *(const float4*)(g + i);
+    yr[i + 0] = from_f<TO>(v.x * r * gg.x);
+    yr[i + 1] = from_f<TO>(v.y * r * gg.y);
+    yr[i + 2] = from_f<TO>(v.z * r * gg.z);
+    yr[i + 3] = from_f<TO>(v.w * r * gg.w);
+  }
+}
+
+hipError_t rmsnorm(hipStream_t s, int odt, const float* x, const float* g, void* y, int M, int D) {
+  if (M <= 0) return hipSuccess;
+  dim3 grid((M + 3) / 4);
+  if (odt == WAM_BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, dim3(256), 0, s, x, g, (bf16_t*)y, M, D);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, x, g, (float*)y, M, D);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ embedding
+// X[m][n] = sum_c x[row(m)][c] * w_in[n][c] + emb[n]  (C <= 64, fp32 FMA in c order)
+constexpr int EMB_ROWS = 32, EMB_MAXC = 64;
+
+template <typename TX, typename TW>
+__global__ __launch_bounds__(256) void embed_kernel(const TX* __restrict__ x, RowMap map,
+                                                    const TW* __restrict__ w_in,
+                                                    const float* __restrict__ emb,
+                                                    float* __restrict__ X, int M, int D, int C) {
+  __shared__ float xs[EMB_ROWS][EMB_MAXC];
+  const int m0 = blockIdx.x * EMB_ROWS;
+  const int n = blockIdx.y * 256 + threadIdx.x;
+  for (int i = threadIdx.x; i < EMB_ROWS * C; i += 256) {
+    int r = i / C, c = i - r * C;
+    int m = m0 + r;
+    float v = 0.f;
+    if (m < M) {
+      int f = m / map.P, t = m - f * map.P;
+      v = to_f<TX>(x[((long long)map.src[f] * map.P + t) * C + c]);
+    }
+    xs[r][c] = v;
+  }
+  __syncthreads();
+  if (n >= D) return;
+  float w[EMB_MAXC];
+#pragma unroll
+  for (int c = 0; c < EMB_MAXC; c++) w[c] = (c < C) ? to_f<TW>(w_in[(long long)n * C + c]) : 0.f;
+  const float en = emb[n];
+  const int rows = min(EMB_ROWS, M - m0);
+  for (int r = 0; r < rows; r++) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < EMB_MAXC; c++)
+      if (c < C) acc = fmaf(xs[r][c], w[c], acc);
+    X[(long long)(m0 + r) * D + n] = acc + en;
+  }
+}
+
+hipError_t embed(hipStream_t s, int xdt, int wdt, const void* x, const RowMap& map,
+                 const void* w_in, const float* emb, float* X, int M, int D, int C) {
+  if (M <= 0) return hipSuccess;
+  if (C > EMB_MAXC) return hipErrorInvalidValue;
+  dim3 grid((M + EMB_ROWS - 1) / EMB_ROWS, (D + 255) / 256);
+#define EMB(TX, TW)                                                                          \
+  hipLaunchKernelGGL((embed_kernel<TX, TW>), grid, dim3(256), 0, s, (const TX*)x, map,       \
+                     (const TW*)w_in, emb, X, M, D, C)
+  if (xdt == WAM_F32 && wdt == WAM_F32) EMB(float, float);
+  else if (xdt == WAM_F32 && wdt == WAM_BF16) EMB(float, bf16_t);
+  else if (xdt == WAM_BF16 && wdt == WAM_BF16) EMB(bf16_t, bf16_t);
+  else return hipErrorInvalidValue;
+#undef EMB
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ time embedding
+struct SigmaList {
+  float v[WAM_MAX_STEPS + 8];
+};
+
+// emb[i] = [cos(t w_j), sin(t w_j)], t = 1000 sigma_i, w_j = 10000^(-j/(D/2)),
+// evaluated in float64 and rounded to fp32.
+__global__ void time_embedding_kernel(SigmaList sig, int D, float* __restrict__ emb) {
+  const int i = blockIdx.y;
+  const int half = D / 2;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < half; j += gridDim.x * blockDim.x) {
+    double t = 1000.0 * (double)sig.v[i];
+    double w = pow(10000.0, -(double)j / (double)half);
+    double a = t * w;
+    emb[(long long)i * D + j] = (float)cos(a);
+    emb[(long long)i * D + half + j] = (float)sin(a);
+  }
+}
+
+hipError_t time_embedding(hipStream_t s, const float* sigma_host, int n, int D, float* emb) {
+  if (n <= 0) return hipSuccess;
+  if (n > WAM_MAX_STEPS + 8) return hipErrorInvalidValue;
+  SigmaList l;
+  for (int i = 0; i < n; i++) l.v[i] = sigma_host[i];
+  dim3 grid((D / 2 + 255) / 256, n);
+  hipLaunchKernelGGL(time_embedding_kernel, grid, dim3(256), 0, s, l, D, emb);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ Euler / copy
+__global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v, int64_t n, float dt) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    x[i] = fmaf(dt, v[i], x[i]);
+}
+
+hipError_t euler(hipStream_t s, float* x, const float* v, int64_t n, float dt) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(euler_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, v, n, dt);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ void cvt_kernel(const T* __restrict__ src, float* __restrict__ dst, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = to_f<T>(src[i]);
+}
+
+hipError_t copy_cvt_f32(hipStream_t s, int sdt, const void* src, float* dst, int64_t n) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (sdt == WAM_BF16)
+    hipLaunchKernelGGL(cvt_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const bf16_t*)src, dst, n);
+  else
+    hipLaunchKernelGGL(cvt_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const float*)src, dst, n);
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int* __restrict__ p, int n, int v) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
+}
+
+// A fill kernel rather than a memset node, so that the call stays capturable.
+hipError_t fill_i32(hipStream_t s, int* p, int n, int v) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0,
+                     s, p, n, v);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ Interval KV-Fusion
+// dst[m][i] = sum_{j < count_m} w[m][j] * src[start_m + j][i], fp32 accumulate in
+// j order, one rounding to the storage type.  8 elements per thread (16-byte
+// bf16 loads); layer_elems is a multiple of 8.
+template <typename T>
+__global__ __launch_bounds__(256) void fuse_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                   long long layer_elems, FuseArgs a) {
+  const int m = blockIdx.y;
+  const int cnt = a.count[m];
+  const T* base = src + (long long)a.start[m] * layer_elems;
+  T* out = dst + (long long)m * layer_elems;
+  for (long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 8; i < layer_elems;
+       i += (long long)gridDim.x * 256 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[e] = 0.f;
+    for (int j = 0; j < cnt; j++) {
+      const float wj = a.w[m][j];
+      T v[8];
+      if constexpr (sizeof(T) == 2) {
+        *(u32x4*)v = __builtin_nontemporal_load((const u32x4*)(base + j * layer_elems + i));
+      } else {
+        *(u32x4*)v = __builtin_nontemporal_load((const u32x4*)(base + j * layer_elems + i));
+        *(u32x4*)(v + 4) = __builtin_nontemporal_load((const u32x4*)(base + j * layer_elems + i + 4));
+      }
+#pragma unroll
+      for (int e = 0; e < 8; e++) acc[e] = fmaf(wj, to_f<T>(v[e]), acc[e]);
+    }
+    T o[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) o[e] = from_f<T>(acc[e]);
+    if constexpr (sizeof(T) == 2) {
+      *(u32x4*)(out + i) = *(u32x4*)o;
+    } else {
+      *(u32x4*)(out + i) = *(u32x4*)o;
+      *(u32x4*)(out + i + 4) = *(u32x4*)(o + 4);
+    }
+  }
+}
+
+hipError_t fuse_kv(hipStream_t s, int dt, const void* src, void* dst, long long layer_elems,
+                   const FuseArgs& a) {
+  if (a.M <= 0 || layer_elems <= 0) return hipSuccess;
+  if (layer_elems % 8) return hipErrorInvalidValue;
+  long long per = (layer_elems / 8 + 255) / 256;
+  unsigned bx = (unsigned)(per < 1024 ? per : 1024);
+  dim3 grid(bx, a.M);
+  if (dt == WAM_BF16)
+    hipLaunchKernelGGL(fuse_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)src,
+                       (bf16_t*)dst, layer_elems, a);
+  else
+    hipLaunchKernelGGL(fuse_kernel<float>, grid, dim3(256), 0, s, (const float*)src,
+                       (float*)dst, layer_elems, a);
+  return hipGetLastError();
+}
+
+}  // namespace wam

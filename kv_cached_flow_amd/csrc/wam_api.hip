@@ -1,0 +1,736 @@
+// C-ABI of libwam: argument validation, schedules, frame tables, workspace
+// planning and the stream-ordered launch sequence of each call.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "wam_internal.h"
+
+using namespace wam;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIPCK(x)                                                                 \
+  do {                                                                           \
+    hipError_t e_ = (x);                                                         \
+    if (e_ != hipSuccess)                                                        \
+      return fail(WAM_E_HIP, "%s failed: %s", #x, hipGetErrorString(e_));       \
+  } while (0)
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t esz(int dt) { return dt == WAM_BF16 ? 2 : 4; }
+
+// Carves a caller-provided workspace (base == nullptr: sizing pass).
+struct Arena {
+  char* base;
+  size_t off = 0;
+  explicit Arena(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+int check_dims(const wam_dims* d) {
+  if (!d) return fail(WAM_E_ARG, "dims is NULL");
+  if (d->dtype != WAM_F32 && d->dtype != WAM_BF16) return fail(WAM_E_ARG, "bad dtype %d", d->dtype);
+  if (d->L < 1 || d->D < 1 || d->Hh < 1 || d->Fm < 1 || d->P < 1)
+    return fail(WAM_E_SHAPE, "non-positive dimension");
+  if (d->dh != 64) return fail(WAM_E_SHAPE, "head dim must be 64 (got %d)", d->dh);
+  if (d->D != d->Hh * d->dh) return fail(WAM_E_SHAPE, "D (%d) != Hh*dh (%d)", d->D, d->Hh * d->dh);
+  if (d->D % 64 || d->Fm % 64) return fail(WAM_E_SHAPE, "D and Fm must be multiples of 64");
+  if (d->H != 32) return fail(WAM_E_SHAPE, "action chunk length must be 32 (got %d)", d->H);
+  if (d->Cv < 1 || d->Cv > 64 || d->A < 1 || d->A > 64)
+    return fail(WAM_E_SHAPE, "Cv and A must be in [1, 64]");
+  return WAM_OK;
+}
+
+int check_expert(const wam_dims* d, const wam_expert_w* e, const char* name) {
+  if (!e || !e->w_in || !e->g_out || !e->w_out || !e->layers)
+    return fail(WAM_E_ARG, "%s expert has a NULL pointer", name);
+  if (e->n_layers != d->L) return fail(WAM_E_SHAPE, "%s expert has %d layers, dims say %d", name, e->n_layers, d->L);
+  if (!aligned16(e->w_in) || !aligned16(e->w_out) || !aligned16(e->g_out))
+    return fail(WAM_E_ALIGN, "%s expert pointer not 16-byte aligned", name);
+  for (int l = 0; l < e->n_layers; l++) {
+    const wam_layer_w& w = e->layers[l];
+    if (!w.g1 || !w.wqkv || !w.wo || !w.g2 || !w.w1 || !w.w2)
+      return fail(WAM_E_ARG, "%s layer %d has a NULL pointer", name, l);
+    if (!aligned16(w.g1) || !aligned16(w.wqkv) || !aligned16(w.wo) || !aligned16(w.g2) ||
+        !aligned16(w.w1) || !aligned16(w.w2))
+      return fail(WAM_E_ALIGN, "%s layer %d pointer not 16-byte aligned", name, l);
+  }
+  return WAM_OK;
+}
+
+int check_kv(const wam_dims* d, const wam_kv* kv, int B, const char* name) {
+  if (!kv->k || !kv->v || !kv->len) return fail(WAM_E_ARG, "%s has a NULL pointer", name);
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(WAM_E_ALIGN, "%s not 16-byte aligned", name);
+  if (kv->dtype != d->dtype) return fail(WAM_E_DTYPE, "%s dtype differs from dims", name);
+  if (kv->B != B || kv->Hh != d->Hh || kv->dh != d->dh)
+    return fail(WAM_E_SHAPE, "%s shape (B=%d Hh=%d dh=%d) does not match", name, kv->B, kv->Hh, kv->dh);
+  if (kv->cap < 64 || kv->cap % 64) return fail(WAM_E_SHAPE, "%s cap must be a positive multiple of 64", name);
+  if (kv->n_layers < 1) return fail(WAM_E_SHAPE, "%s has no layer", name);
+  return WAM_OK;
+}
+
+double phi(double u, double shift) {
+  if (u == 0.0) return 0.0;
+  if (u == 1.0) return 1.0;
+  if (shift == 1.0) return u;
+  return shift * u / (1.0 + (shift - 1.0) * u);
+}
+
+#pragma clang fp contract(off)
+void schedule(int steps, double sigma_end, double shift, float* out) {
+  for (int k = 0; k <= steps; k++) {
+    double u = 1.0 - (double)k / (double)steps;
+    double p = phi(u, shift);
+    double s = sigma_end + (1.0 - sigma_end) * p;
+    out[k] = (float)s;
+  }
+}
+#pragma clang fp contract(on)
+
+// Compacted frames (valid history in order, then future) and key prefix ends.
+int frame_table(const int32_t* block, const uint8_t* valid, int Fh, int Ff, int P,
+                int* src, int* kend) {
+  int n = 0;
+  std::vector<int> blk;
+  for (int f = 0; f < Fh + Ff; f++) {
+    if (f < Fh && valid && !valid[f]) continue;
+    src[n++] = f;
+    blk.push_back(block[f]);
+  }
+  for (int i = 0; i < n; i++) {
+    int j = i;
+    while (j + 1 < n && blk[j + 1] <= blk[i]) j++;
+    kend[i] = (j + 1) * P;
+  }
+  return n;
+}
+
+int check_blocks(const int32_t* block, int F) {
+  for (int f = 1; f < F; f++)
+    if (block[f] < block[f - 1])
+      return fail(WAM_E_SHAPE, "frame_block must be non-decreasing (frame %d)", f);
+  return WAM_OK;
+}
+
+struct Bufs {
+  float* X;
+  void* Y;
+  void* Q;
+  void* Ka;
+  void* Va;
+  void* O;
+  void* Hb;
+  float* Yh;
+  float* emb;
+  GemmScratch gs;
+  void* attn;
+  size_t attn_bytes;
+};
+
+size_t gemm_part_elems(int M, const wam_dims* d) {
+  size_t e = 0;
+  e = std::max(e, gemm_scratch_elems(M, 3 * d->D, d->D));
+  e = std::max(e, gemm_scratch_elems(M, d->D, d->D));
+  e = std::max(e, gemm_scratch_elems(M, d->Fm, d->D));
+  e = std::max(e, gemm_scratch_elems(M, d->D, d->Fm));
+  e = std::max(e, gemm_scratch_elems(M, 2 * d->D, d->D));
+  return e;
+}
+constexpr int N_COUNTERS = 1024;
+
+// ----------------------------------------------------------------- layers
+struct Layer {
+  hipStream_t s;
+  const wam_dims* d;
+  Bufs* b;
+};
+
+// One video layer for rows row0..row0+n-1 of episode cache layer (kl, vl).
+int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const FrameTab& tab,
+                void* kl, void* vl, int cap, bool kv_only) {
+  const wam_dims* d = c.d;
+  const int dt = d->dtype, D = d->D;
+  Bufs& b = *c.b;
+  HIPCK(rmsnorm(c.s, dt, b.X, w.g1, b.Y, n, D));
+  EpiArgs e{};
+  e.q = b.Q;
+  e.k = kl;
+  e.v = vl;
+  e.D = D;
+  e.dh = d->dh;
+  e.rpg = n;
+  e.q_hs = (long long)n * d->dh;
+  e.k_hs = (long long)cap * d->dh;
+  e.v_hs = (long long)d->dh * cap;
+  e.k_row0 = row0;
+  e.v_ld = cap;
+  e.v_col0 = row0;
+  if (kv_only) {
+    e.n_begin = D;
+    HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, 2 * D, D, b.Y, D,
+               (const char*)w.wqkv + (size_t)D * D * esz(dt), D, e, b.gs));
+    return WAM_OK;
+  }
+  HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, 3 * D, D, b.Y, D, w.wqkv, D, e, b.gs));
+  HIPCK(attn_prefill(c.s, dt, d->Hh, n, row0, tab, b.Q, kl, vl, cap, b.O));
+  EpiArgs r{};
+  r.out = b.X;
+  r.ldo = D;
+  HIPCK(gemm(c.s, dt, dt, WAM_F32, EPI_RESID, n, D, D, b.O, D, w.wo, D, r, b.gs));
+  HIPCK(rmsnorm(c.s, dt, b.X, w.g2, b.Y, n, D));
+  EpiArgs gl{};
+  gl.out = b.Hb;
+  gl.ldo = d->Fm;
+  HIPCK(gemm(c.s, dt, dt, dt, EPI_GELU, n, d->Fm, D, b.Y, D, w.w1, D, gl, b.gs));
+  HIPCK(gemm(c.s, dt, dt, WAM_F32, EPI_RESID, n, D, d->Fm, b.Hb, d->Fm, w.w2, d->Fm, r, b.gs));
+  return WAM_OK;
+}
+
+// One action layer on the B*H rows in b.X; kc/vc: that layer's cache for all
+// episodes (or NULL).
+int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, const void* vc,
+                 int cap, const ActLens& lens) {
+  const wam_dims* d = c.d;
+  const int dt = d->dtype, D = d->D, H = d->H, M = B * H;
+  Bufs& b = *c.b;
+  HIPCK(rmsnorm(c.s, dt, b.X, w.g1, b.Y, M, D));
+  EpiArgs e{};
+  e.q = b.Q;
+  e.k = b.Ka;
+  e.v = b.Va;
+  e.D = D;
+  e.dh = d->dh;
+  e.rpg = H;
+  e.q_gs = e.k_gs = (long long)d->Hh * H * d->dh;
+  e.q_hs = e.k_hs = (long long)H * d->dh;
+  e.v_gs = (long long)d->Hh * d->dh * H;
+  e.v_hs = (long long)d->dh * H;
+  e.v_ld = H;
+  HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, M, 3 * D, D, b.Y, D, w.wqkv, D, e, b.gs));
+  HIPCK(attn_action(c.s, dt, B, d->Hh, H, b.Q, b.Ka, b.Va, H, kc, vc, cap, lens, b.O, 0, b.attn,
+                    b.attn_bytes));
+  EpiArgs r{};
+  r.out = b.X;
+  r.ldo = D;
+  HIPCK(gemm(c.s, dt, dt, WAM_F32, EPI_RESID, M, D, D, b.O, D, w.wo, D, r, b.gs));
+  HIPCK(rmsnorm(c.s, dt, b.X, w.g2, b.Y, M, D));
+  EpiArgs gl{};
+  gl.out = b.Hb;
+  gl.ldo = d->Fm;
+  HIPCK(gemm(c.s, dt, dt, dt, EPI_GELU, M, d->Fm, D, b.Y, D, w.w1, D, gl, b.gs));
+  HIPCK(gemm(c.s, dt, dt, WAM_F32, EPI_RESID, M, D, d->Fm, b.Hb, d->Fm, w.w2, d->Fm, r, b.gs));
+  return WAM_OK;
+}
+
+// v = RMSNorm(X; g_out) W_out^T; z += dt * v (and vhat = v).
+int head_euler(const Layer& c, const wam_expert_w* ex, int M, int C, float* z, float dtv, float* vhat) {
+  const wam_dims* d = c.d;
+  Bufs& b = *c.b;
+  HIPCK(rmsnorm(c.s, WAM_F32, b.X, ex->g_out, b.Yh, M, d->D));
+  EpiArgs e{};
+  e.out = z;
+  e.ldo = C;
+  e.dt = dtv;
+  e.vhat = vhat;
+  HIPCK(gemm(c.s, WAM_F32, d->dtype, WAM_F32, EPI_EULER, M, C, d->D, b.Yh, d->D, ex->w_out, d->D, e,
+             b.gs));
+  return WAM_OK;
+}
+
+// workspace of the action path (rows M = B*H)
+void plan_action(Arena& a, const wam_dims* d, int B, int max_len, bool with_emb, Bufs& b) {
+  const int M = B * d->H;
+  const size_t e = esz(d->dtype);
+  b.emb = with_emb ? (float*)a.take((size_t)WAM_MAX_STEPS * d->D * 4) : nullptr;
+  b.X = (float*)a.take((size_t)M * d->D * 4);
+  b.Y = a.take((size_t)M * d->D * e);
+  b.Q = a.take((size_t)M * d->D * e);
+  b.Ka = a.take((size_t)M * d->D * e);
+  b.Va = a.take((size_t)M * d->D * e);
+  b.O = a.take((size_t)M * d->D * e);
+  b.Hb = a.take((size_t)M * d->Fm * e);
+  b.Yh = (float*)a.take((size_t)M * d->D * 4);
+  b.gs.part_elems = gemm_part_elems(M, d);
+  b.gs.part = (float*)a.take(b.gs.part_elems * 4);
+  b.gs.counters = (int*)a.take(N_COUNTERS * 4);
+  b.gs.n_counters = N_COUNTERS;
+  b.attn_bytes = attn_action_scratch_bytes(B, d->Hh, d->H, max_len, 0);
+  b.attn = a.take(b.attn_bytes);
+}
+
+void plan_prefill(Arena& a, const wam_dims* d, int Fh, int Ff, Bufs& b, float** z) {
+  const size_t e = esz(d->dtype);
+  const size_t T = (size_t)std::max(Fh, Ff) * d->P;
+  const size_t Tf = (size_t)Ff * d->P;
+  b.emb = (float*)a.take((size_t)(WAM_MAX_STEPS + 2) * d->D * 4);
+  b.X = (float*)a.take(T * d->D * 4);
+  b.Y = a.take(T * d->D * e);
+  b.Q = a.take(T * d->D * e);
+  b.O = a.take(T * d->D * e);
+  b.Hb = a.take(T * d->Fm * e);
+  b.Yh = (float*)a.take(std::max<size_t>(Tf, 1) * d->D * 4);
+  *z = (float*)a.take(std::max<size_t>(Tf, 1) * d->Cv * 4);
+  // passes of <= 128 rows take the split-K skinny GEMM; size for any of them
+  size_t pe = 0;
+  if ((size_t)d->P <= 128)
+    for (int m = 16; m <= 128; m += 16) pe = std::max(pe, gemm_part_elems(m, d));
+  b.gs.part_elems = pe;
+  b.gs.part = (float*)a.take(pe * 4 + 4);
+  b.gs.counters = (int*)a.take(N_COUNTERS * 4);
+  b.gs.n_counters = N_COUNTERS;
+  b.Ka = b.Va = nullptr;
+  b.attn = nullptr;
+  b.attn_bytes = 0;
+}
+
+size_t layer_stride(const wam_kv* kv) {
+  return (size_t)kv->B * kv->Hh * kv->cap * kv->dh * esz(kv->dtype);
+}
+
+}  // namespace
+
+// =================================================================== C-ABI
+extern "C" {
+
+int wam_abi_version(void) { return WAM_ABI_VERSION; }
+
+const char* wam_status_str(int st) {
+  switch (st) {
+    case WAM_OK: return "ok";
+    case WAM_E_ARG: return "invalid argument";
+    case WAM_E_SHAPE: return "invalid or inconsistent shape";
+    case WAM_E_DTYPE: return "dtype mismatch";
+    case WAM_E_ALIGN: return "pointer not 16-byte aligned";
+    case WAM_E_WORKSPACE: return "workspace missing or too small";
+    case WAM_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* wam_last_error(void) { return g_err.c_str(); }
+
+int wam_schedule(int steps, double sigma_end, double shift, float* out) {
+  if (!out) return fail(WAM_E_ARG, "out is NULL");
+  if (steps < 1 || steps > 4096) return fail(WAM_E_ARG, "steps must be in [1, 4096]");
+  if (!(sigma_end >= 0.0 && sigma_end < 1.0)) return fail(WAM_E_ARG, "sigma_end must be in [0, 1)");
+  if (!(shift > 0.0)) return fail(WAM_E_ARG, "shift must be > 0");
+  schedule(steps, sigma_end, shift, out);
+  return WAM_OK;
+}
+
+int wam_frame_table(const int32_t* frame_block, const uint8_t* valid, int Fh, int Ff, int P,
+                    int32_t* src_frame, int32_t* kend) {
+  if (!frame_block || !src_frame || !kend) return fail(WAM_E_ARG, "NULL pointer");
+  if (Fh < 0 || Ff < 0 || Fh + Ff > WAM_MAX_FRAMES || P < 1)
+    return fail(WAM_E_SHAPE, "bad frame counts");
+  int st = check_blocks(frame_block, Fh + Ff);
+  if (st) return st;
+  return frame_table(frame_block, valid, Fh, Ff, P, src_frame, kend);
+}
+
+size_t wam_prefill_workspace_bytes(const wam_dims* d, int B, int Fh, int Ff) {
+  (void)B;
+  if (check_dims(d)) return 0;
+  Arena a(nullptr);
+  Bufs b;
+  float* z;
+  plan_prefill(a, d, Fh, Ff, b, &z);
+  return a.off + 256;
+}
+
+int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video, const void* hist,
+                            const uint8_t* hist_valid, int B, int Fh, const void* fut_noise,
+                            int Ff, const int32_t* frame_block, int video_steps,
+                            double sigma_star, double shift, wam_kv* cache,
+                            float* fut_latents_out, void* ws, size_t ws_bytes, void* stream) {
+  int st;
+  if ((st = check_dims(d))) return st;
+  if ((st = check_expert(d, video, "video"))) return st;
+  if (B < 1 || B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "B must be in [1, %d]", WAM_MAX_BATCH);
+  if (Fh < 0 || Ff < 0 || Fh + Ff < 1 || Fh + Ff > WAM_MAX_FRAMES)
+    return fail(WAM_E_SHAPE, "frame counts out of range");
+  if (Fh > 0 && !hist) return fail(WAM_E_ARG, "hist is NULL");
+  if (Ff > 0 && !fut_noise) return fail(WAM_E_ARG, "fut_noise is NULL");
+  if ((hist && !aligned16(hist)) || (fut_noise && !aligned16(fut_noise)) ||
+      (fut_latents_out && !aligned16(fut_latents_out)))
+    return fail(WAM_E_ALIGN, "input pointer not 16-byte aligned");
+  if (!frame_block) return fail(WAM_E_ARG, "frame_block is NULL");
+  if ((st = check_blocks(frame_block, Fh + Ff))) return st;
+  if (video_steps < 0 || video_steps > WAM_MAX_STEPS)
+    return fail(WAM_E_ARG, "video_steps must be in [0, %d]", WAM_MAX_STEPS);
+  if (video_steps > 0 && !(sigma_star > 0.0 && sigma_star < 1.0))
+    return fail(WAM_E_ARG, "sigma_star must be in (0, 1)");
+  if (!(shift > 0.0)) return fail(WAM_E_ARG, "shift must be > 0");
+  if (!cache) return fail(WAM_E_ARG, "cache is NULL");
+  if ((st = check_kv(d, cache, B, "cache"))) return st;
+  if (cache->n_layers != d->L) return fail(WAM_E_SHAPE, "cache must hold L layers");
+  if (!ws || !aligned16(ws)) return fail(WAM_E_WORKSPACE, "workspace NULL or unaligned");
+  if (ws_bytes < wam_prefill_workspace_bytes(d, B, Fh, Ff))
+    return fail(WAM_E_WORKSPACE, "workspace too small (%zu < %zu)", ws_bytes,
+                wam_prefill_workspace_bytes(d, B, Fh, Ff));
+
+  // frame tables of every episode, validated before anything is enqueued
+  const int P = d->P;
+  std::vector<FrameTab> tabs(B);
+  std::vector<RowMap> hmaps(B);
+  std::vector<int> nh(B);
+  for (int b = 0; b < B; b++) {
+    int src[WAM_MAX_FRAMES], kend[WAM_MAX_FRAMES];
+    const uint8_t* v = hist_valid ? hist_valid + (size_t)b * Fh : nullptr;
+    int n = frame_table(frame_block, v, Fh, Ff, P, src, kend);
+    if (n == 0) return fail(WAM_E_SHAPE, "episode %d has no valid frame", b);
+    if ((long long)n * P > cache->cap)
+      return fail(WAM_E_SHAPE, "episode %d needs %d cache rows, cap is %d", b, n * P, cache->cap);
+    tabs[b].n = n;
+    tabs[b].P = P;
+    for (int i = 0; i < n; i++) tabs[b].kend[i] = kend[i];
+    nh[b] = n - Ff;
+    hmaps[b].n = nh[b];
+    hmaps[b].P = P;
+    for (int i = 0; i < nh[b]; i++) hmaps[b].src[i] = b * Fh + src[i];
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  Arena a(ws);
+  Bufs bufs;
+  float* z;
+  plan_prefill(a, d, Fh, Ff, bufs, &z);
+  HIPCK(fill_i32(s, bufs.gs.counters, N_COUNTERS, 0));
+
+  // time embeddings: [0 (history), sigma_0 .. sigma_V (V >= 1) | 1 (V = 0)]
+  std::vector<float> sig(video_steps + 1);
+  if (video_steps > 0) schedule(video_steps, sigma_star, shift, sig.data());
+  std::vector<float> embs;
+  embs.push_back(0.f);
+  if (video_steps > 0)
+    for (int k = 0; k <= video_steps; k++) embs.push_back(sig[k]);
+  else
+    embs.push_back(1.f);
+  const int D = d->D;
+  HIPCK(time_embedding(s, embs.data(), (int)embs.size(), D, bufs.emb));
+  const float* emb_hist = bufs.emb;
+  const float* emb_last = bufs.emb + (size_t)(embs.size() - 1) * D;
+
+  const int dt = d->dtype;
+  const size_t ls = layer_stride(cache);
+  const size_t ep = (size_t)d->Hh * cache->cap * d->dh * esz(dt);  // one episode in a layer
+  Layer c{s, d, &bufs};
+  const int Tf = Ff * P;
+  RowMap zmap;
+  zmap.n = 1;
+  zmap.P = Tf;
+  zmap.src[0] = 0;
+
+  for (int b = 0; b < B; b++) {
+    const int Th = nh[b] * P;
+    auto kl = [&](int l) { return (char*)cache->k + l * ls + b * ep; };
+    auto vl = [&](int l) { return (char*)cache->v + l * ls + b * ep; };
+    if (Th > 0) {
+      HIPCK(embed(s, dt, dt, hist, hmaps[b], video->w_in, emb_hist, bufs.X, Th, D, d->Cv));
+      for (int l = 0; l < d->L; l++)
+        if ((st = video_layer(c, video->layers[l], Th, 0, tabs[b], kl(l), vl(l), cache->cap,
+                              l == d->L - 1)))
+          return st;
+    }
+    if (Ff > 0) {
+      HIPCK(copy_cvt_f32(s, dt, (const char*)fut_noise + (size_t)b * Tf * d->Cv * esz(dt), z,
+                         (int64_t)Tf * d->Cv));
+      for (int k = 0; k < video_steps; k++) {
+        HIPCK(embed(s, WAM_F32, dt, z, zmap, video->w_in, bufs.emb + (size_t)(1 + k) * D, bufs.X,
+                    Tf, D, d->Cv));
+        for (int l = 0; l < d->L; l++)
+          if ((st = video_layer(c, video->layers[l], Tf, Th, tabs[b], kl(l), vl(l), cache->cap,
+                                false)))
+            return st;
+        if ((st = head_euler(c, video, Tf, d->Cv, z, sig[k + 1] - sig[k], nullptr))) return st;
+      }
+      HIPCK(embed(s, WAM_F32, dt, z, zmap, video->w_in, emb_last, bufs.X, Tf, D, d->Cv));
+      for (int l = 0; l < d->L; l++)
+        if ((st = video_layer(c, video->layers[l], Tf, Th, tabs[b], kl(l), vl(l), cache->cap,
+                              l == d->L - 1)))
+          return st;
+      if (fut_latents_out)
+        HIPCK(hipMemcpyAsync(fut_latents_out + (size_t)b * Tf * d->Cv, z,
+                             (size_t)Tf * d->Cv * 4, hipMemcpyDeviceToDevice, s));
+    }
+    cache->len[b] = tabs[b].n * P;
+  }
+  return WAM_OK;
+}
+
+int wam_fuse_interval_kv(const wam_kv* src, int M, const int32_t* start, const int32_t* count,
+                         const float* logits, int logits_stride, wam_kv* dst, void* stream) {
+  if (!src || !dst || !start || !count || !logits) return fail(WAM_E_ARG, "NULL pointer");
+  if (!src->k || !src->v || !dst->k || !dst->v || !src->len || !dst->len)
+    return fail(WAM_E_ARG, "NULL cache pointer");
+  if (!aligned16(src->k) || !aligned16(src->v) || !aligned16(dst->k) || !aligned16(dst->v))
+    return fail(WAM_E_ALIGN, "cache not 16-byte aligned");
+  if (src->dtype != dst->dtype) return fail(WAM_E_DTYPE, "src and dst dtypes differ");
+  if (src->dtype != WAM_F32 && src->dtype != WAM_BF16) return fail(WAM_E_ARG, "bad dtype");
+  if (src->B != dst->B || src->Hh != dst->Hh || src->dh != dst->dh || src->cap != dst->cap)
+    return fail(WAM_E_SHAPE, "src and dst shapes differ");
+  if (src->B < 1 || src->B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "bad B");
+  if (M < 1 || M > WAM_MAX_FUSE || dst->n_layers < M)
+    return fail(WAM_E_SHAPE, "M must be in [1, %d] and fit dst", WAM_MAX_FUSE);
+  if (logits_stride < 1) return fail(WAM_E_ARG, "logits_stride must be >= 1");
+  FuseArgs fa;
+  fa.M = M;
+  for (int m = 0; m < M; m++) {
+    if (count[m] < 1 || count[m] > WAM_MAX_INTERVAL || count[m] > logits_stride)
+      return fail(WAM_E_SHAPE, "interval %d has %d layers", m, count[m]);
+    if (start[m] < 0 || start[m] + count[m] > src->n_layers)
+      return fail(WAM_E_SHAPE, "interval %d outside the source layers", m);
+    const float* lg = logits + (size_t)m * logits_stride;
+    double mx = -INFINITY;
+    for (int j = 0; j < count[m]; j++) mx = std::max(mx, (double)lg[j]);
+    if (!(mx > -INFINITY) || std::isnan(mx)) return fail(WAM_E_ARG, "interval %d logits are all -inf or NaN", m);
+    double e[WAM_MAX_INTERVAL], sum = 0.0;
+    for (int j = 0; j < count[m]; j++) {
+      e[j] = exp((double)lg[j] - mx);
+      sum += e[j];
+    }
+    fa.start[m] = start[m];
+    fa.count[m] = count[m];
+    for (int j = 0; j < count[m]; j++) fa.w[m][j] = (float)(e[j] / sum);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const long long le = (long long)src->B * src->Hh * src->cap * src->dh;
+  HIPCK(fuse_kv(s, src->dtype, src->k, dst->k, le, fa));
+  HIPCK(fuse_kv(s, src->dtype, src->v, dst->v, le, fa));
+  for (int b = 0; b < src->B; b++) dst->len[b] = src->len[b];
+  return WAM_OK;
+}
+
+static int max_len_of(const wam_kv* kv, int B) {
+  int m = 0;
+  if (kv)
+    for (int b = 0; b < B; b++) m = std::max(m, (int)kv->len[b]);
+  return m;
+}
+
+size_t wam_action_workspace_bytes(const wam_dims* d, int B, const wam_kv* kv) {
+  if (check_dims(d) || B < 1 || B > WAM_MAX_BATCH) return 0;
+  Arena a(nullptr);
+  Bufs b;
+  plan_action(a, d, B, kv ? std::max(max_len_of(kv, B), kv->cap) : 0, false, b);
+  return a.off + 256;
+}
+
+size_t wam_denoise_workspace_bytes(const wam_dims* d, int B, const wam_kv* kv) {
+  if (check_dims(d) || B < 1 || B > WAM_MAX_BATCH) return 0;
+  Arena a(nullptr);
+  Bufs b;
+  plan_action(a, d, B, kv ? std::max(max_len_of(kv, B), kv->cap) : 0, true, b);
+  return a.off + 256;
+}
+
+static int check_lens(const wam_kv* kv, int B, ActLens* lens) {
+  for (int b = 0; b < B; b++) {
+    if (kv->len[b] < 0 || kv->len[b] > kv->cap)
+      return fail(WAM_E_SHAPE, "len[%d] = %d outside [0, cap]", b, kv->len[b]);
+    lens->len[b] = kv->len[b];
+  }
+  return WAM_OK;
+}
+
+int wam_action_layer(const wam_dims* d, const wam_layer_w* w, float* x, const wam_kv* kv,
+                     int kv_layer, int B, void* ws, size_t ws_bytes, void* stream) {
+  int st;
+  if ((st = check_dims(d))) return st;
+  if (!w || !x) return fail(WAM_E_ARG, "NULL pointer");
+  if (!w->g1 || !w->wqkv || !w->wo || !w->g2 || !w->w1 || !w->w2)
+    return fail(WAM_E_ARG, "layer has a NULL pointer");
+  if (!aligned16(x)) return fail(WAM_E_ALIGN, "x not 16-byte aligned");
+  if (B < 1 || B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "bad B");
+  ActLens lens{};
+  if (kv) {
+    if ((st = check_kv(d, kv, B, "kv"))) return st;
+    if (kv_layer < 0 || kv_layer >= kv->n_layers) return fail(WAM_E_ARG, "kv_layer out of range");
+    if ((st = check_lens(kv, B, &lens))) return st;
+  }
+  if (!ws || !aligned16(ws) || ws_bytes < wam_action_workspace_bytes(d, B, kv))
+    return fail(WAM_E_WORKSPACE, "workspace missing or too small");
+  hipStream_t s = (hipStream_t)stream;
+  Arena a(ws);
+  Bufs b;
+  plan_action(a, d, B, kv ? std::max(max_len_of(kv, B), kv->cap) : 0, false, b);
+  HIPCK(fill_i32(s, b.gs.counters, N_COUNTERS, 0));
+  const size_t bytes = (size_t)B * d->H * d->D * 4;
+  HIPCK(hipMemcpyAsync(b.X, x, bytes, hipMemcpyDeviceToDevice, s));
+  Layer c{s, d, &b};
+  const void* kc = kv ? (const char*)kv->k + kv_layer * layer_stride(kv) : nullptr;
+  const void* vc = kv ? (const char*)kv->v + kv_layer * layer_stride(kv) : nullptr;
+  if ((st = action_layer(c, *w, B, kc, vc, kv ? kv->cap : 0, lens))) return st;
+  HIPCK(hipMemcpyAsync(x, b.X, bytes, hipMemcpyDeviceToDevice, s));
+  return WAM_OK;
+}
+
+int wam_flow_euler_step(float* x, const float* v, int64_t n, float sigma, float sigma_next,
+                        void* stream) {
+  if (n < 0) return fail(WAM_E_ARG, "n < 0");
+  if (n == 0) return WAM_OK;
+  if (!x || !v) return fail(WAM_E_ARG, "NULL pointer");
+  HIPCK(euler((hipStream_t)stream, x, v, n, sigma_next - sigma));
+  return WAM_OK;
+}
+
+int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_kv* kv,
+                      const int32_t* read_map, const float* eps, int B, int N, double shift,
+                      float* actions_out, float* vhat_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int st;
+  if ((st = check_dims(d))) return st;
+  if ((st = check_expert(d, action, "action"))) return st;
+  if (!read_map || !eps || !actions_out) return fail(WAM_E_ARG, "NULL pointer");
+  if (!aligned16(eps) || !aligned16(actions_out) || (vhat_out && !aligned16(vhat_out)))
+    return fail(WAM_E_ALIGN, "pointer not 16-byte aligned");
+  if (B < 1 || B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "bad B");
+  if (N < 1 || N > WAM_MAX_STEPS) return fail(WAM_E_ARG, "N must be in [1, %d]", WAM_MAX_STEPS);
+  if (!(shift > 0.0)) return fail(WAM_E_ARG, "shift must be > 0");
+  ActLens lens{};
+  bool any = false;
+  for (int l = 0; l < d->L; l++) any |= read_map[l] >= 0;
+  if (any) {
+    if (!kv) return fail(WAM_E_ARG, "read_map reads a cache but kv is NULL");
+    if ((st = check_kv(d, kv, B, "kv"))) return st;
+    if ((st = check_lens(kv, B, &lens))) return st;
+    for (int l = 0; l < d->L; l++)
+      if (read_map[l] >= kv->n_layers) return fail(WAM_E_ARG, "read_map[%d] out of range", l);
+  }
+  if (!ws || !aligned16(ws) || ws_bytes < wam_denoise_workspace_bytes(d, B, any ? kv : nullptr))
+    return fail(WAM_E_WORKSPACE, "workspace missing or too small");
+
+  hipStream_t s = (hipStream_t)stream;
+  Arena a(ws);
+  Bufs b;
+  plan_action(a, d, B, any ? std::max(max_len_of(kv, B), kv->cap) : 0, true, b);
+  HIPCK(fill_i32(s, b.gs.counters, N_COUNTERS, 0));
+  std::vector<float> t(N + 1);
+  schedule(N, 0.0, shift, t.data());
+  HIPCK(time_embedding(s, t.data(), N, d->D, b.emb));
+  const int M = B * d->H;
+  HIPCK(hipMemcpyAsync(actions_out, eps, (size_t)M * d->A * 4, hipMemcpyDeviceToDevice, s));
+  RowMap amap;
+  amap.n = 1;
+  amap.P = M;
+  amap.src[0] = 0;
+  Layer c{s, d, &b};
+  const size_t ls = any ? layer_stride(kv) : 0;
+  for (int k = 0; k < N; k++) {
+    HIPCK(embed(s, WAM_F32, d->dtype, actions_out, amap, action->w_in, b.emb + (size_t)k * d->D,
+                b.X, M, d->D, d->A));
+    for (int l = 0; l < d->L; l++) {
+      const int r = read_map[l];
+      const void* kc = r >= 0 ? (const char*)kv->k + r * ls : nullptr;
+      const void* vc = r >= 0 ? (const char*)kv->v + r * ls : nullptr;
+      if ((st = action_layer(c, action->layers[l], B, kc, vc, r >= 0 ? kv->cap : 0, lens))) return st;
+    }
+    if ((st = head_euler(c, action, M, d->A, actions_out, t[k + 1] - t[k],
+                         vhat_out ? vhat_out + (size_t)k * M * d->A : nullptr)))
+      return st;
+  }
+  return WAM_OK;
+}
+
+int wam_debug_visibility(const int32_t* frame_block, const uint8_t* valid, int Fh, int Ff, int P,
+                         uint8_t* vis, void* stream) {
+  if (!frame_block || !vis) return fail(WAM_E_ARG, "NULL pointer");
+  if (Fh < 0 || Ff < 0 || Fh + Ff < 1 || Fh + Ff > WAM_MAX_FRAMES || P < 1)
+    return fail(WAM_E_SHAPE, "bad frame counts");
+  int st;
+  if ((st = check_blocks(frame_block, Fh + Ff))) return st;
+  int src[WAM_MAX_FRAMES], kend[WAM_MAX_FRAMES];
+  int n = frame_table(frame_block, valid, Fh, Ff, P, src, kend);
+  FrameTab tab;
+  tab.n = n;
+  tab.P = P;
+  for (int i = 0; i < n; i++) tab.kend[i] = kend[i];
+  int comp[WAM_MAX_FRAMES];
+  for (int f = 0; f < Fh + Ff; f++) comp[f] = -1;
+  for (int i = 0; i < n; i++) comp[src[i]] = i;
+  HIPCK(debug_visibility((hipStream_t)stream, tab, comp, Fh + Ff, vis));
+  return WAM_OK;
+}
+
+int wam_attention_action(int dtype, int B, int Hh, int dh, int H, const void* q, const void* ka,
+                         const void* va, int n_act, const void* kc, const void* vc, int cap,
+                         const int32_t* len, void* out, int splits_hint, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (dtype != WAM_F32 && dtype != WAM_BF16) return fail(WAM_E_ARG, "bad dtype");
+  if (dh != 64 || H != 32) return fail(WAM_E_SHAPE, "dh must be 64 and H 32");
+  if (B < 1 || B > WAM_MAX_BATCH || Hh < 1) return fail(WAM_E_SHAPE, "bad B or Hh");
+  if (!q || !out) return fail(WAM_E_ARG, "NULL pointer");
+  if (n_act < 0 || n_act > H || (n_act > 0 && (!ka || !va)))
+    return fail(WAM_E_ARG, "bad own keys");
+  if ((kc == nullptr) != (vc == nullptr)) return fail(WAM_E_ARG, "kc and vc must both be set");
+  ActLens lens{};
+  int max_len = 0;
+  if (kc) {
+    if (!len) return fail(WAM_E_ARG, "len is NULL");
+    if (cap < 64 || cap % 64) return fail(WAM_E_SHAPE, "cap must be a multiple of 64");
+    for (int b = 0; b < B; b++) {
+      if (len[b] < 0 || len[b] > cap) return fail(WAM_E_SHAPE, "len out of range");
+      lens.len[b] = len[b];
+      max_len = std::max(max_len, (int)len[b]);
+    }
+  }
+  for (int b = 0; b < B; b++)
+    if ((kc ? lens.len[b] : 0) + n_act == 0) return fail(WAM_E_SHAPE, "episode %d has no key", b);
+  const void* ptrs[] = {q, ka, va, kc, vc, out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(WAM_E_ALIGN, "pointer not 16-byte aligned");
+  size_t need = dtype == WAM_BF16 ? attn_action_scratch_bytes(B, Hh, H, max_len, splits_hint) : 0;
+  if (need && (!ws || ws_bytes < need)) return fail(WAM_E_WORKSPACE, "workspace too small (%zu)", need);
+  HIPCK(attn_action((hipStream_t)stream, dtype, B, Hh, H, q, ka, va, n_act, kc, vc, cap, lens, out,
+                    splits_hint, ws, ws_bytes));
+  return WAM_OK;
+}
+
+int wam_attention_prefill(int dtype, int Hh, int dh, int nq, int row0, int P, const int32_t* kend,
+                          int n_frames, const void* q, const void* kc, const void* vc, int cap,
+                          void* out, void* stream) {
+  if (dtype != WAM_F32 && dtype != WAM_BF16) return fail(WAM_E_ARG, "bad dtype");
+  if (dh != 64 || Hh < 1 || nq < 0 || row0 < 0 || P < 1) return fail(WAM_E_SHAPE, "bad shape");
+  if (!kend || !q || !kc || !vc || !out) return fail(WAM_E_ARG, "NULL pointer");
+  if (n_frames < 1 || n_frames > WAM_MAX_FRAMES) return fail(WAM_E_SHAPE, "bad n_frames");
+  if (cap < 64 || cap % 64) return fail(WAM_E_SHAPE, "cap must be a multiple of 64");
+  if ((row0 + nq + P - 1) / P > n_frames) return fail(WAM_E_SHAPE, "query rows beyond the frame table");
+  FrameTab tab;
+  tab.n = n_frames;
+  tab.P = P;
+  for (int i = 0; i < n_frames; i++) {
+    if (kend[i] < 1 || kend[i] > cap || (i && kend[i] < kend[i - 1]))
+      return fail(WAM_E_SHAPE, "kend must be non-decreasing in [1, cap]");
+    tab.kend[i] = kend[i];
+  }
+  const void* ptrs[] = {q, kc, vc, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(WAM_E_ALIGN, "pointer not 16-byte aligned");
+  HIPCK(attn_prefill((hipStream_t)stream, dtype, Hh, nq, row0, tab, q, kc, vc, cap, out));
+  return WAM_OK;
+}
+
+}  // extern "C"

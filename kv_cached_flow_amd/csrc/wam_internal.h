@@ -1,0 +1,169 @@
+// Internal declarations of libwam: device helpers, kernel-argument structs
+// and the launchers the C-ABI layer calls.  gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/wam.h"
+
+namespace wam {
+
+typedef uint16_t bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+
+// ---------------------------------------------------------------- bf16
+__host__ __device__ inline float bf2f(bf16_t h) {
+  union { uint32_t u; float f; } x;
+  x.u = (uint32_t)h << 16;
+  return x.f;
+}
+
+// Round to nearest even; NaN stays NaN.
+__host__ __device__ inline bf16_t f2bf(float f) {
+  union { uint32_t u; float f; } x;
+  x.f = f;
+  uint32_t u = x.u;
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ inline float to_f(T v);
+template <> __device__ inline float to_f<float>(float v) { return v; }
+template <> __device__ inline float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+
+template <typename T> __device__ inline T from_f(float v);
+template <> __device__ inline float from_f<float>(float v) { return v; }
+template <> __device__ inline bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+__device__ inline float gelu_f(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
+// ---------------------------------------------------------------- block table
+// Compacted frames of one episode: tokens of compacted frame i occupy cache
+// rows [i*P, (i+1)*P); a query in compacted frame i sees rows [0, kend[i]).
+struct FrameTab {
+  int n;
+  int P;
+  int kend[WAM_MAX_FRAMES];
+};
+
+// The one visibility predicate of the block-causal attention (query cache
+// row qr sees key cache row kr).  Used by the attention kernels and the
+// debug export.
+__device__ inline int kend_of_row(const FrameTab& t, int qr) { return t.kend[qr / t.P]; }
+__device__ inline bool visible(const FrameTab& t, int qr, int kr) { return kr < kend_of_row(t, qr); }
+
+// ---------------------------------------------------------------- GEMM epilogues
+enum EpiKind {
+  EPI_STORE = 0,   // out[m*ldo + n] = v                    (out type TO)
+  EPI_GELU = 1,    // out[m*ldo + n] = GELU(v)              (out type TO)
+  EPI_RESID = 2,   // X[m*ldo + n] += v                     (fp32)
+  EPI_QKV = 3,     // scatter to Q / K cache / V^T cache    (out type TO)
+  EPI_EULER = 4    // z[m*ldo + n] += dt*v; vhat[m*ldo+n] = v (fp32)
+};
+
+struct EpiArgs {
+  void* out;      // STORE/GELU/RESID/EULER destination
+  int ldo;
+  float dt;       // EULER
+  float* vhat;    // EULER, nullable
+  // QKV: column n_begin + n of [Q | K | V] (each D wide), row m -> group g = m / rpg, t = m % rpg
+  void* q;
+  void* k;
+  void* v;
+  int D, dh, rpg, n_begin;
+  long long q_gs, q_hs;          // q[g*q_gs + h*q_hs + t*dh + d]
+  long long k_gs, k_hs;          // k[g*k_gs + h*k_hs + (k_row0 + t)*dh + d]
+  long long v_gs, v_hs;          // v[g*v_gs + h*v_hs + d*v_ld + v_col0 + t]
+  int k_row0, v_ld, v_col0;
+};
+
+template <int EPI, typename TO>
+__device__ inline void epi_store(const EpiArgs& e, int m, int n, float v) {
+  if constexpr (EPI == EPI_STORE) {
+    ((TO*)e.out)[(long long)m * e.ldo + n] = from_f<TO>(v);
+  } else if constexpr (EPI == EPI_GELU) {
+    ((TO*)e.out)[(long long)m * e.ldo + n] = from_f<TO>(gelu_f(v));
+  } else if constexpr (EPI == EPI_RESID) {
+    ((float*)e.out)[(long long)m * e.ldo + n] += v;
+  } else if constexpr (EPI == EPI_EULER) {
+    long long i = (long long)m * e.ldo + n;
+    ((float*)e.out)[i] += e.dt * v;
+    if (e.vhat) e.vhat[i] = v;
+  } else {
+    int nn = e.n_begin + n;
+    int part = nn / e.D;
+    int c = nn - part * e.D;
+    int h = c / e.dh, d = c - h * e.dh;
+    int g = m / e.rpg, t = m - g * e.rpg;
+    if (part == 0)
+      ((TO*)e.q)[g * e.q_gs + h * e.q_hs + (long long)t * e.dh + d] = from_f<TO>(v);
+    else if (part == 1)
+      ((TO*)e.k)[g * e.k_gs + h * e.k_hs + (long long)(e.k_row0 + t) * e.dh + d] = from_f<TO>(v);
+    else
+      ((TO*)e.v)[g * e.v_gs + h * e.v_hs + (long long)d * e.v_ld + e.v_col0 + t] = from_f<TO>(v);
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+// C[M][N] = A[M][K] * B[N][K]^T with the epilogue; adt/bdt/odt are WAM_F32 or
+// WAM_BF16 (A, B and epilogue output element types).  part/cnt: split-K
+// scratch (may be null when the launcher does not need it).
+struct GemmScratch {
+  float* part;
+  size_t part_elems;
+  int* counters;
+  int n_counters;
+};
+hipError_t gemm(hipStream_t s, int adt, int bdt, int odt, int epi, int M, int N, int K,
+                const void* A, int lda, const void* B, int ldb, const EpiArgs& e,
+                const GemmScratch& scr);
+size_t gemm_scratch_elems(int M, int N, int K);
+
+hipError_t rmsnorm(hipStream_t s, int odt, const float* x, const float* g, void* y, int M, int D);
+
+// X[m][n] = sum_c x[row(m)][c] * w_in[n][c] + emb[n]; rows are gathered by
+// frame: m -> frame src[m / P], token m % P, of a [*][P][C] input.
+struct RowMap {
+  int n;
+  int P;
+  int src[WAM_MAX_FRAMES];
+};
+hipError_t embed(hipStream_t s, int xdt, int wdt, const void* x, const RowMap& map,
+                 const void* w_in, const float* emb, float* X, int M, int D, int C);
+
+// emb[i][0..D) for sigma[i], i < n (float64 on the device, stored fp32).
+hipError_t time_embedding(hipStream_t s, const float* sigma_host, int n, int D, float* emb);
+
+hipError_t euler(hipStream_t s, float* x, const float* v, int64_t n, float dt);
+hipError_t copy_cvt_f32(hipStream_t s, int sdt, const void* src, float* dst, int64_t n);
+
+struct FuseArgs {
+  int M;
+  int count[WAM_MAX_FUSE];
+  int start[WAM_MAX_FUSE];
+  float w[WAM_MAX_FUSE][WAM_MAX_INTERVAL];
+};
+hipError_t fuse_kv(hipStream_t s, int dt, const void* src, void* dst, long long layer_elems,
+                   const FuseArgs& a);
+
+hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int nq, int row0, const FrameTab& tab,
+                        const void* q, const void* kc, const void* vc, int cap, void* out);
+
+struct ActLens {
+  int len[WAM_MAX_BATCH];
+};
+size_t attn_action_scratch_bytes(int B, int Hh, int H, int max_len, int splits_hint);
+hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* q,
+                       const void* ka, const void* va, int n_act, const void* kc,
+                       const void* vc, int cap, const ActLens& lens, void* out,
+                       int splits_hint, void* scratch, size_t scratch_bytes);
+
+hipError_t debug_visibility(hipStream_t s, const FrameTab& tab, const int* comp_of_frame,
+                            int F, uint8_t* vis);
+hipError_t fill_i32(hipStream_t s, int* p, int n, int v);
+
+}  // namespace wam

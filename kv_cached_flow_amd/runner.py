@@ -1,0 +1,89 @@
+"""One action chunk on the GPU: upload the seeded inputs once, then sequence
+the C calls (prefill -> optional interval fusion -> N-step denoise).  No
+arithmetic of the method here: every step runs in libwam's kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import wam
+from .configs import WamConfig
+
+
+def _tdt(cfg: WamConfig):
+    import torch
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def upload_expert(w: dict, cfg: WamConfig, device="cuda") -> wam.DeviceExpert:
+    import torch
+    mat = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device).to(_tdt(cfg)).contiguous()
+    vec = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    layers = [{"g1": vec(l["g1"]), "wqkv": mat(l["wqkv"]), "wo": mat(l["wo"]), "g2": vec(l["g2"]),
+               "w1": mat(l["w1"]), "w2": mat(l["w2"])} for l in w["layers"]]
+    return wam.DeviceExpert(mat(w["w_in"]), vec(w["g_out"]), mat(w["w_out"]), layers)
+
+
+def cache_rows(cfg: WamConfig, hist_valid: np.ndarray) -> int:
+    """Cache capacity (multiple of 64) for the valid frames of every episode."""
+    n = int(hist_valid.sum(axis=1).max()) + cfg.Ff
+    return ((n * cfg.P + 63) // 64) * 64
+
+
+class DeviceChunk:
+    """Device-resident inputs, outputs and workspaces of one chunk."""
+
+    def __init__(self, cfg: WamConfig, inp: dict, device="cuda"):
+        import torch
+        self.cfg = cfg
+        self.dt = wam.WAM_BF16 if cfg.dtype == "bf16" else wam.WAM_F32
+        self.dims = wam.dims(cfg.L, cfg.D, cfg.Hh, cfg.dh, cfg.Fm, cfg.Cv, cfg.A, cfg.H, cfg.P, self.dt)
+        tdt = _tdt(cfg)
+        self.video = upload_expert(inp["video"], cfg, device)
+        self.action = upload_expert(inp["action"], cfg, device)
+        self.hist = torch.from_numpy(inp["hist"]).to(device).to(tdt).contiguous()
+        self.fut = torch.from_numpy(inp["eps_v"]).to(device).to(tdt).contiguous()
+        self.eps_a = torch.from_numpy(inp["eps_a"]).to(device).contiguous()
+        self.hist_valid = np.ascontiguousarray(inp["hist_valid"], dtype=np.uint8)
+        self.logits = inp["fuse_logits"]
+        cap = cache_rows(cfg, self.hist_valid)
+        self.cache = wam.DeviceKV(cfg.L, cfg.B, cfg.Hh, cfg.dh, cap, self.dt, device)
+        self.fused = (wam.DeviceKV(len(cfg.fuse), cfg.B, cfg.Hh, cfg.dh, cap, self.dt, device)
+                      if cfg.fuse else None)
+        self.z = torch.zeros((cfg.B, cfg.Ff, cfg.P, cfg.Cv), dtype=torch.float32, device=device)
+        self.actions = torch.zeros((cfg.B, cfg.H, cfg.A), dtype=torch.float32, device=device)
+        self.vhat = torch.zeros((cfg.N, cfg.B, cfg.H, cfg.A), dtype=torch.float32, device=device)
+        self.ws_prefill = wam.workspace(wam.prefill_workspace_bytes(self.dims, cfg.B, cfg.Fh, cfg.Ff), device)
+        kv = self.fused if self.fused is not None else self.cache
+        kv.len[:] = cap  # size the workspace for a full cache
+        self.ws_denoise = wam.workspace(wam.denoise_workspace_bytes(self.dims, cfg.B, kv), device)
+
+    @property
+    def read_kv(self) -> wam.DeviceKV:
+        return self.fused if self.fused is not None else self.cache
+
+    def prefill(self, stream=None):
+        c = self.cfg
+        wam.prefill_video_cache(self.dims, self.video, self.hist, self.hist_valid, c.B, c.Fh, self.fut,
+                                c.Ff, c.frame_block, c.V, c.sigma_star, c.shift, self.cache, self.z,
+                                self.ws_prefill, stream)
+
+    def fuse(self, stream=None):
+        c = self.cfg
+        if c.fuse:
+            wam.fuse_interval_kv(self.cache, [s for s, _ in c.fuse], [n for _, n in c.fuse],
+                                 self.logits, self.fused, stream)
+
+    def denoise(self, stream=None):
+        c = self.cfg
+        wam.denoise_chunk(self.dims, self.action, self.read_kv, c.read_map, self.eps_a, c.B, c.N,
+                          c.shift, self.actions, self.vhat, self.ws_denoise, stream)
+
+    def run(self, stream=None):
+        """One whole chunk: prefill, fuse (SparseMoT), N action steps."""
+        self.prefill(stream)
+        self.fuse(stream)
+        self.denoise(stream)
+        return self.actions

@@ -1,0 +1,274 @@
+"""Python binding of libwam (ctypes).  Argument marshalling only: every step
+of the hot path runs in the library's HIP kernels.  Tensors are PyTorch
+device tensors (memory and streams only).  The names follow the C calls in
+``include/wam.h``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwam.so")
+
+WAM_F32, WAM_BF16 = 0, 1
+WAM_MAX_FRAMES = 256
+
+_lib = None
+
+
+class WamError(RuntimeError):
+    pass
+
+
+class WamDims(C.Structure):
+    _fields_ = [(n, C.c_int) for n in ("L", "D", "Hh", "dh", "Fm", "Cv", "A", "H", "P", "dtype")]
+
+
+class WamLayerW(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("g1", "wqkv", "wo", "g2", "w1", "w2")]
+
+
+class WamExpertW(C.Structure):
+    _fields_ = [("w_in", C.c_void_p), ("g_out", C.c_void_p), ("w_out", C.c_void_p),
+                ("layers", C.POINTER(WamLayerW)), ("n_layers", C.c_int)]
+
+
+class WamKV(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("n_layers", C.c_int), ("B", C.c_int),
+                ("Hh", C.c_int), ("dh", C.c_int), ("cap", C.c_int), ("dtype", C.c_int),
+                ("len", C.POINTER(C.c_int32))]
+
+
+_EXPORTS = {
+    "wam_abi_version": (C.c_int, []),
+    "wam_status_str": (C.c_char_p, [C.c_int]),
+    "wam_last_error": (C.c_char_p, []),
+    "wam_schedule": (C.c_int, [C.c_int, C.c_double, C.c_double, C.c_void_p]),
+    "wam_frame_table": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]),
+    "wam_prefill_workspace_bytes": (C.c_size_t, [C.POINTER(WamDims), C.c_int, C.c_int, C.c_int]),
+    "wam_prefill_video_cache": (C.c_int, [C.POINTER(WamDims), C.POINTER(WamExpertW), C.c_void_p, C.c_void_p,
+                                          C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p, C.c_int,
+                                          C.c_double, C.c_double, C.POINTER(WamKV), C.c_void_p,
+                                          C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wam_fuse_interval_kv": (C.c_int, [C.POINTER(WamKV), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                                       C.c_int, C.POINTER(WamKV), C.c_void_p]),
+    "wam_action_workspace_bytes": (C.c_size_t, [C.POINTER(WamDims), C.c_int, C.POINTER(WamKV)]),
+    "wam_action_layer": (C.c_int, [C.POINTER(WamDims), C.POINTER(WamLayerW), C.c_void_p,
+                                   C.POINTER(WamKV), C.c_int, C.c_int, C.c_void_p, C.c_size_t,
+                                   C.c_void_p]),
+    "wam_flow_euler_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_float, C.c_float,
+                                      C.c_void_p]),
+    "wam_denoise_workspace_bytes": (C.c_size_t, [C.POINTER(WamDims), C.c_int, C.POINTER(WamKV)]),
+    "wam_denoise_chunk": (C.c_int, [C.POINTER(WamDims), C.POINTER(WamExpertW), C.POINTER(WamKV),
+                                    C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_double, C.c_void_p,
+                                    C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wam_debug_visibility": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p,
+                                       C.c_void_p]),
+    "wam_attention_action": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p,
+                                       C.c_void_p, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
+                                       C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_void_p,
+                                       C.c_size_t, C.c_void_p]),
+    "wam_attention_prefill": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+                                        C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                                        C.c_int, C.c_void_p, C.c_void_p]),
+}
+
+
+def lib():
+    """Load libwam.so (fails loudly when it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise WamError(f"{LIB_PATH} is missing: build it with `python -m kv_cached_flow_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _EXPORTS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_names() -> List[str]:
+    return list(_EXPORTS)
+
+
+def _check(st: int, what: str):
+    if st < 0:
+        L = lib()
+        raise WamError(f"{what}: {L.wam_status_str(st).decode()} ({st}): {L.wam_last_error().decode()}")
+    return st
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# ------------------------------------------------------------------ host-side calls
+def abi_version() -> int:
+    return lib().wam_abi_version()
+
+
+def schedule(steps: int, sigma_end: float, shift: float = 1.0) -> np.ndarray:
+    out = np.zeros(steps + 1, dtype=np.float32)
+    _check(lib().wam_schedule(steps, sigma_end, shift, out.ctypes.data), "wam_schedule")
+    return out
+
+
+def frame_table(frame_block: Sequence[int], valid: Optional[Sequence[int]], Fh: int, Ff: int, P: int):
+    fb = np.ascontiguousarray(frame_block, dtype=np.int32)
+    va = None if valid is None else np.ascontiguousarray(valid, dtype=np.uint8)
+    src = np.zeros(WAM_MAX_FRAMES, dtype=np.int32)
+    kend = np.zeros(WAM_MAX_FRAMES, dtype=np.int32)
+    n = _check(lib().wam_frame_table(fb.ctypes.data, None if va is None else va.ctypes.data,
+                                     Fh, Ff, P, src.ctypes.data, kend.ctypes.data), "wam_frame_table")
+    return src[:n].copy(), kend[:n].copy()
+
+
+# ------------------------------------------------------------------ device structs
+def dims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype) -> WamDims:
+    return WamDims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype)
+
+
+class DeviceExpert:
+    """An expert's weights as device tensors plus the C struct pointing at them."""
+
+    def __init__(self, w_in, g_out, w_out, layers: List[dict]):
+        self.w_in, self.g_out, self.w_out, self.layers = w_in, g_out, w_out, layers
+        n = len(layers)
+        self._larr = (WamLayerW * n)()
+        for i, lw in enumerate(layers):
+            self._larr[i] = WamLayerW(*[lw[k].data_ptr() for k in ("g1", "wqkv", "wo", "g2", "w1", "w2")])
+        self.c = WamExpertW(w_in.data_ptr(), g_out.data_ptr(), w_out.data_ptr(),
+                            C.cast(self._larr, C.POINTER(WamLayerW)), n)
+
+    def layer_struct(self, l: int) -> WamLayerW:
+        return self._larr[l]
+
+
+class DeviceKV:
+    """Per-layer K/V cache of B episodes: k [n][B][Hh][cap][dh], v [n][B][Hh][dh][cap]."""
+
+    def __init__(self, n_layers: int, B: int, Hh: int, dh: int, cap: int, dtype: int, device="cuda"):
+        import torch
+        if cap % 64:
+            raise WamError("cap must be a multiple of 64")
+        tdt = torch.bfloat16 if dtype == WAM_BF16 else torch.float32
+        self.k = torch.empty((n_layers, B, Hh, cap, dh), dtype=tdt, device=device)
+        self.v = torch.empty((n_layers, B, Hh, dh, cap), dtype=tdt, device=device)
+        self.len = np.zeros(B, dtype=np.int32)
+        self.c = WamKV(self.k.data_ptr(), self.v.data_ptr(), n_layers, B, Hh, dh, cap, dtype,
+                       self.len.ctypes.data_as(C.POINTER(C.c_int32)))
+
+    @property
+    def cap(self):
+        return self.c.cap
+
+
+def workspace(nbytes: int, device="cuda"):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ the C calls
+def prefill_workspace_bytes(d: WamDims, B: int, Fh: int, Ff: int) -> int:
+    return lib().wam_prefill_workspace_bytes(C.byref(d), B, Fh, Ff)
+
+
+def prefill_video_cache(d: WamDims, video: DeviceExpert, hist, hist_valid, B: int, Fh: int,
+                        fut_noise, Ff: int, frame_block, video_steps: int, sigma_star: float,
+                        shift: float, cache: DeviceKV, fut_latents_out=None, ws=None, stream=None):
+    hv = None if hist_valid is None else np.ascontiguousarray(hist_valid, dtype=np.uint8)
+    fb = np.ascontiguousarray(frame_block, dtype=np.int32)
+    if ws is None:
+        ws = workspace(prefill_workspace_bytes(d, B, Fh, Ff))
+    _check(lib().wam_prefill_video_cache(
+        C.byref(d), C.byref(video.c), _ptr(hist), None if hv is None else hv.ctypes.data, B, Fh,
+        _ptr(fut_noise), Ff, fb.ctypes.data, video_steps, sigma_star, shift, C.byref(cache.c),
+        _ptr(fut_latents_out), _ptr(ws), ws.numel(), _stream(stream)), "wam_prefill_video_cache")
+
+
+def fuse_interval_kv(src: DeviceKV, start, count, logits, dst: DeviceKV, stream=None):
+    st = np.ascontiguousarray(start, dtype=np.int32)
+    cn = np.ascontiguousarray(count, dtype=np.int32)
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    _check(lib().wam_fuse_interval_kv(C.byref(src.c), len(st), st.ctypes.data, cn.ctypes.data,
+                                      lg.ctypes.data, lg.shape[1], C.byref(dst.c), _stream(stream)),
+           "wam_fuse_interval_kv")
+
+
+def action_workspace_bytes(d: WamDims, B: int, kv: Optional[DeviceKV]) -> int:
+    return lib().wam_action_workspace_bytes(C.byref(d), B, C.byref(kv.c) if kv is not None else None)
+
+
+def action_layer(d: WamDims, expert: DeviceExpert, l: int, x, kv: Optional[DeviceKV], kv_layer: int,
+                 B: int, ws=None, stream=None):
+    if ws is None:
+        ws = workspace(action_workspace_bytes(d, B, kv))
+    lw = expert.layer_struct(l)
+    _check(lib().wam_action_layer(C.byref(d), C.byref(lw), _ptr(x),
+                                  C.byref(kv.c) if kv is not None else None, kv_layer, B, _ptr(ws),
+                                  ws.numel(), _stream(stream)), "wam_action_layer")
+
+
+def flow_euler_step(x, v, sigma: float, sigma_next: float, stream=None):
+    _check(lib().wam_flow_euler_step(_ptr(x), _ptr(v), x.numel(), sigma, sigma_next, _stream(stream)),
+           "wam_flow_euler_step")
+
+
+def denoise_workspace_bytes(d: WamDims, B: int, kv: Optional[DeviceKV]) -> int:
+    return lib().wam_denoise_workspace_bytes(C.byref(d), B, C.byref(kv.c) if kv is not None else None)
+
+
+def denoise_chunk(d: WamDims, action: DeviceExpert, kv: Optional[DeviceKV], read_map, eps, B: int,
+                  N: int, shift: float, actions_out, vhat_out=None, ws=None, stream=None):
+    rm = np.ascontiguousarray(read_map, dtype=np.int32)
+    if ws is None:
+        ws = workspace(denoise_workspace_bytes(d, B, kv))
+    _check(lib().wam_denoise_chunk(C.byref(d), C.byref(action.c), C.byref(kv.c) if kv is not None else None,
+                                   rm.ctypes.data, _ptr(eps), B, N, shift, _ptr(actions_out),
+                                   _ptr(vhat_out), _ptr(ws), ws.numel(), _stream(stream)),
+           "wam_denoise_chunk")
+
+
+def debug_visibility(frame_block, valid, Fh: int, Ff: int, P: int, stream=None):
+    import torch
+    fb = np.ascontiguousarray(frame_block, dtype=np.int32)
+    va = None if valid is None else np.ascontiguousarray(valid, dtype=np.uint8)
+    n = (Fh + Ff) * P
+    vis = torch.empty((n, n), dtype=torch.uint8, device="cuda")
+    _check(lib().wam_debug_visibility(fb.ctypes.data, None if va is None else va.ctypes.data, Fh, Ff,
+                                      P, _ptr(vis), _stream(stream)), "wam_debug_visibility")
+    return vis
+
+
+def attention_action(dtype: int, q, ka, va, n_act: int, kc, vc, cap: int, lens, out,
+                     splits_hint: int = 0, ws=None, stream=None):
+    B, Hh, H, dh = q.shape
+    ln = None if lens is None else np.ascontiguousarray(lens, dtype=np.int32)
+    if ws is None:
+        ws = workspace(64 << 20)
+    _check(lib().wam_attention_action(dtype, B, Hh, dh, H, _ptr(q), _ptr(ka), _ptr(va), n_act,
+                                      _ptr(kc), _ptr(vc), cap, None if ln is None else ln.ctypes.data,
+                                      _ptr(out), splits_hint, _ptr(ws), ws.numel(), _stream(stream)),
+           "wam_attention_action")
+
+
+def attention_prefill(dtype: int, q, row0: int, P: int, kend, kc, vc, cap: int, out, stream=None):
+    Hh, nq, dh = q.shape
+    ke = np.ascontiguousarray(kend, dtype=np.int32)
+    _check(lib().wam_attention_prefill(dtype, Hh, dh, nq, row0, P, ke.ctypes.data, len(ke), _ptr(q),
+                                       _ptr(kc), _ptr(vc), cap, _ptr(out), _stream(stream)),
+           "wam_attention_prefill")
