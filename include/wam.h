@@ -245,6 +245,21 @@ int wam_attention_prefill(int dtype, int Hh, int dh, int nq, int row0, int P,
                           const int32_t* kend, int n_frames, const void* q,
                           const void* kc, const void* vc, int cap, void* out, void* stream);
 
+/* Measurement: per-kernel-class durations from HIP events recorded around
+ * every launch while timing is on (wam_timing(1) also clears earlier
+ * records), with the algorithmic bytes and flops of those launches.
+ * wam_timing_report waits for the recorded events and returns the number of
+ * classes written to out (at most max). */
+typedef struct {
+  char name[32];
+  int launches;
+  double ms;     /* sum of launch durations */
+  double bytes;  /* algorithmic HBM bytes of those launches */
+  double flops;  /* algorithmic flops of those launches */
+} wam_kernel_stat;
+int wam_timing(int enable);
+int wam_timing_report(wam_kernel_stat* out, int max);
+
 #ifdef __cplusplus
 }
 #endif

@@ -257,6 +257,16 @@ __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(const float* __res
 hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int nq, int row0, const FrameTab& tab,
                         const void* q, const void* kc, const void* vc, int cap, void* out) {
   if (nq <= 0) return hipSuccess;
+  double pairs = 0.0;  // visible (query, key) pairs
+  for (int r = row0; r < row0 + nq;) {
+    int f = r / tab.P, e = std::min(row0 + nq, (f + 1) * tab.P);
+    pairs += (double)(e - r) * tab.kend[f];
+    r = e;
+  }
+  const int es = dt == WAM_BF16 ? 2 : 4;
+  const int kmax = tab.kend[(row0 + nq - 1) / tab.P];
+  TimingScope ts(s, KC_ATTN_PREFILL, (double)Hh * 64 * es * (2.0 * nq + 2.0 * kmax),
+                 4.0 * 64 * Hh * pairs);
   if (dt == WAM_BF16) {
     dim3 grid((nq + pf::QT - 1) / pf::QT, Hh);
     hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, (const bf16_t*)q,
@@ -456,30 +466,30 @@ __global__ __launch_bounds__(256) void attn_action_kernel(
 }
 
 // Merge splits 0..S_b-1 of (b, h) in order; out[b*32 + q][h*64 + d].
+// One wavefront per (query, head, episode); lane d owns one head dim.
 template <typename TO>
-__global__ __launch_bounds__(256) void attn_action_merge_kernel(const float* __restrict__ part,
-                                                                ActGeom G, TO* __restrict__ out) {
+__global__ __launch_bounds__(64) void attn_action_merge_kernel(const float* __restrict__ part,
+                                                               ActGeom G, TO* __restrict__ out) {
   using namespace act;
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
   const int len = G.lens.len[b];
   const int ncs = G.kc_chunk > 0 ? (len + G.kc_chunk - 1) / G.kc_chunk : 0;
   const int ns = ncs + (G.n_act > 0 ? 1 : 0);
   const long long base = ((long long)b * G.Hh + h) * G.S;
-  const float* pm = part + base * H;
-  const float* pl = part + (long long)G.B * G.Hh * G.S * H + base * H;
-  const float* po = part + 2ll * G.B * G.Hh * G.S * H + base * H * 64;
-  for (int i = threadIdx.x; i < H * 64; i += 256) {
-    const int qi = i >> 6, d = i & 63;
-    float M = -INFINITY;
-    for (int sp = 0; sp < ns; sp++) M = fmaxf(M, pm[sp * H + qi]);
-    float L = 0.f, O = 0.f;
-    for (int sp = 0; sp < ns; sp++) {
-      const float f = __builtin_amdgcn_exp2f(pm[sp * H + qi] - M);
-      L += pl[sp * H + qi] * f;
-      O += po[((long long)sp * H + qi) * 64 + d] * f;
-    }
-    out[((long long)b * H + qi) * G.Hh * 64 + h * 64 + d] = from_f<TO>(O / L);
+  const float* pm = part + base * H + qi;
+  const float* pl = part + (long long)G.B * G.Hh * G.S * H + base * H + qi;
+  const float* po = part + 2ll * G.B * G.Hh * G.S * H + (base * H + qi) * 64 + d;
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int sp = 0; sp < ns; sp++) M = fmaxf(M, pm[sp * H]);
+  float L = 0.f, O = 0.f;
+#pragma unroll 8
+  for (int sp = 0; sp < ns; sp++) {
+    const float f = __builtin_amdgcn_exp2f(pm[sp * H] - M);
+    L = fmaf(pl[sp * H], f, L);
+    O = fmaf(po[(long long)sp * H * 64], f, O);
   }
+  out[((long long)b * H + qi) * G.Hh * 64 + h * 64 + d] = from_f<TO>(O / L);
 }
 
 // fp32: one thread per (episode, head, query)
@@ -575,9 +585,14 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* 
     for (int b = 0; b < B; b++) max_len = max(max_len, lens.len[b]);
   if (!kc)
     for (int b = 0; b < B; b++) G.lens.len[b] = 0;
+  double keys = 0.0;
+  for (int b = 0; b < B; b++) keys += (double)G.lens.len[b] + n_act;
+  const int es = dt == WAM_BF16 ? 2 : 4;
   if (dt == WAM_F32) {
     G.kc_chunk = 0;
     G.S = 0;
+    TimingScope ts(s, KC_ATTN_ACTION, keys * Hh * 64 * 2 * es + 2.0 * B * H * Hh * 64 * es,
+                   4.0 * 64 * Hh * H * keys);
     hipLaunchKernelGGL(attn_action_f32_kernel, dim3(Hh, B), dim3(64), 0, s, (const float*)q,
                        (const float*)ka, (const float*)va, (const float*)kc, (const float*)vc,
                        G, (float*)out, 0.125f);
@@ -586,12 +601,17 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* 
   G.kc_chunk = action_chunk(B, Hh, max_len, splits_hint);
   G.S = (G.kc_chunk > 0 ? (max_len + G.kc_chunk - 1) / G.kc_chunk : 0) + 1;
   if (scratch_bytes < (size_t)B * Hh * G.S * H * 66 * sizeof(float)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_action_kernel, dim3(G.S, Hh, B), dim3(256), 0, s, (const bf16_t*)q,
-                     (const bf16_t*)ka, (const bf16_t*)va, (const bf16_t*)kc, (const bf16_t*)vc,
-                     G, (float*)scratch, 0.125f * LOG2E);
+  {
+    TimingScope ts(s, KC_ATTN_ACTION, keys * Hh * 64 * 2 * es + 1.0 * B * H * Hh * 64 * es,
+                   4.0 * 64 * Hh * H * keys);
+    hipLaunchKernelGGL(attn_action_kernel, dim3(G.S, Hh, B), dim3(256), 0, s, (const bf16_t*)q,
+                       (const bf16_t*)ka, (const bf16_t*)va, (const bf16_t*)kc, (const bf16_t*)vc,
+                       G, (float*)scratch, 0.125f * LOG2E);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_action_merge_kernel<bf16_t>, dim3(Hh, B), dim3(256), 0, s,
+  TimingScope ts(s, KC_ATTN_MERGE, (double)B * Hh * G.S * H * 66 * 4 + (double)B * H * Hh * 64 * es, 0.0);
+  hipLaunchKernelGGL(attn_action_merge_kernel<bf16_t>, dim3(H, Hh, B), dim3(64), 0, s,
                      (const float*)scratch, G, (bf16_t*)out);
   return hipGetLastError();
 }

@@ -5,45 +5,85 @@
 namespace wam {
 
 // ------------------------------------------------------------ RMSNorm
-// One wavefront per row: y = x * (mean(x^2) + 1e-6)^(-1/2) * g.
-template <typename TO>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
+// One wavefront per row: (optionally x += sum of split partials, written
+// back), then y = x * (mean(x^2) + 1e-6)^(-1/2) * g.
+template <typename TO, bool ACC>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x,
+                                                      const float* __restrict__ part, int KS,
                                                       const float* __restrict__ g,
                                                       TO* __restrict__ y, int M, int D) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
-  const float* xr = x + (long long)row * D;
+  float* xr = x + (long long)row * D;
+  constexpr int MAXV = 8;  // D <= 2048
+  float4 v[MAXV];
   float ss = 0.f;
-  for (int i = lane * 4; i < D; i += 256) {
-    float4 v = *(const float4*)(xr + i);
-    ss = fmaf(v.x, v.x, ss);
-    ss = fmaf(v.y, v.y, ss);
-    ss = fmaf(v.z, v.z, ss);
-    ss = fmaf(v.w, v.w, ss);
+#pragma unroll
+  for (int j = 0; j < MAXV; j++) {
+    const int i = lane * 4 + 256 * j;
+    if (i < D) {
+      float4 t = *(const float4*)(xr + i);
+      if (ACC) {
+        for (int k = 0; k < KS; k++) {
+          float4 p = *(const float4*)(part + ((long long)k * M + row) * D + i);
+          t.x += p.x;
+          t.y += p.y;
+          t.z += p.z;
+          t.w += p.w;
+        }
+        *(float4*)(xr + i) = t;
+      }
+      v[j] = t;
+      ss = fmaf(t.x, t.x, ss);
+      ss = fmaf(t.y, t.y, ss);
+      ss = fmaf(t.z, t.z, ss);
+      ss = fmaf(t.w, t.w, ss);
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
   const float r = 1.0f / sqrtf(ss / (float)D + 1e-6f);
   TO* yr = y + (long long)row * D;
-  for (int i = lane * 4; i < D; i += 256) {
-    float4 v = *(const float4*)(xr + i);
-    float4 gg = *(const float4*)(g + i);
-    yr[i + 0] = from_f<TO>(v.x * r * gg.x);
-    yr[i + 1] = from_f<TO>(v.y * r * gg.y);
-    yr[i + 2] = from_f<TO>(v.z * r * gg.z);
-    yr[i + 3] = from_f<TO>(v.w * r * gg.w);
+#pragma unroll
+  for (int j = 0; j < MAXV; j++) {
+    const int i = lane * 4 + 256 * j;
+    if (i < D) {
+      float4 gg = *(const float4*)(g + i);
+      TO o4[4] = {from_f<TO>(v[j].x * r * gg.x), from_f<TO>(v[j].y * r * gg.y),
+                  from_f<TO>(v[j].z * r * gg.z), from_f<TO>(v[j].w * r * gg.w)};
+      if constexpr (sizeof(TO) == 2)
+        *(uint2*)(yr + i) = *(uint2*)o4;
+      else
+        *(float4*)(yr + i) = *(float4*)o4;
+    }
   }
 }
 
-hipError_t rmsnorm(hipStream_t s, int odt, const float* x, const float* g, void* y, int M, int D) {
+template <bool ACC>
+static hipError_t rmsnorm_launch(hipStream_t s, int odt, float* x, const float* part, int KS,
+                                 const float* g, void* y, int M, int D) {
   if (M <= 0) return hipSuccess;
+  if (D > 2048 || D % 4) return hipErrorInvalidValue;
   dim3 grid((M + 3) / 4);
+  TimingScope ts(s, KC_RMSNORM,
+                 (double)M * D * ((ACC ? 8 + 4 * KS : 4) + (odt == WAM_BF16 ? 2 : 4)), 0.0);
   if (odt == WAM_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, dim3(256), 0, s, x, g, (bf16_t*)y, M, D);
+    hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, ACC>), grid, dim3(256), 0, s, x, part, KS, g,
+                       (bf16_t*)y, M, D);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, x, g, (float*)y, M, D);
+    hipLaunchKernelGGL((rmsnorm_kernel<float, ACC>), grid, dim3(256), 0, s, x, part, KS, g,
+                       (float*)y, M, D);
   return hipGetLastError();
+}
+
+hipError_t rmsnorm(hipStream_t s, int odt, const float* x, const float* g, void* y, int M, int D) {
+  return rmsnorm_launch<false>(s, odt, const_cast<float*>(x), nullptr, 0, g, y, M, D);
+}
+
+hipError_t rmsnorm_accum(hipStream_t s, int odt, float* x, const float* part, int KS,
+                         const float* g, void* y, int M, int D) {
+  return rmsnorm_launch<true>(s, odt, x, part, KS, g, y, M, D);
 }
 
 // ------------------------------------------------------------ embedding
@@ -89,6 +129,7 @@ hipError_t embed(hipStream_t s, int xdt, int wdt, const void* x, const RowMap& m
   if (M <= 0) return hipSuccess;
   if (C > EMB_MAXC) return hipErrorInvalidValue;
   dim3 grid((M + EMB_ROWS - 1) / EMB_ROWS, (D + 255) / 256);
+  TimingScope ts(s, KC_EMBED, (double)M * D * 4, 2.0 * M * D * C);
 #define EMB(TX, TW)                                                                          \
   hipLaunchKernelGGL((embed_kernel<TX, TW>), grid, dim3(256), 0, s, (const TX*)x, map,       \
                      (const TW*)w_in, emb, X, M, D, C)
@@ -223,6 +264,10 @@ hipError_t fuse_kv(hipStream_t s, int dt, const void* src, void* dst, long long 
   long long per = (layer_elems / 8 + 255) / 256;
   unsigned bx = (unsigned)(per < 1024 ? per : 1024);
   dim3 grid(bx, a.M);
+  int reads = 0;
+  for (int m = 0; m < a.M; m++) reads += a.count[m];
+  TimingScope ts(s, KC_FUSE, (double)(reads + a.M) * layer_elems * (dt == WAM_BF16 ? 2 : 4),
+                 2.0 * reads * layer_elems);
   if (dt == WAM_BF16)
     hipLaunchKernelGGL(fuse_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)src,
                        (bf16_t*)dst, layer_elems, a);

@@ -172,176 +172,118 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const bf16_t* __restrict_
 
 // ============================================================ skinny MFMA (M <= 128)
 namespace skinny {
-constexpr int NT = 64;            // columns per workgroup (16 per wave)
+constexpr int NT = 16;   // columns per workgroup
 constexpr int MAXM = 128;
-constexpr int LDS_ELEMS = 16384;  // A staging: M * (kr + 8) bf16 <= 32 KB
+constexpr int MAXKS = 8;
 }
 
-// Workgroup (kt, ks): columns [kt*64, kt*64+64), k range [ks*kr, ks*kr+kr).
-// k is visited 64 at a time; within a 64-wide step lane group g = lane/16
-// owns k offsets 16g..16g+15, split over two MFMAs (the k order inside a dot
-// product is a free permutation as long as A and B use the same one).  This
-// makes every weight row segment a 128-byte contiguous read.
+// Workgroup (kt, ks) computes columns [16kt, 16kt+16) over the k range
+// [ks*kr, (ks+1)*kr); its four waves take consecutive quarters of that range
+// and are summed through LDS in wave order.  No inter-workgroup
+// synchronisation: with gridDim.y > 1 each workgroup writes its raw fp32
+// partial to part[ks][M][N] and the consumer sums the partials in ks order.
+// k is visited 64 at a time; lane group g = lane/16 owns k offsets
+// 16g..16g+15 of each 64-wide step, split over two MFMAs (a dot product may
+// permute k freely as long as A and B agree), so each weight row segment is
+// one 128-byte contiguous read.
 template <int EPI, typename TO, int MT>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16_t* __restrict__ A, int lda,
                                                           const bf16_t* __restrict__ B, int ldb,
                                                           int M, int N, int K, int kr, EpiArgs e,
-                                                          float* __restrict__ part,
-                                                          int* __restrict__ counters) {
-  using namespace skinny;
-  __shared__ __attribute__((aligned(16))) bf16_t sA[LDS_ELEMS];
-  __shared__ int s_last;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int KS = gridDim.y;
-  const int kt = blockIdx.x, ks = blockIdx.y;
-  const int n0 = kt * NT;
-  const int kb = ks * kr;
-  const int ald = kr + 8;
-
-  // stage A[0..M)[kb..kb+kr) (rows of 16-byte chunks)
-  const int chunks = M * (kr / 8);
-  for (int c = tid; c < chunks; c += 256) {
-    int row = c / (kr / 8), ch = c - row * (kr / 8);
-    *(u32x4*)(sA + row * ald + ch * 8) = *(const u32x4*)(A + (long long)row * lda + kb + ch * 8);
-  }
-  __syncthreads();
+                                                          float* __restrict__ part) {
+  constexpr int U = MT <= 2 ? 4 : (MT <= 4 ? 2 : 1);
+  __shared__ float red[4][MT * 16][17];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int n0 = blockIdx.x * skinny::NT;
+  const int kw = kr / 4;
+  const int kb = blockIdx.y * kr + w * kw;
+  const bf16_t* brow = B + (long long)(n0 + c16) * ldb + kb + 16 * g;
+  const bf16_t* arow = A + (long long)c16 * lda + kb + 16 * g;
 
   floatx4 acc[MT];
 #pragma unroll
   for (int i = 0; i < MT; i++) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const int g = lane >> 4;
-  const bf16_t* brow = B + (long long)(n0 + w * 16 + (lane & 15)) * ldb + kb + 16 * g;
-  const int nsteps = kr / 64;
-  constexpr int U = 4;
-  int st = 0;
-  for (; st + U <= nsteps; st += U) {
-    bf16x8 b0[U], b1[U];
+  const int nsteps = kw / 64;
+  for (int st = 0; st < nsteps; st += U) {
+    bf16x8 b0[U], b1[U], a0[U][MT], a1[U][MT];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      b0[u] = *(const bf16x8*)(brow + (st + u) * 64);
-      b1[u] = *(const bf16x8*)(brow + (st + u) * 64 + 8);
+      if (st + u < nsteps) {
+        b0[u] = *(const bf16x8*)(brow + (st + u) * 64);
+        b1[u] = *(const bf16x8*)(brow + (st + u) * 64 + 8);
+#pragma unroll
+        for (int i = 0; i < MT; i++) {
+          const bf16_t* ap = arow + (long long)(16 * i) * lda + (st + u) * 64;
+          a0[u][i] = *(const bf16x8*)ap;
+          a1[u][i] = *(const bf16x8*)(ap + 8);
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const int kk = (st + u) * 64 + 16 * g;
+      if (st + u < nsteps) {
 #pragma unroll
-      for (int i = 0; i < MT; i++) {
-        bf16x8 a0 = *(const bf16x8*)(sA + (i * 16 + (lane & 15)) * ald + kk);
-        bf16x8 a1 = *(const bf16x8*)(sA + (i * 16 + (lane & 15)) * ald + kk + 8);
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0[u], acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[u], acc[i], 0, 0, 0);
+        for (int i = 0; i < MT; i++) {
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[u][i], b0[u], acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[u][i], b1[u], acc[i], 0, 0, 0);
+        }
       }
     }
   }
-  for (; st < nsteps; st++) {
-    bf16x8 b0 = *(const bf16x8*)(brow + st * 64);
-    bf16x8 b1 = *(const bf16x8*)(brow + st * 64 + 8);
-    const int kk = st * 64 + 16 * g;
-#pragma unroll
-    for (int i = 0; i < MT; i++) {
-      bf16x8 a0 = *(const bf16x8*)(sA + (i * 16 + (lane & 15)) * ald + kk);
-      bf16x8 a1 = *(const bf16x8*)(sA + (i * 16 + (lane & 15)) * ald + kk + 8);
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[i], 0, 0, 0);
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[i], 0, 0, 0);
-    }
-  }
-
-  const int col = n0 + w * 16 + (lane & 15);
-  if (KS == 1) {
-#pragma unroll
-    for (int i = 0; i < MT; i++)
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        int m = i * 16 + 4 * g + r;
-        if (m < M) epi_store<EPI, TO>(e, m, col, acc[i][r]);
-      }
-    return;
-  }
-  // split-K: publish the partial, the last workgroup of this column tile
-  // sums all partials in ks order and runs the epilogue.
-  float* mine = part + (long long)ks * M * N;
+  // C layout: lane holds column c16, rows 16i + 4g + r
 #pragma unroll
   for (int i = 0; i < MT; i++)
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      int m = i * 16 + 4 * g + r;
-      if (m < M) mine[(long long)m * N + col] = acc[i][r];
-    }
-  __threadfence();
+    for (int r = 0; r < 4; r++) red[w][16 * i + 4 * g + r][c16] = acc[i][r];
   __syncthreads();
-  if (tid == 0) {
-    int prev = atomicAdd(&counters[kt], 1);
-    s_last = (prev == KS - 1);
+  for (int idx = tid; idx < M * 16; idx += 256) {
+    const int m = idx >> 4, c = idx & 15;
+    const float v = ((red[0][m][c] + red[1][m][c]) + red[2][m][c]) + red[3][m][c];
+    if (gridDim.y == 1)
+      epi_store<EPI, TO>(e, m, n0 + c, v);
+    else
+      part[((long long)blockIdx.y * M + m) * N + n0 + c] = v;
   }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int idx = tid; idx < M * NT; idx += 256) {
-    int m = idx / NT, c = n0 + (idx - m * NT);
-    float s = 0.f;
-    for (int q = 0; q < KS; q++) s += __builtin_nontemporal_load(part + (long long)q * M * N + (long long)m * N + c);
-    epi_store<EPI, TO>(e, m, c, s);
-  }
-  if (tid == 0) counters[kt] = 0;
 }
 
 // ============================================================ dispatch
+// Algorithmic HBM bytes of one GEMM: read A and B once, write C once (read
+// and write for the accumulate-into epilogues).
+template <int EPI>
+static double gemm_bytes(int M, int N, int K, int ea, int eb, int eo) {
+  double out = (double)M * N * ((EPI == EPI_RESID || EPI == EPI_EULER) ? 8.0 : (double)eo);
+  return (double)M * K * ea + (double)N * K * eb + out;
+}
+
 template <int EPI, typename TO>
 static hipError_t launch_big(hipStream_t s, int M, int N, int K, const void* A, int lda,
                              const void* B, int ldb, const EpiArgs& e) {
   int ntm = (M + big::BM - 1) / big::BM, ntn = N / big::BN;
+  TimingScope ts(s, KC_GEMM_BIG, gemm_bytes<EPI>(M, N, K, 2, 2, sizeof(TO)), 2.0 * M * N * K);
   hipLaunchKernelGGL((gemm_big_kernel<EPI, TO>), dim3(ntm * ntn), dim3(256), 0, s,
                      (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, e);
   return hipGetLastError();
 }
 
-static void skinny_plan(int M, int N, int K, int* KS, int* kr) {
-  // enough workgroups to cover the 256 CUs; k range a multiple of 64 that
-  // divides K and keeps the A stage within LDS
-  int tiles = N / skinny::NT;
-  int best = 1;
-  // cap the split so that partial-sum traffic stays at most half the weights
-  int ks_max = K / (4 * M);
-  if (ks_max < 1) ks_max = 1;
-  for (int ks = 1; ks <= 64; ks *= 2) {
-    if (ks > ks_max && M * (K / ks + 8) <= skinny::LDS_ELEMS) break;
-    if (K % (ks * 64)) break;
-    int r = K / ks;
-    if (M * (r + 8) > skinny::LDS_ELEMS) { best = ks * 2; continue; }
-    best = ks;
-    if (tiles * ks >= 256) break;
-  }
-  while (K % (best * 64)) best /= 2;
-  if (best < 1) best = 1;
-  *KS = best;
-  *kr = K / best;
-}
-
-size_t gemm_scratch_elems(int M, int N, int K) {
-  if (M > skinny::MAXM || (M % 16) || (N % skinny::NT) || (K % 64)) return 0;
-  int KS, kr;
-  skinny_plan(M, N, K, &KS, &kr);
-  return KS > 1 ? (size_t)KS * M * N : 0;
+// k range of one workgroup: a multiple of 256 (64 per wave) dividing K.
+static bool skinny_ok(int M, int N, int K) {
+  return M >= 16 && M <= skinny::MAXM && M % 16 == 0 && N % skinny::NT == 0 && K % 256 == 0;
 }
 
 template <int EPI, typename TO>
 static hipError_t launch_skinny(hipStream_t s, int M, int N, int K, const void* A, int lda,
-                                const void* B, int ldb, const EpiArgs& e,
-                                const GemmScratch& scr) {
-  int KS, kr;
-  skinny_plan(M, N, K, &KS, &kr);
-  if (M * (kr + 8) > skinny::LDS_ELEMS) return hipErrorInvalidValue;
-  if (KS > 1 && (scr.part == nullptr || scr.part_elems < (size_t)KS * M * N ||
-                 scr.counters == nullptr || scr.n_counters < N / skinny::NT))
-    return hipErrorInvalidValue;
+                                const void* B, int ldb, const EpiArgs& e, int KS, float* part) {
+  const int kr = K / KS;
   dim3 grid(N / skinny::NT, KS);
+  TimingScope ts(s, KC_GEMM_SKINNY, gemm_bytes<EPI>(M, N, K, 2, 2, KS > 1 ? 4 * KS : sizeof(TO)),
+                 2.0 * M * N * K);
   const bf16_t* a = (const bf16_t*)A;
   const bf16_t* b = (const bf16_t*)B;
   switch (M / 16) {
 #define SK(mt)                                                                              \
   case mt:                                                                                  \
     hipLaunchKernelGGL((gemm_skinny_kernel<EPI, TO, mt>), grid, dim3(256), 0, s, a, lda, b, \
-                       ldb, M, N, K, kr, e, scr.part, scr.counters);                        \
+                       ldb, M, N, K, kr, e, part);                                          \
     break;
     SK(1) SK(2) SK(3) SK(4) SK(5) SK(6) SK(7) SK(8)
 #undef SK
@@ -351,10 +293,30 @@ static hipError_t launch_skinny(hipStream_t s, int M, int N, int K, const void* 
   return hipGetLastError();
 }
 
+int gemm_partial_splits(int M, int N, int K) {
+  if (!skinny_ok(M, N, K)) return 0;
+  int ks = 1;
+  while (ks < skinny::MAXKS && (N / skinny::NT) * ks < 256 && K % (256 * ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
+hipError_t gemm_partial(hipStream_t s, int M, int N, int K, const void* A, int lda, const void* B,
+                        int ldb, float* part, int* ks_out) {
+  const int ks = gemm_partial_splits(M, N, K);
+  if (ks == 0) return hipErrorInvalidValue;
+  *ks_out = ks;
+  EpiArgs e{};
+  e.out = part;
+  e.ldo = N;
+  return launch_skinny<EPI_STORE, float>(s, M, N, K, A, lda, B, ldb, e, ks, part);
+}
+
 template <typename TA, typename TB, int EPI, typename TO>
 static hipError_t launch_simple(hipStream_t s, int M, int N, int K, const void* A, int lda,
                                 const void* B, int ldb, const EpiArgs& e) {
   dim3 grid((N + 63) / 64, (M + 63) / 64);
+  TimingScope ts(s, KC_GEMM_SIMPLE, gemm_bytes<EPI>(M, N, K, sizeof(TA), sizeof(TB), sizeof(TO)),
+                 2.0 * M * N * K);
   hipLaunchKernelGGL((gemm_simple_kernel<TA, TB, TO, EPI>), grid, dim3(256), 0, s,
                      (const TA*)A, lda, (const TB*)B, ldb, M, N, K, e);
   return hipGetLastError();
@@ -363,12 +325,11 @@ static hipError_t launch_simple(hipStream_t s, int M, int N, int K, const void* 
 template <int EPI, typename TO>
 static hipError_t gemm_epi(hipStream_t s, int adt, int bdt, int M, int N, int K, const void* A,
                            int lda, const void* B, int ldb, const EpiArgs& e,
-                           const GemmScratch& scr) {
+                           int /*unused*/ = 0) {
   const bool aligned = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && (lda % 8 == 0) &&
                        (ldb % 8 == 0);
   if (adt == WAM_BF16 && bdt == WAM_BF16 && aligned && K % 64 == 0) {
-    if (M <= skinny::MAXM && M % 16 == 0 && N % skinny::NT == 0)
-      return launch_skinny<EPI, TO>(s, M, N, K, A, lda, B, ldb, e, scr);
+    if (skinny_ok(M, N, K)) return launch_skinny<EPI, TO>(s, M, N, K, A, lda, B, ldb, e, 1, nullptr);
     if (N % big::BN == 0) return launch_big<EPI, TO>(s, M, N, K, A, lda, B, ldb, e);
   }
   if (adt == WAM_F32 && bdt == WAM_F32)
@@ -381,24 +342,23 @@ static hipError_t gemm_epi(hipStream_t s, int adt, int bdt, int M, int N, int K,
 }
 
 hipError_t gemm(hipStream_t s, int adt, int bdt, int odt, int epi, int M, int N, int K,
-                const void* A, int lda, const void* B, int ldb, const EpiArgs& e,
-                const GemmScratch& scr) {
+                const void* A, int lda, const void* B, int ldb, const EpiArgs& e) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const bool ob = (odt == WAM_BF16);
   switch (epi) {
     case EPI_STORE:
-      return ob ? gemm_epi<EPI_STORE, bf16_t>(s, adt, bdt, M, N, K, A, lda, B, ldb, e, scr)
-                : gemm_epi<EPI_STORE, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e, scr);
+      return ob ? gemm_epi<EPI_STORE, bf16_t>(s, adt, bdt, M, N, K, A, lda, B, ldb, e)
+                : gemm_epi<EPI_STORE, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e);
     case EPI_GELU:
-      return ob ? gemm_epi<EPI_GELU, bf16_t>(s, adt, bdt, M, N, K, A, lda, B, ldb, e, scr)
-                : gemm_epi<EPI_GELU, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e, scr);
+      return ob ? gemm_epi<EPI_GELU, bf16_t>(s, adt, bdt, M, N, K, A, lda, B, ldb, e)
+                : gemm_epi<EPI_GELU, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e);
     case EPI_RESID:
-      return gemm_epi<EPI_RESID, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e, scr);
+      return gemm_epi<EPI_RESID, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e);
     case EPI_EULER:
-      return gemm_epi<EPI_EULER, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e, scr);
+      return gemm_epi<EPI_EULER, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e);
     case EPI_QKV:
-      return ob ? gemm_epi<EPI_QKV, bf16_t>(s, adt, bdt, M, N, K, A, lda, B, ldb, e, scr)
-                : gemm_epi<EPI_QKV, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e, scr);
+      return ob ? gemm_epi<EPI_QKV, bf16_t>(s, adt, bdt, M, N, K, A, lda, B, ldb, e)
+                : gemm_epi<EPI_QKV, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e);
   }
   return hipErrorInvalidValue;
 }

@@ -145,21 +145,16 @@ struct Bufs {
   void* Hb;
   float* Yh;
   float* emb;
-  GemmScratch gs;
+  float* part;     // split partial products of the action path
+  int pend;        // splits of a W2 product not yet added to X (0: none)
   void* attn;
   size_t attn_bytes;
 };
 
 size_t gemm_part_elems(int M, const wam_dims* d) {
-  size_t e = 0;
-  e = std::max(e, gemm_scratch_elems(M, 3 * d->D, d->D));
-  e = std::max(e, gemm_scratch_elems(M, d->D, d->D));
-  e = std::max(e, gemm_scratch_elems(M, d->Fm, d->D));
-  e = std::max(e, gemm_scratch_elems(M, d->D, d->Fm));
-  e = std::max(e, gemm_scratch_elems(M, 2 * d->D, d->D));
-  return e;
+  size_t e = (size_t)gemm_partial_splits(M, d->D, d->D) * M * d->D;
+  return std::max(e, (size_t)gemm_partial_splits(M, d->D, d->Fm) * M * d->D);
 }
-constexpr int N_COUNTERS = 1024;
 
 // ----------------------------------------------------------------- layers
 struct Layer {
@@ -191,32 +186,64 @@ int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const Fra
   if (kv_only) {
     e.n_begin = D;
     HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, 2 * D, D, b.Y, D,
-               (const char*)w.wqkv + (size_t)D * D * esz(dt), D, e, b.gs));
+               (const char*)w.wqkv + (size_t)D * D * esz(dt), D, e));
     return WAM_OK;
   }
-  HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, 3 * D, D, b.Y, D, w.wqkv, D, e, b.gs));
+  HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, 3 * D, D, b.Y, D, w.wqkv, D, e));
   HIPCK(attn_prefill(c.s, dt, d->Hh, n, row0, tab, b.Q, kl, vl, cap, b.O));
   EpiArgs r{};
   r.out = b.X;
   r.ldo = D;
-  HIPCK(gemm(c.s, dt, dt, WAM_F32, EPI_RESID, n, D, D, b.O, D, w.wo, D, r, b.gs));
+  HIPCK(gemm(c.s, dt, dt, WAM_F32, EPI_RESID, n, D, D, b.O, D, w.wo, D, r));
   HIPCK(rmsnorm(c.s, dt, b.X, w.g2, b.Y, n, D));
   EpiArgs gl{};
   gl.out = b.Hb;
   gl.ldo = d->Fm;
-  HIPCK(gemm(c.s, dt, dt, dt, EPI_GELU, n, d->Fm, D, b.Y, D, w.w1, D, gl, b.gs));
-  HIPCK(gemm(c.s, dt, dt, WAM_F32, EPI_RESID, n, D, d->Fm, b.Hb, d->Fm, w.w2, d->Fm, r, b.gs));
+  HIPCK(gemm(c.s, dt, dt, dt, EPI_GELU, n, d->Fm, D, b.Y, D, w.w1, D, gl));
+  HIPCK(gemm(c.s, dt, dt, WAM_F32, EPI_RESID, n, D, d->Fm, b.Hb, d->Fm, w.w2, d->Fm, r));
+  return WAM_OK;
+}
+
+// X += A W^T for the action rows: through split partials that the next
+// RMSNorm adds (bf16 skinny shapes), else directly.
+int action_resid(const Layer& c, int M, int N, int K, const void* A, const void* W, bool* pending,
+                 int* ks) {
+  const wam_dims* d = c.d;
+  Bufs& b = *c.b;
+  if (d->dtype == WAM_BF16 && gemm_partial_splits(M, N, K) > 0) {
+    HIPCK(gemm_partial(c.s, M, N, K, A, K, W, K, b.part, ks));
+    *pending = true;
+    return WAM_OK;
+  }
+  EpiArgs r{};
+  r.out = b.X;
+  r.ldo = N;
+  HIPCK(gemm(c.s, d->dtype, d->dtype, WAM_F32, EPI_RESID, M, N, K, A, K, W, K, r));
+  *pending = false;
+  return WAM_OK;
+}
+
+// y = RMSNorm(X; g), first adding the pending split partials to X.
+int norm_rows(const Layer& c, int odt, const float* g, void* y, int M) {
+  Bufs& b = *c.b;
+  if (b.pend > 0) {
+    HIPCK(rmsnorm_accum(c.s, odt, b.X, b.part, b.pend, g, y, M, c.d->D));
+    b.pend = 0;
+  } else {
+    HIPCK(rmsnorm(c.s, odt, b.X, g, y, M, c.d->D));
+  }
   return WAM_OK;
 }
 
 // One action layer on the B*H rows in b.X; kc/vc: that layer's cache for all
-// episodes (or NULL).
+// episodes (or NULL).  May leave the W2 product pending in b.part (b.pend).
 int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, const void* vc,
                  int cap, const ActLens& lens) {
   const wam_dims* d = c.d;
   const int dt = d->dtype, D = d->D, H = d->H, M = B * H;
   Bufs& b = *c.b;
-  HIPCK(rmsnorm(c.s, dt, b.X, w.g1, b.Y, M, D));
+  int st;
+  if ((st = norm_rows(c, dt, w.g1, b.Y, M))) return st;
   EpiArgs e{};
   e.q = b.Q;
   e.k = b.Ka;
@@ -229,19 +256,20 @@ int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, co
   e.v_gs = (long long)d->Hh * d->dh * H;
   e.v_hs = (long long)d->dh * H;
   e.v_ld = H;
-  HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, M, 3 * D, D, b.Y, D, w.wqkv, D, e, b.gs));
+  HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, M, 3 * D, D, b.Y, D, w.wqkv, D, e));
   HIPCK(attn_action(c.s, dt, B, d->Hh, H, b.Q, b.Ka, b.Va, H, kc, vc, cap, lens, b.O, 0, b.attn,
                     b.attn_bytes));
-  EpiArgs r{};
-  r.out = b.X;
-  r.ldo = D;
-  HIPCK(gemm(c.s, dt, dt, WAM_F32, EPI_RESID, M, D, D, b.O, D, w.wo, D, r, b.gs));
-  HIPCK(rmsnorm(c.s, dt, b.X, w.g2, b.Y, M, D));
+  bool pend;
+  int ks = 0;
+  if ((st = action_resid(c, M, D, D, b.O, w.wo, &pend, &ks))) return st;
+  b.pend = pend ? ks : 0;
+  if ((st = norm_rows(c, dt, w.g2, b.Y, M))) return st;
   EpiArgs gl{};
   gl.out = b.Hb;
   gl.ldo = d->Fm;
-  HIPCK(gemm(c.s, dt, dt, dt, EPI_GELU, M, d->Fm, D, b.Y, D, w.w1, D, gl, b.gs));
-  HIPCK(gemm(c.s, dt, dt, WAM_F32, EPI_RESID, M, D, d->Fm, b.Hb, d->Fm, w.w2, d->Fm, r, b.gs));
+  HIPCK(gemm(c.s, dt, dt, dt, EPI_GELU, M, d->Fm, D, b.Y, D, w.w1, D, gl));
+  if ((st = action_resid(c, M, D, d->Fm, b.Hb, w.w2, &pend, &ks))) return st;
+  b.pend = pend ? ks : 0;
   return WAM_OK;
 }
 
@@ -249,14 +277,14 @@ int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, co
 int head_euler(const Layer& c, const wam_expert_w* ex, int M, int C, float* z, float dtv, float* vhat) {
   const wam_dims* d = c.d;
   Bufs& b = *c.b;
-  HIPCK(rmsnorm(c.s, WAM_F32, b.X, ex->g_out, b.Yh, M, d->D));
+  int st;
+  if ((st = norm_rows(c, WAM_F32, ex->g_out, b.Yh, M))) return st;
   EpiArgs e{};
   e.out = z;
   e.ldo = C;
   e.dt = dtv;
   e.vhat = vhat;
-  HIPCK(gemm(c.s, WAM_F32, d->dtype, WAM_F32, EPI_EULER, M, C, d->D, b.Yh, d->D, ex->w_out, d->D, e,
-             b.gs));
+  HIPCK(gemm(c.s, WAM_F32, d->dtype, WAM_F32, EPI_EULER, M, C, d->D, b.Yh, d->D, ex->w_out, d->D, e));
   return WAM_OK;
 }
 
@@ -273,10 +301,8 @@ void plan_action(Arena& a, const wam_dims* d, int B, int max_len, bool with_emb,
   b.O = a.take((size_t)M * d->D * e);
   b.Hb = a.take((size_t)M * d->Fm * e);
   b.Yh = (float*)a.take((size_t)M * d->D * 4);
-  b.gs.part_elems = gemm_part_elems(M, d);
-  b.gs.part = (float*)a.take(b.gs.part_elems * 4);
-  b.gs.counters = (int*)a.take(N_COUNTERS * 4);
-  b.gs.n_counters = N_COUNTERS;
+  b.part = (float*)a.take(gemm_part_elems(M, d) * 4 + 16);
+  b.pend = 0;
   b.attn_bytes = attn_action_scratch_bytes(B, d->Hh, d->H, max_len, 0);
   b.attn = a.take(b.attn_bytes);
 }
@@ -293,14 +319,8 @@ void plan_prefill(Arena& a, const wam_dims* d, int Fh, int Ff, Bufs& b, float** 
   b.Hb = a.take(T * d->Fm * e);
   b.Yh = (float*)a.take(std::max<size_t>(Tf, 1) * d->D * 4);
   *z = (float*)a.take(std::max<size_t>(Tf, 1) * d->Cv * 4);
-  // passes of <= 128 rows take the split-K skinny GEMM; size for any of them
-  size_t pe = 0;
-  if ((size_t)d->P <= 128)
-    for (int m = 16; m <= 128; m += 16) pe = std::max(pe, gemm_part_elems(m, d));
-  b.gs.part_elems = pe;
-  b.gs.part = (float*)a.take(pe * 4 + 4);
-  b.gs.counters = (int*)a.take(N_COUNTERS * 4);
-  b.gs.n_counters = N_COUNTERS;
+  b.part = nullptr;
+  b.pend = 0;
   b.Ka = b.Va = nullptr;
   b.attn = nullptr;
   b.attn_bytes = 0;
@@ -418,7 +438,6 @@ int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video, const 
   Bufs bufs;
   float* z;
   plan_prefill(a, d, Fh, Ff, bufs, &z);
-  HIPCK(fill_i32(s, bufs.gs.counters, N_COUNTERS, 0));
 
   // time embeddings: [0 (history), sigma_0 .. sigma_V (V >= 1) | 1 (V = 0)]
   std::vector<float> sig(video_steps + 1);
@@ -577,13 +596,13 @@ int wam_action_layer(const wam_dims* d, const wam_layer_w* w, float* x, const wa
   Arena a(ws);
   Bufs b;
   plan_action(a, d, B, kv ? std::max(max_len_of(kv, B), kv->cap) : 0, false, b);
-  HIPCK(fill_i32(s, b.gs.counters, N_COUNTERS, 0));
   const size_t bytes = (size_t)B * d->H * d->D * 4;
   HIPCK(hipMemcpyAsync(b.X, x, bytes, hipMemcpyDeviceToDevice, s));
   Layer c{s, d, &b};
   const void* kc = kv ? (const char*)kv->k + kv_layer * layer_stride(kv) : nullptr;
   const void* vc = kv ? (const char*)kv->v + kv_layer * layer_stride(kv) : nullptr;
   if ((st = action_layer(c, *w, B, kc, vc, kv ? kv->cap : 0, lens))) return st;
+  if (b.pend > 0 && (st = norm_rows(c, d->dtype, w->g1, b.Y, B * d->H))) return st;  // fold W2
   HIPCK(hipMemcpyAsync(x, b.X, bytes, hipMemcpyDeviceToDevice, s));
   return WAM_OK;
 }
@@ -627,7 +646,6 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
   Arena a(ws);
   Bufs b;
   plan_action(a, d, B, any ? std::max(max_len_of(kv, B), kv->cap) : 0, true, b);
-  HIPCK(fill_i32(s, b.gs.counters, N_COUNTERS, 0));
   std::vector<float> t(N + 1);
   schedule(N, 0.0, shift, t.data());
   HIPCK(time_embedding(s, t.data(), N, d->D, b.emb));

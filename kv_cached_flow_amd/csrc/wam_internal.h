@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "../../include/wam.h"
 
@@ -110,20 +111,21 @@ __device__ inline void epi_store(const EpiArgs& e, int m, int n, float v) {
 
 // ---------------------------------------------------------------- launchers
 // C[M][N] = A[M][K] * B[N][K]^T with the epilogue; adt/bdt/odt are WAM_F32 or
-// WAM_BF16 (A, B and epilogue output element types).  part/cnt: split-K
-// scratch (may be null when the launcher does not need it).
-struct GemmScratch {
-  float* part;
-  size_t part_elems;
-  int* counters;
-  int n_counters;
-};
+// WAM_BF16 (A, B and epilogue output element types).
 hipError_t gemm(hipStream_t s, int adt, int bdt, int odt, int epi, int M, int N, int K,
-                const void* A, int lda, const void* B, int ldb, const EpiArgs& e,
-                const GemmScratch& scr);
-size_t gemm_scratch_elems(int M, int N, int K);
+                const void* A, int lda, const void* B, int ldb, const EpiArgs& e);
+
+// bf16 M <= 128: raw fp32 partial products part[ks][M][N], ks < *ks_out (the
+// caller sums them in ks order; rmsnorm_accum does).  gemm_partial_splits
+// gives the split count (0: shape not supported).
+int gemm_partial_splits(int M, int N, int K);
+hipError_t gemm_partial(hipStream_t s, int M, int N, int K, const void* A, int lda, const void* B,
+                        int ldb, float* part, int* ks_out);
 
 hipError_t rmsnorm(hipStream_t s, int odt, const float* x, const float* g, void* y, int M, int D);
+// x[m] += sum_{ks < KS} part[ks][m] (in ks order), then y = RMSNorm(x; g).
+hipError_t rmsnorm_accum(hipStream_t s, int odt, float* x, const float* part, int KS,
+                         const float* g, void* y, int M, int D);
 
 // X[m][n] = sum_c x[row(m)][c] * w_in[n][c] + emb[n]; rows are gathered by
 // frame: m -> frame src[m / P], token m % P, of a [*][P][C] input.
@@ -165,5 +167,24 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* 
 hipError_t debug_visibility(hipStream_t s, const FrameTab& tab, const int* comp_of_frame,
                             int F, uint8_t* vis);
 hipError_t fill_i32(hipStream_t s, int* p, int n, int v);
+
+// ---------------------------------------------------------------- timing
+enum KClass {
+  KC_GEMM_BIG, KC_GEMM_SKINNY, KC_GEMM_SIMPLE, KC_ATTN_PREFILL, KC_ATTN_ACTION,
+  KC_ATTN_MERGE, KC_RMSNORM, KC_EMBED, KC_FUSE, KC_MISC, KC_COUNT
+};
+// RAII event pair around the launches of one kernel class (no-op unless
+// wam_timing(1) was called); bytes/flops are the algorithmic work.
+class TimingScope {
+ public:
+  TimingScope(hipStream_t s, int cls, double bytes, double flops);
+  ~TimingScope();
+
+ private:
+  hipStream_t s_;
+  int cls_;
+  double bytes_, flops_;
+  void* a_;
+};
 
 }  // namespace wam

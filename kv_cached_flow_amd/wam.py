@@ -43,6 +43,11 @@ class WamKV(C.Structure):
                 ("len", C.POINTER(C.c_int32))]
 
 
+class WamKernelStat(C.Structure):
+    _fields_ = [("name", C.c_char * 32), ("launches", C.c_int), ("ms", C.c_double),
+                ("bytes", C.c_double), ("flops", C.c_double)]
+
+
 _EXPORTS = {
     "wam_abi_version": (C.c_int, []),
     "wam_status_str": (C.c_char_p, [C.c_int]),
@@ -75,6 +80,8 @@ _EXPORTS = {
     "wam_attention_prefill": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
                                         C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_int, C.c_void_p, C.c_void_p]),
+    "wam_timing": (C.c_int, [C.c_int]),
+    "wam_timing_report": (C.c_int, [C.POINTER(WamKernelStat), C.c_int]),
 }
 
 
@@ -272,3 +279,16 @@ def attention_prefill(dtype: int, q, row0: int, P: int, kend, kc, vc, cap: int, 
     _check(lib().wam_attention_prefill(dtype, Hh, dh, nq, row0, P, ke.ctypes.data, len(ke), _ptr(q),
                                        _ptr(kc), _ptr(vc), cap, _ptr(out), _stream(stream)),
            "wam_attention_prefill")
+
+
+def timing(enable: bool):
+    """Turn per-kernel-class event timing on (clearing old records) or off."""
+    _check(lib().wam_timing(1 if enable else 0), "wam_timing")
+
+
+def timing_report() -> dict:
+    """{class: {launches, ms, bytes, flops}} of the launches recorded so far."""
+    arr = (WamKernelStat * 32)()
+    n = _check(lib().wam_timing_report(arr, 32), "wam_timing_report")
+    return {arr[i].name.decode(): {"launches": arr[i].launches, "ms": arr[i].ms,
+                                   "bytes": arr[i].bytes, "flops": arr[i].flops} for i in range(n)}
