@@ -288,11 +288,12 @@ constexpr int KT = 64;  // keys per wave tile
 }
 
 struct ActGeom {
-  int B, Hh, cap, n_act, kc_chunk, S;  // S = splits per (b, h) incl. the own-key split
+  int B, Hh, cap, n_act, S;  // S = max splits per (b, h) incl. the own-key split
   ActLens lens;
+  int kc[WAM_MAX_BATCH];     // cache keys per split of episode b (0: no cache)
 };
 
-// Split (b, h, s): cache keys [s*kc_chunk, min(len, (s+1)*kc_chunk)) for s < ncs(b),
+// Split (b, h, s): cache keys [s*kc[b], min(len, (s+1)*kc[b])) for s < ncs(b),
 // the chunk's own keys for s == ncs(b).  Writes the split's (m, l, o) in the
 // log2 domain: m [32], l [32], o [32][64] (unnormalised).
 __global__ __launch_bounds__(256) void attn_action_kernel(
@@ -305,7 +306,8 @@ __global__ __launch_bounds__(256) void attn_action_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int len = G.lens.len[b];
-  const int ncs = (kc != nullptr) ? (len + G.kc_chunk - 1) / G.kc_chunk : 0;
+  const int chunk = G.kc[b];
+  const int ncs = (kc != nullptr && chunk > 0) ? (len + chunk - 1) / chunk : 0;
   const bool own = (s == ncs);
   if (s > ncs || (own && G.n_act == 0)) return;
   const bf16_t* kb;
@@ -314,8 +316,8 @@ __global__ __launch_bounds__(256) void attn_action_kernel(
   if (!own) {
     kb = kc + ((long long)b * G.Hh + h) * G.cap * 64;
     vb = vc + ((long long)b * G.Hh + h) * 64 * G.cap;
-    key0 = s * G.kc_chunk;
-    key1 = min(len, key0 + G.kc_chunk);
+    key0 = s * chunk;
+    key1 = min(len, key0 + chunk);
     vld = G.cap;
   } else {
     kb = ka + ((long long)b * G.Hh + h) * H * 64;
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(64) void attn_action_merge_kernel(const float* __re
   using namespace act;
   const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
   const int len = G.lens.len[b];
-  const int ncs = G.kc_chunk > 0 ? (len + G.kc_chunk - 1) / G.kc_chunk : 0;
+  const int ncs = G.kc[b] > 0 ? (len + G.kc[b] - 1) / G.kc[b] : 0;
   const int ns = ncs + (G.n_act > 0 ? 1 : 0);
   const long long base = ((long long)b * G.Hh + h) * G.S;
   const float* pm = part + base * H + qi;
@@ -543,11 +545,13 @@ __global__ __launch_bounds__(64) void attn_action_f32_kernel(const float* __rest
   for (int d = 0; d < 64; d++) orow[d] = o[d] * inv;
 }
 
-static int action_chunk(int B, int Hh, int max_len, int splits_hint) {
-  if (max_len <= 0) return 0;
-  int splits = splits_hint > 0 ? splits_hint : (512 + B * Hh - 1) / (B * Hh);
-  if (splits < 1) splits = 1;
-  int kc = (max_len + splits - 1) / splits;
+// Keys per split for one episode: a function of that episode's length and the
+// head count only, so an episode is split identically whatever the batch
+// (batch independence of the results is bitwise).
+static int action_chunk(int Hh, int len, int splits_hint) {
+  if (len <= 0) return 0;
+  int splits = splits_hint > 0 ? splits_hint : (512 + Hh - 1) / Hh;
+  int kc = (len + splits - 1) / splits;
   kc = (kc + act::KT - 1) / act::KT * act::KT;
   if (splits_hint <= 0 && kc < 4 * act::KT) kc = 4 * act::KT;
   return kc;
@@ -559,10 +563,9 @@ size_t attn_action_scratch_bytes(int B, int Hh, int H, int max_len, int splits_h
   int S = 1;
   if (max_len > 0) {
     if (splits_hint > 0) {
-      int kc = action_chunk(B, Hh, max_len, splits_hint);
-      S = (max_len + kc - 1) / kc + 1;
+      S = splits_hint + 1;
     } else {
-      int splits = (512 + B * Hh - 1) / (B * Hh);
+      int splits = (512 + Hh - 1) / Hh;
       S = std::min((max_len + 4 * act::KT - 1) / (4 * act::KT), splits + 1) + 1;
     }
   }
@@ -580,16 +583,13 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* 
   G.cap = cap;
   G.n_act = n_act;
   G.lens = lens;
-  int max_len = 0;
-  if (kc)
-    for (int b = 0; b < B; b++) max_len = max(max_len, lens.len[b]);
   if (!kc)
     for (int b = 0; b < B; b++) G.lens.len[b] = 0;
   double keys = 0.0;
   for (int b = 0; b < B; b++) keys += (double)G.lens.len[b] + n_act;
   const int es = dt == WAM_BF16 ? 2 : 4;
+  for (int b = 0; b < B; b++) G.kc[b] = kc ? action_chunk(Hh, G.lens.len[b], splits_hint) : 0;
   if (dt == WAM_F32) {
-    G.kc_chunk = 0;
     G.S = 0;
     TimingScope ts(s, KC_ATTN_ACTION, keys * Hh * 64 * 2 * es + 2.0 * B * H * Hh * 64 * es,
                    4.0 * 64 * Hh * H * keys);
@@ -598,8 +598,9 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* 
                        G, (float*)out, 0.125f);
     return hipGetLastError();
   }
-  G.kc_chunk = action_chunk(B, Hh, max_len, splits_hint);
-  G.S = (G.kc_chunk > 0 ? (max_len + G.kc_chunk - 1) / G.kc_chunk : 0) + 1;
+  G.S = 1;
+  for (int b = 0; b < B; b++)
+    if (G.kc[b] > 0) G.S = std::max(G.S, (G.lens.len[b] + G.kc[b] - 1) / G.kc[b] + 1);
   if (scratch_bytes < (size_t)B * Hh * G.S * H * 66 * sizeof(float)) return hipErrorInvalidValue;
   {
     TimingScope ts(s, KC_ATTN_ACTION, keys * Hh * 64 * 2 * es + 1.0 * B * H * Hh * 64 * es,

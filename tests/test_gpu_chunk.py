@@ -1,4 +1,6 @@
 """End-to-end parity of the HIP path (through the C-ABI) with the oracle."""
+import os
+
 import numpy as np
 import pytest
 
@@ -58,3 +60,119 @@ def test_small_ragged(dtype):
         k, v = gpu_cache_layer(dc, l, 0, T)
         assert rel_l2(k, ref["cache"][0][l][0].numpy()) <= (1e-5 if dtype == "f32" else 1e-2)
         assert rel_l2(v, ref["cache"][0][l][1].numpy()) <= (1e-5 if dtype == "f32" else 1e-2)
+
+
+def test_c0_one_shot_future_fp32():
+    # V = 0: future cached at video time 1 from the noise itself (Faster-WAM 3.1)
+    cfg = configs.get("C0", V=0)
+    inp = inputs.generate(cfg)
+    ref = _oracle(cfg, inp)
+    dc = _run_gpu(cfg, inp)
+    assert rel_l2(to_np(dc.actions), ref["actions"]) <= 1e-5
+    k, v = gpu_cache_layer(dc, 0, 0, cfg.tokens_valid)
+    assert rel_l2(k, ref["cache"][0][0][0].numpy()) <= 1e-5
+
+
+@pytest.mark.parametrize("variant", ["no_future", "no_history"])
+def test_degenerate_frame_sets(variant):
+    # no future frames (observation-only cache, Fast-WAM infer_action); or every
+    # history frame padded (zero history keeps only the future/current frames)
+    if variant == "no_future":
+        cfg = configs.small("NF", dtype="f32", **dict(SMALL, Ff=0, frame_block=(0, 1, 2), V=0))
+    else:
+        cfg = configs.small("NH", dtype="f32", **dict(SMALL, pad_frames=3))
+    inp = inputs.generate(cfg)
+    ref = _oracle(cfg, inp)
+    dc = _run_gpu(cfg, inp)
+    assert rel_l2(to_np(dc.actions), ref["actions"]) <= 1e-5
+
+
+def test_determinism_and_padding_invariance():
+    import torch
+    cfg = configs.small("S", dtype="bf16", **SMALL)
+    inp = inputs.generate(cfg)
+    a = _run_gpu(cfg, inp)
+    b = _run_gpu(cfg, inp)
+    assert torch.equal(a.actions, b.actions)
+    assert torch.equal(a.cache.k[:, :, :, : cfg.tokens_valid], b.cache.k[:, :, :, : cfg.tokens_valid])
+    inp2 = dict(inp)
+    inp2["hist"] = inp["hist"].copy()
+    inp2["hist"][:, 0] = 7.0          # the padded frame
+    c = _run_gpu(cfg, inp2)
+    assert torch.equal(a.actions, c.actions)
+    inp3 = dict(inp)
+    inp3["eps_a"] = inp["eps_a"] * -1.0
+    d = _run_gpu(cfg, inp3)           # action noise never reaches the video cache
+    assert torch.equal(a.cache.k[:, :, :, : cfg.tokens_valid], d.cache.k[:, :, :, : cfg.tokens_valid])
+    assert not torch.equal(a.actions, d.actions)
+
+
+def test_batch_independence():
+    import torch
+    cfg2 = configs.small("B2", dtype="bf16", **dict(SMALL, B=2))
+    inp2 = inputs.generate(cfg2)
+    both = _run_gpu(cfg2, inp2)
+    for b in range(2):
+        one = {k: (v[b:b + 1] if k in ("hist", "hist_valid", "eps_v", "eps_a") else v)
+               for k, v in inp2.items()}
+        single = _run_gpu(configs.small("B1", dtype="bf16", **SMALL), one)
+        assert torch.equal(both.actions[b], single.actions[0])
+
+
+def test_sparse_one_hot_stride_one_equals_dense():
+    import torch
+    dense = configs.small("D", dtype="bf16", **dict(SMALL, V=0))
+    sparse = configs.small("Sp", dtype="bf16", **dict(SMALL, V=0, fuse=((0, 1), (1, 1))))
+    inp = inputs.generate(dense)
+    inp_s = dict(inp)
+    inp_s["fuse_logits"] = np.zeros((2, 1), dtype=np.float32)
+    assert torch.equal(_run_gpu(dense, inp).actions, _run_gpu(sparse, inp_s).actions)
+
+
+def test_sparse_mot_small_vs_oracle():
+    cfg = configs.small("SM", dtype="bf16", **dict(SMALL, L=4, V=0, read_map=(-1, 0, -1, 1),
+                                                      fuse=((0, 2), (2, 2))))
+    inp = inputs.generate(cfg)
+    ref = _oracle(cfg, inp)
+    dc = _run_gpu(cfg, inp)
+    assert rel_l2(to_np(dc.actions), ref["actions"]) <= 2e-2
+    for m in range(2):
+        k = to_np(dc.fused.k[m, 0, :, : cfg.tokens_valid]).transpose(1, 0, 2)
+        assert rel_l2(k, ref["fused"][0][m][0].numpy()) <= 1e-2
+
+
+# ---------------------------------------------------------------- full size
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4"])
+def test_full_size_against_oracle_values(name):
+    import json
+    path = os.path.join(GOLDEN, f"{name}.json")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated (tests/golden/make_golden.py)")
+    g = json.load(open(path))
+    cfg = configs.get(name)
+    print_case(f"full size {name}")
+    inp = inputs.generate(cfg)
+    assert inputs.fingerprint(inp) == g["fingerprint"]
+    dc = _run_gpu(cfg, inp)
+    err = rel_l2(to_np(dc.actions), np.array(g["actions"]))
+    print_case(f"{name} final actions rel-L2 {err:.3e}")
+    assert err <= 2e-2
+    rows, heads = np.array(g["sample_rows"]), np.array(g["sample_heads"])
+    for b in range(cfg.B):
+        for l in g["sample_layers"]:
+            ent = g["cache"][b][str(l)]
+            k = to_np(dc.cache.k[l, b])[heads, rows]
+            v = to_np(dc.cache.v[l, b]).transpose(0, 2, 1)[heads, rows]
+            assert rel_l2(k, np.array(ent["k"])) <= 1e-2
+            assert rel_l2(v, np.array(ent["v"])) <= 1e-2
+        if g["fused"]:
+            for m, ent in g["fused"][b].items():
+                k = to_np(dc.fused.k[int(m), b])[heads, rows]
+                assert rel_l2(k, np.array(ent["k"])) <= 1e-2
+    if g["z"] is not None:
+        zr = np.array(g["z_rows"])
+        z = to_np(dc.z).reshape(cfg.B, -1, cfg.Cv)[:, zr]
+        assert rel_l2(z, np.array(g["z"])) <= 1e-2

@@ -1,0 +1,264 @@
+"""Kernel-level parity of the HIP path (through the C-ABI) with the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from kv_cached_flow_amd import configs, inputs, wam
+from oracle import wam_oracle as O
+from tests._util import print_case, rel_l2, to_np
+
+pytestmark = pytest.mark.gpu
+
+f64 = torch.float64
+
+
+def _tdt(dt):
+    return torch.bfloat16 if dt == wam.WAM_BF16 else torch.float32
+
+
+def _rand(rng, shape, dt, scale=1.0):
+    a = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return inputs.round_bf16(a) if dt == wam.WAM_BF16 else a
+
+
+def _dev(a, dt):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda().to(_tdt(dt)).contiguous()
+
+
+# ---------------------------------------------------------------- visibility
+@pytest.mark.parametrize("case", [
+    ((0, 1, 2, 3, 4), (1, 1, 1), 3, 2, 5),
+    ((0, 1, 1, 1, 1, 1, 1, 1, 1), (1,), 1, 8, 3),
+    ((0, 0, 1, 2, 2, 3), (0, 1, 0, 1), 4, 2, 4),
+    ((0, 1, 2, 3), (0, 0, 1), 3, 1, 7),
+])
+def test_debug_visibility_matches_oracle(case):
+    blocks, valid, Fh, Ff, P = case
+    print_case(f"visibility {case}")
+    vis = wam.debug_visibility(blocks, valid, Fh, Ff, P).cpu().numpy().astype(bool)
+    F = Fh + Ff
+    fr = torch.arange(F).repeat_interleave(P)
+    fvalid = torch.tensor(list(valid) + [1] * Ff)
+    ref = O.video_visible(fr, fr, torch.tensor(blocks), fvalid).numpy()
+    qvalid = fvalid[fr].bool().numpy()
+    assert np.array_equal(vis[qvalid], ref[qvalid])
+    assert not vis[~qvalid].any()
+
+
+# ---------------------------------------------------------------- prefill attention
+@pytest.mark.parametrize("dt", [wam.WAM_F32, wam.WAM_BF16])
+@pytest.mark.parametrize("rows", [(0, 500), (100, 300), (400, 100)])
+def test_attention_prefill_vs_oracle(dt, rows):
+    row0, nq = rows
+    print_case(f"prefill attention dt={dt} rows={rows}")
+    rng = np.random.default_rng(1 + row0)
+    Hh, P, cap = 2, 100, 576
+    blocks = (0, 1, 1, 2, 3)
+    _, kend = wam.frame_table(blocks, None, 5, 0, P)
+    T = 5 * P
+    q = _rand(rng, (Hh, nq, 64), dt)
+    K = _rand(rng, (Hh, cap, 64), dt)
+    V = _rand(rng, (Hh, cap, 64), dt)
+    K[:, T:] = np.nan   # rows past the last frame must never be read
+    V[:, T:] = np.nan
+    out = torch.empty((nq, Hh * 64), dtype=_tdt(dt), device="cuda")
+    wam.attention_prefill(dt, _dev(q, dt), row0, P, kend, _dev(K, dt),
+                          _dev(np.ascontiguousarray(V.transpose(0, 2, 1)), dt), cap, out)
+    torch.cuda.synchronize()
+    qrow = np.arange(row0, row0 + nq)
+    mask = torch.tensor(np.arange(T)[None, :] < kend[qrow // P][:, None])
+    ref = O.attention(torch.tensor(q, dtype=f64).permute(1, 0, 2), torch.tensor(K[:, :T], dtype=f64).permute(1, 0, 2),
+                      torch.tensor(V[:, :T], dtype=f64).permute(1, 0, 2), lambda a, b: mask[a:b])
+    got = to_np(out).reshape(nq, Hh, 64)
+    assert np.isfinite(got).all()
+    assert rel_l2(got, ref.numpy()) <= (1e-5 if dt == wam.WAM_F32 else 5e-3)
+
+
+# ---------------------------------------------------------------- action attention
+def _action_case(rng, dt, B, Hh, lens, n_act, cap=None):
+    H = 32
+    cap = cap or (max(lens) + 63) // 64 * 64 if lens else 64
+    q = _rand(rng, (B, Hh, H, 64), dt)
+    ka = _rand(rng, (B, Hh, H, 64), dt)
+    va = _rand(rng, (B, Hh, H, 64), dt)
+    K = _rand(rng, (B, Hh, cap, 64), dt)
+    V = _rand(rng, (B, Hh, cap, 64), dt)
+    for b, n in enumerate(lens):
+        K[b, :, n:] = np.nan
+        V[b, :, n:] = np.nan
+    return q, ka, va, K, V, cap
+
+
+def _action_ref(q, ka, va, K, V, lens, n_act, with_cache=True):
+    B = q.shape[0]
+    outs = []
+    for b in range(B):
+        ks, vs = [], []
+        if with_cache:
+            ks.append(K[b][:, : lens[b]])
+            vs.append(V[b][:, : lens[b]])
+        if n_act:
+            ks.append(ka[b][:, :n_act])
+            vs.append(va[b][:, :n_act])
+        kk = torch.tensor(np.concatenate(ks, axis=1), dtype=f64).permute(1, 0, 2)
+        vv = torch.tensor(np.concatenate(vs, axis=1), dtype=f64).permute(1, 0, 2)
+        outs.append(O.attention(torch.tensor(q[b], dtype=f64).permute(1, 0, 2), kk, vv).numpy())
+    return np.stack(outs)  # [B, 32, Hh, 64]
+
+
+def _run_action(dt, q, ka, va, n_act, K, V, cap, lens, splits=0, with_cache=True):
+    B, Hh = q.shape[:2]
+    out = torch.empty((B, 32, Hh * 64), dtype=_tdt(dt), device="cuda")
+    vt = lambda a: _dev(np.ascontiguousarray(a.transpose(0, 1, 3, 2)), dt)
+    wam.attention_action(dt, _dev(q, dt), _dev(ka, dt) if n_act else None, vt(va) if n_act else None,
+                         n_act, _dev(K, dt) if with_cache else None, vt(V) if with_cache else None,
+                         cap, lens if with_cache else None, out, splits)
+    torch.cuda.synchronize()
+    return to_np(out).reshape(B, 32, Hh, 64)
+
+
+@pytest.mark.parametrize("dt", [wam.WAM_F32, wam.WAM_BF16])
+def test_attention_action_single_key_is_value_exactly(dt):
+    rng = np.random.default_rng(3)
+    q, ka, va, K, V, cap = _action_case(rng, dt, 2, 3, [1, 1], 0)
+    got = _run_action(dt, q, ka, va, 0, K, V, cap, [1, 1])
+    want = np.broadcast_to(V[:, :, 0][:, None, :, :], got.shape)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dt", [wam.WAM_F32, wam.WAM_BF16])
+def test_attention_action_zero_query_is_mean(dt):
+    rng = np.random.default_rng(4)
+    q, ka, va, K, V, cap = _action_case(rng, dt, 1, 2, [256], 0)
+    q[:] = 0
+    got = _run_action(dt, q, ka, va, 0, K, V, cap, [256])
+    want = V[0, :, :256].astype(np.float64).mean(axis=1)  # [Hh, 64]
+    assert rel_l2(got[0], np.broadcast_to(want[None], got[0].shape)) <= (1e-6 if dt == wam.WAM_F32 else 4e-3)
+
+
+@pytest.mark.parametrize("shape", [
+    ("C1-like", 1, 16, [9216], 32),
+    ("C4-like", 4, 16, [27280] * 4, 32),
+    ("ragged", 3, 4, [100, 3000, 777], 32),
+    ("no-own", 2, 4, [513, 64], 0),
+])
+def test_attention_action_vs_oracle(shape):
+    name, B, Hh, lens, n_act = shape
+    print_case(f"action attention {name}")
+    dt = wam.WAM_BF16
+    rng = np.random.default_rng(5)
+    q, ka, va, K, V, cap = _action_case(rng, dt, B, Hh, lens, n_act)
+    got = _run_action(dt, q, ka, va, n_act, K, V, cap, lens)
+    ref = _action_ref(q, ka, va, K, V, lens, n_act)
+    assert rel_l2(got, ref) <= 5e-3
+
+
+def test_attention_action_only_own_keys():
+    dt = wam.WAM_BF16
+    rng = np.random.default_rng(6)
+    q, ka, va, K, V, cap = _action_case(rng, dt, 2, 4, [64, 64], 32)
+    got = _run_action(dt, q, ka, va, 32, K, V, cap, [64, 64], with_cache=False)
+    ref = _action_ref(q, ka, va, K, V, [0, 0], 32, with_cache=False)
+    assert rel_l2(got, ref) <= 5e-3
+
+
+def test_attention_action_split_invariance_and_determinism():
+    dt = wam.WAM_BF16
+    rng = np.random.default_rng(7)
+    lens = [5000, 4097]
+    q, ka, va, K, V, cap = _action_case(rng, dt, 2, 4, lens, 32)
+    ref = _action_ref(q, ka, va, K, V, lens, 32)
+    outs = {}
+    for splits in (1, 2, 7, 64):
+        outs[splits] = _run_action(dt, q, ka, va, 32, K, V, cap, lens, splits)
+        again = _run_action(dt, q, ka, va, 32, K, V, cap, lens, splits)
+        assert np.array_equal(outs[splits], again)      # bitwise run-to-run
+        assert rel_l2(outs[splits], ref) <= 5e-3
+    # the plans differ only in fp32 summation order: at most one bf16 ulp apart
+    for s in (2, 7, 64):
+        a, b = outs[s], outs[1]
+        assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-30)
+
+
+# ---------------------------------------------------------------- fusion
+def _kv_random(rng, n_layers, B, Hh, cap, dt):
+    kv = wam.DeviceKV(n_layers, B, Hh, 64, cap, dt)
+    kv.k.copy_(torch.from_numpy(_rand(rng, tuple(kv.k.shape), dt)))
+    kv.v.copy_(torch.from_numpy(_rand(rng, tuple(kv.v.shape), dt)))
+    kv.len[:] = cap
+    return kv
+
+
+@pytest.mark.parametrize("dt", [wam.WAM_F32, wam.WAM_BF16])
+def test_fuse_one_hot_is_exact_layer(dt):
+    rng = np.random.default_rng(8)
+    src = _kv_random(rng, 8, 2, 4, 128, dt)
+    dst = wam.DeviceKV(2, 2, 4, 64, 128, dt)
+    logits = np.full((2, 4), -np.inf, np.float32)
+    logits[0, 1] = 0.0
+    logits[1, 3] = 2.0
+    wam.fuse_interval_kv(src, [0, 4], [4, 4], logits, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.k[0], src.k[1]) and torch.equal(dst.v[0], src.v[1])
+    assert torch.equal(dst.k[1], src.k[7]) and torch.equal(dst.v[1], src.v[7])
+    assert list(dst.len) == [128, 128]
+
+
+def test_fuse_vs_oracle():
+    dt = wam.WAM_BF16
+    rng = np.random.default_rng(9)
+    src = _kv_random(rng, 30, 1, 4, 192, dt)
+    read_map, fuse = configs.sparse_mot_tables(30, 4)
+    logits = rng.standard_normal((8, 4)).astype(np.float32)
+    dst = wam.DeviceKV(8, 1, 4, 64, 192, dt)
+    wam.fuse_interval_kv(src, [s for s, _ in fuse], [c for _, c in fuse], logits, dst)
+    torch.cuda.synchronize()
+    layers = [(src.k[l].double().cpu(), src.v[l].double().cpu()) for l in range(30)]
+    ref = O.fuse_interval(layers, fuse, logits)
+    for m in range(8):
+        assert rel_l2(to_np(dst.k[m]), ref[m][0].numpy()) <= 4e-3
+        assert rel_l2(to_np(dst.v[m]), ref[m][1].numpy()) <= 4e-3
+
+
+# ---------------------------------------------------------------- Euler
+def test_flow_euler_step():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal(100003).astype(np.float32)
+    v = rng.standard_normal(100003).astype(np.float32)
+    xd, vd = torch.from_numpy(x).cuda(), torch.from_numpy(v).cuda()
+    s, sn = np.float32(0.925), np.float32(0.9)
+    wam.flow_euler_step(xd, vd, float(s), float(sn))
+    torch.cuda.synchronize()
+    ref = x.astype(np.float64) + (np.float64(sn) - np.float64(s)) * v.astype(np.float64)
+    got = xd.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 2 * np.finfo(np.float32).eps * np.maximum(np.abs(ref), 1e-30) + 1e-30)
+
+
+# ---------------------------------------------------------------- one action layer
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_action_layer_vs_oracle(dtype):
+    from kv_cached_flow_amd.runner import upload_expert
+    cfg = configs.small("AL", dtype=dtype, L=1, B=2, read_map=(0,))
+    print_case(f"action layer {dtype}")
+    dt = wam.WAM_BF16 if dtype == "bf16" else wam.WAM_F32
+    w = inputs.expert_weights(cfg, "action")
+    ex = upload_expert(w, cfg)
+    rng = np.random.default_rng(11)
+    lens = [300, 200]
+    kv = wam.DeviceKV(1, 2, cfg.Hh, 64, 320, dt)
+    Kc = _rand(rng, (2, cfg.Hh, 320, 64), dt)
+    Vc = _rand(rng, (2, cfg.Hh, 320, 64), dt)
+    kv.k[0].copy_(torch.from_numpy(Kc))
+    kv.v[0].copy_(torch.from_numpy(np.ascontiguousarray(Vc.transpose(0, 1, 3, 2))))
+    kv.len[:] = lens
+    x = rng.standard_normal((2, 32, cfg.D)).astype(np.float32)
+    xd = torch.from_numpy(x).cuda()
+    d = wam.dims(1, cfg.D, cfg.Hh, 64, cfg.Fm, cfg.Cv, cfg.A, 32, cfg.P, dt)
+    wam.action_layer(d, ex, 0, xd, kv, 0, 2)
+    torch.cuda.synchronize()
+    lw = O.to_torch_expert(w, f64)["layers"][0]
+    for b in range(2):
+        ctx = (torch.tensor(Kc[b][:, : lens[b]], dtype=f64).permute(1, 0, 2),
+               torch.tensor(Vc[b][:, : lens[b]], dtype=f64).permute(1, 0, 2))
+        ref, _, _ = O.layer(torch.tensor(x[b], dtype=f64), lw, cfg.Hh, ctx, None)
+        assert rel_l2(xd[b].cpu().numpy(), ref.numpy()) <= (1e-5 if dtype == "f32" else 2e-2)

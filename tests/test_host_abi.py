@@ -1,0 +1,219 @@
+"""Host-side tests of libwam (no GPU): exports, schedules, frame tables and
+argument validation.  Every call here returns before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cached_flow_amd import wam
+from oracle import wam_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wam.h")
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(wam_\w+)\s*\(", txt, re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = wam.lib()
+    names = header_functions()
+    assert len(names) == 18
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(wam.exported_names()) == names
+    assert wam.abi_version() == 1
+
+
+def test_status_strings():
+    L = wam.lib()
+    for code in range(0, -7, -1):
+        assert L.wam_status_str(code).decode()
+    assert L.wam_status_str(-99).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("steps", [1, 2, 3, 4, 7, 10, 32])
+@pytest.mark.parametrize("sigma_end", [0.0, 0.9, 0.5, 0.123])
+@pytest.mark.parametrize("shift", [1.0, 3.0, 0.7])
+def test_schedule_bit_exact_with_oracle(steps, sigma_end, shift):
+    got = wam.schedule(steps, sigma_end, shift)
+    ref = O.schedule(steps, sigma_end, shift)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def _brute(frames, block, valid, P):
+    fr = torch.tensor(frames).repeat_interleave(P)
+    return O.video_visible(fr, fr, torch.tensor(block), torch.tensor(valid)).numpy()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_frame_table_matches_oracle_mask(seed):
+    r = np.random.default_rng(seed)
+    Fh, Ff, P = int(r.integers(0, 6)), int(r.integers(0, 3)), int(r.integers(1, 5))
+    if Fh + Ff == 0:
+        Fh = 1
+    F = Fh + Ff
+    block = np.sort(r.integers(0, F + 1, F)).astype(np.int32)
+    valid = (r.uniform(size=Fh) < 0.7).astype(np.uint8)
+    src, kend = wam.frame_table(block, valid, Fh, Ff, P)
+    keep = [f for f in range(Fh) if valid[f]] + list(range(Fh, F))
+    assert list(src) == keep
+    # visibility implied by the table (row i sees rows < kend[i // P]) == oracle on kept frames
+    n = len(keep) * P
+    vis = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        vis[i, : kend[i // P]] = True
+    fvalid = np.concatenate([valid, np.ones(Ff, np.uint8)]).astype(np.int64)
+    assert np.array_equal(vis, _brute(keep, block, fvalid, P))
+
+
+def test_frame_table_rejects_non_monotone_blocks():
+    with pytest.raises(wam.WamError, match="non-decreasing"):
+        wam.frame_table([0, 2, 1], None, 3, 0, 4)
+
+
+# ---------------------------------------------------------------- validation
+FAKE = 0x100000  # aligned, never dereferenced: validation returns first
+
+
+def good_dims(**kw):
+    d = dict(L=2, D=256, Hh=4, dh=64, Fm=512, Cv=64, A=14, H=32, P=100, dtype=wam.WAM_BF16)
+    d.update(kw)
+    return wam.dims(**d)
+
+
+class FakeExpert:
+    def __init__(self, L, ptr=FAKE):
+        self.larr = (wam.WamLayerW * L)(*[wam.WamLayerW(*([ptr] * 6)) for _ in range(L)])
+        self.c = wam.WamExpertW(ptr, ptr, ptr, C.cast(self.larr, C.POINTER(wam.WamLayerW)), L)
+
+
+def fake_kv(n_layers=2, B=1, Hh=4, cap=512, dtype=wam.WAM_BF16, lens=None):
+    ln = np.asarray(lens if lens is not None else [cap] * B, dtype=np.int32)
+    kv = wam.WamKV(FAKE, FAKE, n_layers, B, Hh, 64, cap, dtype, ln.ctypes.data_as(C.POINTER(C.c_int32)))
+    return kv, ln
+
+
+def call_prefill(d=None, expert=None, hist=FAKE, valid=None, B=1, Fh=3, fut=FAKE, Ff=2,
+                 blocks=(0, 1, 2, 3, 4), V=2, sigma=0.9, shift=1.0, kv=None, ws=FAKE, ws_bytes=1 << 40):
+    L = wam.lib()
+    d = d or good_dims()
+    ex = expert or FakeExpert(d.L)
+    if kv is None:
+        kv, _keep = fake_kv(cap=512)
+    fb = np.asarray(blocks, dtype=np.int32)
+    va = None if valid is None else np.ascontiguousarray(valid, dtype=np.uint8)
+    st = L.wam_prefill_video_cache(C.byref(d), C.byref(ex.c), hist, None if va is None else va.ctypes.data,
+                                   B, Fh, fut, Ff, fb.ctypes.data, V, sigma, shift, C.byref(kv), None,
+                                   ws, ws_bytes, None)
+    return st, L.wam_last_error().decode()
+
+
+def test_prefill_validation_errors():
+    assert call_prefill(d=good_dims(dh=32))[0] == -2
+    assert call_prefill(d=good_dims(D=512))[0] == -2          # D != Hh*dh
+    assert call_prefill(d=good_dims(H=16))[0] == -2
+    assert call_prefill(d=good_dims(dtype=7))[0] == -1
+    assert call_prefill(d=good_dims(Cv=65))[0] == -2
+    assert call_prefill(blocks=(0, 2, 1, 3, 4))[0] == -2      # non-monotone
+    assert call_prefill(V=2, sigma=1.0)[0] == -1              # sigma* must be < 1
+    assert call_prefill(V=-1)[0] == -1
+    assert call_prefill(hist=FAKE + 4)[0] == -4               # misaligned
+    assert call_prefill(ws=None)[0] == -5
+    assert call_prefill(ws_bytes=1024)[0] == -5
+    st, msg = call_prefill(expert=FakeExpert(1))
+    assert st == -2 and "layers" in msg
+    kv, _k = fake_kv(cap=500)
+    assert call_prefill(kv=kv)[0] == -2                       # cap not a multiple of 64
+    kv, _k = fake_kv(cap=256)
+    st, msg = call_prefill(kv=kv)                             # needs 4 frames x 100 rows
+    assert st == -2 and "cap" in msg
+    kv, _k = fake_kv(cap=512)
+    st, msg = call_prefill(Ff=0, blocks=(0, 1, 2), valid=np.zeros((1, 3)), kv=kv)
+    assert st == -2 and "no valid frame" in msg
+
+
+def call_denoise(d=None, expert=None, kv=None, read_map=(0, 1), eps=FAKE, B=1, N=4, shift=1.0,
+                 out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    L = wam.lib()
+    d = d or good_dims()
+    ex = expert or FakeExpert(d.L)
+    rm = np.asarray(read_map, dtype=np.int32)
+    kvp = C.byref(kv) if kv is not None else None
+    return L.wam_denoise_chunk(C.byref(d), C.byref(ex.c), kvp, rm.ctypes.data, eps, B, N, shift, out,
+                               None, ws, ws_bytes, None)
+
+
+def test_denoise_validation_errors():
+    kv, _k = fake_kv()
+    assert call_denoise(kv=kv, N=0) == -1
+    assert call_denoise(kv=kv, N=65) == -1
+    assert call_denoise(kv=kv, B=0) == -2
+    assert call_denoise(kv=kv, eps=FAKE + 8) == -4
+    assert call_denoise(kv=None) == -1                        # reads a cache, none given
+    assert call_denoise(kv=kv, read_map=(0, 5)) == -1          # layer 5 does not exist
+    kv2, _k2 = fake_kv(dtype=wam.WAM_F32)
+    assert call_denoise(kv=kv2) == -3                          # dtype mismatch
+    kv3, _k3 = fake_kv(lens=[600], cap=512)
+    assert call_denoise(kv=kv3) == -2                          # len > cap
+    assert call_denoise(kv=kv, ws_bytes=4096) == -5
+    assert call_denoise(kv=kv, shift=0.0) == -1
+
+
+def test_fuse_validation_errors():
+    L = wam.lib()
+    src, _a = fake_kv(n_layers=8)
+    dst, _b = fake_kv(n_layers=2)
+
+    def fuse(start, count, logits, M=None):
+        s = np.asarray(start, np.int32)
+        c = np.asarray(count, np.int32)
+        lg = np.ascontiguousarray(logits, np.float32)
+        return L.wam_fuse_interval_kv(C.byref(src), M or len(s), s.ctypes.data, c.ctypes.data,
+                                      lg.ctypes.data, lg.shape[1], C.byref(dst), None)
+
+    assert fuse([0, 4], [4, 4], np.full((2, 4), -np.inf)) == -1       # all -inf
+    assert fuse([0, 6], [4, 4], np.zeros((2, 4))) == -2               # past the last layer
+    assert fuse([0], [9], np.zeros((1, 9))) == -2                     # interval too long
+    assert fuse([0, 4, 0], [4, 4, 1], np.zeros((3, 4))) == -2         # dst too small
+
+
+def test_attention_entry_validation():
+    L = wam.lib()
+    ln = np.array([100], np.int32)
+    st = L.wam_attention_action(wam.WAM_BF16, 1, 4, 64, 16, FAKE, FAKE, FAKE, 16, FAKE, FAKE, 128,
+                                ln.ctypes.data, FAKE, 0, FAKE, 1 << 30, None)
+    assert st == -2                                            # H must be 32
+    st = L.wam_attention_action(wam.WAM_BF16, 1, 4, 64, 32, FAKE, None, None, 0, None, None, 0,
+                                None, FAKE, 0, FAKE, 1 << 30, None)
+    assert st == -2                                            # no key at all
+    ke = np.array([100, 200], np.int32)
+    st = L.wam_attention_prefill(wam.WAM_BF16, 4, 64, 300, 0, 100, ke.ctypes.data, 2, FAKE, FAKE,
+                                 FAKE, 256, FAKE, None)
+    assert st == -2                                            # rows beyond the table
+    ke = np.array([200, 100], np.int32)
+    st = L.wam_attention_prefill(wam.WAM_BF16, 4, 64, 150, 0, 100, ke.ctypes.data, 2, FAKE, FAKE,
+                                 FAKE, 256, FAKE, None)
+    assert st == -2                                            # kend not monotone
+
+
+def test_workspace_sizes_grow_with_shapes():
+    d = good_dims()
+    small = wam.prefill_workspace_bytes(d, 1, 3, 2)
+    big = wam.prefill_workspace_bytes(good_dims(P=1000), 1, 3, 2)
+    assert 0 < small < big
+    kv, _k = fake_kv(cap=512)
+    kvb, _kb = fake_kv(cap=8192, lens=[8192])
+    a = wam.lib().wam_denoise_workspace_bytes(C.byref(d), 1, C.byref(kv))
+    b = wam.lib().wam_denoise_workspace_bytes(C.byref(d), 1, C.byref(kvb))
+    assert 0 < a <= b
+
+
+def test_euler_rejects_negative_count():
+    assert wam.lib().wam_flow_euler_step(FAKE, FAKE, -1, 1.0, 0.5, None) == -1
+    assert wam.lib().wam_flow_euler_step(FAKE, FAKE, 0, 1.0, 0.5, None) == 0
