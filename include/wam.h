@@ -229,8 +229,8 @@ int wam_debug_visibility(const int32_t* frame_block, const uint8_t* valid, int F
  * Action attention: q [B][Hh][H][dh], ka [B][Hh][H][dh], va [B][Hh][dh][H]
  * (the chunk's own keys; NULL with n_act = 0 to leave them out), cache layer
  * kc [B][Hh][cap][dh], vc [B][Hh][dh][cap] with len[b] (host) rows, or
- * kc = vc = NULL.  out [B][H][Hh*dh] dtype.  splits_hint > 0 forces the
- * number of key splits per (episode, head) (0 = automatic).
+ * kc = vc = NULL.  out [B][H][Hh*dh] dtype.  splits_hint in 1..63 forces
+ * the number of cache-key splits per (episode, head) (0 = automatic).
  * ws: wam_action_workspace_bytes of a matching dims. */
 int wam_attention_action(int dtype, int B, int Hh, int dh, int H, const void* q,
                          const void* ka, const void* va, int n_act,

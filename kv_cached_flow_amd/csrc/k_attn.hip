@@ -38,16 +38,86 @@ __device__ inline float wave_sum16x4(float v) {
   return v;
 }
 
-__device__ inline bf16x8 pack8(const float* p) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; i++) r[i] = (short)f2bf(p[i]);
-  return r;
-}
-
 // key index (0..63) inside a 64-key tile of S^T subtile `sub` (0..3), row r (0..15)
 __device__ inline int perm_key(int sub, int r) {
   return 32 * (sub >> 1) + 8 * (r >> 2) + (r & 3) + 4 * (sub & 1);
+}
+// inverse: the (sub, r) slot 16*sub + r that holds key k of the tile
+__device__ inline int key_slot(int k) {
+  const int j = k & 31;
+  return 16 * (2 * (k >> 5) + ((j >> 2) & 1)) + 4 * (j >> 3) + (j & 3);
+}
+
+// Running softmax state of one wave: 32 queries (two 16-column tiles); O^T
+// accumulators o[dh tile][q tile], row max m and lane-partial row sum l (in
+// units of raw scores; exponentials use exp2 with the scale sl2 folded in).
+struct WaveAcc {
+  floatx4 o[4][2];
+  float m[2], l[2];
+};
+
+__device__ inline void acc_init(WaveAcc& a) {
+#pragma unroll
+  for (int d = 0; d < 4; d++)
+#pragma unroll
+    for (int t = 0; t < 2; t++) a.o[d][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  a.m[0] = a.m[1] = -INFINITY;
+  a.l[0] = a.l[1] = 0.f;
+}
+
+// One 64-key tile: online softmax of the raw scores sacc (S^T, permuted key
+// rows), then O^T += V^T P^T with the V^T operands from vop(d, wd).
+// MASK: keys kbase + index >= kq[t] get probability 0.
+template <bool MASK, typename VOp>
+__device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], int kbase, const int (&kq)[2],
+                                   float sl2, int g, VOp vop) {
+  bf16x8 pf[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 4; sub++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        if (MASK && kbase + 32 * (sub >> 1) + 8 * g + 4 * (sub & 1) + r >= kq[t])
+          sacc[sub][t][r] = -INFINITY;
+        mx = fmaxf(mx, sacc[sub][t][r]);
+      }
+    mx = wave_max16x4(mx);
+    const float mnew = fmaxf(a.m[t], mx);
+    const float alpha = __builtin_amdgcn_exp2f((a.m[t] - mnew) * sl2);
+    a.m[t] = mnew;
+    const float mc = mnew * sl2;
+    float p[4][4], ls = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 4; sub++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        p[sub][r] = __builtin_amdgcn_exp2f(fmaf(sacc[sub][t][r], sl2, -mc));
+        ls += p[sub][r];
+      }
+    a.l[t] = fmaf(a.l[t], alpha, ls);
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int d = 0; d < 4; d++) a.o[d][t] *= alpha;
+    }
+#pragma unroll
+    for (int wd = 0; wd < 2; wd++) {
+      u32x4 u = {pack_bf16x2(p[2 * wd][0], p[2 * wd][1]), pack_bf16x2(p[2 * wd][2], p[2 * wd][3]),
+                 pack_bf16x2(p[2 * wd + 1][0], p[2 * wd + 1][1]),
+                 pack_bf16x2(p[2 * wd + 1][2], p[2 * wd + 1][3])};
+      pf[wd][t] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 4; d++)
+#pragma unroll
+    for (int wd = 0; wd < 2; wd++) {
+      const bf16x8 v = vop(d, wd);
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+        a.o[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pf[wd][t], a.o[d][t], 0, 0, 0);
+    }
 }
 
 // ====================================================================== prefill
@@ -57,16 +127,30 @@ constexpr int KT = 64;                        // keys per tile
 constexpr int LD = 64 + 8;                    // LDS row stride (bf16)
 }
 
-__global__ __launch_bounds__(256) void attn_prefill_kernel(
+// Workgroups are dealt round-robin to the 8 XCDs.  Give every XCD whole heads
+// (their K/V then stay in that XCD's L2) and start the longest (latest) query
+// tiles first.
+__device__ inline void prefill_block(int bid, int Hh, int ntq, int* h, int* qt) {
+  if ((Hh & 7) == 0) {
+    const int x = bid & 7, i = bid >> 3, hpx = Hh >> 3;
+    *h = x + 8 * (i % hpx);
+    *qt = ntq - 1 - i / hpx;
+  } else {
+    *h = bid % Hh;
+    *qt = ntq - 1 - bid / Hh;
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     bf16_t* __restrict__ out, int nq, int row0, int cap, int Hh, FrameTab tab, float sl2) {
   using namespace pf;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[KT * LD];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[64 * LD];
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * LD];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][64 * LD];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int h = blockIdx.y;
   const int ntq = (nq + QT - 1) / QT;
-  const int qt = ntq - 1 - blockIdx.x;  // heaviest (latest) query tiles first
+  int h, qt;
+  prefill_block(blockIdx.x, Hh, ntq, &h, &qt);
   const int q0 = qt * QT;
   const int qlast = min(q0 + QT, nq) - 1;
   const int kend_min = kend_of_row(tab, row0 + q0);
@@ -74,7 +158,6 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
   const bf16_t* kh = kc + (long long)h * cap * 64;
   const bf16_t* vh = vc + (long long)h * 64 * cap;
 
-  // this lane's two query columns and their key ends
   int kq[2];
   bf16x8 qf[2][2];
 #pragma unroll
@@ -83,137 +166,94 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     const bool ok = qi < nq;
     kq[t] = ok ? kend_of_row(tab, row0 + qi) : kend_max;
 #pragma unroll
-    for (int s = 0; s < 2; s++) {
-      if (ok)
-        qf[t][s] = *(const bf16x8*)(q + ((long long)h * nq + qi) * 64 + 32 * s + 8 * g);
-      else
-        qf[t][s] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    for (int s = 0; s < 2; s++)
+      qf[t][s] = ok ? *(const bf16x8*)(q + ((long long)h * nq + qi) * 64 + 32 * s + 8 * g)
+                    : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
-  floatx4 o[4][2];
-#pragma unroll
-  for (int d = 0; d < 4; d++)
-#pragma unroll
-    for (int t = 0; t < 2; t++) o[d][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  WaveAcc acc;
+  acc_init(acc);
 
-  // register staging of the next K / V^T tile (2 chunks of 16 B each per thread)
+  // staging of one K tile (token rows, stored at their S^T slot) and one V^T
+  // tile (head-dim rows): 2 x 16 B of each per thread
   u32x4 rk[2], rv[2];
+  int krow[2], kslot[2], ch8[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int c = tid + 256 * i;
+    krow[i] = c >> 3;
+    ch8[i] = (c & 7) * 8;
+    kslot[i] = key_slot(krow[i]);
+  }
   auto gload = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, ch = c & 7;
-      const int key = kt + row;
-      rk[i] = (key < kend_max) ? *(const u32x4*)(kh + (long long)key * 64 + ch * 8)
+      const int key = kt + krow[i];
+      rk[i] = (key < kend_max) ? *(const u32x4*)(kh + (long long)key * 64 + ch8[i])
                                : u32x4{0u, 0u, 0u, 0u};
-      const int k0 = kt + ch * 8;  // V^T: row = head dim, 8 keys
-      if (k0 + 8 <= kend_max) {
-        rv[i] = *(const u32x4*)(vh + (long long)row * cap + k0);
-      } else if (k0 < kend_max) {
-        u32x4 x = *(const u32x4*)(vh + (long long)row * cap + k0);
+      const int k0 = kt + ch8[i];
+      u32x4 x = u32x4{0u, 0u, 0u, 0u};
+      if (k0 < kend_max) x = *(const u32x4*)(vh + (long long)krow[i] * cap + k0);
+      if (k0 + 8 > kend_max) {
         bf16_t* e = (bf16_t*)&x;
 #pragma unroll
         for (int j = 0; j < 8; j++)
           if (k0 + j >= kend_max) e[j] = 0;
-        rv[i] = x;
-      } else {
-        rv[i] = u32x4{0u, 0u, 0u, 0u};
       }
+      rv[i] = x;
+    }
+  };
+  auto lstore = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      *(u32x4*)(&sK[b][kslot[i] * LD + ch8[i]]) = rk[i];
+      *(u32x4*)(&sV[b][krow[i] * LD + ch8[i]]) = rv[i];
     }
   };
 
   gload(0);
+  lstore(0);
+  __syncthreads();
+  int cur = 0;
   for (int kt = 0; kt < kend_max; kt += KT) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-      const int c = tid + 256 * i;
-      const int row = c >> 3, ch = c & 7;
-      *(u32x4*)(sK + row * LD + ch * 8) = rk[i];
-      *(u32x4*)(sV + row * LD + ch * 8) = rv[i];
-    }
-    __syncthreads();
-    if (kt + KT < kend_max) gload(kt + KT);
-
+    const bool nxt = kt + KT < kend_max;
+    if (nxt) gload(kt + KT);
     floatx4 sacc[4][2];
 #pragma unroll
     for (int sub = 0; sub < 4; sub++) {
 #pragma unroll
       for (int t = 0; t < 2; t++) sacc[sub][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int kr = perm_key(sub, c16);
 #pragma unroll
       for (int s = 0; s < 2; s++) {
-        bf16x8 a = *(const bf16x8*)(sK + kr * LD + 32 * s + 8 * g);
+        const bf16x8 a = *(const bf16x8*)(&sK[cur][(16 * sub + c16) * LD + 32 * s + 8 * g]);
 #pragma unroll
         for (int t = 0; t < 2; t++)
           sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[t][s], sacc[sub][t], 0, 0, 0);
       }
     }
-    const bool need_mask = (kt + KT > kend_min);
-    bf16x8 pf[2][2];  // [window][q tile]
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-      float sv[4][4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sub = 0; sub < 4; sub++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          float x = sacc[sub][t][r] * sl2;
-          if (need_mask) {
-            const int key = kt + 32 * (sub >> 1) + 8 * g + 4 * (sub & 1) + r;
-            if (key >= kq[t]) x = -INFINITY;
-          }
-          sv[sub][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = wave_max16x4(mx);
-      const float mnew = fmaxf(mrun[t], mx);
-      const float alpha = __builtin_amdgcn_exp2f(mrun[t] - mnew);
-      mrun[t] = mnew;
-      float ls = 0.f;
-      float p[4][4];
-#pragma unroll
-      for (int sub = 0; sub < 4; sub++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          p[sub][r] = __builtin_amdgcn_exp2f(sv[sub][r] - mnew);
-          ls += p[sub][r];
-        }
-      lrun[t] = lrun[t] * alpha + ls;
-#pragma unroll
-      for (int d = 0; d < 4; d++) o[d][t] *= alpha;
-#pragma unroll
-      for (int wd = 0; wd < 2; wd++) {
-        float pw[8] = {p[2 * wd][0], p[2 * wd][1], p[2 * wd][2], p[2 * wd][3],
-                       p[2 * wd + 1][0], p[2 * wd + 1][1], p[2 * wd + 1][2], p[2 * wd + 1][3]};
-        pf[wd][t] = pack8(pw);
-      }
-    }
-#pragma unroll
-    for (int d = 0; d < 4; d++)
-#pragma unroll
-      for (int wd = 0; wd < 2; wd++) {
-        bf16x8 a = *(const bf16x8*)(sV + (16 * d + c16) * LD + 32 * wd + 8 * g);
-#pragma unroll
-        for (int t = 0; t < 2; t++)
-          o[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[wd][t], o[d][t], 0, 0, 0);
-      }
+    const bf16_t* sv = sV[cur];
+    auto vop = [&](int d, int wd) {
+      return *(const bf16x8*)(sv + (16 * d + c16) * LD + 32 * wd + 8 * g);
+    };
+    if (kt + KT > kend_min)
+      tile_update<true>(acc, sacc, kt, kq, sl2, g, vop);
+    else
+      tile_update<false>(acc, sacc, kt, kq, sl2, g, vop);
+    if (nxt) lstore(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
   }
   const int D = Hh * 64;
 #pragma unroll
   for (int t = 0; t < 2; t++) {
-    const float l = wave_sum16x4(lrun[t]);
+    const float l = wave_sum16x4(acc.l[t]);
     const int qi = q0 + w * QW + 16 * t + c16;
     if (qi >= nq) continue;
     const float inv = 1.0f / l;
 #pragma unroll
     for (int d = 0; d < 4; d++) {
-      bf16_t v4[4];
-#pragma unroll
-      for (int r = 0; r < 4; r++) v4[r] = f2bf(o[d][t][r] * inv);
-      *(uint2*)(out + (long long)qi * D + h * 64 + 16 * d + 4 * g) = *(uint2*)v4;
+      uint2 v = {pack_bf16x2(acc.o[d][t][0] * inv, acc.o[d][t][1] * inv),
+                 pack_bf16x2(acc.o[d][t][2] * inv, acc.o[d][t][3] * inv)};
+      *(uint2*)(out + (long long)qi * D + h * 64 + 16 * d + 4 * g) = v;
     }
   }
 }
@@ -268,7 +308,7 @@ hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int nq, int row0, const F
   TimingScope ts(s, KC_ATTN_PREFILL, (double)Hh * 64 * es * (2.0 * nq + 2.0 * kmax),
                  4.0 * 64 * Hh * pairs);
   if (dt == WAM_BF16) {
-    dim3 grid((nq + pf::QT - 1) / pf::QT, Hh);
+    dim3 grid(((nq + pf::QT - 1) / pf::QT) * Hh);
     hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, (const bf16_t*)q,
                        (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)out, nq, row0, cap, Hh,
                        tab, 0.125f * LOG2E);
@@ -283,8 +323,9 @@ hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int nq, int row0, const F
 
 // ====================================================================== action
 namespace act {
-constexpr int H = 32;   // queries per (episode, head)
-constexpr int KT = 64;  // keys per wave tile
+constexpr int H = 32;            // queries per (episode, head)
+constexpr int KT = 64;           // keys per wave tile
+constexpr int MAX_SPLITS = 64;   // splits per (episode, head), own keys included
 }
 
 struct ActGeom {
@@ -335,13 +376,9 @@ __global__ __launch_bounds__(256) void attn_action_kernel(
     for (int ss = 0; ss < 2; ss++)
       qf[t][ss] = *(const bf16x8*)(qb + (16 * t + c16) * 64 + 32 * ss + 8 * g);
 
-  floatx4 o[4][2];
-#pragma unroll
-  for (int d = 0; d < 4; d++)
-#pragma unroll
-    for (int t = 0; t < 2; t++) o[d][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
-
+  WaveAcc acc;
+  acc_init(acc);
+  const int kq[2] = {key1, key1};
   for (int kt = key0 + w * KT; kt < key1; kt += 4 * KT) {
     // ---- loads: K rows (A of S^T) and V^T rows (A of P V), zero past key1
     bf16x8 ak[4][2], av[4][2];
@@ -358,18 +395,14 @@ __global__ __launch_bounds__(256) void attn_action_kernel(
 #pragma unroll
       for (int wd = 0; wd < 2; wd++) {
         const int k0 = kt + 32 * wd + 8 * g;
-        const bf16_t* src = vb + (long long)(16 * d + c16) * vld + k0;
-        if (k0 + 8 <= key1) {
-          av[d][wd] = *(const bf16x8*)src;
-        } else if (k0 < key1) {
-          bf16x8 x = *(const bf16x8*)src;
+        bf16x8 x = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (k0 < key1) x = *(const bf16x8*)(vb + (long long)(16 * d + c16) * vld + k0);
+        if (k0 + 8 > key1) {
 #pragma unroll
           for (int j = 0; j < 8; j++)
             if (k0 + j >= key1) x[j] = 0;
-          av[d][wd] = x;
-        } else {
-          av[d][wd] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
+        av[d][wd] = x;
       }
     // ---- S^T
     floatx4 sacc[4][2];
@@ -382,64 +415,25 @@ __global__ __launch_bounds__(256) void attn_action_kernel(
         for (int ss = 0; ss < 2; ss++)
           sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[sub][ss], qf[t][ss], sacc[sub][t], 0, 0, 0);
       }
-    const bool need_mask = (kt + KT > key1);
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-      float sv[4][4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sub = 0; sub < 4; sub++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          float x = sacc[sub][t][r] * sl2;
-          if (need_mask && kt + 32 * (sub >> 1) + 8 * g + 4 * (sub & 1) + r >= key1) x = -INFINITY;
-          sv[sub][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = wave_max16x4(mx);
-      const float mnew = fmaxf(mrun[t], mx);
-      const float alpha = __builtin_amdgcn_exp2f(mrun[t] - mnew);
-      mrun[t] = mnew;
-      float ls = 0.f, p[4][4];
-#pragma unroll
-      for (int sub = 0; sub < 4; sub++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          p[sub][r] = __builtin_amdgcn_exp2f(sv[sub][r] - mnew);
-          ls += p[sub][r];
-        }
-      lrun[t] = lrun[t] * alpha + ls;
-#pragma unroll
-      for (int d = 0; d < 4; d++) o[d][t] *= alpha;
-#pragma unroll
-      for (int wd = 0; wd < 2; wd++) {
-        float pw[8] = {p[2 * wd][0], p[2 * wd][1], p[2 * wd][2], p[2 * wd][3],
-                       p[2 * wd + 1][0], p[2 * wd + 1][1], p[2 * wd + 1][2], p[2 * wd + 1][3]};
-        pf[wd][t] = pack8(pw);
-      }
-    }
-#pragma unroll
-    for (int d = 0; d < 4; d++)
-#pragma unroll
-      for (int wd = 0; wd < 2; wd++)
-#pragma unroll
-        for (int t = 0; t < 2; t++)
-          o[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[d][wd], pf[wd][t], o[d][t], 0, 0, 0);
+    auto vop = [&](int d, int wd) { return av[d][wd]; };
+    if (kt + KT > key1)
+      tile_update<true>(acc, sacc, kt, kq, sl2, g, vop);
+    else
+      tile_update<false>(acc, sacc, kt, kq, sl2, g, vop);
   }
   // ---- per-wave state to LDS (waves without keys hold m = -inf, l = 0, o = 0)
 #pragma unroll
   for (int t = 0; t < 2; t++) {
-    const float l = wave_sum16x4(lrun[t]);
+    const float l = wave_sum16x4(acc.l[t]);
     const int qi = 16 * t + c16;
     if (g == 0) {
-      sm[w][qi] = mrun[t];
+      sm[w][qi] = acc.m[t];
       sl[w][qi] = l;
     }
 #pragma unroll
     for (int d = 0; d < 4; d++)
 #pragma unroll
-      for (int r = 0; r < 4; r++) so[w][qi][16 * d + 4 * g + r] = o[d][t][r];
+      for (int r = 0; r < 4; r++) so[w][qi][16 * d + 4 * g + r] = acc.o[d][t][r];
   }
   __syncthreads();
   // ---- merge the 4 waves in a fixed order, write the split's partial
@@ -455,43 +449,51 @@ __global__ __launch_bounds__(256) void attn_action_kernel(
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ww++) {
-      const float f = (sm[ww][qi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[ww][qi] - M);
+      const float f =
+          (sm[ww][qi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sm[ww][qi] - M) * sl2);
       L += sl[ww][qi] * f;
       O += so[ww][qi][d] * f;
     }
     po[qi * 64 + d] = O;
     if (d == 0) {
-      pm[qi] = M;
+      pm[qi] = M * sl2;  // log2 domain for the split merge
       pl[qi] = L;
     }
   }
 }
 
-// Merge splits 0..S_b-1 of (b, h) in order; out[b*32 + q][h*64 + d].
-// One wavefront per (query, head, episode); lane d owns one head dim.
+// Merge splits 0..ns-1 of (b, h) (ns <= 64): one wavefront per (query, head,
+// episode).  Lane j reads split j's (m, l); lane d reads every split's o[d];
+// all loads are issued before any arithmetic.  Fixed reduction order.
 template <typename TO>
 __global__ __launch_bounds__(64) void attn_action_merge_kernel(const float* __restrict__ part,
                                                                ActGeom G, TO* __restrict__ out) {
   using namespace act;
-  const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z, d = threadIdx.x;
+  const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   const int len = G.lens.len[b];
   const int ncs = G.kc[b] > 0 ? (len + G.kc[b] - 1) / G.kc[b] : 0;
   const int ns = ncs + (G.n_act > 0 ? 1 : 0);
   const long long base = ((long long)b * G.Hh + h) * G.S;
   const float* pm = part + base * H + qi;
   const float* pl = part + (long long)G.B * G.Hh * G.S * H + base * H + qi;
-  const float* po = part + 2ll * G.B * G.Hh * G.S * H + (base * H + qi) * 64 + d;
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int sp = 0; sp < ns; sp++) M = fmaxf(M, pm[sp * H]);
-  float L = 0.f, O = 0.f;
-#pragma unroll 8
-  for (int sp = 0; sp < ns; sp++) {
-    const float f = __builtin_amdgcn_exp2f(pm[sp * H] - M);
-    L = fmaf(pl[sp * H], f, L);
-    O = fmaf(po[(long long)sp * H * 64], f, O);
-  }
-  out[((long long)b * H + qi) * G.Hh * 64 + h * 64 + d] = from_f<TO>(O / L);
+  const float* po = part + 2ll * G.B * G.Hh * G.S * H + (base * H + qi) * 64 + lane;
+  const float mj = lane < ns ? pm[lane * H] : -INFINITY;
+  const float lj = lane < ns ? pl[lane * H] : 0.f;
+  float ov[MAX_SPLITS];
+#pragma unroll
+  for (int j = 0; j < MAX_SPLITS; j++) ov[j] = (j < ns) ? po[(long long)j * H * 64] : 0.f;
+  float M = mj;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  const float wj = lane < ns ? __builtin_amdgcn_exp2f(mj - M) : 0.f;
+  float L = lj * wj;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+  float O = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAX_SPLITS; j++)
+    if (j < ns) O = fmaf(__shfl(wj, j, 64), ov[j], O);
+  out[((long long)b * H + qi) * G.Hh * 64 + h * 64 + lane] = from_f<TO>(O / L);
 }
 
 // fp32: one thread per (episode, head, query)
@@ -545,31 +547,25 @@ __global__ __launch_bounds__(64) void attn_action_f32_kernel(const float* __rest
   for (int d = 0; d < 64; d++) orow[d] = o[d] * inv;
 }
 
-// Keys per split for one episode: a function of that episode's length and the
-// head count only, so an episode is split identically whatever the batch
-// (batch independence of the results is bitwise).
-static int action_chunk(int Hh, int len, int splits_hint) {
+// Keys per split for one episode: a function of that episode's length only,
+// so an episode is split identically whatever the batch (batch independence
+// is bitwise).  Whole 256-key groups (one 64-key tile per wave of the
+// workgroup), as few per split as keeps the split count within the merge's
+// limit; an explicit hint (tests) asks for a split count instead.
+static int action_chunk(int len, int splits_hint) {
   if (len <= 0) return 0;
-  int splits = splits_hint > 0 ? splits_hint : (512 + Hh - 1) / Hh;
-  int kc = (len + splits - 1) / splits;
-  kc = (kc + act::KT - 1) / act::KT * act::KT;
-  if (splits_hint <= 0 && kc < 4 * act::KT) kc = 4 * act::KT;
-  return kc;
+  if (splits_hint > 0) {
+    int kc = (len + splits_hint - 1) / splits_hint;
+    return (kc + act::KT - 1) / act::KT * act::KT;
+  }
+  const int group = 4 * act::KT;
+  const int per = (len + group * (act::MAX_SPLITS - 1) - 1) / (group * (act::MAX_SPLITS - 1));
+  return group * per;
 }
 
-// Upper bound of the split count for any length <= max_len (monotone in
-// max_len, so a workspace sized for a capacity fits every shorter cache).
 size_t attn_action_scratch_bytes(int B, int Hh, int H, int max_len, int splits_hint) {
-  int S = 1;
-  if (max_len > 0) {
-    if (splits_hint > 0) {
-      S = splits_hint + 1;
-    } else {
-      int splits = (512 + Hh - 1) / Hh;
-      S = std::min((max_len + 4 * act::KT - 1) / (4 * act::KT), splits + 1) + 1;
-    }
-  }
-  return (size_t)B * Hh * S * H * (64 + 2) * sizeof(float);
+  (void)splits_hint;
+  return (size_t)B * Hh * act::MAX_SPLITS * H * (64 + 2) * sizeof(float);
 }
 
 hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* q,
@@ -588,7 +584,8 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* 
   double keys = 0.0;
   for (int b = 0; b < B; b++) keys += (double)G.lens.len[b] + n_act;
   const int es = dt == WAM_BF16 ? 2 : 4;
-  for (int b = 0; b < B; b++) G.kc[b] = kc ? action_chunk(Hh, G.lens.len[b], splits_hint) : 0;
+  if (splits_hint >= act::MAX_SPLITS) return hipErrorInvalidValue;
+  for (int b = 0; b < B; b++) G.kc[b] = kc ? action_chunk(G.lens.len[b], splits_hint) : 0;
   if (dt == WAM_F32) {
     G.S = 0;
     TimingScope ts(s, KC_ATTN_ACTION, keys * Hh * 64 * 2 * es + 2.0 * B * H * Hh * 64 * es,

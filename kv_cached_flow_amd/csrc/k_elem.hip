@@ -60,14 +60,83 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x,
   }
 }
 
+// One workgroup per row (small M): thread t owns columns 4t..4t+3 (+1024 j);
+// all loads of a thread are issued before any reduction.
+template <typename TO, bool ACC>
+__global__ __launch_bounds__(256) void rmsnorm_row_kernel(float* __restrict__ x,
+                                                          const float* __restrict__ part, int KS,
+                                                          const float* __restrict__ g,
+                                                          TO* __restrict__ y, int M, int D) {
+  __shared__ float wss[4];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float* xr = x + (long long)row * D;
+  float4 v[2];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int i = 4 * tid + 1024 * j;
+    if (i < D) {
+      float4 t = *(const float4*)(xr + i);
+      if (ACC) {
+        float4 p[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+          if (k < KS) p[k] = *(const float4*)(part + ((long long)k * M + row) * D + i);
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+          if (k < KS) {
+            t.x += p[k].x;
+            t.y += p[k].y;
+            t.z += p[k].z;
+            t.w += p[k].w;
+          }
+        *(float4*)(xr + i) = t;
+      }
+      v[j] = t;
+      ss = fmaf(t.x, t.x, ss);
+      ss = fmaf(t.y, t.y, ss);
+      ss = fmaf(t.z, t.z, ss);
+      ss = fmaf(t.w, t.w, ss);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if (lane == 0) wss[w] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((((wss[0] + wss[1]) + wss[2]) + wss[3]) / (float)D + 1e-6f);
+  TO* yr = y + (long long)row * D;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int i = 4 * tid + 1024 * j;
+    if (i < D) {
+      const float4 gg = *(const float4*)(g + i);
+      TO o4[4] = {from_f<TO>(v[j].x * r * gg.x), from_f<TO>(v[j].y * r * gg.y),
+                  from_f<TO>(v[j].z * r * gg.z), from_f<TO>(v[j].w * r * gg.w)};
+      if constexpr (sizeof(TO) == 2)
+        *(uint2*)(yr + i) = *(uint2*)o4;
+      else
+        *(float4*)(yr + i) = *(float4*)o4;
+    }
+  }
+}
+
 template <bool ACC>
 static hipError_t rmsnorm_launch(hipStream_t s, int odt, float* x, const float* part, int KS,
                                  const float* g, void* y, int M, int D) {
   if (M <= 0) return hipSuccess;
-  if (D > 2048 || D % 4) return hipErrorInvalidValue;
-  dim3 grid((M + 3) / 4);
+  if (D > 2048 || D % 4 || KS > 4) return hipErrorInvalidValue;
   TimingScope ts(s, KC_RMSNORM,
                  (double)M * D * ((ACC ? 8 + 4 * KS : 4) + (odt == WAM_BF16 ? 2 : 4)), 0.0);
+  if (M <= 512) {  // latency bound: a workgroup per row
+    if (odt == WAM_BF16)
+      hipLaunchKernelGGL((rmsnorm_row_kernel<bf16_t, ACC>), dim3(M), dim3(256), 0, s, x, part, KS,
+                         g, (bf16_t*)y, M, D);
+    else
+      hipLaunchKernelGGL((rmsnorm_row_kernel<float, ACC>), dim3(M), dim3(256), 0, s, x, part, KS,
+                         g, (float*)y, M, D);
+    return hipGetLastError();
+  }
+  dim3 grid((M + 3) / 4);
   if (odt == WAM_BF16)
     hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, ACC>), grid, dim3(256), 0, s, x, part, KS, g,
                        (bf16_t*)y, M, D);
@@ -214,6 +283,110 @@ hipError_t fill_i32(hipStream_t s, int* p, int n, int v) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0,
                      s, p, n, v);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ step boundary
+// One workgroup per row m (D <= 2048, C <= 64):
+//   head:  y = RMSNorm(X[m]; g_out); v[n] = y . W_out[n] for n < C;
+//          z[m][n] += dt v[n]; vhat[m][n] = v[n]      (the flow update)
+//   next:  X[m][:] = z[m][:] W_in^T + emb_next[:]       (the next embedding)
+// Either part may be switched off (do_head = 0 / w_in = nullptr).
+template <typename TW>
+__global__ __launch_bounds__(256) void step_kernel(float* __restrict__ X,
+                                                   const float* __restrict__ g_out,
+                                                   const TW* __restrict__ w_out,
+                                                   float* __restrict__ z, float dt,
+                                                   float* __restrict__ vhat,
+                                                   const TW* __restrict__ w_in,
+                                                   const float* __restrict__ emb_next, int D, int C,
+                                                   int do_head) {
+  __shared__ float red[4][64];
+  __shared__ float wss[4];
+  __shared__ float zs[64];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float* xr = X + (long long)m * D;
+  float* zr = z + (long long)m * C;
+  if (do_head) {
+    float4 y[2];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int i = 4 * tid + 1024 * j;
+      y[j] = (i < D) ? *(const float4*)(xr + i) : float4{0.f, 0.f, 0.f, 0.f};
+      ss = fmaf(y[j].x, y[j].x, ss);
+      ss = fmaf(y[j].y, y[j].y, ss);
+      ss = fmaf(y[j].z, y[j].z, ss);
+      ss = fmaf(y[j].w, y[j].w, ss);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if (lane == 0) wss[w] = ss;
+    __syncthreads();
+    const float r = 1.0f / sqrtf((((wss[0] + wss[1]) + wss[2]) + wss[3]) / (float)D + 1e-6f);
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int i = 4 * tid + 1024 * j;
+      if (i < D) {
+        const float4 gg = *(const float4*)(g_out + i);
+        y[j].x *= r * gg.x;
+        y[j].y *= r * gg.y;
+        y[j].z *= r * gg.z;
+        y[j].w *= r * gg.w;
+      }
+    }
+    for (int n = 0; n < C; n++) {
+      float p = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int i = 4 * tid + 1024 * j;
+        if (i < D) {
+          const TW* wr = w_out + (long long)n * D + i;
+          p = fmaf(y[j].x, to_f<TW>(wr[0]), p);
+          p = fmaf(y[j].y, to_f<TW>(wr[1]), p);
+          p = fmaf(y[j].z, to_f<TW>(wr[2]), p);
+          p = fmaf(y[j].w, to_f<TW>(wr[3]), p);
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) p += __shfl_xor(p, o, 64);
+      if (lane == 0) red[w][n] = p;
+    }
+    __syncthreads();
+    if (tid < C) {
+      const float v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+      const float zn = fmaf(dt, v, zr[tid]);
+      zr[tid] = zn;
+      if (vhat) vhat[(long long)m * C + tid] = v;
+      zs[tid] = zn;
+    }
+  } else if (tid < C) {
+    zs[tid] = zr[tid];
+  }
+  if (w_in == nullptr) return;
+  __syncthreads();
+  for (int col = tid; col < D; col += 256) {
+    float acc = 0.f;
+    for (int c = 0; c < C; c++) acc = fmaf(zs[c], to_f<TW>(w_in[(long long)col * C + c]), acc);
+    xr[col] = acc + emb_next[col];
+  }
+}
+
+hipError_t step_boundary(hipStream_t s, int wdt, float* X, const float* g_out, const void* w_out,
+                         float* z, float dt, float* vhat, const void* w_in, const float* emb_next,
+                         int M, int D, int C, bool do_head) {
+  if (M <= 0) return hipSuccess;
+  if (D > 2048 || D % 4 || C > 64) return hipErrorInvalidValue;
+  TimingScope ts(s, KC_MISC,
+                 (double)M * ((do_head ? D * 4.0 + 2.0 * C * 4 : 0.0) + (w_in ? D * 4.0 : 0.0)),
+                 (double)M * ((do_head ? 2.0 * C * D : 0.0) + (w_in ? 2.0 * C * D : 0.0)));
+  if (wdt == WAM_BF16)
+    hipLaunchKernelGGL(step_kernel<bf16_t>, dim3(M), dim3(256), 0, s, X, g_out,
+                       (const bf16_t*)w_out, z, dt, vhat, (const bf16_t*)w_in, emb_next, D, C,
+                       do_head ? 1 : 0);
+  else
+    hipLaunchKernelGGL(step_kernel<float>, dim3(M), dim3(256), 0, s, X, g_out, (const float*)w_out,
+                       z, dt, vhat, (const float*)w_in, emb_next, D, C, do_head ? 1 : 0);
   return hipGetLastError();
 }
 

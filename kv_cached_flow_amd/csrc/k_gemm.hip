@@ -87,87 +87,201 @@ __device__ inline int swizzle_tile(int bid, int nb, int ntm, int ntn, int* tm, i
   return lid;
 }
 
+// Epilogue on 4 consecutive columns n..n+3 of row m (n % 4 == 0).
 template <int EPI, typename TO>
-__global__ __launch_bounds__(256) void gemm_big_kernel(const bf16_t* __restrict__ A, int lda,
-                                                       const bf16_t* __restrict__ B, int ldb,
-                                                       int M, int N, int K, EpiArgs e) {
+__device__ inline void epi_row4(const EpiArgs& e, int m, int n, float4 v) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
+    if (EPI == EPI_GELU) {
+      v.x = gelu_f(v.x);
+      v.y = gelu_f(v.y);
+      v.z = gelu_f(v.z);
+      v.w = gelu_f(v.w);
+    }
+    TO* p = (TO*)e.out + (long long)m * e.ldo + n;
+    if constexpr (sizeof(TO) == 2)
+      *(uint2*)p = uint2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+    else
+      *(float4*)p = v;
+  } else if constexpr (EPI == EPI_RESID) {
+    float4* p = (float4*)((float*)e.out + (long long)m * e.ldo + n);
+    float4 x = *p;
+    x.x += v.x;
+    x.y += v.y;
+    x.z += v.z;
+    x.w += v.w;
+    *p = x;
+  } else if constexpr (EPI == EPI_EULER) {
+    epi_store<EPI, TO>(e, m, n, v.x);
+    epi_store<EPI, TO>(e, m, n + 1, v.y);
+    epi_store<EPI, TO>(e, m, n + 2, v.z);
+    epi_store<EPI, TO>(e, m, n + 3, v.w);
+  } else {  // QKV, Q or K part: 4 consecutive head dims
+    const int nn = e.n_begin + n;
+    const int part = nn / e.D, c = nn - part * e.D;
+    const int h = c / e.dh, d = c - h * e.dh;
+    const int g = m / e.rpg, t = m - g * e.rpg;
+    TO* p = part == 0 ? (TO*)e.q + g * e.q_gs + h * e.q_hs + (long long)t * e.dh + d
+                      : (TO*)e.k + g * e.k_gs + h * e.k_hs + (long long)(e.k_row0 + t) * e.dh + d;
+    if constexpr (sizeof(TO) == 2)
+      *(uint2*)p = uint2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+    else
+      *(float4*)p = v;
+  }
+}
+
+// QKV V part: rows m..m+3 (all < M) of column n go to 4 consecutive tokens of V^T.
+template <typename TO>
+__device__ inline void epi_vt4(const EpiArgs& e, int m, int n, float4 v) {
+  const int nn = e.n_begin + n;
+  const int c = nn - 2 * e.D;
+  const int h = c / e.dh, d = c - h * e.dh;
+  const int g = m / e.rpg, t = m - g * e.rpg;
+  const long long off = g * e.v_gs + h * e.v_hs + (long long)d * e.v_ld + e.v_col0 + t;
+  TO* p = (TO*)e.v + off;
+  if (((e.v_col0 + t) & 3) == 0 && t + 3 < e.rpg) {
+    if constexpr (sizeof(TO) == 2)
+      *(uint2*)p = uint2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+    else
+      *(float4*)p = v;
+  } else {
+    epi_store<EPI_QKV, TO>(e, m, n, v.x);
+    epi_store<EPI_QKV, TO>(e, m + 1, n, v.y);
+    epi_store<EPI_QKV, TO>(e, m + 2, n, v.z);
+    epi_store<EPI_QKV, TO>(e, m + 3, n, v.w);
+  }
+}
+
+// BMT x 128 x 64 tiles (BMT = 128 or 256), 4 waves in a 2x2 grid, each
+// wave (BMT/2) x 64.  Operand tiles double buffered in LDS with one barrier
+// per k step; the C tile is transposed through LDS (64 rows of a wave at a
+// time) so that the epilogue issues 8/16-byte accesses.
+template <int BMT, int EPI, typename TO>
+__global__ __launch_bounds__(256, BMT == 128 ? 2 : 1) void gemm_big_kernel(
+    const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb, int M, int N,
+    int K, EpiArgs e) {
   using namespace big;
-  __shared__ __attribute__((aligned(16))) bf16_t sA[BM * LDS_LD];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[BN * LDS_LD];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int ntm = (M + BM - 1) / BM, ntn = N / BN;
+  constexpr int MI = BMT / 32;             // 16-row tiles per wave
+  constexpr int AOP = BMT * LDS_LD, BOP = BN * LDS_LD;
+  constexpr int AL = BMT / 32;             // 16-byte A chunks per thread per k step
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (AOP + BOP)];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int ntm = (M + BMT - 1) / BMT, ntn = N / BN;
   int tm, tn;
   swizzle_tile(blockIdx.x, gridDim.x, ntm, ntn, &tm, &tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BMT, n0 = tn * BN;
   const int wm = w >> 1, wn = w & 1;
 
-  floatx4 acc[4][4];
+  floatx4 acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < MI; i++)
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // global -> register staging: 4 chunks of 8 bf16 per operand per thread
-  u32x4 ra[4], rb[4];
+  u32x4 ra[AL], rb[4];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      int c = tid + 256 * r;
-      int row = c >> 3, ch = c & 7;
-      int gm = m0 + row;
-      if (gm < M)
-        ra[r] = *(const u32x4*)(A + (long long)gm * lda + k0 + ch * 8);
-      else
-        ra[r] = u32x4{0u, 0u, 0u, 0u};
-      rb[r] = *(const u32x4*)(B + (long long)(n0 + row) * ldb + k0 + ch * 8);
+    for (int r = 0; r < AL; r++) {
+      const int c = tid + 256 * r, row = c >> 3, ch = (c & 7) * 8;
+      const int gm = m0 + row;
+      ra[r] = gm < M ? *(const u32x4*)(A + (long long)gm * lda + k0 + ch) : u32x4{0u, 0u, 0u, 0u};
     }
-  };
-  auto lstore = [&]() {
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      int c = tid + 256 * r;
-      int row = c >> 3, ch = c & 7;
-      *(u32x4*)(sA + row * LDS_LD + ch * 8) = ra[r];
-      *(u32x4*)(sB + row * LDS_LD + ch * 8) = rb[r];
+      const int c = tid + 256 * r, row = c >> 3, ch = (c & 7) * 8;
+      rb[r] = *(const u32x4*)(B + (long long)(n0 + row) * ldb + k0 + ch);
+    }
+  };
+  auto lstore = [&](int b) {
+    bf16_t* sa = smem + b * (AOP + BOP);
+    bf16_t* sb = sa + AOP;
+#pragma unroll
+    for (int r = 0; r < AL; r++) {
+      const int c = tid + 256 * r;
+      *(u32x4*)(sa + (c >> 3) * LDS_LD + (c & 7) * 8) = ra[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int c = tid + 256 * r;
+      *(u32x4*)(sb + (c >> 3) * LDS_LD + (c & 7) * 8) = rb[r];
     }
   };
 
   gload(0);
+  lstore(0);
+  __syncthreads();
+  int cur = 0;
   for (int k0 = 0; k0 < K; k0 += BK) {
-    lstore();
-    __syncthreads();
-    if (k0 + BK < K) gload(k0 + BK);
+    const bool nxt = k0 + BK < K;
+    if (nxt) gload(k0 + BK);
+    const bf16_t* sa = smem + cur * (AOP + BOP);
+    const bf16_t* sb = sa + AOP;
 #pragma unroll
     for (int s = 0; s < 2; s++) {
-      bf16x8 af[4], bfr[4];
-      const int kk = s * 32 + 8 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-        af[i] = *(const bf16x8*)(sA + (wm * 64 + i * 16 + (lane & 15)) * LDS_LD + kk);
+      bf16x8 af[MI], bfr[4];
+      const int kk = s * 32 + 8 * g;
 #pragma unroll
       for (int j = 0; j < 4; j++)
-        bfr[j] = *(const bf16x8*)(sB + (wn * 64 + j * 16 + (lane & 15)) * LDS_LD + kk);
+        bfr[j] = *(const bf16x8*)(sb + (wn * 64 + j * 16 + c16) * LDS_LD + kk);
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int i = 0; i < MI; i++)
+        af[i] = *(const bf16x8*)(sa + (wm * (BMT / 2) + i * 16 + c16) * LDS_LD + kk);
+#pragma unroll
+      for (int i = 0; i < MI; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
+    if (nxt) lstore(cur ^ 1);
     __syncthreads();
+    cur ^= 1;
   }
-  // C layout of 16x16 MFMA: lane holds column lane%16, rows 4*(lane/16)+r
+
+  // epilogue, 64 rows of the wave tile at a time
+  constexpr int CLD = 64 + 4;
+  float* ct = (float*)smem + w * 64 * CLD;
+  bool vt = false;
+  if constexpr (EPI == EPI_QKV) vt = (e.n_begin + n0 + wn * 64) / e.D == 2;
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int half = 0; half < BMT / 128; half++) {
+    if (half) __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      int m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
-      if (m >= M) continue;
+    for (int ii = 0; ii < 4; ii++)
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        int n = n0 + wn * 64 + j * 16 + (lane & 15);
-        epi_store<EPI, TO>(e, m, n, acc[i][j][r]);
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+          ct[(16 * ii + 4 * g + r) * CLD + 16 * j + c16] = acc[half * 4 + ii][j][r];
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    const int mb = m0 + wm * (BMT / 2) + half * 64, nb = n0 + wn * 64;
+    if (!vt) {
+#pragma unroll 4
+      for (int it = 0; it < 16; it++) {
+        const int idx = it * 64 + lane;
+        const int row = idx >> 4, c4 = (idx & 15) * 4;
+        if (mb + row < M) epi_row4<EPI, TO>(e, mb + row, nb + c4, *(const float4*)(ct + row * CLD + c4));
+      }
+    } else {
+      if constexpr (EPI == EPI_QKV) {
+#pragma unroll 4
+        for (int it = 0; it < 16; it++) {
+          const int idx = it * 64 + lane;
+          const int col = idx >> 4, r4 = (idx & 15) * 4;
+          const int m = mb + r4;
+          if (m + 3 < M) {
+            float4 v = {ct[r4 * CLD + col], ct[(r4 + 1) * CLD + col], ct[(r4 + 2) * CLD + col],
+                        ct[(r4 + 3) * CLD + col]};
+            epi_vt4<TO>(e, m, nb + col, v);
+          } else {
+            for (int r = 0; r < 4; r++)
+              if (m + r < M) epi_store<EPI, TO>(e, m + r, nb + col, ct[(r4 + r) * CLD + col]);
+          }
+        }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+  }
 }
 
 // ============================================================ skinny MFMA (M <= 128)
@@ -186,16 +300,15 @@ constexpr int MAXKS = 8;
 // 16g..16g+15 of each 64-wide step, split over two MFMAs (a dot product may
 // permute k freely as long as A and B agree), so each weight row segment is
 // one 128-byte contiguous read.
-template <int EPI, typename TO, int MT>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16_t* __restrict__ A, int lda,
+template <int EPI, typename TO, int MT, int NW, int U = (MT <= 2 ? 4 : (MT <= 4 ? 2 : 1))>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const bf16_t* __restrict__ A, int lda,
                                                           const bf16_t* __restrict__ B, int ldb,
                                                           int M, int N, int K, int kr, EpiArgs e,
                                                           float* __restrict__ part) {
-  constexpr int U = MT <= 2 ? 4 : (MT <= 4 ? 2 : 1);
-  __shared__ float red[4][MT * 16][17];
+  __shared__ float red[NW][MT * 16][17];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int n0 = blockIdx.x * skinny::NT;
-  const int kw = kr / 4;
+  const int kw = kr / NW;
   const int kb = blockIdx.y * kr + w * kw;
   const bf16_t* brow = B + (long long)(n0 + c16) * ldb + kb + 16 * g;
   const bf16_t* arow = A + (long long)c16 * lda + kb + 16 * g;
@@ -236,14 +349,135 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const bf16_t* __restri
 #pragma unroll
     for (int r = 0; r < 4; r++) red[w][16 * i + 4 * g + r][c16] = acc[i][r];
   __syncthreads();
-  for (int idx = tid; idx < M * 16; idx += 256) {
+  for (int idx = tid; idx < M * 16; idx += 64 * NW) {
     const int m = idx >> 4, c = idx & 15;
-    const float v = ((red[0][m][c] + red[1][m][c]) + red[2][m][c]) + red[3][m][c];
+    float v = red[0][m][c];
+#pragma unroll
+    for (int ww = 1; ww < NW; ww++) v += red[ww][m][c];
     if (gridDim.y == 1)
       epi_store<EPI, TO>(e, m, n0 + c, v);
     else
       part[((long long)blockIdx.y * M + m) * N + n0 + c] = v;
   }
+}
+
+// ============================================================ skinny + RMSNorm (M <= 64)
+// C = RMSNorm(X; g) W^T for fp32 rows X[M][K] in one pass: the row scale
+// r_m = (mean(x^2) + eps)^(-1/2) factors out of the dot product, so the bf16
+// operand is built from x*g while the same loads accumulate sum(x^2); the
+// output row is scaled by r_m in the epilogue.  Four waves split K; fixed
+// reduction order.
+template <int EPI, typename TO, int MT, int U = 2>
+__global__ __launch_bounds__(256) void gemm_skinny_norm_kernel(const float* __restrict__ X,
+                                                               const float* __restrict__ gain,
+                                                               const bf16_t* __restrict__ B, int ldb,
+                                                               int M, int N, int K, EpiArgs e) {
+  __shared__ float red[4][MT * 16][17];
+  __shared__ float ssw[4][MT * 16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int n0 = blockIdx.x * skinny::NT;
+  const int kw = K / 4;
+  const int kb = w * kw;
+  const bf16_t* brow = B + (long long)(n0 + c16) * ldb + kb + 16 * g;
+  floatx4 acc[MT];
+  float ss[MT];
+#pragma unroll
+  for (int i = 0; i < MT; i++) {
+    acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    ss[i] = 0.f;
+  }
+  const int nsteps = kw / 64;
+  for (int st = 0; st < nsteps; st += U) {
+    bf16x8 b0[U], b1[U];
+    float4 gg[U][4], xv[U][MT][4];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if (st + u < nsteps) {
+        const int k = kb + (st + u) * 64 + 16 * g;
+        b0[u] = *(const bf16x8*)(brow + (st + u) * 64);
+        b1[u] = *(const bf16x8*)(brow + (st + u) * 64 + 8);
+#pragma unroll
+        for (int q = 0; q < 4; q++) gg[u][q] = *(const float4*)(gain + k + 4 * q);
+#pragma unroll
+        for (int i = 0; i < MT; i++)
+#pragma unroll
+          for (int q = 0; q < 4; q++)
+            xv[u][i][q] = *(const float4*)(X + (long long)(16 * i + c16) * K + k + 4 * q);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if (st + u < nsteps) {
+#pragma unroll
+        for (int i = 0; i < MT; i++) {
+          uint32_t pk[8];
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const float4 x = xv[u][i][q], gq = gg[u][q];
+            ss[i] = fmaf(x.x, x.x, ss[i]);
+            ss[i] = fmaf(x.y, x.y, ss[i]);
+            ss[i] = fmaf(x.z, x.z, ss[i]);
+            ss[i] = fmaf(x.w, x.w, ss[i]);
+            pk[2 * q] = pack_bf16x2(x.x * gq.x, x.y * gq.y);
+            pk[2 * q + 1] = pack_bf16x2(x.z * gq.z, x.w * gq.w);
+          }
+          const u32x4 lo = {pk[0], pk[1], pk[2], pk[3]}, hi = {pk[4], pk[5], pk[6], pk[7]};
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), b0[u], acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), b1[u], acc[i], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // row sums of squares: over the 4 lane groups, then over the 4 waves
+#pragma unroll
+  for (int i = 0; i < MT; i++) {
+    float v = ss[i];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (g == 0) ssw[w][16 * i + c16] = v;
+  }
+#pragma unroll
+  for (int i = 0; i < MT; i++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) red[w][16 * i + 4 * g + r][c16] = acc[i][r];
+  __syncthreads();
+  for (int idx = tid; idx < M * 16; idx += 256) {
+    const int m = idx >> 4, c = idx & 15;
+    const float sq = ((ssw[0][m] + ssw[1][m]) + ssw[2][m]) + ssw[3][m];
+    const float rm = 1.0f / sqrtf(sq / (float)K + 1e-6f);
+    const float v = (((red[0][m][c] + red[1][m][c]) + red[2][m][c]) + red[3][m][c]) * rm;
+    epi_store<EPI, TO>(e, m, n0 + c, v);
+  }
+}
+
+bool gemm_norm_ok(int M, int N, int K) {
+  return M >= 16 && M <= 64 && M % 16 == 0 && N % skinny::NT == 0 && K % 256 == 0;
+}
+
+hipError_t gemm_norm(hipStream_t s, int odt, int epi, int M, int N, int K, const float* X,
+                     const float* gain, const void* B, int ldb, const EpiArgs& e) {
+  if (!gemm_norm_ok(M, N, K)) return hipErrorInvalidValue;
+  dim3 grid(N / skinny::NT);
+  TimingScope ts(s, KC_GEMM_SKINNY, (double)M * K * 4 + (double)N * K * 2 + (double)M * N * 4,
+                 2.0 * M * N * K);
+  const bf16_t* b = (const bf16_t*)B;
+#define GN(E, T, mt) \
+  hipLaunchKernelGGL((gemm_skinny_norm_kernel<E, T, mt>), grid, dim3(256), 0, s, X, gain, b, ldb, M, N, K, e)
+#define GNM(E, T)                 \
+  switch (M / 16) {               \
+    case 1: GN(E, T, 1); break;   \
+    case 2: GN(E, T, 2); break;   \
+    case 3: GN(E, T, 3); break;   \
+    default: GN(E, T, 4); break;  \
+  }
+  if (epi == EPI_QKV && odt == WAM_BF16) { GNM(EPI_QKV, bf16_t) }
+  else if (epi == EPI_GELU && odt == WAM_BF16) { GNM(EPI_GELU, bf16_t) }
+  else if (epi == EPI_STORE && odt == WAM_BF16) { GNM(EPI_STORE, bf16_t) }
+  else if (epi == EPI_STORE && odt == WAM_F32) { GNM(EPI_STORE, float) }
+  else return hipErrorInvalidValue;
+#undef GNM
+#undef GN
+  return hipGetLastError();
 }
 
 // ============================================================ dispatch
@@ -258,14 +492,17 @@ static double gemm_bytes(int M, int N, int K, int ea, int eb, int eo) {
 template <int EPI, typename TO>
 static hipError_t launch_big(hipStream_t s, int M, int N, int K, const void* A, int lda,
                              const void* B, int ldb, const EpiArgs& e) {
-  int ntm = (M + big::BM - 1) / big::BM, ntn = N / big::BN;
+  const int ntn = N / big::BN;
   TimingScope ts(s, KC_GEMM_BIG, gemm_bytes<EPI>(M, N, K, 2, 2, sizeof(TO)), 2.0 * M * N * K);
-  hipLaunchKernelGGL((gemm_big_kernel<EPI, TO>), dim3(ntm * ntn), dim3(256), 0, s,
+  // 256-row tiles need 110 KB of LDS (one workgroup per CU) and measured
+  // slower than two 128-row workgroups per CU
+  const int ntm = (M + 127) / 128;
+  hipLaunchKernelGGL((gemm_big_kernel<128, EPI, TO>), dim3(ntm * ntn), dim3(256), 0, s,
                      (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, e);
   return hipGetLastError();
 }
 
-// k range of one workgroup: a multiple of 256 (64 per wave) dividing K.
+// k range of one workgroup: a multiple of 64 per wave dividing K.
 static bool skinny_ok(int M, int N, int K) {
   return M >= 16 && M <= skinny::MAXM && M % 16 == 0 && N % skinny::NT == 0 && K % 256 == 0;
 }
@@ -279,11 +516,17 @@ static hipError_t launch_skinny(hipStream_t s, int M, int N, int K, const void* 
                  2.0 * M * N * K);
   const bf16_t* a = (const bf16_t*)A;
   const bf16_t* b = (const bf16_t*)B;
+  // long k ranges: 8 waves so that each wave's loads stay few
+  const bool w8 = (kr % 512 == 0) && kr >= 2048;
   switch (M / 16) {
-#define SK(mt)                                                                              \
-  case mt:                                                                                  \
-    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, TO, mt>), grid, dim3(256), 0, s, a, lda, b, \
-                       ldb, M, N, K, kr, e, part);                                          \
+#define SK(mt)                                                                                    \
+  case mt:                                                                                        \
+    if (w8)                                                                                       \
+      hipLaunchKernelGGL((gemm_skinny_kernel<EPI, TO, mt, 8>), grid, dim3(512), 0, s, a, lda, b,  \
+                         ldb, M, N, K, kr, e, part);                                              \
+    else                                                                                          \
+      hipLaunchKernelGGL((gemm_skinny_kernel<EPI, TO, mt, 4>), grid, dim3(256), 0, s, a, lda, b,  \
+                         ldb, M, N, K, kr, e, part);                                              \
     break;
     SK(1) SK(2) SK(3) SK(4) SK(5) SK(6) SK(7) SK(8)
 #undef SK
@@ -293,10 +536,13 @@ static hipError_t launch_skinny(hipStream_t s, int M, int N, int K, const void* 
   return hipGetLastError();
 }
 
+// Split-K partial products for the action rows: part[ks][M][N] (raw fp32,
+// summed by the consumer in ks order).  Four splits measured best for the
+// 1024-wide outputs at M = 32 (each workgroup then reads a quarter of A).
 int gemm_partial_splits(int M, int N, int K) {
   if (!skinny_ok(M, N, K)) return 0;
   int ks = 1;
-  while (ks < skinny::MAXKS && (N / skinny::NT) * ks < 256 && K % (256 * ks * 2) == 0) ks *= 2;
+  while (ks < 4 && (N / skinny::NT) * ks < 256 && K % (256 * ks * 2) == 0) ks *= 2;
   return ks;
 }
 

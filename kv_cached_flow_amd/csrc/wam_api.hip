@@ -145,16 +145,11 @@ struct Bufs {
   void* Hb;
   float* Yh;
   float* emb;
-  float* part;     // split partial products of the action path
-  int pend;        // splits of a W2 product not yet added to X (0: none)
+  float* part;  // split partial products of the action path
+  int pend;     // splits of a product not yet added to X (0: none)
   void* attn;
   size_t attn_bytes;
 };
-
-size_t gemm_part_elems(int M, const wam_dims* d) {
-  size_t e = (size_t)gemm_partial_splits(M, d->D, d->D) * M * d->D;
-  return std::max(e, (size_t)gemm_partial_splits(M, d->D, d->Fm) * M * d->D);
-}
 
 // ----------------------------------------------------------------- layers
 struct Layer {
@@ -204,26 +199,26 @@ int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const Fra
   return WAM_OK;
 }
 
-// X += A W^T for the action rows: through split partials that the next
-// RMSNorm adds (bf16 skinny shapes), else directly.
-int action_resid(const Layer& c, int M, int N, int K, const void* A, const void* W, bool* pending,
-                 int* ks) {
+// X += A W^T for the action rows, as split partials that the next RMSNorm adds
+// (bf16 shapes the split GEMM supports), else directly.
+int action_resid(const Layer& c, int M, int N, int K, const void* A, const void* W) {
   const wam_dims* d = c.d;
   Bufs& b = *c.b;
   if (d->dtype == WAM_BF16 && gemm_partial_splits(M, N, K) > 0) {
-    HIPCK(gemm_partial(c.s, M, N, K, A, K, W, K, b.part, ks));
-    *pending = true;
+    int ks = 0;
+    HIPCK(gemm_partial(c.s, M, N, K, A, K, W, K, b.part, &ks));
+    b.pend = ks;
     return WAM_OK;
   }
   EpiArgs r{};
   r.out = b.X;
   r.ldo = N;
   HIPCK(gemm(c.s, d->dtype, d->dtype, WAM_F32, EPI_RESID, M, N, K, A, K, W, K, r));
-  *pending = false;
+  b.pend = 0;
   return WAM_OK;
 }
 
-// y = RMSNorm(X; g), first adding the pending split partials to X.
+// y = RMSNorm(X; g) (odt), first adding pending split partials to X.
 int norm_rows(const Layer& c, int odt, const float* g, void* y, int M) {
   Bufs& b = *c.b;
   if (b.pend > 0) {
@@ -236,14 +231,13 @@ int norm_rows(const Layer& c, int odt, const float* g, void* y, int M) {
 }
 
 // One action layer on the B*H rows in b.X; kc/vc: that layer's cache for all
-// episodes (or NULL).  May leave the W2 product pending in b.part (b.pend).
+// episodes (or NULL).  May leave the W2 product pending (b.pend).
 int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, const void* vc,
                  int cap, const ActLens& lens) {
   const wam_dims* d = c.d;
   const int dt = d->dtype, D = d->D, H = d->H, M = B * H;
   Bufs& b = *c.b;
   int st;
-  if ((st = norm_rows(c, dt, w.g1, b.Y, M))) return st;
   EpiArgs e{};
   e.q = b.Q;
   e.k = b.Ka;
@@ -256,36 +250,24 @@ int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, co
   e.v_gs = (long long)d->Hh * d->dh * H;
   e.v_hs = (long long)d->dh * H;
   e.v_ld = H;
+  if ((st = norm_rows(c, dt, w.g1, b.Y, M))) return st;
   HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, M, 3 * D, D, b.Y, D, w.wqkv, D, e));
   HIPCK(attn_action(c.s, dt, B, d->Hh, H, b.Q, b.Ka, b.Va, H, kc, vc, cap, lens, b.O, 0, b.attn,
                     b.attn_bytes));
-  bool pend;
-  int ks = 0;
-  if ((st = action_resid(c, M, D, D, b.O, w.wo, &pend, &ks))) return st;
-  b.pend = pend ? ks : 0;
+  if ((st = action_resid(c, M, D, D, b.O, w.wo))) return st;
   if ((st = norm_rows(c, dt, w.g2, b.Y, M))) return st;
   EpiArgs gl{};
   gl.out = b.Hb;
   gl.ldo = d->Fm;
   HIPCK(gemm(c.s, dt, dt, dt, EPI_GELU, M, d->Fm, D, b.Y, D, w.w1, D, gl));
-  if ((st = action_resid(c, M, D, d->Fm, b.Hb, w.w2, &pend, &ks))) return st;
-  b.pend = pend ? ks : 0;
-  return WAM_OK;
+  return action_resid(c, M, D, d->Fm, b.Hb, w.w2);
 }
 
-// v = RMSNorm(X; g_out) W_out^T; z += dt * v (and vhat = v).
-int head_euler(const Layer& c, const wam_expert_w* ex, int M, int C, float* z, float dtv, float* vhat) {
-  const wam_dims* d = c.d;
+// pending partials of the last layer -> X (before the step boundary)
+int flush_pending(const Layer& c, const float* g, int M) {
   Bufs& b = *c.b;
-  int st;
-  if ((st = norm_rows(c, WAM_F32, ex->g_out, b.Yh, M))) return st;
-  EpiArgs e{};
-  e.out = z;
-  e.ldo = C;
-  e.dt = dtv;
-  e.vhat = vhat;
-  HIPCK(gemm(c.s, WAM_F32, d->dtype, WAM_F32, EPI_EULER, M, C, d->D, b.Yh, d->D, ex->w_out, d->D, e));
-  return WAM_OK;
+  if (b.pend == 0) return WAM_OK;
+  return norm_rows(c, c.d->dtype, g, b.Y, M);
 }
 
 // workspace of the action path (rows M = B*H)
@@ -301,7 +283,7 @@ void plan_action(Arena& a, const wam_dims* d, int B, int max_len, bool with_emb,
   b.O = a.take((size_t)M * d->D * e);
   b.Hb = a.take((size_t)M * d->Fm * e);
   b.Yh = (float*)a.take((size_t)M * d->D * 4);
-  b.part = (float*)a.take(gemm_part_elems(M, d) * 4 + 16);
+  b.part = (float*)a.take((size_t)4 * M * d->D * 4);
   b.pend = 0;
   b.attn_bytes = attn_action_scratch_bytes(B, d->Hh, d->H, max_len, 0);
   b.attn = a.take(b.attn_bytes);
@@ -319,9 +301,9 @@ void plan_prefill(Arena& a, const wam_dims* d, int Fh, int Ff, Bufs& b, float** 
   b.Hb = a.take(T * d->Fm * e);
   b.Yh = (float*)a.take(std::max<size_t>(Tf, 1) * d->D * 4);
   *z = (float*)a.take(std::max<size_t>(Tf, 1) * d->Cv * 4);
+  b.Ka = b.Va = nullptr;
   b.part = nullptr;
   b.pend = 0;
-  b.Ka = b.Va = nullptr;
   b.attn = nullptr;
   b.attn_bytes = 0;
 }
@@ -484,7 +466,8 @@ int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video, const 
           if ((st = video_layer(c, video->layers[l], Tf, Th, tabs[b], kl(l), vl(l), cache->cap,
                                 false)))
             return st;
-        if ((st = head_euler(c, video, Tf, d->Cv, z, sig[k + 1] - sig[k], nullptr))) return st;
+        HIPCK(step_boundary(s, dt, bufs.X, video->g_out, video->w_out, z, sig[k + 1] - sig[k],
+                            nullptr, nullptr, nullptr, Tf, D, d->Cv, true));
       }
       HIPCK(embed(s, WAM_F32, dt, z, zmap, video->w_in, emb_last, bufs.X, Tf, D, d->Cv));
       for (int l = 0; l < d->L; l++)
@@ -602,7 +585,7 @@ int wam_action_layer(const wam_dims* d, const wam_layer_w* w, float* x, const wa
   const void* kc = kv ? (const char*)kv->k + kv_layer * layer_stride(kv) : nullptr;
   const void* vc = kv ? (const char*)kv->v + kv_layer * layer_stride(kv) : nullptr;
   if ((st = action_layer(c, *w, B, kc, vc, kv ? kv->cap : 0, lens))) return st;
-  if (b.pend > 0 && (st = norm_rows(c, d->dtype, w->g1, b.Y, B * d->H))) return st;  // fold W2
+  if ((st = flush_pending(c, w->g1, B * d->H))) return st;
   HIPCK(hipMemcpyAsync(x, b.X, bytes, hipMemcpyDeviceToDevice, s));
   return WAM_OK;
 }
@@ -651,24 +634,25 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
   HIPCK(time_embedding(s, t.data(), N, d->D, b.emb));
   const int M = B * d->H;
   HIPCK(hipMemcpyAsync(actions_out, eps, (size_t)M * d->A * 4, hipMemcpyDeviceToDevice, s));
-  RowMap amap;
-  amap.n = 1;
-  amap.P = M;
-  amap.src[0] = 0;
   Layer c{s, d, &b};
   const size_t ls = any ? layer_stride(kv) : 0;
+  // X = eps W_in^T + emb(t_0); then per step: layers, and one step-boundary
+  // kernel doing head + Euler + the next step's embedding
+  HIPCK(step_boundary(s, d->dtype, b.X, nullptr, nullptr, actions_out, 0.f, nullptr, action->w_in,
+                      b.emb, M, d->D, d->A, false));
   for (int k = 0; k < N; k++) {
-    HIPCK(embed(s, WAM_F32, d->dtype, actions_out, amap, action->w_in, b.emb + (size_t)k * d->D,
-                b.X, M, d->D, d->A));
     for (int l = 0; l < d->L; l++) {
       const int r = read_map[l];
       const void* kc = r >= 0 ? (const char*)kv->k + r * ls : nullptr;
       const void* vc = r >= 0 ? (const char*)kv->v + r * ls : nullptr;
       if ((st = action_layer(c, action->layers[l], B, kc, vc, r >= 0 ? kv->cap : 0, lens))) return st;
     }
-    if ((st = head_euler(c, action, M, d->A, actions_out, t[k + 1] - t[k],
-                         vhat_out ? vhat_out + (size_t)k * M * d->A : nullptr)))
-      return st;
+    const bool last = (k + 1 == N);
+    if ((st = flush_pending(c, action->g_out, M))) return st;
+    HIPCK(step_boundary(s, d->dtype, b.X, action->g_out, action->w_out, actions_out,
+                        t[k + 1] - t[k], vhat_out ? vhat_out + (size_t)k * M * d->A : nullptr,
+                        last ? nullptr : action->w_in,
+                        last ? nullptr : b.emb + (size_t)(k + 1) * d->D, M, d->D, d->A, true));
   }
   return WAM_OK;
 }
@@ -704,6 +688,7 @@ int wam_attention_action(int dtype, int B, int Hh, int dh, int H, const void* q,
   if (n_act < 0 || n_act > H || (n_act > 0 && (!ka || !va)))
     return fail(WAM_E_ARG, "bad own keys");
   if ((kc == nullptr) != (vc == nullptr)) return fail(WAM_E_ARG, "kc and vc must both be set");
+  if (splits_hint < 0 || splits_hint > 63) return fail(WAM_E_ARG, "splits_hint must be in [0, 63]");
   ActLens lens{};
   int max_len = 0;
   if (kc) {

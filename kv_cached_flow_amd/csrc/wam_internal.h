@@ -36,9 +36,19 @@ template <typename T> __device__ inline float to_f(T v);
 template <> __device__ inline float to_f<float>(float v) { return v; }
 template <> __device__ inline float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
 
+// Device conversion to bf16 uses the gfx950 v_cvt_pk_bf16_f32 instruction
+// (round to nearest even, like f2bf).
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 hbf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float hfloat2;
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  hfloat2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, hbf16x2));
+}
+__device__ inline bf16_t dev_f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+
 template <typename T> __device__ inline T from_f(float v);
 template <> __device__ inline float from_f<float>(float v) { return v; }
-template <> __device__ inline bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+template <> __device__ inline bf16_t from_f<bf16_t>(float v) { return dev_f2bf(v); }
 
 __device__ inline float gelu_f(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
 
@@ -115,12 +125,18 @@ __device__ inline void epi_store(const EpiArgs& e, int m, int n, float v) {
 hipError_t gemm(hipStream_t s, int adt, int bdt, int odt, int epi, int M, int N, int K,
                 const void* A, int lda, const void* B, int ldb, const EpiArgs& e);
 
-// bf16 M <= 128: raw fp32 partial products part[ks][M][N], ks < *ks_out (the
-// caller sums them in ks order; rmsnorm_accum does).  gemm_partial_splits
-// gives the split count (0: shape not supported).
+// bf16 action rows (M <= 128): raw fp32 split-K partials part[ks][M][N],
+// ks < *ks_out; the consumer adds them in ks order (rmsnorm_accum does).
 int gemm_partial_splits(int M, int N, int K);
 hipError_t gemm_partial(hipStream_t s, int M, int N, int K, const void* A, int lda, const void* B,
                         int ldb, float* part, int* ks_out);
+
+// C = RMSNorm(X; gain) W^T with the epilogue, for fp32 rows X[M][K] and bf16
+// W[N][K], M <= 64 (the action rows): the normalisation is fused into the
+// operand load.  gemm_norm_ok tells whether a shape is supported.
+bool gemm_norm_ok(int M, int N, int K);
+hipError_t gemm_norm(hipStream_t s, int odt, int epi, int M, int N, int K, const float* X,
+                     const float* gain, const void* B, int ldb, const EpiArgs& e);
 
 hipError_t rmsnorm(hipStream_t s, int odt, const float* x, const float* g, void* y, int M, int D);
 // x[m] += sum_{ks < KS} part[ks][m] (in ks order), then y = RMSNorm(x; g).
@@ -141,6 +157,13 @@ hipError_t embed(hipStream_t s, int xdt, int wdt, const void* x, const RowMap& m
 hipError_t time_embedding(hipStream_t s, const float* sigma_host, int n, int D, float* emb);
 
 hipError_t euler(hipStream_t s, float* x, const float* v, int64_t n, float dt);
+
+// Step boundary of the flow, one workgroup per row: optionally the velocity
+// head and Euler update (z += dt * RMSNorm(X; g_out) W_out^T, vhat = the
+// velocity), then optionally the next embedding X = z W_in^T + emb_next.
+hipError_t step_boundary(hipStream_t s, int wdt, float* X, const float* g_out, const void* w_out,
+                         float* z, float dt, float* vhat, const void* w_in, const float* emb_next,
+                         int M, int D, int C, bool do_head);
 hipError_t copy_cvt_f32(hipStream_t s, int sdt, const void* src, float* dst, int64_t n);
 
 struct FuseArgs {

