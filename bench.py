@@ -57,6 +57,29 @@ def kernel_table(stats: dict) -> dict:
     return out
 
 
+def measured_traffic(workload: str, kernel_class: str):
+    """HBM bytes per launch of a kernel class from the committed rocprofv3
+    counter summary (profiles/<workload>_chunk_hbm_counters.txt), or None when
+    there is none or the kernel's source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_chunk_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if not line.startswith("traffic:"):
+            continue
+        f = [x.strip() for x in line[len("traffic:"):].split("|")]
+        if f[0] != kernel_class:
+            continue
+        src = os.path.join(ROOT, f[5])
+        if not os.path.exists(src):
+            return None
+        if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != f[6]:
+            return None
+        return float(f[4])
+    return None
+
+
 def cpu_baseline(cfg_name: str, layers: int) -> dict:
     import numpy as np  # noqa: F401
     import torch
@@ -90,6 +113,11 @@ def main():
     ap.add_argument("--config", default="C1")
     ap.add_argument("--cpu-layers", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--minimal", action="store_true",
+                    help="only warmup + timed chunks (for counter collection)")
+    ap.add_argument("--copy-probe-gib", type=float, default=0.0,
+                    help="run one device-to-device copy of this size and exit "
+                         "(calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
@@ -104,6 +132,15 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU"}))
         sys.exit(1)
+    if args.copy_probe_gib > 0:
+        n = int(args.copy_probe_gib * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n * 4}))
+        return
     cfg = configs.get(args.config)
     inp = inputs.generate(cfg)
     dc = DeviceChunk(cfg, inp)
@@ -124,6 +161,9 @@ def main():
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
     print(f"[bench] {ms:.3f} ms/chunk (wall {wall / args.steps * 1e3:.3f})", file=sys.stderr, flush=True)
+    if args.minimal:
+        print(json.dumps({"value": round(ms, 4), "unit": "ms/chunk", "steps": args.steps}), flush=True)
+        return
 
     # ---- phases (events between the calls of one chunk)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -148,7 +188,9 @@ def main():
     dom = max(kt, key=lambda k: kt[k]["total_ms"])
     d = kt[dom]
     roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
-                "unit": d["unit"], "frac": d["frac"], "traffic": None}
+                "unit": d["unit"], "frac": d["frac"], "traffic": measured_traffic(cfg.name, dom),
+                "algorithmic_per_launch": (d["flops_per_launch"] if d["bound"] != "hbm"
+                                           else d["bytes_per_launch"])}
 
     rec = {
         "metric": "ms per 32-action chunk at 1 GPU; cached-KV attn HBM GB/s; prefill MFMA util",
