@@ -27,15 +27,23 @@ namespace wam {
 
 #define LOG2E 1.4426950408889634f
 
+// Reductions over the four lanes {c, c+16, c+32, c+48} that hold one query
+// column, with the gfx950 lane-swap instructions (VALU, no LDS traffic).
 __device__ inline float wave_max16x4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  const unsigned u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned w = __float_as_uint(v);
+  auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ inline float wave_sum16x4(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  const unsigned u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned w = __float_as_uint(v);
+  auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // key index (0..63) inside a 64-key tile of S^T subtile `sub` (0..3), row r (0..15)
@@ -48,30 +56,50 @@ __device__ inline int key_slot(int k) {
   return 16 * (2 * (k >> 5) + ((j >> 2) & 1)) + 4 * (j >> 3) + (j & 3);
 }
 
-// Running softmax state of one wave: 32 queries (two 16-column tiles); O^T
-// accumulators o[dh tile][q tile], row max m and lane-partial row sum l (in
-// units of raw scores; exponentials use exp2 with the scale sl2 folded in).
+// Running softmax state of one wave: 32 queries (two 16-column tiles).
+// o[0..3][t] are the O^T accumulators (head dim x query); o[4][t] row 0 holds
+// the row sums, accumulated by the same P V MFMA against a row of ones, so
+// numerator and denominator use the same bf16 probabilities.  m is the
+// reference max in raw score units; exponentials use exp2 with the scale sl2
+// folded into one FMA.  The reference max is raised only when a new score
+// exceeds it by more than 2^8 in probability, so rescaling is rare; P <= 256
+// stays exact in bf16 and the result does not depend on the reference.
 struct WaveAcc {
-  floatx4 o[4][2];
-  float m[2], l[2];
+  floatx4 o[5][2];
+  float m[2];
 };
 
 __device__ inline void acc_init(WaveAcc& a) {
 #pragma unroll
-  for (int d = 0; d < 4; d++)
+  for (int d = 0; d < 5; d++)
 #pragma unroll
     for (int t = 0; t < 2; t++) a.o[d][t] = floatx4{0.f, 0.f, 0.f, 0.f};
   a.m[0] = a.m[1] = -INFINITY;
-  a.l[0] = a.l[1] = 0.f;
 }
+
+// bf16 operand of the ones row (head-dim row 0 of the fifth tile)
+__device__ inline bf16x8 ones_row(int c16) {
+  const short one = c16 == 0 ? (short)0x3F80 : (short)0;
+  return bf16x8{one, one, one, one, one, one, one, one};
+}
+
+// Row sum of query column (lane & 15) after the last tile (all lanes).
+__device__ inline float acc_rowsum(const WaveAcc& a, int t) {
+  // row 0 of the fifth tile lives in lane group 0, register 0
+  const float v = a.o[4][t][0];
+  return __shfl(v, threadIdx.x & 15, 64);
+}
+
+constexpr float kLazyLog2 = 8.0f;
 
 // One 64-key tile: online softmax of the raw scores sacc (S^T, permuted key
 // rows), then O^T += V^T P^T with the V^T operands from vop(d, wd).
 // MASK: keys kbase + index >= kq[t] get probability 0.
 template <bool MASK, typename VOp>
 __device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], int kbase, const int (&kq)[2],
-                                   float sl2, int g, VOp vop) {
+                                   float sl2, int g, const bf16x8& ones, VOp vop) {
   bf16x8 pf[2][2];
+  const float thr = kLazyLog2 / sl2;
 #pragma unroll
   for (int t = 0; t < 2; t++) {
     float mx = -INFINITY;
@@ -84,40 +112,55 @@ __device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], int kbase,
         mx = fmaxf(mx, sacc[sub][t][r]);
       }
     mx = wave_max16x4(mx);
-    const float mnew = fmaxf(a.m[t], mx);
-    const float alpha = __builtin_amdgcn_exp2f((a.m[t] - mnew) * sl2);
-    a.m[t] = mnew;
-    const float mc = mnew * sl2;
-    float p[4][4], ls = 0.f;
+    const bool need = mx > a.m[t] + thr;
+    if (__any(need)) {
+      const float mnew = need ? mx : a.m[t];
+      const float alpha = __builtin_amdgcn_exp2f((a.m[t] - mnew) * sl2);
+      a.m[t] = mnew;
 #pragma unroll
-    for (int sub = 0; sub < 4; sub++)
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        p[sub][r] = __builtin_amdgcn_exp2f(fmaf(sacc[sub][t][r], sl2, -mc));
-        ls += p[sub][r];
-      }
-    a.l[t] = fmaf(a.l[t], alpha, ls);
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int d = 0; d < 4; d++) a.o[d][t] *= alpha;
+      for (int d = 0; d < 5; d++) a.o[d][t] *= alpha;
     }
+    const float mc = a.m[t] * sl2;
 #pragma unroll
     for (int wd = 0; wd < 2; wd++) {
-      u32x4 u = {pack_bf16x2(p[2 * wd][0], p[2 * wd][1]), pack_bf16x2(p[2 * wd][2], p[2 * wd][3]),
-                 pack_bf16x2(p[2 * wd + 1][0], p[2 * wd + 1][1]),
-                 pack_bf16x2(p[2 * wd + 1][2], p[2 * wd + 1][3])};
+      float p[8];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[2 * wd][t][r], sl2, -mc));
+        p[4 + r] = __builtin_amdgcn_exp2f(fmaf(sacc[2 * wd + 1][t][r], sl2, -mc));
+      }
+      const u32x4 u = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                       pack_bf16x2(p[6], p[7])};
       pf[wd][t] = __builtin_bit_cast(bf16x8, u);
     }
   }
 #pragma unroll
-  for (int d = 0; d < 4; d++)
+  for (int wd = 0; wd < 2; wd++) {
 #pragma unroll
-    for (int wd = 0; wd < 2; wd++) {
+    for (int d = 0; d < 4; d++) {
       const bf16x8 v = vop(d, wd);
 #pragma unroll
       for (int t = 0; t < 2; t++)
         a.o[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pf[wd][t], a.o[d][t], 0, 0, 0);
     }
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+      a.o[4][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[wd][t], a.o[4][t], 0, 0, 0);
+  }
+}
+
+// S^T for one 64-key tile from K operands kop(sub, s) (16 keys x 32 dims).
+template <typename KOp>
+__device__ inline void tile_scores(floatx4 (&sacc)[4][2], const bf16x8 (&qf)[2][2], KOp kop) {
+#pragma unroll
+  for (int sub = 0; sub < 4; sub++) {
+    const bf16x8 k0 = kop(sub, 0), k1 = kop(sub, 1);
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[t][0], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[t][1], sacc[sub][t], 0, 0, 0);
+    }
+  }
 }
 
 // ====================================================================== prefill
@@ -172,6 +215,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   }
   WaveAcc acc;
   acc_init(acc);
+  const bf16x8 ones = ones_row(c16);
 
   // staging of one K tile (token rows, stored at their S^T slot) and one V^T
   // tile (head-dim rows): 2 x 16 B of each per thread
@@ -185,6 +229,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     kslot[i] = key_slot(krow[i]);
   }
   auto gload = [&](int kt) {
+    if (kt + KT <= kend_max) {  // whole tile valid: plain 16-byte loads
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        rk[i] = *(const u32x4*)(kh + (long long)(kt + krow[i]) * 64 + ch8[i]);
+        rv[i] = *(const u32x4*)(vh + (long long)krow[i] * cap + kt + ch8[i]);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const int key = kt + krow[i];
@@ -218,26 +270,18 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     const bool nxt = kt + KT < kend_max;
     if (nxt) gload(kt + KT);
     floatx4 sacc[4][2];
-#pragma unroll
-    for (int sub = 0; sub < 4; sub++) {
-#pragma unroll
-      for (int t = 0; t < 2; t++) sacc[sub][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 2; s++) {
-        const bf16x8 a = *(const bf16x8*)(&sK[cur][(16 * sub + c16) * LD + 32 * s + 8 * g]);
-#pragma unroll
-        for (int t = 0; t < 2; t++)
-          sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[t][s], sacc[sub][t], 0, 0, 0);
-      }
-    }
+    const bf16_t* sk = sK[cur];
+    tile_scores(sacc, qf, [&](int sub, int s) {
+      return *(const bf16x8*)(sk + (16 * sub + c16) * LD + 32 * s + 8 * g);
+    });
     const bf16_t* sv = sV[cur];
     auto vop = [&](int d, int wd) {
       return *(const bf16x8*)(sv + (16 * d + c16) * LD + 32 * wd + 8 * g);
     };
     if (kt + KT > kend_min)
-      tile_update<true>(acc, sacc, kt, kq, sl2, g, vop);
+      tile_update<true>(acc, sacc, kt, kq, sl2, g, ones, vop);
     else
-      tile_update<false>(acc, sacc, kt, kq, sl2, g, vop);
+      tile_update<false>(acc, sacc, kt, kq, sl2, g, ones, vop);
     if (nxt) lstore(cur ^ 1);
     __syncthreads();
     cur ^= 1;
@@ -245,7 +289,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   const int D = Hh * 64;
 #pragma unroll
   for (int t = 0; t < 2; t++) {
-    const float l = wave_sum16x4(acc.l[t]);
+    const float l = acc_rowsum(acc, t);
     const int qi = q0 + w * QW + 16 * t + c16;
     if (qi >= nq) continue;
     const float inv = 1.0f / l;
@@ -378,6 +422,7 @@ __global__ __launch_bounds__(256) void attn_action_kernel(
 
   WaveAcc acc;
   acc_init(acc);
+  const bf16x8 ones = ones_row(c16);
   const int kq[2] = {key1, key1};
   for (int kt = key0 + w * KT; kt < key1; kt += 4 * KT) {
     // ---- loads: K rows (A of S^T) and V^T rows (A of P V), zero past key1
@@ -404,27 +449,19 @@ __global__ __launch_bounds__(256) void attn_action_kernel(
         }
         av[d][wd] = x;
       }
-    // ---- S^T
+    // ---- S^T, softmax, P V
     floatx4 sacc[4][2];
-#pragma unroll
-    for (int sub = 0; sub < 4; sub++)
-#pragma unroll
-      for (int t = 0; t < 2; t++) {
-        sacc[sub][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ss = 0; ss < 2; ss++)
-          sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[sub][ss], qf[t][ss], sacc[sub][t], 0, 0, 0);
-      }
+    tile_scores(sacc, qf, [&](int sub, int ss) { return ak[sub][ss]; });
     auto vop = [&](int d, int wd) { return av[d][wd]; };
     if (kt + KT > key1)
-      tile_update<true>(acc, sacc, kt, kq, sl2, g, vop);
+      tile_update<true>(acc, sacc, kt, kq, sl2, g, ones, vop);
     else
-      tile_update<false>(acc, sacc, kt, kq, sl2, g, vop);
+      tile_update<false>(acc, sacc, kt, kq, sl2, g, ones, vop);
   }
   // ---- per-wave state to LDS (waves without keys hold m = -inf, l = 0, o = 0)
 #pragma unroll
   for (int t = 0; t < 2; t++) {
-    const float l = wave_sum16x4(acc.l[t]);
+    const float l = acc_rowsum(acc, t);
     const int qi = 16 * t + c16;
     if (g == 0) {
       sm[w][qi] = acc.m[t];
