@@ -92,12 +92,24 @@ __device__ inline float acc_rowsum(const WaveAcc& a, int t) {
 
 constexpr float kLazyLog2 = 8.0f;
 
+// Scores of keys kbase + index >= kq[t] become -inf (probability 0), in place.
+__device__ inline void tile_mask(floatx4 (&sacc)[4][2], int kbase, const int (&kq)[2], int g) {
+#pragma unroll
+  for (int t = 0; t < 2; t++)
+#pragma unroll
+    for (int sub = 0; sub < 4; sub++)
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+        if (kbase + 32 * (sub >> 1) + 8 * g + 4 * (sub & 1) + r >= kq[t]) sacc[sub][t][r] = -INFINITY;
+}
+
 // One 64-key tile: online softmax of the raw scores sacc (S^T, permuted key
-// rows), then O^T += V^T P^T with the V^T operands from vop(d, wd).
-// MASK: keys kbase + index >= kq[t] get probability 0.
-template <bool MASK, typename VOp>
-__device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], int kbase, const int (&kq)[2],
-                                   float sl2, int g, const bf16x8& ones, VOp vop) {
+// rows, masked scores already -inf), then O^T += V^T P^T with the V^T
+// operands from vop(d, wd).  Inlined once per kernel: a second inlined copy
+// makes the register allocator shuffle the accumulators at the join.
+template <typename VOp>
+__device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], float sl2,
+                                   const bf16x8& ones, VOp vop) {
   bf16x8 pf[2][2];
   const float thr = kLazyLog2 / sl2;
 #pragma unroll
@@ -106,11 +118,7 @@ __device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], int kbase,
 #pragma unroll
     for (int sub = 0; sub < 4; sub++)
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        if (MASK && kbase + 32 * (sub >> 1) + 8 * g + 4 * (sub & 1) + r >= kq[t])
-          sacc[sub][t][r] = -INFINITY;
-        mx = fmaxf(mx, sacc[sub][t][r]);
-      }
+      for (int r = 0; r < 4; r++) mx = fmaxf(mx, sacc[sub][t][r]);
     mx = wave_max16x4(mx);
     const bool need = mx > a.m[t] + thr;
     if (__any(need)) {
@@ -278,10 +286,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     auto vop = [&](int d, int wd) {
       return *(const bf16x8*)(sv + (16 * d + c16) * LD + 32 * wd + 8 * g);
     };
-    if (kt + KT > kend_min)
-      tile_update<true>(acc, sacc, kt, kq, sl2, g, ones, vop);
-    else
-      tile_update<false>(acc, sacc, kt, kq, sl2, g, ones, vop);
+    if (kt + KT > kend_min) tile_mask(sacc, kt, kq, g);
+    tile_update(acc, sacc, sl2, ones, vop);
     if (nxt) lstore(cur ^ 1);
     __syncthreads();
     cur ^= 1;
@@ -453,10 +459,8 @@ __global__ __launch_bounds__(256) void attn_action_kernel(
     floatx4 sacc[4][2];
     tile_scores(sacc, qf, [&](int sub, int ss) { return ak[sub][ss]; });
     auto vop = [&](int d, int wd) { return av[d][wd]; };
-    if (kt + KT > key1)
-      tile_update<true>(acc, sacc, kt, kq, sl2, g, ones, vop);
-    else
-      tile_update<false>(acc, sacc, kt, kq, sl2, g, ones, vop);
+    if (kt + KT > key1) tile_mask(sacc, kt, kq, g);
+    tile_update(acc, sacc, sl2, ones, vop);
   }
   // ---- per-wave state to LDS (waves without keys hold m = -inf, l = 0, o = 0)
 #pragma unroll
