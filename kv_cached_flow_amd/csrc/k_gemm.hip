@@ -66,9 +66,6 @@ __global__ __launch_bounds__(256) void gemm_simple_kernel(const TA* __restrict__
 }
 
 // ============================================================ big MFMA
-namespace big {
-constexpr int BM = 128, BN = 128, BK = 64, LDS_LD = BK + 8;  // padded row (bf16 elements)
-}
 
 __device__ inline int swizzle_tile(int bid, int nb, int ntm, int ntn, int* tm, int* tn) {
   // Blocks are dealt round-robin to the 8 XCDs; make consecutive logical ids
@@ -151,112 +148,114 @@ __device__ inline void epi_vt4(const EpiArgs& e, int m, int n, float4 v) {
   }
 }
 
-// BMT x 128 x 64 tiles (BMT = 128 or 256), 4 waves in a 2x2 grid, each
-// wave (BMT/2) x 64.  Operand tiles double buffered in LDS with one barrier
-// per k step; the C tile is transposed through LDS (64 rows of a wave at a
-// time) so that the epilogue issues 8/16-byte accesses.
-template <int BMT, int EPI, typename TO>
-__global__ __launch_bounds__(256, BMT == 128 ? 2 : 1) void gemm_big_kernel(
+// 128 x 128 x 64 tiles, 4 waves in a 2x2 grid (each 64 x 64), two
+// workgroups per CU.  Operand tiles go from global memory straight into LDS
+// (global_load_lds: lane i of a wave fills bytes [16i, 16i+16) of the
+// destination), two stages deep.  A 64-wide k slice of one row is 128 bytes
+// = 8 chunks of 16 bytes; chunk c of row r is stored at slot c ^ (r & 7), so
+// each lane picks the global chunk that belongs at its LDS slot, and the
+// 16-byte fragment reads of 8 consecutive rows hit distinct banks.  All 16
+// fragment reads of a k step are issued before its 32 MFMAs.  The C tile is
+// transposed through LDS (32 rows of a wave at a time) so that the epilogue
+// issues 8/16-byte accesses.
+namespace big2 {
+constexpr int BM = 128, BN = 128, BK = 64, STAGE = (BM + BN) * 128;  // bytes
+}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int EPI, typename TO>
+__global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_big_kernel(
     const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb, int M, int N,
     int K, EpiArgs e) {
-  using namespace big;
-  constexpr int MI = BMT / 32;             // 16-row tiles per wave
-  constexpr int AOP = BMT * LDS_LD, BOP = BN * LDS_LD;
-  constexpr int AL = BMT / 32;             // 16-byte A chunks per thread per k step
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (AOP + BOP)];
+  using namespace big2;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int ntm = (M + BMT - 1) / BMT, ntn = N / BN;
+  const int ntm = (M + BM - 1) / BM, ntn = N / BN;
   int tm, tn;
   swizzle_tile(blockIdx.x, gridDim.x, ntm, ntn, &tm, &tn);
-  const int m0 = tm * BMT, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * BN;
   const int wm = w >> 1, wn = w & 1;
 
-  floatx4 acc[MI][4];
+  // Load instruction i of wave w fills LDS rows 8(4i + w) .. +7 of an
+  // operand; lane l covers row 8(4i + w) + l/8, slot l%8.  Rows past M are
+  // clamped (their products land in accumulator rows never stored).
+  const int lrow = lane >> 3, lkc = (lane & 7) ^ lrow;
+  const bf16_t* asrc[4];
+  const bf16_t* bsrc[4];
 #pragma unroll
-  for (int i = 0; i < MI; i++)
+  for (int i = 0; i < 4; i++) {
+    const int row = (4 * i + w) * 8 + lrow;
+    asrc[i] = A + (long long)min(m0 + row, M - 1) * lda + lkc * 8;
+    bsrc[i] = B + (long long)(n0 + row) * ldb + lkc * 8;
+  }
+  auto issue = [&](int kt, int buf) {
+    char* sa = smem + buf * STAGE;
+    char* sb = sa + BM * 128;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + kt * BK),
+                                       (lds_ptr_t)(sa + (4 * i + w) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + kt * BK),
+                                       (lds_ptr_t)(sb + (4 * i + w) * 1024), 16, 0, 0);
+  };
+
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ra[AL], rb[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int r = 0; r < AL; r++) {
-      const int c = tid + 256 * r, row = c >> 3, ch = (c & 7) * 8;
-      const int gm = m0 + row;
-      ra[r] = gm < M ? *(const u32x4*)(A + (long long)gm * lda + k0 + ch) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int c = tid + 256 * r, row = c >> 3, ch = (c & 7) * 8;
-      rb[r] = *(const u32x4*)(B + (long long)(n0 + row) * ldb + k0 + ch);
-    }
-  };
-  auto lstore = [&](int b) {
-    bf16_t* sa = smem + b * (AOP + BOP);
-    bf16_t* sb = sa + AOP;
-#pragma unroll
-    for (int r = 0; r < AL; r++) {
-      const int c = tid + 256 * r;
-      *(u32x4*)(sa + (c >> 3) * LDS_LD + (c & 7) * 8) = ra[r];
-    }
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int c = tid + 256 * r;
-      *(u32x4*)(sb + (c >> 3) * LDS_LD + (c & 7) * 8) = rb[r];
-    }
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  int cur = 0;
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    const bool nxt = k0 + BK < K;
-    if (nxt) gload(k0 + BK);
-    const bf16_t* sa = smem + cur * (AOP + BOP);
-    const bf16_t* sb = sa + AOP;
+  const int nk = K / BK, x7 = c16 & 7;
+  issue(0, 0);
+  for (int kt = 0; kt < nk; kt++) {
+    __syncthreads();  // waits for this wave's loads of stage kt, then for everyone's
+    const char* sa = smem + (kt & 1) * STAGE;
+    const char* sb = sa + BM * 128;
+    bf16x8 af[2][4], bfr[2][4];
 #pragma unroll
     for (int s = 0; s < 2; s++) {
-      bf16x8 af[MI], bfr[4];
-      const int kk = s * 32 + 8 * g;
+      const int slot = ((4 * s + g) ^ x7) * 16;
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        bfr[j] = *(const bf16x8*)(sb + (wn * 64 + j * 16 + c16) * LDS_LD + kk);
+      for (int i = 0; i < 4; i++) af[s][i] = *(const bf16x8*)(sa + (wm * 64 + i * 16 + c16) * 128 + slot);
 #pragma unroll
-      for (int i = 0; i < MI; i++)
-        af[i] = *(const bf16x8*)(sa + (wm * (BMT / 2) + i * 16 + c16) * LDS_LD + kk);
+      for (int j = 0; j < 4; j++) bfr[s][j] = *(const bf16x8*)(sb + (wn * 64 + j * 16 + c16) * 128 + slot);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the other buffer was last read in step kt - 1, which every wave has left
+    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < MI; i++)
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (nxt) lstore(cur ^ 1);
-    __syncthreads();
-    cur ^= 1;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
   }
+  __syncthreads();  // operand buffers become the C staging area
 
-  // epilogue, 64 rows of the wave tile at a time
+  // epilogue, 32 rows of the wave tile at a time
   constexpr int CLD = 64 + 4;
-  float* ct = (float*)smem + w * 64 * CLD;
+  float* ct = (float*)smem + w * 32 * CLD;
   bool vt = false;
   if constexpr (EPI == EPI_QKV) vt = (e.n_begin + n0 + wn * 64) / e.D == 2;
 #pragma unroll
-  for (int half = 0; half < BMT / 128; half++) {
-    if (half) __syncthreads();
+  for (int half = 0; half < 2; half++) {
 #pragma unroll
-    for (int ii = 0; ii < 4; ii++)
+    for (int ii = 0; ii < 2; ii++)
 #pragma unroll
       for (int j = 0; j < 4; j++)
 #pragma unroll
         for (int r = 0; r < 4; r++)
-          ct[(16 * ii + 4 * g + r) * CLD + 16 * j + c16] = acc[half * 4 + ii][j][r];
+          ct[(16 * ii + 4 * g + r) * CLD + 16 * j + c16] = acc[half * 2 + ii][j][r];
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
-    const int mb = m0 + wm * (BMT / 2) + half * 64, nb = n0 + wn * 64;
+    const int mb = m0 + wm * 64 + half * 32, nb = n0 + wn * 64;
     if (!vt) {
 #pragma unroll 4
-      for (int it = 0; it < 16; it++) {
+      for (int it = 0; it < 8; it++) {
         const int idx = it * 64 + lane;
         const int row = idx >> 4, c4 = (idx & 15) * 4;
         if (mb + row < M) epi_row4<EPI, TO>(e, mb + row, nb + c4, *(const float4*)(ct + row * CLD + c4));
@@ -264,9 +263,9 @@ __global__ __launch_bounds__(256, BMT == 128 ? 2 : 1) void gemm_big_kernel(
     } else {
       if constexpr (EPI == EPI_QKV) {
 #pragma unroll 4
-        for (int it = 0; it < 16; it++) {
+        for (int it = 0; it < 8; it++) {
           const int idx = it * 64 + lane;
-          const int col = idx >> 4, r4 = (idx & 15) * 4;
+          const int col = idx >> 3, r4 = (idx & 7) * 4;
           const int m = mb + r4;
           if (m + 3 < M) {
             float4 v = {ct[r4 * CLD + col], ct[(r4 + 1) * CLD + col], ct[(r4 + 2) * CLD + col],
@@ -492,12 +491,10 @@ static double gemm_bytes(int M, int N, int K, int ea, int eb, int eo) {
 template <int EPI, typename TO>
 static hipError_t launch_big(hipStream_t s, int M, int N, int K, const void* A, int lda,
                              const void* B, int ldb, const EpiArgs& e) {
-  const int ntn = N / big::BN;
+  const int ntn = N / big2::BN;
   TimingScope ts(s, KC_GEMM_BIG, gemm_bytes<EPI>(M, N, K, 2, 2, sizeof(TO)), 2.0 * M * N * K);
-  // 256-row tiles need 110 KB of LDS (one workgroup per CU) and measured
-  // slower than two 128-row workgroups per CU
-  const int ntm = (M + 127) / 128;
-  hipLaunchKernelGGL((gemm_big_kernel<128, EPI, TO>), dim3(ntm * ntn), dim3(256), 0, s,
+  const int ntm = (M + big2::BM - 1) / big2::BM;
+  hipLaunchKernelGGL((gemm_big_kernel<EPI, TO>), dim3(ntm * ntn), dim3(256), 0, s,
                      (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, e);
   return hipGetLastError();
 }
@@ -576,7 +573,7 @@ static hipError_t gemm_epi(hipStream_t s, int adt, int bdt, int M, int N, int K,
                        (ldb % 8 == 0);
   if (adt == WAM_BF16 && bdt == WAM_BF16 && aligned && K % 64 == 0) {
     if (skinny_ok(M, N, K)) return launch_skinny<EPI, TO>(s, M, N, K, A, lda, B, ldb, e, 1, nullptr);
-    if (N % big::BN == 0) return launch_big<EPI, TO>(s, M, N, K, A, lda, B, ldb, e);
+    if (N % big2::BN == 0) return launch_big<EPI, TO>(s, M, N, K, A, lda, B, ldb, e);
   }
   if (adt == WAM_F32 && bdt == WAM_F32)
     return launch_simple<float, float, EPI, TO>(s, M, N, K, A, lda, B, ldb, e);

@@ -291,7 +291,8 @@ void plan_action(Arena& a, const wam_dims* d, int B, int max_len, bool with_emb,
 
 void plan_prefill(Arena& a, const wam_dims* d, int Fh, int Ff, Bufs& b, float** z) {
   const size_t e = esz(d->dtype);
-  const size_t T = (size_t)std::max(Fh, Ff) * d->P;
+  // history and future rows share one pass when the future is not denoised
+  const size_t T = (size_t)(Fh + Ff) * d->P;
   const size_t Tf = (size_t)Ff * d->P;
   b.emb = (float*)a.take((size_t)(WAM_MAX_STEPS + 2) * d->D * 4);
   b.X = (float*)a.take(T * d->D * 4);
@@ -449,6 +450,27 @@ int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video, const 
     const int Th = nh[b] * P;
     auto kl = [&](int l) { return (char*)cache->k + l * ls + b * ep; };
     auto vl = [&](int l) { return (char*)cache->v + l * ls + b * ep; };
+    if (video_steps == 0 && Ff > 0) {
+      // No video denoising: the history rows and the future rows go through
+      // the same layers, so one pass over all of them (history rows see only
+      // history keys through the block-causal frame table) replaces the
+      // history pass plus the future cache pass.
+      if (Th > 0)
+        HIPCK(embed(s, dt, dt, hist, hmaps[b], video->w_in, emb_hist, bufs.X, Th, D, d->Cv));
+      HIPCK(copy_cvt_f32(s, dt, (const char*)fut_noise + (size_t)b * Tf * d->Cv * esz(dt), z,
+                         (int64_t)Tf * d->Cv));
+      HIPCK(embed(s, WAM_F32, dt, z, zmap, video->w_in, emb_last, bufs.X + (size_t)Th * D, Tf, D,
+                  d->Cv));
+      for (int l = 0; l < d->L; l++)
+        if ((st = video_layer(c, video->layers[l], Th + Tf, 0, tabs[b], kl(l), vl(l), cache->cap,
+                              l == d->L - 1)))
+          return st;
+      if (fut_latents_out)
+        HIPCK(hipMemcpyAsync(fut_latents_out + (size_t)b * Tf * d->Cv, z,
+                             (size_t)Tf * d->Cv * 4, hipMemcpyDeviceToDevice, s));
+      cache->len[b] = tabs[b].n * P;
+      continue;
+    }
     if (Th > 0) {
       HIPCK(embed(s, dt, dt, hist, hmaps[b], video->w_in, emb_hist, bufs.X, Th, D, d->Cv));
       for (int l = 0; l < d->L; l++)
