@@ -387,7 +387,7 @@ struct ActGeom {
 // Split (b, h, s): cache keys [s*kc[b], min(len, (s+1)*kc[b])) for s < ncs(b),
 // the chunk's own keys for s == ncs(b).  Writes the split's (m, l, o) in the
 // log2 domain: m [32], l [32], o [32][64] (unnormalised).
-__global__ __launch_bounds__(256) void attn_action_kernel(
+__global__ __launch_bounds__(256, 3) void attn_action_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ ka, const bf16_t* __restrict__ va,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, ActGeom G,
     float* __restrict__ part, float sl2) {
@@ -431,35 +431,43 @@ __global__ __launch_bounds__(256) void attn_action_kernel(
   const bf16x8 ones = ones_row(c16);
   const int kq[2] = {key1, key1};
   for (int kt = key0 + w * KT; kt < key1; kt += 4 * KT) {
-    // ---- loads: K rows (A of S^T) and V^T rows (A of P V), zero past key1
+    // ---- loads: K rows (A of S^T) and V^T rows (A of P V).  All loads are
+    // unconditional so that they are in flight together: K rows past key1
+    // read row key1 - 1 (their scores are masked to -inf), V^T chunks that
+    // start past key1 read the row's first chunk and are zeroed below.
     bf16x8 ak[4][2], av[4][2];
 #pragma unroll
     for (int sub = 0; sub < 4; sub++) {
-      const int key = kt + perm_key(sub, c16);
+      const int key = min(kt + perm_key(sub, c16), key1 - 1);
 #pragma unroll
       for (int ss = 0; ss < 2; ss++)
-        ak[sub][ss] = (key < key1) ? *(const bf16x8*)(kb + (long long)key * 64 + 32 * ss + 8 * g)
-                                   : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        ak[sub][ss] = *(const bf16x8*)(kb + (long long)key * 64 + 32 * ss + 8 * g);
     }
 #pragma unroll
     for (int d = 0; d < 4; d++)
 #pragma unroll
       for (int wd = 0; wd < 2; wd++) {
         const int k0 = kt + 32 * wd + 8 * g;
-        bf16x8 x = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        if (k0 < key1) x = *(const bf16x8*)(vb + (long long)(16 * d + c16) * vld + k0);
-        if (k0 + 8 > key1) {
-#pragma unroll
-          for (int j = 0; j < 8; j++)
-            if (k0 + j >= key1) x[j] = 0;
-        }
-        av[d][wd] = x;
+        av[d][wd] = *(const bf16x8*)(vb + (long long)(16 * d + c16) * vld + (k0 < key1 ? k0 : key0));
       }
+    const bool tail = kt + KT > key1;  // wave-uniform
+    if (tail) {
+      // P is zero past key1, but 0 * V must not meet a non-finite V
+#pragma unroll
+      for (int wd = 0; wd < 2; wd++) {
+        const int k0 = kt + 32 * wd + 8 * g;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+          if (k0 + j >= key1)
+#pragma unroll
+            for (int d = 0; d < 4; d++) av[d][wd][j] = 0;
+      }
+    }
     // ---- S^T, softmax, P V
     floatx4 sacc[4][2];
     tile_scores(sacc, qf, [&](int sub, int ss) { return ak[sub][ss]; });
     auto vop = [&](int d, int wd) { return av[d][wd]; };
-    if (kt + KT > key1) tile_mask(sacc, kt, kq, g);
+    if (tail) tile_mask(sacc, kt, kq, g);
     tile_update(acc, sacc, sl2, ones, vop);
   }
   // ---- per-wave state to LDS (waves without keys hold m = -inf, l = 0, o = 0)

@@ -89,10 +89,17 @@ template <int EPI, typename TO>
 __device__ inline void epi_row4(const EpiArgs& e, int m, int n, float4 v) {
   if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
     if (EPI == EPI_GELU) {
-      v.x = gelu_f(v.x);
-      v.y = gelu_f(v.y);
-      v.z = gelu_f(v.z);
-      v.w = gelu_f(v.w);
+      if constexpr (sizeof(TO) == 2) {
+        v.x = gelu_bf16out(v.x);
+        v.y = gelu_bf16out(v.y);
+        v.z = gelu_bf16out(v.z);
+        v.w = gelu_bf16out(v.w);
+      } else {
+        v.x = gelu_f(v.x);
+        v.y = gelu_f(v.y);
+        v.z = gelu_f(v.z);
+        v.w = gelu_f(v.w);
+      }
     }
     TO* p = (TO*)e.out + (long long)m * e.ldo + n;
     if constexpr (sizeof(TO) == 2)
@@ -208,31 +215,66 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     for (int j = 0; j < 4; j++) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / BK, x7 = c16 & 7;
+  // residual epilogue: this lane's X values (rows it*4 + g of each 32-row
+  // half, columns 4*c16..+3), loaded a few k steps before the end so that the
+  // read overlaps the MFMAs; rows past M are clamped and never stored
+  float4 xr[2][8];
+  auto xload = [&] {
+#pragma unroll
+    for (int half = 0; half < 2; half++)
+#pragma unroll
+      for (int it = 0; it < 8; it++) {
+        const int m = min(m0 + wm * 64 + half * 32 + it * 4 + g, M - 1);
+        xr[half][it] = *(const float4*)((const float*)e.out + (long long)m * e.ldo + n0 + wn * 64 + c16 * 4);
+      }
+  };
+  const int kx = max(nk - 4, 0);
   issue(0, 0);
   for (int kt = 0; kt < nk; kt++) {
+    if constexpr (EPI == EPI_RESID)
+      if (kt == kx) xload();
     __syncthreads();  // waits for this wave's loads of stage kt, then for everyone's
     const char* sa = smem + (kt & 1) * STAGE;
     const char* sb = sa + BM * 128;
-    bf16x8 af[2][4], bfr[2][4];
+    if constexpr (EPI != EPI_RESID) {
+      bf16x8 af[2][4], bfr[2][4];
 #pragma unroll
-    for (int s = 0; s < 2; s++) {
-      const int slot = ((4 * s + g) ^ x7) * 16;
+      for (int s = 0; s < 2; s++) {
+        const int slot = ((4 * s + g) ^ x7) * 16;
 #pragma unroll
-      for (int i = 0; i < 4; i++) af[s][i] = *(const bf16x8*)(sa + (wm * 64 + i * 16 + c16) * 128 + slot);
+        for (int i = 0; i < 4; i++) af[s][i] = *(const bf16x8*)(sa + (wm * 64 + i * 16 + c16) * 128 + slot);
 #pragma unroll
-      for (int j = 0; j < 4; j++) bfr[s][j] = *(const bf16x8*)(sb + (wn * 64 + j * 16 + c16) * 128 + slot);
+        for (int j = 0; j < 4; j++) bfr[s][j] = *(const bf16x8*)(sb + (wn * 64 + j * 16 + c16) * 128 + slot);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // the other buffer was last read in step kt - 1, which every wave has left
+      if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 2; s++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
+    } else {
+      // the prefetched X tile holds 64 registers: fragments one 32-wide k half at a time
+      if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+#pragma unroll
+      for (int s = 0; s < 2; s++) {
+        const int slot = ((4 * s + g) ^ x7) * 16;
+        bf16x8 af[4], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) af[i] = *(const bf16x8*)(sa + (wm * 64 + i * 16 + c16) * 128 + slot);
+#pragma unroll
+        for (int j = 0; j < 4; j++) bfr[j] = *(const bf16x8*)(sb + (wn * 64 + j * 16 + c16) * 128 + slot);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // the other buffer was last read in step kt - 1, which every wave has left
-    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 2; s++)
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
   }
   __syncthreads();  // operand buffers become the C staging area
 
@@ -253,7 +295,21 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
     const int mb = m0 + wm * 64 + half * 32, nb = n0 + wn * 64;
-    if (!vt) {
+    if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+      for (int it = 0; it < 8; it++) {
+        const int row = it * 4 + g, c4 = c16 * 4;
+        if (mb + row < M) {
+          const float4 v = *(const float4*)(ct + row * CLD + c4);
+          float4 x = xr[half][it];
+          x.x += v.x;
+          x.y += v.y;
+          x.z += v.z;
+          x.w += v.w;
+          *(float4*)((float*)e.out + (long long)(mb + row) * e.ldo + nb + c4) = x;
+        }
+      }
+    } else if (!vt) {
 #pragma unroll 4
       for (int it = 0; it < 8; it++) {
         const int idx = it * 64 + lane;

@@ -52,6 +52,24 @@ template <> __device__ inline bf16_t from_f<bf16_t>(float v) { return dev_f2bf(v
 
 __device__ inline float gelu_f(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
 
+// GELU for results rounded to bf16 next: x Phi(x) with the normal tail
+// 1 - Phi(|x|) = erfc(z)/2, z = |x|/sqrt 2, from Abramowitz & Stegun 7.1.26,
+// erfc(z) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1/(1 + p z),
+// absolute error <= 1.5e-7 (some 2^-22, far below the 2^-9 bf16 step).  The
+// tail is used directly for x < 0, so small Phi keeps its relative accuracy.
+__device__ inline float gelu_bf16out(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float poly = fmaf(t, 1.061405429f, -1.453152027f);
+  poly = fmaf(t, poly, 1.421413741f);
+  poly = fmaf(t, poly, -0.284496736f);
+  poly = fmaf(t, poly, 0.254829592f);
+  // exp(-z^2) = 2^(-z^2 log2 e); the argument underflows cleanly to 0 for large z
+  const float e = __builtin_amdgcn_exp2f(-(z * z) * 1.44269504088896341f);
+  const float tail = 0.5f * t * poly * e;  // 1 - Phi(|x|)
+  return x * (x >= 0.f ? 1.0f - tail : tail);
+}
+
 // ---------------------------------------------------------------- block table
 // Compacted frames of one episode: tokens of compacted frame i occupy cache
 // rows [i*P, (i+1)*P); a query in compacted frame i sees rows [0, kend[i]).
@@ -97,7 +115,8 @@ __device__ inline void epi_store(const EpiArgs& e, int m, int n, float v) {
   if constexpr (EPI == EPI_STORE) {
     ((TO*)e.out)[(long long)m * e.ldo + n] = from_f<TO>(v);
   } else if constexpr (EPI == EPI_GELU) {
-    ((TO*)e.out)[(long long)m * e.ldo + n] = from_f<TO>(gelu_f(v));
+    ((TO*)e.out)[(long long)m * e.ldo + n] =
+        from_f<TO>(sizeof(TO) == 2 ? gelu_bf16out(v) : gelu_f(v));
   } else if constexpr (EPI == EPI_RESID) {
     ((float*)e.out)[(long long)m * e.ldo + n] += v;
   } else if constexpr (EPI == EPI_EULER) {

@@ -86,6 +86,8 @@ def _action_case(rng, dt, B, Hh, lens, n_act, cap=None):
     for b, n in enumerate(lens):
         K[b, :, n:] = np.nan
         V[b, :, n:] = np.nan
+    ka[:, :, n_act:] = np.nan   # own-key rows past n_act must never be used
+    va[:, :, n_act:] = np.nan
     return q, ka, va, K, V, cap
 
 
@@ -141,6 +143,7 @@ def test_attention_action_zero_query_is_mean(dt):
     ("C4-like", 4, 16, [27280] * 4, 32),
     ("ragged", 3, 4, [100, 3000, 777], 32),
     ("no-own", 2, 4, [513, 64], 0),
+    ("partial-own", 2, 4, [300, 129], 20),
 ])
 def test_attention_action_vs_oracle(shape):
     name, B, Hh, lens, n_act = shape
