@@ -50,12 +50,6 @@ __device__ inline float wave_sum16x4(float v) {
 __device__ inline int perm_key(int sub, int r) {
   return 32 * (sub >> 1) + 8 * (r >> 2) + (r & 3) + 4 * (sub & 1);
 }
-// inverse: the (sub, r) slot 16*sub + r that holds key k of the tile
-__device__ inline int key_slot(int k) {
-  const int j = k & 31;
-  return 16 * (2 * (k >> 5) + ((j >> 2) & 1)) + 4 * (j >> 3) + (j & 3);
-}
-
 // Running softmax state of one wave: 32 queries (two 16-column tiles).
 // o[0..3][t] are the O^T accumulators (head dim x query); o[4][t] row 0 holds
 // the row sums, accumulated by the same P V MFMA against a row of ones, so
@@ -175,7 +169,7 @@ __device__ inline void tile_scores(floatx4 (&sacc)[4][2], const bf16x8 (&qf)[2][
 namespace pf {
 constexpr int QW = 32, NW = 4, QT = QW * NW;  // queries per wave / per workgroup
 constexpr int KT = 64;                        // keys per tile
-constexpr int LD = 64 + 8;                    // LDS row stride (bf16)
+constexpr int TILE = KT * 128;                // bytes of one K tile (= one V^T tile)
 }
 
 // Workgroups are dealt round-robin to the 8 XCDs.  Give every XCD whole heads
@@ -192,12 +186,20 @@ __device__ inline void prefill_block(int bid, int Hh, int ntq, int* h, int* qt) 
   }
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// K and V^T tiles go from global memory straight into LDS (global_load_lds:
+// lane i of a wave fills bytes [16i, 16i+16) of the destination).  Both use
+// 128-byte rows of 8 16-byte chunks, chunk c of row r stored at slot
+// c ^ (r & 7): the 16-byte fragment reads of 16 consecutive rows are then
+// free of bank conflicts.  K row j of the tile holds the key whose S^T slot is
+// j, so each lane fetches the key that belongs at its LDS position.  Two
+// stages, one barrier per tile.
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     bf16_t* __restrict__ out, int nq, int row0, int cap, int Hh, FrameTab tab, float sl2) {
   using namespace pf;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * LD];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[2][64 * LD];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // [stage][K | V^T]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int ntq = (nq + QT - 1) / QT;
   int h, qt;
@@ -225,72 +227,77 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   acc_init(acc);
   const bf16x8 ones = ones_row(c16);
 
-  // staging of one K tile (token rows, stored at their S^T slot) and one V^T
-  // tile (head-dim rows): 2 x 16 B of each per thread
-  u32x4 rk[2], rv[2];
-  int krow[2], kslot[2], ch8[2];
+  // Load instruction i of wave w fills tile rows 8(4i + w) .. +7; lane l
+  // covers row 8(4i + w) + l/8, slot l%8, i.e. chunk (l%8) ^ (row & 7).
+  // K rows stay inside the cache (kt + 64 <= cap); rows past kend_max are
+  // masked, V^T columns past kend_max are zeroed after the tile lands.
+  const int lrow = lane >> 3, lkc = (lane & 7) ^ lrow;
+  long long koff[2], voff[2];
 #pragma unroll
   for (int i = 0; i < 2; i++) {
-    const int c = tid + 256 * i;
-    krow[i] = c >> 3;
-    ch8[i] = (c & 7) * 8;
-    kslot[i] = key_slot(krow[i]);
+    const int row = (4 * i + w) * 8 + lrow;
+    koff[i] = (long long)perm_key(row >> 4, row & 15) * 64 + lkc * 8;
+    voff[i] = (long long)row * cap + lkc * 8;
   }
-  auto gload = [&](int kt) {
-    if (kt + KT <= kend_max) {  // whole tile valid: plain 16-byte loads
+  auto issue = [&](int kt, int buf) {
+    char* sk = smem + buf * 2 * TILE;
+    char* sv = sk + TILE;
 #pragma unroll
-      for (int i = 0; i < 2; i++) {
-        rk[i] = *(const u32x4*)(kh + (long long)(kt + krow[i]) * 64 + ch8[i]);
-        rv[i] = *(const u32x4*)(vh + (long long)krow[i] * cap + kt + ch8[i]);
-      }
-      return;
-    }
+    for (int i = 0; i < 2; i++)
+      __builtin_amdgcn_global_load_lds((const void*)(kh + (long long)kt * 64 + koff[i]),
+                                       (lds_ptr_t)(sk + (4 * i + w) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-      const int key = kt + krow[i];
-      rk[i] = (key < kend_max) ? *(const u32x4*)(kh + (long long)key * 64 + ch8[i])
-                               : u32x4{0u, 0u, 0u, 0u};
-      const int k0 = kt + ch8[i];
-      u32x4 x = u32x4{0u, 0u, 0u, 0u};
-      if (k0 < kend_max) x = *(const u32x4*)(vh + (long long)krow[i] * cap + k0);
-      if (k0 + 8 > kend_max) {
-        bf16_t* e = (bf16_t*)&x;
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-          if (k0 + j >= kend_max) e[j] = 0;
-      }
-      rv[i] = x;
-    }
-  };
-  auto lstore = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-      *(u32x4*)(&sK[b][kslot[i] * LD + ch8[i]]) = rk[i];
-      *(u32x4*)(&sV[b][krow[i] * LD + ch8[i]]) = rv[i];
-    }
+    for (int i = 0; i < 2; i++)
+      __builtin_amdgcn_global_load_lds((const void*)(vh + kt + voff[i]),
+                                       (lds_ptr_t)(sv + (4 * i + w) * 1024), 16, 0, 0);
   };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  int cur = 0;
+  const int x7 = c16 & 7;
+  // every issued tile is waited for inside the loop (no LDS write may land
+  // after the workgroup has left)
+  if (kend_max > 0) issue(0, 0);
   for (int kt = 0; kt < kend_max; kt += KT) {
-    const bool nxt = kt + KT < kend_max;
-    if (nxt) gload(kt + KT);
+    const int buf = (kt / KT) & 1;
+    char* sk = smem + buf * 2 * TILE;
+    char* sv = sk + TILE;
+    wait_vmem();      // this wave's transfers of the tile have landed in LDS,
+    __syncthreads();  // then everyone's
+    if (kt + KT > kend_max) {
+      // tail tile: V^T columns past kend_max may hold anything (0 * NaN)
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        const int c = tid + 256 * i, row = c >> 3, slot = c & 7, ch = slot ^ (row & 7);
+        const int k0 = kt + 8 * ch;
+        if (k0 + 8 > kend_max) {
+          bf16x8* p = (bf16x8*)(sv + row * 128 + slot * 16);
+          bf16x8 x = *p;
+#pragma unroll
+          for (int j = 0; j < 8; j++)
+            if (k0 + j >= kend_max) x[j] = 0;
+          *p = x;
+        }
+      }
+      __syncthreads();
+    }
+    bf16x8 kf[4][2], vf[4][2];
+#pragma unroll
+    for (int sub = 0; sub < 4; sub++)
+#pragma unroll
+      for (int s = 0; s < 2; s++)
+        kf[sub][s] = *(const bf16x8*)(sk + (16 * sub + c16) * 128 + (((4 * s + g) ^ x7) * 16));
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+#pragma unroll
+      for (int wd = 0; wd < 2; wd++)
+        vf[d][wd] = *(const bf16x8*)(sv + (16 * d + c16) * 128 + (((4 * wd + g) ^ x7) * 16));
+    __builtin_amdgcn_sched_barrier(0);
+    // the other stage was last read in the previous tile, which every wave has left
+    if (kt + KT < kend_max) issue(kt + KT, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
     floatx4 sacc[4][2];
-    const bf16_t* sk = sK[cur];
-    tile_scores(sacc, qf, [&](int sub, int s) {
-      return *(const bf16x8*)(sk + (16 * sub + c16) * LD + 32 * s + 8 * g);
-    });
-    const bf16_t* sv = sV[cur];
-    auto vop = [&](int d, int wd) {
-      return *(const bf16x8*)(sv + (16 * d + c16) * LD + 32 * wd + 8 * g);
-    };
+    tile_scores(sacc, qf, [&](int sub, int s) { return kf[sub][s]; });
     if (kt + KT > kend_min) tile_mask(sacc, kt, kq, g);
-    tile_update(acc, sacc, sl2, ones, vop);
-    if (nxt) lstore(cur ^ 1);
-    __syncthreads();
-    cur ^= 1;
+    tile_update(acc, sacc, sl2, ones, [&](int d, int wd) { return vf[d][wd]; });
   }
   const int D = Hh * 64;
 #pragma unroll

@@ -229,11 +229,14 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       }
   };
   const int kx = max(nk - 4, 0);
-  issue(0, 0);
+  // every issued stage is waited for inside the loop (no LDS write may land
+  // after the workgroup has left)
+  if (nk > 0) issue(0, 0);
   for (int kt = 0; kt < nk; kt++) {
     if constexpr (EPI == EPI_RESID)
       if (kt == kx) xload();
-    __syncthreads();  // waits for this wave's loads of stage kt, then for everyone's
+    wait_vmem();      // this wave's transfers of stage kt have landed in LDS,
+    __syncthreads();  // then everyone's
     const char* sa = smem + (kt & 1) * STAGE;
     const char* sb = sa + BM * 128;
     if constexpr (EPI != EPI_RESID) {

@@ -52,6 +52,12 @@ template <> __device__ inline bf16_t from_f<bf16_t>(float v) { return dev_f2bf(v
 
 __device__ inline float gelu_f(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
 
+// Wait until every vector-memory load of this wave has completed, including
+// global_load_lds transfers into LDS.  A barrier alone does not imply this:
+// its lowering waits for LDS instructions but not necessarily for those
+// transfers.  (s_waitcnt vmcnt(0), expcnt and lgkmcnt left free.)
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // GELU for results rounded to bf16 next: x Phi(x) with the normal tail
 // 1 - Phi(|x|) = erfc(z)/2, z = |x|/sqrt 2, from Abramowitz & Stegun 7.1.26,
 // erfc(z) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1/(1 + p z),

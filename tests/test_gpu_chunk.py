@@ -107,6 +107,32 @@ def test_determinism_and_padding_invariance():
     assert not torch.equal(a.actions, d.actions)
 
 
+@pytest.mark.parametrize("name", ["C3", "C1"])
+def test_prefill_reads_only_written_memory(name):
+    """With the cache and both workspaces poisoned (NaN / 0xFF bytes), every
+    cache row below len, the future latents and the actions come out finite:
+    no kernel reads memory the chunk has not written (tiles staged in LDS
+    included), and the ragged key tiles of 880-token frames are masked."""
+    import torch
+    from kv_cached_flow_amd.runner import DeviceChunk
+    cfg = configs.get(name, L=2, read_map=(0, 1), fuse=None)
+    print_case(f"{name} shapes, 2 layers, poisoned buffers")
+    inp = inputs.generate(cfg)
+    for _ in range(2):
+        dc = DeviceChunk(cfg, inp)
+        dc.cache.k.fill_(float("nan"))
+        dc.cache.v.fill_(float("nan"))
+        dc.ws_prefill.fill_(0xFF)
+        dc.ws_denoise.fill_(0xFF)
+        dc.run()
+        torch.cuda.synchronize()
+        n = int(dc.cache.len[0])
+        assert torch.isfinite(dc.cache.k[:, :, :, :n].float()).all()
+        assert torch.isfinite(dc.cache.v[:, :, :, :, :n].float()).all()
+        assert torch.isfinite(dc.z).all()
+        assert torch.isfinite(dc.actions).all()
+
+
 def test_batch_independence():
     import torch
     cfg2 = configs.small("B2", dtype="bf16", **dict(SMALL, B=2))
