@@ -111,7 +111,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="C1")
-    ap.add_argument("--cpu-layers", type=int, default=3)
+    ap.add_argument("--cpu-layers", type=int, default=10,
+                    help="layers per expert in the CPU oracle sample (about 1.1 s each for C1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--minimal", action="store_true",
                     help="only warmup + timed chunks (for counter collection)")
