@@ -603,20 +603,24 @@ __global__ __launch_bounds__(64) void attn_action_f32_kernel(const float* __rest
   for (int d = 0; d < 64; d++) orow[d] = o[d] * inv;
 }
 
-// Keys per split for one episode: a function of that episode's length only,
-// so an episode is split identically whatever the batch (batch independence
-// is bitwise).  Whole 256-key groups (one 64-key tile per wave of the
-// workgroup), as few per split as keeps the split count within the merge's
-// limit; an explicit hint (tests) asks for a split count instead.
-static int action_chunk(int len, int splits_hint) {
+// Keys per split for one episode: a function of that episode's length, the
+// head count and the device only, so an episode is split identically
+// whatever the batch (batch independence is bitwise).  Measured on MI355X,
+// about one workgroup per CU for a single episode is best: n_cu / Hh - 1
+// cache splits (plus the own-key split) of whole 64-key tiles, at most 63.
+// An explicit hint (tests) asks for a split count instead.
+static int action_chunk(int len, int Hh, int splits_hint) {
   if (len <= 0) return 0;
-  if (splits_hint > 0) {
-    int kc = (len + splits_hint - 1) / splits_hint;
-    return (kc + act::KT - 1) / act::KT * act::KT;
+  int splits = splits_hint;
+  if (splits <= 0) {
+    int dev = 0, n_cu = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n_cu = 256;
+    splits = std::max(1, std::min(act::MAX_SPLITS - 1, n_cu / std::max(Hh, 1) - 1));
   }
-  const int group = 4 * act::KT;
-  const int per = (len + group * (act::MAX_SPLITS - 1) - 1) / (group * (act::MAX_SPLITS - 1));
-  return group * per;
+  const int kc = (len + splits - 1) / splits;
+  return (kc + act::KT - 1) / act::KT * act::KT;
 }
 
 size_t attn_action_scratch_bytes(int B, int Hh, int H, int max_len, int splits_hint) {
@@ -641,7 +645,7 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* 
   for (int b = 0; b < B; b++) keys += (double)G.lens.len[b] + n_act;
   const int es = dt == WAM_BF16 ? 2 : 4;
   if (splits_hint >= act::MAX_SPLITS) return hipErrorInvalidValue;
-  for (int b = 0; b < B; b++) G.kc[b] = kc ? action_chunk(G.lens.len[b], splits_hint) : 0;
+  for (int b = 0; b < B; b++) G.kc[b] = kc ? action_chunk(G.lens.len[b], Hh, splits_hint) : 0;
   if (dt == WAM_F32) {
     G.S = 0;
     TimingScope ts(s, KC_ATTN_ACTION, keys * Hh * 64 * 2 * es + 2.0 * B * H * Hh * 64 * es,

@@ -58,6 +58,16 @@ __device__ inline float gelu_f(float v) { return 0.5f * v * (1.0f + erff(v * 0.7
 // transfers.  (s_waitcnt vmcnt(0), expcnt and lgkmcnt left free.)
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(n) lgkmcnt(0) (n < 64), then a workgroup barrier that
+// does not wait for the remaining loads: stages still in flight stay in
+// flight.  The memory clobber keeps LDS accesses on their side of it.
+template <int n>
+__device__ inline void barrier_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4));
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // GELU for results rounded to bf16 next: x Phi(x) with the normal tail
 // 1 - Phi(|x|) = erfc(z)/2, z = |x|/sqrt 2, from Abramowitz & Stegun 7.1.26,
 // erfc(z) ~ t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1/(1 + p z),
