@@ -157,47 +157,136 @@ hipError_t rmsnorm_accum(hipStream_t s, int odt, float* x, const float* part, in
 
 // ------------------------------------------------------------ embedding
 // X[m][n] = sum_c x[row(m)][c] * w_in[n][c] + emb[n]  (C <= 64, fp32 FMA in c order)
-constexpr int EMB_ROWS = 32, EMB_MAXC = 64;
+//
+// A workgroup computes a 64-row x 128-column tile: x rows and the W_in slice
+// (transposed, so a thread reads its 4 columns as one float4) are staged in
+// LDS as fp32; each thread accumulates an 8 x 4 register tile and writes
+// 16-byte rows.
+constexpr int EMB_MAXC = 64, EMB_BM = 64, EMB_BN = 128;
+
+// four consecutive elements as fp32 (8- or 16-byte load; p 8/16-byte aligned)
+__device__ inline void load4(const float* p, float (&v)[4]) {
+  const float4 a = *(const float4*)p;
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+__device__ inline void load4(const bf16_t* p, float (&v)[4]) {
+  const uint2 a = *(const uint2*)p;
+  v[0] = __uint_as_float(a.x << 16);
+  v[1] = __uint_as_float(a.x & 0xFFFF0000u);
+  v[2] = __uint_as_float(a.y << 16);
+  v[3] = __uint_as_float(a.y & 0xFFFF0000u);
+}
 
 template <typename TX, typename TW>
 __global__ __launch_bounds__(256) void embed_kernel(const TX* __restrict__ x, RowMap map,
                                                     const TW* __restrict__ w_in,
                                                     const float* __restrict__ emb,
                                                     float* __restrict__ X, int M, int D, int C) {
-  __shared__ float xs[EMB_ROWS][EMB_MAXC];
-  const int m0 = blockIdx.x * EMB_ROWS;
-  const int n = blockIdx.y * 256 + threadIdx.x;
-  for (int i = threadIdx.x; i < EMB_ROWS * C; i += 256) {
-    int r = i / C, c = i - r * C;
-    int m = m0 + r;
-    float v = 0.f;
+  __shared__ __attribute__((aligned(16))) float xs[EMB_BM][EMB_MAXC + 4];
+  __shared__ __attribute__((aligned(16))) float ws[EMB_MAXC][EMB_BN];
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.x * EMB_BM, n0 = blockIdx.y * EMB_BN;
+  if (C % 16 == 0) {
+    // four threads per x row (C/4 values each, whole 16-byte pieces), one
+    // row-map lookup per thread; all loads independent
+    const int r = tid >> 2, q = tid & 3, cq = C / 4, m = m0 + r;
     if (m < M) {
-      int f = m / map.P, t = m - f * map.P;
-      v = to_f<TX>(x[((long long)map.src[f] * map.P + t) * C + c]);
+      const int f = m / map.P, t = m - f * map.P;
+      const TX* xr = x + ((long long)map.src[f] * map.P + t) * C + q * cq;
+      for (int c = 0; c < cq; c += 4) {
+        float v[4];
+        load4(xr + c, v);
+#pragma unroll
+        for (int j = 0; j < 4; j++) xs[r][q * cq + c + j] = v[j];
+      }
+    } else {
+      for (int c = 0; c < cq; c++) xs[r][q * cq + c] = 0.f;
     }
-    xs[r][c] = v;
+    // two threads per weight row; consecutive lanes hold consecutive columns
+    // n, so the transposed LDS writes of a wave hit consecutive banks
+    const int n = tid & (EMB_BN - 1), half = tid >> 7, ch = C / 2;
+    const TW* wr = w_in + (long long)(n0 + n) * C + half * ch;
+    const bool ok = n0 + n < D;
+    for (int c = 0; c < ch; c += 4) {
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (ok) load4(wr + c, v);
+#pragma unroll
+      for (int j = 0; j < 4; j++) ws[half * ch + c + j][n] = v[j];
+    }
+  } else {
+    for (int i = tid; i < EMB_BM * C; i += 256) {
+      const int r = i / C, c = i - r * C, m = m0 + r;
+      float v = 0.f;
+      if (m < M) {
+        const int f = m / map.P, t = m - f * map.P;
+        v = to_f<TX>(x[((long long)map.src[f] * map.P + t) * C + c]);
+      }
+      xs[r][c] = v;
+    }
+    for (int i = tid; i < EMB_BN * C; i += 256) {
+      const int n = i & (EMB_BN - 1), c = i / EMB_BN;
+      ws[c][n] = (n0 + n < D) ? to_f<TW>(w_in[(long long)(n0 + n) * C + c]) : 0.f;
+    }
   }
   __syncthreads();
-  if (n >= D) return;
-  float w[EMB_MAXC];
+  const int cg = tid & 31, rg = tid >> 5;  // columns 4cg..4cg+3, rows 8rg..8rg+7
+  float acc[8][4];
 #pragma unroll
-  for (int c = 0; c < EMB_MAXC; c++) w[c] = (c < C) ? to_f<TW>(w_in[(long long)n * C + c]) : 0.f;
-  const float en = emb[n];
-  const int rows = min(EMB_ROWS, M - m0);
-  for (int r = 0; r < rows; r++) {
-    float acc = 0.f;
+  for (int r = 0; r < 8; r++)
 #pragma unroll
-    for (int c = 0; c < EMB_MAXC; c++)
-      if (c < C) acc = fmaf(xs[r][c], w[c], acc);
-    X[(long long)(m0 + r) * D + n] = acc + en;
+    for (int j = 0; j < 4; j++) acc[r][j] = 0.f;
+  auto step = [&](int c, float xv[8]) {
+    const float4 wv = *(const float4*)&ws[c][4 * cg];
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      acc[r][0] = fmaf(xv[r], wv.x, acc[r][0]);
+      acc[r][1] = fmaf(xv[r], wv.y, acc[r][1]);
+      acc[r][2] = fmaf(xv[r], wv.z, acc[r][2]);
+      acc[r][3] = fmaf(xv[r], wv.w, acc[r][3]);
+    }
+  };
+  int c = 0;
+  for (; c + 4 <= C; c += 4) {  // x values of 8 rows x 4 c as 16-byte reads
+    float4 xq[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) xq[r] = *(const float4*)&xs[8 * rg + r][c];
+    float xv[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) xv[r] = xq[r].x;
+    step(c, xv);
+#pragma unroll
+    for (int r = 0; r < 8; r++) xv[r] = xq[r].y;
+    step(c + 1, xv);
+#pragma unroll
+    for (int r = 0; r < 8; r++) xv[r] = xq[r].z;
+    step(c + 2, xv);
+#pragma unroll
+    for (int r = 0; r < 8; r++) xv[r] = xq[r].w;
+    step(c + 3, xv);
+  }
+  for (; c < C; c++) {
+    float xv[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) xv[r] = xs[8 * rg + r][c];
+    step(c, xv);
+  }
+  const int n = n0 + 4 * cg;
+  if (n >= D) return;  // D is a multiple of 4
+  const float4 e = *(const float4*)(emb + n);
+#pragma unroll
+  for (int r = 0; r < 8; r++) {
+    const int m = m0 + 8 * rg + r;
+    if (m < M)
+      *(float4*)(X + (long long)m * D + n) =
+          float4{acc[r][0] + e.x, acc[r][1] + e.y, acc[r][2] + e.z, acc[r][3] + e.w};
   }
 }
 
 hipError_t embed(hipStream_t s, int xdt, int wdt, const void* x, const RowMap& map,
                  const void* w_in, const float* emb, float* X, int M, int D, int C) {
   if (M <= 0) return hipSuccess;
-  if (C > EMB_MAXC) return hipErrorInvalidValue;
-  dim3 grid((M + EMB_ROWS - 1) / EMB_ROWS, (D + 255) / 256);
+  if (C > EMB_MAXC || D % 4) return hipErrorInvalidValue;
+  dim3 grid((M + EMB_BM - 1) / EMB_BM, (D + EMB_BN - 1) / EMB_BN);
   TimingScope ts(s, KC_EMBED, (double)M * D * 4, 2.0 * M * D * C);
 #define EMB(TX, TW)                                                                          \
   hipLaunchKernelGGL((embed_kernel<TX, TW>), grid, dim3(256), 0, s, (const TX*)x, map,       \
