@@ -80,6 +80,43 @@ def measured_traffic(workload: str, kernel_class: str):
     return None
 
 
+def yardsticks() -> dict:
+    """Achievable peaks on this GPU with random data, as context for the roofline
+    fractions (which stay against the spec peaks): a 1 GiB device copy and one
+    plain library bf16 GEMM (torch.matmul) at the W1 shape of the C1 prefill."""
+    import torch
+    out = {}
+    n = (1 << 30) // 4
+    src = torch.rand(n, device="cuda")
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["copy_gbs"] = round(2 * n * 4 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst
+    M, N, K = 9216, 4096, 1024
+    a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    bt = torch.randn(N, K, device="cuda").to(torch.bfloat16).t().contiguous()  # [K][N], contiguous
+    for _ in range(3):
+        c = a @ bt
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        c = a @ bt
+    e1.record()
+    torch.cuda.synchronize()
+    out["library_bf16_gemm_tflops"] = round(2.0 * M * N * K * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    out["library_gemm_shape"] = f"{M}x{N}x{K} bf16 (torch.matmul, random data)"
+    del a, bt, c
+    return out
+
+
 def cpu_baseline(cfg_name: str, layers: int) -> dict:
     import numpy as np  # noqa: F401
     import torch
@@ -217,6 +254,7 @@ def main():
         "kernels": {k: {kk: v[kk] for kk in ("launches", "total_ms", "avg_us", "achieved", "unit", "frac")}
                     for k, v in kt.items()},
     }
+    rec["yardsticks"] = yardsticks()
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg.name, min(args.cpu_layers, cfg.L))
