@@ -363,17 +363,6 @@ hipError_t copy_cvt_f32(hipStream_t s, int sdt, const void* src, float* dst, int
   return hipGetLastError();
 }
 
-__global__ void fill_i32_kernel(int* __restrict__ p, int n, int v) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
-}
-
-// A fill kernel rather than a memset node, so that the call stays capturable.
-hipError_t fill_i32(hipStream_t s, int* p, int n, int v) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0,
-                     s, p, n, v);
-  return hipGetLastError();
-}
 
 // ------------------------------------------------------------ step boundary
 // One workgroup per row m (D <= 2048, C <= 64):

@@ -114,11 +114,6 @@ __device__ inline void epi_row4(const EpiArgs& e, int m, int n, float4 v) {
     x.z += v.z;
     x.w += v.w;
     *p = x;
-  } else if constexpr (EPI == EPI_EULER) {
-    epi_store<EPI, TO>(e, m, n, v.x);
-    epi_store<EPI, TO>(e, m, n + 1, v.y);
-    epi_store<EPI, TO>(e, m, n + 2, v.z);
-    epi_store<EPI, TO>(e, m, n + 3, v.w);
   } else {  // QKV, Q or K part: 4 consecutive head dims
     const int nn = e.n_begin + n;
     const int part = nn / e.D, c = nn - part * e.D;
@@ -419,131 +414,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const bf16_t* __re
   }
 }
 
-// ============================================================ skinny + RMSNorm (M <= 64)
-// C = RMSNorm(X; g) W^T for fp32 rows X[M][K] in one pass: the row scale
-// r_m = (mean(x^2) + eps)^(-1/2) factors out of the dot product, so the bf16
-// operand is built from x*g while the same loads accumulate sum(x^2); the
-// output row is scaled by r_m in the epilogue.  Four waves split K; fixed
-// reduction order.
-template <int EPI, typename TO, int MT, int U = 2>
-__global__ __launch_bounds__(256) void gemm_skinny_norm_kernel(const float* __restrict__ X,
-                                                               const float* __restrict__ gain,
-                                                               const bf16_t* __restrict__ B, int ldb,
-                                                               int M, int N, int K, EpiArgs e) {
-  __shared__ float red[4][MT * 16][17];
-  __shared__ float ssw[4][MT * 16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int n0 = blockIdx.x * skinny::NT;
-  const int kw = K / 4;
-  const int kb = w * kw;
-  const bf16_t* brow = B + (long long)(n0 + c16) * ldb + kb + 16 * g;
-  floatx4 acc[MT];
-  float ss[MT];
-#pragma unroll
-  for (int i = 0; i < MT; i++) {
-    acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-    ss[i] = 0.f;
-  }
-  const int nsteps = kw / 64;
-  for (int st = 0; st < nsteps; st += U) {
-    bf16x8 b0[U], b1[U];
-    float4 gg[U][4], xv[U][MT][4];
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-      if (st + u < nsteps) {
-        const int k = kb + (st + u) * 64 + 16 * g;
-        b0[u] = *(const bf16x8*)(brow + (st + u) * 64);
-        b1[u] = *(const bf16x8*)(brow + (st + u) * 64 + 8);
-#pragma unroll
-        for (int q = 0; q < 4; q++) gg[u][q] = *(const float4*)(gain + k + 4 * q);
-#pragma unroll
-        for (int i = 0; i < MT; i++)
-#pragma unroll
-          for (int q = 0; q < 4; q++)
-            xv[u][i][q] = *(const float4*)(X + (long long)(16 * i + c16) * K + k + 4 * q);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-      if (st + u < nsteps) {
-#pragma unroll
-        for (int i = 0; i < MT; i++) {
-          uint32_t pk[8];
-#pragma unroll
-          for (int q = 0; q < 4; q++) {
-            const float4 x = xv[u][i][q], gq = gg[u][q];
-            ss[i] = fmaf(x.x, x.x, ss[i]);
-            ss[i] = fmaf(x.y, x.y, ss[i]);
-            ss[i] = fmaf(x.z, x.z, ss[i]);
-            ss[i] = fmaf(x.w, x.w, ss[i]);
-            pk[2 * q] = pack_bf16x2(x.x * gq.x, x.y * gq.y);
-            pk[2 * q + 1] = pack_bf16x2(x.z * gq.z, x.w * gq.w);
-          }
-          const u32x4 lo = {pk[0], pk[1], pk[2], pk[3]}, hi = {pk[4], pk[5], pk[6], pk[7]};
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), b0[u], acc[i], 0, 0, 0);
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), b1[u], acc[i], 0, 0, 0);
-        }
-      }
-    }
-  }
-  // row sums of squares: over the 4 lane groups, then over the 4 waves
-#pragma unroll
-  for (int i = 0; i < MT; i++) {
-    float v = ss[i];
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    if (g == 0) ssw[w][16 * i + c16] = v;
-  }
-#pragma unroll
-  for (int i = 0; i < MT; i++)
-#pragma unroll
-    for (int r = 0; r < 4; r++) red[w][16 * i + 4 * g + r][c16] = acc[i][r];
-  __syncthreads();
-  for (int idx = tid; idx < M * 16; idx += 256) {
-    const int m = idx >> 4, c = idx & 15;
-    const float sq = ((ssw[0][m] + ssw[1][m]) + ssw[2][m]) + ssw[3][m];
-    const float rm = 1.0f / sqrtf(sq / (float)K + 1e-6f);
-    const float v = (((red[0][m][c] + red[1][m][c]) + red[2][m][c]) + red[3][m][c]) * rm;
-    epi_store<EPI, TO>(e, m, n0 + c, v);
-  }
-}
-
-bool gemm_norm_ok(int M, int N, int K) {
-  return M >= 16 && M <= 64 && M % 16 == 0 && N % skinny::NT == 0 && K % 256 == 0;
-}
-
-hipError_t gemm_norm(hipStream_t s, int odt, int epi, int M, int N, int K, const float* X,
-                     const float* gain, const void* B, int ldb, const EpiArgs& e) {
-  if (!gemm_norm_ok(M, N, K)) return hipErrorInvalidValue;
-  dim3 grid(N / skinny::NT);
-  TimingScope ts(s, KC_GEMM_SKINNY, (double)M * K * 4 + (double)N * K * 2 + (double)M * N * 4,
-                 2.0 * M * N * K);
-  const bf16_t* b = (const bf16_t*)B;
-#define GN(E, T, mt) \
-  hipLaunchKernelGGL((gemm_skinny_norm_kernel<E, T, mt>), grid, dim3(256), 0, s, X, gain, b, ldb, M, N, K, e)
-#define GNM(E, T)                 \
-  switch (M / 16) {               \
-    case 1: GN(E, T, 1); break;   \
-    case 2: GN(E, T, 2); break;   \
-    case 3: GN(E, T, 3); break;   \
-    default: GN(E, T, 4); break;  \
-  }
-  if (epi == EPI_QKV && odt == WAM_BF16) { GNM(EPI_QKV, bf16_t) }
-  else if (epi == EPI_GELU && odt == WAM_BF16) { GNM(EPI_GELU, bf16_t) }
-  else if (epi == EPI_STORE && odt == WAM_BF16) { GNM(EPI_STORE, bf16_t) }
-  else if (epi == EPI_STORE && odt == WAM_F32) { GNM(EPI_STORE, float) }
-  else return hipErrorInvalidValue;
-#undef GNM
-#undef GN
-  return hipGetLastError();
-}
 
 // ============================================================ dispatch
 // Algorithmic HBM bytes of one GEMM: read A and B once, write C once (read
 // and write for the accumulate-into epilogues).
 template <int EPI>
 static double gemm_bytes(int M, int N, int K, int ea, int eb, int eo) {
-  double out = (double)M * N * ((EPI == EPI_RESID || EPI == EPI_EULER) ? 8.0 : (double)eo);
+  double out = (double)M * N * (EPI == EPI_RESID ? 8.0 : (double)eo);
   return (double)M * K * ea + (double)N * K * eb + out;
 }
 
@@ -656,8 +533,6 @@ hipError_t gemm(hipStream_t s, int adt, int bdt, int odt, int epi, int M, int N,
                 : gemm_epi<EPI_GELU, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e);
     case EPI_RESID:
       return gemm_epi<EPI_RESID, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e);
-    case EPI_EULER:
-      return gemm_epi<EPI_EULER, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e);
     case EPI_QKV:
       return ob ? gemm_epi<EPI_QKV, bf16_t>(s, adt, bdt, M, N, K, A, lda, B, ldb, e)
                 : gemm_epi<EPI_QKV, float>(s, adt, bdt, M, N, K, A, lda, B, ldb, e);

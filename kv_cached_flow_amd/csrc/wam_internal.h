@@ -106,15 +106,12 @@ enum EpiKind {
   EPI_STORE = 0,   // out[m*ldo + n] = v                    (out type TO)
   EPI_GELU = 1,    // out[m*ldo + n] = GELU(v)              (out type TO)
   EPI_RESID = 2,   // X[m*ldo + n] += v                     (fp32)
-  EPI_QKV = 3,     // scatter to Q / K cache / V^T cache    (out type TO)
-  EPI_EULER = 4    // z[m*ldo + n] += dt*v; vhat[m*ldo+n] = v (fp32)
+  EPI_QKV = 3      // scatter to Q / K cache / V^T cache    (out type TO)
 };
 
 struct EpiArgs {
-  void* out;      // STORE/GELU/RESID/EULER destination
+  void* out;      // STORE/GELU/RESID destination
   int ldo;
-  float dt;       // EULER
-  float* vhat;    // EULER, nullable
   // QKV: column n_begin + n of [Q | K | V] (each D wide), row m -> group g = m / rpg, t = m % rpg
   void* q;
   void* k;
@@ -135,10 +132,6 @@ __device__ inline void epi_store(const EpiArgs& e, int m, int n, float v) {
         from_f<TO>(sizeof(TO) == 2 ? gelu_bf16out(v) : gelu_f(v));
   } else if constexpr (EPI == EPI_RESID) {
     ((float*)e.out)[(long long)m * e.ldo + n] += v;
-  } else if constexpr (EPI == EPI_EULER) {
-    long long i = (long long)m * e.ldo + n;
-    ((float*)e.out)[i] += e.dt * v;
-    if (e.vhat) e.vhat[i] = v;
   } else {
     int nn = e.n_begin + n;
     int part = nn / e.D;
@@ -165,13 +158,6 @@ hipError_t gemm(hipStream_t s, int adt, int bdt, int odt, int epi, int M, int N,
 int gemm_partial_splits(int M, int N, int K);
 hipError_t gemm_partial(hipStream_t s, int M, int N, int K, const void* A, int lda, const void* B,
                         int ldb, float* part, int* ks_out);
-
-// C = RMSNorm(X; gain) W^T with the epilogue, for fp32 rows X[M][K] and bf16
-// W[N][K], M <= 64 (the action rows): the normalisation is fused into the
-// operand load.  gemm_norm_ok tells whether a shape is supported.
-bool gemm_norm_ok(int M, int N, int K);
-hipError_t gemm_norm(hipStream_t s, int odt, int epi, int M, int N, int K, const float* X,
-                     const float* gain, const void* B, int ldb, const EpiArgs& e);
 
 hipError_t rmsnorm(hipStream_t s, int odt, const float* x, const float* g, void* y, int M, int D);
 // x[m] += sum_{ks < KS} part[ks][m] (in ks order), then y = RMSNorm(x; g).
@@ -224,7 +210,6 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* 
 
 hipError_t debug_visibility(hipStream_t s, const FrameTab& tab, const int* comp_of_frame,
                             int F, uint8_t* vis);
-hipError_t fill_i32(hipStream_t s, int* p, int n, int v);
 
 // ---------------------------------------------------------------- timing
 enum KClass {
