@@ -150,77 +150,103 @@ __device__ inline void epi_vt4(const EpiArgs& e, int m, int n, float4 v) {
   }
 }
 
-// 128 x 128 x 64 tiles, 4 waves in a 2x2 grid (each 64 x 64), two
-// workgroups per CU.  Operand tiles go from global memory straight into LDS
-// (global_load_lds: lane i of a wave fills bytes [16i, 16i+16) of the
-// destination), two stages deep.  A 64-wide k slice of one row is 128 bytes
-// = 8 chunks of 16 bytes; chunk c of row r is stored at slot c ^ (r & 7), so
-// each lane picks the global chunk that belongs at its LDS slot, and the
-// 16-byte fragment reads of 8 consecutive rows hit distinct banks.  All 16
-// fragment reads of a k step are issued before its 32 MFMAs.  The C tile is
-// transposed through LDS (32 rows of a wave at a time) so that the epilogue
-// issues 8/16-byte accesses.
+// BM x 128 x 64 tiles, 4 waves, two workgroups per CU.  BM = 128: waves in a
+// 2x2 grid, each 64 x 64; BM = 144 (9 row tiles of 16): waves side by side,
+// each 144 x 32.  The host picks the height that fills the CUs in whole
+// rounds (e.g. 9216 rows = 64 x 144: exactly 2 x 256 tiles for N = 1024).
+// Operand tiles go from global memory straight into LDS (global_load_lds:
+// lane i of a wave fills bytes [16i, 16i+16) of the destination), two stages
+// deep.  A 64-wide k slice of one row is 128 bytes = 8 chunks of 16 bytes;
+// chunk c of row r is stored at slot c ^ (r & 7), so each lane picks the
+// global chunk that belongs at its LDS slot, and the 16-byte fragment reads of
+// 8 consecutive rows hit distinct banks.  The fragment reads of a k step are
+// issued before its MFMAs.  The C tile is transposed through LDS (a pass of
+// 2048 values per wave at a time) so that the epilogue issues 8/16-byte
+// accesses.
 namespace big2 {
-constexpr int BM = 128, BN = 128, BK = 64, STAGE = (BM + BN) * 128;  // bytes
+constexpr int BN = 128, BK = 64;
 }
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int EPI, typename TO>
+template <int BM>
+struct BigGeom {
+  static constexpr int NWM = BM == 144 ? 1 : 2, NWN = 4 / NWM;
+  static constexpr int WM = BM / NWM, WN = big2::BN / NWN;  // wave tile
+  static constexpr int MI = WM / 16, NI = WN / 16;
+  static constexpr int ACH = BM / 8, BCH = big2::BN / 8;    // 1 KB chunks per stage
+  static constexpr int AL = (ACH + 3) / 4;                   // A load instructions per wave
+  static constexpr int STAGE = (BM + big2::BN) * 128;        // bytes
+  static constexpr int RP = BM == 144 ? 48 : 32;            // epilogue rows per pass
+  static constexpr int PASSES = WM / RP, TPP = RP / 16;      // passes, row tiles per pass
+  static constexpr int ITEMS = RP * WN / 256;                // float4 items per lane per pass
+  static_assert(BM == 128 || BM == 144, "tile height");
+  static_assert(WM % RP == 0 && RP % 16 == 0, "epilogue passes");
+};
+
+template <int BM, int EPI, typename TO>
 __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_big_kernel(
     const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb, int M, int N,
     int K, EpiArgs e) {
+  using G = BigGeom<BM>;
   using namespace big2;
+  constexpr int MI = G::MI, NI = G::NI, WM = G::WM, WN = G::WN, STAGE = G::STAGE;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int ntm = (M + BM - 1) / BM, ntn = N / BN;
   int tm, tn;
   swizzle_tile(blockIdx.x, gridDim.x, ntm, ntn, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / G::NWN, wn = w % G::NWN;
 
   // Load instruction i of wave w fills LDS rows 8(4i + w) .. +7 of an
   // operand; lane l covers row 8(4i + w) + l/8, slot l%8.  Rows past M are
   // clamped (their products land in accumulator rows never stored).
   const int lrow = lane >> 3, lkc = (lane & 7) ^ lrow;
-  const bf16_t* asrc[4];
+  const bf16_t* asrc[G::AL];
   const bf16_t* bsrc[4];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int row = (4 * i + w) * 8 + lrow;
+  for (int i = 0; i < G::AL; i++) {
+    const int row = min((4 * i + w) * 8, BM - 8) + lrow;
     asrc[i] = A + (long long)min(m0 + row, M - 1) * lda + lkc * 8;
-    bsrc[i] = B + (long long)(n0 + row) * ldb + lkc * 8;
   }
+#pragma unroll
+  for (int i = 0; i < 4; i++) bsrc[i] = B + (long long)(n0 + (4 * i + w) * 8 + lrow) * ldb + lkc * 8;
   auto issue = [&](int kt, int buf) {
     char* sa = smem + buf * STAGE;
     char* sb = sa + BM * 128;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + kt * BK),
-                                       (lds_ptr_t)(sa + (4 * i + w) * 1024), 16, 0, 0);
+    for (int i = 0; i < G::AL; i++)
+      if (4 * i + w < G::ACH)
+        __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + kt * BK),
+                                         (lds_ptr_t)(sa + (4 * i + w) * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; i++)
       __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + kt * BK),
                                        (lds_ptr_t)(sb + (4 * i + w) * 1024), 16, 0, 0);
   };
 
-  floatx4 acc[4][4];
+  floatx4 acc[MI][NI];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < MI; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NI; j++) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // epilogue item `it` of pass `p`: row it*(64/(WN/4)) + lane/(WN/4) of the
+  // pass, columns 4*(lane%(WN/4)) .. +3
+  constexpr int CPL = WN / 4, RPI = 64 / CPL;  // lanes per row, rows per item step
   const int nk = K / BK, x7 = c16 & 7;
-  // residual epilogue: this lane's X values (rows it*4 + g of each 32-row
-  // half, columns 4*c16..+3), loaded a few k steps before the end so that the
-  // read overlaps the MFMAs; rows past M are clamped and never stored
-  float4 xr[2][8];
+  // residual epilogue: this lane's X values, loaded a few k steps before the
+  // end so that the read overlaps the MFMAs; rows past M are clamped and never
+  // stored
+  float4 xr[G::PASSES][G::ITEMS];
   auto xload = [&] {
 #pragma unroll
-    for (int half = 0; half < 2; half++)
+    for (int p = 0; p < G::PASSES; p++)
 #pragma unroll
-      for (int it = 0; it < 8; it++) {
-        const int m = min(m0 + wm * 64 + half * 32 + it * 4 + g, M - 1);
-        xr[half][it] = *(const float4*)((const float*)e.out + (long long)m * e.ldo + n0 + wn * 64 + c16 * 4);
+      for (int it = 0; it < G::ITEMS; it++) {
+        const int m = min(m0 + wm * WM + p * G::RP + it * RPI + lane / CPL, M - 1);
+        xr[p][it] = *(const float4*)((const float*)e.out + (long long)m * e.ldo + n0 + wn * WN +
+                                     (lane % CPL) * 4);
       }
   };
   const int kx = max(nk - 4, 0);
@@ -235,14 +261,14 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const char* sa = smem + (kt & 1) * STAGE;
     const char* sb = sa + BM * 128;
     if constexpr (EPI != EPI_RESID) {
-      bf16x8 af[2][4], bfr[2][4];
+      bf16x8 af[2][MI], bfr[2][NI];
 #pragma unroll
       for (int s = 0; s < 2; s++) {
         const int slot = ((4 * s + g) ^ x7) * 16;
 #pragma unroll
-        for (int i = 0; i < 4; i++) af[s][i] = *(const bf16x8*)(sa + (wm * 64 + i * 16 + c16) * 128 + slot);
+        for (int i = 0; i < MI; i++) af[s][i] = *(const bf16x8*)(sa + (wm * WM + i * 16 + c16) * 128 + slot);
 #pragma unroll
-        for (int j = 0; j < 4; j++) bfr[s][j] = *(const bf16x8*)(sb + (wn * 64 + j * 16 + c16) * 128 + slot);
+        for (int j = 0; j < NI; j++) bfr[s][j] = *(const bf16x8*)(sb + (wn * WN + j * 16 + c16) * 128 + slot);
       }
       __builtin_amdgcn_sched_barrier(0);
       // the other buffer was last read in step kt - 1, which every wave has left
@@ -251,55 +277,55 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
       for (int s = 0; s < 2; s++)
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < MI; i++)
 #pragma unroll
-          for (int j = 0; j < 4; j++)
+          for (int j = 0; j < NI; j++)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
     } else {
-      // the prefetched X tile holds 64 registers: fragments one 32-wide k half at a time
+      // the prefetched X tile holds registers: fragments one 32-wide k half at a time
       if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
 #pragma unroll
       for (int s = 0; s < 2; s++) {
         const int slot = ((4 * s + g) ^ x7) * 16;
-        bf16x8 af[4], bfr[4];
+        bf16x8 af[MI], bfr[NI];
 #pragma unroll
-        for (int i = 0; i < 4; i++) af[i] = *(const bf16x8*)(sa + (wm * 64 + i * 16 + c16) * 128 + slot);
+        for (int i = 0; i < MI; i++) af[i] = *(const bf16x8*)(sa + (wm * WM + i * 16 + c16) * 128 + slot);
 #pragma unroll
-        for (int j = 0; j < 4; j++) bfr[j] = *(const bf16x8*)(sb + (wn * 64 + j * 16 + c16) * 128 + slot);
+        for (int j = 0; j < NI; j++) bfr[j] = *(const bf16x8*)(sb + (wn * WN + j * 16 + c16) * 128 + slot);
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < MI; i++)
 #pragma unroll
-          for (int j = 0; j < 4; j++)
+          for (int j = 0; j < NI; j++)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
     }
   }
   __syncthreads();  // operand buffers become the C staging area
 
-  // epilogue, 32 rows of the wave tile at a time
-  constexpr int CLD = 64 + 4;
-  float* ct = (float*)smem + w * 32 * CLD;
+  // epilogue: RP rows x WN columns of the wave tile per pass
+  constexpr int CLD = WN + 4;
+  float* ct = (float*)smem + w * G::RP * CLD;
   bool vt = false;
-  if constexpr (EPI == EPI_QKV) vt = (e.n_begin + n0 + wn * 64) / e.D == 2;
+  if constexpr (EPI == EPI_QKV) vt = (e.n_begin + n0 + wn * WN) / e.D == 2;
 #pragma unroll
-  for (int half = 0; half < 2; half++) {
+  for (int p = 0; p < G::PASSES; p++) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ii++)
+    for (int ii = 0; ii < G::TPP; ii++)
 #pragma unroll
-      for (int j = 0; j < 4; j++)
+      for (int j = 0; j < NI; j++)
 #pragma unroll
         for (int r = 0; r < 4; r++)
-          ct[(16 * ii + 4 * g + r) * CLD + 16 * j + c16] = acc[half * 2 + ii][j][r];
+          ct[(16 * ii + 4 * g + r) * CLD + 16 * j + c16] = acc[p * G::TPP + ii][j][r];
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
-    const int mb = m0 + wm * 64 + half * 32, nb = n0 + wn * 64;
+    const int mb = m0 + wm * WM + p * G::RP, nb = n0 + wn * WN;
     if constexpr (EPI == EPI_RESID) {
 #pragma unroll
-      for (int it = 0; it < 8; it++) {
-        const int row = it * 4 + g, c4 = c16 * 4;
+      for (int it = 0; it < G::ITEMS; it++) {
+        const int row = it * RPI + lane / CPL, c4 = (lane % CPL) * 4;
         if (mb + row < M) {
           const float4 v = *(const float4*)(ct + row * CLD + c4);
-          float4 x = xr[half][it];
+          float4 x = xr[p][it];
           x.x += v.x;
           x.y += v.y;
           x.z += v.z;
@@ -308,18 +334,20 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
       }
     } else if (!vt) {
-#pragma unroll 4
-      for (int it = 0; it < 8; it++) {
-        const int idx = it * 64 + lane;
-        const int row = idx >> 4, c4 = (idx & 15) * 4;
+#pragma unroll 2
+      for (int it = 0; it < G::ITEMS; it++) {
+        const int row = it * RPI + lane / CPL, c4 = (lane % CPL) * 4;
         if (mb + row < M) epi_row4<EPI, TO>(e, mb + row, nb + c4, *(const float4*)(ct + row * CLD + c4));
       }
     } else {
       if constexpr (EPI == EPI_QKV) {
-#pragma unroll 4
-        for (int it = 0; it < 8; it++) {
+        // V^T: lanes walk 4-row groups of one column, so a column's keys are
+        // written contiguously
+        constexpr int RG = G::RP / 4;  // 4-row groups per column
+#pragma unroll 2
+        for (int it = 0; it < G::ITEMS; it++) {
           const int idx = it * 64 + lane;
-          const int col = idx >> 3, r4 = (idx & 7) * 4;
+          const int col = idx / RG, r4 = (idx % RG) * 4;
           const int m = mb + r4;
           if (m + 3 < M) {
             float4 v = {ct[r4 * CLD + col], ct[(r4 + 1) * CLD + col], ct[(r4 + 2) * CLD + col],
@@ -429,9 +457,28 @@ static hipError_t launch_big(hipStream_t s, int M, int N, int K, const void* A, 
                              const void* B, int ldb, const EpiArgs& e) {
   const int ntn = N / big2::BN;
   TimingScope ts(s, KC_GEMM_BIG, gemm_bytes<EPI>(M, N, K, 2, 2, sizeof(TO)), 2.0 * M * N * K);
-  const int ntm = (M + big2::BM - 1) / big2::BM;
-  hipLaunchKernelGGL((gemm_big_kernel<EPI, TO>), dim3(ntm * ntn), dim3(256), 0, s,
-                     (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, e);
+  // Tile height: fewest rounds (two resident workgroups per CU) weighted by
+  // the measured time of one round: a 144-row round takes about 1.4x a
+  // 128-row one (side-by-side waves read more LDS per MFMA), so 144 pays
+  // only where it removes many rounds (9216 x 1024: 2 rounds -> 1).
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 256;
+  const long long slots = 2ll * n_cu;
+  auto rounds = [&](int bm) {
+    const long long tiles = (long long)((M + bm - 1) / bm) * ntn;
+    return (tiles + slots - 1) / slots;
+  };
+  if (rounds(144) * 7 < rounds(128) * 5) {
+    const int ntm = (M + 143) / 144;
+    hipLaunchKernelGGL((gemm_big_kernel<144, EPI, TO>), dim3(ntm * ntn), dim3(256), 0, s,
+                       (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, e);
+  } else {
+    const int ntm = (M + 127) / 128;
+    hipLaunchKernelGGL((gemm_big_kernel<128, EPI, TO>), dim3(ntm * ntn), dim3(256), 0, s,
+                       (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, e);
+  }
   return hipGetLastError();
 }
 
