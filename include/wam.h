@@ -230,7 +230,10 @@ int wam_debug_visibility(const int32_t* frame_block, const uint8_t* valid, int F
  * (the chunk's own keys; NULL with n_act = 0 to leave them out), cache layer
  * kc [B][Hh][cap][dh], vc [B][Hh][dh][cap] with len[b] (host) rows, or
  * kc = vc = NULL.  out [B][H][Hh*dh] dtype.  splits_hint in 1..63 forces
- * the number of cache-key splits per (episode, head) (0 = automatic).
+ * the number of cache-key splits per (episode, head); 0 = automatic:
+ * (compute units / Hh) - 1 splits of whole 64-key tiles, at most 63, which
+ * depends on the episode's length, Hh and the device but not on B, so an
+ * episode's result does not depend on the batch it is in.
  * ws: wam_action_workspace_bytes of a matching dims. */
 int wam_attention_action(int dtype, int B, int Hh, int dh, int H, const void* q,
                          const void* ka, const void* va, int n_act,
