@@ -53,11 +53,13 @@ __device__ inline int perm_key(int sub, int r) {
 // Running softmax state of one wave: 32 queries (two 16-column tiles).
 // o[0..3][t] are the O^T accumulators (head dim x query); o[4][t] row 0 holds
 // the row sums, accumulated by the same P V MFMA against a row of ones, so
-// numerator and denominator use the same bf16 probabilities.  m is the
-// reference max in raw score units; exponentials use exp2 with the scale sl2
-// folded into one FMA.  The reference max is raised only when a new score
-// exceeds it by more than 2^8 in probability, so rescaling is rare; P <= 256
-// stays exact in bf16 and the result does not depend on the reference.
+// numerator and denominator use the same bf16 probabilities.  Scores are in
+// log2 units (the queries carry the softmax scale times log2 e), and m is the
+// reference max in those units.  The score MFMA starts from -m instead of 0,
+// so it yields s - m directly and p = exp2(s - m) costs one exponential and
+// no FMA.  The reference max is raised only when a score exceeds it by more
+// than 2^8 in probability, so rescaling is rare; P <= 256 stays exact in bf16
+// and the result does not depend on the reference.
 struct WaveAcc {
   floatx4 o[5][2];
   float m[2];
@@ -97,15 +99,21 @@ __device__ inline void tile_mask(floatx4 (&sacc)[4][2], int kbase, const int (&k
         if (kbase + 32 * (sub >> 1) + 8 * g + 4 * (sub & 1) + r >= kq[t]) sacc[sub][t][r] = -INFINITY;
 }
 
-// One 64-key tile: online softmax of the raw scores sacc (S^T, permuted key
-// rows, masked scores already -inf), then O^T += V^T P^T with the V^T
-// operands from vop(d, wd).  Inlined once per kernel: a second inlined copy
-// makes the register allocator shuffle the accumulators at the join.
+// The accumulator the score MFMAs of query tile t start from: -m, or 0
+// before the first score (m = -inf).
+__device__ inline floatx4 score_init(const WaveAcc& a, int t) {
+  const float b = a.m[t] == -INFINITY ? 0.f : -a.m[t];
+  return floatx4{b, b, b, b};
+}
+
+// One 64-key tile: online softmax of sacc = s - m0[t] (S^T in log2 units,
+// permuted key rows, masked scores already -inf, m0 the value score_init
+// used), then O^T += V^T P^T with the V^T operands from vop(d, wd).  Inlined
+// once per kernel: a second inlined copy makes the register allocator shuffle
+// the accumulators at the join.
 template <typename VOp>
-__device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], float sl2,
-                                   const bf16x8& ones, VOp vop) {
+__device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], const bf16x8& ones, VOp vop) {
   bf16x8 pf[2][2];
-  const float thr = kLazyLog2 / sl2;
 #pragma unroll
   for (int t = 0; t < 2; t++) {
     float mx = -INFINITY;
@@ -114,22 +122,29 @@ __device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], float sl2,
 #pragma unroll
       for (int r = 0; r < 4; r++) mx = fmaxf(mx, sacc[sub][t][r]);
     mx = wave_max16x4(mx);
-    const bool need = mx > a.m[t] + thr;
+    // scores are relative to m0 = (m == -inf ? 0 : m): the tile max is m0 + mx
+    const bool fresh = a.m[t] == -INFINITY;
+    const bool need = fresh ? mx > -INFINITY : mx > kLazyLog2;
     if (__any(need)) {
-      const float mnew = need ? mx : a.m[t];
-      const float alpha = __builtin_amdgcn_exp2f((a.m[t] - mnew) * sl2);
+      const float m0 = fresh ? 0.f : a.m[t];
+      const float mnew = need ? m0 + mx : a.m[t];
+      const float alpha = fresh ? 0.f : __builtin_amdgcn_exp2f(a.m[t] - mnew);
       a.m[t] = mnew;
 #pragma unroll
       for (int d = 0; d < 5; d++) a.o[d][t] *= alpha;
+      const float delta = need ? mnew - m0 : 0.f;  // rows without a new max keep m0
+#pragma unroll
+      for (int sub = 0; sub < 4; sub++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) sacc[sub][t][r] -= delta;
     }
-    const float mc = a.m[t] * sl2;
 #pragma unroll
     for (int wd = 0; wd < 2; wd++) {
       float p[8];
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[2 * wd][t][r], sl2, -mc));
-        p[4 + r] = __builtin_amdgcn_exp2f(fmaf(sacc[2 * wd + 1][t][r], sl2, -mc));
+        p[r] = __builtin_amdgcn_exp2f(sacc[2 * wd][t][r]);
+        p[4 + r] = __builtin_amdgcn_exp2f(sacc[2 * wd + 1][t][r]);
       }
       const u32x4 u = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                        pack_bf16x2(p[6], p[7])};
@@ -151,18 +166,33 @@ __device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], float sl2,
   }
 }
 
-// S^T for one 64-key tile from K operands kop(sub, s) (16 keys x 32 dims).
+// S^T - m0 for one 64-key tile from K operands kop(sub, s) (16 keys x 32
+// dims); the first MFMA of each subtile starts from score_init.
 template <typename KOp>
-__device__ inline void tile_scores(floatx4 (&sacc)[4][2], const bf16x8 (&qf)[2][2], KOp kop) {
+__device__ inline void tile_scores(floatx4 (&sacc)[4][2], const bf16x8 (&qf)[2][2], const WaveAcc& a,
+                                   KOp kop) {
+  const floatx4 init[2] = {score_init(a, 0), score_init(a, 1)};
 #pragma unroll
   for (int sub = 0; sub < 4; sub++) {
     const bf16x8 k0 = kop(sub, 0), k1 = kop(sub, 1);
 #pragma unroll
     for (int t = 0; t < 2; t++) {
-      sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[t][0], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[t][0], init[t], 0, 0, 0);
       sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[t][1], sacc[sub][t], 0, 0, 0);
     }
   }
+}
+
+// A query fragment scaled into log2 units (scale * log2 e) and rounded to bf16.
+__device__ inline bf16x8 scale_q(bf16x8 q, float sl2) {
+  const u32x4 u = __builtin_bit_cast(u32x4, q);
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const float lo = __uint_as_float(u[i] << 16) * sl2, hi = __uint_as_float(u[i] & 0xFFFF0000u) * sl2;
+    o[i] = pack_bf16x2(lo, hi);
+  }
+  return __builtin_bit_cast(bf16x8, o);
 }
 
 // ====================================================================== prefill
@@ -220,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     kq[t] = ok ? kend_of_row(tab, row0 + qi) : kend_max;
 #pragma unroll
     for (int s = 0; s < 2; s++)
-      qf[t][s] = ok ? *(const bf16x8*)(q + ((long long)h * nq + qi) * 64 + 32 * s + 8 * g)
+      qf[t][s] = ok ? scale_q(*(const bf16x8*)(q + ((long long)h * nq + qi) * 64 + 32 * s + 8 * g), sl2)
                     : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
   WaveAcc acc;
@@ -295,9 +325,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     if (kt + KT < kend_max) issue(kt + KT, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     floatx4 sacc[4][2];
-    tile_scores(sacc, qf, [&](int sub, int s) { return kf[sub][s]; });
+    tile_scores(sacc, qf, acc, [&](int sub, int s) { return kf[sub][s]; });
     if (kt + KT > kend_min) tile_mask(sacc, kt, kq, g);
-    tile_update(acc, sacc, sl2, ones, [&](int d, int wd) { return vf[d][wd]; });
+    tile_update(acc, sacc, ones, [&](int d, int wd) { return vf[d][wd]; });
   }
   const int D = Hh * 64;
 #pragma unroll
@@ -394,7 +424,7 @@ struct ActGeom {
 // Split (b, h, s): cache keys [s*kc[b], min(len, (s+1)*kc[b])) for s < ncs(b),
 // the chunk's own keys for s == ncs(b).  Writes the split's (m, l, o) in the
 // log2 domain: m [32], l [32], o [32][64] (unnormalised).
-__global__ __launch_bounds__(256, 3) void attn_action_kernel(
+__global__ __launch_bounds__(256, 2) void attn_action_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ ka, const bf16_t* __restrict__ va,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, ActGeom G,
     float* __restrict__ part, float sl2) {
@@ -431,7 +461,7 @@ __global__ __launch_bounds__(256, 3) void attn_action_kernel(
   for (int t = 0; t < 2; t++)
 #pragma unroll
     for (int ss = 0; ss < 2; ss++)
-      qf[t][ss] = *(const bf16x8*)(qb + (16 * t + c16) * 64 + 32 * ss + 8 * g);
+      qf[t][ss] = scale_q(*(const bf16x8*)(qb + (16 * t + c16) * 64 + 32 * ss + 8 * g), sl2);
 
   WaveAcc acc;
   acc_init(acc);
@@ -472,10 +502,10 @@ __global__ __launch_bounds__(256, 3) void attn_action_kernel(
     }
     // ---- S^T, softmax, P V
     floatx4 sacc[4][2];
-    tile_scores(sacc, qf, [&](int sub, int ss) { return ak[sub][ss]; });
+    tile_scores(sacc, qf, acc, [&](int sub, int ss) { return ak[sub][ss]; });
     auto vop = [&](int d, int wd) { return av[d][wd]; };
     if (tail) tile_mask(sacc, kt, kq, g);
-    tile_update(acc, sacc, sl2, ones, vop);
+    tile_update(acc, sacc, ones, vop);
   }
   // ---- per-wave state to LDS (waves without keys hold m = -inf, l = 0, o = 0)
 #pragma unroll
@@ -506,13 +536,13 @@ __global__ __launch_bounds__(256, 3) void attn_action_kernel(
 #pragma unroll
     for (int ww = 0; ww < 4; ww++) {
       const float f =
-          (sm[ww][qi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((sm[ww][qi] - M) * sl2);
+          (sm[ww][qi] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[ww][qi] - M);
       L += sl[ww][qi] * f;
       O += so[ww][qi][d] * f;
     }
     po[qi * 64 + d] = O;
     if (d == 0) {
-      pm[qi] = M * sl2;  // log2 domain for the split merge
+      pm[qi] = M;  // log2 units, as the split merge expects
       pl[qi] = L;
     }
   }
