@@ -99,20 +99,15 @@ __device__ inline void tile_mask(floatx4 (&sacc)[4][2], int kbase, const int (&k
         if (kbase + 32 * (sub >> 1) + 8 * g + 4 * (sub & 1) + r >= kq[t]) sacc[sub][t][r] = -INFINITY;
 }
 
-// The accumulator the score MFMAs of query tile t start from: -m, or 0
-// before the first score (m = -inf).
-__device__ inline floatx4 score_init(const WaveAcc& a, int t) {
-  const float b = a.m[t] == -INFINITY ? 0.f : -a.m[t];
-  return floatx4{b, b, b, b};
-}
-
-// One 64-key tile: online softmax of sacc = s - m0[t] (S^T in log2 units,
-// permuted key rows, masked scores already -inf, m0 the value score_init
-// used), then O^T += V^T P^T with the V^T operands from vop(d, wd).  Inlined
-// once per kernel: a second inlined copy makes the register allocator shuffle
-// the accumulators at the join.
+// One 64-key tile: online softmax of sacc = s - m (S^T in log2 units,
+// permuted key rows, masked scores already -inf), then
+// O^T += V^T P^T with the V^T operands from vop(d, wd).  `first` (wave-
+// uniform) marks a wave's first tile, where every query has a visible key:
+// there m is the tile max itself.  Inlined once per kernel: a second inlined
+// copy makes the register allocator shuffle the accumulators at the join.
 template <typename VOp>
-__device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], const bf16x8& ones, VOp vop) {
+__device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], bool first, const bf16x8& ones,
+                                   VOp vop) {
   bf16x8 pf[2][2];
 #pragma unroll
   for (int t = 0; t < 2; t++) {
@@ -121,18 +116,21 @@ __device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], const bf16
     for (int sub = 0; sub < 4; sub++)
 #pragma unroll
       for (int r = 0; r < 4; r++) mx = fmaxf(mx, sacc[sub][t][r]);
-    mx = wave_max16x4(mx);
-    // scores are relative to m0 = (m == -inf ? 0 : m): the tile max is m0 + mx
-    const bool fresh = a.m[t] == -INFINITY;
-    const bool need = fresh ? mx > -INFINITY : mx > kLazyLog2;
-    if (__any(need)) {
-      const float m0 = fresh ? 0.f : a.m[t];
-      const float mnew = need ? m0 + mx : a.m[t];
-      const float alpha = fresh ? 0.f : __builtin_amdgcn_exp2f(a.m[t] - mnew);
-      a.m[t] = mnew;
+    mx = wave_max16x4(mx);  // tile max relative to m (to 0 on the first tile)
+    const bool need = mx > kLazyLog2;
+    if (first || __any(need)) {
+      float delta;
+      if (first) {
+        a.m[t] = mx;
+        delta = mx;
+      } else {
+        const float mnew = need ? a.m[t] + mx : a.m[t];
+        const float alpha = __builtin_amdgcn_exp2f(a.m[t] - mnew);
+        a.m[t] = mnew;
 #pragma unroll
-      for (int d = 0; d < 5; d++) a.o[d][t] *= alpha;
-      const float delta = need ? mnew - m0 : 0.f;  // rows without a new max keep m0
+        for (int d = 0; d < 5; d++) a.o[d][t] *= alpha;
+        delta = need ? mx : 0.f;  // rows without a new max keep their reference
+      }
 #pragma unroll
       for (int sub = 0; sub < 4; sub++)
 #pragma unroll
@@ -166,12 +164,18 @@ __device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], const bf16
   }
 }
 
-// S^T - m0 for one 64-key tile from K operands kop(sub, s) (16 keys x 32
-// dims); the first MFMA of each subtile starts from score_init.
+// S^T - m for one 64-key tile from K operands kop(sub, s) (16 keys x 32
+// dims): the first MFMA of each subtile starts from -m (from 0 on a wave's
+// first tile, where m is not set yet).
 template <typename KOp>
 __device__ inline void tile_scores(floatx4 (&sacc)[4][2], const bf16x8 (&qf)[2][2], const WaveAcc& a,
-                                   KOp kop) {
-  const floatx4 init[2] = {score_init(a, 0), score_init(a, 1)};
+                                   bool first, KOp kop) {
+  floatx4 init[2];
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+    const float b = first ? 0.f : -a.m[t];
+    init[t] = floatx4{b, b, b, b};
+  }
 #pragma unroll
   for (int sub = 0; sub < 4; sub++) {
     const bf16x8 k0 = kop(sub, 0), k1 = kop(sub, 1);
@@ -325,9 +329,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     if (kt + KT < kend_max) issue(kt + KT, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     floatx4 sacc[4][2];
-    tile_scores(sacc, qf, acc, [&](int sub, int s) { return kf[sub][s]; });
+    tile_scores(sacc, qf, acc, kt == 0, [&](int sub, int s) { return kf[sub][s]; });
     if (kt + KT > kend_min) tile_mask(sacc, kt, kq, g);
-    tile_update(acc, sacc, ones, [&](int d, int wd) { return vf[d][wd]; });
+    tile_update(acc, sacc, kt == 0, ones, [&](int d, int wd) { return vf[d][wd]; });
   }
   const int D = Hh * 64;
 #pragma unroll
@@ -502,10 +506,10 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
     }
     // ---- S^T, softmax, P V
     floatx4 sacc[4][2];
-    tile_scores(sacc, qf, acc, [&](int sub, int ss) { return ak[sub][ss]; });
+    tile_scores(sacc, qf, acc, kt == key0 + w * KT, [&](int sub, int ss) { return ak[sub][ss]; });
     auto vop = [&](int d, int wd) { return av[d][wd]; };
     if (tail) tile_mask(sacc, kt, kq, g);
-    tile_update(acc, sacc, ones, vop);
+    tile_update(acc, sacc, kt == key0 + w * KT, ones, vop);
   }
   // ---- per-wave state to LDS (waves without keys hold m = -inf, l = 0, o = 0)
 #pragma unroll
