@@ -15,7 +15,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwam.so")
 
 WAM_F32, WAM_BF16 = 0, 1
-WAM_MAX_FRAMES = 256
+WAM_MAX_FRAMES = 256   # limits of the C-ABI (include/wam.h)
+WAM_MAX_BATCH = 64
+WAM_MAX_FUSE = 32
+WAM_MAX_INTERVAL = 8
+WAM_MAX_STEPS = 64
 
 _lib = None
 

@@ -133,6 +133,42 @@ def test_prefill_reads_only_written_memory(name):
         assert torch.isfinite(dc.actions).all()
 
 
+def test_max_frames_and_steps():
+    """256 latent frames, the most one call takes (10 padded, temporal blocks
+    of 4, a 6-frame future block), together with 64 Euler steps."""
+    blocks = tuple(f // 4 for f in range(250)) + (63,) * 6
+    cfg = configs.small("MAXF", dtype="bf16", L=1, D=128, Hh=2, Fm=256, P=8, Fh=250, Ff=6,
+                        frame_block=blocks, pad_frames=10, V=2, N=64, B=2, read_map=(0,))
+    print_case("max frames (256) and max steps (64)")
+    inp = inputs.generate(cfg)
+    ref = _oracle(cfg, inp)
+    dc = _run_gpu(cfg, inp)
+    assert rel_l2(to_np(dc.actions), ref["actions"]) <= 2e-2
+    for b in range(cfg.B):
+        k, v = gpu_cache_layer(dc, 0, b, cfg.tokens_valid)
+        assert rel_l2(k, ref["cache"][b][0][0].numpy()) <= 1e-2
+        assert rel_l2(v, ref["cache"][b][0][1].numpy()) <= 1e-2
+
+
+def test_max_batch():
+    """64 episodes, the most one call takes, with one padded history frame
+    in every other episode."""
+    cfg = configs.small("MAXB", dtype="bf16", L=1, D=128, Hh=2, Fm=256, P=20, Fh=2, Ff=1,
+                        frame_block=(0, 1, 2), pad_frames=0, V=1, N=2, B=64, read_map=(0,))
+    print_case("max batch (64)")
+    inp = inputs.generate(cfg)
+    inp["hist_valid"] = inp["hist_valid"].copy()
+    inp["hist_valid"][1::2, 0] = 0
+    ref = _oracle(cfg, inp)
+    dc = _run_gpu(cfg, inp)
+    assert rel_l2(to_np(dc.actions), ref["actions"]) <= 2e-2
+    for b in (0, 1, 62, 63):
+        n = 2 * cfg.P if b % 2 else 3 * cfg.P
+        assert int(dc.cache.len[b]) == n
+        k, v = gpu_cache_layer(dc, 0, b, n)
+        assert rel_l2(k, ref["cache"][b][0][0].numpy()) <= 1e-2
+
+
 def test_batch_independence():
     import torch
     cfg2 = configs.small("B2", dtype="bf16", **dict(SMALL, B=2))

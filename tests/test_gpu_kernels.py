@@ -223,6 +223,30 @@ def test_fuse_vs_oracle():
         assert rel_l2(to_np(dst.v[m]), ref[m][1].numpy()) <= 4e-3
 
 
+def test_fuse_max_pairs_and_interval():
+    """32 fused pairs (the most one call takes), each over an 8-layer interval
+    (the longest allowed), intervals overlapping, two episodes."""
+    dt = wam.WAM_BF16
+    rng = np.random.default_rng(12)
+    print_case("fuse 32 pairs x 8 layers")
+    src = _kv_random(rng, 16, 2, 2, 128, dt)
+    src.len[:] = [128, 70]
+    M = wam.WAM_MAX_FUSE
+    starts = [m % 9 for m in range(M)]
+    counts = [wam.WAM_MAX_INTERVAL] * M
+    logits = (rng.standard_normal((M, wam.WAM_MAX_INTERVAL)) * 2).astype(np.float32)
+    dst = wam.DeviceKV(M, 2, 2, 64, 128, dt)
+    wam.fuse_interval_kv(src, starts, counts, logits, dst)
+    torch.cuda.synchronize()
+    assert list(dst.len) == [128, 70]
+    for b, n in ((0, 128), (1, 70)):
+        layers = [(src.k[l, b].double().cpu(), src.v[l, b].double().cpu()) for l in range(16)]
+        ref = O.fuse_interval(layers, list(zip(starts, counts)), logits)
+        for m in range(M):
+            assert rel_l2(to_np(dst.k[m, b, :, :n]), ref[m][0].numpy()[:, :n]) <= 4e-3
+            assert rel_l2(to_np(dst.v[m, b, :, :, :n]), ref[m][1].numpy()[:, :, :n]) <= 4e-3
+
+
 # ---------------------------------------------------------------- Euler
 def test_flow_euler_step():
     rng = np.random.default_rng(10)

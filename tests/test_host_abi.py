@@ -138,6 +138,19 @@ def test_prefill_validation_errors():
     assert st == -2 and "no valid frame" in msg
 
 
+def test_prefill_limits():
+    # the documented maxima pass validation, one past them is rejected
+    kv, _k = fake_kv(cap=512)
+    kv65, _k65 = fake_kv(B=wam.WAM_MAX_BATCH + 1, cap=512)
+    st, msg = call_prefill(B=wam.WAM_MAX_BATCH + 1, kv=kv65)
+    assert st == -2 and "B must be" in msg
+    F = wam.WAM_MAX_FRAMES + 1
+    st, msg = call_prefill(Fh=F - 2, Ff=2, blocks=tuple(range(F)), kv=kv)
+    assert st == -2 and "frame counts" in msg
+    st, msg = call_prefill(V=wam.WAM_MAX_STEPS + 1)
+    assert st == -1 and "video_steps" in msg
+
+
 def call_denoise(d=None, expert=None, kv=None, read_map=(0, 1), eps=FAKE, B=1, N=4, shift=1.0,
                  out=FAKE, ws=FAKE, ws_bytes=1 << 40):
     L = wam.lib()
@@ -217,3 +230,10 @@ def test_workspace_sizes_grow_with_shapes():
 def test_euler_rejects_negative_count():
     assert wam.lib().wam_flow_euler_step(FAKE, FAKE, -1, 1.0, 0.5, None) == -1
     assert wam.lib().wam_flow_euler_step(FAKE, FAKE, 0, 1.0, 0.5, None) == 0
+
+
+def test_python_limits_match_header():
+    hdr = open(os.path.join(os.path.dirname(wam.__file__), os.pardir, "include", "wam.h")).read()
+    for name in ("WAM_MAX_FRAMES", "WAM_MAX_BATCH", "WAM_MAX_FUSE", "WAM_MAX_INTERVAL", "WAM_MAX_STEPS"):
+        m = re.search(r"#define %s (\d+)" % name, hdr)
+        assert m and int(m.group(1)) == getattr(wam, name)
