@@ -223,7 +223,14 @@ def main():
     stats = wam.timing_report()
     wam.timing(False)
     kt = kernel_table(stats)
-    dom = max(kt, key=lambda k: kt[k]["total_ms"])
+    # The dominant class is the one with the largest roofline floor (its total
+    # algorithmic work at peak): event pairs add a fixed ~2 us to every launch,
+    # so summed event time would favour classes of many short launches.
+    def floor_ms(k):
+        v = kt[k]
+        work = v["flops_per_launch"] / 1e12 if v["bound"] != "hbm" else v["bytes_per_launch"] / 1e9
+        return v["launches"] * work / v["peak"] * 1e3
+    dom = max(kt, key=floor_ms)
     d = kt[dom]
     roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
                 "unit": d["unit"], "frac": d["frac"], "traffic": measured_traffic(cfg.name, dom),

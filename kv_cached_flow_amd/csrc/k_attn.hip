@@ -20,6 +20,7 @@
 //
 // fp32 variants (one thread per query, plain FMA) serve the fp32 workload.
 #include <algorithm>
+#include <type_traits>
 
 #include "wam_internal.h"
 
@@ -116,9 +117,12 @@ __device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], bool first
     for (int sub = 0; sub < 4; sub++)
 #pragma unroll
       for (int r = 0; r < 4; r++) mx = fmaxf(mx, sacc[sub][t][r]);
-    mx = wave_max16x4(mx);  // tile max relative to m (to 0 on the first tile)
-    const bool need = mx > kLazyLog2;
-    if (first || __any(need)) {
+    // Some column's tile max exceeds the threshold iff some lane's does, so
+    // the check needs no cross-lane step; the column max (relative to m, or
+    // to 0 on the first tile) is formed only when the reference moves.
+    if (first || __any(mx > kLazyLog2)) {
+      mx = wave_max16x4(mx);
+      const bool need = mx > kLazyLog2;
       float delta;
       if (first) {
         a.m[t] = mx;
@@ -265,32 +269,42 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   // covers row 8(4i + w) + l/8, slot l%8, i.e. chunk (l%8) ^ (row & 7).
   // K rows stay inside the cache (kt + 64 <= cap); rows past kend_max are
   // masked, V^T columns past kend_max are zeroed after the tile lands.
+  // The tiles come in through buffer loads into LDS: a per-head descriptor,
+  // a fixed per-lane byte offset and the tile's offset in a scalar register,
+  // so issuing a tile costs no vector arithmetic.  Offsets stay below 2 GiB
+  // (cap * 128 bytes per head).
   const int lrow = lane >> 3, lkc = (lane & 7) ^ lrow;
-  long long koff[2], voff[2];
+  unsigned koff[2], voff[2];
 #pragma unroll
   for (int i = 0; i < 2; i++) {
     const int row = (4 * i + w) * 8 + lrow;
-    koff[i] = (long long)perm_key(row >> 4, row & 15) * 64 + lkc * 8;
-    voff[i] = (long long)row * cap + lkc * 8;
+    koff[i] = (unsigned)(perm_key(row >> 4, row & 15) * 64 + lkc * 8) * 2u;
+    voff[i] = (unsigned)(row * cap + lkc * 8) * 2u;
   }
+  const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, 0x7FFFFFFF, 0x00020000);
+  const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vh, (short)0, 0x7FFFFFFF, 0x00020000);
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the LDS destinations are scalar
   auto issue = [&](int kt, int buf) {
     char* sk = smem + buf * 2 * TILE;
     char* sv = sk + TILE;
 #pragma unroll
     for (int i = 0; i < 2; i++)
-      __builtin_amdgcn_global_load_lds((const void*)(kh + (long long)kt * 64 + koff[i]),
-                                       (lds_ptr_t)(sk + (4 * i + w) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(sk + (4 * i + wu) * 1024), 16,
+                                               koff[i], (unsigned)kt * 128u, 0, 0);
 #pragma unroll
     for (int i = 0; i < 2; i++)
-      __builtin_amdgcn_global_load_lds((const void*)(vh + kt + voff[i]),
-                                       (lds_ptr_t)(sv + (4 * i + w) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(sv + (4 * i + wu) * 1024), 16,
+                                               voff[i], (unsigned)kt * 2u, 0, 0);
   };
 
   const int x7 = c16 & 7;
   // every issued tile is waited for inside the loop (no LDS write may land
   // after the workgroup has left)
   if (kend_max > 0) issue(0, 0);
-  for (int kt = 0; kt < kend_max; kt += KT) {
+  // One tile; FIRST (tile 0, where every query sees a key) is a compile-time
+  // flag so that the later tiles carry no test of it.
+  auto tile = [&](int kt, auto first_tag) {
+    constexpr bool FIRST = decltype(first_tag)::value;
     const int buf = (kt / KT) & 1;
     char* sk = smem + buf * 2 * TILE;
     char* sv = sk + TILE;
@@ -329,10 +343,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     if (kt + KT < kend_max) issue(kt + KT, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     floatx4 sacc[4][2];
-    tile_scores(sacc, qf, acc, kt == 0, [&](int sub, int s) { return kf[sub][s]; });
+    tile_scores(sacc, qf, acc, FIRST, [&](int sub, int s) { return kf[sub][s]; });
     if (kt + KT > kend_min) tile_mask(sacc, kt, kq, g);
-    tile_update(acc, sacc, kt == 0, ones, [&](int d, int wd) { return vf[d][wd]; });
-  }
+    tile_update(acc, sacc, FIRST, ones, [&](int d, int wd) { return vf[d][wd]; });
+  };
+  if (kend_max > 0) tile(0, std::true_type{});
+  for (int kt = KT; kt < kend_max; kt += KT) tile(kt, std::false_type{});
   const int D = Hh * 64;
 #pragma unroll
   for (int t = 0; t < 2; t++) {

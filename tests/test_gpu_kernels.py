@@ -156,6 +156,25 @@ def test_attention_action_vs_oracle(shape):
     assert rel_l2(got, ref) <= 5e-3
 
 
+def test_attention_action_batch_independent_bitwise():
+    """An episode's attention output does not depend on the batch around it,
+    bit for bit, at C1's shape (16 heads, 9216 and 6000 cached keys): the
+    split plan is a function of the episode alone, so the same workgroups do
+    the same arithmetic whether the grid holds one episode or two."""
+    dt = wam.WAM_BF16
+    rng = np.random.default_rng(13)
+    print_case("action attention batch independence, C1 shape")
+    lens = [9216, 6000]
+    q, ka, va, K, V, cap = _action_case(rng, dt, 2, 16, lens, 32)
+    both = _run_action(dt, q, ka, va, 32, K, V, cap, lens)
+    for b in range(2):
+        one = _run_action(dt, q[b:b + 1], ka[b:b + 1], va[b:b + 1], 32, K[b:b + 1], V[b:b + 1], cap,
+                          lens[b:b + 1])
+        assert np.array_equal(both[b], one[0])
+    ref = _action_ref(q, ka, va, K, V, lens, 32)
+    assert rel_l2(both, ref) <= 5e-3
+
+
 def test_attention_action_only_own_keys():
     dt = wam.WAM_BF16
     rng = np.random.default_rng(6)
