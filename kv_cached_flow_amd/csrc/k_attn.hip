@@ -208,20 +208,32 @@ namespace pf {
 constexpr int QW = 32, NW = 4, QT = QW * NW;  // queries per wave / per workgroup
 constexpr int KT = 64;                        // keys per tile
 constexpr int TILE = KT * 128;                // bytes of one K tile (= one V^T tile)
+constexpr int MAX_SPLIT = 4;                  // key splits per (query tile, head)
 }
 
 // Workgroups are dealt round-robin to the 8 XCDs.  Give every XCD whole heads
 // (their K/V then stay in that XCD's L2) and start the longest (latest) query
-// tiles first.
-__device__ inline void prefill_block(int bid, int Hh, int ntq, int* h, int* qt) {
+// tiles first.  j in [0, nj) numbers the (query tile, key split) units of a
+// head, longest first.
+__device__ inline void prefill_block(int bid, int Hh, int nj, int* h, int* j) {
   if ((Hh & 7) == 0) {
     const int x = bid & 7, i = bid >> 3, hpx = Hh >> 3;
     *h = x + 8 * (i % hpx);
-    *qt = ntq - 1 - i / hpx;
+    *j = nj - 1 - i / hpx;
   } else {
     *h = bid % Hh;
-    *qt = ntq - 1 - bid / Hh;
+    *j = nj - 1 - bid / Hh;
   }
+}
+
+// Key range of split sp of a query tile whose keys end at kend_max: whole
+// 64-key tiles, as even as the tile count allows.
+__device__ __host__ inline void prefill_split_range(int kend_max, int sp, int nsplit, int* k_lo,
+                                                    int* k_hi) {
+  const int ntile = (kend_max + pf::KT - 1) / pf::KT;
+  *k_lo = (sp * ntile / nsplit) * pf::KT;
+  const int hi = ((sp + 1) * ntile / nsplit) * pf::KT;
+  *k_hi = hi < kend_max ? hi : kend_max;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -235,17 +247,23 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // stages, one barrier per tile.
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
-    bf16_t* __restrict__ out, int nq, int row0, int cap, int Hh, FrameTab tab, float sl2) {
+    bf16_t* __restrict__ out, int nq, int row0, int cap, int Hh, FrameTab tab, float sl2,
+    int nsplit, float* __restrict__ part) {
   using namespace pf;
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // [stage][K | V^T]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int ntq = (nq + QT - 1) / QT;
-  int h, qt;
-  prefill_block(blockIdx.x, Hh, ntq, &h, &qt);
+  int h, j;
+  prefill_block(blockIdx.x, Hh, ntq * nsplit, &h, &j);
+  const int qt = j / nsplit, sp = j % nsplit;
   const int q0 = qt * QT;
   const int qlast = min(q0 + QT, nq) - 1;
   const int kend_min = kend_of_row(tab, row0 + q0);
   const int kend_max = kend_of_row(tab, row0 + qlast);
+  // This workgroup's keys: [k_lo, k_hi).  The host splits only where the first
+  // tile of every split holds a visible key for every query of the tile.
+  int k_lo, k_hi;
+  prefill_split_range(kend_max, sp, nsplit, &k_lo, &k_hi);
   const bf16_t* kh = kc + (long long)h * cap * 64;
   const bf16_t* vh = vc + (long long)h * 64 * cap;
 
@@ -300,7 +318,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   const int x7 = c16 & 7;
   // every issued tile is waited for inside the loop (no LDS write may land
   // after the workgroup has left)
-  if (kend_max > 0) issue(0, 0);
+  if (k_lo < k_hi) issue(k_lo, (k_lo / KT) & 1);
   // One tile; FIRST (tile 0, where every query sees a key) is a compile-time
   // flag so that the later tiles carry no test of it.
   auto tile = [&](int kt, auto first_tag) {
@@ -340,16 +358,36 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
         vf[d][wd] = *(const bf16x8*)(sv + (16 * d + c16) * 128 + (((4 * wd + g) ^ x7) * 16));
     __builtin_amdgcn_sched_barrier(0);
     // the other stage was last read in the previous tile, which every wave has left
-    if (kt + KT < kend_max) issue(kt + KT, buf ^ 1);
+    if (kt + KT < k_hi) issue(kt + KT, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     floatx4 sacc[4][2];
     tile_scores(sacc, qf, acc, FIRST, [&](int sub, int s) { return kf[sub][s]; });
     if (kt + KT > kend_min) tile_mask(sacc, kt, kq, g);
     tile_update(acc, sacc, FIRST, ones, [&](int d, int wd) { return vf[d][wd]; });
   };
-  if (kend_max > 0) tile(0, std::true_type{});
-  for (int kt = KT; kt < kend_max; kt += KT) tile(kt, std::false_type{});
+  if (k_lo < k_hi) tile(k_lo, std::true_type{});
+  for (int kt = k_lo + KT; kt < k_hi; kt += KT) tile(kt, std::false_type{});
   const int D = Hh * 64;
+  if (part != nullptr) {
+    // split partial (log2-domain max m, row sum l, unnormalised O):
+    // m [nsplit][Hh][nq], l [nsplit][Hh][nq], o [nsplit][Hh][nq][64]
+    const long long plane = (long long)nsplit * Hh * nq;
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const float l = acc_rowsum(acc, t);
+      const int qi = q0 + w * QW + 16 * t + c16;
+      if (qi >= nq) continue;
+      const long long pi = ((long long)sp * Hh + h) * nq + qi;
+      if (g == 0) {
+        part[pi] = acc.m[t];
+        part[plane + pi] = l;
+      }
+#pragma unroll
+      for (int d = 0; d < 4; d++)
+        *(floatx4*)(part + 2 * plane + pi * 64 + 16 * d + 4 * g) = acc.o[d][t];
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < 2; t++) {
     const float l = acc_rowsum(acc, t);
@@ -363,6 +401,41 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
       *(uint2*)(out + (long long)qi * D + h * 64 + 16 * d + 4 * g) = v;
     }
   }
+}
+
+// Merge of the key splits of one launch: one wavefront per (query, head),
+// lane = head-dim index, splits combined in a fixed order.
+__global__ __launch_bounds__(256) void attn_prefill_merge_kernel(const float* __restrict__ part,
+                                                                 int nsplit, int Hh, int nq,
+                                                                 bf16_t* __restrict__ out) {
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wv >= nq * Hh) return;
+  const int qi = wv / Hh, h = wv - qi * Hh;
+  const long long plane = (long long)nsplit * Hh * nq;
+  float mv[pf::MAX_SPLIT], lv[pf::MAX_SPLIT], ov[pf::MAX_SPLIT];
+#pragma unroll
+  for (int s = 0; s < pf::MAX_SPLIT; s++) {
+    if (s < nsplit) {
+      const long long pi = ((long long)s * Hh + h) * nq + qi;
+      mv[s] = part[pi];
+      lv[s] = part[plane + pi];
+      ov[s] = part[2 * plane + pi * 64 + lane];
+    }
+  }
+  float M = mv[0];
+#pragma unroll
+  for (int s = 1; s < pf::MAX_SPLIT; s++)
+    if (s < nsplit) M = fmaxf(M, mv[s]);
+  float L = 0.f, O = 0.f;
+#pragma unroll
+  for (int s = 0; s < pf::MAX_SPLIT; s++) {
+    if (s < nsplit) {
+      const float f = __builtin_amdgcn_exp2f(mv[s] - M);
+      L = fmaf(lv[s], f, L);
+      O = fmaf(ov[s], f, O);
+    }
+  }
+  out[(long long)qi * Hh * 64 + h * 64 + lane] = dev_f2bf(O / L);
 }
 
 // fp32: one thread per (query, head)
@@ -401,8 +474,51 @@ __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(const float* __res
   for (int d = 0; d < 64; d++) orow[d] = o[d] * inv;
 }
 
+static int device_cus() {
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 256;
+  return n_cu;
+}
+
+size_t attn_prefill_split_bytes(int Hh, int max_rows) {
+  // a launch splits only below 2 workgroups per CU, so splits x workgroups
+  // stays below 4 per CU: at most 4 n_cu QT (query, head, split) partials
+  const long long n = std::min<long long>((long long)pf::MAX_SPLIT * Hh * max_rows,
+                                          4ll * device_cus() * pf::QT);
+  return (size_t)n * 66 * sizeof(float);
+}
+
+// Key splits of a launch: enough (query tile, head, split) workgroups for two
+// per CU, at most MAX_SPLIT, and only where, for every query tile, the first
+// tile of every split holds a key that every query of the tile sees (the
+// tile loop takes a split's first tile as setting the reference max).  Under
+// the block-causal mask a query sees a key prefix, so that holds when the
+// last split starts below the tile's smallest prefix end.
+static int prefill_splits(int Hh, int nq, int row0, const FrameTab& tab, size_t part_bytes) {
+  const int ntq = (nq + pf::QT - 1) / pf::QT, n_cu = device_cus();
+  const long long g = (long long)ntq * Hh;
+  if (g >= 2ll * n_cu) return 1;
+  int S = (int)std::min<long long>(pf::MAX_SPLIT, (2ll * n_cu + g - 1) / g);
+  for (; S > 1; S--) {
+    if ((size_t)S * Hh * nq * 66 * sizeof(float) > part_bytes) continue;
+    bool ok = true;
+    for (int qt = 0; qt < ntq && ok; qt++) {
+      const int q0 = qt * pf::QT, ql = std::min(q0 + pf::QT, nq) - 1;
+      const int kmin = tab.kend[(row0 + q0) / tab.P], kmax = tab.kend[(row0 + ql) / tab.P];
+      int lo, hi;
+      prefill_split_range(kmax, S - 1, S, &lo, &hi);
+      ok = (kmax + pf::KT - 1) / pf::KT >= S && lo < kmin;
+    }
+    if (ok) break;
+  }
+  return S;
+}
+
 hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int nq, int row0, const FrameTab& tab,
-                        const void* q, const void* kc, const void* vc, int cap, void* out) {
+                        const void* q, const void* kc, const void* vc, int cap, void* out,
+                        float* part, size_t part_bytes) {
   if (nq <= 0) return hipSuccess;
   double pairs = 0.0;  // visible (query, key) pairs
   for (int r = row0; r < row0 + nq;) {
@@ -412,14 +528,27 @@ hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int nq, int row0, const F
   }
   const int es = dt == WAM_BF16 ? 2 : 4;
   const int kmax = tab.kend[(row0 + nq - 1) / tab.P];
-  TimingScope ts(s, KC_ATTN_PREFILL, (double)Hh * 64 * es * (2.0 * nq + 2.0 * kmax),
-                 4.0 * 64 * Hh * pairs);
   if (dt == WAM_BF16) {
-    dim3 grid(((nq + pf::QT - 1) / pf::QT) * Hh);
-    hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, (const bf16_t*)q,
-                       (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)out, nq, row0, cap, Hh,
-                       tab, 0.125f * LOG2E);
+    const int nsplit = part ? prefill_splits(Hh, nq, row0, tab, part_bytes) : 1;
+    {
+      TimingScope ts(s, KC_ATTN_PREFILL, (double)Hh * 64 * es * (2.0 * nq + 2.0 * kmax),
+                     4.0 * 64 * Hh * pairs);
+      dim3 grid(((nq + pf::QT - 1) / pf::QT) * Hh * nsplit);
+      hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, (const bf16_t*)q,
+                         (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)out, nq, row0, cap, Hh,
+                         tab, 0.125f * LOG2E, nsplit, nsplit > 1 ? part : nullptr);
+    }
+    if (nsplit > 1) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      TimingScope ts(s, KC_ATTN_MERGE, (double)nsplit * Hh * nq * 66 * 4 + (double)nq * Hh * 64 * es,
+                     0.0);
+      hipLaunchKernelGGL(attn_prefill_merge_kernel, dim3((nq * Hh + 3) / 4), dim3(256), 0, s,
+                         (const float*)part, nsplit, Hh, nq, (bf16_t*)out);
+    }
   } else {
+    TimingScope ts(s, KC_ATTN_PREFILL, (double)Hh * 64 * es * (2.0 * nq + 2.0 * kmax),
+                   4.0 * 64 * Hh * pairs);
     dim3 grid((nq + 63) / 64, Hh);
     hipLaunchKernelGGL(attn_prefill_f32_kernel, grid, dim3(64), 0, s, (const float*)q,
                        (const float*)kc, (const float*)vc, (float*)out, nq, row0, cap, Hh, tab,

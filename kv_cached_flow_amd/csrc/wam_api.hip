@@ -149,6 +149,8 @@ struct Bufs {
   int pend;     // splits of a product not yet added to X (0: none)
   void* attn;
   size_t attn_bytes;
+  float* pattn;  // split partials of the prefill attention
+  size_t pattn_bytes;
 };
 
 // ----------------------------------------------------------------- layers
@@ -185,7 +187,7 @@ int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const Fra
     return WAM_OK;
   }
   HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, 3 * D, D, b.Y, D, w.wqkv, D, e));
-  HIPCK(attn_prefill(c.s, dt, d->Hh, n, row0, tab, b.Q, kl, vl, cap, b.O));
+  HIPCK(attn_prefill(c.s, dt, d->Hh, n, row0, tab, b.Q, kl, vl, cap, b.O, b.pattn, b.pattn_bytes));
   EpiArgs r{};
   r.out = b.X;
   r.ldo = D;
@@ -287,6 +289,8 @@ void plan_action(Arena& a, const wam_dims* d, int B, int max_len, bool with_emb,
   b.pend = 0;
   b.attn_bytes = attn_action_scratch_bytes(B, d->Hh, d->H, max_len, 0);
   b.attn = a.take(b.attn_bytes);
+  b.pattn = nullptr;
+  b.pattn_bytes = 0;
 }
 
 void plan_prefill(Arena& a, const wam_dims* d, int Fh, int Ff, Bufs& b, float** z) {
@@ -307,6 +311,8 @@ void plan_prefill(Arena& a, const wam_dims* d, int Fh, int Ff, Bufs& b, float** 
   b.pend = 0;
   b.attn = nullptr;
   b.attn_bytes = 0;
+  b.pattn_bytes = attn_prefill_split_bytes(d->Hh, (int)T);
+  b.pattn = (float*)a.take(b.pattn_bytes);
 }
 
 size_t layer_stride(const wam_kv* kv) {
@@ -754,7 +760,7 @@ int wam_attention_prefill(int dtype, int Hh, int dh, int nq, int row0, int P, co
   const void* ptrs[] = {q, kc, vc, out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(WAM_E_ALIGN, "pointer not 16-byte aligned");
-  HIPCK(attn_prefill((hipStream_t)stream, dtype, Hh, nq, row0, tab, q, kc, vc, cap, out));
+  HIPCK(attn_prefill((hipStream_t)stream, dtype, Hh, nq, row0, tab, q, kc, vc, cap, out, nullptr, 0));
   return WAM_OK;
 }
 

@@ -196,8 +196,13 @@ struct FuseArgs {
 hipError_t fuse_kv(hipStream_t s, int dt, const void* src, void* dst, long long layer_elems,
                    const FuseArgs& a);
 
+// part / part_bytes: workspace for split partials (bf16 launches with few
+// query tiles split their keys and merge; NULL: never split).
 hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int nq, int row0, const FrameTab& tab,
-                        const void* q, const void* kc, const void* vc, int cap, void* out);
+                        const void* q, const void* kc, const void* vc, int cap, void* out,
+                        float* part, size_t part_bytes);
+// Partial workspace a prefill of up to max_rows query rows can use.
+size_t attn_prefill_split_bytes(int Hh, int max_rows);
 
 struct ActLens {
   int len[WAM_MAX_BATCH];
