@@ -192,6 +192,14 @@ __global__ __launch_bounds__(256, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   constexpr int MI = G::MI, NI = G::NI, WM = G::WM, WN = G::WN, STAGE = G::STAGE;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  // k split (gridDim.y > 1, plain fp32 stores only): workgroup (., ks) takes
+  // k range [ks K, (ks + 1) K) and writes its partial to out + ks M ldo.
+  if constexpr (EPI == EPI_STORE) {
+    const int ks = blockIdx.y;
+    A += (long long)ks * K;
+    B += (long long)ks * K;
+    e.out = (TO*)e.out + (long long)ks * M * e.ldo;
+  }
   const int ntm = (M + BM - 1) / BM, ntn = N / BN;
   int tm, tn;
   swizzle_tile(blockIdx.x, gridDim.x, ntm, ntn, &tm, &tn);
@@ -479,6 +487,34 @@ static hipError_t launch_big(hipStream_t s, int M, int N, int K, const void* A, 
     hipLaunchKernelGGL((gemm_big_kernel<128, EPI, TO>), dim3(ntm * ntn), dim3(256), 0, s,
                        (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K, e);
   }
+  return hipGetLastError();
+}
+
+// Split-K for row counts whose 128x128 tiles leave CUs idle: ks partial
+// products part[ks][M][N] (raw fp32, 128-row tiles), summed by the consumer
+// in ks order.  1 where the tiles fill the CUs or K does not split evenly.
+int gemm_big_splits(int M, int N, int K) {
+  if (N % big2::BN || K % big2::BK) return 1;
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 256;
+  const long long tiles = (long long)((M + 127) / 128) * (N / big2::BN);
+  int ks = 1;
+  while (ks < 4 && tiles * ks * 2 <= n_cu * 2 && K % (ks * 2 * big2::BK) == 0) ks *= 2;
+  return ks;
+}
+
+hipError_t gemm_big_partial(hipStream_t s, int M, int N, int K, const void* A, int lda,
+                            const void* B, int ldb, float* part, int ks) {
+  if (ks < 1 || K % (ks * big2::BK) || N % big2::BN) return hipErrorInvalidValue;
+  TimingScope ts(s, KC_GEMM_BIG, gemm_bytes<EPI_STORE>(M, N, K, 2, 2, 4 * ks), 2.0 * M * N * K);
+  EpiArgs e{};
+  e.out = part;
+  e.ldo = N;
+  const int ntm = (M + 127) / 128, ntn = N / big2::BN;
+  hipLaunchKernelGGL((gemm_big_kernel<128, EPI_STORE, float>), dim3(ntm * ntn, ks), dim3(256), 0, s,
+                     (const bf16_t*)A, lda, (const bf16_t*)B, ldb, M, N, K / ks, e);
   return hipGetLastError();
 }
 

@@ -145,7 +145,8 @@ struct Bufs {
   void* Hb;
   float* Yh;
   float* emb;
-  float* part;  // split partial products of the action path
+  float* part;  // split partial products (action path; prefill rows that split)
+  size_t part_bytes;
   int pend;     // splits of a product not yet added to X (0: none)
   void* attn;
   size_t attn_bytes;
@@ -160,13 +161,17 @@ struct Layer {
   Bufs* b;
 };
 
+int norm_rows(const Layer& c, int odt, const float* g, void* y, int M);
+int video_resid(const Layer& c, int M, int N, int K, const void* A, const void* W);
+
 // One video layer for rows row0..row0+n-1 of episode cache layer (kl, vl).
 int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const FrameTab& tab,
                 void* kl, void* vl, int cap, bool kv_only) {
   const wam_dims* d = c.d;
   const int dt = d->dtype, D = d->D;
   Bufs& b = *c.b;
-  HIPCK(rmsnorm(c.s, dt, b.X, w.g1, b.Y, n, D));
+  int st;
+  if ((st = norm_rows(c, dt, w.g1, b.Y, n))) return st;
   EpiArgs e{};
   e.q = b.Q;
   e.k = kl;
@@ -188,17 +193,13 @@ int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const Fra
   }
   HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, 3 * D, D, b.Y, D, w.wqkv, D, e));
   HIPCK(attn_prefill(c.s, dt, d->Hh, n, row0, tab, b.Q, kl, vl, cap, b.O, b.pattn, b.pattn_bytes));
-  EpiArgs r{};
-  r.out = b.X;
-  r.ldo = D;
-  HIPCK(gemm(c.s, dt, dt, WAM_F32, EPI_RESID, n, D, D, b.O, D, w.wo, D, r));
-  HIPCK(rmsnorm(c.s, dt, b.X, w.g2, b.Y, n, D));
+  if ((st = video_resid(c, n, D, D, b.O, w.wo))) return st;
+  if ((st = norm_rows(c, dt, w.g2, b.Y, n))) return st;
   EpiArgs gl{};
   gl.out = b.Hb;
   gl.ldo = d->Fm;
   HIPCK(gemm(c.s, dt, dt, dt, EPI_GELU, n, d->Fm, D, b.Y, D, w.w1, D, gl));
-  HIPCK(gemm(c.s, dt, dt, WAM_F32, EPI_RESID, n, D, d->Fm, b.Hb, d->Fm, w.w2, d->Fm, r));
-  return WAM_OK;
+  return video_resid(c, n, D, d->Fm, b.Hb, w.w2);
 }
 
 // X += A W^T for the action rows, as split partials that the next RMSNorm adds
@@ -209,6 +210,26 @@ int action_resid(const Layer& c, int M, int N, int K, const void* A, const void*
   if (d->dtype == WAM_BF16 && gemm_partial_splits(M, N, K) > 0) {
     int ks = 0;
     HIPCK(gemm_partial(c.s, M, N, K, A, K, W, K, b.part, &ks));
+    b.pend = ks;
+    return WAM_OK;
+  }
+  EpiArgs r{};
+  r.out = b.X;
+  r.ldo = N;
+  HIPCK(gemm(c.s, d->dtype, d->dtype, WAM_F32, EPI_RESID, M, N, K, A, K, W, K, r));
+  b.pend = 0;
+  return WAM_OK;
+}
+
+// X += A W^T for video rows: as split partials (b.pend) where the rows are
+// too few to fill the CUs with output tiles and the workspace holds them,
+// else directly.  The next RMSNorm adds pending partials to X.
+int video_resid(const Layer& c, int M, int N, int K, const void* A, const void* W) {
+  const wam_dims* d = c.d;
+  Bufs& b = *c.b;
+  const int ks = d->dtype == WAM_BF16 && b.part ? gemm_big_splits(M, N, K) : 1;
+  if (ks > 1 && (size_t)ks * M * N * 4 <= b.part_bytes) {
+    HIPCK(gemm_big_partial(c.s, M, N, K, A, K, W, K, b.part, ks));
     b.pend = ks;
     return WAM_OK;
   }
@@ -285,7 +306,8 @@ void plan_action(Arena& a, const wam_dims* d, int B, int max_len, bool with_emb,
   b.O = a.take((size_t)M * d->D * e);
   b.Hb = a.take((size_t)M * d->Fm * e);
   b.Yh = (float*)a.take((size_t)M * d->D * 4);
-  b.part = (float*)a.take((size_t)4 * M * d->D * 4);
+  b.part_bytes = (size_t)4 * M * d->D * 4;
+  b.part = (float*)a.take(b.part_bytes);
   b.pend = 0;
   b.attn_bytes = attn_action_scratch_bytes(B, d->Hh, d->H, max_len, 0);
   b.attn = a.take(b.attn_bytes);
@@ -307,7 +329,14 @@ void plan_prefill(Arena& a, const wam_dims* d, int Fh, int Ff, Bufs& b, float** 
   b.Yh = (float*)a.take(std::max<size_t>(Tf, 1) * d->D * 4);
   *z = (float*)a.take(std::max<size_t>(Tf, 1) * d->Cv * 4);
   b.Ka = b.Va = nullptr;
-  b.part = nullptr;
+  // residual products of row counts that leave CUs idle split k 4 ways at most,
+  // and only while their 128x128 tiles number at most one per CU
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 256;
+  b.part_bytes = (size_t)4 * std::min(T * d->D, (size_t)n_cu * 128 * 128 + (size_t)128 * d->D) * 4;
+  b.part = (float*)a.take(b.part_bytes);
   b.pend = 0;
   b.attn = nullptr;
   b.attn_bytes = 0;
@@ -494,6 +523,7 @@ int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video, const 
           if ((st = video_layer(c, video->layers[l], Tf, Th, tabs[b], kl(l), vl(l), cache->cap,
                                 false)))
             return st;
+        if ((st = flush_pending(c, video->g_out, Tf))) return st;  // X whole for the head
         HIPCK(step_boundary(s, dt, bufs.X, video->g_out, video->w_out, z, sig[k + 1] - sig[k],
                             nullptr, nullptr, nullptr, Tf, D, d->Cv, true));
       }

@@ -159,6 +159,13 @@ int gemm_partial_splits(int M, int N, int K);
 hipError_t gemm_partial(hipStream_t s, int M, int N, int K, const void* A, int lda, const void* B,
                         int ldb, float* part, int* ks_out);
 
+// bf16 rows whose tiles leave CUs idle (M in the thousands): the same split
+// partials with the large-tile kernel; gemm_big_splits gives the split count
+// (1: do not split).
+int gemm_big_splits(int M, int N, int K);
+hipError_t gemm_big_partial(hipStream_t s, int M, int N, int K, const void* A, int lda,
+                            const void* B, int ldb, float* part, int ks);
+
 hipError_t rmsnorm(hipStream_t s, int odt, const float* x, const float* g, void* y, int M, int D);
 // x[m] += sum_{ks < KS} part[ks][m] (in ks order), then y = RMSNorm(x; g).
 hipError_t rmsnorm_accum(hipStream_t s, int odt, float* x, const float* part, int KS,
