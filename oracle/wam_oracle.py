@@ -258,25 +258,15 @@ def oracle_dtype(cfg) -> torch.dtype:
     return torch.float64 if cfg.dtype == "f32" else torch.float32
 
 
-def video_prefill(cfg, vw: dict, hist_b, valid_b, eps_v_b, drop_padded: bool = True):
-    """Video expert for one episode: history prefill, imagine, cache pass.
+def history_cache(cfg, vw: dict, hist_b, valid_b, drop_padded: bool = True):
+    """History/anchor prefill of one episode: the history tokens at sigma = 0
+    run through the L layers with block-causal attention and each layer's
+    K, V are kept (Fast-WAM page section 七.1, ``prefill_video_cache``;
+    Long-WAM Summary section 3.2).  The last layer only needs K, V.
 
-    * History/anchor tokens at sigma = 0 run through the L layers with
-      block-causal attention; each layer's K, V are kept (Fast-WAM page
-      section 七.1, ``prefill_video_cache``; Long-WAM Summary section 3.2).
-    * Imagine (V >= 1): future latents start from noise and take V Euler steps
-      to sigma* = 0.9, keys = [history cache ; future] under the same block
-      rule; they are never decoded (Long-WAM close-reading sections 03-04;
-      Summary section 3.2).
-    * Cache pass: the future latents at sigma* (or, with V = 0, the noise at
-      video time 1, Faster-WAM page section 3.1) run once more and their
-      per-layer K, V are appended to the cache.  The last layer only needs K, V.
-
-    ``drop_padded`` leaves padded history frames out of the token list; with
-    False they are kept as tokens and masked as keys (the result on valid
-    rows is the same, a pinned identity).
-    Returns (cache: list of (K, V) [T, Hh, dh] per layer over the valid rows
-             in frame order, z: [Ff*P, Cv], frames: frame index per cache row).
+    Returns (cache_h: list of (K, V) [Th, Hh, dh] per layer, fall: frame index
+    of every [history ; future] token, valid: frame validity [Fh + Ff],
+    mask_f: visibility of [history ; future] keys for the future queries).
     """
     dt = vw["w_in"].dtype
     P, Fh, Ff, D, Hh, L = cfg.P, cfg.Fh, cfg.Ff, cfg.D, cfg.Hh, len(vw["layers"])
@@ -301,6 +291,32 @@ def video_prefill(cfg, vw: dict, hist_b, valid_b, eps_v_b, drop_padded: bool = T
     else:
         empty = torch.zeros((0, Hh, D // Hh), dtype=dt)
         cache_h = [(empty, empty)] * L
+    return cache_h, fall, valid, mask_f
+
+
+def video_prefill(cfg, vw: dict, hist_b, valid_b, eps_v_b, drop_padded: bool = True):
+    """Video expert for one episode: history prefill, imagine, cache pass.
+
+    * History/anchor tokens at sigma = 0 run through the L layers with
+      block-causal attention; each layer's K, V are kept (Fast-WAM page
+      section 七.1, ``prefill_video_cache``; Long-WAM Summary section 3.2).
+    * Imagine (V >= 1): future latents start from noise and take V Euler steps
+      to sigma* = 0.9, keys = [history cache ; future] under the same block
+      rule; they are never decoded (Long-WAM close-reading sections 03-04;
+      Summary section 3.2).
+    * Cache pass: the future latents at sigma* (or, with V = 0, the noise at
+      video time 1, Faster-WAM page section 3.1) run once more and their
+      per-layer K, V are appended to the cache.  The last layer only needs K, V.
+
+    ``drop_padded`` leaves padded history frames out of the token list; with
+    False they are kept as tokens and masked as keys (the result on valid
+    rows is the same, a pinned identity).
+    Returns (cache: list of (K, V) [T, Hh, dh] per layer over the valid rows
+             in frame order, z: [Ff*P, Cv], frames: frame index per cache row).
+    """
+    dt = vw["w_in"].dtype
+    D, Hh, L = cfg.D, cfg.Hh, len(vw["layers"])
+    cache_h, fall, valid, mask_f = history_cache(cfg, vw, hist_b, valid_b, drop_padded)
 
     z = torch.from_numpy(np.ascontiguousarray(eps_v_b)).to(dt).reshape(-1, cfg.Cv)
     if cfg.V >= 1:
@@ -414,12 +430,92 @@ def run_chunk(cfg, inp: dict, dtype=None, drop_padded: bool = True,
 
 
 # --------------------------------------------------------------------------
+# Co-denoising (CoD)
+# --------------------------------------------------------------------------
+
+
+def codenoise(cfg, vw: dict, aw: dict, hist_b, valid_b, eps_v_b, eps_a_b, steps: int,
+              sigma_video_end: float = 0.0):
+    """Co-denoising of one episode: the future video latents and the action
+    chunk take the same number of Euler steps together.
+
+    The pages set CoD beside IDM: video and actions are updated jointly
+    (Long-WAM Summary section 3.2, Figure 2; the page "Long-WAM：机器人操作模型
+    的长历史..." section 三, the four-strategy figure), and the joint inference
+    call creates both latents and returns both after its iterations ("Fast-WAM
+    精读" page, section 03).  In every pass video queries never read action
+    tokens, and action queries read the observed history, the partially
+    denoised future and the whole noisy chunk (same two places).
+
+    Reading adopted (the pages give no step-level listing): one shared step
+    count (the pages time CoD as V4/A4 and V2/A2, Long-WAM Summary appendix F);
+    video levels sigma_v = schedule(steps, sigma_video_end) (0: the returned
+    video is fully denoised), action levels t = schedule(steps, 0).  Step k:
+      1. the future at sigma_v[k] runs through the video layers with keys
+         [history cache ; future] under the block rule -> v-hat_video and the
+         future K, V of every layer;
+      2. the action expert at t[k] reads [history ; future at sigma_v[k]] at
+         every layer it pairs with -> v-hat_action;
+      3. z += (sigma_v[k+1] - sigma_v[k]) v-hat_video, a += (t[k+1] - t[k])
+         v-hat_action.
+    Since video rows never read actions, computing step 1 before step 2 is
+    the same as one joint pass over [history ; future ; actions].
+
+    Returns (a, z, per-step list of (z_k, a_k, vhat_video_k, vhat_action_k),
+    cache: per layer (K, V) over [history ; future at the last video level]).
+    """
+    dt = vw["w_in"].dtype
+    D, Hh = cfg.D, cfg.Hh
+    if cfg.fuse:
+        raise ValueError("co-denoising reads the per-layer cache (no interval fusion)")
+    cache_h, fall, valid, mask_f = history_cache(cfg, vw, hist_b, valid_b)
+    sv = schedule(steps, sigma_video_end, cfg.shift)
+    ta = schedule(steps, 0.0, cfg.shift)
+    z = torch.from_numpy(np.ascontiguousarray(eps_v_b)).to(dt).reshape(-1, cfg.Cv)
+    a = torch.from_numpy(np.ascontiguousarray(eps_a_b)).to(dt)
+    traj = []
+    cache = None
+    for k in range(steps):
+        X = embed(z, vw["w_in"], float(sv[k]), D)
+        cache = []
+        for l, lw in enumerate(vw["layers"]):
+            X, K, V = layer(X, lw, Hh, cache_h[l], mask_f)
+            cache.append((torch.cat([cache_h[l][0], K]), torch.cat([cache_h[l][1], V])))
+        v_v = head(X, vw["g_out"], vw["w_out"])
+        v_a = action_velocity(cfg, aw, [None if r < 0 else cache[r] for r in cfg.read_map],
+                              a, float(ta[k]))
+        traj.append((z, a, v_v, v_a))
+        z = euler_step(z, v_v, sv[k], sv[k + 1])
+        a = euler_step(a, v_a, ta[k], ta[k + 1])
+    return a, z, traj, cache
+
+
+def run_codenoise(cfg, inp: dict, dtype=None, steps: Optional[int] = None,
+                  sigma_video_end: float = 0.0):
+    """CoD for every episode (``codenoise``), ``steps`` = cfg.N by default.
+    Returns actions [B, H, A], z [B, Ff*P, Cv] (float64 numpy) and the action
+    v-hat per step [steps, B, H, A]."""
+    dt = dtype or oracle_dtype(cfg)
+    n = steps or cfg.N
+    vw = to_torch_expert(inp["video"], dt)
+    aw = to_torch_expert(inp["action"], dt)
+    acts, zs, vhs = [], [], []
+    for b in range(cfg.B):
+        a, z, traj, _ = codenoise(cfg, vw, aw, inp["hist"][b], inp["hist_valid"][b],
+                                  inp["eps_v"][b], inp["eps_a"][b], n, sigma_video_end)
+        acts.append(a.double().numpy())
+        zs.append(z.double().numpy())
+        vhs.append(np.stack([t[3].double().numpy() for t in traj]))
+    return {"actions": np.stack(acts), "z": np.stack(zs), "vhat": np.stack(vhs, axis=1)}
+
+
+# --------------------------------------------------------------------------
 # Uncached references used by the structural pins
 # --------------------------------------------------------------------------
 
 
 def joint_mot_step(cfg, vw: dict, aw: dict, video_tok, video_sigma, video_frames,
-                   frame_valid, a, t: float):
+                   frame_valid, a, t: float, video_head: bool = False):
     """One pass of the two experts over ONE joint sequence [video ; action],
     with no cache: each row uses its expert's weights, one attention over the
     union with an explicit mask where video rows see video columns by the
@@ -428,7 +524,8 @@ def joint_mot_step(cfg, vw: dict, aw: dict, video_tok, video_sigma, video_frames
     asymmetric interface; Fast-WAM page section 四.4 layer pairing).
 
     video_tok [Nv, Cv] at per-row levels video_sigma [Nv]; a [H, A] at t.
-    Returns (v-hat of the action rows, per-layer video (K, V)).
+    Returns (v-hat of the action rows, per-layer video (K, V)), and with
+    ``video_head`` also the video expert's v-hat of every video row.
     """
     D, Hh = cfg.D, cfg.Hh
     dh = D // Hh
@@ -457,6 +554,8 @@ def joint_mot_step(cfg, vw: dict, aw: dict, video_tok, video_sigma, video_frames
         Xa = Xa + O[Nv:] @ la["wo"].T
         Xv = Xv + gelu(rmsnorm(Xv, lv["g2"]) @ lv["w1"].T) @ lv["w2"].T
         Xa = Xa + gelu(rmsnorm(Xa, la["g2"]) @ la["w1"].T) @ la["w2"].T
+    if video_head:
+        return head(Xa, aw["g_out"], aw["w_out"]), kv, head(Xv, vw["g_out"], vw["w_out"])
     return head(Xa, aw["g_out"], aw["w_out"]), kv
 
 

@@ -423,3 +423,68 @@ def test_action_only_layers_ignore_video():
     inp2["hist"] = inp["hist"] * 3.0
     inp2["eps_v"] = inp["eps_v"] * -1.0
     assert np.array_equal(a1, O.run_chunk(cfg, inp2)["actions"])
+
+
+# ---------------------------------------------------------------- co-denoising
+def test_codenoise_video_trajectory_equals_imagine():
+    # Video rows never read actions, so CoD's video latents follow exactly the
+    # IDM imagine trajectory on the same schedule (here: 2 steps to 0.9).
+    cfg = _tiny(V=2, N=2)
+    inp = inputs.generate(cfg, threads=1)
+    vw = O.to_torch_expert(inp["video"], f64)
+    aw = O.to_torch_expert(inp["action"], f64)
+    _, z_idm, _ = O.video_prefill(cfg, vw, inp["hist"][0], inp["hist_valid"][0], inp["eps_v"][0])
+    _, z_cod, traj, _ = O.codenoise(cfg, vw, aw, inp["hist"][0], inp["hist_valid"][0],
+                                    inp["eps_v"][0], inp["eps_a"][0], 2, 0.9)
+    assert torch.max(torch.abs(z_cod - z_idm)) < 1e-12
+    assert len(traj) == 2
+
+
+def test_codenoise_one_step_equals_faster_wam():
+    # One joint step reads the future at video level 1 (pure noise): the
+    # Faster-WAM path (V = 0, future cached at sigma = 1) with N = 1.
+    cfg = _tiny(V=0, N=1)
+    inp = inputs.generate(cfg, threads=1)
+    ref = O.run_chunk(cfg, inp)["actions"]
+    cod = O.run_codenoise(cfg, inp, steps=1)["actions"]
+    assert np.max(np.abs(cod - ref)) < 1e-12
+    # with two steps the second action step sees a moved future
+    cfg2 = _tiny(V=0, N=2)
+    two_idm = O.run_chunk(cfg2, inp)["actions"]
+    two_cod = O.run_codenoise(cfg2, inp, steps=2)["actions"]
+    assert np.max(np.abs(two_cod - two_idm)) > 1e-6
+
+
+@pytest.mark.parametrize("end", [0.0, 0.5])
+def test_codenoise_steps_equal_joint_sequence(end):
+    # Every CoD step equals one uncached joint pass over [history ; future at
+    # the step's video level ; actions at the step's action level]: both
+    # velocities, at every step (a stale or wrong-level future would differ).
+    cfg = _tiny(N=3)
+    inp = inputs.generate(cfg, threads=1)
+    vw = O.to_torch_expert(inp["video"], f64)
+    aw = O.to_torch_expert(inp["action"], f64)
+    a_fin, z_fin, traj, cache = O.codenoise(cfg, vw, aw, inp["hist"][0], inp["hist_valid"][0],
+                                            inp["eps_v"][0], inp["eps_a"][0], 3, end)
+    sv = O.schedule(3, end)
+    ta = O.schedule(3, 0.0)
+    valid_frames = [f for f in range(cfg.Fh) if inp["hist_valid"][0][f]]
+    hist_tok = torch.tensor(inp["hist"][0][valid_frames], dtype=f64).reshape(-1, cfg.Cv)
+    nh = hist_tok.shape[0]
+    frames = torch.tensor(valid_frames + [cfg.Fh + j for j in range(cfg.Ff)]).repeat_interleave(cfg.P)
+    fvalid = list(inp["hist_valid"][0]) + [1] * cfg.Ff
+    for k, (z_k, a_k, vv_k, va_k) in enumerate(traj):
+        vtok = torch.cat([hist_tok, z_k])
+        vsig = [0.0] * nh + [float(sv[k])] * z_k.shape[0]
+        va, kv, vv = O.joint_mot_step(cfg, vw, aw, vtok, vsig, frames, fvalid, a_k, float(ta[k]),
+                                      video_head=True)
+        assert torch.max(torch.abs(va - va_k)) < 1e-12
+        assert torch.max(torch.abs(vv[nh:] - vv_k)) < 1e-12
+        if k == len(traj) - 1:
+            for (Kc, Vc), (Kj, Vj) in zip(cache, kv):
+                assert torch.max(torch.abs(Kc - Kj)) < 1e-12
+                assert torch.max(torch.abs(Vc - Vj)) < 1e-12
+    # the trajectories end where the schedules say: a_N from the last step
+    z_last, a_last, vv_last, va_last = traj[-1]
+    assert torch.max(torch.abs(a_fin - (a_last + float(ta[3] - ta[2]) * va_last))) < 1e-12
+    assert torch.max(torch.abs(z_fin - (z_last + float(sv[3] - sv[2]) * vv_last))) < 1e-12
