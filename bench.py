@@ -33,6 +33,7 @@ WORKLOAD_TEXT = {
     "C2": "Faster-WAM SparseMoT: C1 shape, 8 interaction layers reading interval-fused K/V (stride 4)",
     "C3": "Long-WAM IDM: 24 history + 2 future frames x 880 tokens, V=4 to sigma*=0.9, N=4",
     "C4": "long-context: 48 history (19 padded) + 2 future x 880 tokens, V=4, N=10, B=4",
+    "C5": "Long-WAM co-denoising: 24 history + 2 future frames x 880 tokens, 4 joint video+action steps (V4/A4)",
 }
 
 
@@ -133,7 +134,10 @@ def cpu_baseline(cfg_name: str, layers: int) -> dict:
     cfg = configs.get(cfg_name, **kw)
     inp = inputs.generate(cfg)
     t0 = time.perf_counter()
-    O.run_chunk(cfg, inp)
+    if cfg.joint:
+        O.run_codenoise(cfg, inp)
+    else:
+        O.run_chunk(cfg, inp)
     dt = time.perf_counter() - t0
     scale = full.L / layers
     return {"value": round(dt * scale * 1e3, 1), "unit": "ms/chunk", "cores": torch.get_num_threads(),
@@ -252,7 +256,8 @@ def main():
         "data": "synthetic (seeded N(0,1) latents/noise, N(0,0.02^2) random-init weights)",
         "config": {"workload": f"{cfg.name}: {WORKLOAD_TEXT.get(cfg.name, '')}", "B": cfg.B,
                    "L": cfg.L, "D": cfg.D, "heads": f"{cfg.Hh}x{cfg.dh}", "kv_tokens": cfg.tokens_valid,
-                   "action_steps": cfg.N, "video_steps": cfg.V},
+                   "action_steps": cfg.N, "video_steps": cfg.N if cfg.joint else cfg.V,
+                   "joint": cfg.joint},
         "roofline": roofline,
         "attn_action_hbm_gbps": kt.get("attn_action", {}).get("achieved"),
         "prefill_attn_mfma_util": kt.get("attn_prefill", {}).get("frac"),

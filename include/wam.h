@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define WAM_ABI_VERSION 1
+#define WAM_ABI_VERSION 2
 #define WAM_MAX_FRAMES 256   /* latent frames per episode (history + future) */
 #define WAM_MAX_BATCH 64     /* episodes per call */
 #define WAM_MAX_FUSE 32      /* fused pairs per wam_fuse_interval_kv call */
@@ -200,6 +200,44 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
                       const int32_t* read_map, const float* eps, int B, int N,
                       double shift, float* actions_out, float* vhat_out,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * wam_codenoise_chunk -- co-denoising (CoD): the future video latents and the
+ * action chunk take N Euler steps together (Long-WAM Summary section 3.2 and
+ * Figure 2; the joint call creates and returns both latents, "Fast-WAM 精读"
+ * section 03).  Video levels sigma_k = sigma_video_end + (1 - sigma_video_end)
+ * phi(1 - k/N), action levels t_k = phi(1 - k/N).  Step k:
+ *   1. per episode, z at sigma_k runs through the L video layers with keys
+ *      [history rows ; future] under the block rule of wam_prefill_video_cache
+ *      (video rows never read actions); every layer writes its future K, V to
+ *      cache rows [len_h[b], len_h[b] + Ff*P) and v_video = head(X);
+ *   2. the action expert at t_k, layer l attending over cache layer l rows
+ *      [0, len_h[b] + Ff*P) (history and the future at sigma_k) and the
+ *      chunk's own keys;
+ *   3. z += (sigma_{k+1} - sigma_k) v_video, a += (t_{k+1} - t_k) v_action.
+ * Step 1 before step 2 is the same as one joint pass over [history ; future ;
+ * actions], since video rows read no action token.
+ *   cache       in: the history rows only, as wam_prefill_video_cache leaves
+ *               them with Ff = 0 (len[b] must equal valid history frames * P);
+ *               out: plus the future rows at the last video level, len updated.
+ *               n_layers == L; the action layers pair with it densely.
+ *   hist_valid  host [B][Fh] uint8 or NULL, frame_block host [Fh + Ff]: the
+ *               tables of the history prefill
+ *   fut_noise   device [B][Ff][P][Cv] dtype      video noise at sigma_0 = 1
+ *   eps         device [B][H][A] fp32            action noise at t_0 = 1
+ *   actions_out device [B][H][A] fp32
+ *   fut_latents_out device [B][Ff][P][Cv] fp32  (required: holds z during the
+ *               call; z at sigma_N on return)
+ *   vhat_out    device [N][B][H][A] fp32 or NULL (action velocity per step)
+ * Requires Ff >= 1, 1 <= N <= WAM_MAX_STEPS, 0 <= sigma_video_end < 1.
+ * ------------------------------------------------------------------------- */
+size_t wam_codenoise_workspace_bytes(const wam_dims* d, int B, int Ff, const wam_kv* cache);
+int wam_codenoise_chunk(const wam_dims* d, const wam_expert_w* video,
+                        const wam_expert_w* action, const uint8_t* hist_valid, int B, int Fh,
+                        const void* fut_noise, int Ff, const int32_t* frame_block,
+                        const float* eps, int N, double sigma_video_end, double shift,
+                        wam_kv* cache, float* actions_out, float* fut_latents_out,
+                        float* vhat_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Auxiliary calls.

@@ -15,6 +15,9 @@ Five synthetic workloads span the three systems the pages describe:
   section 3.2 and section 6.2, V4/A4).
 * ``C4`` long-context stress: 48 history frames (the earliest 19 zero-padded
   and masked), 10 action steps, 4 independent episodes.
+* ``C5`` Long-WAM co-denoising (CoD): the C3 shape with the two future frames
+  and the action chunk denoised together, 4 joint steps (V4/A4), the video to
+  flow time 0 ("Long-WAM ... Summary" page, section 3.2 and appendix F).
 
 This module holds shapes and tables only; no arithmetic of the method.
 """
@@ -51,6 +54,8 @@ class WamConfig:
     seed: int = 0
     qk_std: float = 0.02  # std of the Wq/Wk rows (0.06 gives the "sharp" variant)
     w_std: float = 0.02   # std of every other matrix
+    joint: bool = False   # co-denoising: video and actions take the N steps together
+    video_end: float = 0.0  # co-denoising: flow time the video reaches after N steps
 
     @property
     def F(self) -> int:
@@ -118,6 +123,11 @@ CONFIGS = {
         name="C4", dtype="bf16", L=30, D=1024, Hh=16, dh=64, Fm=4096, Cv=64, A=14,
         H=32, B=4, P=880, Fh=48, Ff=2, frame_block=tuple(range(50)), pad_frames=19,
         V=4, sigma_star=0.9, N=10, shift=1.0, read_map=_dense(30), seed=1004),
+    "C5": WamConfig(
+        name="C5", dtype="bf16", L=30, D=1024, Hh=16, dh=64, Fm=4096, Cv=64, A=14,
+        H=32, B=1, P=880, Fh=24, Ff=2, frame_block=tuple(range(26)), pad_frames=0,
+        V=4, sigma_star=0.9, N=4, shift=1.0, read_map=_dense(30), seed=1005,
+        joint=True, video_end=0.0),
 }
 
 

@@ -715,6 +715,128 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
   return WAM_OK;
 }
 
+// ----------------------------------------------------------------- co-denoising
+size_t wam_codenoise_workspace_bytes(const wam_dims* d, int B, int Ff, const wam_kv* cache) {
+  if (check_dims(d) || B < 1 || B > WAM_MAX_BATCH || Ff < 1 || !cache) return 0;
+  Arena a(nullptr);
+  Bufs vb, ab;
+  float* z;
+  plan_prefill(a, d, 0, Ff, vb, &z);
+  plan_action(a, d, B, cache->cap, true, ab);
+  return a.off + 256;
+}
+
+int wam_codenoise_chunk(const wam_dims* d, const wam_expert_w* video, const wam_expert_w* action,
+                        const uint8_t* hist_valid, int B, int Fh, const void* fut_noise, int Ff,
+                        const int32_t* frame_block, const float* eps, int N,
+                        double sigma_video_end, double shift, wam_kv* cache, float* actions_out,
+                        float* fut_latents_out, float* vhat_out, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int st;
+  if ((st = check_dims(d))) return st;
+  if ((st = check_expert(d, video, "video"))) return st;
+  if ((st = check_expert(d, action, "action"))) return st;
+  if (B < 1 || B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "B must be in [1, %d]", WAM_MAX_BATCH);
+  if (Fh < 0 || Ff < 1 || Fh + Ff > WAM_MAX_FRAMES)
+    return fail(WAM_E_SHAPE, "co-denoising needs Ff >= 1 and Fh + Ff <= %d", WAM_MAX_FRAMES);
+  if (!fut_noise || !eps || !actions_out || !fut_latents_out || !frame_block)
+    return fail(WAM_E_ARG, "NULL pointer");
+  if (!aligned16(fut_noise) || !aligned16(eps) || !aligned16(actions_out) ||
+      !aligned16(fut_latents_out) || (vhat_out && !aligned16(vhat_out)))
+    return fail(WAM_E_ALIGN, "pointer not 16-byte aligned");
+  if ((st = check_blocks(frame_block, Fh + Ff))) return st;
+  if (N < 1 || N > WAM_MAX_STEPS) return fail(WAM_E_ARG, "N must be in [1, %d]", WAM_MAX_STEPS);
+  if (!(sigma_video_end >= 0.0 && sigma_video_end < 1.0))
+    return fail(WAM_E_ARG, "sigma_video_end must be in [0, 1)");
+  if (!(shift > 0.0)) return fail(WAM_E_ARG, "shift must be > 0");
+  if (!cache) return fail(WAM_E_ARG, "cache is NULL");
+  if ((st = check_kv(d, cache, B, "cache"))) return st;
+  if (cache->n_layers != d->L) return fail(WAM_E_SHAPE, "cache must hold L layers");
+  if (!ws || !aligned16(ws) || ws_bytes < wam_codenoise_workspace_bytes(d, B, Ff, cache))
+    return fail(WAM_E_WORKSPACE, "workspace missing or too small");
+
+  // frame tables; the cache must hold exactly the valid history rows
+  const int P = d->P;
+  std::vector<FrameTab> tabs(B);
+  std::vector<int> nh(B);
+  ActLens lens{};
+  for (int b = 0; b < B; b++) {
+    int src[WAM_MAX_FRAMES], kend[WAM_MAX_FRAMES];
+    const uint8_t* v = hist_valid ? hist_valid + (size_t)b * Fh : nullptr;
+    const int n = frame_table(frame_block, v, Fh, Ff, P, src, kend);
+    if (n == 0) return fail(WAM_E_SHAPE, "episode %d has no valid frame", b);
+    if ((long long)n * P > cache->cap)
+      return fail(WAM_E_SHAPE, "episode %d needs %d cache rows, cap is %d", b, n * P, cache->cap);
+    nh[b] = n - Ff;
+    if (cache->len[b] != nh[b] * P)
+      return fail(WAM_E_SHAPE, "episode %d: cache holds %d rows, its valid history has %d", b,
+                  cache->len[b], nh[b] * P);
+    tabs[b].n = n;
+    tabs[b].P = P;
+    for (int i = 0; i < n; i++) tabs[b].kend[i] = kend[i];
+    lens.len[b] = n * P;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  Arena a(ws);
+  Bufs vb, ab;
+  float* zs;
+  plan_prefill(a, d, 0, Ff, vb, &zs);
+  plan_action(a, d, B, cache->cap, true, ab);
+  std::vector<float> sv(N + 1), ta(N + 1);
+  schedule(N, sigma_video_end, shift, sv.data());
+  schedule(N, 0.0, shift, ta.data());
+  const int D = d->D, dt = d->dtype, M = B * d->H, Tf = Ff * P;
+  HIPCK(time_embedding(s, sv.data(), N, D, vb.emb));
+  HIPCK(time_embedding(s, ta.data(), N, D, ab.emb));
+  for (int b = 0; b < B; b++)
+    HIPCK(copy_cvt_f32(s, dt, (const char*)fut_noise + (size_t)b * Tf * d->Cv * esz(dt),
+                       fut_latents_out + (size_t)b * Tf * d->Cv, (int64_t)Tf * d->Cv));
+  HIPCK(hipMemcpyAsync(actions_out, eps, (size_t)M * d->A * 4, hipMemcpyDeviceToDevice, s));
+  HIPCK(step_boundary(s, dt, ab.X, nullptr, nullptr, actions_out, 0.f, nullptr, action->w_in,
+                      ab.emb, M, D, d->A, false));
+
+  Layer cv{s, d, &vb}, ca{s, d, &ab};
+  const size_t ls = layer_stride(cache);
+  const size_t ep = (size_t)d->Hh * cache->cap * d->dh * esz(dt);  // one episode in a layer
+  RowMap zmap;
+  zmap.n = 1;
+  zmap.P = Tf;
+  zmap.src[0] = 0;
+  for (int k = 0; k < N; k++) {
+    // 1. the video pass at sigma_k of every episode (future K/V into the cache)
+    for (int b = 0; b < B; b++) {
+      float* z = fut_latents_out + (size_t)b * Tf * d->Cv;
+      const int Th = nh[b] * P;
+      HIPCK(embed(s, WAM_F32, dt, z, zmap, video->w_in, vb.emb + (size_t)k * D, vb.X, Tf, D,
+                  d->Cv));
+      for (int l = 0; l < d->L; l++) {
+        char* kl = (char*)cache->k + l * ls + b * ep;
+        char* vl = (char*)cache->v + l * ls + b * ep;
+        if ((st = video_layer(cv, video->layers[l], Tf, Th, tabs[b], kl, vl, cache->cap, false)))
+          return st;
+      }
+      if ((st = flush_pending(cv, video->g_out, Tf))) return st;
+      HIPCK(step_boundary(s, dt, vb.X, video->g_out, video->w_out, z, sv[k + 1] - sv[k], nullptr,
+                          nullptr, nullptr, Tf, D, d->Cv, true));
+    }
+    // 2. the action pass at t_k over [history ; future at sigma_k], 3. Euler
+    for (int l = 0; l < d->L; l++) {
+      const void* kc = (const char*)cache->k + l * ls;
+      const void* vc = (const char*)cache->v + l * ls;
+      if ((st = action_layer(ca, action->layers[l], B, kc, vc, cache->cap, lens))) return st;
+    }
+    const bool last = (k + 1 == N);
+    if ((st = flush_pending(ca, action->g_out, M))) return st;
+    HIPCK(step_boundary(s, dt, ab.X, action->g_out, action->w_out, actions_out, ta[k + 1] - ta[k],
+                        vhat_out ? vhat_out + (size_t)k * M * d->A : nullptr,
+                        last ? nullptr : action->w_in,
+                        last ? nullptr : ab.emb + (size_t)(k + 1) * D, M, D, d->A, true));
+  }
+  for (int b = 0; b < B; b++) cache->len[b] = lens.len[b];
+  return WAM_OK;
+}
+
 int wam_debug_visibility(const int32_t* frame_block, const uint8_t* valid, int Fh, int Ff, int P,
                          uint8_t* vis, void* stream) {
   if (!frame_block || !vis) return fail(WAM_E_ARG, "NULL pointer");

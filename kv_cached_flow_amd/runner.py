@@ -55,6 +55,14 @@ class DeviceChunk:
         self.z = torch.zeros((cfg.B, cfg.Ff, cfg.P, cfg.Cv), dtype=torch.float32, device=device)
         self.actions = torch.zeros((cfg.B, cfg.H, cfg.A), dtype=torch.float32, device=device)
         self.vhat = torch.zeros((cfg.N, cfg.B, cfg.H, cfg.A), dtype=torch.float32, device=device)
+        if cfg.joint:
+            # co-denoising: the prefill covers the history only; the future is
+            # denoised together with the actions
+            self.ws_prefill = wam.workspace(wam.prefill_workspace_bytes(self.dims, cfg.B, cfg.Fh, 0),
+                                            device)
+            self.ws_denoise = wam.workspace(
+                wam.codenoise_workspace_bytes(self.dims, cfg.B, cfg.Ff, self.cache), device)
+            return
         self.ws_prefill = wam.workspace(wam.prefill_workspace_bytes(self.dims, cfg.B, cfg.Fh, cfg.Ff), device)
         kv = self.fused if self.fused is not None else self.cache
         kv.len[:] = cap  # size the workspace for a full cache
@@ -66,6 +74,14 @@ class DeviceChunk:
 
     def prefill(self, stream=None):
         c = self.cfg
+        if c.joint:
+            if c.Fh == 0 or not self.hist_valid.any():
+                self.cache.len[:] = 0   # no observed history: the joint steps see the future alone
+                return
+            wam.prefill_video_cache(self.dims, self.video, self.hist, self.hist_valid, c.B, c.Fh, None,
+                                    0, c.frame_block[:c.Fh], 0, c.sigma_star, c.shift, self.cache,
+                                    None, self.ws_prefill, stream)
+            return
         wam.prefill_video_cache(self.dims, self.video, self.hist, self.hist_valid, c.B, c.Fh, self.fut,
                                 c.Ff, c.frame_block, c.V, c.sigma_star, c.shift, self.cache, self.z,
                                 self.ws_prefill, stream)
@@ -78,11 +94,18 @@ class DeviceChunk:
 
     def denoise(self, stream=None):
         c = self.cfg
+        if c.joint:
+            wam.codenoise_chunk(self.dims, self.video, self.action, self.hist_valid, c.B, c.Fh,
+                                self.fut, c.Ff, c.frame_block, self.eps_a, c.N, c.video_end,
+                                c.shift, self.cache, self.actions, self.z, self.vhat,
+                                self.ws_denoise, stream)
+            return
         wam.denoise_chunk(self.dims, self.action, self.read_kv, c.read_map, self.eps_a, c.B, c.N,
                           c.shift, self.actions, self.vhat, self.ws_denoise, stream)
 
     def run(self, stream=None):
-        """One whole chunk: prefill, fuse (SparseMoT), N action steps."""
+        """One whole chunk: prefill, fuse (SparseMoT), N action steps (with
+        co-denoising: the history prefill, then N joint video + action steps)."""
         self.prefill(stream)
         self.fuse(stream)
         self.denoise(stream)

@@ -75,6 +75,12 @@ _EXPORTS = {
     "wam_denoise_chunk": (C.c_int, [C.POINTER(WamDims), C.POINTER(WamExpertW), C.POINTER(WamKV),
                                     C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_double, C.c_void_p,
                                     C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wam_codenoise_workspace_bytes": (C.c_size_t, [C.POINTER(WamDims), C.c_int, C.c_int, C.POINTER(WamKV)]),
+    "wam_codenoise_chunk": (C.c_int, [C.POINTER(WamDims), C.POINTER(WamExpertW), C.POINTER(WamExpertW),
+                                      C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p,
+                                      C.c_void_p, C.c_int, C.c_double, C.c_double, C.POINTER(WamKV),
+                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                      C.c_void_p]),
     "wam_debug_visibility": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p,
                                        C.c_void_p]),
     "wam_attention_action": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p,
@@ -252,6 +258,25 @@ def denoise_chunk(d: WamDims, action: DeviceExpert, kv: Optional[DeviceKV], read
                                    rm.ctypes.data, _ptr(eps), B, N, shift, _ptr(actions_out),
                                    _ptr(vhat_out), _ptr(ws), ws.numel(), _stream(stream)),
            "wam_denoise_chunk")
+
+
+def codenoise_workspace_bytes(d: WamDims, B: int, Ff: int, cache: DeviceKV) -> int:
+    return lib().wam_codenoise_workspace_bytes(C.byref(d), B, Ff, C.byref(cache.c))
+
+
+def codenoise_chunk(d: WamDims, video: DeviceExpert, action: DeviceExpert, hist_valid, B: int,
+                    Fh: int, fut_noise, Ff: int, frame_block, eps, N: int, sigma_video_end: float,
+                    shift: float, cache: DeviceKV, actions_out, fut_latents_out, vhat_out=None,
+                    ws=None, stream=None):
+    hv = None if hist_valid is None else np.ascontiguousarray(hist_valid, dtype=np.uint8)
+    fb = np.ascontiguousarray(frame_block, dtype=np.int32)
+    if ws is None:
+        ws = workspace(codenoise_workspace_bytes(d, B, Ff, cache))
+    _check(lib().wam_codenoise_chunk(
+        C.byref(d), C.byref(video.c), C.byref(action.c), None if hv is None else hv.ctypes.data, B,
+        Fh, _ptr(fut_noise), Ff, fb.ctypes.data, _ptr(eps), N, sigma_video_end, shift,
+        C.byref(cache.c), _ptr(actions_out), _ptr(fut_latents_out), _ptr(vhat_out), _ptr(ws),
+        ws.numel(), _stream(stream)), "wam_codenoise_chunk")
 
 
 def debug_visibility(frame_block, valid, Fh: int, Ff: int, P: int, stream=None):

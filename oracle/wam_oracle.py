@@ -491,22 +491,34 @@ def codenoise(cfg, vw: dict, aw: dict, hist_b, valid_b, eps_v_b, eps_a_b, steps:
 
 
 def run_codenoise(cfg, inp: dict, dtype=None, steps: Optional[int] = None,
-                  sigma_video_end: float = 0.0):
-    """CoD for every episode (``codenoise``), ``steps`` = cfg.N by default.
-    Returns actions [B, H, A], z [B, Ff*P, Cv] (float64 numpy) and the action
-    v-hat per step [steps, B, H, A]."""
+                  sigma_video_end: Optional[float] = None, keep_cache: bool = False,
+                  cache_sampler: Optional[Callable] = None):
+    """CoD for every episode (``codenoise``); ``steps`` = cfg.N and
+    ``sigma_video_end`` = cfg.video_end by default.  Returns actions
+    [B, H, A], z [B, Ff*P, Cv] (float64 numpy) and the action v-hat per step
+    [steps, B, H, A]; with ``keep_cache`` also the cache per episode
+    (history ; future at the last video level).  ``cache_sampler(b, cache,
+    None)`` is called per episode before the cache is dropped."""
     dt = dtype or oracle_dtype(cfg)
     n = steps or cfg.N
+    end = cfg.video_end if sigma_video_end is None else sigma_video_end
     vw = to_torch_expert(inp["video"], dt)
     aw = to_torch_expert(inp["action"], dt)
-    acts, zs, vhs = [], [], []
+    acts, zs, vhs, caches = [], [], [], []
     for b in range(cfg.B):
-        a, z, traj, _ = codenoise(cfg, vw, aw, inp["hist"][b], inp["hist_valid"][b],
-                                  inp["eps_v"][b], inp["eps_a"][b], n, sigma_video_end)
+        a, z, traj, cache = codenoise(cfg, vw, aw, inp["hist"][b], inp["hist_valid"][b],
+                                      inp["eps_v"][b], inp["eps_a"][b], n, end)
+        if cache_sampler is not None:
+            cache_sampler(b, cache, None)
         acts.append(a.double().numpy())
         zs.append(z.double().numpy())
         vhs.append(np.stack([t[3].double().numpy() for t in traj]))
-    return {"actions": np.stack(acts), "z": np.stack(zs), "vhat": np.stack(vhs, axis=1)}
+        if keep_cache:
+            caches.append(cache)
+    out = {"actions": np.stack(acts), "z": np.stack(zs), "vhat": np.stack(vhs, axis=1)}
+    if keep_cache:
+        out["cache"] = caches
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -1,7 +1,7 @@
-"""Write the expected values of the full-size workloads C1-C4 by running the
+"""Write the expected values of the full-size workloads C1-C5 by running the
 CPU oracle (and nothing else) on the seeded inputs.
 
-    python tests/golden/make_golden.py C1 C2 C3 C4
+    python tests/golden/make_golden.py C1 C2 C3 C4 C5
 
 Each ``<name>.json`` holds the input fingerprint, the final action chunk of
 every episode, the v-hat of the first and last action steps, and sampled
@@ -63,13 +63,17 @@ def main(names):
                                   "v": V[rows, heads].double().numpy().tolist()}
                 samples["fused"].append(fe)
 
-        out = O.run_chunk(cfg, inp, cache_sampler=sampler)
+        if cfg.joint:
+            out = O.run_codenoise(cfg, inp, cache_sampler=sampler)
+        else:
+            out = O.run_chunk(cfg, inp, cache_sampler=sampler)
         zrows = np.sort(np.random.default_rng(777).choice(cfg.Ff * cfg.P, size=64, replace=False))
         rec = {
             "config": name,
             "seed": cfg.seed,
             "fingerprint": inputs.fingerprint(inp),
-            "source": "oracle/wam_oracle.py run_chunk (float32), tests/golden/make_golden.py",
+            "source": ("oracle/wam_oracle.py " + ("run_codenoise" if cfg.joint else "run_chunk")
+                       + " (float32), tests/golden/make_golden.py"),
             "actions": out["actions"].tolist(),
             "vhat_first": out["vhat"][0].tolist(),
             "vhat_last": out["vhat"][-1].tolist(),
@@ -79,7 +83,7 @@ def main(names):
             "cache": samples["cache"],
             "fused": samples["fused"],
             "z_rows": zrows.tolist(),
-            "z": out["z"][:, zrows].tolist() if cfg.V >= 1 else None,
+            "z": out["z"][:, zrows].tolist() if (cfg.V >= 1 or cfg.joint) else None,
             "oracle_seconds": time.time() - t0,
         }
         with open(os.path.join(HERE, f"{name}.json"), "w") as f:
@@ -88,4 +92,4 @@ def main(names):
 
 
 if __name__ == "__main__":
-    main(sys.argv[1:] or ["C1", "C2", "C3", "C4"])
+    main(sys.argv[1:] or ["C1", "C2", "C3", "C4", "C5"])

@@ -23,11 +23,11 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = wam.lib()
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
     assert sorted(wam.exported_names()) == names
-    assert wam.abi_version() == 1
+    assert wam.abi_version() == 2
 
 
 def test_status_strings():
@@ -176,6 +176,60 @@ def test_denoise_validation_errors():
     assert call_denoise(kv=kv3) == -2                          # len > cap
     assert call_denoise(kv=kv, ws_bytes=4096) == -5
     assert call_denoise(kv=kv, shift=0.0) == -1
+
+
+def call_codenoise(d=None, video=None, action=None, valid=None, B=1, Fh=3, fut=FAKE, Ff=2,
+                   blocks=(0, 1, 2, 3, 4), eps=FAKE, N=4, end=0.0, shift=1.0, kv=None, out=FAKE,
+                   z=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    L = wam.lib()
+    d = d or good_dims()
+    vx = video or FakeExpert(d.L)
+    ax = action or FakeExpert(d.L)
+    if kv is None:
+        kv, _keep = fake_kv(cap=512, lens=[300])
+    fb = np.asarray(blocks, dtype=np.int32)
+    va = None if valid is None else np.ascontiguousarray(valid, dtype=np.uint8)
+    st = L.wam_codenoise_chunk(C.byref(d), C.byref(vx.c), C.byref(ax.c),
+                               None if va is None else va.ctypes.data, B, Fh, fut, Ff, fb.ctypes.data,
+                               eps, N, end, shift, C.byref(kv), out, z, None, ws, ws_bytes, None)
+    return st, L.wam_last_error().decode()
+
+
+def test_codenoise_validation_errors():
+    st, msg = call_codenoise(Ff=0, blocks=(0, 1, 2))
+    assert st == -2 and "Ff >= 1" in msg
+    assert call_codenoise(N=0)[0] == -1
+    assert call_codenoise(N=wam.WAM_MAX_STEPS + 1)[0] == -1
+    assert call_codenoise(end=1.0)[0] == -1
+    assert call_codenoise(end=-0.25)[0] == -1
+    assert call_codenoise(shift=0.0)[0] == -1
+    assert call_codenoise(z=None)[0] == -1                     # the video latents are required
+    assert call_codenoise(eps=FAKE + 8)[0] == -4
+    assert call_codenoise(blocks=(0, 2, 1, 3, 4))[0] == -2      # non-monotone
+    assert call_codenoise(action=FakeExpert(1))[0] == -2        # layer count
+    assert call_codenoise(ws_bytes=4096)[0] == -5
+    kv, _k = fake_kv(cap=512, lens=[512])
+    st, msg = call_codenoise(kv=kv)                              # not a history-only cache
+    assert st == -2 and "valid history" in msg
+    kv, _k = fake_kv(cap=256, lens=[300])
+    st, msg = call_codenoise(kv=kv)                              # 5 frames x 100 rows > cap
+    assert st == -2 and "cap" in msg
+    kv, _k = fake_kv(n_layers=1, cap=512, lens=[300])
+    assert call_codenoise(kv=kv)[0] == -2                       # cache must hold L layers
+    # one padded history frame: the cache must then hold 2 frames of rows
+    kv, _k = fake_kv(cap=512, lens=[300])
+    st, msg = call_codenoise(kv=kv, valid=np.array([[0, 1, 1]]))
+    assert st == -2 and "valid history" in msg
+
+
+def test_codenoise_workspace_covers_both_experts():
+    d = good_dims()
+    kv, _k = fake_kv(cap=512, lens=[300])
+    L = wam.lib()
+    w = L.wam_codenoise_workspace_bytes(C.byref(d), 1, 2, C.byref(kv))
+    assert w >= L.wam_prefill_workspace_bytes(C.byref(d), 1, 0, 2)
+    assert w >= L.wam_denoise_workspace_bytes(C.byref(d), 1, C.byref(kv))
+    assert L.wam_codenoise_workspace_bytes(C.byref(d), 1, 0, C.byref(kv)) == 0
 
 
 def test_fuse_validation_errors():
