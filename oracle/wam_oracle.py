@@ -396,12 +396,14 @@ def read_layers(cfg, cache, fused):
 
 
 def run_chunk(cfg, inp: dict, dtype=None, drop_padded: bool = True,
-              cache_sampler: Optional[Callable] = None, keep_cache: bool = False):
+              cache_sampler: Optional[Callable] = None, keep_cache: bool = False,
+              kv_fp8: bool = False):
     """Whole chunk per episode: prefill -> (fuse) -> N action steps.
 
     Returns actions [B, H, A] (numpy float64), z [B, Ff*P, Cv], v-hat per
     step [N, B, H, A]; with ``keep_cache`` also the cache per episode (valid
-    rows, in frame order) and the fused pairs.  ``cache_sampler(b, cache,
+    rows, in frame order) and the fused pairs.  ``kv_fp8``: the action layers
+    read the E4M3 form of their K/V (``quantize_kv_fp8``).  ``cache_sampler(b, cache,
     fused)`` is called per episode before the cache is dropped.
     """
     dt = dtype or oracle_dtype(cfg)
@@ -412,7 +414,10 @@ def run_chunk(cfg, inp: dict, dtype=None, drop_padded: bool = True,
         cache, z, _ = video_prefill(cfg, vw, inp["hist"][b], inp["hist_valid"][b],
                                     inp["eps_v"][b], drop_padded)
         fused = fuse_interval(cache, cfg.fuse, inp["fuse_logits"]) if cfg.fuse else None
-        a, vh = denoise(cfg, aw, read_layers(cfg, cache, fused), inp["eps_a"][b])
+        kv_read = read_layers(cfg, cache, fused)
+        if kv_fp8:
+            kv_read = quantize_read(kv_read)
+        a, vh = denoise(cfg, aw, kv_read, inp["eps_a"][b])
         if cache_sampler is not None:
             cache_sampler(b, cache, fused)
         acts.append(a.double().numpy())
@@ -519,6 +524,108 @@ def run_codenoise(cfg, inp: dict, dtype=None, steps: Optional[int] = None,
     if keep_cache:
         out["cache"] = caches
     return out
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) key/value cache: an option that departs from the pages' bf16 cache
+# --------------------------------------------------------------------------
+#
+# Long-WAM keeps its KV storage in bf16 (Long-WAM Summary section 4.2), while
+# the LongLive-2.0 stack it builds on quantises its KV cache block by block
+# (the Long-WAM tutorial, section 三).  The option here stores the cache the
+# action expert reads as OCP E4M3 codes with one power-of-two scale per
+# (head, 64-key tile) for K and one for V.  A power of two makes code * scale
+# exact in bf16 and fp32, so the GPU's dequantised operands are exactly the
+# values below.
+
+E4M3_MAX = 448.0
+KV_TILE = 64
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP 8-bit E4M3 code: sign bit, 4 exponent bits (bias 7),
+    3 mantissa bits; exponent field 0 is subnormal, (m/8) 2^-6; S.1111.111 is
+    NaN and there is no infinity (OCP 8-bit floating-point specification)."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)])
+_E4M3_POS = _E4M3_TABLE[:0x7F]        # codes 0..126: the finite non-negative values, increasing
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.int64)]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code, ties to the even code (|x| <= 448, no NaN); the sign
+    bit follows the sign of x (negative values that round to 0 give 0x80)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.isnan(a).any() or (a > E4M3_MAX).any():
+        raise ValueError("E4M3 encoding needs finite |x| <= 448")
+    hi = np.minimum(np.searchsorted(_E4M3_POS, a, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def kv_tile_exponent(amax: float) -> int:
+    """Smallest integer e with amax <= 448 * 2^e (0 for an all-zero tile)."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    e = math.ceil(math.log2(amax / E4M3_MAX))
+    while amax > E4M3_MAX * 2.0 ** e:
+        e += 1
+    while amax <= E4M3_MAX * 2.0 ** (e - 1):
+        e -= 1
+    return e
+
+
+def quantize_kv_fp8(K, V):
+    """E4M3 cache of one layer (K, V [T, Hh, dh], the valid rows from row 0).
+
+    Per head and 64-row tile (the last one ragged) of K, and likewise of V:
+    e = kv_tile_exponent(max |x| over the tile), code = E4M3(x / 2^e) and the
+    value read back is value(code) 2^e.  Returns (K', V') dequantised in the
+    input dtype and, for the bit-exact tests, (codes_K, exps_K, codes_V,
+    exps_V) with exps [Hh, tiles].
+    """
+    res = []
+    for X in (K, V):
+        Xn = X.double().numpy()
+        T, Hh, dh = Xn.shape
+        nt = (T + KV_TILE - 1) // KV_TILE
+        exps = np.zeros((Hh, nt), dtype=np.int64)
+        codes = np.zeros(Xn.shape, dtype=np.uint8)
+        deq = np.zeros(Xn.shape)
+        for h in range(Hh):
+            for t in range(nt):
+                r0, r1 = t * KV_TILE, min(T, (t + 1) * KV_TILE)
+                blk = Xn[r0:r1, h, :]
+                e = kv_tile_exponent(np.max(np.abs(blk)))
+                c = e4m3_encode(blk / 2.0 ** e)
+                exps[h, t] = e
+                codes[r0:r1, h, :] = c
+                deq[r0:r1, h, :] = e4m3_decode(c) * 2.0 ** e
+        res.append((torch.from_numpy(deq).to(X.dtype), codes, exps))
+    (Kq, ck, ek), (Vq, cv, ev) = res
+    return Kq, Vq, (ck, ek, cv, ev)
+
+
+def quantize_read(kv_read):
+    """The FP8 option applied to what the action layers read (None stays)."""
+    return [None if kv is None else quantize_kv_fp8(kv[0], kv[1])[:2] for kv in kv_read]
 
 
 # --------------------------------------------------------------------------

@@ -488,3 +488,89 @@ def test_codenoise_steps_equal_joint_sequence(end):
     z_last, a_last, vv_last, va_last = traj[-1]
     assert torch.max(torch.abs(a_fin - (a_last + float(ta[3] - ta[2]) * va_last))) < 1e-12
     assert torch.max(torch.abs(z_fin - (z_last + float(sv[3] - sv[2]) * vv_last))) < 1e-12
+
+
+# ---------------------------------------------------------------- FP8 (E4M3) cache option
+def test_e4m3_codes_closed_form():
+    v = O.e4m3_value
+    assert v(0x00) == 0.0 and v(0x01) == 2.0 ** -9 and v(0x07) == 7 * 2.0 ** -9
+    assert v(0x08) == 2.0 ** -6 and v(0x38) == 1.0 and v(0x39) == 1.125
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0 and v(0xB8) == -1.0
+    assert math.isnan(v(0x7F)) and math.isnan(v(0xFF))
+    pos = O._E4M3_POS
+    assert len(pos) == 127 and np.all(np.diff(pos) > 0)
+    assert sum(not math.isnan(v(c)) for c in range(256)) == 254
+
+
+def test_e4m3_encode_round_trip_and_ties():
+    finite = [c for c in range(256) if not math.isnan(O.e4m3_value(c))]
+    vals = np.array([O.e4m3_value(c) if c != 0x80 else -0.0 for c in finite])
+    assert np.array_equal(O.e4m3_encode(vals), np.array(finite, dtype=np.uint8))
+    pos = O._E4M3_POS
+    for i in range(len(pos) - 1):
+        mid = 0.5 * (pos[i] + pos[i + 1])
+        want = i if i % 2 == 0 else i + 1          # ties go to the even code
+        assert O.e4m3_encode([mid])[0] == want
+        assert O.e4m3_encode([-mid])[0] == want | 0x80
+        assert O.e4m3_encode([np.nextafter(mid, 0)])[0] == i
+        assert O.e4m3_encode([np.nextafter(mid, 1e9)])[0] == i + 1
+    with pytest.raises(ValueError):
+        O.e4m3_encode([448.5])
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_e4m3_encode_is_nearest_by_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    x = np.concatenate([rng.uniform(-448, 448, 2000), rng.normal(0, 0.01, 2000)])
+    got = O.e4m3_decode(O.e4m3_encode(x))
+    table = O._E4M3_POS
+    best = np.min(np.abs(np.abs(x)[:, None] - table[None, :]), axis=1)
+    assert np.array_equal(np.abs(np.abs(got) - np.abs(x)), best)
+    assert np.all((got == 0) | (np.sign(got) == np.sign(x)))
+
+
+def test_kv_tile_exponent_boundaries():
+    for e in (-12, -3, 0, 4):
+        edge = 448.0 * 2.0 ** e
+        assert O.kv_tile_exponent(edge) == e
+        assert O.kv_tile_exponent(np.nextafter(edge, 1e30)) == e + 1
+        assert O.kv_tile_exponent(np.nextafter(edge, 0)) == e
+    assert O.kv_tile_exponent(0.0) == 0
+    rng = np.random.default_rng(5)
+    for a in rng.lognormal(0, 4, 200):
+        e = O.kv_tile_exponent(a)
+        assert 448.0 * 2.0 ** (e - 1) < a <= 448.0 * 2.0 ** e
+
+
+def test_quantize_kv_error_bound_and_ragged_tiles():
+    rng = np.random.default_rng(9)
+    T, Hh, dh = 150, 3, 64                     # two full tiles and a ragged one
+    K = torch.tensor(rng.normal(0, 1, (T, Hh, dh)), dtype=f64)
+    V = torch.tensor(rng.normal(0, 1, (T, Hh, dh)), dtype=f64)
+    V[128:, 1] *= 1e-3                          # a tile of its own scale
+    Kq, Vq, (ck, ek, cv, ev) = O.quantize_kv_fp8(K, V)
+    assert ek.shape == (Hh, 3) and ev.shape == (Hh, 3)
+    for X, Xq, ex in ((K, Kq, ek), (V, Vq, ev)):
+        for h in range(Hh):
+            for t in range(3):
+                blk, q = X[64 * t:64 * t + 64, h].numpy(), Xq[64 * t:64 * t + 64, h].numpy()
+                s = 2.0 ** ex[h, t]
+                assert np.max(np.abs(blk)) <= 448 * s and np.max(np.abs(blk)) > 224 * s
+                # half a step of 3 mantissa bits, or half the subnormal step
+                bound = np.maximum(np.abs(blk) * 2.0 ** -4, 2.0 ** -10 * s)
+                assert np.all(np.abs(q - blk) <= bound)
+    assert ev[1, 2] < ev[1, 1] - 5                # the small tile got its own scale
+    # values already on the grid come back exactly
+    Kg = torch.tensor(O.e4m3_decode(ck.astype(np.int64)) * 2.0 ** np.repeat(ek.T, 64, axis=0)[:T, :, None])
+    Kg2, _, _ = O.quantize_kv_fp8(Kg, V)
+    assert torch.equal(Kg2, Kg)
+
+
+def test_fp8_option_touches_only_what_the_action_layers_read():
+    cfg = _tiny()
+    inp = inputs.generate(cfg, threads=1)
+    a = O.run_chunk(cfg, inp)
+    b = O.run_chunk(cfg, inp, kv_fp8=True)
+    assert np.array_equal(a["z"], b["z"])
+    d = np.linalg.norm(b["actions"] - a["actions"]) / np.linalg.norm(a["actions"])
+    assert 0 < d < 0.1
