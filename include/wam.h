@@ -60,7 +60,10 @@ enum {
   WAM_E_HIP = -6         /* a HIP runtime call failed (see wam_last_error) */
 };
 
-enum { WAM_F32 = 0, WAM_BF16 = 1 };
+/* WAM_FP8 is a K/V cache type only (see wam_quantize_kv_fp8): OCP E4M3 codes
+ * with one power-of-two fp32 scale per (layer, episode, head, 64-key tile)
+ * for K and one for V.  Every other tensor of a WAM_BF16 model stays bf16. */
+enum { WAM_F32 = 0, WAM_BF16 = 1, WAM_FP8 = 2 };
 
 /* Shapes shared by both experts (layer count, heads and head dim must match
  * so that video layer i pairs with action layer i, "Fast-WAM 精读" section 四.4). */
@@ -103,12 +106,21 @@ typedef struct {
  *   k: [n_layers][B][Hh][cap][dh]   (token-major within a head)
  *   v: [n_layers][B][Hh][dh][cap]   (transposed: tokens contiguous)
  * Rows 0..len[b]-1 of episode b are valid: the valid history frames in frame
- * order, then the future frames.  cap must be a multiple of 64. */
+ * order, then the future frames.  cap must be a multiple of 64.
+ * dtype WAM_FP8 (one byte per element; written by wam_quantize_kv_fp8 only):
+ *   within each K row, bytes 16g..16g+7 hold dims 8g..8g+7 and bytes
+ *   16g+8..16g+15 dims 32+8g..32+8g+7 (g = 0..3); within each 64-key tile of
+ *   a V row, bytes 16g..16g+7 hold keys 8g..8g+7 of the tile and bytes
+ *   16g+8..16g+15 keys 32+8g..32+8g+7.  k_scale, v_scale: device
+ *   [n_layers][B][Hh][cap/64] fp32, each a power of two; a value is
+ *   E4M3(code) * scale of its tile.  NULL for the other dtypes. */
 typedef struct {
   void* k;
   void* v;
   int n_layers, B, Hh, dh, cap, dtype;
   int32_t* len;                /* host [B] */
+  float* k_scale;
+  float* v_scale;
 } wam_kv;
 
 /* ---------------------------------------------------------------------------
@@ -163,6 +175,23 @@ int wam_fuse_interval_kv(const wam_kv* src, int M, const int32_t* start,
                          wam_kv* dst, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * wam_quantize_kv_fp8 -- an option that departs from the pages' bf16 cache
+ * (Long-WAM keeps bf16 KV storage, Long-WAM Summary section 4.2; the
+ * LongLive-2.0 stack under it quantises its KV cache block by block, the
+ * Long-WAM tutorial section 三): the bf16 cache src becomes an E4M3 cache dst
+ * that the action layers read (wam_action_layer, wam_denoise_chunk) at half
+ * the HBM bytes.
+ * For every layer, episode b, head and 64-key tile of rows [0, len[b]) of K,
+ * and likewise of V: e = the smallest integer with max|x| <= 448 * 2^e over
+ * the tile's valid rows (0 for an all-zero tile), code = E4M3(x / 2^e)
+ * rounded to nearest even, scale = 2^e.  Codes of rows >= len[b] in the last
+ * tile are 0; later tiles are not written.  dst->len is set to src->len.
+ *   src: dtype WAM_BF16; dst: dtype WAM_FP8 with the same n_layers, B, Hh,
+ *   dh and cap, k_scale and v_scale set.
+ * ------------------------------------------------------------------------- */
+int wam_quantize_kv_fp8(const wam_kv* src, wam_kv* dst, void* stream);
+
+/* ---------------------------------------------------------------------------
  * wam_action_layer -- one action-expert layer on the chunk, in place
  * (forward_action_with_video_cache for one layer): the B*H action queries of
  * episode b attend over [kv layer kv_layer of episode b ; the chunk's own H
@@ -193,7 +222,9 @@ int wam_flow_euler_step(float* x, const float* v, int64_t n, float sigma,
  *   eps        device [B][H][A] fp32   initial noise
  *   actions_out device [B][H][A] fp32
  *   vhat_out   device [N][B][H][A] fp32 or NULL
- * kv may be NULL only if every read_map entry is negative.
+ * kv may be NULL only if every read_map entry is negative.  With a WAM_BF16
+ * model kv may be a WAM_FP8 cache (wam_quantize_kv_fp8); the same holds for
+ * wam_action_layer.
  * ------------------------------------------------------------------------- */
 size_t wam_denoise_workspace_bytes(const wam_dims* d, int B, const wam_kv* kv);
 int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_kv* kv,
@@ -277,6 +308,13 @@ int wam_attention_action(int dtype, int B, int Hh, int dh, int H, const void* q,
                          const void* ka, const void* va, int n_act,
                          const void* kc, const void* vc, int cap, const int32_t* len,
                          void* out, int splits_hint, void* ws, size_t ws_bytes, void* stream);
+/* The same over an E4M3 cache layer (layouts and scales [B][Hh][cap/64] as
+ * in wam_kv with dtype WAM_FP8); q, ka, va, out bf16.  ws as above (bf16). */
+int wam_attention_action_fp8(int B, int Hh, int dh, int H, const void* q, const void* ka,
+                             const void* va, int n_act, const void* kc8, const void* vc8,
+                             const float* k_scale, const float* v_scale, int cap,
+                             const int32_t* len, void* out, int splits_hint, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* Block-causal prefill attention for rows row0..row0+nq-1 of one episode's
  * cache layer: q [Hh][nq][dh], kc [Hh][cap][dh], vc [Hh][dh][cap];

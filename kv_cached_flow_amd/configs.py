@@ -56,6 +56,7 @@ class WamConfig:
     w_std: float = 0.02   # std of every other matrix
     joint: bool = False   # co-denoising: video and actions take the N steps together
     video_end: float = 0.0  # co-denoising: flow time the video reaches after N steps
+    kv_fp8: bool = False  # the action layers read an E4M3 copy of their K/V (not the pages' bf16)
 
     @property
     def F(self) -> int:

@@ -570,13 +570,31 @@ struct ActGeom {
   int kc[WAM_MAX_BATCH];     // cache keys per split of episode b (0: no cache)
 };
 
+// Eight E4M3 codes (two words) -> eight bf16 operand values times a
+// power-of-two scale (v_cvt_scalef32_pk_bf16_fp8, exact for such scales).
+__device__ inline bf16x8 e4m3x8_bf16(unsigned lo, unsigned hi, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false));
+  r[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true));
+  r[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false));
+  r[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // Split (b, h, s): cache keys [s*kc[b], min(len, (s+1)*kc[b])) for s < ncs(b),
 // the chunk's own keys for s == ncs(b).  Writes the split's (m, l, o) in the
 // log2 domain: m [32], l [32], o [32][64] (unnormalised).
+// F8: the cache is E4M3 (kc, vc bytes; ksc, vsc tile scales [B][Hh][cap/64]).
+// Its rows are stored in the order the lanes consume them, so one 16-byte
+// load gives a lane both 8-element fragments of a K row (dims 8g.. and
+// 32+8g..) or of a V^T row (keys 8g.. and 32+8g.. of the tile); converted
+// with the tile's scale they are the bf16 operands of the same MFMAs.  The
+// chunk's own keys stay bf16.
+template <bool F8>
 __global__ __launch_bounds__(256, 2) void attn_action_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ ka, const bf16_t* __restrict__ va,
-    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, ActGeom G,
-    float* __restrict__ part, float sl2) {
+    const void* __restrict__ kc, const void* __restrict__ vc, const float* __restrict__ ksc,
+    const float* __restrict__ vsc, ActGeom G, float* __restrict__ part, float sl2) {
   using namespace act;
   __shared__ float sm[4][H], sl[4][H];
   __shared__ float so[4][H][65];
@@ -589,10 +607,21 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
   if (s > ncs || (own && G.n_act == 0)) return;
   const bf16_t* kb;
   const bf16_t* vb;
+  const uint8_t* k8 = nullptr;
+  const uint8_t* v8 = nullptr;
+  const float* ksh = nullptr;
+  const float* vsh = nullptr;
   int key0, key1, vld;
   if (!own) {
-    kb = kc + ((long long)b * G.Hh + h) * G.cap * 64;
-    vb = vc + ((long long)b * G.Hh + h) * 64 * G.cap;
+    const long long hb = (long long)b * G.Hh + h;
+    kb = (const bf16_t*)kc + hb * G.cap * 64;
+    vb = (const bf16_t*)vc + hb * 64 * G.cap;
+    if constexpr (F8) {
+      k8 = (const uint8_t*)kc + hb * G.cap * 64;
+      v8 = (const uint8_t*)vc + hb * 64 * G.cap;
+      ksh = ksc + hb * (G.cap / 64);
+      vsh = vsc + hb * (G.cap / 64);
+    }
     key0 = s * chunk;
     key1 = min(len, key0 + chunk);
     vld = G.cap;
@@ -622,20 +651,46 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
     // read row key1 - 1 (their scores are masked to -inf), V^T chunks that
     // start past key1 read the row's first chunk and are zeroed below.
     bf16x8 ak[4][2], av[4][2];
+    if (F8 && !own) {
+      // E4M3 tile: kt is a multiple of 64 (splits are whole tiles), and the
+      // 16-byte V^T reads stay inside the tile, hence below cap; keys past
+      // key1 are zeroed below like the bf16 ones
+      const float sk = ksh[kt >> 6], sv = vsh[kt >> 6];
+      u32x4 rk[4], rv[4];
 #pragma unroll
-    for (int sub = 0; sub < 4; sub++) {
-      const int key = min(kt + perm_key(sub, c16), key1 - 1);
-#pragma unroll
-      for (int ss = 0; ss < 2; ss++)
-        ak[sub][ss] = *(const bf16x8*)(kb + (long long)key * 64 + 32 * ss + 8 * g);
-    }
-#pragma unroll
-    for (int d = 0; d < 4; d++)
-#pragma unroll
-      for (int wd = 0; wd < 2; wd++) {
-        const int k0 = kt + 32 * wd + 8 * g;
-        av[d][wd] = *(const bf16x8*)(vb + (long long)(16 * d + c16) * vld + (k0 < key1 ? k0 : key0));
+      for (int sub = 0; sub < 4; sub++) {
+        const int key = min(kt + perm_key(sub, c16), key1 - 1);
+        rk[sub] = *(const u32x4*)(k8 + (long long)key * 64 + 16 * g);
       }
+#pragma unroll
+      for (int d = 0; d < 4; d++)
+        rv[d] = *(const u32x4*)(v8 + (long long)(16 * d + c16) * G.cap + kt + 16 * g);
+#pragma unroll
+      for (int sub = 0; sub < 4; sub++) {
+        ak[sub][0] = e4m3x8_bf16(rk[sub][0], rk[sub][1], sk);
+        ak[sub][1] = e4m3x8_bf16(rk[sub][2], rk[sub][3], sk);
+      }
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        av[d][0] = e4m3x8_bf16(rv[d][0], rv[d][1], sv);
+        av[d][1] = e4m3x8_bf16(rv[d][2], rv[d][3], sv);
+      }
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < 4; sub++) {
+        const int key = min(kt + perm_key(sub, c16), key1 - 1);
+#pragma unroll
+        for (int ss = 0; ss < 2; ss++)
+          ak[sub][ss] = *(const bf16x8*)(kb + (long long)key * 64 + 32 * ss + 8 * g);
+      }
+#pragma unroll
+      for (int d = 0; d < 4; d++)
+#pragma unroll
+        for (int wd = 0; wd < 2; wd++) {
+          const int k0 = kt + 32 * wd + 8 * g;
+          av[d][wd] = *(const bf16x8*)(vb + (long long)(16 * d + c16) * vld + (k0 < key1 ? k0 : key0));
+        }
+    }
     const bool tail = kt + KT > key1;  // wave-uniform
     if (tail) {
       // P is zero past key1, but 0 * V must not meet a non-finite V
@@ -810,7 +865,10 @@ size_t attn_action_scratch_bytes(int B, int Hh, int H, int max_len, int splits_h
 hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* q,
                        const void* ka, const void* va, int n_act, const void* kc,
                        const void* vc, int cap, const ActLens& lens, void* out,
-                       int splits_hint, void* scratch, size_t scratch_bytes) {
+                       int splits_hint, void* scratch, size_t scratch_bytes, const float* ksc,
+                       const float* vsc) {
+  const bool f8 = ksc != nullptr;
+  if (f8 && (dt != WAM_BF16 || !vsc || !kc)) return hipErrorInvalidValue;
   if (H != act::H) return hipErrorInvalidValue;
   ActGeom G;
   G.B = B;
@@ -823,6 +881,7 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* 
   double keys = 0.0;
   for (int b = 0; b < B; b++) keys += (double)G.lens.len[b] + n_act;
   const int es = dt == WAM_BF16 ? 2 : 4;
+  const double ces = f8 ? 1.0 : es;  // bytes per cached element
   if (splits_hint >= act::MAX_SPLITS) return hipErrorInvalidValue;
   for (int b = 0; b < B; b++) G.kc[b] = kc ? action_chunk(G.lens.len[b], Hh, splits_hint) : 0;
   if (dt == WAM_F32) {
@@ -839,11 +898,21 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* 
     if (G.kc[b] > 0) G.S = std::max(G.S, (G.lens.len[b] + G.kc[b] - 1) / G.kc[b] + 1);
   if (scratch_bytes < (size_t)B * Hh * G.S * H * 66 * sizeof(float)) return hipErrorInvalidValue;
   {
-    TimingScope ts(s, KC_ATTN_ACTION, keys * Hh * 64 * 2 * es + 1.0 * B * H * Hh * 64 * es,
+    double cached = 0.0;
+    for (int b = 0; b < B; b++) cached += G.lens.len[b];
+    const double kv_bytes = cached * Hh * 64 * 2 * ces + (double)B * n_act * Hh * 64 * 2 * es +
+                            (f8 ? 2.0 * 4 * Hh * (cached / 64.0) : 0.0);
+    TimingScope ts(s, KC_ATTN_ACTION, kv_bytes + 1.0 * B * H * Hh * 64 * es,
                    4.0 * 64 * Hh * H * keys);
-    hipLaunchKernelGGL(attn_action_kernel, dim3(G.S, Hh, B), dim3(256), 0, s, (const bf16_t*)q,
-                       (const bf16_t*)ka, (const bf16_t*)va, (const bf16_t*)kc, (const bf16_t*)vc,
-                       G, (float*)scratch, 0.125f * LOG2E);
+    if (f8)
+      hipLaunchKernelGGL(attn_action_kernel<true>, dim3(G.S, Hh, B), dim3(256), 0, s,
+                         (const bf16_t*)q, (const bf16_t*)ka, (const bf16_t*)va, kc, vc, ksc, vsc,
+                         G, (float*)scratch, 0.125f * LOG2E);
+    else
+      hipLaunchKernelGGL(attn_action_kernel<false>, dim3(G.S, Hh, B), dim3(256), 0, s,
+                         (const bf16_t*)q, (const bf16_t*)ka, (const bf16_t*)va, kc, vc,
+                         (const float*)nullptr, (const float*)nullptr, G, (float*)scratch,
+                         0.125f * LOG2E);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -32,7 +32,7 @@ hipEvent_t get_event() {
 
 const char* kNames[KC_COUNT] = {"gemm_big",    "gemm_skinny", "gemm_simple", "attn_prefill",
                                 "attn_action", "attn_merge",  "rmsnorm",     "embed",
-                                "fuse_kv",     "misc"};
+                                "fuse_kv",     "quant_kv",    "misc"};
 }  // namespace
 
 bool timing_on() { return g_on; }

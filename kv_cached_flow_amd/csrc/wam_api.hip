@@ -35,7 +35,7 @@ int fail(int code, const char* fmt, ...) {
   } while (0)
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-inline size_t esz(int dt) { return dt == WAM_BF16 ? 2 : 4; }
+inline size_t esz(int dt) { return dt == WAM_FP8 ? 1 : (dt == WAM_BF16 ? 2 : 4); }
 
 // Carves a caller-provided workspace (base == nullptr: sizing pass).
 struct Arena {
@@ -81,10 +81,19 @@ int check_expert(const wam_dims* d, const wam_expert_w* e, const char* name) {
   return WAM_OK;
 }
 
-int check_kv(const wam_dims* d, const wam_kv* kv, int B, const char* name) {
+// fp8_ok: the caller only reads kv through the action attention, which takes
+// an E4M3 cache next to a bf16 model.
+int check_kv(const wam_dims* d, const wam_kv* kv, int B, const char* name, bool fp8_ok = false) {
   if (!kv->k || !kv->v || !kv->len) return fail(WAM_E_ARG, "%s has a NULL pointer", name);
   if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(WAM_E_ALIGN, "%s not 16-byte aligned", name);
-  if (kv->dtype != d->dtype) return fail(WAM_E_DTYPE, "%s dtype differs from dims", name);
+  if (kv->dtype == WAM_FP8) {
+    if (!fp8_ok || d->dtype != WAM_BF16)
+      return fail(WAM_E_DTYPE, "%s: an E4M3 cache is read only by the action layers of a bf16 model",
+                  name);
+    if (!kv->k_scale || !kv->v_scale) return fail(WAM_E_ARG, "%s has no tile scales", name);
+  } else if (kv->dtype != d->dtype) {
+    return fail(WAM_E_DTYPE, "%s dtype differs from dims", name);
+  }
   if (kv->B != B || kv->Hh != d->Hh || kv->dh != d->dh)
     return fail(WAM_E_SHAPE, "%s shape (B=%d Hh=%d dh=%d) does not match", name, kv->B, kv->Hh, kv->dh);
   if (kv->cap < 64 || kv->cap % 64) return fail(WAM_E_SHAPE, "%s cap must be a positive multiple of 64", name);
@@ -256,7 +265,8 @@ int norm_rows(const Layer& c, int odt, const float* g, void* y, int M) {
 // One action layer on the B*H rows in b.X; kc/vc: that layer's cache for all
 // episodes (or NULL).  May leave the W2 product pending (b.pend).
 int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, const void* vc,
-                 int cap, const ActLens& lens) {
+                 int cap, const ActLens& lens, const float* ksc = nullptr,
+                 const float* vsc = nullptr) {
   const wam_dims* d = c.d;
   const int dt = d->dtype, D = d->D, H = d->H, M = B * H;
   Bufs& b = *c.b;
@@ -276,7 +286,7 @@ int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, co
   if ((st = norm_rows(c, dt, w.g1, b.Y, M))) return st;
   HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, M, 3 * D, D, b.Y, D, w.wqkv, D, e));
   HIPCK(attn_action(c.s, dt, B, d->Hh, H, b.Q, b.Ka, b.Va, H, kc, vc, cap, lens, b.O, 0, b.attn,
-                    b.attn_bytes));
+                    b.attn_bytes, ksc, vsc));
   if ((st = action_resid(c, M, D, D, b.O, w.wo))) return st;
   if ((st = norm_rows(c, dt, w.g2, b.Y, M))) return st;
   EpiArgs gl{};
@@ -346,6 +356,12 @@ void plan_prefill(Arena& a, const wam_dims* d, int Fh, int Ff, Bufs& b, float** 
 
 size_t layer_stride(const wam_kv* kv) {
   return (size_t)kv->B * kv->Hh * kv->cap * kv->dh * esz(kv->dtype);
+}
+
+// Tile scales of layer l of an E4M3 cache (NULL for the other dtypes).
+const float* layer_scales(const wam_kv* kv, const float* base, int l) {
+  if (kv->dtype != WAM_FP8) return nullptr;
+  return base + (size_t)l * kv->B * kv->Hh * (kv->cap / 64);
 }
 
 }  // namespace
@@ -627,7 +643,7 @@ int wam_action_layer(const wam_dims* d, const wam_layer_w* w, float* x, const wa
   if (B < 1 || B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "bad B");
   ActLens lens{};
   if (kv) {
-    if ((st = check_kv(d, kv, B, "kv"))) return st;
+    if ((st = check_kv(d, kv, B, "kv", true))) return st;
     if (kv_layer < 0 || kv_layer >= kv->n_layers) return fail(WAM_E_ARG, "kv_layer out of range");
     if ((st = check_lens(kv, B, &lens))) return st;
   }
@@ -642,7 +658,10 @@ int wam_action_layer(const wam_dims* d, const wam_layer_w* w, float* x, const wa
   Layer c{s, d, &b};
   const void* kc = kv ? (const char*)kv->k + kv_layer * layer_stride(kv) : nullptr;
   const void* vc = kv ? (const char*)kv->v + kv_layer * layer_stride(kv) : nullptr;
-  if ((st = action_layer(c, *w, B, kc, vc, kv ? kv->cap : 0, lens))) return st;
+  if ((st = action_layer(c, *w, B, kc, vc, kv ? kv->cap : 0, lens,
+                         kv ? layer_scales(kv, kv->k_scale, kv_layer) : nullptr,
+                         kv ? layer_scales(kv, kv->v_scale, kv_layer) : nullptr)))
+    return st;
   if ((st = flush_pending(c, w->g1, B * d->H))) return st;
   HIPCK(hipMemcpyAsync(x, b.X, bytes, hipMemcpyDeviceToDevice, s));
   return WAM_OK;
@@ -675,7 +694,7 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
   for (int l = 0; l < d->L; l++) any |= read_map[l] >= 0;
   if (any) {
     if (!kv) return fail(WAM_E_ARG, "read_map reads a cache but kv is NULL");
-    if ((st = check_kv(d, kv, B, "kv"))) return st;
+    if ((st = check_kv(d, kv, B, "kv", true))) return st;
     if ((st = check_lens(kv, B, &lens))) return st;
     for (int l = 0; l < d->L; l++)
       if (read_map[l] >= kv->n_layers) return fail(WAM_E_ARG, "read_map[%d] out of range", l);
@@ -703,7 +722,10 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
       const int r = read_map[l];
       const void* kc = r >= 0 ? (const char*)kv->k + r * ls : nullptr;
       const void* vc = r >= 0 ? (const char*)kv->v + r * ls : nullptr;
-      if ((st = action_layer(c, action->layers[l], B, kc, vc, r >= 0 ? kv->cap : 0, lens))) return st;
+      if ((st = action_layer(c, action->layers[l], B, kc, vc, r >= 0 ? kv->cap : 0, lens,
+                             r >= 0 ? layer_scales(kv, kv->k_scale, r) : nullptr,
+                             r >= 0 ? layer_scales(kv, kv->v_scale, r) : nullptr)))
+        return st;
     }
     const bool last = (k + 1 == N);
     if ((st = flush_pending(c, action->g_out, M))) return st;
@@ -857,11 +879,13 @@ int wam_debug_visibility(const int32_t* frame_block, const uint8_t* valid, int F
   return WAM_OK;
 }
 
-int wam_attention_action(int dtype, int B, int Hh, int dh, int H, const void* q, const void* ka,
-                         const void* va, int n_act, const void* kc, const void* vc, int cap,
-                         const int32_t* len, void* out, int splits_hint, void* ws,
-                         size_t ws_bytes, void* stream) {
+static int attention_action_entry(int dtype, int B, int Hh, int dh, int H, const void* q,
+                                  const void* ka, const void* va, int n_act, const void* kc,
+                                  const void* vc, const float* ksc, const float* vsc, int cap,
+                                  const int32_t* len, void* out, int splits_hint, void* ws,
+                                  size_t ws_bytes, void* stream) {
   if (dtype != WAM_F32 && dtype != WAM_BF16) return fail(WAM_E_ARG, "bad dtype");
+  if (ksc && (!kc || !vsc)) return fail(WAM_E_ARG, "an E4M3 cache needs kc, vc and both scales");
   if (dh != 64 || H != 32) return fail(WAM_E_SHAPE, "dh must be 64 and H 32");
   if (B < 1 || B > WAM_MAX_BATCH || Hh < 1) return fail(WAM_E_SHAPE, "bad B or Hh");
   if (!q || !out) return fail(WAM_E_ARG, "NULL pointer");
@@ -888,7 +912,53 @@ int wam_attention_action(int dtype, int B, int Hh, int dh, int H, const void* q,
   size_t need = dtype == WAM_BF16 ? attn_action_scratch_bytes(B, Hh, H, max_len, splits_hint) : 0;
   if (need && (!ws || ws_bytes < need)) return fail(WAM_E_WORKSPACE, "workspace too small (%zu)", need);
   HIPCK(attn_action((hipStream_t)stream, dtype, B, Hh, H, q, ka, va, n_act, kc, vc, cap, lens, out,
-                    splits_hint, ws, ws_bytes));
+                    splits_hint, ws, ws_bytes, ksc, vsc));
+  return WAM_OK;
+}
+
+int wam_attention_action(int dtype, int B, int Hh, int dh, int H, const void* q, const void* ka,
+                         const void* va, int n_act, const void* kc, const void* vc, int cap,
+                         const int32_t* len, void* out, int splits_hint, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return attention_action_entry(dtype, B, Hh, dh, H, q, ka, va, n_act, kc, vc, nullptr, nullptr,
+                                cap, len, out, splits_hint, ws, ws_bytes, stream);
+}
+
+int wam_attention_action_fp8(int B, int Hh, int dh, int H, const void* q, const void* ka,
+                             const void* va, int n_act, const void* kc8, const void* vc8,
+                             const float* k_scale, const float* v_scale, int cap,
+                             const int32_t* len, void* out, int splits_hint, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (!kc8 || !vc8 || !k_scale || !v_scale) return fail(WAM_E_ARG, "NULL cache pointer");
+  return attention_action_entry(WAM_BF16, B, Hh, dh, H, q, ka, va, n_act, kc8, vc8, k_scale,
+                                v_scale, cap, len, out, splits_hint, ws, ws_bytes, stream);
+}
+
+int wam_quantize_kv_fp8(const wam_kv* src, wam_kv* dst, void* stream) {
+  if (!src || !dst) return fail(WAM_E_ARG, "NULL pointer");
+  if (!src->k || !src->v || !src->len || !dst->k || !dst->v || !dst->len || !dst->k_scale ||
+      !dst->v_scale)
+    return fail(WAM_E_ARG, "NULL cache pointer");
+  if (!aligned16(src->k) || !aligned16(src->v) || !aligned16(dst->k) || !aligned16(dst->v))
+    return fail(WAM_E_ALIGN, "cache not 16-byte aligned");
+  if (src->dtype != WAM_BF16 || dst->dtype != WAM_FP8)
+    return fail(WAM_E_DTYPE, "src must be WAM_BF16 and dst WAM_FP8");
+  if (src->n_layers != dst->n_layers || src->B != dst->B || src->Hh != dst->Hh ||
+      src->dh != dst->dh || src->cap != dst->cap)
+    return fail(WAM_E_SHAPE, "src and dst shapes differ");
+  if (src->dh != 64) return fail(WAM_E_SHAPE, "dh must be 64");
+  if (src->n_layers < 1 || src->Hh < 1) return fail(WAM_E_SHAPE, "bad n_layers or Hh");
+  if (src->B < 1 || src->B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "bad B");
+  if (src->cap < 64 || src->cap % 64) return fail(WAM_E_SHAPE, "cap must be a positive multiple of 64");
+  ActLens lens{};
+  for (int b = 0; b < src->B; b++) {
+    if (src->len[b] < 0 || src->len[b] > src->cap)
+      return fail(WAM_E_SHAPE, "len[%d] = %d outside [0, cap]", b, src->len[b]);
+    lens.len[b] = src->len[b];
+  }
+  HIPCK(quantize_kv_fp8((hipStream_t)stream, src->k, src->v, dst->k, dst->v, dst->k_scale,
+                        dst->v_scale, src->n_layers, src->B, src->Hh, src->cap, lens));
+  for (int b = 0; b < src->B; b++) dst->len[b] = src->len[b];
   return WAM_OK;
 }
 

@@ -215,10 +215,19 @@ struct ActLens {
   int len[WAM_MAX_BATCH];
 };
 size_t attn_action_scratch_bytes(int B, int Hh, int H, int max_len, int splits_hint);
+// ksc/vsc non-NULL: kc/vc is an E4M3 cache layer (bf16 model) with these
+// per-(episode, head, 64-key tile) scales, [B][Hh][cap/64].
 hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* q,
                        const void* ka, const void* va, int n_act, const void* kc,
                        const void* vc, int cap, const ActLens& lens, void* out,
-                       int splits_hint, void* scratch, size_t scratch_bytes);
+                       int splits_hint, void* scratch, size_t scratch_bytes,
+                       const float* ksc = nullptr, const float* vsc = nullptr);
+
+// bf16 cache (n_layers x B episodes) -> E4M3 cache with power-of-two tile
+// scales, rows [0, len[b]) of every episode.
+hipError_t quantize_kv_fp8(hipStream_t s, const void* k, const void* v, void* k8, void* v8,
+                           float* ks, float* vs, int n_layers, int B, int Hh, int cap,
+                           const ActLens& lens);
 
 hipError_t debug_visibility(hipStream_t s, const FrameTab& tab, const int* comp_of_frame,
                             int F, uint8_t* vis);
@@ -226,7 +235,7 @@ hipError_t debug_visibility(hipStream_t s, const FrameTab& tab, const int* comp_
 // ---------------------------------------------------------------- timing
 enum KClass {
   KC_GEMM_BIG, KC_GEMM_SKINNY, KC_GEMM_SIMPLE, KC_ATTN_PREFILL, KC_ATTN_ACTION,
-  KC_ATTN_MERGE, KC_RMSNORM, KC_EMBED, KC_FUSE, KC_MISC, KC_COUNT
+  KC_ATTN_MERGE, KC_RMSNORM, KC_EMBED, KC_FUSE, KC_QUANT, KC_MISC, KC_COUNT
 };
 // RAII event pair around the launches of one kernel class (no-op unless
 // wam_timing(1) was called); bytes/flops are the algorithmic work.

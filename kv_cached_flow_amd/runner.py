@@ -52,6 +52,11 @@ class DeviceChunk:
         self.cache = wam.DeviceKV(cfg.L, cfg.B, cfg.Hh, cfg.dh, cap, self.dt, device)
         self.fused = (wam.DeviceKV(len(cfg.fuse), cfg.B, cfg.Hh, cfg.dh, cap, self.dt, device)
                       if cfg.fuse else None)
+        self.kv8 = None
+        if cfg.kv_fp8:
+            if cfg.dtype != "bf16" or cfg.joint:
+                raise wam.WamError("the E4M3 cache option is for bf16 IDM / Faster-WAM chunks")
+            self.kv8 = wam.DeviceKV(cfg.n_kv, cfg.B, cfg.Hh, cfg.dh, cap, wam.WAM_FP8, device)
         self.z = torch.zeros((cfg.B, cfg.Ff, cfg.P, cfg.Cv), dtype=torch.float32, device=device)
         self.actions = torch.zeros((cfg.B, cfg.H, cfg.A), dtype=torch.float32, device=device)
         self.vhat = torch.zeros((cfg.N, cfg.B, cfg.H, cfg.A), dtype=torch.float32, device=device)
@@ -70,6 +75,8 @@ class DeviceChunk:
 
     @property
     def read_kv(self) -> wam.DeviceKV:
+        if self.kv8 is not None:
+            return self.kv8
         return self.fused if self.fused is not None else self.cache
 
     def prefill(self, stream=None):
@@ -87,10 +94,15 @@ class DeviceChunk:
                                 self.ws_prefill, stream)
 
     def fuse(self, stream=None):
+        """Cache transforms between the prefill and the action steps: the
+        interval fusion (SparseMoT) and, with the E4M3 option, quantising what
+        the action layers read."""
         c = self.cfg
         if c.fuse:
             wam.fuse_interval_kv(self.cache, [s for s, _ in c.fuse], [n for _, n in c.fuse],
                                  self.logits, self.fused, stream)
+        if self.kv8 is not None:
+            wam.quantize_kv_fp8(self.fused if self.fused is not None else self.cache, self.kv8, stream)
 
     def denoise(self, stream=None):
         c = self.cfg

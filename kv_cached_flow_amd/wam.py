@@ -14,7 +14,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwam.so")
 
-WAM_F32, WAM_BF16 = 0, 1
+WAM_F32, WAM_BF16, WAM_FP8 = 0, 1, 2
 WAM_MAX_FRAMES = 256   # limits of the C-ABI (include/wam.h)
 WAM_MAX_BATCH = 64
 WAM_MAX_FUSE = 32
@@ -44,7 +44,7 @@ class WamExpertW(C.Structure):
 class WamKV(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("n_layers", C.c_int), ("B", C.c_int),
                 ("Hh", C.c_int), ("dh", C.c_int), ("cap", C.c_int), ("dtype", C.c_int),
-                ("len", C.POINTER(C.c_int32))]
+                ("len", C.POINTER(C.c_int32)), ("k_scale", C.c_void_p), ("v_scale", C.c_void_p)]
 
 
 class WamKernelStat(C.Structure):
@@ -87,6 +87,11 @@ _EXPORTS = {
                                        C.c_void_p, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
                                        C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_void_p,
                                        C.c_size_t, C.c_void_p]),
+    "wam_attention_action_fp8": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
+                                           C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_int,
+                                           C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wam_quantize_kv_fp8": (C.c_int, [C.POINTER(WamKV), C.POINTER(WamKV), C.c_void_p]),
     "wam_attention_prefill": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
                                         C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_int, C.c_void_p, C.c_void_p]),
@@ -176,18 +181,25 @@ class DeviceExpert:
 
 
 class DeviceKV:
-    """Per-layer K/V cache of B episodes: k [n][B][Hh][cap][dh], v [n][B][Hh][dh][cap]."""
+    """Per-layer K/V cache of B episodes: k [n][B][Hh][cap][dh], v [n][B][Hh][dh][cap];
+    WAM_FP8: uint8 codes in the lane order of the header, plus tile scales
+    k_scale / v_scale [n][B][Hh][cap/64] fp32."""
 
     def __init__(self, n_layers: int, B: int, Hh: int, dh: int, cap: int, dtype: int, device="cuda"):
         import torch
         if cap % 64:
             raise WamError("cap must be a multiple of 64")
-        tdt = torch.bfloat16 if dtype == WAM_BF16 else torch.float32
+        tdt = {WAM_BF16: torch.bfloat16, WAM_F32: torch.float32, WAM_FP8: torch.uint8}[dtype]
         self.k = torch.empty((n_layers, B, Hh, cap, dh), dtype=tdt, device=device)
         self.v = torch.empty((n_layers, B, Hh, dh, cap), dtype=tdt, device=device)
+        self.k_scale = self.v_scale = None
+        if dtype == WAM_FP8:
+            self.k_scale = torch.empty((n_layers, B, Hh, cap // 64), dtype=torch.float32, device=device)
+            self.v_scale = torch.empty((n_layers, B, Hh, cap // 64), dtype=torch.float32, device=device)
         self.len = np.zeros(B, dtype=np.int32)
         self.c = WamKV(self.k.data_ptr(), self.v.data_ptr(), n_layers, B, Hh, dh, cap, dtype,
-                       self.len.ctypes.data_as(C.POINTER(C.c_int32)))
+                       self.len.ctypes.data_as(C.POINTER(C.c_int32)), _ptr(self.k_scale),
+                       _ptr(self.v_scale))
 
     @property
     def cap(self):
@@ -300,6 +312,23 @@ def attention_action(dtype: int, q, ka, va, n_act: int, kc, vc, cap: int, lens, 
                                       _ptr(kc), _ptr(vc), cap, None if ln is None else ln.ctypes.data,
                                       _ptr(out), splits_hint, _ptr(ws), ws.numel(), _stream(stream)),
            "wam_attention_action")
+
+
+def attention_action_fp8(q, ka, va, n_act: int, kc8, vc8, k_scale, v_scale, cap: int, lens, out,
+                         splits_hint: int = 0, ws=None, stream=None):
+    B, Hh, H, dh = q.shape
+    ln = np.ascontiguousarray(lens, dtype=np.int32)
+    if ws is None:
+        ws = workspace(64 << 20)
+    _check(lib().wam_attention_action_fp8(B, Hh, dh, H, _ptr(q), _ptr(ka), _ptr(va), n_act, _ptr(kc8),
+                                          _ptr(vc8), _ptr(k_scale), _ptr(v_scale), cap,
+                                          ln.ctypes.data, _ptr(out), splits_hint, _ptr(ws),
+                                          ws.numel(), _stream(stream)), "wam_attention_action_fp8")
+
+
+def quantize_kv_fp8(src: "DeviceKV", dst: "DeviceKV", stream=None):
+    _check(lib().wam_quantize_kv_fp8(C.byref(src.c), C.byref(dst.c), _stream(stream)),
+           "wam_quantize_kv_fp8")
 
 
 def attention_prefill(dtype: int, q, row0: int, P: int, kend, kc, vc, cap: int, out, stream=None):

@@ -42,7 +42,10 @@ def sample_points(cfg, seed=12345):
 def main(names):
     torch.set_num_threads(int(os.environ.get("ORACLE_THREADS", "8")))
     for name in names:
-        cfg = configs.get(name)
+        # "<config>+fp8": the same workload with the E4M3 cache option
+        base, _, opt = name.partition("+")
+        cfg = configs.get(base, kv_fp8=True) if opt == "fp8" else configs.get(base)
+        fname = f"{base}_fp8" if opt == "fp8" else base
         t0 = time.time()
         inp = inputs.generate(cfg)
         rows, heads, layers = sample_points(cfg)
@@ -66,10 +69,11 @@ def main(names):
         if cfg.joint:
             out = O.run_codenoise(cfg, inp, cache_sampler=sampler)
         else:
-            out = O.run_chunk(cfg, inp, cache_sampler=sampler)
+            out = O.run_chunk(cfg, inp, cache_sampler=sampler, kv_fp8=cfg.kv_fp8)
         zrows = np.sort(np.random.default_rng(777).choice(cfg.Ff * cfg.P, size=64, replace=False))
         rec = {
             "config": name,
+            "kv_fp8": cfg.kv_fp8,
             "seed": cfg.seed,
             "fingerprint": inputs.fingerprint(inp),
             "source": ("oracle/wam_oracle.py " + ("run_codenoise" if cfg.joint else "run_chunk")
@@ -86,7 +90,7 @@ def main(names):
             "z": out["z"][:, zrows].tolist() if (cfg.V >= 1 or cfg.joint) else None,
             "oracle_seconds": time.time() - t0,
         }
-        with open(os.path.join(HERE, f"{name}.json"), "w") as f:
+        with open(os.path.join(HERE, f"{fname}.json"), "w") as f:
             json.dump(rec, f)
         print(f"{name}: {time.time() - t0:.1f}s", flush=True)
 

@@ -23,7 +23,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = wam.lib()
     names = header_functions()
-    assert len(names) == 20
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
     assert sorted(wam.exported_names()) == names
@@ -230,6 +230,40 @@ def test_codenoise_workspace_covers_both_experts():
     assert w >= L.wam_prefill_workspace_bytes(C.byref(d), 1, 0, 2)
     assert w >= L.wam_denoise_workspace_bytes(C.byref(d), 1, C.byref(kv))
     assert L.wam_codenoise_workspace_bytes(C.byref(d), 1, 0, C.byref(kv)) == 0
+
+
+def test_fp8_cache_validation_errors():
+    L = wam.lib()
+    src, _a = fake_kv(n_layers=2, cap=512, lens=[300])
+    dst, _b = fake_kv(n_layers=2, cap=512, lens=[0], dtype=wam.WAM_FP8)
+    dst.k_scale = dst.v_scale = FAKE
+
+    def q(a, b):
+        return L.wam_quantize_kv_fp8(C.byref(a), C.byref(b), None), L.wam_last_error().decode()
+
+    src32, _c = fake_kv(n_layers=2, cap=512, lens=[300], dtype=wam.WAM_F32)
+    assert q(src32, dst)[0] == -3                      # source must be bf16
+    dstb, _d = fake_kv(n_layers=2, cap=512, lens=[0])
+    dstb.k_scale = dstb.v_scale = FAKE
+    assert q(src, dstb)[0] == -3                       # destination must be E4M3
+    dst3, _e = fake_kv(n_layers=3, cap=512, lens=[0], dtype=wam.WAM_FP8)
+    dst3.k_scale = dst3.v_scale = FAKE
+    assert q(src, dst3)[0] == -2                       # layer counts differ
+    dstn, _f = fake_kv(n_layers=2, cap=512, lens=[0], dtype=wam.WAM_FP8)
+    assert q(src, dstn)[0] == -1                       # no tile scales
+    big, _g = fake_kv(n_layers=2, cap=512, lens=[600])
+    assert q(big, dst)[0] == -2                        # len > cap
+    # an E4M3 cache is read by the action layers of a bf16 model only
+    kv8, _h = fake_kv(dtype=wam.WAM_FP8)
+    kv8.k_scale = kv8.v_scale = FAKE
+    assert call_denoise(kv=kv8, ws_bytes=4096) == -5   # accepted up to the workspace check
+    assert call_denoise(d=good_dims(dtype=wam.WAM_F32), kv=kv8) == -3
+    kv8n, _i = fake_kv(dtype=wam.WAM_FP8)
+    assert call_denoise(kv=kv8n) == -1                 # no scales
+    assert call_prefill(kv=kv8)[0] == -3               # the prefill writes bf16 only
+    kv8c, _j = fake_kv(cap=512, lens=[300], dtype=wam.WAM_FP8)
+    kv8c.k_scale = kv8c.v_scale = FAKE
+    assert call_codenoise(kv=kv8c)[0] == -3
 
 
 def test_fuse_validation_errors():
