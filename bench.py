@@ -25,7 +25,7 @@ PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # fp32 vector
 
 MFMA_CLASSES = {"gemm_big", "attn_prefill"}
-HBM_CLASSES = {"gemm_skinny", "attn_action", "attn_merge", "fuse_kv", "rmsnorm", "embed"}
+HBM_CLASSES = {"gemm_skinny", "attn_action", "attn_merge", "fuse_kv", "quant_kv", "rmsnorm", "embed"}
 
 WORKLOAD_TEXT = {
     "C0": "tiny fp32 IDM: 1 layer, 2x64 heads, 1 history + 1 future frame x 128 tokens, V=4, N=4",
@@ -118,7 +118,7 @@ def yardsticks() -> dict:
     return out
 
 
-def cpu_baseline(cfg_name: str, layers: int) -> dict:
+def cpu_baseline(cfg_name: str, layers: int, kv_fp8: bool = False) -> dict:
     import numpy as np  # noqa: F401
     import torch
 
@@ -131,13 +131,13 @@ def cpu_baseline(cfg_name: str, layers: int) -> dict:
         # one interaction layer (the last) reading the fusion of the sampled layers
         kw["fuse"] = ((0, layers),)
         kw["read_map"] = (-1,) * (layers - 1) + (0,)
-    cfg = configs.get(cfg_name, **kw)
+    cfg = configs.get(cfg_name, kv_fp8=kv_fp8, **kw)
     inp = inputs.generate(cfg)
     t0 = time.perf_counter()
     if cfg.joint:
         O.run_codenoise(cfg, inp)
     else:
-        O.run_chunk(cfg, inp)
+        O.run_chunk(cfg, inp, kv_fp8=cfg.kv_fp8)
     dt = time.perf_counter() - t0
     scale = full.L / layers
     return {"value": round(dt * scale * 1e3, 1), "unit": "ms/chunk", "cores": torch.get_num_threads(),
@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=10,
                     help="layers per expert in the CPU oracle sample (about 1.1 s each for C1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="the action layers read an E4M3 copy of the cache (an option that departs "
+                         "from the pages' bf16 cache; quantised once per chunk)")
     ap.add_argument("--minimal", action="store_true",
                     help="only warmup + timed chunks (for counter collection)")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -183,7 +186,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n * 4}))
         return
-    cfg = configs.get(args.config)
+    cfg = configs.get(args.config, kv_fp8=True) if args.kv_fp8 else configs.get(args.config)
     inp = inputs.generate(cfg)
     dc = DeviceChunk(cfg, inp)
     print(f"[bench] {cfg.name}: inputs resident, warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -254,7 +257,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) latents/noise, N(0,0.02^2) random-init weights)",
-        "config": {"workload": f"{cfg.name}: {WORKLOAD_TEXT.get(cfg.name, '')}", "B": cfg.B,
+        "config": {"workload": f"{cfg.name}: {WORKLOAD_TEXT.get(cfg.name, '')}"
+                               + (", E4M3 K/V read by the action layers" if cfg.kv_fp8 else ""),
+                   "kv_cache": "e4m3" if cfg.kv_fp8 else ("bf16" if cfg.dtype == "bf16" else "f32"),
+                   "B": cfg.B,
                    "L": cfg.L, "D": cfg.D, "heads": f"{cfg.Hh}x{cfg.dh}", "kv_tokens": cfg.tokens_valid,
                    "action_steps": cfg.N, "video_steps": cfg.N if cfg.joint else cfg.V,
                    "joint": cfg.joint},
@@ -269,7 +275,7 @@ def main():
     rec["yardsticks"] = yardsticks()
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(cfg.name, min(args.cpu_layers, cfg.L))
+        rec["cpu_baseline"] = cpu_baseline(cfg.name, min(args.cpu_layers, cfg.L), cfg.kv_fp8)
     print(json.dumps(rec), flush=True)
 
 
