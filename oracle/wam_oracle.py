@@ -294,6 +294,42 @@ def history_cache(cfg, vw: dict, hist_b, valid_b, drop_padded: bool = True):
     return cache_h, fall, valid, mask_f
 
 
+def extend_history(cfg, vw: dict, cache_old, n_old: int, hist_b, valid_b):
+    """Append history frames n_old..Fh-1 of one episode to the cache of its
+    first n_old frames (their valid rows, in order): the new frames' tokens at
+    sigma = 0 run through the L layers with keys [cached rows ; new rows]
+    under the block rule, and their K, V are appended.
+
+    Streaming observation encoding: frames are encoded as they arrive, not
+    when the whole window is complete (the Long-WAM tutorial, section 三;
+    Long-WAM Summary section 4.1).  Old rows are not recomputed: under the
+    block rule a frame reads no later block, so appending is exact when the
+    new frames start a new temporal block (frames of one block read each
+    other) and no frame leaves the window; eviction, or a change of the
+    temporal positions, invalidates the cache (Long-WAM Summary appendix
+    B.2) and needs a new prefill.
+    """
+    dt = vw["w_in"].dtype
+    P, Fh, Ff, D, Hh, L = cfg.P, cfg.Fh, cfg.Ff, cfg.D, cfg.Hh, len(vw["layers"])
+    old = [f for f in range(n_old) if valid_b[f]]
+    new = [f for f in range(n_old, Fh) if valid_b[f]]
+    if not new:
+        return cache_old
+    block = torch.tensor(cfg.frame_block, dtype=torch.int64)
+    valid = torch.tensor(list(valid_b) + [1] * Ff, dtype=torch.int64)
+    fo = torch.tensor(old, dtype=torch.int64).repeat_interleave(P)
+    fn = torch.tensor(new, dtype=torch.int64).repeat_interleave(P)
+    fall = torch.cat([fo, fn])
+    mask = lambda q0, q1: video_visible(fn[q0:q1], fall, block, valid)
+    tok = torch.from_numpy(np.ascontiguousarray(hist_b[new])).to(dt).reshape(-1, cfg.Cv)
+    X = embed(tok, vw["w_in"], 0.0, D)
+    cache = []
+    for l, lw in enumerate(vw["layers"]):
+        X, K, V = layer(X, lw, Hh, cache_old[l], mask, kv_only=(l == L - 1))
+        cache.append((torch.cat([cache_old[l][0], K]), torch.cat([cache_old[l][1], V])))
+    return cache
+
+
 def video_prefill(cfg, vw: dict, hist_b, valid_b, eps_v_b, drop_padded: bool = True):
     """Video expert for one episode: history prefill, imagine, cache pass.
 

@@ -574,3 +574,40 @@ def test_fp8_option_touches_only_what_the_action_layers_read():
     assert np.array_equal(a["z"], b["z"])
     d = np.linalg.norm(b["actions"] - a["actions"]) / np.linalg.norm(a["actions"])
     assert 0 < d < 0.1
+
+
+# ---------------------------------------------------------------- streaming history
+def _extended_and_full(blocks, pad, n_old):
+    cfg = _tiny(Fh=5, Ff=2, frame_block=blocks, pad_frames=pad)
+    inp = inputs.generate(cfg, threads=1)
+    vw = O.to_torch_expert(inp["video"], f64)
+    hist, valid = inp["hist"][0], inp["hist_valid"][0]
+    full, _, _, _ = O.history_cache(cfg, vw, hist, valid)
+    # the first n_old frames alone (later frames marked invalid cannot be seen)
+    valid_old = np.array([v if f < n_old else 0 for f, v in enumerate(valid)])
+    if valid_old.any():
+        part, _, _, _ = O.history_cache(cfg, vw, hist, valid_old)
+    else:
+        part = [(torch.zeros((0, cfg.Hh, cfg.dh), dtype=f64),) * 2 for _ in range(cfg.L)]
+    return full, O.extend_history(cfg, vw, part, n_old, hist, valid)
+
+
+@pytest.mark.parametrize("blocks,pad,n_old", [
+    ((0, 1, 2, 3, 4, 5, 6), 1, 3),        # one frame per block, a padded first frame
+    ((0, 0, 1, 1, 2, 3, 4), 0, 2),        # blocks of two frames, the split at a block boundary
+    ((0, 1, 2, 3, 4, 5, 6), 2, 1),        # every old frame padded
+])
+def test_extending_the_history_at_a_block_boundary_equals_one_prefill(blocks, pad, n_old):
+    # block causality: appending whole blocks never changes the rows already cached
+    full, ext = _extended_and_full(blocks, pad, n_old)
+    for (Kf, Vf), (Ke, Ve) in zip(full, ext):
+        assert Kf.shape == Ke.shape
+        assert torch.max(torch.abs(Kf - Ke)) < 1e-12
+        assert torch.max(torch.abs(Vf - Ve)) < 1e-12
+
+
+def test_extending_inside_a_block_is_not_exact():
+    # frames of one block read each other: appending half a block would leave
+    # the cached half stale, which is why the C-ABI rejects such a split
+    full, ext = _extended_and_full((0, 0, 1, 1, 2, 3, 4), 0, 3)
+    assert max(float(torch.max(torch.abs(Kf - Ke))) for (Kf, _), (Ke, _) in zip(full, ext)) > 1e-6
