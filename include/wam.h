@@ -161,6 +161,61 @@ int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video,
                             void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Streaming the history (the observation encoding runs as frames arrive, not
+ * when the window is complete: the Long-WAM tutorial section 三, Long-WAM
+ * Summary section 4.1).  A decision then costs the new frames and the future
+ * instead of the whole window:
+ *   1. after a chunk, set cache->len[b] back to the valid history rows (the
+ *      future rows are recomputed at every decision);
+ *   2. wam_extend_history_cache appends the frames that arrived;
+ *   3. wam_prefill_future adds the future rows; then fuse / denoise as usual.
+ * The result equals wam_prefill_video_cache over the whole window (the
+ * block rule: no frame reads a later block).  Appending is exact only while
+ * frames are appended in whole temporal blocks and no frame leaves the
+ * window: eviction or a change of the temporal positions invalidates the
+ * cached rows (Long-WAM Summary appendix B.2) and needs a new prefill.
+ *
+ * wam_extend_history_cache -- history frames Fh_old .. Fh_old+Fn-1 (at
+ * sigma = 0) through the L layers with keys [cached rows ; new rows] under
+ * the block rule; their valid rows are appended to the cache.
+ *   hist_new    device [B][Fn][P][Cv] dtype
+ *   hist_valid  host [B][Fh_old + Fn] uint8 or NULL (validity of every frame)
+ *   frame_block host [Fh_old + Fn], non-decreasing
+ *   cache       in: len[b] = valid rows of frames 0..Fh_old-1; out: + new rows
+ *   ws          wam_prefill_workspace_bytes(d, B, Fn, 0)
+ * Errors: WAM_E_SHAPE if len does not match, if a new valid frame shares a
+ * temporal block with a cached frame, or if cap is too small.
+ * ------------------------------------------------------------------------- */
+int wam_extend_history_cache(const wam_dims* d, const wam_expert_w* video,
+                             const void* hist_new, const uint8_t* hist_valid, int B,
+                             int Fh_old, int Fn, const int32_t* frame_block, wam_kv* cache,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* wam_prefill_future -- the future part of wam_prefill_video_cache over a
+ * cache that holds the valid history rows (len[b] checked): video_steps
+ * imagine steps to sigma_star and one caching pass, or (video_steps = 0) one
+ * pass of the noise at sigma = 1.  Arguments as wam_prefill_video_cache;
+ * Ff >= 1; ws: wam_prefill_workspace_bytes(d, B, 0, Ff). */
+int wam_prefill_future(const wam_dims* d, const wam_expert_w* video,
+                       const uint8_t* hist_valid, int B, int Fh, const void* fut_noise,
+                       int Ff, const int32_t* frame_block, int video_steps,
+                       double sigma_star, double shift, wam_kv* cache,
+                       float* fut_latents_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Asynchronous execution (Long-WAM Summary section 4.1): of each H-step
+ * chunk the first R steps may execute and inference triggers every S control
+ * steps, with R/2 <= S < R <= H, leaving an overlap O = R - S.
+ * wam_async_check returns WAM_OK or WAM_E_ARG for (H, R, S).
+ * wam_async_handoff: a chunk triggered `elapsed` control steps ago is handed
+ * over by discarding its first `elapsed` actions and executing the aligned
+ * suffix; *first = elapsed, *count = R - elapsed actions of it may run.
+ * Returns WAM_E_ARG if (H, R, S) is invalid or elapsed < 0, and WAM_E_SHAPE
+ * if elapsed > O: the chunk missed its deadline (T_ready <= O control
+ * steps) and the robot has waited. */
+int wam_async_check(int H, int R, int S);
+int wam_async_handoff(int H, int R, int S, int elapsed, int* first, int* count);
+
+/* ---------------------------------------------------------------------------
  * wam_fuse_interval_kv -- Interval KV-Fusion ("世界模型之Faster-WAM详解",
  * section 3.3): for m < M,
  *   (Kbar_m, Vbar_m) = sum_{j < count[m]} w_{m,j} (K_{start[m]+j}, V_{start[m]+j}),

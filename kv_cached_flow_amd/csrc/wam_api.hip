@@ -415,73 +415,162 @@ size_t wam_prefill_workspace_bytes(const wam_dims* d, int B, int Fh, int Ff) {
   return a.off + 256;
 }
 
-int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video, const void* hist,
-                            const uint8_t* hist_valid, int B, int Fh, const void* fut_noise,
-                            int Ff, const int32_t* frame_block, int video_steps,
-                            double sigma_star, double shift, wam_kv* cache,
-                            float* fut_latents_out, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// Frame tables of every episode of a call, validated before anything is
+// enqueued: the compacted table (valid history in order, then the future),
+// the gather map of the valid history frames (rows of the history input,
+// b * Fh + frame) and the number of valid history frames.
+struct Tables {
+  std::vector<FrameTab> tab;
+  std::vector<RowMap> hmap;
+  std::vector<int> nh;
+};
+
+int build_tables(const int32_t* frame_block, const uint8_t* hist_valid, int B, int Fh, int Ff,
+                 int P, int cap, Tables& t) {
+  t.tab.assign(B, FrameTab{});
+  t.hmap.assign(B, RowMap{});
+  t.nh.assign(B, 0);
+  for (int b = 0; b < B; b++) {
+    int src[WAM_MAX_FRAMES], kend[WAM_MAX_FRAMES];
+    const uint8_t* v = hist_valid ? hist_valid + (size_t)b * Fh : nullptr;
+    const int n = frame_table(frame_block, v, Fh, Ff, P, src, kend);
+    if (n == 0) return fail(WAM_E_SHAPE, "episode %d has no valid frame", b);
+    if ((long long)n * P > cap)
+      return fail(WAM_E_SHAPE, "episode %d needs %d cache rows, cap is %d", b, n * P, cap);
+    t.tab[b].n = n;
+    t.tab[b].P = P;
+    for (int i = 0; i < n; i++) t.tab[b].kend[i] = kend[i];
+    t.nh[b] = n - Ff;
+    t.hmap[b].n = t.nh[b];
+    t.hmap[b].P = P;
+    for (int i = 0; i < t.nh[b]; i++) t.hmap[b].src[i] = b * Fh + src[i];
+  }
+  return WAM_OK;
+}
+
+// History rows [row0, row0 + n) of one episode at sigma = 0 (emb0), gathered
+// from `hist` by `map`, through the L layers; their K/V go to the cache rows.
+// The last layer computes K/V only.
+int history_rows(const Layer& c, const wam_expert_w* video, const void* hist, const RowMap& map,
+                 const float* emb0, const FrameTab& tab, int row0, int n, char* k, char* v,
+                 size_t ls, int cap) {
+  const wam_dims* d = c.d;
+  Bufs& b = *c.b;
+  int st;
+  HIPCK(embed(c.s, d->dtype, d->dtype, hist, map, video->w_in, emb0, b.X, n, d->D, d->Cv));
+  for (int l = 0; l < d->L; l++)
+    if ((st = video_layer(c, video->layers[l], n, row0, tab, k + l * ls, v + l * ls, cap,
+                          l == d->L - 1)))
+      return st;
+  return WAM_OK;
+}
+
+// The future rows [Th, Th + Tf) of one episode over its cached history:
+// video_steps Euler steps of z over sig (embeddings emb_steps[k]) attending
+// to [history ; future], then one caching pass at emb_last; z (fp32) starts
+// as fut_noise_b (dtype).  video_steps == 0: the caching pass of the noise.
+int future_rows(const Layer& c, const wam_expert_w* video, const void* fut_noise_b, float* z,
+                const std::vector<float>& sig, int video_steps, const float* emb_steps,
+                const float* emb_last, const FrameTab& tab, int Th, int Tf, char* k, char* v,
+                size_t ls, int cap) {
+  const wam_dims* d = c.d;
+  Bufs& b = *c.b;
+  const int D = d->D, dt = d->dtype;
+  int st;
+  RowMap zmap;
+  zmap.n = 1;
+  zmap.P = Tf;
+  zmap.src[0] = 0;
+  HIPCK(copy_cvt_f32(c.s, dt, fut_noise_b, z, (int64_t)Tf * d->Cv));
+  for (int s = 0; s < video_steps; s++) {
+    HIPCK(embed(c.s, WAM_F32, dt, z, zmap, video->w_in, emb_steps + (size_t)s * D, b.X, Tf, D,
+                d->Cv));
+    for (int l = 0; l < d->L; l++)
+      if ((st = video_layer(c, video->layers[l], Tf, Th, tab, k + l * ls, v + l * ls, cap, false)))
+        return st;
+    if ((st = flush_pending(c, video->g_out, Tf))) return st;  // X whole for the head
+    HIPCK(step_boundary(c.s, dt, b.X, video->g_out, video->w_out, z, sig[s + 1] - sig[s], nullptr,
+                        nullptr, nullptr, Tf, D, d->Cv, true));
+  }
+  HIPCK(embed(c.s, WAM_F32, dt, z, zmap, video->w_in, emb_last, b.X, Tf, D, d->Cv));
+  for (int l = 0; l < d->L; l++)
+    if ((st = video_layer(c, video->layers[l], Tf, Th, tab, k + l * ls, v + l * ls, cap,
+                          l == d->L - 1)))
+      return st;
+  return WAM_OK;
+}
+
+// Time embeddings of a video call into emb: [0 (history), sigma_0 ..
+// sigma_{V-1} (imagine steps), sigma_V (V >= 1) | 1 (V = 0) (caching pass)].
+void video_schedule(int video_steps, double sigma_star, double shift, std::vector<float>& sig,
+                    std::vector<float>& embs) {
+  sig.assign(video_steps + 1, 0.f);
+  if (video_steps > 0) schedule(video_steps, sigma_star, shift, sig.data());
+  embs.clear();
+  embs.push_back(0.f);
+  if (video_steps > 0)
+    for (int k = 0; k <= video_steps; k++) embs.push_back(sig[k]);
+  else
+    embs.push_back(1.f);
+}
+
+int check_video_call(const wam_dims* d, const wam_expert_w* video, int B, int Fh, int Ff,
+                     const int32_t* frame_block, const wam_kv* cache) {
   int st;
   if ((st = check_dims(d))) return st;
   if ((st = check_expert(d, video, "video"))) return st;
   if (B < 1 || B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "B must be in [1, %d]", WAM_MAX_BATCH);
   if (Fh < 0 || Ff < 0 || Fh + Ff < 1 || Fh + Ff > WAM_MAX_FRAMES)
     return fail(WAM_E_SHAPE, "frame counts out of range");
-  if (Fh > 0 && !hist) return fail(WAM_E_ARG, "hist is NULL");
-  if (Ff > 0 && !fut_noise) return fail(WAM_E_ARG, "fut_noise is NULL");
-  if ((hist && !aligned16(hist)) || (fut_noise && !aligned16(fut_noise)) ||
-      (fut_latents_out && !aligned16(fut_latents_out)))
-    return fail(WAM_E_ALIGN, "input pointer not 16-byte aligned");
   if (!frame_block) return fail(WAM_E_ARG, "frame_block is NULL");
   if ((st = check_blocks(frame_block, Fh + Ff))) return st;
+  if (!cache) return fail(WAM_E_ARG, "cache is NULL");
+  if ((st = check_kv(d, cache, B, "cache"))) return st;
+  if (cache->n_layers != d->L) return fail(WAM_E_SHAPE, "cache must hold L layers");
+  return WAM_OK;
+}
+
+int check_future_args(int video_steps, double sigma_star, double shift) {
   if (video_steps < 0 || video_steps > WAM_MAX_STEPS)
     return fail(WAM_E_ARG, "video_steps must be in [0, %d]", WAM_MAX_STEPS);
   if (video_steps > 0 && !(sigma_star > 0.0 && sigma_star < 1.0))
     return fail(WAM_E_ARG, "sigma_star must be in (0, 1)");
   if (!(shift > 0.0)) return fail(WAM_E_ARG, "shift must be > 0");
-  if (!cache) return fail(WAM_E_ARG, "cache is NULL");
-  if ((st = check_kv(d, cache, B, "cache"))) return st;
-  if (cache->n_layers != d->L) return fail(WAM_E_SHAPE, "cache must hold L layers");
+  return WAM_OK;
+}
+
+}  // namespace
+
+int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video, const void* hist,
+                            const uint8_t* hist_valid, int B, int Fh, const void* fut_noise,
+                            int Ff, const int32_t* frame_block, int video_steps,
+                            double sigma_star, double shift, wam_kv* cache,
+                            float* fut_latents_out, void* ws, size_t ws_bytes, void* stream) {
+  int st;
+  if ((st = check_video_call(d, video, B, Fh, Ff, frame_block, cache))) return st;
+  if (Fh > 0 && !hist) return fail(WAM_E_ARG, "hist is NULL");
+  if (Ff > 0 && !fut_noise) return fail(WAM_E_ARG, "fut_noise is NULL");
+  if ((hist && !aligned16(hist)) || (fut_noise && !aligned16(fut_noise)) ||
+      (fut_latents_out && !aligned16(fut_latents_out)))
+    return fail(WAM_E_ALIGN, "input pointer not 16-byte aligned");
+  if ((st = check_future_args(video_steps, sigma_star, shift))) return st;
   if (!ws || !aligned16(ws)) return fail(WAM_E_WORKSPACE, "workspace NULL or unaligned");
   if (ws_bytes < wam_prefill_workspace_bytes(d, B, Fh, Ff))
     return fail(WAM_E_WORKSPACE, "workspace too small (%zu < %zu)", ws_bytes,
                 wam_prefill_workspace_bytes(d, B, Fh, Ff));
-
-  // frame tables of every episode, validated before anything is enqueued
   const int P = d->P;
-  std::vector<FrameTab> tabs(B);
-  std::vector<RowMap> hmaps(B);
-  std::vector<int> nh(B);
-  for (int b = 0; b < B; b++) {
-    int src[WAM_MAX_FRAMES], kend[WAM_MAX_FRAMES];
-    const uint8_t* v = hist_valid ? hist_valid + (size_t)b * Fh : nullptr;
-    int n = frame_table(frame_block, v, Fh, Ff, P, src, kend);
-    if (n == 0) return fail(WAM_E_SHAPE, "episode %d has no valid frame", b);
-    if ((long long)n * P > cache->cap)
-      return fail(WAM_E_SHAPE, "episode %d needs %d cache rows, cap is %d", b, n * P, cache->cap);
-    tabs[b].n = n;
-    tabs[b].P = P;
-    for (int i = 0; i < n; i++) tabs[b].kend[i] = kend[i];
-    nh[b] = n - Ff;
-    hmaps[b].n = nh[b];
-    hmaps[b].P = P;
-    for (int i = 0; i < nh[b]; i++) hmaps[b].src[i] = b * Fh + src[i];
-  }
+  Tables t;
+  if ((st = build_tables(frame_block, hist_valid, B, Fh, Ff, P, cache->cap, t))) return st;
 
   hipStream_t s = (hipStream_t)stream;
   Arena a(ws);
   Bufs bufs;
   float* z;
   plan_prefill(a, d, Fh, Ff, bufs, &z);
-
-  // time embeddings: [0 (history), sigma_0 .. sigma_V (V >= 1) | 1 (V = 0)]
-  std::vector<float> sig(video_steps + 1);
-  if (video_steps > 0) schedule(video_steps, sigma_star, shift, sig.data());
-  std::vector<float> embs;
-  embs.push_back(0.f);
-  if (video_steps > 0)
-    for (int k = 0; k <= video_steps; k++) embs.push_back(sig[k]);
-  else
-    embs.push_back(1.f);
+  std::vector<float> sig, embs;
+  video_schedule(video_steps, sigma_star, shift, sig, embs);
   const int D = d->D;
   HIPCK(time_embedding(s, embs.data(), (int)embs.size(), D, bufs.emb));
   const float* emb_hist = bufs.emb;
@@ -492,68 +581,172 @@ int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video, const 
   const size_t ep = (size_t)d->Hh * cache->cap * d->dh * esz(dt);  // one episode in a layer
   Layer c{s, d, &bufs};
   const int Tf = Ff * P;
-  RowMap zmap;
-  zmap.n = 1;
-  zmap.P = Tf;
-  zmap.src[0] = 0;
-
   for (int b = 0; b < B; b++) {
-    const int Th = nh[b] * P;
-    auto kl = [&](int l) { return (char*)cache->k + l * ls + b * ep; };
-    auto vl = [&](int l) { return (char*)cache->v + l * ls + b * ep; };
+    const int Th = t.nh[b] * P;
+    char* kb = (char*)cache->k + b * ep;
+    char* vb = (char*)cache->v + b * ep;
+    const void* fut_b = Ff > 0 ? (const char*)fut_noise + (size_t)b * Tf * d->Cv * esz(dt) : nullptr;
     if (video_steps == 0 && Ff > 0) {
       // No video denoising: the history rows and the future rows go through
       // the same layers, so one pass over all of them (history rows see only
       // history keys through the block-causal frame table) replaces the
       // history pass plus the future cache pass.
       if (Th > 0)
-        HIPCK(embed(s, dt, dt, hist, hmaps[b], video->w_in, emb_hist, bufs.X, Th, D, d->Cv));
-      HIPCK(copy_cvt_f32(s, dt, (const char*)fut_noise + (size_t)b * Tf * d->Cv * esz(dt), z,
-                         (int64_t)Tf * d->Cv));
+        HIPCK(embed(s, dt, dt, hist, t.hmap[b], video->w_in, emb_hist, bufs.X, Th, D, d->Cv));
+      RowMap zmap;
+      zmap.n = 1;
+      zmap.P = Tf;
+      zmap.src[0] = 0;
+      HIPCK(copy_cvt_f32(s, dt, fut_b, z, (int64_t)Tf * d->Cv));
       HIPCK(embed(s, WAM_F32, dt, z, zmap, video->w_in, emb_last, bufs.X + (size_t)Th * D, Tf, D,
                   d->Cv));
       for (int l = 0; l < d->L; l++)
-        if ((st = video_layer(c, video->layers[l], Th + Tf, 0, tabs[b], kl(l), vl(l), cache->cap,
-                              l == d->L - 1)))
+        if ((st = video_layer(c, video->layers[l], Th + Tf, 0, t.tab[b], kb + l * ls, vb + l * ls,
+                              cache->cap, l == d->L - 1)))
           return st;
-      if (fut_latents_out)
-        HIPCK(hipMemcpyAsync(fut_latents_out + (size_t)b * Tf * d->Cv, z,
-                             (size_t)Tf * d->Cv * 4, hipMemcpyDeviceToDevice, s));
-      cache->len[b] = tabs[b].n * P;
-      continue;
+    } else {
+      if (Th > 0 && (st = history_rows(c, video, hist, t.hmap[b], emb_hist, t.tab[b], 0, Th, kb, vb,
+                                        ls, cache->cap)))
+        return st;
+      if (Ff > 0 && (st = future_rows(c, video, fut_b, z, sig, video_steps, bufs.emb + D, emb_last,
+                                       t.tab[b], Th, Tf, kb, vb, ls, cache->cap)))
+        return st;
     }
-    if (Th > 0) {
-      HIPCK(embed(s, dt, dt, hist, hmaps[b], video->w_in, emb_hist, bufs.X, Th, D, d->Cv));
-      for (int l = 0; l < d->L; l++)
-        if ((st = video_layer(c, video->layers[l], Th, 0, tabs[b], kl(l), vl(l), cache->cap,
-                              l == d->L - 1)))
-          return st;
-    }
-    if (Ff > 0) {
-      HIPCK(copy_cvt_f32(s, dt, (const char*)fut_noise + (size_t)b * Tf * d->Cv * esz(dt), z,
-                         (int64_t)Tf * d->Cv));
-      for (int k = 0; k < video_steps; k++) {
-        HIPCK(embed(s, WAM_F32, dt, z, zmap, video->w_in, bufs.emb + (size_t)(1 + k) * D, bufs.X,
-                    Tf, D, d->Cv));
-        for (int l = 0; l < d->L; l++)
-          if ((st = video_layer(c, video->layers[l], Tf, Th, tabs[b], kl(l), vl(l), cache->cap,
-                                false)))
-            return st;
-        if ((st = flush_pending(c, video->g_out, Tf))) return st;  // X whole for the head
-        HIPCK(step_boundary(s, dt, bufs.X, video->g_out, video->w_out, z, sig[k + 1] - sig[k],
-                            nullptr, nullptr, nullptr, Tf, D, d->Cv, true));
-      }
-      HIPCK(embed(s, WAM_F32, dt, z, zmap, video->w_in, emb_last, bufs.X, Tf, D, d->Cv));
-      for (int l = 0; l < d->L; l++)
-        if ((st = video_layer(c, video->layers[l], Tf, Th, tabs[b], kl(l), vl(l), cache->cap,
-                              l == d->L - 1)))
-          return st;
-      if (fut_latents_out)
-        HIPCK(hipMemcpyAsync(fut_latents_out + (size_t)b * Tf * d->Cv, z,
-                             (size_t)Tf * d->Cv * 4, hipMemcpyDeviceToDevice, s));
-    }
-    cache->len[b] = tabs[b].n * P;
+    if (Ff > 0 && fut_latents_out)
+      HIPCK(hipMemcpyAsync(fut_latents_out + (size_t)b * Tf * d->Cv, z, (size_t)Tf * d->Cv * 4,
+                           hipMemcpyDeviceToDevice, s));
+    cache->len[b] = t.tab[b].n * P;
   }
+  return WAM_OK;
+}
+
+int wam_extend_history_cache(const wam_dims* d, const wam_expert_w* video, const void* hist_new,
+                             const uint8_t* hist_valid, int B, int Fh_old, int Fn,
+                             const int32_t* frame_block, wam_kv* cache, void* ws, size_t ws_bytes,
+                             void* stream) {
+  int st;
+  if (Fh_old < 0 || Fn < 1) return fail(WAM_E_SHAPE, "need Fh_old >= 0 and Fn >= 1");
+  if ((st = check_video_call(d, video, B, Fh_old + Fn, 0, frame_block, cache))) return st;
+  if (!hist_new) return fail(WAM_E_ARG, "hist_new is NULL");
+  if (!aligned16(hist_new)) return fail(WAM_E_ALIGN, "hist_new not 16-byte aligned");
+  if (!ws || !aligned16(ws) || ws_bytes < wam_prefill_workspace_bytes(d, B, Fn, 0))
+    return fail(WAM_E_WORKSPACE, "workspace missing or too small");
+  const int P = d->P, Fh = Fh_old + Fn;
+  std::vector<FrameTab> tab(B);
+  std::vector<RowMap> map(B);
+  std::vector<int> n_old(B), n_all(B);
+  for (int b = 0; b < B; b++) {
+    int src[WAM_MAX_FRAMES], kend[WAM_MAX_FRAMES];
+    const uint8_t* v = hist_valid ? hist_valid + (size_t)b * Fh : nullptr;
+    const int n = frame_table(frame_block, v, Fh, 0, P, src, kend);
+    int no = 0;
+    while (no < n && src[no] < Fh_old) no++;
+    if ((long long)n * P > cache->cap)
+      return fail(WAM_E_SHAPE, "episode %d needs %d cache rows, cap is %d", b, n * P, cache->cap);
+    if (cache->len[b] != no * P)
+      return fail(WAM_E_SHAPE, "episode %d: cache holds %d rows, its %d valid old frames %d", b,
+                  cache->len[b], no, no * P);
+    // frames of one block read each other: the new frames must start a block
+    if (no > 0 && no < n && frame_block[src[no]] <= frame_block[src[no - 1]])
+      return fail(WAM_E_SHAPE,
+                  "episode %d: new frame %d shares temporal block %d with a cached frame", b,
+                  src[no], frame_block[src[no]]);
+    tab[b].n = n;
+    tab[b].P = P;
+    for (int i = 0; i < n; i++) tab[b].kend[i] = kend[i];
+    map[b].n = n - no;
+    map[b].P = P;
+    for (int i = no; i < n; i++) map[b].src[i - no] = b * Fn + (src[i] - Fh_old);
+    n_old[b] = no;
+    n_all[b] = n;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  Arena a(ws);
+  Bufs bufs;
+  float* z;
+  plan_prefill(a, d, Fn, 0, bufs, &z);
+  const float zero = 0.f;
+  HIPCK(time_embedding(s, &zero, 1, d->D, bufs.emb));
+  const size_t ls = layer_stride(cache);
+  const size_t ep = (size_t)d->Hh * cache->cap * d->dh * esz(d->dtype);
+  Layer c{s, d, &bufs};
+  for (int b = 0; b < B; b++) {
+    const int rows = (n_all[b] - n_old[b]) * P;
+    if (rows > 0 &&
+        (st = history_rows(c, video, hist_new, map[b], bufs.emb, tab[b], n_old[b] * P, rows,
+                           (char*)cache->k + b * ep, (char*)cache->v + b * ep, ls, cache->cap)))
+      return st;
+    cache->len[b] = n_all[b] * P;
+  }
+  return WAM_OK;
+}
+
+int wam_prefill_future(const wam_dims* d, const wam_expert_w* video, const uint8_t* hist_valid,
+                       int B, int Fh, const void* fut_noise, int Ff, const int32_t* frame_block,
+                       int video_steps, double sigma_star, double shift, wam_kv* cache,
+                       float* fut_latents_out, void* ws, size_t ws_bytes, void* stream) {
+  int st;
+  if (Ff < 1) return fail(WAM_E_SHAPE, "Ff must be >= 1");
+  if ((st = check_video_call(d, video, B, Fh, Ff, frame_block, cache))) return st;
+  if (!fut_noise) return fail(WAM_E_ARG, "fut_noise is NULL");
+  if (!aligned16(fut_noise) || (fut_latents_out && !aligned16(fut_latents_out)))
+    return fail(WAM_E_ALIGN, "pointer not 16-byte aligned");
+  if ((st = check_future_args(video_steps, sigma_star, shift))) return st;
+  if (!ws || !aligned16(ws) || ws_bytes < wam_prefill_workspace_bytes(d, B, 0, Ff))
+    return fail(WAM_E_WORKSPACE, "workspace missing or too small");
+  const int P = d->P;
+  Tables t;
+  if ((st = build_tables(frame_block, hist_valid, B, Fh, Ff, P, cache->cap, t))) return st;
+  for (int b = 0; b < B; b++)
+    if (cache->len[b] != t.nh[b] * P)
+      return fail(WAM_E_SHAPE, "episode %d: cache holds %d rows, its valid history has %d", b,
+                  cache->len[b], t.nh[b] * P);
+
+  hipStream_t s = (hipStream_t)stream;
+  Arena a(ws);
+  Bufs bufs;
+  float* z;
+  plan_prefill(a, d, 0, Ff, bufs, &z);
+  std::vector<float> sig, embs;
+  video_schedule(video_steps, sigma_star, shift, sig, embs);
+  const int D = d->D, dt = d->dtype;
+  HIPCK(time_embedding(s, embs.data(), (int)embs.size(), D, bufs.emb));
+  const size_t ls = layer_stride(cache);
+  const size_t ep = (size_t)d->Hh * cache->cap * d->dh * esz(dt);
+  Layer c{s, d, &bufs};
+  const int Tf = Ff * P;
+  for (int b = 0; b < B; b++) {
+    const void* fut_b = (const char*)fut_noise + (size_t)b * Tf * d->Cv * esz(dt);
+    if ((st = future_rows(c, video, fut_b, z, sig, video_steps, bufs.emb + D,
+                          bufs.emb + (size_t)(embs.size() - 1) * D, t.tab[b], t.nh[b] * P, Tf,
+                          (char*)cache->k + b * ep, (char*)cache->v + b * ep, ls, cache->cap)))
+      return st;
+    if (fut_latents_out)
+      HIPCK(hipMemcpyAsync(fut_latents_out + (size_t)b * Tf * d->Cv, z, (size_t)Tf * d->Cv * 4,
+                           hipMemcpyDeviceToDevice, s));
+    cache->len[b] = t.tab[b].n * P;
+  }
+  return WAM_OK;
+}
+
+int wam_async_check(int H, int R, int S) {
+  if (!(0 < S && S < R && R <= H) || 2 * S < R)
+    return fail(WAM_E_ARG, "asynchronous execution needs R/2 <= S < R <= H (H=%d R=%d S=%d)", H, R,
+                S);
+  return WAM_OK;
+}
+
+int wam_async_handoff(int H, int R, int S, int elapsed, int* first, int* count) {
+  int st;
+  if ((st = wam_async_check(H, R, S))) return st;
+  if (!first || !count) return fail(WAM_E_ARG, "NULL pointer");
+  if (elapsed < 0) return fail(WAM_E_ARG, "elapsed must be >= 0");
+  if (elapsed > R - S)
+    return fail(WAM_E_SHAPE, "chunk ready %d steps after its trigger, the overlap is %d", elapsed,
+                R - S);
+  *first = elapsed;
+  *count = R - elapsed;
   return WAM_OK;
 }
 

@@ -63,6 +63,16 @@ _EXPORTS = {
                                           C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p, C.c_int,
                                           C.c_double, C.c_double, C.POINTER(WamKV), C.c_void_p,
                                           C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wam_extend_history_cache": (C.c_int, [C.POINTER(WamDims), C.POINTER(WamExpertW), C.c_void_p,
+                                           C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p,
+                                           C.POINTER(WamKV), C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wam_prefill_future": (C.c_int, [C.POINTER(WamDims), C.POINTER(WamExpertW), C.c_void_p, C.c_int,
+                                     C.c_int, C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_double,
+                                     C.c_double, C.POINTER(WamKV), C.c_void_p, C.c_void_p,
+                                     C.c_size_t, C.c_void_p]),
+    "wam_async_check": (C.c_int, [C.c_int, C.c_int, C.c_int]),
+    "wam_async_handoff": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.POINTER(C.c_int),
+                                    C.POINTER(C.c_int)]),
     "wam_fuse_interval_kv": (C.c_int, [C.POINTER(WamKV), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                                        C.c_int, C.POINTER(WamKV), C.c_void_p]),
     "wam_action_workspace_bytes": (C.c_size_t, [C.POINTER(WamDims), C.c_int, C.POINTER(WamKV)]),
@@ -227,6 +237,43 @@ def prefill_video_cache(d: WamDims, video: DeviceExpert, hist, hist_valid, B: in
         C.byref(d), C.byref(video.c), _ptr(hist), None if hv is None else hv.ctypes.data, B, Fh,
         _ptr(fut_noise), Ff, fb.ctypes.data, video_steps, sigma_star, shift, C.byref(cache.c),
         _ptr(fut_latents_out), _ptr(ws), ws.numel(), _stream(stream)), "wam_prefill_video_cache")
+
+
+def extend_history_cache(d: WamDims, video: DeviceExpert, hist_new, hist_valid, B: int, Fh_old: int,
+                         Fn: int, frame_block, cache: DeviceKV, ws=None, stream=None):
+    hv = None if hist_valid is None else np.ascontiguousarray(hist_valid, dtype=np.uint8)
+    fb = np.ascontiguousarray(frame_block, dtype=np.int32)
+    if ws is None:
+        ws = workspace(prefill_workspace_bytes(d, B, Fn, 0))
+    _check(lib().wam_extend_history_cache(
+        C.byref(d), C.byref(video.c), _ptr(hist_new), None if hv is None else hv.ctypes.data, B,
+        Fh_old, Fn, fb.ctypes.data, C.byref(cache.c), _ptr(ws), ws.numel(), _stream(stream)),
+        "wam_extend_history_cache")
+
+
+def prefill_future(d: WamDims, video: DeviceExpert, hist_valid, B: int, Fh: int, fut_noise, Ff: int,
+                   frame_block, video_steps: int, sigma_star: float, shift: float, cache: DeviceKV,
+                   fut_latents_out=None, ws=None, stream=None):
+    hv = None if hist_valid is None else np.ascontiguousarray(hist_valid, dtype=np.uint8)
+    fb = np.ascontiguousarray(frame_block, dtype=np.int32)
+    if ws is None:
+        ws = workspace(prefill_workspace_bytes(d, B, 0, Ff))
+    _check(lib().wam_prefill_future(
+        C.byref(d), C.byref(video.c), None if hv is None else hv.ctypes.data, B, Fh, _ptr(fut_noise),
+        Ff, fb.ctypes.data, video_steps, sigma_star, shift, C.byref(cache.c),
+        _ptr(fut_latents_out), _ptr(ws), ws.numel(), _stream(stream)), "wam_prefill_future")
+
+
+def async_check(H: int, R: int, S: int) -> bool:
+    """True iff (H, R, S) satisfies R/2 <= S < R <= H."""
+    return lib().wam_async_check(H, R, S) == 0
+
+
+def async_handoff(H: int, R: int, S: int, elapsed: int):
+    """(first, count): the aligned suffix of a chunk ready `elapsed` steps after its trigger."""
+    f, c = C.c_int(), C.c_int()
+    _check(lib().wam_async_handoff(H, R, S, elapsed, C.byref(f), C.byref(c)), "wam_async_handoff")
+    return f.value, c.value
 
 
 def fuse_interval_kv(src: DeviceKV, start, count, logits, dst: DeviceKV, stream=None):

@@ -23,7 +23,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = wam.lib()
     names = header_functions()
-    assert len(names) == 22
+    assert len(names) == 26
     for n in names:
         assert hasattr(L, n), n
     assert sorted(wam.exported_names()) == names
@@ -264,6 +264,84 @@ def test_fp8_cache_validation_errors():
     kv8c, _j = fake_kv(cap=512, lens=[300], dtype=wam.WAM_FP8)
     kv8c.k_scale = kv8c.v_scale = FAKE
     assert call_codenoise(kv=kv8c)[0] == -3
+
+
+def test_async_schedule_rule_by_brute_force():
+    # R/2 <= S < R <= H with S > 0 (Long-WAM Summary section 4.1), over every small triple
+    for H in range(0, 12):
+        for R in range(-1, 13):
+            for S in range(-1, 13):
+                want = 0 < S < R <= H and 2 * S >= R
+                assert wam.async_check(H, R, S) == want, (H, R, S)
+    # the deployed settings: R = 24 with strides 12, 16, 20; the default stride (R+1)//2
+    for S in (12, 16, 20, (24 + 1) // 2):
+        assert wam.async_check(32, 24, S)
+
+
+def test_async_handoff():
+    assert wam.async_handoff(32, 24, 16, 0) == (0, 24)
+    assert wam.async_handoff(32, 24, 16, 5) == (5, 19)
+    assert wam.async_handoff(32, 24, 16, 8) == (8, 16)       # exactly at the deadline O = 8
+    with pytest.raises(wam.WamError, match="overlap"):
+        wam.async_handoff(32, 24, 16, 9)                       # missed: the robot waited
+    with pytest.raises(wam.WamError):
+        wam.async_handoff(32, 24, 16, -1)
+    with pytest.raises(wam.WamError):
+        wam.async_handoff(32, 24, 11, 0)                       # S < R/2
+
+
+def call_extend(d=None, hist=FAKE, valid=None, B=1, Fh_old=3, Fn=2, blocks=(0, 1, 2, 3, 4), kv=None,
+                ws=FAKE, ws_bytes=1 << 40):
+    L = wam.lib()
+    d = d or good_dims()
+    ex = FakeExpert(d.L)
+    if kv is None:
+        kv, _keep = fake_kv(cap=512, lens=[300])
+    fb = np.asarray(blocks, dtype=np.int32)
+    va = None if valid is None else np.ascontiguousarray(valid, dtype=np.uint8)
+    st = L.wam_extend_history_cache(C.byref(d), C.byref(ex.c), hist, None if va is None else va.ctypes.data,
+                                    B, Fh_old, Fn, fb.ctypes.data, C.byref(kv), ws, ws_bytes, None)
+    return st, L.wam_last_error().decode()
+
+
+def call_future(d=None, valid=None, B=1, Fh=3, fut=FAKE, Ff=2, blocks=(0, 1, 2, 3, 4), V=2, kv=None,
+                ws=FAKE, ws_bytes=1 << 40):
+    L = wam.lib()
+    d = d or good_dims()
+    ex = FakeExpert(d.L)
+    if kv is None:
+        kv, _keep = fake_kv(cap=512, lens=[300])
+    fb = np.asarray(blocks, dtype=np.int32)
+    va = None if valid is None else np.ascontiguousarray(valid, dtype=np.uint8)
+    st = L.wam_prefill_future(C.byref(d), C.byref(ex.c), None if va is None else va.ctypes.data, B, Fh,
+                              fut, Ff, fb.ctypes.data, V, 0.9, 1.0, C.byref(kv), None, ws, ws_bytes, None)
+    return st, L.wam_last_error().decode()
+
+
+def test_streaming_validation_errors():
+    assert call_extend(Fn=0)[0] == -2
+    assert call_extend(hist=None)[0] == -1
+    assert call_extend(hist=FAKE + 2)[0] == -4
+    assert call_extend(ws_bytes=1024)[0] == -5
+    kv, _k = fake_kv(cap=512, lens=[200])
+    st, msg = call_extend(kv=kv)                               # len must be the old frames' rows
+    assert st == -2 and "cache holds" in msg
+    st, msg = call_extend(blocks=(0, 1, 1, 1, 2))              # new frame 3 shares block 1 with frame 2
+    assert st == -2 and "shares temporal block" in msg
+    kv, _k = fake_kv(cap=256, lens=[300])
+    st, msg = call_extend(kv=kv)
+    assert st == -2
+    # one padded old frame: the cache must hold 2 frames of rows
+    kv, _k = fake_kv(cap=512, lens=[200])
+    st, msg = call_extend(kv=kv, valid=np.array([[0, 1, 1, 1, 1]]), ws_bytes=16)
+    assert st == -5                                            # validation passed up to the workspace
+    assert call_future(Ff=0, blocks=(0, 1, 2))[0] == -2
+    assert call_future(fut=None)[0] == -1
+    assert call_future(V=-1)[0] == -1
+    kv, _k = fake_kv(cap=512, lens=[500])
+    st, msg = call_future(kv=kv)
+    assert st == -2 and "valid history" in msg
+    assert call_future(ws_bytes=1024)[0] == -5
 
 
 def test_fuse_validation_errors():
