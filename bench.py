@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=10,
                     help="layers per expert in the CPU oracle sample (about 1.1 s each for C1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream", type=int, default=0, metavar="K",
+                    help="streamed history: each timed step is one decision whose last K history "
+                         "frames just arrived (append them, add the future, denoise)")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="the action layers read an E4M3 copy of the cache (an option that departs "
                          "from the pages' bf16 cache; quantised once per chunk)")
@@ -190,8 +193,15 @@ def main():
     inp = inputs.generate(cfg)
     dc = DeviceChunk(cfg, inp)
     print(f"[bench] {cfg.name}: inputs resident, warmup {args.warmup}", file=sys.stderr, flush=True)
+    step = dc.run
+    if args.stream > 0:
+        if cfg.joint or not 0 < args.stream < cfg.Fh:
+            print(json.dumps({"error": "--stream needs an IDM/Faster-WAM workload and 0 < K < Fh"}))
+            sys.exit(2)
+        dc.prepare_stream(args.stream)
+        step = lambda: dc.stream_decision(args.stream)
     for _ in range(args.warmup):
-        dc.run()
+        step()
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K chunks
@@ -200,7 +210,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
-        dc.run()
+        step()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -213,7 +223,16 @@ def main():
     # ---- phases (events between the calls of one chunk)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     evs[0].record()
-    dc.prefill()
+    if args.stream > 0:   # append + future in place of the whole-window prefill
+        c = cfg
+        old = c.Fh - args.stream
+        dc.cache.len[:] = dc.hist_valid[:, :old].sum(axis=1) * c.P
+        wam.extend_history_cache(dc.dims, dc.video, dc.hist[:, old:].contiguous(), dc.hist_valid, c.B,
+                                 old, args.stream, c.frame_block[:c.Fh], dc.cache, dc.ws_extend)
+        wam.prefill_future(dc.dims, dc.video, dc.hist_valid, c.B, c.Fh, dc.fut, c.Ff, c.frame_block,
+                           c.V, c.sigma_star, c.shift, dc.cache, dc.z, dc.ws_future)
+    else:
+        dc.prefill()
     evs[1].record()
     dc.fuse()
     evs[2].record()
@@ -226,7 +245,7 @@ def main():
     # ---- live per-kernel timing pass (HIP events around every launch)
     wam.timing(True)
     for _ in range(2):
-        dc.run()
+        step()
     stats = wam.timing_report()
     wam.timing(False)
     kt = kernel_table(stats)
@@ -258,11 +277,14 @@ def main():
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) latents/noise, N(0,0.02^2) random-init weights)",
         "config": {"workload": f"{cfg.name}: {WORKLOAD_TEXT.get(cfg.name, '')}"
-                               + (", E4M3 K/V read by the action layers" if cfg.kv_fp8 else ""),
+                               + (", E4M3 K/V read by the action layers" if cfg.kv_fp8 else "")
+                               + (f", streamed: {args.stream} new history frame(s) per decision"
+                                  if args.stream else ""),
                    "kv_cache": "e4m3" if cfg.kv_fp8 else ("bf16" if cfg.dtype == "bf16" else "f32"),
                    "B": cfg.B,
                    "L": cfg.L, "D": cfg.D, "heads": f"{cfg.Hh}x{cfg.dh}", "kv_tokens": cfg.tokens_valid,
                    "action_steps": cfg.N, "video_steps": cfg.N if cfg.joint else cfg.V,
+                   "streamed_new_frames": args.stream,
                    "joint": cfg.joint},
         "roofline": roofline,
         "attn_action_hbm_gbps": kt.get("attn_action", {}).get("achieved"),

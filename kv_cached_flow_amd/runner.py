@@ -115,6 +115,36 @@ class DeviceChunk:
         wam.denoise_chunk(self.dims, self.action, self.read_kv, c.read_map, self.eps_a, c.B, c.N,
                           c.shift, self.actions, self.vhat, self.ws_denoise, stream)
 
+    def stream_decision(self, new_frames: int, stream=None):
+        """One decision of a streamed history whose last ``new_frames`` history
+        frames just arrived: drop the previous future rows, append the new
+        frames to the cached history, add the future, then fuse and denoise.
+        The first Fh - new_frames frames must already be cached (one
+        ``prefill`` of them, or earlier decisions)."""
+        c = self.cfg
+        old = c.Fh - new_frames
+        self.cache.len[:] = self.hist_valid[:, :old].sum(axis=1) * c.P
+        wam.extend_history_cache(self.dims, self.video, self.hist[:, old:].contiguous(), self.hist_valid,
+                                 c.B, old, new_frames, c.frame_block[:c.Fh], self.cache, self.ws_extend,
+                                 stream)
+        wam.prefill_future(self.dims, self.video, self.hist_valid, c.B, c.Fh, self.fut, c.Ff,
+                           c.frame_block, c.V, c.sigma_star, c.shift, self.cache, self.z,
+                           self.ws_future, stream)
+        self.fuse(stream)
+        self.denoise(stream)
+        return self.actions
+
+    def prepare_stream(self, new_frames: int, stream=None):
+        """Cache the first Fh - new_frames history frames (workspaces for
+        ``stream_decision``)."""
+        c = self.cfg
+        old = c.Fh - new_frames
+        self.ws_extend = wam.workspace(wam.prefill_workspace_bytes(self.dims, c.B, new_frames, 0))
+        self.ws_future = wam.workspace(wam.prefill_workspace_bytes(self.dims, c.B, 0, c.Ff))
+        wam.prefill_video_cache(self.dims, self.video, self.hist[:, :old].contiguous(),
+                                self.hist_valid[:, :old], c.B, old, None, 0, c.frame_block[:old], 0,
+                                c.sigma_star, c.shift, self.cache, None, self.ws_prefill, stream)
+
     def run(self, stream=None):
         """One whole chunk: prefill, fuse (SparseMoT), N action steps (with
         co-denoising: the history prefill, then N joint video + action steps)."""
