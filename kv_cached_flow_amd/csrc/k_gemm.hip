@@ -4,8 +4,10 @@
 //                staged with register prefetch; the prefill / imagine
 //                projections (M = thousands of tokens).
 //  * gemm_skinny bf16 MFMA for M <= 128 (the 32*B action rows): weight
-//                streaming, A staged once in LDS, split-K across workgroups
-//                merged by the last-arriving workgroup in a fixed order.
+//                streaming, A and B fragments loaded straight into registers,
+//                k split over the waves of a workgroup (summed through LDS in
+//                wave order) and, for the residual products, over workgroups
+//                (fp32 partials that the next RMSNorm adds in split order).
 //  * gemm_simple fp32-accumulate FMA tiles for any type/size: the fp32
 //                workload and the narrow heads (N = Cv or A).
 #include "wam_internal.h"
