@@ -57,10 +57,27 @@ class WamConfig:
     joint: bool = False   # co-denoising: video and actions take the N steps together
     video_end: float = 0.0  # co-denoising: flow time the video reaches after N steps
     kv_fp8: bool = False  # the action layers read an E4M3 copy of their K/V (not the pages' bf16)
+    Da: int = 0           # action expert width (0: D); the attention interface is Hh x dh for both
+    Fma: int = 0          # action expert MLP width (0: Fm)
 
     @property
     def F(self) -> int:
         return self.Fh + self.Ff
+
+    @property
+    def Dq(self) -> int:
+        """Attention interface width Hh * dh, shared by both experts."""
+        return self.Hh * self.dh
+
+    @property
+    def Dact(self) -> int:
+        """Hidden width of the action expert."""
+        return self.Da or self.D
+
+    @property
+    def Fact(self) -> int:
+        """MLP width of the action expert."""
+        return self.Fma or self.Fm
 
     @property
     def n_valid_hist(self) -> int:

@@ -62,14 +62,17 @@ def expert_weights(cfg: WamConfig, which: str, n_layers: int | None = None,
     layers are identical to the first layers of the full stack)."""
     g = _G_VIDEO if which == "video" else _G_ACTION
     cio = cfg.Cv if which == "video" else cfg.A
-    D, Fm = cfg.D, cfg.Fm
+    # hidden width D and MLP width Fm of this expert; Q/K/V use the shared
+    # attention interface Dq = Hh * dh
+    D, Fm = (cfg.D, cfg.Fm) if which == "video" else (cfg.Dact, cfg.Fact)
+    Dq = cfg.Dq
     L = cfg.L if n_layers is None else n_layers
 
     def qkv(l):
-        w = _normal(cfg, (g, l, _S_QKV), (3 * D, D), cfg.w_std)
+        w = _normal(cfg, (g, l, _S_QKV), (3 * Dq, D), cfg.w_std)
         if cfg.qk_std != cfg.w_std:
-            qk = _normal(cfg, (g, l, _S_QKV, 1), (2 * D, D), cfg.qk_std)
-            w[: 2 * D] = qk
+            qk = _normal(cfg, (g, l, _S_QKV, 1), (2 * Dq, D), cfg.qk_std)
+            w[: 2 * Dq] = qk
         return w
 
     jobs = {"w_in": lambda: _normal(cfg, (g, 0, _S_WIN), (D, cio), cfg.w_std),
@@ -78,7 +81,7 @@ def expert_weights(cfg: WamConfig, which: str, n_layers: int | None = None,
     for l in range(L):
         jobs[("g1", l)] = (lambda l=l: _normal(cfg, (g, l, _S_G1), (D,), cfg.w_std, 1.0))
         jobs[("wqkv", l)] = (lambda l=l: qkv(l))
-        jobs[("wo", l)] = (lambda l=l: _normal(cfg, (g, l, _S_WO), (D, D), cfg.w_std))
+        jobs[("wo", l)] = (lambda l=l: _normal(cfg, (g, l, _S_WO), (D, Dq), cfg.w_std))
         jobs[("g2", l)] = (lambda l=l: _normal(cfg, (g, l, _S_G2), (D,), cfg.w_std, 1.0))
         jobs[("w1", l)] = (lambda l=l: _normal(cfg, (g, l, _S_W1), (Fm, D), cfg.w_std))
         jobs[("w2", l)] = (lambda l=l: _normal(cfg, (g, l, _S_W2), (D, Fm), cfg.w_std))

@@ -189,14 +189,18 @@ def layer(X, w: dict, Hh: int, ctx: Optional[Tuple[torch.Tensor, torch.Tensor]] 
       X += concat(attn) Wo^T;  X += GELU(RMSNorm(X; g2) W1^T) W2^T.
     No biases.  Returns (X_out, K, V); K, V are this layer's cache rows.
     With ``kv_only`` only K, V are produced (X_out is None).
+    Q, K and V have the width Dq = Hh * dh of the attention interface the two
+    experts share (24 heads x 128 on the "Fast-WAM 精读" page, section 四.4),
+    which may differ from the expert's own width D (Wqkv [3 Dq][D], Wo [D][Dq]).
     """
     n, D = X.shape
-    dh = D // Hh
+    Dq = w["wqkv"].shape[0] // 3
+    dh = Dq // Hh
     Y = rmsnorm(X, w["g1"])
     qkv = Y @ w["wqkv"].T
-    Q = qkv[:, :D].reshape(n, Hh, dh)
-    K = qkv[:, D:2 * D].reshape(n, Hh, dh)
-    V = qkv[:, 2 * D:].reshape(n, Hh, dh)
+    Q = qkv[:, :Dq].reshape(n, Hh, dh)
+    K = qkv[:, Dq:2 * Dq].reshape(n, Hh, dh)
+    V = qkv[:, 2 * Dq:].reshape(n, Hh, dh)
     if kv_only:
         return None, K, V
     if ctx is not None:
@@ -205,7 +209,7 @@ def layer(X, w: dict, Hh: int, ctx: Optional[Tuple[torch.Tensor, torch.Tensor]] 
     else:
         Kall, Vall = K, V
     O = attention(Q, Kall, Vall, allow)
-    X = X + O.reshape(n, D) @ w["wo"].T
+    X = X + O.reshape(n, Dq) @ w["wo"].T
     X = X + gelu(rmsnorm(X, w["g2"]) @ w["w1"].T) @ w["w2"].T
     return X, K, V
 
@@ -289,7 +293,7 @@ def history_cache(cfg, vw: dict, hist_b, valid_b, drop_padded: bool = True):
             X, K, V = layer(X, lw, Hh, None, mask_h, kv_only=(l == L - 1))
             cache_h.append((K, V))
     else:
-        empty = torch.zeros((0, Hh, D // Hh), dtype=dt)
+        empty = torch.zeros((0, Hh, cfg.dh), dtype=dt)
         cache_h = [(empty, empty)] * L
     return cache_h, fall, valid, mask_f
 
@@ -410,7 +414,7 @@ def action_velocity(cfg, aw: dict, kv_read: List[Optional[Tuple]], a, sigma: flo
     nothing (SparseMoT, Faster-WAM page section 3.2); no mask among action
     tokens (Long-WAM Summary section 3.2: the entire noisy chunk is visible).
     """
-    X = embed(a, aw["w_in"], sigma, cfg.D)
+    X = embed(a, aw["w_in"], sigma, cfg.Dact)
     for l, lw in enumerate(aw["layers"]):
         X, _, _ = layer(X, lw, cfg.Hh, kv_read[l], None)
     return head(X, aw["g_out"], aw["w_out"])
@@ -682,13 +686,12 @@ def joint_mot_step(cfg, vw: dict, aw: dict, video_tok, video_sigma, video_frames
     Returns (v-hat of the action rows, per-layer video (K, V)), and with
     ``video_head`` also the video expert's v-hat of every video row.
     """
-    D, Hh = cfg.D, cfg.Hh
-    dh = D // Hh
+    D, Hh, dh, Dq = cfg.D, cfg.Hh, cfg.dh, cfg.Dq
     dt = vw["w_in"].dtype
     Nv, H = video_tok.shape[0], a.shape[0]
     Xv = video_tok @ vw["w_in"].T + torch.stack(
         [time_embedding(float(s), D, dt) for s in video_sigma])
-    Xa = embed(a, aw["w_in"], t, D)
+    Xa = embed(a, aw["w_in"], t, cfg.Dact)
     block = torch.tensor(cfg.frame_block, dtype=torch.int64)
     valid = torch.as_tensor(frame_valid, dtype=torch.int64)
     vv = video_visible(video_frames, video_frames, block, valid)
@@ -700,11 +703,11 @@ def joint_mot_step(cfg, vw: dict, aw: dict, video_tok, video_sigma, video_frames
     for lv, la in zip(vw["layers"], aw["layers"]):
         Yv, Ya = rmsnorm(Xv, lv["g1"]), rmsnorm(Xa, la["g1"])
         qv, qa = Yv @ lv["wqkv"].T, Ya @ la["wqkv"].T
-        Q = torch.cat([qv[:, :D], qa[:, :D]]).reshape(-1, Hh, dh)
-        K = torch.cat([qv[:, D:2 * D], qa[:, D:2 * D]]).reshape(-1, Hh, dh)
-        V = torch.cat([qv[:, 2 * D:], qa[:, 2 * D:]]).reshape(-1, Hh, dh)
+        Q = torch.cat([qv[:, :Dq], qa[:, :Dq]]).reshape(-1, Hh, dh)
+        K = torch.cat([qv[:, Dq:2 * Dq], qa[:, Dq:2 * Dq]]).reshape(-1, Hh, dh)
+        V = torch.cat([qv[:, 2 * Dq:], qa[:, 2 * Dq:]]).reshape(-1, Hh, dh)
         kv.append((K[:Nv], V[:Nv]))
-        O = attention(Q, K, V, lambda q0, q1: full[q0:q1]).reshape(-1, D)
+        O = attention(Q, K, V, lambda q0, q1: full[q0:q1]).reshape(-1, Dq)
         Xv = Xv + O[:Nv] @ lv["wo"].T
         Xa = Xa + O[Nv:] @ la["wo"].T
         Xv = Xv + gelu(rmsnorm(Xv, lv["g2"]) @ lv["w1"].T) @ lv["w2"].T

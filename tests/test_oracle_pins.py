@@ -228,6 +228,53 @@ def test_layer_vs_library_composition():
     assert torch.equal(K, K2) and torch.equal(V, V2)
 
 
+def test_layer_with_a_wider_attention_interface_vs_library():
+    # the expert width D differs from the attention width Hh * dh (the action
+    # expert: 1024 wide, 24 heads x 128): Wqkv [3 Dq][D], Wo [D][Dq]
+    r = np.random.default_rng(12)
+    D, Hh, dh, Fm, n, nc = 40, 3, 32, 72, 9, 13
+    Dq = Hh * dh
+    t = lambda *sh: torch.tensor(r.standard_normal(sh) * 0.2, dtype=f64)
+    w = {"g1": 1 + t(D), "wqkv": t(3 * Dq, D), "wo": t(D, Dq), "g2": 1 + t(D), "w1": t(Fm, D),
+         "w2": t(D, Fm)}
+    X = torch.tensor(r.standard_normal((n, D)), dtype=f64)
+    ctx = (t(nc, Hh, dh), t(nc, Hh, dh))
+    got, K, V = O.layer(X, w, Hh, ctx, None)
+    Y = F.rms_norm(X, (D,), w["g1"], eps=1e-6)
+    q, k, v = F.linear(Y, w["wqkv"]).split(Dq, dim=1)
+    q, k, v = (u.reshape(n, Hh, dh) for u in (q, k, v))
+    assert torch.equal(K, k) and torch.equal(V, v)
+    k = torch.cat([ctx[0], k])
+    v = torch.cat([ctx[1], v])
+    o = F.scaled_dot_product_attention(q.permute(1, 0, 2), k.permute(1, 0, 2), v.permute(1, 0, 2))
+    ref = X + F.linear(o.permute(1, 0, 2).reshape(n, Dq), w["wo"])
+    ref = ref + F.linear(F.gelu(F.linear(F.rms_norm(ref, (D,), w["g2"], eps=1e-6), w["w1"])), w["w2"])
+    assert torch.max(torch.abs(got - ref)) < 1e-12
+
+
+def test_real_width_chunk_structure():
+    # a chunk whose experts differ in width (video 48 = 3 heads x 16, action 20)
+    # keeps the identities: joint sequence == cached path
+    cfg = _tiny(D=48, Hh=3, dh=16, Da=20, Fma=36)
+    inp = inputs.generate(cfg, threads=1)
+    assert inp["action"]["layers"][0]["wqkv"].shape == (3 * 48, 20)
+    assert inp["action"]["layers"][0]["wo"].shape == (20, 48)
+    vw = O.to_torch_expert(inp["video"], f64)
+    aw = O.to_torch_expert(inp["action"], f64)
+    cache, z, frames = O.video_prefill(cfg, vw, inp["hist"][0], inp["hist_valid"][0], inp["eps_v"][0])
+    t0 = float(O.schedule(cfg.N, 0.0)[0])
+    a = torch.tensor(inp["eps_a"][0], dtype=f64)
+    v_cached = O.action_velocity(cfg, aw, O.read_layers(cfg, cache, None), a, t0)
+    valid_frames = [f for f in range(cfg.Fh) if inp["hist_valid"][0][f]]
+    hist_tok = torch.tensor(inp["hist"][0][valid_frames], dtype=f64).reshape(-1, cfg.Cv)
+    vtok = torch.cat([hist_tok, z])
+    sig_f = float(O.schedule(cfg.V, cfg.sigma_star)[-1])
+    vsig = [0.0] * hist_tok.shape[0] + [sig_f] * z.shape[0]
+    fvalid = list(inp["hist_valid"][0]) + [1] * cfg.Ff
+    v_joint, _ = O.joint_mot_step(cfg, vw, aw, vtok, vsig, frames, fvalid, a, t0)
+    assert torch.max(torch.abs(v_joint - v_cached)) < 1e-12
+
+
 def test_layer_zero_output_projections_is_identity():
     r = np.random.default_rng(11)
     w = _rand_layer(r, 32, 64)
