@@ -65,19 +65,23 @@ enum {
  * for K and one for V.  Every other tensor of a WAM_BF16 model stays bf16. */
 enum { WAM_F32 = 0, WAM_BF16 = 1, WAM_FP8 = 2 };
 
-/* Shapes shared by both experts (layer count, heads and head dim must match
- * so that video layer i pairs with action layer i, "Fast-WAM 精读" section 四.4). */
+/* Shapes of the two experts.  Layer count, heads and head dim are shared, so
+ * that video layer i pairs with action layer i over one attention interface of
+ * Hh heads x dh ("Fast-WAM 精读" section 四.4: both branches project to 24 x 128
+ * whatever their own widths, 3072 and 1024). */
 typedef struct {
   int L;      /* layers per expert */
-  int D;      /* hidden width; D == Hh * dh */
+  int D;      /* video expert width; D == Hh * dh */
   int Hh;     /* attention heads */
   int dh;     /* head dim; must be 64 */
-  int Fm;     /* MLP inner width */
+  int Fm;     /* video expert MLP inner width */
   int Cv;     /* channels per video latent token */
   int A;      /* action dims per action token */
   int H;      /* action tokens per chunk; must be 32 */
   int P;      /* tokens per latent frame */
   int dtype;  /* WAM_F32 or WAM_BF16 */
+  int Da;     /* action expert width (0: D); its Wqkv is [3 Hh dh][Da], Wo [Da][Hh dh] */
+  int Fma;    /* action expert MLP inner width (0: Fm) */
 } wam_dims;
 
 /* One layer: Y = RMSNorm(X; g1); [Q K V] = Y Wqkv^T; X += Attn Wo^T;

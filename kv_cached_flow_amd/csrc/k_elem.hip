@@ -7,7 +7,7 @@ namespace wam {
 // ------------------------------------------------------------ RMSNorm
 // One wavefront per row: (optionally x += sum of split partials, written
 // back), then y = x * (mean(x^2) + 1e-6)^(-1/2) * g.
-template <typename TO, bool ACC>
+template <typename TO, bool ACC, int MAXV = 8>  // D <= 256 MAXV
 __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x,
                                                       const float* __restrict__ part, int KS,
                                                       const float* __restrict__ g,
@@ -16,7 +16,6 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x,
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
   float* xr = x + (long long)row * D;
-  constexpr int MAXV = 8;  // D <= 2048
   float4 v[MAXV];
   float ss = 0.f;
 #pragma unroll
@@ -60,9 +59,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x,
   }
 }
 
-// One workgroup per row (small M): thread t owns columns 4t..4t+3 (+1024 j);
-// all loads of a thread are issued before any reduction.
-template <typename TO, bool ACC>
+// One workgroup per row (small M): thread t owns columns 4t..4t+3 (+1024 j),
+// D <= 1024 NJ; all loads of a thread are issued before any reduction.
+template <typename TO, bool ACC, int NJ = 2>
 __global__ __launch_bounds__(256) void rmsnorm_row_kernel(float* __restrict__ x,
                                                           const float* __restrict__ part, int KS,
                                                           const float* __restrict__ g,
@@ -70,10 +69,10 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(float* __restrict__ x,
   __shared__ float wss[4];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float* xr = x + (long long)row * D;
-  float4 v[2];
+  float4 v[NJ];
   float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
+  for (int j = 0; j < NJ; j++) {
     const int i = 4 * tid + 1024 * j;
     if (i < D) {
       float4 t = *(const float4*)(xr + i);
@@ -106,7 +105,7 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(float* __restrict__ x,
   const float r = 1.0f / sqrtf((((wss[0] + wss[1]) + wss[2]) + wss[3]) / (float)D + 1e-6f);
   TO* yr = y + (long long)row * D;
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
+  for (int j = 0; j < NJ; j++) {
     const int i = 4 * tid + 1024 * j;
     if (i < D) {
       const float4 gg = *(const float4*)(g + i);
@@ -124,24 +123,37 @@ template <bool ACC>
 static hipError_t rmsnorm_launch(hipStream_t s, int odt, float* x, const float* part, int KS,
                                  const float* g, void* y, int M, int D) {
   if (M <= 0) return hipSuccess;
-  if (D > 2048 || D % 4 || KS > 4) return hipErrorInvalidValue;
+  if (D > 4096 || D % 4 || KS > 4) return hipErrorInvalidValue;
+  const bool wide = D > 2048;
   TimingScope ts(s, KC_RMSNORM,
                  (double)M * D * ((ACC ? 8 + 4 * KS : 4) + (odt == WAM_BF16 ? 2 : 4)), 0.0);
   if (M <= 512) {  // latency bound: a workgroup per row
-    if (odt == WAM_BF16)
+    if (odt == WAM_BF16 && !wide)
       hipLaunchKernelGGL((rmsnorm_row_kernel<bf16_t, ACC>), dim3(M), dim3(256), 0, s, x, part, KS,
                          g, (bf16_t*)y, M, D);
-    else
+    else if (odt == WAM_BF16)
+      hipLaunchKernelGGL((rmsnorm_row_kernel<bf16_t, ACC, 4>), dim3(M), dim3(256), 0, s, x, part,
+                         KS, g, (bf16_t*)y, M, D);
+    else if (!wide)
       hipLaunchKernelGGL((rmsnorm_row_kernel<float, ACC>), dim3(M), dim3(256), 0, s, x, part, KS,
                          g, (float*)y, M, D);
+    else
+      hipLaunchKernelGGL((rmsnorm_row_kernel<float, ACC, 4>), dim3(M), dim3(256), 0, s, x, part,
+                         KS, g, (float*)y, M, D);
     return hipGetLastError();
   }
   dim3 grid((M + 3) / 4);
-  if (odt == WAM_BF16)
+  if (odt == WAM_BF16 && !wide)
     hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, ACC>), grid, dim3(256), 0, s, x, part, KS, g,
                        (bf16_t*)y, M, D);
-  else
+  else if (odt == WAM_BF16)
+    hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, ACC, 16>), grid, dim3(256), 0, s, x, part, KS, g,
+                       (bf16_t*)y, M, D);
+  else if (!wide)
     hipLaunchKernelGGL((rmsnorm_kernel<float, ACC>), grid, dim3(256), 0, s, x, part, KS, g,
+                       (float*)y, M, D);
+  else
+    hipLaunchKernelGGL((rmsnorm_kernel<float, ACC, 16>), grid, dim3(256), 0, s, x, part, KS, g,
                        (float*)y, M, D);
   return hipGetLastError();
 }
@@ -365,12 +377,12 @@ hipError_t copy_cvt_f32(hipStream_t s, int sdt, const void* src, float* dst, int
 
 
 // ------------------------------------------------------------ step boundary
-// One workgroup per row m (D <= 2048, C <= 64):
+// One workgroup per row m (D <= 1024 NJ, C <= 64):
 //   head:  y = RMSNorm(X[m]; g_out); v[n] = y . W_out[n] for n < C;
 //          z[m][n] += dt v[n]; vhat[m][n] = v[n]      (the flow update)
 //   next:  X[m][:] = z[m][:] W_in^T + emb_next[:]       (the next embedding)
 // Either part may be switched off (do_head = 0 / w_in = nullptr).
-template <typename TW>
+template <typename TW, int NJ = 2>
 __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ X,
                                                    const float* __restrict__ g_out,
                                                    const TW* __restrict__ w_out,
@@ -386,10 +398,10 @@ __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ X,
   float* xr = X + (long long)m * D;
   float* zr = z + (long long)m * C;
   if (do_head) {
-    float4 y[2];
+    float4 y[NJ];
     float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < NJ; j++) {
       const int i = 4 * tid + 1024 * j;
       y[j] = (i < D) ? *(const float4*)(xr + i) : float4{0.f, 0.f, 0.f, 0.f};
       ss = fmaf(y[j].x, y[j].x, ss);
@@ -403,7 +415,7 @@ __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ X,
     __syncthreads();
     const float r = 1.0f / sqrtf((((wss[0] + wss[1]) + wss[2]) + wss[3]) / (float)D + 1e-6f);
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < NJ; j++) {
       const int i = 4 * tid + 1024 * j;
       if (i < D) {
         const float4 gg = *(const float4*)(g_out + i);
@@ -416,7 +428,7 @@ __global__ __launch_bounds__(256) void step_kernel(float* __restrict__ X,
     for (int n = 0; n < C; n++) {
       float p = 0.f;
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
+      for (int j = 0; j < NJ; j++) {
         const int i = 4 * tid + 1024 * j;
         if (i < D) {
           const TW* wr = w_out + (long long)n * D + i;
@@ -454,17 +466,26 @@ hipError_t step_boundary(hipStream_t s, int wdt, float* X, const float* g_out, c
                          float* z, float dt, float* vhat, const void* w_in, const float* emb_next,
                          int M, int D, int C, bool do_head) {
   if (M <= 0) return hipSuccess;
-  if (D > 2048 || D % 4 || C > 64) return hipErrorInvalidValue;
+  if (D > 4096 || D % 4 || C > 64) return hipErrorInvalidValue;
   TimingScope ts(s, KC_MISC,
                  (double)M * ((do_head ? D * 4.0 + 2.0 * C * 4 : 0.0) + (w_in ? D * 4.0 : 0.0)),
                  (double)M * ((do_head ? 2.0 * C * D : 0.0) + (w_in ? 2.0 * C * D : 0.0)));
-  if (wdt == WAM_BF16)
+  const bool wide = D > 2048;
+  if (wdt == WAM_BF16 && !wide)
     hipLaunchKernelGGL(step_kernel<bf16_t>, dim3(M), dim3(256), 0, s, X, g_out,
                        (const bf16_t*)w_out, z, dt, vhat, (const bf16_t*)w_in, emb_next, D, C,
                        do_head ? 1 : 0);
-  else
+  else if (wdt == WAM_BF16)
+    hipLaunchKernelGGL((step_kernel<bf16_t, 4>), dim3(M), dim3(256), 0, s, X, g_out,
+                       (const bf16_t*)w_out, z, dt, vhat, (const bf16_t*)w_in, emb_next, D, C,
+                       do_head ? 1 : 0);
+  else if (!wide)
     hipLaunchKernelGGL(step_kernel<float>, dim3(M), dim3(256), 0, s, X, g_out, (const float*)w_out,
                        z, dt, vhat, (const float*)w_in, emb_next, D, C, do_head ? 1 : 0);
+  else
+    hipLaunchKernelGGL((step_kernel<float, 4>), dim3(M), dim3(256), 0, s, X, g_out,
+                       (const float*)w_out, z, dt, vhat, (const float*)w_in, emb_next, D, C,
+                       do_head ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -58,10 +58,22 @@ int check_dims(const wam_dims* d) {
   if (d->dh != 64) return fail(WAM_E_SHAPE, "head dim must be 64 (got %d)", d->dh);
   if (d->D != d->Hh * d->dh) return fail(WAM_E_SHAPE, "D (%d) != Hh*dh (%d)", d->D, d->Hh * d->dh);
   if (d->D % 64 || d->Fm % 64) return fail(WAM_E_SHAPE, "D and Fm must be multiples of 64");
+  if (d->Da < 0 || d->Da % 64 || d->Fma < 0 || d->Fma % 64)
+    return fail(WAM_E_SHAPE, "Da and Fma must be 0 or positive multiples of 64");
+  if (d->D > 4096 || d->Da > 4096) return fail(WAM_E_SHAPE, "expert widths above 4096 are not supported");
   if (d->H != 32) return fail(WAM_E_SHAPE, "action chunk length must be 32 (got %d)", d->H);
   if (d->Cv < 1 || d->Cv > 64 || d->A < 1 || d->A > 64)
     return fail(WAM_E_SHAPE, "Cv and A must be in [1, 64]");
   return WAM_OK;
+}
+
+// The action expert's shapes: width Da and MLP width Fma in D and Fm (the
+// attention interface Hh x dh is unchanged).
+wam_dims action_view(const wam_dims* d) {
+  wam_dims a = *d;
+  if (d->Da) a.D = d->Da;
+  if (d->Fma) a.Fm = d->Fma;
+  return a;
 }
 
 int check_expert(const wam_dims* d, const wam_expert_w* e, const char* name) {
@@ -267,15 +279,15 @@ int norm_rows(const Layer& c, int odt, const float* g, void* y, int M) {
 int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, const void* vc,
                  int cap, const ActLens& lens, const float* ksc = nullptr,
                  const float* vsc = nullptr) {
-  const wam_dims* d = c.d;
-  const int dt = d->dtype, D = d->D, H = d->H, M = B * H;
+  const wam_dims* d = c.d;  // the action view: D = the action width
+  const int dt = d->dtype, D = d->D, Dq = d->Hh * d->dh, H = d->H, M = B * H;
   Bufs& b = *c.b;
   int st;
   EpiArgs e{};
   e.q = b.Q;
   e.k = b.Ka;
   e.v = b.Va;
-  e.D = D;
+  e.D = Dq;
   e.dh = d->dh;
   e.rpg = H;
   e.q_gs = e.k_gs = (long long)d->Hh * H * d->dh;
@@ -284,10 +296,10 @@ int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, co
   e.v_hs = (long long)d->dh * H;
   e.v_ld = H;
   if ((st = norm_rows(c, dt, w.g1, b.Y, M))) return st;
-  HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, M, 3 * D, D, b.Y, D, w.wqkv, D, e));
+  HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, M, 3 * Dq, D, b.Y, D, w.wqkv, D, e));
   HIPCK(attn_action(c.s, dt, B, d->Hh, H, b.Q, b.Ka, b.Va, H, kc, vc, cap, lens, b.O, 0, b.attn,
                     b.attn_bytes, ksc, vsc));
-  if ((st = action_resid(c, M, D, D, b.O, w.wo))) return st;
+  if ((st = action_resid(c, M, D, Dq, b.O, w.wo))) return st;
   if ((st = norm_rows(c, dt, w.g2, b.Y, M))) return st;
   EpiArgs gl{};
   gl.out = b.Hb;
@@ -303,17 +315,17 @@ int flush_pending(const Layer& c, const float* g, int M) {
   return norm_rows(c, c.d->dtype, g, b.Y, M);
 }
 
-// workspace of the action path (rows M = B*H)
+// workspace of the action path (rows M = B*H); d is the action view
 void plan_action(Arena& a, const wam_dims* d, int B, int max_len, bool with_emb, Bufs& b) {
   const int M = B * d->H;
-  const size_t e = esz(d->dtype);
+  const size_t e = esz(d->dtype), Dq = (size_t)d->Hh * d->dh;
   b.emb = with_emb ? (float*)a.take((size_t)WAM_MAX_STEPS * d->D * 4) : nullptr;
   b.X = (float*)a.take((size_t)M * d->D * 4);
   b.Y = a.take((size_t)M * d->D * e);
-  b.Q = a.take((size_t)M * d->D * e);
-  b.Ka = a.take((size_t)M * d->D * e);
-  b.Va = a.take((size_t)M * d->D * e);
-  b.O = a.take((size_t)M * d->D * e);
+  b.Q = a.take((size_t)M * Dq * e);
+  b.Ka = a.take((size_t)M * Dq * e);
+  b.Va = a.take((size_t)M * Dq * e);
+  b.O = a.take((size_t)M * Dq * e);
   b.Hb = a.take((size_t)M * d->Fm * e);
   b.Yh = (float*)a.take((size_t)M * d->D * 4);
   b.part_bytes = (size_t)4 * M * d->D * 4;
@@ -802,6 +814,8 @@ static int max_len_of(const wam_kv* kv, int B) {
 
 size_t wam_action_workspace_bytes(const wam_dims* d, int B, const wam_kv* kv) {
   if (check_dims(d) || B < 1 || B > WAM_MAX_BATCH) return 0;
+  const wam_dims dav = action_view(d);
+  d = &dav;
   Arena a(nullptr);
   Bufs b;
   plan_action(a, d, B, kv ? std::max(max_len_of(kv, B), kv->cap) : 0, false, b);
@@ -810,6 +824,8 @@ size_t wam_action_workspace_bytes(const wam_dims* d, int B, const wam_kv* kv) {
 
 size_t wam_denoise_workspace_bytes(const wam_dims* d, int B, const wam_kv* kv) {
   if (check_dims(d) || B < 1 || B > WAM_MAX_BATCH) return 0;
+  const wam_dims dav = action_view(d);
+  d = &dav;
   Arena a(nullptr);
   Bufs b;
   plan_action(a, d, B, kv ? std::max(max_len_of(kv, B), kv->cap) : 0, true, b);
@@ -829,6 +845,9 @@ int wam_action_layer(const wam_dims* d, const wam_layer_w* w, float* x, const wa
                      int kv_layer, int B, void* ws, size_t ws_bytes, void* stream) {
   int st;
   if ((st = check_dims(d))) return st;
+  const wam_dims* d_in = d;
+  const wam_dims dav = action_view(d);
+  d = &dav;  // the action expert's shapes from here on
   if (!w || !x) return fail(WAM_E_ARG, "NULL pointer");
   if (!w->g1 || !w->wqkv || !w->wo || !w->g2 || !w->w1 || !w->w2)
     return fail(WAM_E_ARG, "layer has a NULL pointer");
@@ -840,7 +859,7 @@ int wam_action_layer(const wam_dims* d, const wam_layer_w* w, float* x, const wa
     if (kv_layer < 0 || kv_layer >= kv->n_layers) return fail(WAM_E_ARG, "kv_layer out of range");
     if ((st = check_lens(kv, B, &lens))) return st;
   }
-  if (!ws || !aligned16(ws) || ws_bytes < wam_action_workspace_bytes(d, B, kv))
+  if (!ws || !aligned16(ws) || ws_bytes < wam_action_workspace_bytes(d_in, B, kv))
     return fail(WAM_E_WORKSPACE, "workspace missing or too small");
   hipStream_t s = (hipStream_t)stream;
   Arena a(ws);
@@ -875,6 +894,9 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
                       void* stream) {
   int st;
   if ((st = check_dims(d))) return st;
+  const wam_dims* d_in = d;
+  const wam_dims dav = action_view(d);
+  d = &dav;  // the action expert's shapes from here on
   if ((st = check_expert(d, action, "action"))) return st;
   if (!read_map || !eps || !actions_out) return fail(WAM_E_ARG, "NULL pointer");
   if (!aligned16(eps) || !aligned16(actions_out) || (vhat_out && !aligned16(vhat_out)))
@@ -892,7 +914,7 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
     for (int l = 0; l < d->L; l++)
       if (read_map[l] >= kv->n_layers) return fail(WAM_E_ARG, "read_map[%d] out of range", l);
   }
-  if (!ws || !aligned16(ws) || ws_bytes < wam_denoise_workspace_bytes(d, B, any ? kv : nullptr))
+  if (!ws || !aligned16(ws) || ws_bytes < wam_denoise_workspace_bytes(d_in, B, any ? kv : nullptr))
     return fail(WAM_E_WORKSPACE, "workspace missing or too small");
 
   hipStream_t s = (hipStream_t)stream;
@@ -937,7 +959,8 @@ size_t wam_codenoise_workspace_bytes(const wam_dims* d, int B, int Ff, const wam
   Bufs vb, ab;
   float* z;
   plan_prefill(a, d, 0, Ff, vb, &z);
-  plan_action(a, d, B, cache->cap, true, ab);
+  const wam_dims da = action_view(d);
+  plan_action(a, &da, B, cache->cap, true, ab);
   return a.off + 256;
 }
 
@@ -997,21 +1020,22 @@ int wam_codenoise_chunk(const wam_dims* d, const wam_expert_w* video, const wam_
   Bufs vb, ab;
   float* zs;
   plan_prefill(a, d, 0, Ff, vb, &zs);
-  plan_action(a, d, B, cache->cap, true, ab);
+  const wam_dims da = action_view(d);
+  plan_action(a, &da, B, cache->cap, true, ab);
   std::vector<float> sv(N + 1), ta(N + 1);
   schedule(N, sigma_video_end, shift, sv.data());
   schedule(N, 0.0, shift, ta.data());
   const int D = d->D, dt = d->dtype, M = B * d->H, Tf = Ff * P;
   HIPCK(time_embedding(s, sv.data(), N, D, vb.emb));
-  HIPCK(time_embedding(s, ta.data(), N, D, ab.emb));
+  HIPCK(time_embedding(s, ta.data(), N, da.D, ab.emb));
   for (int b = 0; b < B; b++)
     HIPCK(copy_cvt_f32(s, dt, (const char*)fut_noise + (size_t)b * Tf * d->Cv * esz(dt),
                        fut_latents_out + (size_t)b * Tf * d->Cv, (int64_t)Tf * d->Cv));
   HIPCK(hipMemcpyAsync(actions_out, eps, (size_t)M * d->A * 4, hipMemcpyDeviceToDevice, s));
   HIPCK(step_boundary(s, dt, ab.X, nullptr, nullptr, actions_out, 0.f, nullptr, action->w_in,
-                      ab.emb, M, D, d->A, false));
+                      ab.emb, M, da.D, d->A, false));
 
-  Layer cv{s, d, &vb}, ca{s, d, &ab};
+  Layer cv{s, d, &vb}, ca{s, &da, &ab};
   const size_t ls = layer_stride(cache);
   const size_t ep = (size_t)d->Hh * cache->cap * d->dh * esz(dt);  // one episode in a layer
   RowMap zmap;
@@ -1046,7 +1070,7 @@ int wam_codenoise_chunk(const wam_dims* d, const wam_expert_w* video, const wam_
     HIPCK(step_boundary(s, dt, ab.X, action->g_out, action->w_out, actions_out, ta[k + 1] - ta[k],
                         vhat_out ? vhat_out + (size_t)k * M * d->A : nullptr,
                         last ? nullptr : action->w_in,
-                        last ? nullptr : ab.emb + (size_t)(k + 1) * D, M, D, d->A, true));
+                        last ? nullptr : ab.emb + (size_t)(k + 1) * da.D, M, da.D, d->A, true));
   }
   for (int b = 0; b < B; b++) cache->len[b] = lens.len[b];
   return WAM_OK;

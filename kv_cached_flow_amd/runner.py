@@ -39,7 +39,8 @@ class DeviceChunk:
         import torch
         self.cfg = cfg
         self.dt = wam.WAM_BF16 if cfg.dtype == "bf16" else wam.WAM_F32
-        self.dims = wam.dims(cfg.L, cfg.D, cfg.Hh, cfg.dh, cfg.Fm, cfg.Cv, cfg.A, cfg.H, cfg.P, self.dt)
+        self.dims = wam.dims(cfg.L, cfg.D, cfg.Hh, cfg.dh, cfg.Fm, cfg.Cv, cfg.A, cfg.H, cfg.P, self.dt,
+                             cfg.Da, cfg.Fma)
         tdt = _tdt(cfg)
         self.video = upload_expert(inp["video"], cfg, device)
         self.action = upload_expert(inp["action"], cfg, device)

@@ -29,7 +29,8 @@ class WamError(RuntimeError):
 
 
 class WamDims(C.Structure):
-    _fields_ = [(n, C.c_int) for n in ("L", "D", "Hh", "dh", "Fm", "Cv", "A", "H", "P", "dtype")]
+    _fields_ = [(n, C.c_int) for n in ("L", "D", "Hh", "dh", "Fm", "Cv", "A", "H", "P", "dtype", "Da",
+                                        "Fma")]
 
 
 class WamLayerW(C.Structure):
@@ -170,8 +171,9 @@ def frame_table(frame_block: Sequence[int], valid: Optional[Sequence[int]], Fh: 
 
 
 # ------------------------------------------------------------------ device structs
-def dims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype) -> WamDims:
-    return WamDims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype)
+def dims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype, Da=0, Fma=0) -> WamDims:
+    """Shapes of a call; Da / Fma: the action expert's width and MLP width (0: D / Fm)."""
+    return WamDims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype, Da, Fma)
 
 
 class DeviceExpert:

@@ -1,0 +1,48 @@
+"""Experts of different widths over one attention interface (the action
+expert narrower or wider than Hh x dh, its own MLP width) against the oracle,
+for the IDM chunk and for co-denoising."""
+import pytest
+import torch
+
+from kv_cached_flow_amd import configs, inputs
+from kv_cached_flow_amd.runner import DeviceChunk
+from oracle import wam_oracle as O
+from tests._util import gpu_cache_layer, print_case, rel_l2, to_np
+
+pytestmark = pytest.mark.gpu
+
+SMALL = dict(L=2, D=256, Hh=4, dh=64, Fm=512, P=100, Fh=3, Ff=2, frame_block=(0, 1, 2, 3, 4),
+             pad_frames=1, V=2, N=3, read_map=(0, 1))
+
+
+def _run(cfg, inp):
+    dc = DeviceChunk(cfg, inp)
+    dc.run()
+    torch.cuda.synchronize()
+    return dc
+
+
+@pytest.mark.parametrize("dtype,Da,Fma", [("f32", 128, 384), ("bf16", 512, 768), ("bf16", 1024, 256)])
+def test_chunk_with_an_action_expert_of_its_own_width(dtype, Da, Fma):
+    cfg = configs.small("W", dtype=dtype, **dict(SMALL, Da=Da, Fma=Fma))
+    print_case(f"action width {Da}, MLP {Fma}, {dtype}")
+    inp = inputs.generate(cfg)
+    assert inp["action"]["layers"][0]["wqkv"].shape == (3 * cfg.Dq, Da)
+    ref = O.run_chunk(cfg, inp, keep_cache=True)
+    dc = _run(cfg, inp)
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    assert rel_l2(to_np(dc.actions), ref["actions"]) <= tol
+    assert rel_l2(to_np(dc.vhat), ref["vhat"]) <= tol
+    T = cfg.tokens_valid
+    k, v = gpu_cache_layer(dc, 1, 0, T)
+    assert rel_l2(k, ref["cache"][0][1][0].numpy()) <= (1e-5 if dtype == "f32" else 1e-2)
+
+
+def test_codenoise_with_an_action_expert_of_its_own_width():
+    cfg = configs.small("WJ", dtype="bf16", **dict(SMALL, Da=512, Fma=768, joint=True))
+    print_case("co-denoising, action width 512")
+    inp = inputs.generate(cfg)
+    ref = O.run_codenoise(cfg, inp)
+    dc = _run(cfg, inp)
+    assert rel_l2(to_np(dc.actions), ref["actions"]) <= 2e-2
+    assert rel_l2(to_np(dc.z).reshape(ref["z"].shape), ref["z"]) <= 2e-2

@@ -120,6 +120,9 @@ def test_prefill_validation_errors():
     assert call_prefill(d=good_dims(H=16))[0] == -2
     assert call_prefill(d=good_dims(dtype=7))[0] == -1
     assert call_prefill(d=good_dims(Cv=65))[0] == -2
+    assert call_prefill(d=good_dims(Da=100))[0] == -2         # action width not a multiple of 64
+    assert call_prefill(d=good_dims(Fma=-64))[0] == -2
+    assert call_prefill(d=good_dims(Hh=80, D=5120))[0] == -2  # widths above 4096
     assert call_prefill(blocks=(0, 2, 1, 3, 4))[0] == -2      # non-monotone
     assert call_prefill(V=2, sigma=1.0)[0] == -1              # sigma* must be < 1
     assert call_prefill(V=-1)[0] == -1
