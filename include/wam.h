@@ -73,7 +73,7 @@ typedef struct {
   int L;      /* layers per expert */
   int D;      /* video expert width; D == Hh * dh */
   int Hh;     /* attention heads */
-  int dh;     /* head dim; must be 64 */
+  int dh;     /* head dim: 64 or 128 (scores scaled by 1/sqrt(dh)) */
   int Fm;     /* video expert MLP inner width */
   int Cv;     /* channels per video latent token */
   int A;      /* action dims per action token */
@@ -246,7 +246,8 @@ int wam_fuse_interval_kv(const wam_kv* src, int M, const int32_t* start,
  * rounded to nearest even, scale = 2^e.  Codes of rows >= len[b] in the last
  * tile are 0; later tiles are not written.  dst->len is set to src->len.
  *   src: dtype WAM_BF16; dst: dtype WAM_FP8 with the same n_layers, B, Hh,
- *   dh and cap, k_scale and v_scale set.
+ *   dh and cap, k_scale and v_scale set.  dh must be 64 (the E4M3 byte
+ *   order is defined for 64-wide rows).
  * ------------------------------------------------------------------------- */
 int wam_quantize_kv_fp8(const wam_kv* src, wam_kv* dst, void* stream);
 
@@ -367,8 +368,10 @@ int wam_attention_action(int dtype, int B, int Hh, int dh, int H, const void* q,
                          const void* ka, const void* va, int n_act,
                          const void* kc, const void* vc, int cap, const int32_t* len,
                          void* out, int splits_hint, void* ws, size_t ws_bytes, void* stream);
-/* The same over an E4M3 cache layer (layouts and scales [B][Hh][cap/64] as
- * in wam_kv with dtype WAM_FP8); q, ka, va, out bf16.  ws as above (bf16). */
+/* dh is 64 or 128 in both attention entries; WAM_E_SHAPE otherwise.
+ * The same over an E4M3 cache layer (layouts and scales [B][Hh][cap/64] as
+ * in wam_kv with dtype WAM_FP8, dh = 64 only); q, ka, va, out bf16.  ws as
+ * above (bf16). */
 int wam_attention_action_fp8(int B, int Hh, int dh, int H, const void* q, const void* ka,
                              const void* va, int n_act, const void* kc8, const void* vc8,
                              const float* k_scale, const float* v_scale, int cap,
@@ -378,7 +381,7 @@ int wam_attention_action_fp8(int B, int Hh, int dh, int H, const void* q, const 
 /* Block-causal prefill attention for rows row0..row0+nq-1 of one episode's
  * cache layer: q [Hh][nq][dh], kc [Hh][cap][dh], vc [Hh][dh][cap];
  * query row r (cache position row0 + r) sees cache rows 0..kend[(row0+r)/P]-1
- * (kend from wam_frame_table).  out [nq][Hh*dh] dtype. */
+ * (kend from wam_frame_table).  out [nq][Hh*dh] dtype; dh 64 or 128. */
 int wam_attention_prefill(int dtype, int Hh, int dh, int nq, int row0, int P,
                           const int32_t* kend, int n_frames, const void* q,
                           const void* kc, const void* vc, int cap, void* out, void* stream);

@@ -146,6 +146,15 @@ CONFIGS = {
         H=32, B=1, P=880, Fh=24, Ff=2, frame_block=tuple(range(26)), pad_frames=0,
         V=4, sigma_star=0.9, N=4, shift=1.0, read_map=_dense(30), seed=1005,
         joint=True, video_end=0.0),
+    # C1's chunk at the experts' own widths: video expert 3072 wide with
+    # 24 x 128 heads (MLP 4 x 3072: the width is not given, the usual ratio is
+    # taken), action expert 1024 wide (MLP 4096) over the same 24 x 128
+    # attention interface
+    "C6": WamConfig(
+        name="C6", dtype="bf16", L=30, D=3072, Hh=24, dh=128, Fm=12288, Cv=64, A=14,
+        H=32, B=1, P=1024, Fh=1, Ff=8, frame_block=(0,) + (1,) * 8, pad_frames=0,
+        V=0, sigma_star=0.9, N=10, shift=1.0, read_map=_dense(30), seed=1006,
+        Da=1024, Fma=4096),
 }
 
 

@@ -61,14 +61,20 @@ __device__ inline int perm_key(int sub, int r) {
 // no FMA.  The reference max is raised only when a score exceeds it by more
 // than 2^8 in probability, so rescaling is rare; P <= 256 stays exact in bf16
 // and the result does not depend on the reference.
-struct WaveAcc {
-  floatx4 o[5][2];
+// DH: head dim (64 or 128); o[0 .. DH/16 - 1] hold O^T, o[DH/16] the row sums.
+template <int DH>
+struct WaveAccT {
+  static constexpr int ND = DH / 16;  // 16-row head-dim tiles of O^T
+  static constexpr int NS = DH / 32;  // 32-dim k steps of a score MFMA chain
+  floatx4 o[ND + 1][2];
   float m[2];
 };
+using WaveAcc = WaveAccT<64>;
 
-__device__ inline void acc_init(WaveAcc& a) {
+template <int DH>
+__device__ inline void acc_init(WaveAccT<DH>& a) {
 #pragma unroll
-  for (int d = 0; d < 5; d++)
+  for (int d = 0; d <= WaveAccT<DH>::ND; d++)
 #pragma unroll
     for (int t = 0; t < 2; t++) a.o[d][t] = floatx4{0.f, 0.f, 0.f, 0.f};
   a.m[0] = a.m[1] = -INFINITY;
@@ -81,9 +87,10 @@ __device__ inline bf16x8 ones_row(int c16) {
 }
 
 // Row sum of query column (lane & 15) after the last tile (all lanes).
-__device__ inline float acc_rowsum(const WaveAcc& a, int t) {
-  // row 0 of the fifth tile lives in lane group 0, register 0
-  const float v = a.o[4][t][0];
+template <int DH>
+__device__ inline float acc_rowsum(const WaveAccT<DH>& a, int t) {
+  // row 0 of the sums tile lives in lane group 0, register 0
+  const float v = a.o[WaveAccT<DH>::ND][t][0];
   return __shfl(v, threadIdx.x & 15, 64);
 }
 
@@ -106,9 +113,10 @@ __device__ inline void tile_mask(floatx4 (&sacc)[4][2], int kbase, const int (&k
 // uniform) marks a wave's first tile, where every query has a visible key:
 // there m is the tile max itself.  Inlined once per kernel: a second inlined
 // copy makes the register allocator shuffle the accumulators at the join.
-template <typename VOp>
-__device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], bool first, const bf16x8& ones,
-                                   VOp vop) {
+template <int DH, typename VOp>
+__device__ inline void tile_update(WaveAccT<DH>& a, floatx4 (&sacc)[4][2], bool first,
+                                   const bf16x8& ones, VOp vop) {
+  constexpr int ND = WaveAccT<DH>::ND;
   bf16x8 pf[2][2];
 #pragma unroll
   for (int t = 0; t < 2; t++) {
@@ -132,7 +140,7 @@ __device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], bool first
         const float alpha = __builtin_amdgcn_exp2f(a.m[t] - mnew);
         a.m[t] = mnew;
 #pragma unroll
-        for (int d = 0; d < 5; d++) a.o[d][t] *= alpha;
+        for (int d = 0; d <= ND; d++) a.o[d][t] *= alpha;
         delta = need ? mx : 0.f;  // rows without a new max keep their reference
       }
 #pragma unroll
@@ -156,7 +164,7 @@ __device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], bool first
 #pragma unroll
   for (int wd = 0; wd < 2; wd++) {
 #pragma unroll
-    for (int d = 0; d < 4; d++) {
+    for (int d = 0; d < ND; d++) {
       const bf16x8 v = vop(d, wd);
 #pragma unroll
       for (int t = 0; t < 2; t++)
@@ -164,16 +172,17 @@ __device__ inline void tile_update(WaveAcc& a, floatx4 (&sacc)[4][2], bool first
     }
 #pragma unroll
     for (int t = 0; t < 2; t++)
-      a.o[4][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[wd][t], a.o[4][t], 0, 0, 0);
+      a.o[ND][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[wd][t], a.o[ND][t], 0, 0, 0);
   }
 }
 
 // S^T - m for one 64-key tile from K operands kop(sub, s) (16 keys x 32
 // dims): the first MFMA of each subtile starts from -m (from 0 on a wave's
 // first tile, where m is not set yet).
-template <typename KOp>
-__device__ inline void tile_scores(floatx4 (&sacc)[4][2], const bf16x8 (&qf)[2][2], const WaveAcc& a,
-                                   bool first, KOp kop) {
+template <int DH, typename KOp>
+__device__ inline void tile_scores(floatx4 (&sacc)[4][2], const bf16x8 (&qf)[2][DH / 32],
+                                   const WaveAccT<DH>& a, bool first, KOp kop) {
+  constexpr int NS = WaveAccT<DH>::NS;
   floatx4 init[2];
 #pragma unroll
   for (int t = 0; t < 2; t++) {
@@ -182,11 +191,15 @@ __device__ inline void tile_scores(floatx4 (&sacc)[4][2], const bf16x8 (&qf)[2][
   }
 #pragma unroll
   for (int sub = 0; sub < 4; sub++) {
-    const bf16x8 k0 = kop(sub, 0), k1 = kop(sub, 1);
+    bf16x8 kk[NS];
+#pragma unroll
+    for (int s = 0; s < NS; s++) kk[s] = kop(sub, s);
 #pragma unroll
     for (int t = 0; t < 2; t++) {
-      sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[t][0], init[t], 0, 0, 0);
-      sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[t][1], sacc[sub][t], 0, 0, 0);
+      sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[0], qf[t][0], init[t], 0, 0, 0);
+#pragma unroll
+      for (int s = 1; s < NS; s++)
+        sacc[sub][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[s], qf[t][s], sacc[sub][t], 0, 0, 0);
     }
   }
 }
@@ -207,7 +220,6 @@ __device__ inline bf16x8 scale_q(bf16x8 q, float sl2) {
 namespace pf {
 constexpr int QW = 32, NW = 4, QT = QW * NW;  // queries per wave / per workgroup
 constexpr int KT = 64;                        // keys per tile
-constexpr int TILE = KT * 128;                // bytes of one K tile (= one V^T tile)
 constexpr int MAX_SPLIT = 4;                  // key splits per (query tile, head)
 }
 
@@ -238,6 +250,13 @@ __device__ __host__ inline void prefill_split_range(int kend_max, int sp, int ns
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// One 16-byte-per-lane buffer load into LDS (64 lanes fill 1 KiB at lds).
+// A plain function, so that template kernels never hand dependent operands
+// to the builtin (the host pass drops such kernels' launch stubs).
+__device__ inline void buffer_lds16(__amdgpu_buffer_rsrc_t rs, char* lds, unsigned voff, unsigned soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+
 // K and V^T tiles go from global memory straight into LDS (global_load_lds:
 // lane i of a wave fills bytes [16i, 16i+16) of the destination).  Both use
 // 128-byte rows of 8 16-byte chunks, chunk c of row r stored at slot
@@ -245,12 +264,17 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // free of bank conflicts.  K row j of the tile holds the key whose S^T slot is
 // j, so each lane fetches the key that belongs at its LDS position.  Two
 // stages, one barrier per tile.
+template <int DH>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     bf16_t* __restrict__ out, int nq, int row0, int cap, int Hh, FrameTab tab, float sl2,
     int nsplit, float* __restrict__ part) {
   using namespace pf;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE];  // [stage][K | V^T]
+  static_assert(DH == 64 || DH == 128, "head dim");
+  // A K tile is DH/64 halves of 64 keys x 64 dims (128-byte rows), a V^T
+  // tile DH rows of 64 keys: both DH * 128 bytes.
+  constexpr int NS = DH / 32, ND = DH / 16, TB = KT * DH * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];  // [stage][K | V^T]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int ntq = (nq + QT - 1) / QT;
   int h, j;
@@ -264,22 +288,22 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   // tile of every split holds a visible key for every query of the tile.
   int k_lo, k_hi;
   prefill_split_range(kend_max, sp, nsplit, &k_lo, &k_hi);
-  const bf16_t* kh = kc + (long long)h * cap * 64;
-  const bf16_t* vh = vc + (long long)h * 64 * cap;
+  const bf16_t* kh = kc + (long long)h * cap * DH;
+  const bf16_t* vh = vc + (long long)h * DH * cap;
 
   int kq[2];
-  bf16x8 qf[2][2];
+  bf16x8 qf[2][NS];
 #pragma unroll
   for (int t = 0; t < 2; t++) {
     const int qi = q0 + w * QW + 16 * t + c16;
     const bool ok = qi < nq;
     kq[t] = ok ? kend_of_row(tab, row0 + qi) : kend_max;
 #pragma unroll
-    for (int s = 0; s < 2; s++)
-      qf[t][s] = ok ? scale_q(*(const bf16x8*)(q + ((long long)h * nq + qi) * 64 + 32 * s + 8 * g), sl2)
+    for (int s = 0; s < NS; s++)
+      qf[t][s] = ok ? scale_q(*(const bf16x8*)(q + ((long long)h * nq + qi) * DH + 32 * s + 8 * g), sl2)
                     : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
-  WaveAcc acc;
+  WaveAccT<DH> acc;
   acc_init(acc);
   const bf16x8 ones = ones_row(c16);
 
@@ -291,28 +315,33 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   // a fixed per-lane byte offset and the tile's offset in a scalar register,
   // so issuing a tile costs no vector arithmetic.  Offsets stay below 2 GiB
   // (cap * 128 bytes per head).
+  // K half hf (dims 64 hf ..) of tile row `row` holds key perm_key(row): load
+  // (hf, i) fills half hf, rows 8(4i + w) .. +7; V^T load i fills rows 8(4i + w) ..
   const int lrow = lane >> 3, lkc = (lane & 7) ^ lrow;
-  unsigned koff[2], voff[2];
+  constexpr int KH = DH / 64, VL = DH / 32;
+  unsigned koff[KH][2], voff[VL];
 #pragma unroll
   for (int i = 0; i < 2; i++) {
     const int row = (4 * i + w) * 8 + lrow;
-    koff[i] = (unsigned)(perm_key(row >> 4, row & 15) * 64 + lkc * 8) * 2u;
-    voff[i] = (unsigned)(row * cap + lkc * 8) * 2u;
+#pragma unroll
+    for (int hf = 0; hf < KH; hf++)
+      koff[hf][i] = (unsigned)(perm_key(row >> 4, row & 15) * DH + 64 * hf + lkc * 8) * 2u;
   }
+#pragma unroll
+  for (int i = 0; i < VL; i++) voff[i] = (unsigned)(((4 * i + w) * 8 + lrow) * cap + lkc * 8) * 2u;
   const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, 0x7FFFFFFF, 0x00020000);
   const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vh, (short)0, 0x7FFFFFFF, 0x00020000);
   const int wu = __builtin_amdgcn_readfirstlane(w);  // the LDS destinations are scalar
   auto issue = [&](int kt, int buf) {
-    char* sk = smem + buf * 2 * TILE;
-    char* sv = sk + TILE;
+    char* sk = smem + buf * 2 * TB;
+    char* sv = sk + TB;
 #pragma unroll
-    for (int i = 0; i < 2; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(sk + (4 * i + wu) * 1024), 16,
-                                               koff[i], (unsigned)kt * 128u, 0, 0);
+    for (int hf = 0; hf < KH; hf++)
 #pragma unroll
-    for (int i = 0; i < 2; i++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(sv + (4 * i + wu) * 1024), 16,
-                                               voff[i], (unsigned)kt * 2u, 0, 0);
+      for (int i = 0; i < 2; i++)
+        buffer_lds16(krs, sk + hf * 8192 + (4 * i + wu) * 1024, koff[hf][i], (unsigned)kt * (2u * DH));
+#pragma unroll
+    for (int i = 0; i < VL; i++) buffer_lds16(vrs, sv + (4 * i + wu) * 1024, voff[i], (unsigned)kt * 2u);
   };
 
   const int x7 = c16 & 7;
@@ -324,14 +353,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   auto tile = [&](int kt, auto first_tag) {
     constexpr bool FIRST = decltype(first_tag)::value;
     const int buf = (kt / KT) & 1;
-    char* sk = smem + buf * 2 * TILE;
-    char* sv = sk + TILE;
+    char* sk = smem + buf * 2 * TB;
+    char* sv = sk + TB;
     wait_vmem();      // this wave's transfers of the tile have landed in LDS,
     __syncthreads();  // then everyone's
     if (kt + KT > kend_max) {
       // tail tile: V^T columns past kend_max may hold anything (0 * NaN)
 #pragma unroll
-      for (int i = 0; i < 2; i++) {
+      for (int i = 0; i < DH / 32; i++) {
         const int c = tid + 256 * i, row = c >> 3, slot = c & 7, ch = slot ^ (row & 7);
         const int k0 = kt + 8 * ch;
         if (k0 + 8 > kend_max) {
@@ -345,32 +374,40 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
       }
       __syncthreads();
     }
-    bf16x8 kf[4][2], vf[4][2];
+    bf16x8 kf[4][NS], vf[ND][2];
+    auto read_v = [&] {
+#pragma unroll
+      for (int d = 0; d < ND; d++)
+#pragma unroll
+        for (int wd = 0; wd < 2; wd++)
+          vf[d][wd] = *(const bf16x8*)(sv + (16 * d + c16) * 128 + (((4 * wd + g) ^ x7) * 16));
+    };
 #pragma unroll
     for (int sub = 0; sub < 4; sub++)
 #pragma unroll
-      for (int s = 0; s < 2; s++)
-        kf[sub][s] = *(const bf16x8*)(sk + (16 * sub + c16) * 128 + (((4 * s + g) ^ x7) * 16));
-#pragma unroll
-    for (int d = 0; d < 4; d++)
-#pragma unroll
-      for (int wd = 0; wd < 2; wd++)
-        vf[d][wd] = *(const bf16x8*)(sv + (16 * d + c16) * 128 + (((4 * wd + g) ^ x7) * 16));
+      for (int s = 0; s < NS; s++)
+        kf[sub][s] = *(const bf16x8*)(sk + (s >> 1) * 8192 + (16 * sub + c16) * 128 +
+                                      (((4 * (s & 1) + g) ^ x7) * 16));
+    // dh = 64: every fragment read of the tile before its MFMAs; dh = 128
+    // reads V^T after the scores so that K and V^T fragments are never live
+    // together
+    if constexpr (DH == 64) read_v();
     __builtin_amdgcn_sched_barrier(0);
     // the other stage was last read in the previous tile, which every wave has left
     if (kt + KT < k_hi) issue(kt + KT, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     floatx4 sacc[4][2];
     tile_scores(sacc, qf, acc, FIRST, [&](int sub, int s) { return kf[sub][s]; });
+    if constexpr (DH != 64) read_v();
     if (kt + KT > kend_min) tile_mask(sacc, kt, kq, g);
     tile_update(acc, sacc, FIRST, ones, [&](int d, int wd) { return vf[d][wd]; });
   };
   if (k_lo < k_hi) tile(k_lo, std::true_type{});
   for (int kt = k_lo + KT; kt < k_hi; kt += KT) tile(kt, std::false_type{});
-  const int D = Hh * 64;
+  const int D = Hh * DH;
   if (part != nullptr) {
     // split partial (log2-domain max m, row sum l, unnormalised O):
-    // m [nsplit][Hh][nq], l [nsplit][Hh][nq], o [nsplit][Hh][nq][64]
+    // m [nsplit][Hh][nq], l [nsplit][Hh][nq], o [nsplit][Hh][nq][DH]
     const long long plane = (long long)nsplit * Hh * nq;
 #pragma unroll
     for (int t = 0; t < 2; t++) {
@@ -383,8 +420,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
         part[plane + pi] = l;
       }
 #pragma unroll
-      for (int d = 0; d < 4; d++)
-        *(floatx4*)(part + 2 * plane + pi * 64 + 16 * d + 4 * g) = acc.o[d][t];
+      for (int d = 0; d < ND; d++)
+        *(floatx4*)(part + 2 * plane + pi * DH + 16 * d + 4 * g) = acc.o[d][t];
     }
     return;
   }
@@ -395,16 +432,17 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     if (qi >= nq) continue;
     const float inv = 1.0f / l;
 #pragma unroll
-    for (int d = 0; d < 4; d++) {
+    for (int d = 0; d < ND; d++) {
       uint2 v = {pack_bf16x2(acc.o[d][t][0] * inv, acc.o[d][t][1] * inv),
                  pack_bf16x2(acc.o[d][t][2] * inv, acc.o[d][t][3] * inv)};
-      *(uint2*)(out + (long long)qi * D + h * 64 + 16 * d + 4 * g) = v;
+      *(uint2*)(out + (long long)qi * D + h * DH + 16 * d + 4 * g) = v;
     }
   }
 }
 
 // Merge of the key splits of one launch: one wavefront per (query, head),
 // lane = head-dim index, splits combined in a fixed order.
+template <int DH>
 __global__ __launch_bounds__(256) void attn_prefill_merge_kernel(const float* __restrict__ part,
                                                                  int nsplit, int Hh, int nq,
                                                                  bf16_t* __restrict__ out) {
@@ -412,33 +450,40 @@ __global__ __launch_bounds__(256) void attn_prefill_merge_kernel(const float* __
   if (wv >= nq * Hh) return;
   const int qi = wv / Hh, h = wv - qi * Hh;
   const long long plane = (long long)nsplit * Hh * nq;
-  float mv[pf::MAX_SPLIT], lv[pf::MAX_SPLIT], ov[pf::MAX_SPLIT];
+  float mv[pf::MAX_SPLIT], lv[pf::MAX_SPLIT], ov[pf::MAX_SPLIT][DH / 64];
 #pragma unroll
   for (int s = 0; s < pf::MAX_SPLIT; s++) {
     if (s < nsplit) {
       const long long pi = ((long long)s * Hh + h) * nq + qi;
       mv[s] = part[pi];
       lv[s] = part[plane + pi];
-      ov[s] = part[2 * plane + pi * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < DH / 64; r++) ov[s][r] = part[2 * plane + pi * DH + 64 * r + lane];
     }
   }
   float M = mv[0];
 #pragma unroll
   for (int s = 1; s < pf::MAX_SPLIT; s++)
     if (s < nsplit) M = fmaxf(M, mv[s]);
-  float L = 0.f, O = 0.f;
+  float L = 0.f, O[DH / 64];
+#pragma unroll
+  for (int r = 0; r < DH / 64; r++) O[r] = 0.f;
 #pragma unroll
   for (int s = 0; s < pf::MAX_SPLIT; s++) {
     if (s < nsplit) {
       const float f = __builtin_amdgcn_exp2f(mv[s] - M);
       L = fmaf(lv[s], f, L);
-      O = fmaf(ov[s], f, O);
+#pragma unroll
+      for (int r = 0; r < DH / 64; r++) O[r] = fmaf(ov[s][r], f, O[r]);
     }
   }
-  out[(long long)qi * Hh * 64 + h * 64 + lane] = dev_f2bf(O / L);
+#pragma unroll
+  for (int r = 0; r < DH / 64; r++)
+    out[(long long)qi * Hh * DH + h * DH + 64 * r + lane] = dev_f2bf(O[r] / L);
 }
 
 // fp32: one thread per (query, head)
+template <int DH>
 __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(const float* __restrict__ q,
                                                               const float* __restrict__ kc,
                                                               const float* __restrict__ vc,
@@ -448,30 +493,37 @@ __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(const float* __res
   const int h = blockIdx.y;
   const int qi = blockIdx.x * 64 + threadIdx.x;
   if (qi >= nq) return;
-  const float* qr = q + ((long long)h * nq + qi) * 64;
-  const float* kh = kc + (long long)h * cap * 64;
-  const float* vh = vc + (long long)h * 64 * cap;
-  float qv[64], o[64];
+  const float* qr = q + ((long long)h * nq + qi) * DH;
+  const float* kh = kc + (long long)h * cap * DH;
+  const float* vh = vc + (long long)h * DH * cap;
+  float qv[DH], o[DH];
 #pragma unroll
-  for (int d = 0; d < 64; d++) { qv[d] = qr[d]; o[d] = 0.f; }
+  for (int d = 0; d < DH; d++) { qv[d] = qr[d]; o[d] = 0.f; }
   const int kend = kend_of_row(tab, row0 + qi);
   float m = -INFINITY, l = 0.f;
   for (int j = 0; j < kend; j++) {
     float s = 0.f;
 #pragma unroll
-    for (int d = 0; d < 64; d++) s = fmaf(qv[d], kh[(long long)j * 64 + d], s);
-    s *= scale;
-    const float mn = fmaxf(m, s);
-    const float a = expf(m - mn), p = expf(s - mn);
+    for (int d = 0; d < DH; d++) s = fmaf(qv[d], kh[(long long)j * DH + d], s);
+    float mn, a, p;
+    {
+      // the scaled score is rounded once and never fused into s - mn: the
+      // largest key then weighs exactly 1
+#pragma clang fp contract(off)
+      s = s * scale;
+      mn = fmaxf(m, s);
+      a = expf(m - mn);
+      p = expf(s - mn);
+    }
     l = l * a + p;
 #pragma unroll
-    for (int d = 0; d < 64; d++) o[d] = fmaf(p, vh[(long long)d * cap + j], o[d] * a);
+    for (int d = 0; d < DH; d++) o[d] = fmaf(p, vh[(long long)d * cap + j], o[d] * a);
     m = mn;
   }
   const float inv = 1.0f / l;
-  float* orow = out + (long long)qi * Hh * 64 + h * 64;
+  float* orow = out + (long long)qi * Hh * DH + h * DH;
 #pragma unroll
-  for (int d = 0; d < 64; d++) orow[d] = o[d] * inv;
+  for (int d = 0; d < DH; d++) orow[d] = o[d] * inv;
 }
 
 static int device_cus() {
@@ -482,12 +534,12 @@ static int device_cus() {
   return n_cu;
 }
 
-size_t attn_prefill_split_bytes(int Hh, int max_rows) {
+size_t attn_prefill_split_bytes(int Hh, int dh, int max_rows) {
   // a launch splits only below 2 workgroups per CU, so splits x workgroups
   // stays below 4 per CU: at most 4 n_cu QT (query, head, split) partials
   const long long n = std::min<long long>((long long)pf::MAX_SPLIT * Hh * max_rows,
                                           4ll * device_cus() * pf::QT);
-  return (size_t)n * 66 * sizeof(float);
+  return (size_t)n * (dh + 2) * sizeof(float);
 }
 
 // Key splits of a launch: enough (query tile, head, split) workgroups for two
@@ -496,13 +548,13 @@ size_t attn_prefill_split_bytes(int Hh, int max_rows) {
 // tile loop takes a split's first tile as setting the reference max).  Under
 // the block-causal mask a query sees a key prefix, so that holds when the
 // last split starts below the tile's smallest prefix end.
-static int prefill_splits(int Hh, int nq, int row0, const FrameTab& tab, size_t part_bytes) {
+static int prefill_splits(int Hh, int dh, int nq, int row0, const FrameTab& tab, size_t part_bytes) {
   const int ntq = (nq + pf::QT - 1) / pf::QT, n_cu = device_cus();
   const long long g = (long long)ntq * Hh;
   if (g >= 2ll * n_cu) return 1;
   int S = (int)std::min<long long>(pf::MAX_SPLIT, (2ll * n_cu + g - 1) / g);
   for (; S > 1; S--) {
-    if ((size_t)S * Hh * nq * 66 * sizeof(float) > part_bytes) continue;
+    if ((size_t)S * Hh * nq * (dh + 2) * sizeof(float) > part_bytes) continue;
     bool ok = true;
     for (int qt = 0; qt < ntq && ok; qt++) {
       const int q0 = qt * pf::QT, ql = std::min(q0 + pf::QT, nq) - 1;
@@ -516,10 +568,12 @@ static int prefill_splits(int Hh, int nq, int row0, const FrameTab& tab, size_t 
   return S;
 }
 
-hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int nq, int row0, const FrameTab& tab,
-                        const void* q, const void* kc, const void* vc, int cap, void* out,
-                        float* part, size_t part_bytes) {
+hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int dh, int nq, int row0,
+                        const FrameTab& tab, const void* q, const void* kc, const void* vc, int cap,
+                        void* out, float* part, size_t part_bytes) {
   if (nq <= 0) return hipSuccess;
+  if (dh != 64 && dh != 128) return hipErrorInvalidValue;
+  const float scale = dh == 64 ? 0.125f : 0.08838834764831845f;  // 1 / sqrt(dh)
   double pairs = 0.0;  // visible (query, key) pairs
   for (int r = row0; r < row0 + nq;) {
     int f = r / tab.P, e = std::min(row0 + nq, (f + 1) * tab.P);
@@ -529,30 +583,44 @@ hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int nq, int row0, const F
   const int es = dt == WAM_BF16 ? 2 : 4;
   const int kmax = tab.kend[(row0 + nq - 1) / tab.P];
   if (dt == WAM_BF16) {
-    const int nsplit = part ? prefill_splits(Hh, nq, row0, tab, part_bytes) : 1;
+    const int nsplit = part ? prefill_splits(Hh, dh, nq, row0, tab, part_bytes) : 1;
     {
-      TimingScope ts(s, KC_ATTN_PREFILL, (double)Hh * 64 * es * (2.0 * nq + 2.0 * kmax),
-                     4.0 * 64 * Hh * pairs);
+      TimingScope ts(s, KC_ATTN_PREFILL, (double)Hh * dh * es * (2.0 * nq + 2.0 * kmax),
+                     4.0 * dh * Hh * pairs);
       dim3 grid(((nq + pf::QT - 1) / pf::QT) * Hh * nsplit);
-      hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, (const bf16_t*)q,
-                         (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)out, nq, row0, cap, Hh,
-                         tab, 0.125f * LOG2E, nsplit, nsplit > 1 ? part : nullptr);
+      if (dh == 64)
+        hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), 0, s, (const bf16_t*)q,
+                           (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)out, nq, row0, cap, Hh,
+                           tab, scale * LOG2E, nsplit, nsplit > 1 ? part : nullptr);
+      else
+        hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)q,
+                           (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)out, nq, row0, cap, Hh,
+                           tab, scale * LOG2E, nsplit, nsplit > 1 ? part : nullptr);
     }
     if (nsplit > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      TimingScope ts(s, KC_ATTN_MERGE, (double)nsplit * Hh * nq * 66 * 4 + (double)nq * Hh * 64 * es,
-                     0.0);
-      hipLaunchKernelGGL(attn_prefill_merge_kernel, dim3((nq * Hh + 3) / 4), dim3(256), 0, s,
-                         (const float*)part, nsplit, Hh, nq, (bf16_t*)out);
+      TimingScope ts(s, KC_ATTN_MERGE,
+                     (double)nsplit * Hh * nq * (dh + 2) * 4 + (double)nq * Hh * dh * es, 0.0);
+      if (dh == 64)
+        hipLaunchKernelGGL(attn_prefill_merge_kernel<64>, dim3((nq * Hh + 3) / 4), dim3(256), 0, s,
+                           (const float*)part, nsplit, Hh, nq, (bf16_t*)out);
+      else
+        hipLaunchKernelGGL(attn_prefill_merge_kernel<128>, dim3((nq * Hh + 3) / 4), dim3(256), 0,
+                           s, (const float*)part, nsplit, Hh, nq, (bf16_t*)out);
     }
   } else {
-    TimingScope ts(s, KC_ATTN_PREFILL, (double)Hh * 64 * es * (2.0 * nq + 2.0 * kmax),
-                   4.0 * 64 * Hh * pairs);
+    TimingScope ts(s, KC_ATTN_PREFILL, (double)Hh * dh * es * (2.0 * nq + 2.0 * kmax),
+                   4.0 * dh * Hh * pairs);
     dim3 grid((nq + 63) / 64, Hh);
-    hipLaunchKernelGGL(attn_prefill_f32_kernel, grid, dim3(64), 0, s, (const float*)q,
-                       (const float*)kc, (const float*)vc, (float*)out, nq, row0, cap, Hh, tab,
-                       0.125f);
+    if (dh == 64)
+      hipLaunchKernelGGL(attn_prefill_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q,
+                         (const float*)kc, (const float*)vc, (float*)out, nq, row0, cap, Hh, tab,
+                         scale);
+    else
+      hipLaunchKernelGGL(attn_prefill_f32_kernel<128>, grid, dim3(64), 0, s, (const float*)q,
+                         (const float*)kc, (const float*)vc, (float*)out, nq, row0, cap, Hh, tab,
+                         scale);
   }
   return hipGetLastError();
 }
@@ -581,6 +649,30 @@ __device__ inline bf16x8 e4m3x8_bf16(unsigned lo, unsigned hi, float scale) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// One 64-key tile of bf16 K rows (A of S^T) and V^T rows (A of P V), all
+// loads unconditional so that they are in flight together: K rows past key1
+// read row key1 - 1 (their scores are masked to -inf), V^T chunks that start
+// past key1 read the row's first chunk (zeroed by the caller).
+template <int DH>
+__device__ inline void bf16_tiles(bf16x8 (&ak)[4][DH / 32], bf16x8 (&av)[DH / 16][2],
+                                  const bf16_t* kb, const bf16_t* vb, int kt, int key0, int key1,
+                                  int vld, int c16, int g) {
+#pragma unroll
+  for (int sub = 0; sub < 4; sub++) {
+    const int key = min(kt + perm_key(sub, c16), key1 - 1);
+#pragma unroll
+    for (int ss = 0; ss < DH / 32; ss++)
+      ak[sub][ss] = *(const bf16x8*)(kb + (long long)key * DH + 32 * ss + 8 * g);
+  }
+#pragma unroll
+  for (int d = 0; d < DH / 16; d++)
+#pragma unroll
+    for (int wd = 0; wd < 2; wd++) {
+      const int k0 = kt + 32 * wd + 8 * g;
+      av[d][wd] = *(const bf16x8*)(vb + (long long)(16 * d + c16) * vld + (k0 < key1 ? k0 : key0));
+    }
+}
+
 // Split (b, h, s): cache keys [s*kc[b], min(len, (s+1)*kc[b])) for s < ncs(b),
 // the chunk's own keys for s == ncs(b).  Writes the split's (m, l, o) in the
 // log2 domain: m [32], l [32], o [32][64] (unnormalised).
@@ -590,14 +682,17 @@ __device__ inline bf16x8 e4m3x8_bf16(unsigned lo, unsigned hi, float scale) {
 // 32+8g..) or of a V^T row (keys 8g.. and 32+8g.. of the tile); converted
 // with the tile's scale they are the bf16 operands of the same MFMAs.  The
 // chunk's own keys stay bf16.
-template <bool F8>
-__global__ __launch_bounds__(256, 2) void attn_action_kernel(
+template <bool F8, int DH>
+__global__ __launch_bounds__(256, DH == 64 ? 2 : 1) void attn_action_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ ka, const bf16_t* __restrict__ va,
     const void* __restrict__ kc, const void* __restrict__ vc, const float* __restrict__ ksc,
     const float* __restrict__ vsc, ActGeom G, float* __restrict__ part, float sl2) {
   using namespace act;
+  static_assert(DH == 64 || DH == 128, "head dim");
+  static_assert(!F8 || DH == 64, "the E4M3 cache layout is for dh = 64");
+  constexpr int NS = DH / 32, ND = DH / 16;
   __shared__ float sm[4][H], sl[4][H];
-  __shared__ float so[4][H][65];
+  __shared__ float so[4][H][DH + 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int len = G.lens.len[b];
@@ -614,8 +709,8 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
   int key0, key1, vld;
   if (!own) {
     const long long hb = (long long)b * G.Hh + h;
-    kb = (const bf16_t*)kc + hb * G.cap * 64;
-    vb = (const bf16_t*)vc + hb * 64 * G.cap;
+    kb = (const bf16_t*)kc + hb * G.cap * DH;
+    vb = (const bf16_t*)vc + hb * DH * G.cap;
     if constexpr (F8) {
       k8 = (const uint8_t*)kc + hb * G.cap * 64;
       v8 = (const uint8_t*)vc + hb * 64 * G.cap;
@@ -626,22 +721,22 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
     key1 = min(len, key0 + chunk);
     vld = G.cap;
   } else {
-    kb = ka + ((long long)b * G.Hh + h) * H * 64;
-    vb = va + ((long long)b * G.Hh + h) * 64 * H;
+    kb = ka + ((long long)b * G.Hh + h) * H * DH;
+    vb = va + ((long long)b * G.Hh + h) * DH * H;
     key0 = 0;
     key1 = G.n_act;
     vld = H;
   }
   // queries: B operand of S^T = K Q^T
-  bf16x8 qf[2][2];
-  const bf16_t* qb = q + ((long long)b * G.Hh + h) * H * 64;
+  bf16x8 qf[2][NS];
+  const bf16_t* qb = q + ((long long)b * G.Hh + h) * H * DH;
 #pragma unroll
   for (int t = 0; t < 2; t++)
 #pragma unroll
-    for (int ss = 0; ss < 2; ss++)
-      qf[t][ss] = scale_q(*(const bf16x8*)(qb + (16 * t + c16) * 64 + 32 * ss + 8 * g), sl2);
+    for (int ss = 0; ss < NS; ss++)
+      qf[t][ss] = scale_q(*(const bf16x8*)(qb + (16 * t + c16) * DH + 32 * ss + 8 * g), sl2);
 
-  WaveAcc acc;
+  WaveAccT<DH> acc;
   acc_init(acc);
   const bf16x8 ones = ones_row(c16);
   const int kq[2] = {key1, key1};
@@ -650,8 +745,9 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
     // unconditional so that they are in flight together: K rows past key1
     // read row key1 - 1 (their scores are masked to -inf), V^T chunks that
     // start past key1 read the row's first chunk and are zeroed below.
-    bf16x8 ak[4][2], av[4][2];
-    if (F8 && !own) {
+    bf16x8 ak[4][NS], av[ND][2];
+    if constexpr (F8) {
+    if (!own) {
       // E4M3 tile: kt is a multiple of 64 (splits are whole tiles), and the
       // 16-byte V^T reads stay inside the tile, hence below cap; keys past
       // key1 are zeroed below like the bf16 ones
@@ -676,20 +772,10 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
         av[d][1] = e4m3x8_bf16(rv[d][2], rv[d][3], sv);
       }
     } else {
-#pragma unroll
-      for (int sub = 0; sub < 4; sub++) {
-        const int key = min(kt + perm_key(sub, c16), key1 - 1);
-#pragma unroll
-        for (int ss = 0; ss < 2; ss++)
-          ak[sub][ss] = *(const bf16x8*)(kb + (long long)key * 64 + 32 * ss + 8 * g);
-      }
-#pragma unroll
-      for (int d = 0; d < 4; d++)
-#pragma unroll
-        for (int wd = 0; wd < 2; wd++) {
-          const int k0 = kt + 32 * wd + 8 * g;
-          av[d][wd] = *(const bf16x8*)(vb + (long long)(16 * d + c16) * vld + (k0 < key1 ? k0 : key0));
-        }
+      bf16_tiles<DH>(ak, av, kb, vb, kt, key0, key1, vld, c16, g);
+    }
+    } else {
+      bf16_tiles<DH>(ak, av, kb, vb, kt, key0, key1, vld, c16, g);
     }
     const bool tail = kt + KT > key1;  // wave-uniform
     if (tail) {
@@ -701,7 +787,7 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
         for (int j = 0; j < 8; j++)
           if (k0 + j >= key1)
 #pragma unroll
-            for (int d = 0; d < 4; d++) av[d][wd][j] = 0;
+            for (int d = 0; d < ND; d++) av[d][wd][j] = 0;
       }
     }
     // ---- S^T, softmax, P V
@@ -721,7 +807,7 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
       sl[w][qi] = l;
     }
 #pragma unroll
-    for (int d = 0; d < 4; d++)
+    for (int d = 0; d < ND; d++)
 #pragma unroll
       for (int r = 0; r < 4; r++) so[w][qi][16 * d + 4 * g + r] = acc.o[d][t][r];
   }
@@ -730,9 +816,9 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
   const long long pidx = (((long long)b * G.Hh + h) * G.S + s);
   float* pm = part + pidx * H;
   float* pl = part + (long long)G.B * G.Hh * G.S * H + pidx * H;
-  float* po = part + 2ll * G.B * G.Hh * G.S * H + pidx * H * 64;
-  for (int i = tid; i < H * 64; i += 256) {
-    const int qi = i >> 6, d = i & 63;
+  float* po = part + 2ll * G.B * G.Hh * G.S * H + pidx * H * DH;
+  for (int i = tid; i < H * DH; i += 256) {
+    const int qi = i / DH, d = i % DH;
     float M = sm[0][qi];
 #pragma unroll
     for (int ww = 1; ww < 4; ww++) M = fmaxf(M, sm[ww][qi]);
@@ -744,7 +830,7 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
       L += sl[ww][qi] * f;
       O += so[ww][qi][d] * f;
     }
-    po[qi * 64 + d] = O;
+    po[qi * DH + d] = O;
     if (d == 0) {
       pm[qi] = M;  // log2 units, as the split merge expects
       pl[qi] = L;
@@ -755,7 +841,7 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
 // Merge splits 0..ns-1 of (b, h) (ns <= 64): one wavefront per (query, head,
 // episode).  Lane j reads split j's (m, l); lane d reads every split's o[d];
 // all loads are issued before any arithmetic.  Fixed reduction order.
-template <typename TO>
+template <typename TO, int DH>
 __global__ __launch_bounds__(64) void attn_action_merge_kernel(const float* __restrict__ part,
                                                                ActGeom G, TO* __restrict__ out) {
   using namespace act;
@@ -766,12 +852,8 @@ __global__ __launch_bounds__(64) void attn_action_merge_kernel(const float* __re
   const long long base = ((long long)b * G.Hh + h) * G.S;
   const float* pm = part + base * H + qi;
   const float* pl = part + (long long)G.B * G.Hh * G.S * H + base * H + qi;
-  const float* po = part + 2ll * G.B * G.Hh * G.S * H + (base * H + qi) * 64 + lane;
   const float mj = lane < ns ? pm[lane * H] : -INFINITY;
   const float lj = lane < ns ? pl[lane * H] : 0.f;
-  float ov[MAX_SPLITS];
-#pragma unroll
-  for (int j = 0; j < MAX_SPLITS; j++) ov[j] = (j < ns) ? po[(long long)j * H * 64] : 0.f;
   float M = mj;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
@@ -779,14 +861,24 @@ __global__ __launch_bounds__(64) void attn_action_merge_kernel(const float* __re
   float L = lj * wj;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
-  float O = 0.f;
+  // lane d takes head dims d, d + 64, ..
 #pragma unroll
-  for (int j = 0; j < MAX_SPLITS; j++)
-    if (j < ns) O = fmaf(__shfl(wj, j, 64), ov[j], O);
-  out[((long long)b * H + qi) * G.Hh * 64 + h * 64 + lane] = from_f<TO>(O / L);
+  for (int r = 0; r < DH / 64; r++) {
+    const float* po =
+        part + 2ll * G.B * G.Hh * G.S * H + (base * H + qi) * DH + 64 * r + lane;
+    float ov[MAX_SPLITS];
+#pragma unroll
+    for (int j = 0; j < MAX_SPLITS; j++) ov[j] = (j < ns) ? po[(long long)j * H * DH] : 0.f;
+    float O = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAX_SPLITS; j++)
+      if (j < ns) O = fmaf(__shfl(wj, j, 64), ov[j], O);
+    out[((long long)b * H + qi) * G.Hh * DH + h * DH + 64 * r + lane] = from_f<TO>(O / L);
+  }
 }
 
 // fp32: one thread per (episode, head, query)
+template <int DH>
 __global__ __launch_bounds__(64) void attn_action_f32_kernel(const float* __restrict__ q,
                                                              const float* __restrict__ ka,
                                                              const float* __restrict__ va,
@@ -797,10 +889,10 @@ __global__ __launch_bounds__(64) void attn_action_f32_kernel(const float* __rest
   using namespace act;
   const int h = blockIdx.x, b = blockIdx.y, qi = threadIdx.x;
   if (qi >= H) return;
-  const float* qr = q + (((long long)b * G.Hh + h) * H + qi) * 64;
-  float qv[64], o[64];
+  const float* qr = q + (((long long)b * G.Hh + h) * H + qi) * DH;
+  float qv[DH], o[DH];
 #pragma unroll
-  for (int d = 0; d < 64; d++) { qv[d] = qr[d]; o[d] = 0.f; }
+  for (int d = 0; d < DH; d++) { qv[d] = qr[d]; o[d] = 0.f; }
   float m = -INFINITY, l = 0.f;
   for (int part = 0; part < 2; part++) {
     const float* kb;
@@ -808,33 +900,40 @@ __global__ __launch_bounds__(64) void attn_action_f32_kernel(const float* __rest
     int n, ld;
     if (part == 0) {
       if (!kc) continue;
-      kb = kc + ((long long)b * G.Hh + h) * G.cap * 64;
-      vb = vc + ((long long)b * G.Hh + h) * 64 * G.cap;
+      kb = kc + ((long long)b * G.Hh + h) * G.cap * DH;
+      vb = vc + ((long long)b * G.Hh + h) * DH * G.cap;
       n = G.lens.len[b];
       ld = G.cap;
     } else {
-      kb = ka + ((long long)b * G.Hh + h) * H * 64;
-      vb = va + ((long long)b * G.Hh + h) * 64 * H;
+      kb = ka + ((long long)b * G.Hh + h) * H * DH;
+      vb = va + ((long long)b * G.Hh + h) * DH * H;
       n = G.n_act;
       ld = H;
     }
     for (int j = 0; j < n; j++) {
       float s = 0.f;
 #pragma unroll
-      for (int d = 0; d < 64; d++) s = fmaf(qv[d], kb[(long long)j * 64 + d], s);
-      s *= scale;
-      const float mn = fmaxf(m, s);
-      const float a = expf(m - mn), p = expf(s - mn);
+      for (int d = 0; d < DH; d++) s = fmaf(qv[d], kb[(long long)j * DH + d], s);
+      float mn, a, p;
+      {
+        // the scaled score is rounded once and never fused into s - mn: the
+        // largest key then weighs exactly 1
+#pragma clang fp contract(off)
+        s = s * scale;
+        mn = fmaxf(m, s);
+        a = expf(m - mn);
+        p = expf(s - mn);
+      }
       l = l * a + p;
 #pragma unroll
-      for (int d = 0; d < 64; d++) o[d] = fmaf(p, vb[(long long)d * ld + j], o[d] * a);
+      for (int d = 0; d < DH; d++) o[d] = fmaf(p, vb[(long long)d * ld + j], o[d] * a);
       m = mn;
     }
   }
   const float inv = 1.0f / l;
-  float* orow = out + ((long long)b * H + qi) * G.Hh * 64 + h * 64;
+  float* orow = out + ((long long)b * H + qi) * G.Hh * DH + h * DH;
 #pragma unroll
-  for (int d = 0; d < 64; d++) orow[d] = o[d] * inv;
+  for (int d = 0; d < DH; d++) orow[d] = o[d] * inv;
 }
 
 // Keys per split for one episode: a function of that episode's length, the
@@ -857,19 +956,21 @@ static int action_chunk(int len, int Hh, int splits_hint) {
   return (kc + act::KT - 1) / act::KT * act::KT;
 }
 
-size_t attn_action_scratch_bytes(int B, int Hh, int H, int max_len, int splits_hint) {
+size_t attn_action_scratch_bytes(int B, int Hh, int H, int dh, int max_len, int splits_hint) {
+  (void)max_len;
   (void)splits_hint;
-  return (size_t)B * Hh * act::MAX_SPLITS * H * (64 + 2) * sizeof(float);
+  return (size_t)B * Hh * act::MAX_SPLITS * H * (dh + 2) * sizeof(float);
 }
 
-hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* q,
+hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, int dh, const void* q,
                        const void* ka, const void* va, int n_act, const void* kc,
                        const void* vc, int cap, const ActLens& lens, void* out,
                        int splits_hint, void* scratch, size_t scratch_bytes, const float* ksc,
                        const float* vsc) {
   const bool f8 = ksc != nullptr;
   if (f8 && (dt != WAM_BF16 || !vsc || !kc)) return hipErrorInvalidValue;
-  if (H != act::H) return hipErrorInvalidValue;
+  if (H != act::H || (dh != 64 && dh != 128) || (f8 && dh != 64)) return hipErrorInvalidValue;
+  const float scale = dh == 64 ? 0.125f : 0.08838834764831845f;  // 1 / sqrt(dh)
   ActGeom G;
   G.B = B;
   G.Hh = Hh;
@@ -886,39 +987,53 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* 
   for (int b = 0; b < B; b++) G.kc[b] = kc ? action_chunk(G.lens.len[b], Hh, splits_hint) : 0;
   if (dt == WAM_F32) {
     G.S = 0;
-    TimingScope ts(s, KC_ATTN_ACTION, keys * Hh * 64 * 2 * es + 2.0 * B * H * Hh * 64 * es,
-                   4.0 * 64 * Hh * H * keys);
-    hipLaunchKernelGGL(attn_action_f32_kernel, dim3(Hh, B), dim3(64), 0, s, (const float*)q,
-                       (const float*)ka, (const float*)va, (const float*)kc, (const float*)vc,
-                       G, (float*)out, 0.125f);
+    TimingScope ts(s, KC_ATTN_ACTION, keys * Hh * dh * 2 * es + 2.0 * B * H * Hh * dh * es,
+                   4.0 * dh * Hh * H * keys);
+    if (dh == 64)
+      hipLaunchKernelGGL(attn_action_f32_kernel<64>, dim3(Hh, B), dim3(64), 0, s, (const float*)q,
+                         (const float*)ka, (const float*)va, (const float*)kc, (const float*)vc,
+                         G, (float*)out, scale);
+    else
+      hipLaunchKernelGGL(attn_action_f32_kernel<128>, dim3(Hh, B), dim3(64), 0, s, (const float*)q,
+                         (const float*)ka, (const float*)va, (const float*)kc, (const float*)vc,
+                         G, (float*)out, scale);
     return hipGetLastError();
   }
   G.S = 1;
   for (int b = 0; b < B; b++)
     if (G.kc[b] > 0) G.S = std::max(G.S, (G.lens.len[b] + G.kc[b] - 1) / G.kc[b] + 1);
-  if (scratch_bytes < (size_t)B * Hh * G.S * H * 66 * sizeof(float)) return hipErrorInvalidValue;
+  if (scratch_bytes < (size_t)B * Hh * G.S * H * (dh + 2) * sizeof(float)) return hipErrorInvalidValue;
   {
     double cached = 0.0;
     for (int b = 0; b < B; b++) cached += G.lens.len[b];
-    const double kv_bytes = cached * Hh * 64 * 2 * ces + (double)B * n_act * Hh * 64 * 2 * es +
+    const double kv_bytes = cached * Hh * dh * 2 * ces + (double)B * n_act * Hh * dh * 2 * es +
                             (f8 ? 2.0 * 4 * Hh * (cached / 64.0) : 0.0);
-    TimingScope ts(s, KC_ATTN_ACTION, kv_bytes + 1.0 * B * H * Hh * 64 * es,
-                   4.0 * 64 * Hh * H * keys);
+    TimingScope ts(s, KC_ATTN_ACTION, kv_bytes + 1.0 * B * H * Hh * dh * es,
+                   4.0 * dh * Hh * H * keys);
+    const float sl2 = scale * LOG2E;
     if (f8)
-      hipLaunchKernelGGL(attn_action_kernel<true>, dim3(G.S, Hh, B), dim3(256), 0, s,
+      hipLaunchKernelGGL((attn_action_kernel<true, 64>), dim3(G.S, Hh, B), dim3(256), 0, s,
                          (const bf16_t*)q, (const bf16_t*)ka, (const bf16_t*)va, kc, vc, ksc, vsc,
-                         G, (float*)scratch, 0.125f * LOG2E);
-    else
-      hipLaunchKernelGGL(attn_action_kernel<false>, dim3(G.S, Hh, B), dim3(256), 0, s,
+                         G, (float*)scratch, sl2);
+    else if (dh == 64)
+      hipLaunchKernelGGL((attn_action_kernel<false, 64>), dim3(G.S, Hh, B), dim3(256), 0, s,
                          (const bf16_t*)q, (const bf16_t*)ka, (const bf16_t*)va, kc, vc,
-                         (const float*)nullptr, (const float*)nullptr, G, (float*)scratch,
-                         0.125f * LOG2E);
+                         (const float*)nullptr, (const float*)nullptr, G, (float*)scratch, sl2);
+    else
+      hipLaunchKernelGGL((attn_action_kernel<false, 128>), dim3(G.S, Hh, B), dim3(256), 0, s,
+                         (const bf16_t*)q, (const bf16_t*)ka, (const bf16_t*)va, kc, vc,
+                         (const float*)nullptr, (const float*)nullptr, G, (float*)scratch, sl2);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  TimingScope ts(s, KC_ATTN_MERGE, (double)B * Hh * G.S * H * 66 * 4 + (double)B * H * Hh * 64 * es, 0.0);
-  hipLaunchKernelGGL(attn_action_merge_kernel<bf16_t>, dim3(H, Hh, B), dim3(64), 0, s,
-                     (const float*)scratch, G, (bf16_t*)out);
+  TimingScope ts(s, KC_ATTN_MERGE,
+                 (double)B * Hh * G.S * H * (dh + 2) * 4 + (double)B * H * Hh * dh * es, 0.0);
+  if (dh == 64)
+    hipLaunchKernelGGL((attn_action_merge_kernel<bf16_t, 64>), dim3(H, Hh, B), dim3(64), 0, s,
+                       (const float*)scratch, G, (bf16_t*)out);
+  else
+    hipLaunchKernelGGL((attn_action_merge_kernel<bf16_t, 128>), dim3(H, Hh, B), dim3(64), 0, s,
+                       (const float*)scratch, G, (bf16_t*)out);
   return hipGetLastError();
 }
 

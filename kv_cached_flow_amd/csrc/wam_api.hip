@@ -55,7 +55,7 @@ int check_dims(const wam_dims* d) {
   if (d->dtype != WAM_F32 && d->dtype != WAM_BF16) return fail(WAM_E_ARG, "bad dtype %d", d->dtype);
   if (d->L < 1 || d->D < 1 || d->Hh < 1 || d->Fm < 1 || d->P < 1)
     return fail(WAM_E_SHAPE, "non-positive dimension");
-  if (d->dh != 64) return fail(WAM_E_SHAPE, "head dim must be 64 (got %d)", d->dh);
+  if (d->dh != 64 && d->dh != 128) return fail(WAM_E_SHAPE, "head dim must be 64 or 128 (got %d)", d->dh);
   if (d->D != d->Hh * d->dh) return fail(WAM_E_SHAPE, "D (%d) != Hh*dh (%d)", d->D, d->Hh * d->dh);
   if (d->D % 64 || d->Fm % 64) return fail(WAM_E_SHAPE, "D and Fm must be multiples of 64");
   if (d->Da < 0 || d->Da % 64 || d->Fma < 0 || d->Fma % 64)
@@ -103,6 +103,7 @@ int check_kv(const wam_dims* d, const wam_kv* kv, int B, const char* name, bool 
       return fail(WAM_E_DTYPE, "%s: an E4M3 cache is read only by the action layers of a bf16 model",
                   name);
     if (!kv->k_scale || !kv->v_scale) return fail(WAM_E_ARG, "%s has no tile scales", name);
+    if (kv->dh != 64) return fail(WAM_E_SHAPE, "%s: an E4M3 cache needs dh = 64", name);
   } else if (kv->dtype != d->dtype) {
     return fail(WAM_E_DTYPE, "%s dtype differs from dims", name);
   }
@@ -213,7 +214,7 @@ int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const Fra
     return WAM_OK;
   }
   HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, 3 * D, D, b.Y, D, w.wqkv, D, e));
-  HIPCK(attn_prefill(c.s, dt, d->Hh, n, row0, tab, b.Q, kl, vl, cap, b.O, b.pattn, b.pattn_bytes));
+  HIPCK(attn_prefill(c.s, dt, d->Hh, d->dh, n, row0, tab, b.Q, kl, vl, cap, b.O, b.pattn, b.pattn_bytes));
   if ((st = video_resid(c, n, D, D, b.O, w.wo))) return st;
   if ((st = norm_rows(c, dt, w.g2, b.Y, n))) return st;
   EpiArgs gl{};
@@ -297,7 +298,7 @@ int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, co
   e.v_ld = H;
   if ((st = norm_rows(c, dt, w.g1, b.Y, M))) return st;
   HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, M, 3 * Dq, D, b.Y, D, w.wqkv, D, e));
-  HIPCK(attn_action(c.s, dt, B, d->Hh, H, b.Q, b.Ka, b.Va, H, kc, vc, cap, lens, b.O, 0, b.attn,
+  HIPCK(attn_action(c.s, dt, B, d->Hh, H, d->dh, b.Q, b.Ka, b.Va, H, kc, vc, cap, lens, b.O, 0, b.attn,
                     b.attn_bytes, ksc, vsc));
   if ((st = action_resid(c, M, D, Dq, b.O, w.wo))) return st;
   if ((st = norm_rows(c, dt, w.g2, b.Y, M))) return st;
@@ -331,7 +332,7 @@ void plan_action(Arena& a, const wam_dims* d, int B, int max_len, bool with_emb,
   b.part_bytes = (size_t)4 * M * d->D * 4;
   b.part = (float*)a.take(b.part_bytes);
   b.pend = 0;
-  b.attn_bytes = attn_action_scratch_bytes(B, d->Hh, d->H, max_len, 0);
+  b.attn_bytes = attn_action_scratch_bytes(B, d->Hh, d->H, d->dh, max_len, 0);
   b.attn = a.take(b.attn_bytes);
   b.pattn = nullptr;
   b.pattn_bytes = 0;
@@ -362,7 +363,7 @@ void plan_prefill(Arena& a, const wam_dims* d, int Fh, int Ff, Bufs& b, float** 
   b.pend = 0;
   b.attn = nullptr;
   b.attn_bytes = 0;
-  b.pattn_bytes = attn_prefill_split_bytes(d->Hh, (int)T);
+  b.pattn_bytes = attn_prefill_split_bytes(d->Hh, d->dh, (int)T);
   b.pattn = (float*)a.take(b.pattn_bytes);
 }
 
@@ -1103,7 +1104,8 @@ static int attention_action_entry(int dtype, int B, int Hh, int dh, int H, const
                                   size_t ws_bytes, void* stream) {
   if (dtype != WAM_F32 && dtype != WAM_BF16) return fail(WAM_E_ARG, "bad dtype");
   if (ksc && (!kc || !vsc)) return fail(WAM_E_ARG, "an E4M3 cache needs kc, vc and both scales");
-  if (dh != 64 || H != 32) return fail(WAM_E_SHAPE, "dh must be 64 and H 32");
+  if ((dh != 64 && dh != 128) || H != 32) return fail(WAM_E_SHAPE, "dh must be 64 or 128 and H 32");
+  if (ksc && dh != 64) return fail(WAM_E_SHAPE, "an E4M3 cache needs dh = 64");
   if (B < 1 || B > WAM_MAX_BATCH || Hh < 1) return fail(WAM_E_SHAPE, "bad B or Hh");
   if (!q || !out) return fail(WAM_E_ARG, "NULL pointer");
   if (n_act < 0 || n_act > H || (n_act > 0 && (!ka || !va)))
@@ -1126,9 +1128,9 @@ static int attention_action_entry(int dtype, int B, int Hh, int dh, int H, const
   const void* ptrs[] = {q, ka, va, kc, vc, out};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(WAM_E_ALIGN, "pointer not 16-byte aligned");
-  size_t need = dtype == WAM_BF16 ? attn_action_scratch_bytes(B, Hh, H, max_len, splits_hint) : 0;
+  size_t need = dtype == WAM_BF16 ? attn_action_scratch_bytes(B, Hh, H, dh, max_len, splits_hint) : 0;
   if (need && (!ws || ws_bytes < need)) return fail(WAM_E_WORKSPACE, "workspace too small (%zu)", need);
-  HIPCK(attn_action((hipStream_t)stream, dtype, B, Hh, H, q, ka, va, n_act, kc, vc, cap, lens, out,
+  HIPCK(attn_action((hipStream_t)stream, dtype, B, Hh, H, dh, q, ka, va, n_act, kc, vc, cap, lens, out,
                     splits_hint, ws, ws_bytes, ksc, vsc));
   return WAM_OK;
 }
@@ -1183,7 +1185,8 @@ int wam_attention_prefill(int dtype, int Hh, int dh, int nq, int row0, int P, co
                           int n_frames, const void* q, const void* kc, const void* vc, int cap,
                           void* out, void* stream) {
   if (dtype != WAM_F32 && dtype != WAM_BF16) return fail(WAM_E_ARG, "bad dtype");
-  if (dh != 64 || Hh < 1 || nq < 0 || row0 < 0 || P < 1) return fail(WAM_E_SHAPE, "bad shape");
+  if ((dh != 64 && dh != 128) || Hh < 1 || nq < 0 || row0 < 0 || P < 1)
+    return fail(WAM_E_SHAPE, "bad shape");
   if (!kend || !q || !kc || !vc || !out) return fail(WAM_E_ARG, "NULL pointer");
   if (n_frames < 1 || n_frames > WAM_MAX_FRAMES) return fail(WAM_E_SHAPE, "bad n_frames");
   if (cap < 64 || cap % 64) return fail(WAM_E_SHAPE, "cap must be a multiple of 64");
@@ -1199,7 +1202,7 @@ int wam_attention_prefill(int dtype, int Hh, int dh, int nq, int row0, int P, co
   const void* ptrs[] = {q, kc, vc, out};
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(WAM_E_ALIGN, "pointer not 16-byte aligned");
-  HIPCK(attn_prefill((hipStream_t)stream, dtype, Hh, nq, row0, tab, q, kc, vc, cap, out, nullptr, 0));
+  HIPCK(attn_prefill((hipStream_t)stream, dtype, Hh, dh, nq, row0, tab, q, kc, vc, cap, out, nullptr, 0));
   return WAM_OK;
 }
 

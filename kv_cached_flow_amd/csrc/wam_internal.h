@@ -205,19 +205,20 @@ hipError_t fuse_kv(hipStream_t s, int dt, const void* src, void* dst, long long 
 
 // part / part_bytes: workspace for split partials (bf16 launches with few
 // query tiles split their keys and merge; NULL: never split).
-hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int nq, int row0, const FrameTab& tab,
-                        const void* q, const void* kc, const void* vc, int cap, void* out,
-                        float* part, size_t part_bytes);
+// dh is 64 or 128.
+hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int dh, int nq, int row0,
+                        const FrameTab& tab, const void* q, const void* kc, const void* vc, int cap,
+                        void* out, float* part, size_t part_bytes);
 // Partial workspace a prefill of up to max_rows query rows can use.
-size_t attn_prefill_split_bytes(int Hh, int max_rows);
+size_t attn_prefill_split_bytes(int Hh, int dh, int max_rows);
 
 struct ActLens {
   int len[WAM_MAX_BATCH];
 };
-size_t attn_action_scratch_bytes(int B, int Hh, int H, int max_len, int splits_hint);
+size_t attn_action_scratch_bytes(int B, int Hh, int H, int dh, int max_len, int splits_hint);
 // ksc/vsc non-NULL: kc/vc is an E4M3 cache layer (bf16 model) with these
 // per-(episode, head, 64-key tile) scales, [B][Hh][cap/64].
-hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, const void* q,
+hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, int dh, const void* q,
                        const void* ka, const void* va, int n_act, const void* kc,
                        const void* vc, int cap, const ActLens& lens, void* out,
                        int splits_hint, void* scratch, size_t scratch_bytes,

@@ -46,22 +46,23 @@ def test_debug_visibility_matches_oracle(case):
 
 
 # ---------------------------------------------------------------- prefill attention
+@pytest.mark.parametrize("dh", [64, 128])
 @pytest.mark.parametrize("dt", [wam.WAM_F32, wam.WAM_BF16])
 @pytest.mark.parametrize("rows", [(0, 500), (100, 300), (400, 100)])
-def test_attention_prefill_vs_oracle(dt, rows):
+def test_attention_prefill_vs_oracle(dt, rows, dh):
     row0, nq = rows
-    print_case(f"prefill attention dt={dt} rows={rows}")
+    print_case(f"prefill attention dt={dt} rows={rows} dh={dh}")
     rng = np.random.default_rng(1 + row0)
     Hh, P, cap = 2, 100, 576
     blocks = (0, 1, 1, 2, 3)
     _, kend = wam.frame_table(blocks, None, 5, 0, P)
     T = 5 * P
-    q = _rand(rng, (Hh, nq, 64), dt)
-    K = _rand(rng, (Hh, cap, 64), dt)
-    V = _rand(rng, (Hh, cap, 64), dt)
+    q = _rand(rng, (Hh, nq, dh), dt)
+    K = _rand(rng, (Hh, cap, dh), dt)
+    V = _rand(rng, (Hh, cap, dh), dt)
     K[:, T:] = np.nan   # rows past the last frame must never be read
     V[:, T:] = np.nan
-    out = torch.empty((nq, Hh * 64), dtype=_tdt(dt), device="cuda")
+    out = torch.empty((nq, Hh * dh), dtype=_tdt(dt), device="cuda")
     wam.attention_prefill(dt, _dev(q, dt), row0, P, kend, _dev(K, dt),
                           _dev(np.ascontiguousarray(V.transpose(0, 2, 1)), dt), cap, out)
     torch.cuda.synchronize()
@@ -69,20 +70,20 @@ def test_attention_prefill_vs_oracle(dt, rows):
     mask = torch.tensor(np.arange(T)[None, :] < kend[qrow // P][:, None])
     ref = O.attention(torch.tensor(q, dtype=f64).permute(1, 0, 2), torch.tensor(K[:, :T], dtype=f64).permute(1, 0, 2),
                       torch.tensor(V[:, :T], dtype=f64).permute(1, 0, 2), lambda a, b: mask[a:b])
-    got = to_np(out).reshape(nq, Hh, 64)
+    got = to_np(out).reshape(nq, Hh, dh)
     assert np.isfinite(got).all()
     assert rel_l2(got, ref.numpy()) <= (1e-5 if dt == wam.WAM_F32 else 5e-3)
 
 
 # ---------------------------------------------------------------- action attention
-def _action_case(rng, dt, B, Hh, lens, n_act, cap=None):
+def _action_case(rng, dt, B, Hh, lens, n_act, cap=None, dh=64):
     H = 32
     cap = cap or (max(lens) + 63) // 64 * 64 if lens else 64
-    q = _rand(rng, (B, Hh, H, 64), dt)
-    ka = _rand(rng, (B, Hh, H, 64), dt)
-    va = _rand(rng, (B, Hh, H, 64), dt)
-    K = _rand(rng, (B, Hh, cap, 64), dt)
-    V = _rand(rng, (B, Hh, cap, 64), dt)
+    q = _rand(rng, (B, Hh, H, dh), dt)
+    ka = _rand(rng, (B, Hh, H, dh), dt)
+    va = _rand(rng, (B, Hh, H, dh), dt)
+    K = _rand(rng, (B, Hh, cap, dh), dt)
+    V = _rand(rng, (B, Hh, cap, dh), dt)
     for b, n in enumerate(lens):
         K[b, :, n:] = np.nan
         V[b, :, n:] = np.nan
@@ -105,24 +106,25 @@ def _action_ref(q, ka, va, K, V, lens, n_act, with_cache=True):
         kk = torch.tensor(np.concatenate(ks, axis=1), dtype=f64).permute(1, 0, 2)
         vv = torch.tensor(np.concatenate(vs, axis=1), dtype=f64).permute(1, 0, 2)
         outs.append(O.attention(torch.tensor(q[b], dtype=f64).permute(1, 0, 2), kk, vv).numpy())
-    return np.stack(outs)  # [B, 32, Hh, 64]
+    return np.stack(outs)  # [B, 32, Hh, dh]
 
 
 def _run_action(dt, q, ka, va, n_act, K, V, cap, lens, splits=0, with_cache=True):
-    B, Hh = q.shape[:2]
-    out = torch.empty((B, 32, Hh * 64), dtype=_tdt(dt), device="cuda")
+    B, Hh, _, dh = q.shape
+    out = torch.empty((B, 32, Hh * dh), dtype=_tdt(dt), device="cuda")
     vt = lambda a: _dev(np.ascontiguousarray(a.transpose(0, 1, 3, 2)), dt)
     wam.attention_action(dt, _dev(q, dt), _dev(ka, dt) if n_act else None, vt(va) if n_act else None,
                          n_act, _dev(K, dt) if with_cache else None, vt(V) if with_cache else None,
                          cap, lens if with_cache else None, out, splits)
     torch.cuda.synchronize()
-    return to_np(out).reshape(B, 32, Hh, 64)
+    return to_np(out).reshape(B, 32, Hh, dh)
 
 
+@pytest.mark.parametrize("dh", [64, 128])
 @pytest.mark.parametrize("dt", [wam.WAM_F32, wam.WAM_BF16])
-def test_attention_action_single_key_is_value_exactly(dt):
+def test_attention_action_single_key_is_value_exactly(dt, dh):
     rng = np.random.default_rng(3)
-    q, ka, va, K, V, cap = _action_case(rng, dt, 2, 3, [1, 1], 0)
+    q, ka, va, K, V, cap = _action_case(rng, dt, 2, 3, [1, 1], 0, dh=dh)
     got = _run_action(dt, q, ka, va, 0, K, V, cap, [1, 1])
     want = np.broadcast_to(V[:, :, 0][:, None, :, :], got.shape)
     assert np.array_equal(got, want)
@@ -139,21 +141,35 @@ def test_attention_action_zero_query_is_mean(dt):
 
 
 @pytest.mark.parametrize("shape", [
-    ("C1-like", 1, 16, [9216], 32),
-    ("C4-like", 4, 16, [27280] * 4, 32),
-    ("ragged", 3, 4, [100, 3000, 777], 32),
-    ("no-own", 2, 4, [513, 64], 0),
-    ("partial-own", 2, 4, [300, 129], 20),
+    ("C1-like", 1, 16, [9216], 32, 64),
+    ("C4-like", 4, 16, [27280] * 4, 32, 64),
+    ("ragged", 3, 4, [100, 3000, 777], 32, 64),
+    ("no-own", 2, 4, [513, 64], 0, 64),
+    ("partial-own", 2, 4, [300, 129], 20, 64),
+    ("24x128 heads", 1, 24, [9216], 32, 128),
+    ("ragged dh=128", 3, 4, [100, 3000, 777], 32, 128),
+    ("no-own dh=128", 2, 4, [513, 64], 0, 128),
+    ("partial-own dh=128", 2, 4, [300, 129], 20, 128),
 ])
 def test_attention_action_vs_oracle(shape):
-    name, B, Hh, lens, n_act = shape
+    name, B, Hh, lens, n_act, dh = shape
     print_case(f"action attention {name}")
     dt = wam.WAM_BF16
     rng = np.random.default_rng(5)
-    q, ka, va, K, V, cap = _action_case(rng, dt, B, Hh, lens, n_act)
+    q, ka, va, K, V, cap = _action_case(rng, dt, B, Hh, lens, n_act, dh=dh)
     got = _run_action(dt, q, ka, va, n_act, K, V, cap, lens)
     ref = _action_ref(q, ka, va, K, V, lens, n_act)
     assert rel_l2(got, ref) <= 5e-3
+
+
+def test_attention_action_f32_dh128_vs_oracle():
+    dt = wam.WAM_F32
+    rng = np.random.default_rng(15)
+    lens = [700, 64, 1]
+    print_case("action attention fp32, dh=128")
+    q, ka, va, K, V, cap = _action_case(rng, dt, 3, 3, lens, 20, dh=128)
+    got = _run_action(dt, q, ka, va, 20, K, V, cap, lens)
+    assert rel_l2(got, _action_ref(q, ka, va, K, V, lens, 20)) <= 1e-5
 
 
 def test_attention_action_batch_independent_bitwise():
@@ -184,11 +200,12 @@ def test_attention_action_only_own_keys():
     assert rel_l2(got, ref) <= 5e-3
 
 
-def test_attention_action_split_invariance_and_determinism():
+@pytest.mark.parametrize("dh", [64, 128])
+def test_attention_action_split_invariance_and_determinism(dh):
     dt = wam.WAM_BF16
     rng = np.random.default_rng(7)
     lens = [5000, 4097]
-    q, ka, va, K, V, cap = _action_case(rng, dt, 2, 4, lens, 32)
+    q, ka, va, K, V, cap = _action_case(rng, dt, 2, 4, lens, 32, dh=dh)
     ref = _action_ref(q, ka, va, K, V, lens, 32)
     outs = {}
     for splits in (1, 2, 7, 63):

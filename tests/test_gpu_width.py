@@ -46,3 +46,35 @@ def test_codenoise_with_an_action_expert_of_its_own_width():
     dc = _run(cfg, inp)
     assert rel_l2(to_np(dc.actions), ref["actions"]) <= 2e-2
     assert rel_l2(to_np(dc.z).reshape(ref["z"].shape), ref["z"]) <= 2e-2
+
+
+# 128-wide heads: the attention tiles of both experts change shape
+WIDE = dict(SMALL, D=256, Hh=2, dh=128)
+
+
+@pytest.mark.parametrize("dtype,Da,Fma", [("f32", 0, 0), ("bf16", 0, 0), ("bf16", 512, 768)])
+def test_chunk_with_128_wide_heads(dtype, Da, Fma):
+    cfg = configs.small("H128", dtype=dtype, **dict(WIDE, Da=Da, Fma=Fma))
+    print_case(f"dh 128, action width {Da or cfg.D}, {dtype}")
+    inp = inputs.generate(cfg)
+    ref = O.run_chunk(cfg, inp, keep_cache=True)
+    dc = _run(cfg, inp)
+    tol, ktol = (1e-5, 1e-5) if dtype == "f32" else (2e-2, 1e-2)
+    assert rel_l2(to_np(dc.actions), ref["actions"]) <= tol
+    assert rel_l2(to_np(dc.vhat), ref["vhat"]) <= tol
+    assert rel_l2(to_np(dc.z).reshape(ref["z"].shape), ref["z"]) <= tol
+    T = cfg.tokens_valid
+    for l in range(cfg.L):
+        k, v = gpu_cache_layer(dc, l, 0, T)
+        assert rel_l2(k, ref["cache"][0][l][0].numpy()) <= ktol
+        assert rel_l2(v, ref["cache"][0][l][1].numpy()) <= ktol
+
+
+def test_codenoise_with_128_wide_heads():
+    cfg = configs.small("H128J", dtype="bf16", **dict(WIDE, Hh=4, D=512, Da=256, Fma=512, joint=True))
+    print_case("co-denoising, 4 x 128 heads, action width 256")
+    inp = inputs.generate(cfg)
+    ref = O.run_codenoise(cfg, inp)
+    dc = _run(cfg, inp)
+    assert rel_l2(to_np(dc.actions), ref["actions"]) <= 2e-2
+    assert rel_l2(to_np(dc.z).reshape(ref["z"].shape), ref["z"]) <= 2e-2

@@ -93,9 +93,9 @@ class FakeExpert:
         self.c = wam.WamExpertW(ptr, ptr, ptr, C.cast(self.larr, C.POINTER(wam.WamLayerW)), L)
 
 
-def fake_kv(n_layers=2, B=1, Hh=4, cap=512, dtype=wam.WAM_BF16, lens=None):
+def fake_kv(n_layers=2, B=1, Hh=4, cap=512, dtype=wam.WAM_BF16, lens=None, dh=64):
     ln = np.asarray(lens if lens is not None else [cap] * B, dtype=np.int32)
-    kv = wam.WamKV(FAKE, FAKE, n_layers, B, Hh, 64, cap, dtype, ln.ctypes.data_as(C.POINTER(C.c_int32)))
+    kv = wam.WamKV(FAKE, FAKE, n_layers, B, Hh, dh, cap, dtype, ln.ctypes.data_as(C.POINTER(C.c_int32)))
     return kv, ln
 
 
@@ -123,6 +123,10 @@ def test_prefill_validation_errors():
     assert call_prefill(d=good_dims(Da=100))[0] == -2         # action width not a multiple of 64
     assert call_prefill(d=good_dims(Fma=-64))[0] == -2
     assert call_prefill(d=good_dims(Hh=80, D=5120))[0] == -2  # widths above 4096
+    assert call_prefill(d=good_dims(Hh=2, dh=96, D=192))[0] == -2  # heads of 64 or 128 only
+    kv128, _k = fake_kv(Hh=2, dh=128)
+    assert call_prefill(d=good_dims(Hh=2, dh=128), kv=kv128, ws_bytes=4096)[0] == -5  # 128 accepted
+    assert call_prefill(d=good_dims(Hh=2, dh=128), kv=fake_kv(Hh=2)[0])[0] == -2     # cache dh differs
     assert call_prefill(blocks=(0, 2, 1, 3, 4))[0] == -2      # non-monotone
     assert call_prefill(V=2, sigma=1.0)[0] == -1              # sigma* must be < 1
     assert call_prefill(V=-1)[0] == -1
@@ -267,6 +271,18 @@ def test_fp8_cache_validation_errors():
     kv8c, _j = fake_kv(cap=512, lens=[300], dtype=wam.WAM_FP8)
     kv8c.k_scale = kv8c.v_scale = FAKE
     assert call_codenoise(kv=kv8c)[0] == -3
+    # the E4M3 layout is defined for 64-wide heads only
+    s128, _l = fake_kv(n_layers=2, cap=512, lens=[300], dh=128)
+    d128, _m = fake_kv(n_layers=2, cap=512, lens=[0], dtype=wam.WAM_FP8, dh=128)
+    d128.k_scale = d128.v_scale = FAKE
+    assert q(s128, d128)[0] == -2
+    k128, _n = fake_kv(Hh=2, dtype=wam.WAM_FP8, dh=128)
+    k128.k_scale = k128.v_scale = FAKE
+    assert call_denoise(d=good_dims(Hh=2, dh=128), kv=k128) == -2
+    ln = np.array([100], np.int32)
+    st = L.wam_attention_action_fp8(1, 4, 128, 32, FAKE, FAKE, FAKE, 32, FAKE, FAKE, FAKE, FAKE, 128,
+                                    ln.ctypes.data, FAKE, 0, FAKE, 1 << 30, None)
+    assert st == -2
 
 
 def test_async_schedule_rule_by_brute_force():
