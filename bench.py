@@ -34,6 +34,7 @@ WORKLOAD_TEXT = {
     "C3": "Long-WAM IDM: 24 history + 2 future frames x 880 tokens, V=4 to sigma*=0.9, N=4",
     "C4": "long-context: 48 history (19 padded) + 2 future x 880 tokens, V=4, N=10, B=4",
     "C5": "Long-WAM co-denoising: 24 history + 2 future frames x 880 tokens, 4 joint video+action steps (V4/A4)",
+    "C6": "C1's chunk at the experts' own widths: video 3072 wide (24x128 heads, MLP 12288), action 1024 wide (MLP 4096) over 24x128 heads",
 }
 
 

@@ -654,9 +654,8 @@ __device__ inline bf16x8 e4m3x8_bf16(unsigned lo, unsigned hi, float scale) {
 // read row key1 - 1 (their scores are masked to -inf), V^T chunks that start
 // past key1 read the row's first chunk (zeroed by the caller).
 template <int DH>
-__device__ inline void bf16_tiles(bf16x8 (&ak)[4][DH / 32], bf16x8 (&av)[DH / 16][2],
-                                  const bf16_t* kb, const bf16_t* vb, int kt, int key0, int key1,
-                                  int vld, int c16, int g) {
+__device__ inline void bf16_k_tile(bf16x8 (&ak)[4][DH / 32], const bf16_t* kb, int kt, int key1,
+                                   int c16, int g) {
 #pragma unroll
   for (int sub = 0; sub < 4; sub++) {
     const int key = min(kt + perm_key(sub, c16), key1 - 1);
@@ -664,6 +663,10 @@ __device__ inline void bf16_tiles(bf16x8 (&ak)[4][DH / 32], bf16x8 (&av)[DH / 16
     for (int ss = 0; ss < DH / 32; ss++)
       ak[sub][ss] = *(const bf16x8*)(kb + (long long)key * DH + 32 * ss + 8 * g);
   }
+}
+template <int DH>
+__device__ inline void bf16_v_tile(bf16x8 (&av)[DH / 16][2], const bf16_t* vb, int kt, int key0,
+                                   int key1, int vld, int c16, int g) {
 #pragma unroll
   for (int d = 0; d < DH / 16; d++)
 #pragma unroll
@@ -671,6 +674,26 @@ __device__ inline void bf16_tiles(bf16x8 (&ak)[4][DH / 32], bf16x8 (&av)[DH / 16
       const int k0 = kt + 32 * wd + 8 * g;
       av[d][wd] = *(const bf16x8*)(vb + (long long)(16 * d + c16) * vld + (k0 < key1 ? k0 : key0));
     }
+}
+template <int DH>
+__device__ inline void bf16_tiles(bf16x8 (&ak)[4][DH / 32], bf16x8 (&av)[DH / 16][2],
+                                  const bf16_t* kb, const bf16_t* vb, int kt, int key0, int key1,
+                                  int vld, int c16, int g) {
+  bf16_k_tile<DH>(ak, kb, kt, key1, c16, g);
+  bf16_v_tile<DH>(av, vb, kt, key0, key1, vld, c16, g);
+}
+// P is zero past key1, but 0 * V must not meet a non-finite V
+template <int DH>
+__device__ inline void zero_v_tail(bf16x8 (&av)[DH / 16][2], int kt, int key1, int g) {
+#pragma unroll
+  for (int wd = 0; wd < 2; wd++) {
+    const int k0 = kt + 32 * wd + 8 * g;
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      if (k0 + j >= key1)
+#pragma unroll
+        for (int d = 0; d < DH / 16; d++) av[d][wd][j] = 0;
+  }
 }
 
 // Split (b, h, s): cache keys [s*kc[b], min(len, (s+1)*kc[b])) for s < ncs(b),
@@ -683,7 +706,7 @@ __device__ inline void bf16_tiles(bf16x8 (&ak)[4][DH / 32], bf16x8 (&av)[DH / 16
 // with the tile's scale they are the bf16 operands of the same MFMAs.  The
 // chunk's own keys stay bf16.
 template <bool F8, int DH>
-__global__ __launch_bounds__(256, DH == 64 ? 2 : 1) void attn_action_kernel(
+__global__ __launch_bounds__(256, 2) void attn_action_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ ka, const bf16_t* __restrict__ va,
     const void* __restrict__ kc, const void* __restrict__ vc, const float* __restrict__ ksc,
     const float* __restrict__ vsc, ActGeom G, float* __restrict__ part, float sl2) {
@@ -741,6 +764,22 @@ __global__ __launch_bounds__(256, DH == 64 ? 2 : 1) void attn_action_kernel(
   const bf16x8 ones = ones_row(c16);
   const int kq[2] = {key1, key1};
   for (int kt = key0 + w * KT; kt < key1; kt += 4 * KT) {
+    if constexpr (DH == 128) {
+      // 128-wide heads: the V^T tile is loaded after the scores, so that the
+      // K and V^T fragments (64 registers each) are never live together
+      const bool tail = kt + KT > key1;  // wave-uniform
+      const bool first = kt == key0 + w * KT;
+      floatx4 sacc[4][2];
+      bf16x8 ak[4][NS], av[ND][2];
+      bf16_k_tile<DH>(ak, kb, kt, key1, c16, g);
+      tile_scores(sacc, qf, acc, first, [&](int sub, int ss) { return ak[sub][ss]; });
+      bf16_v_tile<DH>(av, vb, kt, key0, key1, vld, c16, g);
+      if (tail) {
+        zero_v_tail<DH>(av, kt, key1, g);
+        tile_mask(sacc, kt, kq, g);
+      }
+      tile_update(acc, sacc, first, ones, [&](int d, int wd) { return av[d][wd]; });
+    } else {
     // ---- loads: K rows (A of S^T) and V^T rows (A of P V).  All loads are
     // unconditional so that they are in flight together: K rows past key1
     // read row key1 - 1 (their scores are masked to -inf), V^T chunks that
@@ -796,6 +835,7 @@ __global__ __launch_bounds__(256, DH == 64 ? 2 : 1) void attn_action_kernel(
     auto vop = [&](int d, int wd) { return av[d][wd]; };
     if (tail) tile_mask(sacc, kt, kq, g);
     tile_update(acc, sacc, kt == key0 + w * KT, ones, vop);
+    }
   }
   // ---- per-wave state to LDS (waves without keys hold m = -inf, l = 0, o = 0)
 #pragma unroll
