@@ -1,7 +1,7 @@
-"""Write the expected values of the full-size workloads C1-C5 by running the
+"""Write the expected values of the full-size workloads C1-C6 by running the
 CPU oracle (and nothing else) on the seeded inputs.
 
-    python tests/golden/make_golden.py C1 C2 C3 C4 C5
+    python tests/golden/make_golden.py C1 C2 C3 C4 C5 C6
 
 Each ``<name>.json`` holds the input fingerprint, the final action chunk of
 every episode, the v-hat of the first and last action steps, and sampled

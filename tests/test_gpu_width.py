@@ -1,6 +1,10 @@
 """Experts of different widths over one attention interface (the action
 expert narrower or wider than Hh x dh, its own MLP width) against the oracle,
 for the IDM chunk and for co-denoising."""
+import json
+import os
+
+import numpy as np
 import pytest
 import torch
 
@@ -78,3 +82,30 @@ def test_codenoise_with_128_wide_heads():
     dc = _run(cfg, inp)
     assert rel_l2(to_np(dc.actions), ref["actions"]) <= 2e-2
     assert rel_l2(to_np(dc.z).reshape(ref["z"].shape), ref["z"]) <= 2e-2
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_real_widths_full_size_against_oracle_values():
+    """C6 (3072-wide video expert with 24 x 128 heads, 1024-wide action
+    expert) against the oracle's stored values."""
+    path = os.path.join(GOLDEN, "C6.json")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated (tests/golden/make_golden.py C6)")
+    g = json.load(open(path))
+    cfg = configs.get("C6")
+    print_case("full size C6 (real widths)")
+    inp = inputs.generate(cfg)
+    assert inputs.fingerprint(inp) == g["fingerprint"]
+    dc = _run(cfg, inp)
+    err = rel_l2(to_np(dc.actions), np.array(g["actions"]))
+    print_case(f"C6 final actions rel-L2 {err:.3e}")
+    assert err <= 2e-2
+    rows, heads = np.array(g["sample_rows"]), np.array(g["sample_heads"])
+    for l in g["sample_layers"]:
+        ent = g["cache"][0][str(l)]
+        k = to_np(dc.cache.k[l, 0])[heads, rows]
+        v = to_np(dc.cache.v[l, 0]).transpose(0, 2, 1)[heads, rows]
+        assert rel_l2(k, np.array(ent["k"])) <= 1e-2
+        assert rel_l2(v, np.array(ent["v"])) <= 1e-2
