@@ -59,6 +59,7 @@ class WamConfig:
     kv_fp8: bool = False  # the action layers read an E4M3 copy of their K/V (not the pages' bf16)
     Da: int = 0           # action expert width (0: D); the attention interface is Hh x dh for both
     Fma: int = 0          # action expert MLP width (0: Fm)
+    rope: bool = False    # rotary position embedding on Q and K of both experts (an option)
 
     @property
     def F(self) -> int:

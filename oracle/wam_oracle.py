@@ -179,8 +179,47 @@ def attention(q, k, v, allow: Optional[MaskFn] = None, q_chunk: int = 1024):
     return out
 
 
+ROPE_BASE = 10000.0
+
+
+def rope(x, pos):
+    """Rotary position embedding of x [n, Hh, dh] at token positions pos [n].
+
+    The pages only say that the rotary position tables, which encode token
+    positions, are computed once per inference call and reused across the
+    denoising steps (Long-WAM Summary section 4.2).  Reading adopted (an
+    option; the workloads C1-C6 run without it): the rotation of the usual
+    rotary embedding, pair j = (x[2j], x[2j+1]) of every head taken as the
+    complex number x[2j] + i x[2j+1] and multiplied by exp(i p w_j) with
+    w_j = 10000^(-2j/dh), p the token's position.  Angles in float64.
+    """
+    n, Hh, dh = x.shape
+    j = torch.arange(dh // 2, dtype=torch.float64)
+    w = ROPE_BASE ** (-2.0 * j / dh)
+    ang = pos.to(torch.float64)[:, None] * w[None, :]            # [n, dh/2]
+    c = torch.cos(ang).to(x.dtype)[:, None, :]
+    sn = torch.sin(ang).to(x.dtype)[:, None, :]
+    a, b = x[..., 0::2], x[..., 1::2]
+    out = torch.empty_like(x)
+    out[..., 0::2] = a * c - b * sn
+    out[..., 1::2] = a * sn + b * c
+    return out
+
+
+def token_positions(cfg, first: int, n: int) -> Optional[torch.Tensor]:
+    """Positions first .. first + n - 1 with the rotary option on, else None.
+
+    Reading adopted for the position of a token: its index in the episode's
+    joint sequence as the attention sees it, [valid history rows in frame
+    order ; future rows ; the action chunk] (padded frames are not in it), so
+    that appending frames leaves every cached row's position unchanged."""
+    if not getattr(cfg, "rope", False):
+        return None
+    return torch.arange(first, first + n, dtype=torch.int64)
+
+
 def layer(X, w: dict, Hh: int, ctx: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
-          allow: Optional[MaskFn] = None, kv_only: bool = False):
+          allow: Optional[MaskFn] = None, kv_only: bool = False, pos=None):
     """One expert layer on token states X [n, D] with attention context ctx.
 
     Keys and values are [ctx ; this layer's own K, V] ("Fast-WAM" page
@@ -192,6 +231,8 @@ def layer(X, w: dict, Hh: int, ctx: Optional[Tuple[torch.Tensor, torch.Tensor]] 
     Q, K and V have the width Dq = Hh * dh of the attention interface the two
     experts share (24 heads x 128 on the "Fast-WAM 精读" page, section 四.4),
     which may differ from the expert's own width D (Wqkv [3 Dq][D], Wo [D][Dq]).
+    With ``pos`` (token positions [n]) Q and K are rotated by ``rope`` before
+    the attention, so the K rows returned for the cache are rotated too.
     """
     n, D = X.shape
     Dq = w["wqkv"].shape[0] // 3
@@ -201,6 +242,8 @@ def layer(X, w: dict, Hh: int, ctx: Optional[Tuple[torch.Tensor, torch.Tensor]] 
     Q = qkv[:, :Dq].reshape(n, Hh, dh)
     K = qkv[:, Dq:2 * Dq].reshape(n, Hh, dh)
     V = qkv[:, 2 * Dq:].reshape(n, Hh, dh)
+    if pos is not None:
+        Q, K = rope(Q, pos), rope(K, pos)
     if kv_only:
         return None, K, V
     if ctx is not None:
@@ -289,8 +332,14 @@ def history_cache(cfg, vw: dict, hist_b, valid_b, drop_padded: bool = True):
     cache_h = []
     if len(hist_frames):
         X = embed(hist_tok, vw["w_in"], 0.0, D)
+        pos = None
+        if getattr(cfg, "rope", False):
+            # a token's position counts the valid tokens before it (padded
+            # tokens, kept only with drop_padded=False, are masked keys)
+            vt = valid[fh]
+            pos = torch.cumsum(vt, 0) - vt
         for l, lw in enumerate(vw["layers"]):
-            X, K, V = layer(X, lw, Hh, None, mask_h, kv_only=(l == L - 1))
+            X, K, V = layer(X, lw, Hh, None, mask_h, kv_only=(l == L - 1), pos=pos)
             cache_h.append((K, V))
     else:
         empty = torch.zeros((0, Hh, cfg.dh), dtype=dt)
@@ -327,9 +376,10 @@ def extend_history(cfg, vw: dict, cache_old, n_old: int, hist_b, valid_b):
     mask = lambda q0, q1: video_visible(fn[q0:q1], fall, block, valid)
     tok = torch.from_numpy(np.ascontiguousarray(hist_b[new])).to(dt).reshape(-1, cfg.Cv)
     X = embed(tok, vw["w_in"], 0.0, D)
+    pos = token_positions(cfg, int(cache_old[0][0].shape[0]), X.shape[0])
     cache = []
     for l, lw in enumerate(vw["layers"]):
-        X, K, V = layer(X, lw, Hh, cache_old[l], mask, kv_only=(l == L - 1))
+        X, K, V = layer(X, lw, Hh, cache_old[l], mask, kv_only=(l == L - 1), pos=pos)
         cache.append((torch.cat([cache_old[l][0], K]), torch.cat([cache_old[l][1], V])))
     return cache
 
@@ -359,13 +409,14 @@ def video_prefill(cfg, vw: dict, hist_b, valid_b, eps_v_b, drop_padded: bool = T
     cache_h, fall, valid, mask_f = history_cache(cfg, vw, hist_b, valid_b, drop_padded)
 
     z = torch.from_numpy(np.ascontiguousarray(eps_v_b)).to(dt).reshape(-1, cfg.Cv)
+    pos_f = token_positions(cfg, int(sum(valid_b[:cfg.Fh])) * cfg.P, z.shape[0])
     if cfg.V >= 1:
         sig = schedule(cfg.V, cfg.sigma_star, cfg.shift)
 
         def vel(zc, k, s):
             X = embed(zc, vw["w_in"], s, D)
             for l, lw in enumerate(vw["layers"]):
-                X, _, _ = layer(X, lw, Hh, cache_h[l], mask_f)
+                X, _, _ = layer(X, lw, Hh, cache_h[l], mask_f, pos=pos_f)
             return head(X, vw["g_out"], vw["w_out"])
 
         z, _ = integrate(z, sig, vel)
@@ -377,7 +428,7 @@ def video_prefill(cfg, vw: dict, hist_b, valid_b, eps_v_b, drop_padded: bool = T
     keep = valid[fall].bool()          # the cache holds valid rows only
     X = embed(z, vw["w_in"], sigma_f, D)
     for l, lw in enumerate(vw["layers"]):
-        X, K, V = layer(X, lw, Hh, cache_h[l], mask_f, kv_only=(l == L - 1))
+        X, K, V = layer(X, lw, Hh, cache_h[l], mask_f, kv_only=(l == L - 1), pos=pos_f)
         cache.append((torch.cat([cache_h[l][0], K])[keep], torch.cat([cache_h[l][1], V])[keep]))
     return cache, z, fall[keep]
 
@@ -406,26 +457,30 @@ def fuse_interval(cache: List[Tuple[torch.Tensor, torch.Tensor]], fuse, logits):
     return out
 
 
-def action_velocity(cfg, aw: dict, kv_read: List[Optional[Tuple]], a, sigma: float):
+def action_velocity(cfg, aw: dict, kv_read: List[Optional[Tuple]], a, sigma: float,
+                    pos0: int = 0):
     """One pass of the action expert at flow time sigma: v-hat for the chunk.
 
     Per layer the 32 action queries attend over [video K/V read by this layer ;
     the chunk's own K/V], or over the chunk alone where the layer reads
     nothing (SparseMoT, Faster-WAM page section 3.2); no mask among action
     tokens (Long-WAM Summary section 3.2: the entire noisy chunk is visible).
+    ``pos0``: position of the first action token (the episode's cached rows
+    come first) for the rotary option.
     """
     X = embed(a, aw["w_in"], sigma, cfg.Dact)
+    pos = token_positions(cfg, pos0, X.shape[0])
     for l, lw in enumerate(aw["layers"]):
-        X, _, _ = layer(X, lw, cfg.Hh, kv_read[l], None)
+        X, _, _ = layer(X, lw, cfg.Hh, kv_read[l], None, pos=pos)
     return head(X, aw["g_out"], aw["w_out"])
 
 
-def denoise(cfg, aw: dict, kv_read, eps_a_b):
+def denoise(cfg, aw: dict, kv_read, eps_a_b, pos0: int = 0):
     """N Euler steps of the action flow from noise at t=1 to t=0, re-reading
     the same video K/V at every step (Fast-WAM page section 七.2-七.3)."""
     t = schedule(cfg.N, 0.0, cfg.shift)
     a = torch.from_numpy(np.ascontiguousarray(eps_a_b)).to(aw["w_in"].dtype)
-    return integrate(a, t, lambda x, k, s: action_velocity(cfg, aw, kv_read, x, s))
+    return integrate(a, t, lambda x, k, s: action_velocity(cfg, aw, kv_read, x, s, pos0))
 
 
 def read_layers(cfg, cache, fused):
@@ -457,7 +512,7 @@ def run_chunk(cfg, inp: dict, dtype=None, drop_padded: bool = True,
         kv_read = read_layers(cfg, cache, fused)
         if kv_fp8:
             kv_read = quantize_read(kv_read)
-        a, vh = denoise(cfg, aw, kv_read, inp["eps_a"][b])
+        a, vh = denoise(cfg, aw, kv_read, inp["eps_a"][b], int(cache[0][0].shape[0]))
         if cache_sampler is not None:
             cache_sampler(b, cache, fused)
         acts.append(a.double().numpy())
@@ -518,17 +573,19 @@ def codenoise(cfg, vw: dict, aw: dict, hist_b, valid_b, eps_v_b, eps_a_b, steps:
     ta = schedule(steps, 0.0, cfg.shift)
     z = torch.from_numpy(np.ascontiguousarray(eps_v_b)).to(dt).reshape(-1, cfg.Cv)
     a = torch.from_numpy(np.ascontiguousarray(eps_a_b)).to(dt)
+    Th = int(cache_h[0][0].shape[0])
+    pos_f = token_positions(cfg, Th, z.shape[0])
     traj = []
     cache = None
     for k in range(steps):
         X = embed(z, vw["w_in"], float(sv[k]), D)
         cache = []
         for l, lw in enumerate(vw["layers"]):
-            X, K, V = layer(X, lw, Hh, cache_h[l], mask_f)
+            X, K, V = layer(X, lw, Hh, cache_h[l], mask_f, pos=pos_f)
             cache.append((torch.cat([cache_h[l][0], K]), torch.cat([cache_h[l][1], V])))
         v_v = head(X, vw["g_out"], vw["w_out"])
         v_a = action_velocity(cfg, aw, [None if r < 0 else cache[r] for r in cfg.read_map],
-                              a, float(ta[k]))
+                              a, float(ta[k]), Th + z.shape[0])
         traj.append((z, a, v_v, v_a))
         z = euler_step(z, v_v, sv[k], sv[k + 1])
         a = euler_step(a, v_a, ta[k], ta[k + 1])
@@ -706,6 +763,9 @@ def joint_mot_step(cfg, vw: dict, aw: dict, video_tok, video_sigma, video_frames
         Q = torch.cat([qv[:, :Dq], qa[:, :Dq]]).reshape(-1, Hh, dh)
         K = torch.cat([qv[:, Dq:2 * Dq], qa[:, Dq:2 * Dq]]).reshape(-1, Hh, dh)
         V = torch.cat([qv[:, 2 * Dq:], qa[:, 2 * Dq:]]).reshape(-1, Hh, dh)
+        pos = token_positions(cfg, 0, Nv + H)   # the joint sequence's own order
+        if pos is not None:
+            Q, K = rope(Q, pos), rope(K, pos)
         kv.append((K[:Nv], V[:Nv]))
         O = attention(Q, K, V, lambda q0, q1: full[q0:q1]).reshape(-1, Dq)
         Xv = Xv + O[:Nv] @ lv["wo"].T

@@ -384,17 +384,22 @@ def _tiny(**kw):
     return configs.small("T", **base)
 
 
-def test_joint_sequence_equals_cached_path():
+@pytest.mark.parametrize("rope", [False, True])
+def test_joint_sequence_equals_cached_path(rope):
     # Asymmetric mask => caching is exact: one joint [video ; action] pass with
     # the explicit mask reproduces the cache rows and the first action v-hat.
-    cfg = _tiny()
+    # With the rotary option the joint pass takes positions from its own
+    # sequence order, the cached path from the history, future and action
+    # offsets it computes separately.
+    cfg = _tiny(rope=rope)
     inp = inputs.generate(cfg, threads=1)
     vw = O.to_torch_expert(inp["video"], f64)
     aw = O.to_torch_expert(inp["action"], f64)
     cache, z, frames = O.video_prefill(cfg, vw, inp["hist"][0], inp["hist_valid"][0], inp["eps_v"][0])
     t0 = float(O.schedule(cfg.N, 0.0)[0])
     a = torch.tensor(inp["eps_a"][0], dtype=f64)
-    v_cached = O.action_velocity(cfg, aw, O.read_layers(cfg, cache, None), a, t0)
+    v_cached = O.action_velocity(cfg, aw, O.read_layers(cfg, cache, None), a, t0,
+                                 int(cache[0][0].shape[0]))
 
     valid_frames = [f for f in range(cfg.Fh) if inp["hist_valid"][0][f]]
     hist_tok = torch.tensor(inp["hist"][0][valid_frames], dtype=f64).reshape(-1, cfg.Cv)
@@ -624,8 +629,8 @@ def test_fp8_option_touches_only_what_the_action_layers_read():
 
 
 # ---------------------------------------------------------------- streaming history
-def _extended_and_full(blocks, pad, n_old):
-    cfg = _tiny(Fh=5, Ff=2, frame_block=blocks, pad_frames=pad)
+def _extended_and_full(blocks, pad, n_old, rope=False):
+    cfg = _tiny(Fh=5, Ff=2, frame_block=blocks, pad_frames=pad, rope=rope)
     inp = inputs.generate(cfg, threads=1)
     vw = O.to_torch_expert(inp["video"], f64)
     hist, valid = inp["hist"][0], inp["hist_valid"][0]
@@ -658,3 +663,54 @@ def test_extending_inside_a_block_is_not_exact():
     # the cached half stale, which is why the C-ABI rejects such a split
     full, ext = _extended_and_full((0, 0, 1, 1, 2, 3, 4), 0, 3)
     assert max(float(torch.max(torch.abs(Kf - Ke))) for (Kf, _), (Ke, _) in zip(full, ext)) > 1e-6
+
+
+# ---------------------------------------------------------------- rotary option
+def test_rope_closed_forms():
+    c1, s1, c5, s5 = math.cos(1), math.sin(1), math.cos(5), math.sin(5)
+    # one pair (dh = 2): (x0 + i x1) exp(i p)
+    x = torch.tensor([[[1.0, 0.0]], [[0.0, 1.0]], [[0.3, -0.7]]], dtype=f64)
+    y = O.rope(x, torch.tensor([1, 1, 5]))
+    want = torch.tensor([[[c1, s1]], [[-s1, c1]], [[0.3 * c5 + 0.7 * s5, 0.3 * s5 - 0.7 * c5]]],
+                        dtype=f64)
+    assert torch.max(torch.abs(y - want)) < 1e-15
+    # dh = 4: pair 0 turns at rate 1, pair 1 at 10000^(-1/2) = 0.01
+    y4 = O.rope(torch.tensor([[[1.0, 0.0, 1.0, 0.0]]], dtype=f64), torch.tensor([100]))
+    want4 = torch.tensor([math.cos(100), math.sin(100), c1, s1], dtype=f64)
+    assert torch.max(torch.abs(y4[0, 0] - want4)) < 1e-13
+    # position 0 is the identity; every pair keeps its length
+    r = torch.randn((7, 3, 8), dtype=f64, generator=torch.Generator().manual_seed(3))
+    assert torch.equal(O.rope(r, torch.zeros(7, dtype=torch.int64)), r)
+    rr = O.rope(r, torch.arange(7) * 977)
+    n0 = r[..., 0::2] ** 2 + r[..., 1::2] ** 2
+    n1 = rr[..., 0::2] ** 2 + rr[..., 1::2] ** 2
+    assert torch.max(torch.abs(n0 - n1)) < 1e-12
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn((1, 2, 16), dtype=f64, generator=g)
+    k = torch.randn((1, 2, 16), dtype=f64, generator=g)
+
+    def score(m, n):
+        return (O.rope(q, torch.tensor([m])) * O.rope(k, torch.tensor([n]))).sum(-1)
+
+    for m, n, sh in [(3, 0, 11), (0, 40, 1000), (9216, 17, 123)]:
+        assert torch.max(torch.abs(score(m, n) - score(m + sh, n + sh))) < 1e-9
+    assert torch.max(torch.abs(score(3, 0) - score(4, 0))) > 1e-3
+
+
+def test_rope_option_padding_and_streaming():
+    cfg = _tiny(rope=True)
+    inp = inputs.generate(cfg, threads=1)
+    ref = O.run_chunk(cfg, inp, drop_padded=True)
+    kept = O.run_chunk(cfg, inp, drop_padded=False)
+    # positions count valid tokens: padded frames left out or kept and masked agree
+    assert np.max(np.abs(ref["actions"] - kept["actions"])) < 1e-12
+    # the option does change the result
+    assert np.max(np.abs(ref["actions"] - O.run_chunk(_tiny(), inp)["actions"])) > 1e-6
+    # appending whole blocks leaves every cached row (and its position) unchanged
+    full, ext = _extended_and_full((0, 1, 2, 3, 4, 5, 6), 1, 3, rope=True)
+    for (Kf, Vf), (Ke, Ve) in zip(full, ext):
+        assert torch.max(torch.abs(Kf - Ke)) < 1e-12
+        assert torch.max(torch.abs(Vf - Ve)) < 1e-12
