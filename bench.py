@@ -119,7 +119,7 @@ def yardsticks() -> dict:
     return out
 
 
-def cpu_baseline(cfg_name: str, layers: int, kv_fp8: bool = False) -> dict:
+def cpu_baseline(cfg_name: str, layers: int, kv_fp8: bool = False, rope: bool = False) -> dict:
     import numpy as np  # noqa: F401
     import torch
 
@@ -132,7 +132,7 @@ def cpu_baseline(cfg_name: str, layers: int, kv_fp8: bool = False) -> dict:
         # one interaction layer (the last) reading the fusion of the sampled layers
         kw["fuse"] = ((0, layers),)
         kw["read_map"] = (-1,) * (layers - 1) + (0,)
-    cfg = configs.get(cfg_name, kv_fp8=kv_fp8, **kw)
+    cfg = configs.get(cfg_name, kv_fp8=kv_fp8, rope=rope, **kw)
     inp = inputs.generate(cfg)
     t0 = time.perf_counter()
     if cfg.joint:
@@ -162,6 +162,9 @@ def main():
     ap.add_argument("--kv-fp8", action="store_true",
                     help="the action layers read an E4M3 copy of the cache (an option that departs "
                          "from the pages' bf16 cache; quantised once per chunk)")
+    ap.add_argument("--rope", action="store_true",
+                    help="rotary position option: Q and K of both experts rotated by their "
+                         "token's index in the joint sequence")
     ap.add_argument("--minimal", action="store_true",
                     help="only warmup + timed chunks (for counter collection)")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -190,7 +193,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n * 4}))
         return
-    cfg = configs.get(args.config, kv_fp8=True) if args.kv_fp8 else configs.get(args.config)
+    cfg = configs.get(args.config, kv_fp8=args.kv_fp8, rope=args.rope)
     inp = inputs.generate(cfg)
     dc = DeviceChunk(cfg, inp)
     print(f"[bench] {cfg.name}: inputs resident, warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -279,6 +282,7 @@ def main():
         "data": "synthetic (seeded N(0,1) latents/noise, N(0,0.02^2) random-init weights)",
         "config": {"workload": f"{cfg.name}: {WORKLOAD_TEXT.get(cfg.name, '')}"
                                + (", E4M3 K/V read by the action layers" if cfg.kv_fp8 else "")
+                               + (", rotary positions on Q and K" if cfg.rope else "")
                                + (f", streamed: {args.stream} new history frame(s) per decision"
                                   if args.stream else ""),
                    "kv_cache": "e4m3" if cfg.kv_fp8 else ("bf16" if cfg.dtype == "bf16" else "f32"),
@@ -286,7 +290,7 @@ def main():
                    "L": cfg.L, "D": cfg.D, "heads": f"{cfg.Hh}x{cfg.dh}", "kv_tokens": cfg.tokens_valid,
                    "action_steps": cfg.N, "video_steps": cfg.N if cfg.joint else cfg.V,
                    "streamed_new_frames": args.stream,
-                   "joint": cfg.joint},
+                   "joint": cfg.joint, "rope": cfg.rope},
         "roofline": roofline,
         "attn_action_hbm_gbps": kt.get("attn_action", {}).get("achieved"),
         "prefill_attn_mfma_util": kt.get("attn_prefill", {}).get("frac"),
@@ -298,7 +302,7 @@ def main():
     rec["yardsticks"] = yardsticks()
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(cfg.name, min(args.cpu_layers, cfg.L), cfg.kv_fp8)
+        rec["cpu_baseline"] = cpu_baseline(cfg.name, min(args.cpu_layers, cfg.L), cfg.kv_fp8, cfg.rope)
     print(json.dumps(rec), flush=True)
 
 

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define WAM_ABI_VERSION 2
+#define WAM_ABI_VERSION 3
 #define WAM_MAX_FRAMES 256   /* latent frames per episode (history + future) */
 #define WAM_MAX_BATCH 64     /* episodes per call */
 #define WAM_MAX_FUSE 32      /* fused pairs per wam_fuse_interval_kv call */
@@ -82,7 +82,18 @@ typedef struct {
   int dtype;  /* WAM_F32 or WAM_BF16 */
   int Da;     /* action expert width (0: D); its Wqkv is [3 Hh dh][Da], Wo [Da][Hh dh] */
   int Fma;    /* action expert MLP inner width (0: Fm) */
+  int rope;   /* 0: no position embedding (C1-C6); 1: rotary option, below */
 } wam_dims;
+
+/* Rotary option (rope = 1).  The pages say only that rotary position tables
+ * are computed once per inference call and reused across the denoising steps
+ * (Long-WAM Summary section 4.2).  Here, in both experts, every layer rotates
+ * Q and K after the projection (K before it is cached): pair j of a head,
+ * x[2j] + i x[2j+1], is multiplied by exp(i p w_j), w_j = 10000^(-2j/dh),
+ * where p is the token's index in its episode's joint sequence
+ * [cached rows in cache order ; the action chunk]: cache row r is at p = r,
+ * action token i at p = len[b] + i (i alone where no cache is given).
+ * Angles, sines and cosines in float64, rounded to float32 once. */
 
 /* One layer: Y = RMSNorm(X; g1); [Q K V] = Y Wqkv^T; X += Attn Wo^T;
  * X += GELU(RMSNorm(X; g2) W1^T) W2^T.  No biases.  RMSNorm eps = 1e-6. */

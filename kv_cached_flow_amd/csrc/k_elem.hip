@@ -644,4 +644,53 @@ hipError_t quantize_kv_fp8(hipStream_t s, const void* k, const void* v, void* k8
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- rotary option
+// Rotary position embedding in place on one or two tensors of layout
+// [G][Hh][rows][dh] (group stride gs, head stride hs): row r of group g is the
+// token at position base[g] + r, and pair j = (x[2j], x[2j+1]) of every head
+// is multiplied, as x[2j] + i x[2j+1], by exp(i p w_j), w_j = 10000^(-2j/dh).
+// One thread per (row, pair) computes the angle and its sine and cosine in
+// float64, rounds them to float32 once, and rotates that pair in every head
+// of both tensors.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ x0, long long gs0, long long hs0,
+                                                   T* __restrict__ x1, long long gs1, long long hs1,
+                                                   int rows, int Hh, int dh, RopeRows rb) {
+  const int half = dh >> 1, g = blockIdx.y;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)rows * half) return;
+  const int r = (int)(i / half), j = (int)(i - (long long)r * half);
+  const double w = pow(10000.0, -2.0 * j / dh);
+  double sd, cd;
+  sincos((double)(rb.base[g] + r) * w, &sd, &cd);
+  const float c = (float)cd, sn = (float)sd;
+  const long long off = (long long)r * dh + 2 * j;
+  auto rot = [&](T* p) {
+    const float a = to_f<T>(p[0]), b = to_f<T>(p[1]);
+    p[0] = from_f<T>(a * c - b * sn);
+    p[1] = from_f<T>(a * sn + b * c);
+  };
+  for (int h = 0; h < Hh; h++) {
+    rot(x0 + g * gs0 + h * hs0 + off);
+    if (x1) rot(x1 + g * gs1 + h * hs1 + off);
+  }
+}
+
+hipError_t rope_qk(hipStream_t s, int dt, void* x0, long long gs0, long long hs0, void* x1,
+                   long long gs1, long long hs1, int G, int rows, int Hh, int dh,
+                   const RopeRows& rb) {
+  if (rows <= 0 || G <= 0) return hipSuccess;
+  if (G > WAM_MAX_BATCH || dh % 2) return hipErrorInvalidValue;
+  const double es = dt == WAM_BF16 ? 2.0 : 4.0;
+  TimingScope ts(s, KC_MISC, (x1 ? 4.0 : 2.0) * G * Hh * (double)rows * dh * es, 0.0);
+  dim3 grid((unsigned)(((long long)rows * (dh / 2) + 255) / 256), G);
+  if (dt == WAM_BF16)
+    hipLaunchKernelGGL(rope_kernel<bf16_t>, grid, dim3(256), 0, s, (bf16_t*)x0, gs0, hs0,
+                       (bf16_t*)x1, gs1, hs1, rows, Hh, dh, rb);
+  else
+    hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, s, (float*)x0, gs0, hs0,
+                       (float*)x1, gs1, hs1, rows, Hh, dh, rb);
+  return hipGetLastError();
+}
+
 }  // namespace wam

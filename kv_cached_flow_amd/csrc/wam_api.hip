@@ -62,6 +62,7 @@ int check_dims(const wam_dims* d) {
     return fail(WAM_E_SHAPE, "Da and Fma must be 0 or positive multiples of 64");
   if (d->D > 4096 || d->Da > 4096) return fail(WAM_E_SHAPE, "expert widths above 4096 are not supported");
   if (d->H != 32) return fail(WAM_E_SHAPE, "action chunk length must be 32 (got %d)", d->H);
+  if (d->rope != 0 && d->rope != 1) return fail(WAM_E_ARG, "rope must be 0 or 1");
   if (d->Cv < 1 || d->Cv > 64 || d->A < 1 || d->A > 64)
     return fail(WAM_E_SHAPE, "Cv and A must be in [1, 64]");
   return WAM_OK;
@@ -207,13 +208,21 @@ int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const Fra
   e.k_row0 = row0;
   e.v_ld = cap;
   e.v_col0 = row0;
+  // rotary option: Q rows and the K rows just cached sit at positions row0 ..
+  RopeRows rb{};
+  rb.base[0] = row0;
+  void* krows = (char*)kl + (size_t)row0 * d->dh * esz(dt);
   if (kv_only) {
     e.n_begin = D;
     HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, 2 * D, D, b.Y, D,
                (const char*)w.wqkv + (size_t)D * D * esz(dt), D, e));
+    if (d->rope)
+      HIPCK(rope_qk(c.s, dt, krows, 0, e.k_hs, nullptr, 0, 0, 1, n, d->Hh, d->dh, rb));
     return WAM_OK;
   }
   HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, 3 * D, D, b.Y, D, w.wqkv, D, e));
+  if (d->rope)
+    HIPCK(rope_qk(c.s, dt, b.Q, 0, e.q_hs, krows, 0, e.k_hs, 1, n, d->Hh, d->dh, rb));
   HIPCK(attn_prefill(c.s, dt, d->Hh, d->dh, n, row0, tab, b.Q, kl, vl, cap, b.O, b.pattn, b.pattn_bytes));
   if ((st = video_resid(c, n, D, D, b.O, w.wo))) return st;
   if ((st = norm_rows(c, dt, w.g2, b.Y, n))) return st;
@@ -298,6 +307,12 @@ int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, co
   e.v_ld = H;
   if ((st = norm_rows(c, dt, w.g1, b.Y, M))) return st;
   HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, M, 3 * Dq, D, b.Y, D, w.wqkv, D, e));
+  if (d->rope) {
+    // action token i of episode b follows that episode's cached rows
+    RopeRows rb{};
+    for (int i = 0; i < B; i++) rb.base[i] = lens.len[i];
+    HIPCK(rope_qk(c.s, dt, b.Q, e.q_gs, e.q_hs, b.Ka, e.k_gs, e.k_hs, B, H, d->Hh, d->dh, rb));
+  }
   HIPCK(attn_action(c.s, dt, B, d->Hh, H, d->dh, b.Q, b.Ka, b.Va, H, kc, vc, cap, lens, b.O, 0, b.attn,
                     b.attn_bytes, ksc, vsc));
   if ((st = action_resid(c, M, D, Dq, b.O, w.wo))) return st;

@@ -226,6 +226,16 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, int dh, cons
 
 // bf16 cache (n_layers x B episodes) -> E4M3 cache with power-of-two tile
 // scales, rows [0, len[b]) of every episode.
+// Rotary position embedding in place on x0 (and x1 unless NULL), layout
+// [G][Hh][rows][dh] with group stride gs and head stride hs (elements); row r
+// of group g sits at position base[g] + r.
+struct RopeRows {
+  int base[WAM_MAX_BATCH];
+};
+hipError_t rope_qk(hipStream_t s, int dt, void* x0, long long gs0, long long hs0, void* x1,
+                   long long gs1, long long hs1, int G, int rows, int Hh, int dh,
+                   const RopeRows& rb);
+
 hipError_t quantize_kv_fp8(hipStream_t s, const void* k, const void* v, void* k8, void* v8,
                            float* ks, float* vs, int n_layers, int B, int Hh, int cap,
                            const ActLens& lens);

@@ -40,7 +40,7 @@ class DeviceChunk:
         self.cfg = cfg
         self.dt = wam.WAM_BF16 if cfg.dtype == "bf16" else wam.WAM_F32
         self.dims = wam.dims(cfg.L, cfg.D, cfg.Hh, cfg.dh, cfg.Fm, cfg.Cv, cfg.A, cfg.H, cfg.P, self.dt,
-                             cfg.Da, cfg.Fma)
+                             cfg.Da, cfg.Fma, int(cfg.rope))
         tdt = _tdt(cfg)
         self.video = upload_expert(inp["video"], cfg, device)
         self.action = upload_expert(inp["action"], cfg, device)

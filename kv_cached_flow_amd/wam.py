@@ -30,7 +30,7 @@ class WamError(RuntimeError):
 
 class WamDims(C.Structure):
     _fields_ = [(n, C.c_int) for n in ("L", "D", "Hh", "dh", "Fm", "Cv", "A", "H", "P", "dtype", "Da",
-                                        "Fma")]
+                                        "Fma", "rope")]
 
 
 class WamLayerW(C.Structure):
@@ -171,9 +171,10 @@ def frame_table(frame_block: Sequence[int], valid: Optional[Sequence[int]], Fh: 
 
 
 # ------------------------------------------------------------------ device structs
-def dims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype, Da=0, Fma=0) -> WamDims:
-    """Shapes of a call; Da / Fma: the action expert's width and MLP width (0: D / Fm)."""
-    return WamDims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype, Da, Fma)
+def dims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype, Da=0, Fma=0, rope=0) -> WamDims:
+    """Shapes of a call; Da / Fma: the action expert's width and MLP width (0: D / Fm);
+    rope: 1 for the rotary position option."""
+    return WamDims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype, Da, Fma, rope)
 
 
 class DeviceExpert:

@@ -27,7 +27,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(wam.exported_names()) == names
-    assert wam.abi_version() == 2
+    assert wam.abi_version() == 3
 
 
 def test_status_strings():
@@ -124,6 +124,8 @@ def test_prefill_validation_errors():
     assert call_prefill(d=good_dims(Fma=-64))[0] == -2
     assert call_prefill(d=good_dims(Hh=80, D=5120))[0] == -2  # widths above 4096
     assert call_prefill(d=good_dims(Hh=2, dh=96, D=192))[0] == -2  # heads of 64 or 128 only
+    assert call_prefill(d=good_dims(rope=2))[0] == -1              # rope is 0 or 1
+    assert call_prefill(d=good_dims(rope=1), ws_bytes=4096)[0] == -5  # accepted up to the workspace
     kv128, _k = fake_kv(Hh=2, dh=128)
     assert call_prefill(d=good_dims(Hh=2, dh=128), kv=kv128, ws_bytes=4096)[0] == -5  # 128 accepted
     assert call_prefill(d=good_dims(Hh=2, dh=128), kv=fake_kv(Hh=2)[0])[0] == -2     # cache dh differs
