@@ -649,14 +649,16 @@ hipError_t quantize_kv_fp8(hipStream_t s, const void* k, const void* v, void* k8
 // [G][Hh][rows][dh] (group stride gs, head stride hs): row r of group g is the
 // token at position base[g] + r, and pair j = (x[2j], x[2j+1]) of every head
 // is multiplied, as x[2j] + i x[2j+1], by exp(i p w_j), w_j = 10000^(-2j/dh).
-// One thread per (row, pair) computes the angle and its sine and cosine in
-// float64, rounds them to float32 once, and rotates that pair in every head
-// of both tensors.
+// One thread per (row, pair, group of RH heads) computes the angle and its
+// sine and cosine in float64, rounds them to float32 once, loads the pair of
+// each of its heads in both tensors, then rotates and stores them: the loads
+// are all in flight together.
+constexpr int RH = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ x0, long long gs0, long long hs0,
                                                    T* __restrict__ x1, long long gs1, long long hs1,
                                                    int rows, int Hh, int dh, RopeRows rb) {
-  const int half = dh >> 1, g = blockIdx.y;
+  const int half = dh >> 1, g = blockIdx.y, h0 = blockIdx.z * RH;
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= (long long)rows * half) return;
   const int r = (int)(i / half), j = (int)(i - (long long)r * half);
@@ -665,14 +667,28 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ x0, long long
   sincos((double)(rb.base[g] + r) * w, &sd, &cd);
   const float c = (float)cd, sn = (float)sd;
   const long long off = (long long)r * dh + 2 * j;
-  auto rot = [&](T* p) {
-    const float a = to_f<T>(p[0]), b = to_f<T>(p[1]);
-    p[0] = from_f<T>(a * c - b * sn);
-    p[1] = from_f<T>(a * sn + b * c);
-  };
-  for (int h = 0; h < Hh; h++) {
-    rot(x0 + g * gs0 + h * hs0 + off);
-    if (x1) rot(x1 + g * gs1 + h * hs1 + off);
+  T* p0[RH];
+  T* p1[RH];
+  float a0[RH], b0[RH], a1[RH], b1[RH];
+#pragma unroll
+  for (int u = 0; u < RH; u++) {
+    const int h = min(h0 + u, Hh - 1);  // heads past Hh repeat the last one and store nothing
+    p0[u] = x0 + g * gs0 + h * hs0 + off;
+    p1[u] = x1 ? x1 + g * gs1 + h * hs1 + off : p0[u];
+    a0[u] = to_f<T>(p0[u][0]);
+    b0[u] = to_f<T>(p0[u][1]);
+    a1[u] = to_f<T>(p1[u][0]);
+    b1[u] = to_f<T>(p1[u][1]);
+  }
+#pragma unroll
+  for (int u = 0; u < RH; u++) {
+    if (h0 + u >= Hh) break;
+    p0[u][0] = from_f<T>(a0[u] * c - b0[u] * sn);
+    p0[u][1] = from_f<T>(a0[u] * sn + b0[u] * c);
+    if (x1) {
+      p1[u][0] = from_f<T>(a1[u] * c - b1[u] * sn);
+      p1[u][1] = from_f<T>(a1[u] * sn + b1[u] * c);
+    }
   }
 }
 
@@ -683,7 +699,7 @@ hipError_t rope_qk(hipStream_t s, int dt, void* x0, long long gs0, long long hs0
   if (G > WAM_MAX_BATCH || dh % 2) return hipErrorInvalidValue;
   const double es = dt == WAM_BF16 ? 2.0 : 4.0;
   TimingScope ts(s, KC_MISC, (x1 ? 4.0 : 2.0) * G * Hh * (double)rows * dh * es, 0.0);
-  dim3 grid((unsigned)(((long long)rows * (dh / 2) + 255) / 256), G);
+  dim3 grid((unsigned)(((long long)rows * (dh / 2) + 255) / 256), G, (Hh + RH - 1) / RH);
   if (dt == WAM_BF16)
     hipLaunchKernelGGL(rope_kernel<bf16_t>, grid, dim3(256), 0, s, (bf16_t*)x0, gs0, hs0,
                        (bf16_t*)x1, gs1, hs1, rows, Hh, dh, rb);
