@@ -84,11 +84,13 @@ def test_rotary_codenoise(dtype):
     assert rel_l2(to_np(dc.z).reshape(ref["z"].shape), ref["z"]) <= tol
 
 
-def test_rotary_streamed_history():
+@pytest.mark.parametrize("dh", [64, 128])
+def test_rotary_streamed_history(dh):
     # frames appended one block at a time keep their positions: the streamed
     # chunk equals the oracle's one-prefill chunk
-    cfg = configs.small("RST", dtype="f32", **dict(SMALL, Fh=4, frame_block=(0, 1, 2, 3, 4, 5)))
-    print_case("rotary option, streamed history (1, 1, 2 frames)")
+    cfg = configs.small("RST", dtype="f32", **dict(SMALL, Fh=4, frame_block=(0, 1, 2, 3, 4, 5),
+                                                    Hh=256 // dh, dh=dh))
+    print_case(f"rotary option, streamed history (1, 1, 2 frames), dh {dh}")
     inp = inputs.generate(cfg)
     dc = DeviceChunk(cfg, inp)
     d, B = dc.dims, cfg.B
