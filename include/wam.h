@@ -123,8 +123,10 @@ typedef struct {
  * Rows 0..len[b]-1 of episode b are valid: the valid history frames in frame
  * order, then the future frames.  cap must be a multiple of 64.
  * dtype WAM_FP8 (one byte per element; written by wam_quantize_kv_fp8 only):
- *   within each K row, bytes 16g..16g+7 hold dims 8g..8g+7 and bytes
- *   16g+8..16g+15 dims 32+8g..32+8g+7 (g = 0..3); within each 64-key tile of
+ *   within each K row, with U = dh/64 and g = 0..3, u = 0..U-1, bytes
+ *   16(Ug+u)..+7 hold dims 64u+8g..+7 and bytes 16(Ug+u)+8..+15 dims
+ *   64u+32+8g..+7 (dh = 64: bytes 16g.. dims 8g.., bytes 16g+8.. dims
+ *   32+8g..); within each 64-key tile of
  *   a V row, bytes 16g..16g+7 hold keys 8g..8g+7 of the tile and bytes
  *   16g+8..16g+15 keys 32+8g..32+8g+7.  k_scale, v_scale: device
  *   [n_layers][B][Hh][cap/64] fp32, each a power of two; a value is
@@ -257,8 +259,7 @@ int wam_fuse_interval_kv(const wam_kv* src, int M, const int32_t* start,
  * rounded to nearest even, scale = 2^e.  Codes of rows >= len[b] in the last
  * tile are 0; later tiles are not written.  dst->len is set to src->len.
  *   src: dtype WAM_BF16; dst: dtype WAM_FP8 with the same n_layers, B, Hh,
- *   dh and cap, k_scale and v_scale set.  dh must be 64 (the E4M3 byte
- *   order is defined for 64-wide rows).
+ *   dh (64 or 128) and cap, k_scale and v_scale set.
  * ------------------------------------------------------------------------- */
 int wam_quantize_kv_fp8(const wam_kv* src, wam_kv* dst, void* stream);
 
@@ -381,7 +382,7 @@ int wam_attention_action(int dtype, int B, int Hh, int dh, int H, const void* q,
                          void* out, int splits_hint, void* ws, size_t ws_bytes, void* stream);
 /* dh is 64 or 128 in both attention entries; WAM_E_SHAPE otherwise.
  * The same over an E4M3 cache layer (layouts and scales [B][Hh][cap/64] as
- * in wam_kv with dtype WAM_FP8, dh = 64 only); q, ka, va, out bf16.  ws as
+ * in wam_kv with dtype WAM_FP8); q, ka, va, out bf16.  ws as
  * above (bf16). */
 int wam_attention_action_fp8(int B, int Hh, int dh, int H, const void* q, const void* ka,
                              const void* va, int n_act, const void* kc8, const void* vc8,

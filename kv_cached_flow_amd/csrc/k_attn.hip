@@ -701,10 +701,10 @@ __device__ inline void zero_v_tail(bf16x8 (&av)[DH / 16][2], int kt, int key1, i
 // log2 domain: m [32], l [32], o [32][64] (unnormalised).
 // F8: the cache is E4M3 (kc, vc bytes; ksc, vsc tile scales [B][Hh][cap/64]).
 // Its rows are stored in the order the lanes consume them, so one 16-byte
-// load gives a lane both 8-element fragments of a K row (dims 8g.. and
-// 32+8g..) or of a V^T row (keys 8g.. and 32+8g.. of the tile); converted
-// with the tile's scale they are the bf16 operands of the same MFMAs.  The
-// chunk's own keys stay bf16.
+// load gives a lane two 8-element fragments of a K row (dims 64u + 8g.. and
+// 64u + 32 + 8g.., lane group g's DH/4 bytes contiguous) or of a V^T row
+// (keys 8g.. and 32+8g.. of the tile); converted with the tile's scale they
+// are the bf16 operands of the same MFMAs.  The chunk's own keys stay bf16.
 template <bool F8, int DH>
 __global__ __launch_bounds__(256, 2) void attn_action_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ ka, const bf16_t* __restrict__ va,
@@ -712,7 +712,6 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
     const float* __restrict__ vsc, ActGeom G, float* __restrict__ part, float sl2) {
   using namespace act;
   static_assert(DH == 64 || DH == 128, "head dim");
-  static_assert(!F8 || DH == 64, "the E4M3 cache layout is for dh = 64");
   constexpr int NS = DH / 32, ND = DH / 16;
   __shared__ float sm[4][H], sl[4][H];
   __shared__ float so[4][H][DH + 1];
@@ -735,8 +734,8 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
     kb = (const bf16_t*)kc + hb * G.cap * DH;
     vb = (const bf16_t*)vc + hb * DH * G.cap;
     if constexpr (F8) {
-      k8 = (const uint8_t*)kc + hb * G.cap * 64;
-      v8 = (const uint8_t*)vc + hb * 64 * G.cap;
+      k8 = (const uint8_t*)kc + hb * G.cap * DH;
+      v8 = (const uint8_t*)vc + hb * DH * G.cap;
       ksh = ksc + hb * (G.cap / 64);
       vsh = vsc + hb * (G.cap / 64);
     }
@@ -771,9 +770,41 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
       const bool first = kt == key0 + w * KT;
       floatx4 sacc[4][2];
       bf16x8 ak[4][NS], av[ND][2];
-      bf16_k_tile<DH>(ak, kb, kt, key1, c16, g);
+      const bool f8 = F8 && !own;  // an E4M3 split (kt is then a multiple of 64)
+      if (f8) {
+        const float sk = ksh[kt >> 6];
+        u32x4 rk[4][2];
+#pragma unroll
+        for (int sub = 0; sub < 4; sub++) {
+          const int key = min(kt + perm_key(sub, c16), key1 - 1);
+#pragma unroll
+          for (int u = 0; u < 2; u++) rk[sub][u] = *(const u32x4*)(k8 + (long long)key * DH + 32 * g + 16 * u);
+        }
+#pragma unroll
+        for (int sub = 0; sub < 4; sub++)
+#pragma unroll
+          for (int u = 0; u < 2; u++) {
+            ak[sub][2 * u] = e4m3x8_bf16(rk[sub][u][0], rk[sub][u][1], sk);
+            ak[sub][2 * u + 1] = e4m3x8_bf16(rk[sub][u][2], rk[sub][u][3], sk);
+          }
+      } else {
+        bf16_k_tile<DH>(ak, kb, kt, key1, c16, g);
+      }
       tile_scores(sacc, qf, acc, first, [&](int sub, int ss) { return ak[sub][ss]; });
-      bf16_v_tile<DH>(av, vb, kt, key0, key1, vld, c16, g);
+      if (f8) {
+        const float sv = vsh[kt >> 6];
+        u32x4 rv[ND];
+#pragma unroll
+        for (int d = 0; d < ND; d++)
+          rv[d] = *(const u32x4*)(v8 + (long long)(16 * d + c16) * G.cap + kt + 16 * g);
+#pragma unroll
+        for (int d = 0; d < ND; d++) {
+          av[d][0] = e4m3x8_bf16(rv[d][0], rv[d][1], sv);
+          av[d][1] = e4m3x8_bf16(rv[d][2], rv[d][3], sv);
+        }
+      } else {
+        bf16_v_tile<DH>(av, vb, kt, key0, key1, vld, c16, g);
+      }
       if (tail) {
         zero_v_tail<DH>(av, kt, key1, g);
         tile_mask(sacc, kt, kq, g);
@@ -1009,7 +1040,7 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, int dh, cons
                        const float* vsc) {
   const bool f8 = ksc != nullptr;
   if (f8 && (dt != WAM_BF16 || !vsc || !kc)) return hipErrorInvalidValue;
-  if (H != act::H || (dh != 64 && dh != 128) || (f8 && dh != 64)) return hipErrorInvalidValue;
+  if (H != act::H || (dh != 64 && dh != 128)) return hipErrorInvalidValue;
   const float scale = dh == 64 ? 0.125f : 0.08838834764831845f;  // 1 / sqrt(dh)
   ActGeom G;
   G.B = B;
@@ -1051,8 +1082,12 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, int dh, cons
     TimingScope ts(s, KC_ATTN_ACTION, kv_bytes + 1.0 * B * H * Hh * dh * es,
                    4.0 * dh * Hh * H * keys);
     const float sl2 = scale * LOG2E;
-    if (f8)
+    if (f8 && dh == 64)
       hipLaunchKernelGGL((attn_action_kernel<true, 64>), dim3(G.S, Hh, B), dim3(256), 0, s,
+                         (const bf16_t*)q, (const bf16_t*)ka, (const bf16_t*)va, kc, vc, ksc, vsc,
+                         G, (float*)scratch, sl2);
+    else if (f8)
+      hipLaunchKernelGGL((attn_action_kernel<true, 128>), dim3(G.S, Hh, B), dim3(256), 0, s,
                          (const bf16_t*)q, (const bf16_t*)ka, (const bf16_t*)va, kc, vc, ksc, vsc,
                          G, (float*)scratch, sl2);
     else if (dh == 64)

@@ -558,6 +558,7 @@ hipError_t fuse_kv(hipStream_t s, int dt, const void* src, void* dst, long long 
 // amax = m 2^q (m in [0.5, 1)), the smallest e with amax <= 448 2^e =
 // 0.875 2^(9+e) is q-9 when m <= 0.875, else q-8.  Scaling by 2^-e is exact,
 // and v_cvt_pk_fp8_f32 rounds to nearest even (|x 2^-e| <= 448).
+template <int DH>
 __global__ __launch_bounds__(256) void quantize_kv_kernel(const bf16_t* __restrict__ k,
                                                           const bf16_t* __restrict__ v,
                                                           uint8_t* __restrict__ k8,
@@ -565,43 +566,53 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const bf16_t* __restri
                                                           float* __restrict__ ks,
                                                           float* __restrict__ vs, int B, int Hh,
                                                           int cap, ActLens lens) {
+  // NU units of 16 elements per thread: K row r, dims 64u + {8g.., 32 + 8g..};
+  // V^T rows r + 64u, keys {8g.., 32 + 8g..} of the tile
+  constexpr int NU = DH / 64;
   __shared__ float wmax[4];
   const int t = blockIdx.x, h = blockIdx.y, which = blockIdx.z & 1, lb = blockIdx.z >> 1;
   const int len = lens.len[lb % B];
   if (t * 64 >= len) return;
   const int tid = threadIdx.x, r = tid >> 2, g = tid & 3;
-  const long long head = ((long long)lb * Hh + h) * cap * 64;  // one head's elements
-  float x[16];
-  long long dst;
+  const long long head = ((long long)lb * Hh + h) * cap * DH;  // one head's elements
+  float x[16 * NU];
+  long long dst[NU];
   if (which == 0) {
     const int key = t * 64 + r;
-    dst = head + (long long)key * 64 + 16 * g;
-    if (key < len) {
-      const bf16x8 a = *(const bf16x8*)(k + head + (long long)key * 64 + 8 * g);
-      const bf16x8 b = *(const bf16x8*)(k + head + (long long)key * 64 + 32 + 8 * g);
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        x[j] = bf2f((bf16_t)a[j]);
-        x[8 + j] = bf2f((bf16_t)b[j]);
+    for (int u = 0; u < NU; u++) {
+      // a lane group's NU * 16 bytes of a K row are contiguous
+      dst[u] = head + (long long)key * DH + 16 * NU * g + 16 * u;
+      if (key < len) {
+        const bf16x8 a = *(const bf16x8*)(k + head + (long long)key * DH + 64 * u + 8 * g);
+        const bf16x8 b = *(const bf16x8*)(k + head + (long long)key * DH + 64 * u + 32 + 8 * g);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          x[16 * u + j] = bf2f((bf16_t)a[j]);
+          x[16 * u + 8 + j] = bf2f((bf16_t)b[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; j++) x[16 * u + j] = 0.f;
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; j++) x[j] = 0.f;
     }
   } else {
-    const long long row = head + (long long)r * cap + t * 64;
-    dst = row + 16 * g;
-    const bf16x8 a = *(const bf16x8*)(v + row + 8 * g);
-    const bf16x8 b = *(const bf16x8*)(v + row + 32 + 8 * g);
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      x[j] = (t * 64 + 8 * g + j < len) ? bf2f((bf16_t)a[j]) : 0.f;
-      x[8 + j] = (t * 64 + 32 + 8 * g + j < len) ? bf2f((bf16_t)b[j]) : 0.f;
+    for (int u = 0; u < NU; u++) {
+      const long long row = head + (long long)(r + 64 * u) * cap + t * 64;
+      dst[u] = row + 16 * g;
+      const bf16x8 a = *(const bf16x8*)(v + row + 8 * g);
+      const bf16x8 b = *(const bf16x8*)(v + row + 32 + 8 * g);
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        x[16 * u + j] = (t * 64 + 8 * g + j < len) ? bf2f((bf16_t)a[j]) : 0.f;
+        x[16 * u + 8 + j] = (t * 64 + 32 + 8 * g + j < len) ? bf2f((bf16_t)b[j]) : 0.f;
+      }
     }
   }
   float amax = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; j++) amax = fmaxf(amax, fabsf(x[j]));
+  for (int j = 0; j < 16 * NU; j++) amax = fmaxf(amax, fabsf(x[j]));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
   if ((tid & 63) == 0) wmax[tid >> 6] = amax;
@@ -614,19 +625,23 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const bf16_t* __restri
     e = (m <= 0.875f) ? q - 9 : q - 8;
   }
   const float inv = ldexpf(1.0f, -e);
-  u32x4 o;
 #pragma unroll
-  for (int w = 0; w < 4; w++) {
-    unsigned word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w] * inv, x[4 * w + 1] * inv, 0u, false);
-    word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * w + 2] * inv, x[4 * w + 3] * inv, word, true);
-    o[w] = word;
+  for (int u = 0; u < NU; u++) {
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      const float* y = x + 16 * u + 4 * w;
+      unsigned word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] * inv, y[1] * inv, 0u, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * inv, y[3] * inv, word, true);
+      o[w] = word;
+    }
+    *(u32x4*)((which == 0 ? k8 : v8) + dst[u]) = o;
   }
-  *(u32x4*)((which == 0 ? k8 : v8) + dst) = o;
   if (tid == 0) (which == 0 ? ks : vs)[((long long)lb * Hh + h) * (cap / 64) + t] = ldexpf(1.0f, e);
 }
 
 hipError_t quantize_kv_fp8(hipStream_t s, const void* k, const void* v, void* k8, void* v8,
-                           float* ks, float* vs, int n_layers, int B, int Hh, int cap,
+                           float* ks, float* vs, int n_layers, int B, int Hh, int dh, int cap,
                            const ActLens& lens) {
   int maxlen = 0;
   double rows = 0.0;
@@ -635,12 +650,16 @@ hipError_t quantize_kv_fp8(hipStream_t s, const void* k, const void* v, void* k8
     rows += lens.len[b];
   }
   if (maxlen == 0 || n_layers <= 0) return hipSuccess;
-  if (cap % 64 || maxlen > cap) return hipErrorInvalidValue;
-  const double elems = 2.0 * n_layers * Hh * 64 * rows;  // K and V
+  if (cap % 64 || maxlen > cap || (dh != 64 && dh != 128)) return hipErrorInvalidValue;
+  const double elems = 2.0 * n_layers * Hh * dh * rows;  // K and V
   TimingScope ts(s, KC_QUANT, elems * 3.0, 0.0);
   dim3 grid((maxlen + 63) / 64, Hh, 2 * n_layers * B);
-  hipLaunchKernelGGL(quantize_kv_kernel, grid, dim3(256), 0, s, (const bf16_t*)k, (const bf16_t*)v,
-                     (uint8_t*)k8, (uint8_t*)v8, ks, vs, B, Hh, cap, lens);
+  if (dh == 64)
+    hipLaunchKernelGGL(quantize_kv_kernel<64>, grid, dim3(256), 0, s, (const bf16_t*)k,
+                       (const bf16_t*)v, (uint8_t*)k8, (uint8_t*)v8, ks, vs, B, Hh, cap, lens);
+  else
+    hipLaunchKernelGGL(quantize_kv_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)k,
+                       (const bf16_t*)v, (uint8_t*)k8, (uint8_t*)v8, ks, vs, B, Hh, cap, lens);
   return hipGetLastError();
 }
 

@@ -104,7 +104,6 @@ int check_kv(const wam_dims* d, const wam_kv* kv, int B, const char* name, bool 
       return fail(WAM_E_DTYPE, "%s: an E4M3 cache is read only by the action layers of a bf16 model",
                   name);
     if (!kv->k_scale || !kv->v_scale) return fail(WAM_E_ARG, "%s has no tile scales", name);
-    if (kv->dh != 64) return fail(WAM_E_SHAPE, "%s: an E4M3 cache needs dh = 64", name);
   } else if (kv->dtype != d->dtype) {
     return fail(WAM_E_DTYPE, "%s dtype differs from dims", name);
   }
@@ -1120,7 +1119,6 @@ static int attention_action_entry(int dtype, int B, int Hh, int dh, int H, const
   if (dtype != WAM_F32 && dtype != WAM_BF16) return fail(WAM_E_ARG, "bad dtype");
   if (ksc && (!kc || !vsc)) return fail(WAM_E_ARG, "an E4M3 cache needs kc, vc and both scales");
   if ((dh != 64 && dh != 128) || H != 32) return fail(WAM_E_SHAPE, "dh must be 64 or 128 and H 32");
-  if (ksc && dh != 64) return fail(WAM_E_SHAPE, "an E4M3 cache needs dh = 64");
   if (B < 1 || B > WAM_MAX_BATCH || Hh < 1) return fail(WAM_E_SHAPE, "bad B or Hh");
   if (!q || !out) return fail(WAM_E_ARG, "NULL pointer");
   if (n_act < 0 || n_act > H || (n_act > 0 && (!ka || !va)))
@@ -1180,7 +1178,7 @@ int wam_quantize_kv_fp8(const wam_kv* src, wam_kv* dst, void* stream) {
   if (src->n_layers != dst->n_layers || src->B != dst->B || src->Hh != dst->Hh ||
       src->dh != dst->dh || src->cap != dst->cap)
     return fail(WAM_E_SHAPE, "src and dst shapes differ");
-  if (src->dh != 64) return fail(WAM_E_SHAPE, "dh must be 64");
+  if (src->dh != 64 && src->dh != 128) return fail(WAM_E_SHAPE, "dh must be 64 or 128");
   if (src->n_layers < 1 || src->Hh < 1) return fail(WAM_E_SHAPE, "bad n_layers or Hh");
   if (src->B < 1 || src->B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "bad B");
   if (src->cap < 64 || src->cap % 64) return fail(WAM_E_SHAPE, "cap must be a positive multiple of 64");
@@ -1191,7 +1189,7 @@ int wam_quantize_kv_fp8(const wam_kv* src, wam_kv* dst, void* stream) {
     lens.len[b] = src->len[b];
   }
   HIPCK(quantize_kv_fp8((hipStream_t)stream, src->k, src->v, dst->k, dst->v, dst->k_scale,
-                        dst->v_scale, src->n_layers, src->B, src->Hh, src->cap, lens));
+                        dst->v_scale, src->n_layers, src->B, src->Hh, src->dh, src->cap, lens));
   for (int b = 0; b < src->B; b++) dst->len[b] = src->len[b];
   return WAM_OK;
 }

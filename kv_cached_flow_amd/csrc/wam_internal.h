@@ -237,7 +237,7 @@ hipError_t rope_qk(hipStream_t s, int dt, void* x0, long long gs0, long long hs0
                    const RopeRows& rb);
 
 hipError_t quantize_kv_fp8(hipStream_t s, const void* k, const void* v, void* k8, void* v8,
-                           float* ks, float* vs, int n_layers, int B, int Hh, int cap,
+                           float* ks, float* vs, int n_layers, int B, int Hh, int dh, int cap,
                            const ActLens& lens);
 
 hipError_t debug_visibility(hipStream_t s, const FrameTab& tab, const int* comp_of_frame,

@@ -15,17 +15,22 @@ from tests._util import print_case, rel_l2, to_np
 
 pytestmark = pytest.mark.gpu
 
-# byte p of a K row holds dim LANE[p]; byte p of a V^T tile row holds key LANE[p]
+# byte p of a V^T tile row holds key LANE[p]; byte p of a K row holds dim lane_k(dh)[p]
 LANE = np.array([32 * ss + 8 * g + j for g in range(4) for ss in range(2) for j in range(8)])
+
+
+def lane_k(dh):
+    return np.array([64 * u + 32 * ss + 8 * g + j for g in range(4) for u in range(dh // 64)
+                     for ss in range(2) for j in range(8)])
 
 
 def _bf16(a):
     return torch.tensor(a, dtype=torch.float32).to(torch.bfloat16).float().numpy()
 
 
-def _case(rng, B, Hh, lens, cap):
-    K = _bf16(rng.standard_normal((B, Hh, cap, 64)))
-    V = _bf16(rng.standard_normal((B, Hh, cap, 64)))
+def _case(rng, B, Hh, lens, cap, dh=64):
+    K = _bf16(rng.standard_normal((B, Hh, cap, dh)))
+    V = _bf16(rng.standard_normal((B, Hh, cap, dh)))
     K[0, 0, 64:128] *= 1e-3          # a tile with its own small scale
     V[0, 1, :64] = 0.0               # an all-zero tile
     K[-1, -1, :64] *= 4.0            # and a large one (scores stay in the workloads' range)
@@ -37,12 +42,12 @@ def _case(rng, B, Hh, lens, cap):
 
 
 def _device_caches(K, V, lens, cap):
-    B, Hh = K.shape[:2]
-    src = wam.DeviceKV(1, B, Hh, 64, cap, wam.WAM_BF16)
+    B, Hh, _, dh = K.shape
+    src = wam.DeviceKV(1, B, Hh, dh, cap, wam.WAM_BF16)
     src.k.copy_(torch.tensor(K[None]).to(torch.bfloat16))
     src.v.copy_(torch.tensor(np.ascontiguousarray(V.transpose(0, 1, 3, 2))[None]).to(torch.bfloat16))
     src.len[:] = lens
-    dst = wam.DeviceKV(1, B, Hh, 64, cap, wam.WAM_FP8)
+    dst = wam.DeviceKV(1, B, Hh, dh, cap, wam.WAM_FP8)
     dst.k.fill_(0x7F)                 # NaN codes: every byte read must have been written
     dst.v.fill_(0x7F)
     wam.quantize_kv_fp8(src, dst)
@@ -51,23 +56,24 @@ def _device_caches(K, V, lens, cap):
 
 
 def _codes_in_order(dst, b, n):
-    """(codes_K [n, Hh, 64], codes_V [n, Hh, 64]) of episode b in dim/key order."""
-    k8 = dst.k[0, b, :, :n].cpu().numpy()                       # [Hh, n, 64 bytes]
+    """(codes_K [n, Hh, dh], codes_V [n, Hh, dh]) of episode b in dim/key order."""
+    k8 = dst.k[0, b, :, :n].cpu().numpy()                       # [Hh, n, dh bytes]
     ck = np.empty_like(k8)
-    ck[:, :, LANE] = k8
-    v8 = dst.v[0, b].cpu().numpy()                             # [Hh, 64 dims, cap bytes]
+    ck[:, :, lane_k(k8.shape[2])] = k8
+    v8 = dst.v[0, b].cpu().numpy()                             # [Hh, dh dims, cap bytes]
     nt = (n + 63) // 64
-    cv = np.empty((v8.shape[0], 64, nt * 64), dtype=np.uint8)
+    cv = np.empty((v8.shape[0], v8.shape[1], nt * 64), dtype=np.uint8)
     for t in range(nt):
         cv[:, :, 64 * t + LANE] = v8[:, :, 64 * t:64 * t + 64]
     return ck.transpose(1, 0, 2), cv[:, :, :n].transpose(2, 0, 1)
 
 
-def test_quantize_bit_exact_against_oracle():
+@pytest.mark.parametrize("dh", [64, 128])
+def test_quantize_bit_exact_against_oracle(dh):
     rng = np.random.default_rng(11)
     lens, cap = [150, 64, 1], 192
-    print_case("E4M3 quantisation vs the oracle codec")
-    K, V = _case(rng, 3, 3, lens, cap)
+    print_case(f"E4M3 quantisation vs the oracle codec, dh {dh}")
+    K, V = _case(rng, 3, 3, lens, cap, dh)
     _, dst = _device_caches(K, V, lens, cap)
     assert list(dst.len) == lens
     for b, n in enumerate(lens):
@@ -91,9 +97,9 @@ def test_quantize_bit_exact_against_oracle():
 
 def _dequant_bf16_cache(dst, lens, cap):
     """A bf16 cache holding exactly the values the E4M3 cache stands for."""
-    B, Hh = dst.k.shape[1], dst.k.shape[2]
-    K = np.zeros((B, Hh, cap, 64), np.float32)
-    V = np.zeros((B, Hh, cap, 64), np.float32)
+    B, Hh, dh = dst.k.shape[1], dst.k.shape[2], dst.k.shape[4]
+    K = np.zeros((B, Hh, cap, dh), np.float32)
+    V = np.zeros((B, Hh, cap, dh), np.float32)
     for b, n in enumerate(lens):
         if n == 0:
             continue
@@ -107,22 +113,25 @@ def _dequant_bf16_cache(dst, lens, cap):
 
 
 @pytest.mark.parametrize("shape", [
-    ("C1-like", 1, 16, [9216], 32),
-    ("ragged", 3, 4, [100, 3000, 777], 32),
-    ("partial-own", 2, 4, [300, 129], 20),
+    ("C1-like", 1, 16, [9216], 32, 64),
+    ("ragged", 3, 4, [100, 3000, 777], 32, 64),
+    ("partial-own", 2, 4, [300, 129], 20, 64),
+    ("C6-like", 1, 24, [9216], 32, 128),
+    ("ragged dh=128", 3, 4, [100, 3000, 777], 32, 128),
+    ("partial-own dh=128", 2, 4, [300, 129], 20, 128),
 ])
 def test_attention_fp8_equals_bf16_on_dequantised_values(shape):
-    name, B, Hh, lens, n_act = shape
+    name, B, Hh, lens, n_act, dh = shape
     print_case(f"E4M3 action attention {name}")
     rng = np.random.default_rng(17)
     cap = (max(lens) + 63) // 64 * 64
-    K, V = _case(rng, B, Hh, lens, cap)
+    K, V = _case(rng, B, Hh, lens, cap, dh)
     _, dst = _device_caches(K, V, lens, cap)
     Kd, Vd = _dequant_bf16_cache(dst, lens, cap)
-    q = torch.tensor(_bf16(rng.standard_normal((B, Hh, 32, 64)))).to(torch.bfloat16).cuda()
-    ka = torch.tensor(_bf16(rng.standard_normal((B, Hh, 32, 64)))).to(torch.bfloat16).cuda()
-    va = torch.tensor(_bf16(rng.standard_normal((B, Hh, 64, 32)))).to(torch.bfloat16).cuda()
-    o8 = torch.empty((B, 32, Hh * 64), dtype=torch.bfloat16, device="cuda")
+    q = torch.tensor(_bf16(rng.standard_normal((B, Hh, 32, dh)))).to(torch.bfloat16).cuda()
+    ka = torch.tensor(_bf16(rng.standard_normal((B, Hh, 32, dh)))).to(torch.bfloat16).cuda()
+    va = torch.tensor(_bf16(rng.standard_normal((B, Hh, dh, 32)))).to(torch.bfloat16).cuda()
+    o8 = torch.empty((B, 32, Hh * dh), dtype=torch.bfloat16, device="cuda")
     o16 = torch.empty_like(o8)
     lens_a = np.asarray(lens, np.int32)
     wam.attention_action_fp8(q, ka, va, n_act, dst.k[0], dst.v[0], dst.k_scale[0], dst.v_scale[0],
@@ -142,7 +151,7 @@ def test_attention_fp8_equals_bf16_on_dequantised_values(shape):
         ref.append(O.attention(torch.tensor(qq, dtype=torch.float64).permute(1, 0, 2),
                                torch.tensor(kk, dtype=torch.float64).permute(1, 0, 2),
                                torch.tensor(vv, dtype=torch.float64).permute(1, 0, 2)).numpy())
-    got = to_np(o8).reshape(B, 32, Hh, 64)
+    got = to_np(o8).reshape(B, 32, Hh, dh)
     assert rel_l2(got, np.stack(ref)) <= 5e-3
 
 
@@ -158,11 +167,13 @@ def _run_gpu(cfg, inp):
     return dc
 
 
-@pytest.mark.parametrize("variant", ["dense", "sparse"])
+@pytest.mark.parametrize("variant", ["dense", "sparse", "dh128"])
 def test_chunk_with_fp8_cache_vs_oracle(variant):
     kw = dict(SMALL)
     if variant == "sparse":
         kw.update(L=4, V=0, read_map=(-1, 0, -1, 1), fuse=((0, 2), (2, 2)))
+    if variant == "dh128":
+        kw.update(Hh=2, dh=128)
     cfg = configs.small("Q", dtype="bf16", **kw)
     print_case(f"chunk with E4M3 cache, {variant}")
     inp = inputs.generate(cfg)

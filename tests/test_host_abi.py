@@ -273,16 +273,17 @@ def test_fp8_cache_validation_errors():
     kv8c, _j = fake_kv(cap=512, lens=[300], dtype=wam.WAM_FP8)
     kv8c.k_scale = kv8c.v_scale = FAKE
     assert call_codenoise(kv=kv8c)[0] == -3
-    # the E4M3 layout is defined for 64-wide heads only
-    s128, _l = fake_kv(n_layers=2, cap=512, lens=[300], dh=128)
-    d128, _m = fake_kv(n_layers=2, cap=512, lens=[0], dtype=wam.WAM_FP8, dh=128)
-    d128.k_scale = d128.v_scale = FAKE
-    assert q(s128, d128)[0] == -2
+    # E4M3 caches of 64- and 128-wide heads (nothing is launched: every call
+    # below stops at a check)
+    s96, _l = fake_kv(n_layers=2, cap=512, lens=[300], dh=96)
+    d96, _m = fake_kv(n_layers=2, cap=512, lens=[0], dtype=wam.WAM_FP8, dh=96)
+    d96.k_scale = d96.v_scale = FAKE
+    assert q(s96, d96)[0] == -2                        # heads of 64 or 128 only
     k128, _n = fake_kv(Hh=2, dtype=wam.WAM_FP8, dh=128)
     k128.k_scale = k128.v_scale = FAKE
-    assert call_denoise(d=good_dims(Hh=2, dh=128), kv=k128) == -2
+    assert call_denoise(d=good_dims(Hh=2, dh=128), kv=k128, ws_bytes=4096) == -5   # accepted
     ln = np.array([100], np.int32)
-    st = L.wam_attention_action_fp8(1, 4, 128, 32, FAKE, FAKE, FAKE, 32, FAKE, FAKE, FAKE, FAKE, 128,
+    st = L.wam_attention_action_fp8(1, 4, 96, 32, FAKE, FAKE, FAKE, 32, FAKE, FAKE, FAKE, FAKE, 128,
                                     ln.ctypes.data, FAKE, 0, FAKE, 1 << 30, None)
     assert st == -2
 
