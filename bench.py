@@ -1,13 +1,20 @@
 """Benchmark: one whole action chunk (video prefill -> interval fusion when the
 workload has it -> N action Euler steps) per step, on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config C1]
+    python bench.py [--steps K] [--warmup W] [--config C4]
 
-Prints one JSON line.  ``value`` is milliseconds per 32-action chunk with the
-inputs resident in HBM (lower is better).  ``roofline`` describes the kernel
-class that takes the most time, from live HIP-event timing of every launch in
+The default workload is C4, the largest single-GPU configuration (four
+episodes of 48 history frames, 19 of them padded, two future frames of 880
+tokens, 4 video and 10 action steps).
+
+Prints one JSON line.  ``value`` is the mean milliseconds per 32-action chunk
+(one call over all B episodes) with the inputs resident in HBM (lower is
+better); ``median_ms`` is the median of the per-chunk times, the statistic the
+Long-WAM Summary's appendix F reports.  ``roofline`` describes the kernel class
+with the largest roofline floor, from live HIP-event timing of every launch in
 a separate timing pass.  ``cpu_baseline`` times the CPU oracle on a bounded
-sample of the same workload (the first few layers of each expert), scaled.
+sample of the same workload (one episode, the first layers of each expert),
+scaled to the whole chunk.
 """
 from __future__ import annotations
 
@@ -119,7 +126,20 @@ def yardsticks() -> dict:
     return out
 
 
+def blas_threads() -> list:
+    """BLAS libraries loaded in this process and their thread counts."""
+    try:
+        from threadpoolctl import threadpool_info
+        return [{"api": i.get("internal_api"), "threads": i.get("num_threads")}
+                for i in threadpool_info()]
+    except Exception:  # threadpoolctl missing or failing: report nothing
+        return []
+
+
 def cpu_baseline(cfg_name: str, layers: int, kv_fp8: bool = False, rope: bool = False) -> dict:
+    """The oracle, as it stands, on one episode of the workload with the first
+    `layers` layers of each expert; the time is scaled by B and by L / layers
+    (the per-layer work of prefill, imagine and the action steps dominates)."""
     import numpy as np  # noqa: F401
     import torch
 
@@ -127,7 +147,7 @@ def cpu_baseline(cfg_name: str, layers: int, kv_fp8: bool = False, rope: bool = 
     from oracle import wam_oracle as O
 
     full = configs.get(cfg_name)
-    kw = {"L": layers, "read_map": tuple(range(layers))}
+    kw = {"L": layers, "read_map": tuple(range(layers)), "B": 1}
     if full.fuse:
         # one interaction layer (the last) reading the fusion of the sampled layers
         kw["fuse"] = ((0, layers),)
@@ -140,21 +160,23 @@ def cpu_baseline(cfg_name: str, layers: int, kv_fp8: bool = False, rope: bool = 
     else:
         O.run_chunk(cfg, inp, kv_fp8=cfg.kv_fp8)
     dt = time.perf_counter() - t0
-    scale = full.L / layers
+    scale = full.L / layers * full.B
     return {"value": round(dt * scale * 1e3, 1), "unit": "ms/chunk", "cores": torch.get_num_threads(),
+            "affinity_cores": len(os.sched_getaffinity(0)), "blas": blas_threads(),
             "kind": "oracle",
-            "sample": f"{cfg_name} chunk with the first {layers} of {full.L} layers per expert "
-                      f"(measured {dt:.1f} s), scaled x{scale:g} to {full.L} layers"}
+            "sample": f"{cfg_name}, 1 of {full.B} episode(s), the first {layers} of {full.L} layers "
+                      f"per expert (measured {dt:.1f} s with {torch.get_num_threads()} torch threads), "
+                      f"scaled x{scale:g} to {full.B} episode(s) x {full.L} layers"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="C1")
-    ap.add_argument("--cpu-layers", type=int, default=10,
-                    help="layers per expert in the CPU oracle sample (about 1.1 s each for C1)")
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C4")
+    ap.add_argument("--cpu-layers", type=int, default=0,
+                    help="layers per expert in the CPU oracle sample (0: 1 for C3-C5, 10 else)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stream", type=int, default=0, metavar="K",
                     help="streamed history: each timed step is one decision whose last K history "
@@ -208,20 +230,24 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K chunks
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- timed region: exactly K chunks, an event between consecutive chunks
+    evs_t = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
+    evs_t[0].record()
+    for i in range(args.steps):
         step()
-    ev1.record()
+        evs_t[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
-    print(f"[bench] {ms:.3f} ms/chunk (wall {wall / args.steps * 1e3:.3f})", file=sys.stderr, flush=True)
+    per = [evs_t[i].elapsed_time(evs_t[i + 1]) for i in range(args.steps)]
+    ms = evs_t[0].elapsed_time(evs_t[-1]) / args.steps
+    med = sorted(per)[len(per) // 2] if len(per) % 2 else 0.5 * sum(sorted(per)[len(per) // 2 - 1:len(per) // 2 + 1])
+    print(f"[bench] {ms:.3f} ms/chunk mean, {med:.3f} median (wall {wall / args.steps * 1e3:.3f})",
+          file=sys.stderr, flush=True)
     if args.minimal:
-        print(json.dumps({"value": round(ms, 4), "unit": "ms/chunk", "steps": args.steps}), flush=True)
+        print(json.dumps({"value": round(ms, 4), "median_ms": round(med, 4), "unit": "ms/chunk",
+                          "steps": args.steps}), flush=True)
         return
 
     # ---- phases (events between the calls of one chunk)
@@ -271,6 +297,10 @@ def main():
         "metric": "ms per 32-action chunk at 1 GPU; cached-KV attn HBM GB/s; prefill MFMA util",
         "value": round(ms, 4),
         "unit": "ms/chunk",
+        "median_ms": round(med, 4),
+        "min_ms": round(min(per), 4),
+        "max_ms": round(max(per), 4),
+        "ms_per_episode": round(ms / cfg.B, 4),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -302,7 +332,8 @@ def main():
     rec["yardsticks"] = yardsticks()
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(cfg.name, min(args.cpu_layers, cfg.L), cfg.kv_fp8, cfg.rope)
+        layers = args.cpu_layers or (1 if cfg.name in ("C3", "C4", "C5") else 10)
+        rec["cpu_baseline"] = cpu_baseline(cfg.name, min(layers, cfg.L), cfg.kv_fp8, cfg.rope)
     print(json.dumps(rec), flush=True)
 
 

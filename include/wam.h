@@ -367,6 +367,10 @@ int wam_debug_visibility(const int32_t* frame_block, const uint8_t* valid, int F
                          int P, uint8_t* vis, void* stream);
 
 /* Kernel-level attention entries (the kernels the calls above use).
+ * Query contract: fp32 q holds the queries; bf16 q holds the queries times
+ * log2(e) / sqrt(dh), rounded to bf16 once (the projection epilogue of the
+ * calls above writes Q that way), so that the bf16 kernels' score MFMAs give
+ * scores in log2 units with no second rounding of q.
  * Action attention: q [B][Hh][H][dh], ka [B][Hh][H][dh], va [B][Hh][dh][H]
  * (the chunk's own keys; NULL with n_act = 0 to leave them out), cache layer
  * kc [B][Hh][cap][dh], vc [B][Hh][dh][cap] with len[b] (host) rows, or

@@ -26,7 +26,6 @@
 
 namespace wam {
 
-#define LOG2E 1.4426950408889634f
 
 // Reductions over the four lanes {c, c+16, c+32, c+48} that hold one query
 // column, with the gfx950 lane-swap instructions (VALU, no LDS traffic).
@@ -55,7 +54,8 @@ __device__ inline int perm_key(int sub, int r) {
 // o[0..3][t] are the O^T accumulators (head dim x query); o[4][t] row 0 holds
 // the row sums, accumulated by the same P V MFMA against a row of ones, so
 // numerator and denominator use the same bf16 probabilities.  Scores are in
-// log2 units (the queries carry the softmax scale times log2 e), and m is the
+// log2 units (the bf16 queries arrive as Q log2(e) / sqrt(dh), scaled in the
+// projection's fp32 epilogue before their one rounding), and m is the
 // reference max in those units.  The score MFMA starts from -m instead of 0,
 // so it yields s - m directly and p = exp2(s - m) costs one exponential and
 // no FMA.  The reference max is raised only when a score exceeds it by more
@@ -204,18 +204,6 @@ __device__ inline void tile_scores(floatx4 (&sacc)[4][2], const bf16x8 (&qf)[2][
   }
 }
 
-// A query fragment scaled into log2 units (scale * log2 e) and rounded to bf16.
-__device__ inline bf16x8 scale_q(bf16x8 q, float sl2) {
-  const u32x4 u = __builtin_bit_cast(u32x4, q);
-  u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const float lo = __uint_as_float(u[i] << 16) * sl2, hi = __uint_as_float(u[i] & 0xFFFF0000u) * sl2;
-    o[i] = pack_bf16x2(lo, hi);
-  }
-  return __builtin_bit_cast(bf16x8, o);
-}
-
 // ====================================================================== prefill
 namespace pf {
 constexpr int QW = 32, NW = 4, QT = QW * NW;  // queries per wave / per workgroup
@@ -267,8 +255,8 @@ __device__ inline void buffer_lds16(__amdgpu_buffer_rsrc_t rs, char* lds, unsign
 template <int DH>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
-    bf16_t* __restrict__ out, int nq, int row0, int cap, int Hh, FrameTab tab, float sl2,
-    int nsplit, float* __restrict__ part) {
+    bf16_t* __restrict__ out, int nq, int row0, int cap, int Hh, FrameTab tab, int nsplit,
+    float* __restrict__ part) {
   using namespace pf;
   static_assert(DH == 64 || DH == 128, "head dim");
   // A K tile is DH/64 halves of 64 keys x 64 dims (128-byte rows), a V^T
@@ -300,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     kq[t] = ok ? kend_of_row(tab, row0 + qi) : kend_max;
 #pragma unroll
     for (int s = 0; s < NS; s++)
-      qf[t][s] = ok ? scale_q(*(const bf16x8*)(q + ((long long)h * nq + qi) * DH + 32 * s + 8 * g), sl2)
+      qf[t][s] = ok ? *(const bf16x8*)(q + ((long long)h * nq + qi) * DH + 32 * s + 8 * g)
                     : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
   WaveAccT<DH> acc;
@@ -591,11 +579,11 @@ hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int dh, int nq, int row0,
       if (dh == 64)
         hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), 0, s, (const bf16_t*)q,
                            (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)out, nq, row0, cap, Hh,
-                           tab, scale * LOG2E, nsplit, nsplit > 1 ? part : nullptr);
+                           tab, nsplit, nsplit > 1 ? part : nullptr);
       else
         hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)q,
                            (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)out, nq, row0, cap, Hh,
-                           tab, scale * LOG2E, nsplit, nsplit > 1 ? part : nullptr);
+                           tab, nsplit, nsplit > 1 ? part : nullptr);
     }
     if (nsplit > 1) {
       hipError_t e = hipGetLastError();
@@ -709,7 +697,7 @@ template <bool F8, int DH>
 __global__ __launch_bounds__(256, 2) void attn_action_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ ka, const bf16_t* __restrict__ va,
     const void* __restrict__ kc, const void* __restrict__ vc, const float* __restrict__ ksc,
-    const float* __restrict__ vsc, ActGeom G, float* __restrict__ part, float sl2) {
+    const float* __restrict__ vsc, ActGeom G, float* __restrict__ part) {
   using namespace act;
   static_assert(DH == 64 || DH == 128, "head dim");
   constexpr int NS = DH / 32, ND = DH / 16;
@@ -756,7 +744,7 @@ __global__ __launch_bounds__(256, 2) void attn_action_kernel(
   for (int t = 0; t < 2; t++)
 #pragma unroll
     for (int ss = 0; ss < NS; ss++)
-      qf[t][ss] = scale_q(*(const bf16x8*)(qb + (16 * t + c16) * DH + 32 * ss + 8 * g), sl2);
+      qf[t][ss] = *(const bf16x8*)(qb + (16 * t + c16) * DH + 32 * ss + 8 * g);
 
   WaveAccT<DH> acc;
   acc_init(acc);
@@ -1081,23 +1069,22 @@ hipError_t attn_action(hipStream_t s, int dt, int B, int Hh, int H, int dh, cons
                             (f8 ? 2.0 * 4 * Hh * (cached / 64.0) : 0.0);
     TimingScope ts(s, KC_ATTN_ACTION, kv_bytes + 1.0 * B * H * Hh * dh * es,
                    4.0 * dh * Hh * H * keys);
-    const float sl2 = scale * LOG2E;
     if (f8 && dh == 64)
       hipLaunchKernelGGL((attn_action_kernel<true, 64>), dim3(G.S, Hh, B), dim3(256), 0, s,
                          (const bf16_t*)q, (const bf16_t*)ka, (const bf16_t*)va, kc, vc, ksc, vsc,
-                         G, (float*)scratch, sl2);
+                         G, (float*)scratch);
     else if (f8)
       hipLaunchKernelGGL((attn_action_kernel<true, 128>), dim3(G.S, Hh, B), dim3(256), 0, s,
                          (const bf16_t*)q, (const bf16_t*)ka, (const bf16_t*)va, kc, vc, ksc, vsc,
-                         G, (float*)scratch, sl2);
+                         G, (float*)scratch);
     else if (dh == 64)
       hipLaunchKernelGGL((attn_action_kernel<false, 64>), dim3(G.S, Hh, B), dim3(256), 0, s,
                          (const bf16_t*)q, (const bf16_t*)ka, (const bf16_t*)va, kc, vc,
-                         (const float*)nullptr, (const float*)nullptr, G, (float*)scratch, sl2);
+                         (const float*)nullptr, (const float*)nullptr, G, (float*)scratch);
     else
       hipLaunchKernelGGL((attn_action_kernel<false, 128>), dim3(G.S, Hh, B), dim3(256), 0, s,
                          (const bf16_t*)q, (const bf16_t*)ka, (const bf16_t*)va, kc, vc,
-                         (const float*)nullptr, (const float*)nullptr, G, (float*)scratch, sl2);
+                         (const float*)nullptr, (const float*)nullptr, G, (float*)scratch);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -556,8 +556,9 @@ hipError_t fuse_kv(hipStream_t s, int dt, const void* src, void* dst, long long 
 // 16g..16g+15 of that row, g = t%4: elements 8g..8g+7 and 32+8g..32+8g+7
 // (dims of K, keys of the V^T tile).  The tile exponent is exact: with
 // amax = m 2^q (m in [0.5, 1)), the smallest e with amax <= 448 2^e =
-// 0.875 2^(9+e) is q-9 when m <= 0.875, else q-8.  Scaling by 2^-e is exact,
-// and v_cvt_pk_fp8_f32 rounds to nearest even (|x 2^-e| <= 448).
+// 0.875 2^(9+e) is q-9 when m <= 0.875, else q-8, and at least -126.  Scaling
+// by 2^-e is exact, and v_cvt_pk_fp8_f32 rounds to nearest even
+// (|x 2^-e| <= 448).
 template <int DH>
 __global__ __launch_bounds__(256) void quantize_kv_kernel(const bf16_t* __restrict__ k,
                                                           const bf16_t* __restrict__ v,
@@ -623,6 +624,9 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const bf16_t* __restri
     int q;
     const float m = frexpf(amax, &q);
     e = (m <= 0.875f) ? q - 9 : q - 8;
+    // the scale stays a normal float32 number (and 2^-e finite): tiles
+    // below 448 * 2^-127 keep e = -126, their codes then stay under 224
+    e = e < -126 ? -126 : e;
   }
   const float inv = ldexpf(1.0f, -e);
 #pragma unroll

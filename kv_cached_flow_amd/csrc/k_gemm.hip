@@ -123,6 +123,12 @@ __device__ inline void epi_row4(const EpiArgs& e, int m, int n, float4 v) {
     const int g = m / e.rpg, t = m - g * e.rpg;
     TO* p = part == 0 ? (TO*)e.q + g * e.q_gs + h * e.q_hs + (long long)t * e.dh + d
                       : (TO*)e.k + g * e.k_gs + h * e.k_hs + (long long)(e.k_row0 + t) * e.dh + d;
+    if (part == 0) {
+      v.x *= e.q_scale;
+      v.y *= e.q_scale;
+      v.z *= e.q_scale;
+      v.w *= e.q_scale;
+    }
     if constexpr (sizeof(TO) == 2)
       *(uint2*)p = uint2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
     else

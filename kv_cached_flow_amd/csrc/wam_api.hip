@@ -50,6 +50,14 @@ struct Arena {
   }
 };
 
+// Multiplier of the Q columns in the QKV epilogue: bf16 models keep Q as
+// Q log2(e) / sqrt(dh), rounded once, and the bf16 attention kernels take
+// their scores in log2 units straight from the MFMAs; the fp32 kernels scale
+// the scores themselves.
+float qkv_q_scale(const wam_dims* d) {
+  return d->dtype == WAM_BF16 ? (float)(1.4426950408889634 / sqrt((double)d->dh)) : 1.0f;
+}
+
 int check_dims(const wam_dims* d) {
   if (!d) return fail(WAM_E_ARG, "dims is NULL");
   if (d->dtype != WAM_F32 && d->dtype != WAM_BF16) return fail(WAM_E_ARG, "bad dtype %d", d->dtype);
@@ -207,6 +215,7 @@ int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const Fra
   e.k_row0 = row0;
   e.v_ld = cap;
   e.v_col0 = row0;
+  e.q_scale = qkv_q_scale(d);
   // rotary option: Q rows and the K rows just cached sit at positions row0 ..
   RopeRows rb{};
   rb.base[0] = row0;
@@ -304,6 +313,7 @@ int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, co
   e.v_gs = (long long)d->Hh * d->dh * H;
   e.v_hs = (long long)d->dh * H;
   e.v_ld = H;
+  e.q_scale = qkv_q_scale(d);
   if ((st = norm_rows(c, dt, w.g1, b.Y, M))) return st;
   HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, M, 3 * Dq, D, b.Y, D, w.wqkv, D, e));
   if (d->rope) {

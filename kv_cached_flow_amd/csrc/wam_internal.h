@@ -117,6 +117,10 @@ struct EpiArgs {
   void* k;
   void* v;
   int D, dh, rpg, n_begin;
+  // Q part: the fp32 accumulator is multiplied by q_scale before its one
+  // rounding to the output type (bf16 models: log2(e) / sqrt(dh), so that the
+  // attention kernels' score MFMAs yield log2-domain scores; fp32 models: 1)
+  float q_scale;
   long long q_gs, q_hs;          // q[g*q_gs + h*q_hs + t*dh + d]
   long long k_gs, k_hs;          // k[g*k_gs + h*k_hs + (k_row0 + t)*dh + d]
   long long v_gs, v_hs;          // v[g*v_gs + h*v_hs + d*v_ld + v_col0 + t]
@@ -139,7 +143,7 @@ __device__ inline void epi_store(const EpiArgs& e, int m, int n, float v) {
     int h = c / e.dh, d = c - h * e.dh;
     int g = m / e.rpg, t = m - g * e.rpg;
     if (part == 0)
-      ((TO*)e.q)[g * e.q_gs + h * e.q_hs + (long long)t * e.dh + d] = from_f<TO>(v);
+      ((TO*)e.q)[g * e.q_gs + h * e.q_hs + (long long)t * e.dh + d] = from_f<TO>(v * e.q_scale);
     else if (part == 1)
       ((TO*)e.k)[g * e.k_gs + h * e.k_hs + (long long)(e.k_row0 + t) * e.dh + d] = from_f<TO>(v);
     else

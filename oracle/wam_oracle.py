@@ -676,11 +676,20 @@ def e4m3_encode(x) -> np.ndarray:
     return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 
 
+KV_MIN_EXP = -126   # 2^-126: the smallest normal float32 number
+
+
 def kv_tile_exponent(amax: float) -> int:
-    """Smallest integer e with amax <= 448 * 2^e (0 for an all-zero tile)."""
+    """Smallest integer e >= -126 with amax <= 448 * 2^e (0 for an all-zero
+    tile).  The pages fix no scale format (the LongLive-2.0 stack quantises its
+    KV cache block by block, the Long-WAM tutorial section 三); reading adopted:
+    the scale 2^e is a normal float32 number, so tiles whose largest value is
+    below 448 * 2^-127 keep e = -126 (their codes are then smaller than 224)."""
     amax = float(amax)
     if amax == 0.0:
         return 0
+    if amax <= E4M3_MAX * 2.0 ** (KV_MIN_EXP - 1):
+        return KV_MIN_EXP
     e = math.ceil(math.log2(amax / E4M3_MAX))
     while amax > E4M3_MAX * 2.0 ** e:
         e += 1

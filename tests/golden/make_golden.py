@@ -1,7 +1,12 @@
 """Write the expected values of the full-size workloads C1-C6 by running the
 CPU oracle (and nothing else) on the seeded inputs.
 
-    python tests/golden/make_golden.py C1 C2 C3 C4 C5 C6
+    python tests/golden/make_golden.py C1 C2 C3 C4 C5 C6 C1+fp8 C1+sharp C6+fp8
+
+A name may carry options after "+": ``fp8`` (the E4M3 cache option) and
+``sharp`` (the diagnostic variant with Wq, Wk ~ N(0, 0.06^2): peaked
+attention, score std about 3.7 at width 1024); the file is then
+``<config>_<option>.json``.
 
 Each ``<name>.json`` holds the input fingerprint, the final action chunk of
 every episode, the v-hat of the first and last action steps, and sampled
@@ -42,10 +47,18 @@ def sample_points(cfg, seed=12345):
 def main(names):
     torch.set_num_threads(int(os.environ.get("ORACLE_THREADS", "8")))
     for name in names:
-        # "<config>+fp8": the same workload with the E4M3 cache option
-        base, _, opt = name.partition("+")
-        cfg = configs.get(base, kv_fp8=True) if opt == "fp8" else configs.get(base)
-        fname = f"{base}_fp8" if opt == "fp8" else base
+        # "<config>+<option>+...": the same workload with options
+        base, *opts = name.split("+")
+        kw = {}
+        for o in opts:
+            if o == "fp8":
+                kw["kv_fp8"] = True
+            elif o == "sharp":
+                kw["qk_std"] = 0.06
+            else:
+                raise SystemExit(f"unknown option {o}")
+        cfg = configs.get(base, **kw)
+        fname = "_".join([base] + opts)
         t0 = time.time()
         inp = inputs.generate(cfg)
         rows, heads, layers = sample_points(cfg)
@@ -74,6 +87,7 @@ def main(names):
         rec = {
             "config": name,
             "kv_fp8": cfg.kv_fp8,
+            "qk_std": cfg.qk_std,
             "seed": cfg.seed,
             "fingerprint": inputs.fingerprint(inp),
             "source": ("oracle/wam_oracle.py " + ("run_codenoise" if cfg.joint else "run_chunk")

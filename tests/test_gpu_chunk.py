@@ -203,18 +203,49 @@ def test_sparse_mot_small_vs_oracle():
         assert rel_l2(k, ref["fused"][0][m][0].numpy()) <= 1e-2
 
 
+# ---------------------------------------------------------------- sharp variant
+# Wq, Wk ~ N(0, s^2) with s chosen so that the score std D s^2 is about 3.7, as
+# the 0.06 of the 1024-wide workloads gives: near one-hot attention, which a
+# wrong score (scale, mask, rounding) cannot hide the way near-uniform
+# attention can.  0.12 at D = 256.
+@pytest.mark.parametrize("case", [("f32", "dense"), ("bf16", "dense"), ("bf16", "sparse"),
+                                  ("f32", "dh128"), ("bf16", "dh128")])
+def test_sharp_attention_small_vs_oracle(case):
+    dtype, variant = case
+    kw = dict(SMALL, qk_std=0.12)
+    if variant == "sparse":
+        kw.update(L=4, V=0, read_map=(-1, 0, -1, 1), fuse=((0, 2), (2, 2)))
+    if variant == "dh128":
+        kw.update(Hh=2, dh=128)
+    cfg = configs.small("SH", dtype=dtype, **kw)
+    print_case(f"sharp attention {dtype} {variant}")
+    inp = inputs.generate(cfg)
+    ref = _oracle(cfg, inp)
+    dc = _run_gpu(cfg, inp)
+    f32 = dtype == "f32"
+    assert rel_l2(to_np(dc.actions), ref["actions"]) <= (1e-5 if f32 else 2e-2)
+    T = cfg.tokens_valid
+    for l in range(cfg.L):
+        k, v = gpu_cache_layer(dc, l, 0, T)
+        assert rel_l2(k, ref["cache"][0][l][0].numpy()) <= (1e-5 if f32 else 1e-2)
+        assert rel_l2(v, ref["cache"][0][l][1].numpy()) <= (1e-5 if f32 else 1e-2)
+    if cfg.V >= 1:
+        assert rel_l2(to_np(dc.z).reshape(ref["z"].shape), ref["z"]) <= (1e-5 if f32 else 1e-2)
+
+
 # ---------------------------------------------------------------- full size
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4"])
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C1+sharp"])
 def test_full_size_against_oracle_values(name):
     import json
-    path = os.path.join(GOLDEN, f"{name}.json")
+    base, *opts = name.split("+")
+    path = os.path.join(GOLDEN, "_".join([base] + opts) + ".json")
     if not os.path.exists(path):
         pytest.skip(f"{path} not generated (tests/golden/make_golden.py)")
     g = json.load(open(path))
-    cfg = configs.get(name)
+    cfg = configs.get(base, qk_std=0.06) if "sharp" in opts else configs.get(base)
     print_case(f"full size {name}")
     inp = inputs.generate(cfg)
     assert inputs.fingerprint(inp) == g["fingerprint"]

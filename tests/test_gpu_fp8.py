@@ -33,7 +33,12 @@ def _case(rng, B, Hh, lens, cap, dh=64):
     V = _bf16(rng.standard_normal((B, Hh, cap, dh)))
     K[0, 0, 64:128] *= 1e-3          # a tile with its own small scale
     V[0, 1, :64] = 0.0               # an all-zero tile
-    K[-1, -1, :64] *= 4.0            # and a large one (scores stay in the workloads' range)
+    K[-1, -1, :64] *= 4.0            # and a large one
+    # tiles whose largest value is about 1e-37 (below 448 * 2^-127, so the
+    # scale exponent stays at -126); every value a normal number
+    tiny = lambda a: np.sign(a) * np.maximum(np.abs(a), 0.25) * 1e-37
+    K[0, 1 % Hh, :64] = tiny(K[0, 1 % Hh, :64])
+    V[0, 2 % Hh, :64] = tiny(V[0, 2 % Hh, :64])
     K, V = _bf16(K), _bf16(V)        # the values the bf16 cache holds
     for b, n in enumerate(lens):
         K[b, :, n:] = np.nan         # rows past len must never be read
@@ -113,22 +118,27 @@ def _dequant_bf16_cache(dst, lens, cap):
 
 
 @pytest.mark.parametrize("shape", [
-    ("C1-like", 1, 16, [9216], 32, 64),
-    ("ragged", 3, 4, [100, 3000, 777], 32, 64),
-    ("partial-own", 2, 4, [300, 129], 20, 64),
-    ("C6-like", 1, 24, [9216], 32, 128),
-    ("ragged dh=128", 3, 4, [100, 3000, 777], 32, 128),
-    ("partial-own dh=128", 2, 4, [300, 129], 20, 128),
+    ("C1-like", 1, 16, [9216], 32, 64, 1.0),
+    ("ragged", 3, 4, [100, 3000, 777], 32, 64, 1.0),
+    ("partial-own", 2, 4, [300, 129], 20, 64, 1.0),
+    ("peaked scores", 2, 4, [3000, 700], 32, 64, 3.0),
+    ("C6-like", 1, 24, [9216], 32, 128, 1.0),
+    ("ragged dh=128", 3, 4, [100, 3000, 777], 32, 128, 1.0),
+    ("partial-own dh=128", 2, 4, [300, 129], 20, 128, 1.0),
+    ("peaked scores dh=128", 2, 4, [3000, 700], 32, 128, 3.0),
 ])
 def test_attention_fp8_equals_bf16_on_dequantised_values(shape):
-    name, B, Hh, lens, n_act, dh = shape
+    """q_std 3 gives score std 3 (12 on the tile whose keys are 4x larger)."""
+    name, B, Hh, lens, n_act, dh, q_std = shape
     print_case(f"E4M3 action attention {name}")
     rng = np.random.default_rng(17)
     cap = (max(lens) + 63) // 64 * 64
     K, V = _case(rng, B, Hh, lens, cap, dh)
     _, dst = _device_caches(K, V, lens, cap)
     Kd, Vd = _dequant_bf16_cache(dst, lens, cap)
-    q = torch.tensor(_bf16(rng.standard_normal((B, Hh, 32, dh)))).to(torch.bfloat16).cuda()
+    # the bf16 kernels take q as Q log2(e) / sqrt(dh), rounded once
+    qs = np.log2(np.e) / np.sqrt(dh)
+    q = torch.tensor(_bf16(rng.standard_normal((B, Hh, 32, dh)) * q_std * qs)).to(torch.bfloat16).cuda()
     ka = torch.tensor(_bf16(rng.standard_normal((B, Hh, 32, dh)))).to(torch.bfloat16).cuda()
     va = torch.tensor(_bf16(rng.standard_normal((B, Hh, dh, 32)))).to(torch.bfloat16).cuda()
     o8 = torch.empty((B, 32, Hh * dh), dtype=torch.bfloat16, device="cuda")
@@ -147,7 +157,7 @@ def test_attention_fp8_equals_bf16_on_dequantised_values(shape):
         kk = np.concatenate([Kd[b][:, :lens[b]], ka[b, :, :n_act].float().cpu().numpy()], axis=1)
         vv = np.concatenate([Vd[b][:, :lens[b]], va[b, :, :, :n_act].float().cpu().numpy().transpose(0, 2, 1)],
                             axis=1)
-        qq = q[b].float().cpu().numpy()
+        qq = q[b].double().cpu().numpy() / qs
         ref.append(O.attention(torch.tensor(qq, dtype=torch.float64).permute(1, 0, 2),
                                torch.tensor(kk, dtype=torch.float64).permute(1, 0, 2),
                                torch.tensor(vv, dtype=torch.float64).permute(1, 0, 2)).numpy())
@@ -189,16 +199,19 @@ def test_chunk_with_fp8_cache_vs_oracle(variant):
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-def test_fp8_full_size_against_oracle_values():
-    path = os.path.join(GOLDEN, "C1_fp8.json")
+@pytest.mark.parametrize("name", ["C1", "C6"])
+def test_fp8_full_size_against_oracle_values(name):
+    """Full size with the E4M3 cache: C1 (16 x 64 heads) and C6 (the real
+    widths, 24 x 128 heads) against the oracle with the same quantisation."""
+    path = os.path.join(GOLDEN, f"{name}_fp8.json")
     if not os.path.exists(path):
-        pytest.skip(f"{path} not generated (tests/golden/make_golden.py C1+fp8)")
+        pytest.skip(f"{path} not generated (tests/golden/make_golden.py {name}+fp8)")
     g = json.load(open(path))
-    cfg = configs.get("C1", kv_fp8=True)
-    print_case("full size C1 with the E4M3 cache")
+    cfg = configs.get(name, kv_fp8=True)
+    print_case(f"full size {name} with the E4M3 cache")
     inp = inputs.generate(cfg)
     assert inputs.fingerprint(inp) == g["fingerprint"]
     dc = _run_gpu(cfg, inp)
     err = rel_l2(to_np(dc.actions), np.array(g["actions"]))
-    print_case(f"C1 E4M3 final actions rel-L2 {err:.3e}")
+    print_case(f"{name} E4M3 final actions rel-L2 {err:.3e}")
     assert err <= 2e-2

@@ -25,6 +25,22 @@ def _dev(a, dt):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda().to(_tdt(dt)).contiguous()
 
 
+def _qscale(dt, dh):
+    """Factor the bf16 kernels expect in q (log2 e / sqrt(dh)); fp32 q is plain."""
+    return np.log2(np.e) / np.sqrt(dh) if dt == wam.WAM_BF16 else 1.0
+
+
+def _q_device(q, dt, dh):
+    """The query array the kernel entry takes: bf16 q carries log2 e / sqrt(dh),
+    rounded once."""
+    return inputs.round_bf16((q * _qscale(dt, dh)).astype(np.float32)) if dt == wam.WAM_BF16 else q
+
+
+def _q_oracle(qd, dt, dh):
+    """The plain queries whose scores the kernel computes from qd (float64)."""
+    return qd.astype(np.float64) / _qscale(dt, dh)
+
+
 # ---------------------------------------------------------------- visibility
 @pytest.mark.parametrize("case", [
     ((0, 1, 2, 3, 4), (1, 1, 1), 3, 2, 5),
@@ -46,40 +62,61 @@ def test_debug_visibility_matches_oracle(case):
 
 
 # ---------------------------------------------------------------- prefill attention
-@pytest.mark.parametrize("dh", [64, 128])
-@pytest.mark.parametrize("dt", [wam.WAM_F32, wam.WAM_BF16])
-@pytest.mark.parametrize("rows", [(0, 500), (100, 300), (400, 100)])
-def test_attention_prefill_vs_oracle(dt, rows, dh):
+def _prefill_case(dt, rows, dh, seed, q_std=1.0, k_std=(1.0, 1.0)):
+    """Prefill attention of rows row0..row0+nq-1 over 5 frames of 100 tokens
+    (blocks 0,1,1,2,3) against the float64 oracle; returns rel-L2.  q ~ N(0,
+    q_std^2), K ~ N(0, k_std[h]^2) per head: score std = q_std * k_std."""
     row0, nq = rows
-    print_case(f"prefill attention dt={dt} rows={rows} dh={dh}")
-    rng = np.random.default_rng(1 + row0)
+    rng = np.random.default_rng(seed)
     Hh, P, cap = 2, 100, 576
     blocks = (0, 1, 1, 2, 3)
     _, kend = wam.frame_table(blocks, None, 5, 0, P)
     T = 5 * P
-    q = _rand(rng, (Hh, nq, dh), dt)
-    K = _rand(rng, (Hh, cap, dh), dt)
+    qd = _q_device(_rand(rng, (Hh, nq, dh), dt, q_std), dt, dh)
+    K = _rand(rng, (Hh, cap, dh), dt) * np.asarray(k_std, np.float32)[:, None, None]
     V = _rand(rng, (Hh, cap, dh), dt)
     K[:, T:] = np.nan   # rows past the last frame must never be read
     V[:, T:] = np.nan
     out = torch.empty((nq, Hh * dh), dtype=_tdt(dt), device="cuda")
-    wam.attention_prefill(dt, _dev(q, dt), row0, P, kend, _dev(K, dt),
+    wam.attention_prefill(dt, _dev(qd, dt), row0, P, kend, _dev(K, dt),
                           _dev(np.ascontiguousarray(V.transpose(0, 2, 1)), dt), cap, out)
     torch.cuda.synchronize()
     qrow = np.arange(row0, row0 + nq)
     mask = torch.tensor(np.arange(T)[None, :] < kend[qrow // P][:, None])
-    ref = O.attention(torch.tensor(q, dtype=f64).permute(1, 0, 2), torch.tensor(K[:, :T], dtype=f64).permute(1, 0, 2),
+    ref = O.attention(torch.tensor(_q_oracle(qd, dt, dh)).permute(1, 0, 2),
+                      torch.tensor(K[:, :T], dtype=f64).permute(1, 0, 2),
                       torch.tensor(V[:, :T], dtype=f64).permute(1, 0, 2), lambda a, b: mask[a:b])
     got = to_np(out).reshape(nq, Hh, dh)
     assert np.isfinite(got).all()
-    assert rel_l2(got, ref.numpy()) <= (1e-5 if dt == wam.WAM_F32 else 5e-3)
+    return rel_l2(got, ref.numpy())
+
+
+@pytest.mark.parametrize("dh", [64, 128])
+@pytest.mark.parametrize("dt", [wam.WAM_F32, wam.WAM_BF16])
+@pytest.mark.parametrize("rows", [(0, 500), (100, 300), (400, 100)])
+def test_attention_prefill_vs_oracle(dt, rows, dh):
+    print_case(f"prefill attention dt={dt} rows={rows} dh={dh}")
+    err = _prefill_case(dt, rows, dh, 1 + rows[0])
+    assert err <= (1e-5 if dt == wam.WAM_F32 else 5e-3)
+
+
+@pytest.mark.parametrize("dh", [64, 128])
+@pytest.mark.parametrize("dt", [wam.WAM_F32, wam.WAM_BF16])
+def test_attention_prefill_peaked_scores(dt, dh):
+    """Peaked attention: score std 3 on head 0 and 24 on head 1 (keys 8x
+    larger), where the softmax is close to one-hot; a second rounding of the
+    queries would show here as an error growing with the scores."""
+    print_case(f"prefill attention peaked scores dt={dt} dh={dh}")
+    err = _prefill_case(dt, (0, 500), dh, 21, q_std=3.0, k_std=(1.0, 8.0))
+    assert err <= (1e-5 if dt == wam.WAM_F32 else 5e-3)
 
 
 # ---------------------------------------------------------------- action attention
-def _action_case(rng, dt, B, Hh, lens, n_act, cap=None, dh=64):
+def _action_case(rng, dt, B, Hh, lens, n_act, cap=None, dh=64, q_std=1.0):
+    """q is returned in the form the kernel entry takes (see _q_device)."""
     H = 32
     cap = cap or (max(lens) + 63) // 64 * 64 if lens else 64
-    q = _rand(rng, (B, Hh, H, dh), dt)
+    q = _q_device(_rand(rng, (B, Hh, H, dh), dt, q_std), dt, dh)
     ka = _rand(rng, (B, Hh, H, dh), dt)
     va = _rand(rng, (B, Hh, H, dh), dt)
     K = _rand(rng, (B, Hh, cap, dh), dt)
@@ -92,8 +129,9 @@ def _action_case(rng, dt, B, Hh, lens, n_act, cap=None, dh=64):
     return q, ka, va, K, V, cap
 
 
-def _action_ref(q, ka, va, K, V, lens, n_act, with_cache=True):
-    B = q.shape[0]
+def _action_ref(q, ka, va, K, V, lens, n_act, with_cache=True, dt=wam.WAM_BF16):
+    B, dh = q.shape[0], q.shape[3]
+    q = _q_oracle(q, dt, dh)
     outs = []
     for b in range(B):
         ks, vs = [], []
@@ -162,6 +200,21 @@ def test_attention_action_vs_oracle(shape):
     assert rel_l2(got, ref) <= 5e-3
 
 
+@pytest.mark.parametrize("dh", [64, 128])
+@pytest.mark.parametrize("dt", [wam.WAM_F32, wam.WAM_BF16])
+def test_attention_action_peaked_scores(dt, dh):
+    """Peaked attention over [cache ; own keys]: score std 3, and 24 on the
+    last head (its cached keys 8x larger), several splits per head."""
+    rng = np.random.default_rng(19)
+    lens = [3000, 700]
+    print_case(f"action attention peaked scores dt={dt} dh={dh}")
+    q, ka, va, K, V, cap = _action_case(rng, dt, 2, 4, lens, 32, dh=dh, q_std=3.0)
+    K[:, -1] *= 8.0
+    got = _run_action(dt, q, ka, va, 32, K, V, cap, lens)
+    ref = _action_ref(q, ka, va, K, V, lens, 32, dt=dt)
+    assert rel_l2(got, ref) <= (1e-5 if dt == wam.WAM_F32 else 5e-3)
+
+
 def test_attention_action_f32_dh128_vs_oracle():
     dt = wam.WAM_F32
     rng = np.random.default_rng(15)
@@ -169,7 +222,7 @@ def test_attention_action_f32_dh128_vs_oracle():
     print_case("action attention fp32, dh=128")
     q, ka, va, K, V, cap = _action_case(rng, dt, 3, 3, lens, 20, dh=128)
     got = _run_action(dt, q, ka, va, 20, K, V, cap, lens)
-    assert rel_l2(got, _action_ref(q, ka, va, K, V, lens, 20)) <= 1e-5
+    assert rel_l2(got, _action_ref(q, ka, va, K, V, lens, 20, dt=dt)) <= 1e-5
 
 
 def test_attention_action_batch_independent_bitwise():

@@ -130,6 +130,43 @@ def test_rmsnorm_vs_library():
     assert torch.max(torch.abs((y * y).mean(-1) - 1)) < 1e-5
 
 
+def test_head_vs_library():
+    # the velocity head: the expert's final RMSNorm with its own gain, then the
+    # output projection [C][D] (non-square, so a transposed W fails), on rows
+    # whose RMS is far from 1 (so a dropped RMSNorm fails)
+    r = np.random.default_rng(6)
+    X = torch.tensor(r.standard_normal((7, 96)) * 5.0, dtype=f64)
+    g = torch.tensor(1 + 0.3 * r.standard_normal(96), dtype=f64)
+    W = torch.tensor(r.standard_normal((5, 96)), dtype=f64)
+    got = O.head(X, g, W)
+    assert tuple(got.shape) == (7, 5)
+    ref = F.linear(F.rms_norm(X, (96,), g, eps=1e-6), W)
+    assert torch.max(torch.abs(got - ref)) < 1e-12
+    assert torch.max(torch.abs(got - F.linear(X, W))) > 1.0
+
+
+def test_heads_read_their_own_expert_gain():
+    # Doubling an expert's g_out doubles exactly its velocity (the head is
+    # linear in the gain, and 2 is exact): a head that dropped the gain or
+    # took another weight's fails.
+    cfg = configs.small("HG", dtype="f32", L=1, D=128, Hh=2, Fm=256, P=16, Fh=2, Ff=1,
+                        frame_block=(0, 1, 2), pad_frames=0, V=1, N=1, read_map=(0,))
+    inp = inputs.generate(cfg)
+    vw = O.to_torch_expert(inp["video"], f64)
+    aw = O.to_torch_expert(inp["action"], f64)
+    cache, z, _ = O.video_prefill(cfg, vw, inp["hist"][0], inp["hist_valid"][0], inp["eps_v"][0])
+    a = torch.tensor(inp["eps_a"][0], dtype=f64)
+    v1 = O.action_velocity(cfg, aw, O.read_layers(cfg, cache, None), a, 0.7)
+    aw2 = dict(aw, g_out=aw["g_out"] * 2.0)
+    vw2 = dict(vw, g_out=vw["g_out"] * 2.0)
+    assert torch.equal(O.action_velocity(cfg, aw2, O.read_layers(cfg, cache, None), a, 0.7), 2.0 * v1)
+    # the video head: one imagine step moves z by (sigma_1 - sigma_0) v-hat
+    eps = torch.tensor(inp["eps_v"][0], dtype=f64).reshape(-1, cfg.Cv)
+    _, z2, _ = O.video_prefill(cfg, vw2, inp["hist"][0], inp["hist_valid"][0], inp["eps_v"][0])
+    assert torch.allclose(z2 - eps, 2.0 * (z - eps), rtol=1e-12, atol=1e-14)
+    assert not torch.allclose(z - eps, torch.zeros_like(z))
+
+
 def test_gelu_vs_library():
     x = torch.linspace(-8, 8, 1001, dtype=f64)
     assert torch.max(torch.abs(O.gelu(x) - F.gelu(x))) < 1e-15
@@ -588,6 +625,12 @@ def test_kv_tile_exponent_boundaries():
         assert O.kv_tile_exponent(np.nextafter(edge, 1e30)) == e + 1
         assert O.kv_tile_exponent(np.nextafter(edge, 0)) == e
     assert O.kv_tile_exponent(0.0) == 0
+    # the scale stays a normal float32 number: e >= -126, and codes still fit
+    # (|x| 2^126 <= 448 whenever the unclamped e would be below -126)
+    for a in (1e-37, 448.0 * 2.0 ** -127, 448.0 * 2.0 ** -126, 2.0 ** -130):
+        e = O.kv_tile_exponent(a)
+        assert e == -126 and a * 2.0 ** 126 <= 448.0
+    assert O.kv_tile_exponent(np.nextafter(448.0 * 2.0 ** -126, 1.0)) == -125
     rng = np.random.default_rng(5)
     for a in rng.lognormal(0, 4, 200):
         e = O.kv_tile_exponent(a)
@@ -714,3 +757,24 @@ def test_rope_option_padding_and_streaming():
     for (Kf, Vf), (Ke, Ve) in zip(full, ext):
         assert torch.max(torch.abs(Kf - Ke)) < 1e-12
         assert torch.max(torch.abs(Vf - Ve)) < 1e-12
+
+
+# ---------------------------------------------------------------- sharp variant
+@pytest.mark.parametrize("D,qk_std", [(256, 0.12), (1024, 0.06)])
+def test_sharp_variant_scores_are_peaked(D, qk_std):
+    # the diagnostic variant does what it is for: Wq, Wk ~ N(0, qk_std^2) give
+    # pre-softmax scores of std about D qk_std^2 (3.7 here) in the first video
+    # layer, against about 0.4 with 0.02 at width 1024
+    cfg = configs.small("SH", dtype="f32", L=1, D=D, Hh=D // 64, Fm=256, P=64, Fh=2, Ff=1,
+                        frame_block=(0, 1, 2), pad_frames=0, V=1, N=1, read_map=(0,),
+                        qk_std=qk_std)
+    inp = inputs.generate(cfg)
+    w = O.to_torch_expert(inp["video"], f64)
+    x = torch.from_numpy(inp["hist"][0].reshape(-1, cfg.Cv)).double()
+    X = O.embed(x, w["w_in"], 0.0, cfg.D)
+    lw = w["layers"][0]
+    qkv = O.rmsnorm(X, lw["g1"]) @ lw["wqkv"].T
+    q = qkv[:, :cfg.D].reshape(-1, cfg.Hh, cfg.dh).permute(1, 0, 2)
+    k = qkv[:, cfg.D:2 * cfg.D].reshape(-1, cfg.Hh, cfg.dh).permute(1, 2, 0)
+    s = torch.matmul(q, k) / math.sqrt(cfg.dh)
+    assert 2.5 < float(s.std()) < 5.5
