@@ -18,6 +18,15 @@ Five synthetic workloads span the three systems the pages describe:
 * ``C5`` Long-WAM co-denoising (CoD): the C3 shape with the two future frames
   and the action chunk denoised together, 4 joint steps (V4/A4), the video to
   flow time 0 ("Long-WAM ... Summary" page, section 3.2 and appendix F).
+* ``C6`` C1's chunk at the experts' own widths (see below).
+
+Options (``get(name, ...)``): ``kv_fp8`` (E4M3 cache read by the action
+layers), ``rope`` (rotary positions), ``qk_std=0.06`` (the sharp variant) and
+the text/state condition ``Tc``/``Ct``/``S``: ``Tc - 1`` text tokens of width
+``Ct`` (standing in for the text encoder's output) and one proprio token that a
+linear layer makes from the ``S`` robot-state numbers, read by every layer of
+both experts through cross-attention ("Fast-WAM 精读" section 四.5 and
+section 五, step 3); ``CONDITION`` holds the setting used with C6.
 
 This module holds shapes and tables only; no arithmetic of the method.
 """
@@ -60,6 +69,9 @@ class WamConfig:
     Da: int = 0           # action expert width (0: D); the attention interface is Hh x dh for both
     Fma: int = 0          # action expert MLP width (0: Fm)
     rope: bool = False    # rotary position embedding on Q and K of both experts (an option)
+    Tc: int = 0           # condition tokens per episode: Tc - 1 text tokens + 1 proprio token (0: none)
+    Ct: int = 0           # width of a condition token (the text encoder's output width)
+    S: int = 0            # proprio (robot state) dims (0: A)
 
     @property
     def F(self) -> int:
@@ -79,6 +91,11 @@ class WamConfig:
     def Fact(self) -> int:
         """MLP width of the action expert."""
         return self.Fma or self.Fm
+
+    @property
+    def Sdim(self) -> int:
+        """Robot state dims the proprio encoder reads."""
+        return self.S or self.A
 
     @property
     def n_valid_hist(self) -> int:
@@ -157,6 +174,12 @@ CONFIGS = {
         V=0, sigma_star=0.9, N=10, shift=1.0, read_map=_dense(30), seed=1006,
         Da=1024, Fma=4096),
 }
+
+
+# 100 text tokens of the text encoder's width 4096 plus one proprio token made
+# from 14 state numbers (RoboTwin's actions and states are both 14-dim,
+# "Fast-WAM 精读" section 四.3)
+CONDITION = dict(Tc=101, Ct=4096, S=14)
 
 
 def get(name: str, **overrides) -> WamConfig:

@@ -12,6 +12,10 @@ Recipe (stated once, used everywhere):
   ``qk_std``); RMSNorm gains ~ 1 + N(0, w_std^2);
 * history/anchor latent tokens, future noise eps_v and action noise eps_a
   ~ N(0, 1); padded history frames are exact zeros; fusion logits ~ N(0, 1);
+* with a text/state condition: text tokens (standing in for the text
+  encoder's output) and robot state ~ N(0, 1), the proprio encoder and the
+  cross-attention matrices ~ N(0, w_std^2), their RMSNorm gains
+  ~ 1 + N(0, w_std^2);
 * in bf16 workloads every device array is rounded to bf16
   (round-to-nearest-even) and kept as float32 holding bf16 values, so both
   paths consume identical numbers.
@@ -28,7 +32,9 @@ import numpy as np
 from .configs import WamConfig
 
 _G_VIDEO, _G_ACTION, _G_LOGITS, _G_HIST, _G_EPSV, _G_EPSA = 1, 2, 3, 4, 5, 6
+_G_TEXT, _G_STATE, _G_PROPRIO = 7, 8, 9
 _S_WIN, _S_G1, _S_QKV, _S_WO, _S_G2, _S_W1, _S_W2, _S_GOUT, _S_WOUT = range(9)
+_S_GX, _S_WQX, _S_WKVX, _S_WOX = 9, 10, 11, 12
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -53,6 +59,10 @@ def _normal(cfg: WamConfig, key, shape, std=1.0, mean=0.0) -> np.ndarray:
     if mean != 0.0:
         a += np.float32(mean)
     return round_bf16(a) if cfg.dtype == "bf16" else a
+
+
+LAYER_NAMES = ("g1", "wqkv", "wo", "g2", "w1", "w2")
+COND_NAMES = ("gx", "wqx", "wkvx", "wox")
 
 
 def expert_weights(cfg: WamConfig, which: str, n_layers: int | None = None,
@@ -85,13 +95,20 @@ def expert_weights(cfg: WamConfig, which: str, n_layers: int | None = None,
         jobs[("g2", l)] = (lambda l=l: _normal(cfg, (g, l, _S_G2), (D,), cfg.w_std, 1.0))
         jobs[("w1", l)] = (lambda l=l: _normal(cfg, (g, l, _S_W1), (Fm, D), cfg.w_std))
         jobs[("w2", l)] = (lambda l=l: _normal(cfg, (g, l, _S_W2), (D, Fm), cfg.w_std))
+        if cfg.Tc > 0:
+            # cross-attention to the condition: RMSNorm gain, Q from the
+            # expert's width, K and V from the condition width, output
+            jobs[("gx", l)] = (lambda l=l: _normal(cfg, (g, l, _S_GX), (D,), cfg.w_std, 1.0))
+            jobs[("wqx", l)] = (lambda l=l: _normal(cfg, (g, l, _S_WQX), (Dq, D), cfg.w_std))
+            jobs[("wkvx", l)] = (lambda l=l: _normal(cfg, (g, l, _S_WKVX), (2 * Dq, cfg.Ct), cfg.w_std))
+            jobs[("wox", l)] = (lambda l=l: _normal(cfg, (g, l, _S_WOX), (D, Dq), cfg.w_std))
     if pool is not None:
         futs = {k: pool.submit(f) for k, f in jobs.items()}
         res = {k: f.result() for k, f in futs.items()}
     else:
         res = {k: f() for k, f in jobs.items()}
-    layers = [{n: res[(n, l)] for n in ("g1", "wqkv", "wo", "g2", "w1", "w2")}
-              for l in range(L)]
+    names = LAYER_NAMES + (COND_NAMES if cfg.Tc > 0 else ())
+    layers = [{n: res[(n, l)] for n in names} for l in range(L)]
     return {"w_in": res["w_in"], "layers": layers, "g_out": res["g_out"],
             "w_out": res["w_out"]}
 
@@ -119,8 +136,13 @@ def generate(cfg: WamConfig, n_layers: int | None = None, threads: int = 8) -> d
     hist[valid == 0] = 0.0
     eps_v = _normal(cfg, (_G_EPSV,), (cfg.B, cfg.Ff, cfg.P, cfg.Cv))
     eps_a = _normal(cfg, (_G_EPSA,), (cfg.B, cfg.H, cfg.A))
-    return {"video": video, "action": action, "fuse_logits": logits,
-            "hist": hist, "hist_valid": valid, "eps_v": eps_v, "eps_a": eps_a}
+    out = {"video": video, "action": action, "fuse_logits": logits,
+           "hist": hist, "hist_valid": valid, "eps_v": eps_v, "eps_a": eps_a}
+    if cfg.Tc > 0:
+        out["text"] = _normal(cfg, (_G_TEXT,), (cfg.B, cfg.Tc - 1, cfg.Ct))
+        out["state"] = _normal(cfg, (_G_STATE,), (cfg.B, cfg.Sdim))
+        out["proprio_w"] = _normal(cfg, (_G_PROPRIO,), (cfg.Ct, cfg.Sdim), cfg.w_std)
+    return out
 
 
 def fingerprint(inp: dict) -> str:
@@ -139,10 +161,12 @@ def fingerprint(inp: dict) -> str:
         w = inp[ex]
         add(w["w_in"]); add(w["g_out"]); add(w["w_out"])
         for lw in w["layers"]:
-            for n in ("g1", "wqkv", "wo", "g2", "w1", "w2"):
-                add(lw[n])
+            for n in LAYER_NAMES + COND_NAMES:
+                if n in lw:
+                    add(lw[n])
     if inp["fuse_logits"] is not None:
         add(inp["fuse_logits"])
-    for n in ("hist", "hist_valid", "eps_v", "eps_a"):
-        add(inp[n])
+    for n in ("hist", "hist_valid", "eps_v", "eps_a", "text", "state", "proprio_w"):
+        if n in inp:
+            add(inp[n])
     return h.hexdigest()[:16]

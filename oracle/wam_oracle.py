@@ -14,9 +14,12 @@ rounded here.  Every function states the passage of the pages it follows.  The
 pages are:
 
 * "Long-WAM 源码精读" (yeyulingfeng.com), sections 03-04;
-* "Fast-WAM 精读" (alicepotter4869.xyz), sections 四, 五 and 七;
+* "Fast-WAM 精读" (alicepotter4869.xyz), sections 四 (the text/state
+  condition, 四.5), 五 (both experts read the condition through
+  cross-attention, step 3) and 七;
 * "Long-WAM: Scaling the Context of World-Action Models | Summary"
-  (greeksharifa.github.io), sections 3.1, 3.2, 4.2 and appendix B.2;
+  (greeksharifa.github.io), sections 3.1, 3.2, 4.2 (text/state KV reused
+  across denoising steps) and appendix B.2;
 * "世界模型之Faster-WAM详解" (171host.com), sections 3.1-3.4.
 
 Pins: every function here is checked by ``tests/test_oracle_pins.py`` against
@@ -219,7 +222,8 @@ def token_positions(cfg, first: int, n: int) -> Optional[torch.Tensor]:
 
 
 def layer(X, w: dict, Hh: int, ctx: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
-          allow: Optional[MaskFn] = None, kv_only: bool = False, pos=None):
+          allow: Optional[MaskFn] = None, kv_only: bool = False, pos=None,
+          cond: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
     """One expert layer on token states X [n, D] with attention context ctx.
 
     Keys and values are [ctx ; this layer's own K, V] ("Fast-WAM" page
@@ -233,6 +237,11 @@ def layer(X, w: dict, Hh: int, ctx: Optional[Tuple[torch.Tensor, torch.Tensor]] 
     which may differ from the expert's own width D (Wqkv [3 Dq][D], Wo [D][Dq]).
     With ``pos`` (token positions [n]) Q and K are rotated by ``rope`` before
     the attention, so the K rows returned for the cache are rotated too.
+    With ``cond`` (this layer's condition K, V [Tc, Hh, dh], ``condition_kv``)
+    a cross-attention sub-layer follows the self-attention:
+      X += Attn(RMSNorm(X; gx) Wqx^T ; K_c, V_c) Wox^T
+    (the tokens read the text/state condition through cross-attention,
+    "Fast-WAM 精读" section 五, step 3; no rotary positions there).
     """
     n, D = X.shape
     Dq = w["wqkv"].shape[0] // 3
@@ -253,8 +262,41 @@ def layer(X, w: dict, Hh: int, ctx: Optional[Tuple[torch.Tensor, torch.Tensor]] 
         Kall, Vall = K, V
     O = attention(Q, Kall, Vall, allow)
     X = X + O.reshape(n, Dq) @ w["wo"].T
+    if cond is not None:
+        Qx = (rmsnorm(X, w["gx"]) @ w["wqx"].T).reshape(n, Hh, dh)
+        X = X + attention(Qx, cond[0], cond[1]).reshape(n, Dq) @ w["wox"].T
     X = X + gelu(rmsnorm(X, w["g2"]) @ w["w1"].T) @ w["w2"].T
     return X, K, V
+
+
+def condition(text_b, state_b, proprio_w):
+    """The condition sequence of one episode [Tc, Ct]: the text tokens (the
+    text encoder's output, "Fast-WAM 精读" section 四.5), then one proprio token
+    that a linear layer makes from the robot state, of the text tokens' width,
+    appended after them (same section)."""
+    return torch.cat([text_b, (state_b @ proprio_w.T).unsqueeze(0)])
+
+
+def condition_kv(ctx, lw: dict, Hh: int):
+    """K, V [Tc, Hh, dh] of the condition for one expert layer: ctx Wk_x^T and
+    ctx Wv_x^T with wkvx = [Wk_x ; Wv_x].  They do not depend on the flow time
+    or on any latent, so they are computed once per inference call and reused
+    at every denoising step (text/state KV, Long-WAM Summary section 4.2)."""
+    Dq = lw["wkvx"].shape[0] // 2
+    kv = ctx @ lw["wkvx"].T
+    n = ctx.shape[0]
+    return kv[:, :Dq].reshape(n, Hh, -1), kv[:, Dq:].reshape(n, Hh, -1)
+
+
+def condition_cache(cfg, w: dict, ctx):
+    """Per-layer condition K, V of one expert (None without a condition)."""
+    if ctx is None:
+        return None
+    return [condition_kv(ctx, lw, cfg.Hh) for lw in w["layers"]]
+
+
+def _cl(cond, l):
+    return None if cond is None else cond[l]
 
 
 def head(X, g_out, w_out):
@@ -305,7 +347,7 @@ def oracle_dtype(cfg) -> torch.dtype:
     return torch.float64 if cfg.dtype == "f32" else torch.float32
 
 
-def history_cache(cfg, vw: dict, hist_b, valid_b, drop_padded: bool = True):
+def history_cache(cfg, vw: dict, hist_b, valid_b, drop_padded: bool = True, cond=None):
     """History/anchor prefill of one episode: the history tokens at sigma = 0
     run through the L layers with block-causal attention and each layer's
     K, V are kept (Fast-WAM page section 七.1, ``prefill_video_cache``;
@@ -339,7 +381,8 @@ def history_cache(cfg, vw: dict, hist_b, valid_b, drop_padded: bool = True):
             vt = valid[fh]
             pos = torch.cumsum(vt, 0) - vt
         for l, lw in enumerate(vw["layers"]):
-            X, K, V = layer(X, lw, Hh, None, mask_h, kv_only=(l == L - 1), pos=pos)
+            X, K, V = layer(X, lw, Hh, None, mask_h, kv_only=(l == L - 1), pos=pos,
+                            cond=_cl(cond, l))
             cache_h.append((K, V))
     else:
         empty = torch.zeros((0, Hh, cfg.dh), dtype=dt)
@@ -347,7 +390,7 @@ def history_cache(cfg, vw: dict, hist_b, valid_b, drop_padded: bool = True):
     return cache_h, fall, valid, mask_f
 
 
-def extend_history(cfg, vw: dict, cache_old, n_old: int, hist_b, valid_b):
+def extend_history(cfg, vw: dict, cache_old, n_old: int, hist_b, valid_b, cond=None):
     """Append history frames n_old..Fh-1 of one episode to the cache of its
     first n_old frames (their valid rows, in order): the new frames' tokens at
     sigma = 0 run through the L layers with keys [cached rows ; new rows]
@@ -379,12 +422,13 @@ def extend_history(cfg, vw: dict, cache_old, n_old: int, hist_b, valid_b):
     pos = token_positions(cfg, int(cache_old[0][0].shape[0]), X.shape[0])
     cache = []
     for l, lw in enumerate(vw["layers"]):
-        X, K, V = layer(X, lw, Hh, cache_old[l], mask, kv_only=(l == L - 1), pos=pos)
+        X, K, V = layer(X, lw, Hh, cache_old[l], mask, kv_only=(l == L - 1), pos=pos,
+                        cond=_cl(cond, l))
         cache.append((torch.cat([cache_old[l][0], K]), torch.cat([cache_old[l][1], V])))
     return cache
 
 
-def video_prefill(cfg, vw: dict, hist_b, valid_b, eps_v_b, drop_padded: bool = True):
+def video_prefill(cfg, vw: dict, hist_b, valid_b, eps_v_b, drop_padded: bool = True, cond=None):
     """Video expert for one episode: history prefill, imagine, cache pass.
 
     * History/anchor tokens at sigma = 0 run through the L layers with
@@ -406,7 +450,7 @@ def video_prefill(cfg, vw: dict, hist_b, valid_b, eps_v_b, drop_padded: bool = T
     """
     dt = vw["w_in"].dtype
     D, Hh, L = cfg.D, cfg.Hh, len(vw["layers"])
-    cache_h, fall, valid, mask_f = history_cache(cfg, vw, hist_b, valid_b, drop_padded)
+    cache_h, fall, valid, mask_f = history_cache(cfg, vw, hist_b, valid_b, drop_padded, cond)
 
     z = torch.from_numpy(np.ascontiguousarray(eps_v_b)).to(dt).reshape(-1, cfg.Cv)
     pos_f = token_positions(cfg, int(sum(valid_b[:cfg.Fh])) * cfg.P, z.shape[0])
@@ -416,7 +460,7 @@ def video_prefill(cfg, vw: dict, hist_b, valid_b, eps_v_b, drop_padded: bool = T
         def vel(zc, k, s):
             X = embed(zc, vw["w_in"], s, D)
             for l, lw in enumerate(vw["layers"]):
-                X, _, _ = layer(X, lw, Hh, cache_h[l], mask_f, pos=pos_f)
+                X, _, _ = layer(X, lw, Hh, cache_h[l], mask_f, pos=pos_f, cond=_cl(cond, l))
             return head(X, vw["g_out"], vw["w_out"])
 
         z, _ = integrate(z, sig, vel)
@@ -428,7 +472,8 @@ def video_prefill(cfg, vw: dict, hist_b, valid_b, eps_v_b, drop_padded: bool = T
     keep = valid[fall].bool()          # the cache holds valid rows only
     X = embed(z, vw["w_in"], sigma_f, D)
     for l, lw in enumerate(vw["layers"]):
-        X, K, V = layer(X, lw, Hh, cache_h[l], mask_f, kv_only=(l == L - 1), pos=pos_f)
+        X, K, V = layer(X, lw, Hh, cache_h[l], mask_f, kv_only=(l == L - 1), pos=pos_f,
+                        cond=_cl(cond, l))
         cache.append((torch.cat([cache_h[l][0], K])[keep], torch.cat([cache_h[l][1], V])[keep]))
     return cache, z, fall[keep]
 
@@ -458,7 +503,7 @@ def fuse_interval(cache: List[Tuple[torch.Tensor, torch.Tensor]], fuse, logits):
 
 
 def action_velocity(cfg, aw: dict, kv_read: List[Optional[Tuple]], a, sigma: float,
-                    pos0: int = 0):
+                    pos0: int = 0, cond=None):
     """One pass of the action expert at flow time sigma: v-hat for the chunk.
 
     Per layer the 32 action queries attend over [video K/V read by this layer ;
@@ -466,21 +511,23 @@ def action_velocity(cfg, aw: dict, kv_read: List[Optional[Tuple]], a, sigma: flo
     nothing (SparseMoT, Faster-WAM page section 3.2); no mask among action
     tokens (Long-WAM Summary section 3.2: the entire noisy chunk is visible).
     ``pos0``: position of the first action token (the episode's cached rows
-    come first) for the rotary option.
+    come first) for the rotary option.  ``cond``: the action expert's
+    per-layer condition K, V (``condition_cache``), or None.
     """
     X = embed(a, aw["w_in"], sigma, cfg.Dact)
     pos = token_positions(cfg, pos0, X.shape[0])
     for l, lw in enumerate(aw["layers"]):
-        X, _, _ = layer(X, lw, cfg.Hh, kv_read[l], None, pos=pos)
+        X, _, _ = layer(X, lw, cfg.Hh, kv_read[l], None, pos=pos, cond=_cl(cond, l))
     return head(X, aw["g_out"], aw["w_out"])
 
 
-def denoise(cfg, aw: dict, kv_read, eps_a_b, pos0: int = 0):
+def denoise(cfg, aw: dict, kv_read, eps_a_b, pos0: int = 0, cond=None):
     """N Euler steps of the action flow from noise at t=1 to t=0, re-reading
-    the same video K/V at every step (Fast-WAM page section 七.2-七.3)."""
+    the same video K/V (and condition K/V) at every step (Fast-WAM page
+    section 七.2-七.3)."""
     t = schedule(cfg.N, 0.0, cfg.shift)
     a = torch.from_numpy(np.ascontiguousarray(eps_a_b)).to(aw["w_in"].dtype)
-    return integrate(a, t, lambda x, k, s: action_velocity(cfg, aw, kv_read, x, s, pos0))
+    return integrate(a, t, lambda x, k, s: action_velocity(cfg, aw, kv_read, x, s, pos0, cond))
 
 
 def read_layers(cfg, cache, fused):
@@ -488,6 +535,14 @@ def read_layers(cfg, cache, fused):
     page section 四.4), fused pair m at interaction layers, nothing elsewhere."""
     src = fused if cfg.fuse else cache
     return [None if r < 0 else src[r] for r in cfg.read_map]
+
+
+def episode_condition(cfg, inp: dict, b: int, dt):
+    """Condition sequence of episode b (None without one)."""
+    if cfg.Tc <= 0:
+        return None
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dt)
+    return condition(t(inp["text"][b]), t(inp["state"][b]), t(inp["proprio_w"]))
 
 
 def run_chunk(cfg, inp: dict, dtype=None, drop_padded: bool = True,
@@ -506,13 +561,15 @@ def run_chunk(cfg, inp: dict, dtype=None, drop_padded: bool = True,
     aw = to_torch_expert(inp["action"], dt)
     acts, zs, vhs, caches, fuseds = [], [], [], [], []
     for b in range(cfg.B):
+        ctx = episode_condition(cfg, inp, b, dt)
+        condv, conda = condition_cache(cfg, vw, ctx), condition_cache(cfg, aw, ctx)
         cache, z, _ = video_prefill(cfg, vw, inp["hist"][b], inp["hist_valid"][b],
-                                    inp["eps_v"][b], drop_padded)
+                                    inp["eps_v"][b], drop_padded, condv)
         fused = fuse_interval(cache, cfg.fuse, inp["fuse_logits"]) if cfg.fuse else None
         kv_read = read_layers(cfg, cache, fused)
         if kv_fp8:
             kv_read = quantize_read(kv_read)
-        a, vh = denoise(cfg, aw, kv_read, inp["eps_a"][b], int(cache[0][0].shape[0]))
+        a, vh = denoise(cfg, aw, kv_read, inp["eps_a"][b], int(cache[0][0].shape[0]), conda)
         if cache_sampler is not None:
             cache_sampler(b, cache, fused)
         acts.append(a.double().numpy())
@@ -535,7 +592,7 @@ def run_chunk(cfg, inp: dict, dtype=None, drop_padded: bool = True,
 
 
 def codenoise(cfg, vw: dict, aw: dict, hist_b, valid_b, eps_v_b, eps_a_b, steps: int,
-              sigma_video_end: float = 0.0):
+              sigma_video_end: float = 0.0, condv=None, conda=None):
     """Co-denoising of one episode: the future video latents and the action
     chunk take the same number of Euler steps together.
 
@@ -568,7 +625,7 @@ def codenoise(cfg, vw: dict, aw: dict, hist_b, valid_b, eps_v_b, eps_a_b, steps:
     D, Hh = cfg.D, cfg.Hh
     if cfg.fuse:
         raise ValueError("co-denoising reads the per-layer cache (no interval fusion)")
-    cache_h, fall, valid, mask_f = history_cache(cfg, vw, hist_b, valid_b)
+    cache_h, fall, valid, mask_f = history_cache(cfg, vw, hist_b, valid_b, cond=condv)
     sv = schedule(steps, sigma_video_end, cfg.shift)
     ta = schedule(steps, 0.0, cfg.shift)
     z = torch.from_numpy(np.ascontiguousarray(eps_v_b)).to(dt).reshape(-1, cfg.Cv)
@@ -581,11 +638,11 @@ def codenoise(cfg, vw: dict, aw: dict, hist_b, valid_b, eps_v_b, eps_a_b, steps:
         X = embed(z, vw["w_in"], float(sv[k]), D)
         cache = []
         for l, lw in enumerate(vw["layers"]):
-            X, K, V = layer(X, lw, Hh, cache_h[l], mask_f, pos=pos_f)
+            X, K, V = layer(X, lw, Hh, cache_h[l], mask_f, pos=pos_f, cond=_cl(condv, l))
             cache.append((torch.cat([cache_h[l][0], K]), torch.cat([cache_h[l][1], V])))
         v_v = head(X, vw["g_out"], vw["w_out"])
         v_a = action_velocity(cfg, aw, [None if r < 0 else cache[r] for r in cfg.read_map],
-                              a, float(ta[k]), Th + z.shape[0])
+                              a, float(ta[k]), Th + z.shape[0], conda)
         traj.append((z, a, v_v, v_a))
         z = euler_step(z, v_v, sv[k], sv[k + 1])
         a = euler_step(a, v_a, ta[k], ta[k + 1])
@@ -608,8 +665,10 @@ def run_codenoise(cfg, inp: dict, dtype=None, steps: Optional[int] = None,
     aw = to_torch_expert(inp["action"], dt)
     acts, zs, vhs, caches = [], [], [], []
     for b in range(cfg.B):
+        ctx = episode_condition(cfg, inp, b, dt)
         a, z, traj, cache = codenoise(cfg, vw, aw, inp["hist"][b], inp["hist_valid"][b],
-                                      inp["eps_v"][b], inp["eps_a"][b], n, end)
+                                      inp["eps_v"][b], inp["eps_a"][b], n, end,
+                                      condition_cache(cfg, vw, ctx), condition_cache(cfg, aw, ctx))
         if cache_sampler is not None:
             cache_sampler(b, cache, None)
         acts.append(a.double().numpy())
@@ -740,7 +799,7 @@ def quantize_read(kv_read):
 
 
 def joint_mot_step(cfg, vw: dict, aw: dict, video_tok, video_sigma, video_frames,
-                   frame_valid, a, t: float, video_head: bool = False):
+                   frame_valid, a, t: float, video_head: bool = False, ctx=None):
     """One pass of the two experts over ONE joint sequence [video ; action],
     with no cache: each row uses its expert's weights, one attention over the
     union with an explicit mask where video rows see video columns by the
@@ -751,6 +810,9 @@ def joint_mot_step(cfg, vw: dict, aw: dict, video_tok, video_sigma, video_frames
     video_tok [Nv, Cv] at per-row levels video_sigma [Nv]; a [H, A] at t.
     Returns (v-hat of the action rows, per-layer video (K, V)), and with
     ``video_head`` also the video expert's v-hat of every video row.
+    With a condition sequence ``ctx`` [Tc, Ct], every row then reads it
+    through its own expert's cross-attention, its K, V projected from ctx
+    inside this pass (nothing cached).
     """
     D, Hh, dh, Dq = cfg.D, cfg.Hh, cfg.dh, cfg.Dq
     dt = vw["w_in"].dtype
@@ -779,6 +841,18 @@ def joint_mot_step(cfg, vw: dict, aw: dict, video_tok, video_sigma, video_frames
         O = attention(Q, K, V, lambda q0, q1: full[q0:q1]).reshape(-1, Dq)
         Xv = Xv + O[:Nv] @ lv["wo"].T
         Xa = Xa + O[Nv:] @ la["wo"].T
+        if ctx is not None:
+            for lw, rows in ((lv, "v"), (la, "a")):
+                Xr = Xv if rows == "v" else Xa
+                kvc = ctx @ lw["wkvx"].T
+                Kc = kvc[:, :Dq].reshape(-1, Hh, dh)
+                Vc = kvc[:, Dq:].reshape(-1, Hh, dh)
+                Qx = (rmsnorm(Xr, lw["gx"]) @ lw["wqx"].T).reshape(-1, Hh, dh)
+                Xr = Xr + attention(Qx, Kc, Vc).reshape(-1, Dq) @ lw["wox"].T
+                if rows == "v":
+                    Xv = Xr
+                else:
+                    Xa = Xr
         Xv = Xv + gelu(rmsnorm(Xv, lv["g2"]) @ lv["w1"].T) @ lv["w2"].T
         Xa = Xa + gelu(rmsnorm(Xa, la["g2"]) @ la["w1"].T) @ la["w2"].T
     if video_head:
@@ -786,7 +860,7 @@ def joint_mot_step(cfg, vw: dict, aw: dict, video_tok, video_sigma, video_frames
     return head(Xa, aw["g_out"], aw["w_out"]), kv
 
 
-def imagine_recompute(cfg, vw: dict, hist_b, valid_b, eps_v_b):
+def imagine_recompute(cfg, vw: dict, hist_b, valid_b, eps_v_b, cond=None):
     """Imagine without a history cache: at every video step the whole
     [history ; future] sequence runs through the layers (history at sigma=0).
     Returns z after V steps.  Equal to ``video_prefill``'s z because history
@@ -804,8 +878,8 @@ def imagine_recompute(cfg, vw: dict, hist_b, valid_b, eps_v_b):
 
     def vel(zc, k, s):
         X = torch.cat([embed(hist_tok, vw["w_in"], 0.0, D), embed(zc, vw["w_in"], s, D)])
-        for lw in vw["layers"]:
-            X, _, _ = layer(X, lw, Hh, None, mask)
+        for l, lw in enumerate(vw["layers"]):
+            X, _, _ = layer(X, lw, Hh, None, mask, cond=_cl(cond, l))
         return head(X[nh:], vw["g_out"], vw["w_out"])
 
     z0 = torch.from_numpy(np.ascontiguousarray(eps_v_b)).to(dt).reshape(-1, cfg.Cv)

@@ -62,18 +62,22 @@ def test_debug_visibility_matches_oracle(case):
 
 
 # ---------------------------------------------------------------- prefill attention
-def _prefill_case(dt, rows, dh, seed, q_std=1.0, k_std=(1.0, 1.0)):
-    """Prefill attention of rows row0..row0+nq-1 over 5 frames of 100 tokens
-    (blocks 0,1,1,2,3) against the float64 oracle; returns rel-L2.  q ~ N(0,
-    q_std^2), K ~ N(0, k_std[h]^2) per head: score std = q_std * k_std."""
+def _prefill_case(dt, rows, dh, seed, q_std=1.0, k_std=(1.0, 1.0), P=100, blocks=(0, 1, 1, 2, 3)):
+    """Prefill attention of rows row0..row0+nq-1 over frames of P tokens with
+    the given temporal blocks (default 5 frames of 100, blocks 0,1,1,2,3)
+    against the float64 oracle; returns rel-L2.  q ~ N(0, q_std^2),
+    K ~ N(0, k_std[h]^2) per head: score std = q_std * k_std."""
     row0, nq = rows
     rng = np.random.default_rng(seed)
-    Hh, P, cap = 2, 100, 576
-    blocks = (0, 1, 1, 2, 3)
-    _, kend = wam.frame_table(blocks, None, 5, 0, P)
-    T = 5 * P
+    Hh = 2
+    F = len(blocks)
+    _, kend = wam.frame_table(blocks, None, F, 0, P)
+    T = F * P
+    cap = (T + 63) // 64 * 64 + 64
     qd = _q_device(_rand(rng, (Hh, nq, dh), dt, q_std), dt, dh)
     K = _rand(rng, (Hh, cap, dh), dt) * np.asarray(k_std, np.float32)[:, None, None]
+    if dt == wam.WAM_BF16:
+        K = inputs.round_bf16(K)   # the values the device holds
     V = _rand(rng, (Hh, cap, dh), dt)
     K[:, T:] = np.nan   # rows past the last frame must never be read
     V[:, T:] = np.nan
@@ -97,7 +101,28 @@ def _prefill_case(dt, rows, dh, seed, q_std=1.0, k_std=(1.0, 1.0)):
 def test_attention_prefill_vs_oracle(dt, rows, dh):
     print_case(f"prefill attention dt={dt} rows={rows} dh={dh}")
     err = _prefill_case(dt, rows, dh, 1 + rows[0])
+    print_case(f"  rel-L2 {err:.2e}")
     assert err <= (1e-5 if dt == wam.WAM_F32 else 5e-3)
+
+
+@pytest.mark.parametrize("dh", [64, 128])
+@pytest.mark.parametrize("case", [
+    # first frames of 40 keys: query tiles whose keys (or key splits) fit one tile
+    ("one-tile runs", (0, 300), 40, (0, 1, 2, 3, 4, 5, 6, 7)),
+    # 3000 keys: runs of up to 47 tiles, ragged block ends
+    ("long runs", (1000, 2000), 1000, (0, 1, 2)),
+    # frames of 65 keys in blocks of 2 or 3: a tile boundary inside most blocks
+    ("ragged blocks", (0, 650), 65, (0, 0, 1, 1, 1, 2, 2, 3, 4, 4)),
+])
+def test_attention_prefill_tile_runs(case, dh):
+    """Short and long runs of key tiles per query tile (the tile loop's first,
+    steady and last iterations), bf16, against the float64 oracle, with
+    peaked scores on head 1 so that the reference max moves inside a run."""
+    name, rows, P, blocks = case
+    print_case(f"prefill attention {name} dh={dh}")
+    err = _prefill_case(wam.WAM_BF16, rows, dh, 23, k_std=(1.0, 6.0), P=P, blocks=blocks)
+    print_case(f"  rel-L2 {err:.2e}")
+    assert err <= 5e-3
 
 
 @pytest.mark.parametrize("dh", [64, 128])
@@ -108,6 +133,7 @@ def test_attention_prefill_peaked_scores(dt, dh):
     queries would show here as an error growing with the scores."""
     print_case(f"prefill attention peaked scores dt={dt} dh={dh}")
     err = _prefill_case(dt, (0, 500), dh, 21, q_std=3.0, k_std=(1.0, 8.0))
+    print_case(f"  rel-L2 {err:.2e}")
     assert err <= (1e-5 if dt == wam.WAM_F32 else 5e-3)
 
 

@@ -549,12 +549,17 @@ def test_codenoise_steps_equal_joint_sequence(end):
     # Every CoD step equals one uncached joint pass over [history ; future at
     # the step's video level ; actions at the step's action level]: both
     # velocities, at every step (a stale or wrong-level future would differ).
-    cfg = _tiny(N=3)
+    # With end = 0.5 a text/state condition rides along: the cached condition
+    # K, V of both experts equal the joint pass's own projections.
+    cfg = _tiny(N=3, **(dict(Tc=4, Ct=10, S=3) if end else {}))
     inp = inputs.generate(cfg, threads=1)
     vw = O.to_torch_expert(inp["video"], f64)
     aw = O.to_torch_expert(inp["action"], f64)
+    ctx = O.episode_condition(cfg, inp, 0, f64)
     a_fin, z_fin, traj, cache = O.codenoise(cfg, vw, aw, inp["hist"][0], inp["hist_valid"][0],
-                                            inp["eps_v"][0], inp["eps_a"][0], 3, end)
+                                            inp["eps_v"][0], inp["eps_a"][0], 3, end,
+                                            O.condition_cache(cfg, vw, ctx),
+                                            O.condition_cache(cfg, aw, ctx))
     sv = O.schedule(3, end)
     ta = O.schedule(3, 0.0)
     valid_frames = [f for f in range(cfg.Fh) if inp["hist_valid"][0][f]]
@@ -566,7 +571,7 @@ def test_codenoise_steps_equal_joint_sequence(end):
         vtok = torch.cat([hist_tok, z_k])
         vsig = [0.0] * nh + [float(sv[k])] * z_k.shape[0]
         va, kv, vv = O.joint_mot_step(cfg, vw, aw, vtok, vsig, frames, fvalid, a_k, float(ta[k]),
-                                      video_head=True)
+                                      video_head=True, ctx=ctx)
         assert torch.max(torch.abs(va - va_k)) < 1e-12
         assert torch.max(torch.abs(vv[nh:] - vv_k)) < 1e-12
         if k == len(traj) - 1:
@@ -778,3 +783,116 @@ def test_sharp_variant_scores_are_peaked(D, qk_std):
     k = qkv[:, cfg.D:2 * cfg.D].reshape(-1, cfg.Hh, cfg.dh).permute(1, 2, 0)
     s = torch.matmul(q, k) / math.sqrt(cfg.dh)
     assert 2.5 < float(s.std()) < 5.5
+
+
+# ---------------------------------------------------------------- text/state condition
+def test_condition_sequence_closed_form():
+    # the text tokens as they are, then one proprio token: the robot state
+    # through one linear layer, of the text width ("Fast-WAM 精读" section 四.5)
+    r = np.random.default_rng(30)
+    text = torch.tensor(r.standard_normal((5, 12)), dtype=f64)
+    state = torch.tensor(r.standard_normal(7), dtype=f64)
+    W = torch.tensor(r.standard_normal((12, 7)), dtype=f64)     # [Ct][S]
+    ctx = O.condition(text, state, W)
+    assert tuple(ctx.shape) == (6, 12)
+    assert torch.equal(ctx[:5], text)
+    assert torch.max(torch.abs(ctx[5] - F.linear(state, W))) < 1e-13
+
+
+def _cond_weights(r, D, Dq, Ct, Fm, std=0.2):
+    t = lambda *sh: torch.tensor(r.standard_normal(sh) * std, dtype=f64)
+    return {"g1": 1 + t(D), "wqkv": t(3 * Dq, D), "wo": t(D, Dq), "g2": 1 + t(D), "w1": t(Fm, D),
+            "w2": t(D, Fm), "gx": 1 + t(D), "wqx": t(Dq, D), "wkvx": t(2 * Dq, Ct), "wox": t(D, Dq)}
+
+
+def test_cross_attention_layer_vs_library():
+    # self-attention, then cross-attention to the condition, then the MLP, with
+    # the expert width (40), the attention width (48 = 3 x 16) and the
+    # condition width (24) all different, so a transposed or swapped weight fails
+    r = np.random.default_rng(31)
+    D, Hh, dh, Ct, Fm, n, nc, Tc = 40, 3, 16, 24, 56, 9, 11, 7
+    Dq = Hh * dh
+    w = _cond_weights(r, D, Dq, Ct, Fm)
+    X = torch.tensor(r.standard_normal((n, D)), dtype=f64)
+    sctx = (torch.tensor(r.standard_normal((nc, Hh, dh)), dtype=f64),
+            torch.tensor(r.standard_normal((nc, Hh, dh)), dtype=f64))
+    c = torch.tensor(r.standard_normal((Tc, Ct)), dtype=f64)
+    cond = O.condition_kv(c, w, Hh)
+    kc, vc = F.linear(c, w["wkvx"]).split(Dq, dim=1)
+    assert torch.equal(cond[0], kc.reshape(Tc, Hh, dh)) and torch.equal(cond[1], vc.reshape(Tc, Hh, dh))
+    got, _, _ = O.layer(X, w, Hh, sctx, None, cond=cond)
+
+    sdpa = lambda q, k, v: F.scaled_dot_product_attention(
+        q.permute(1, 0, 2), k.permute(1, 0, 2), v.permute(1, 0, 2)).permute(1, 0, 2)
+    Y = F.rms_norm(X, (D,), w["g1"], eps=1e-6)
+    q, k, v = (u.reshape(n, Hh, dh) for u in F.linear(Y, w["wqkv"]).split(Dq, dim=1))
+    X1 = X + F.linear(sdpa(q, torch.cat([sctx[0], k]), torch.cat([sctx[1], v])).reshape(n, Dq), w["wo"])
+    qx = F.linear(F.rms_norm(X1, (D,), w["gx"], eps=1e-6), w["wqx"]).reshape(n, Hh, dh)
+    X2 = X1 + F.linear(sdpa(qx, kc.reshape(Tc, Hh, dh), vc.reshape(Tc, Hh, dh)).reshape(n, Dq), w["wox"])
+    ref = X2 + F.linear(F.gelu(F.linear(F.rms_norm(X2, (D,), w["g2"], eps=1e-6), w["w1"])), w["w2"])
+    assert torch.max(torch.abs(got - ref)) < 1e-12
+    # the sub-layer is there: without it the result differs
+    plain, _, _ = O.layer(X, w, Hh, sctx, None)
+    assert torch.max(torch.abs(got - plain)) > 1e-3
+
+
+def test_cross_attention_zero_output_is_the_plain_layer():
+    r = np.random.default_rng(32)
+    w = _cond_weights(r, 32, 32, 20, 48)
+    w["wox"] = torch.zeros_like(w["wox"])
+    X = torch.tensor(r.standard_normal((6, 32)), dtype=f64)
+    cond = O.condition_kv(torch.tensor(r.standard_normal((5, 20)), dtype=f64), w, 2)
+    a, _, _ = O.layer(X, w, 2, None, None, cond=cond)
+    b, _, _ = O.layer(X, w, 2, None, None)
+    assert torch.equal(a, b)
+
+
+def test_single_condition_token_reads_its_value():
+    # one condition token: every query's cross-attention returns that token's
+    # V exactly (softmax over one key), so with the other residual branches
+    # zeroed the layer adds V_c Wox^T to every row
+    r = np.random.default_rng(33)
+    D, Hh, Ct = 32, 2, 20
+    w = _cond_weights(r, D, D, Ct, 48)
+    w["wo"] = torch.zeros_like(w["wo"])
+    w["w2"] = torch.zeros_like(w["w2"])
+    X = torch.tensor(r.standard_normal((6, D)), dtype=f64)
+    c = torch.tensor(r.standard_normal((1, Ct)), dtype=f64)
+    got, _, _ = O.layer(X, w, Hh, None, None, cond=O.condition_kv(c, w, Hh))
+    vc = F.linear(c, w["wkvx"])[:, D:]
+    assert torch.max(torch.abs(got - (X + F.linear(vc, w["wox"])))) < 1e-13
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_joint_sequence_with_condition_equals_cached_path(rope):
+    # The text/state K, V computed once per call (condition_cache) equal the
+    # joint pass's own projections of the condition: the cache rows and the
+    # action v-hat of one uncached joint [video ; action] pass, in which every
+    # row reads the condition through its expert's cross-attention.
+    cfg = _tiny(rope=rope, Tc=4, Ct=10, S=3)
+    inp = inputs.generate(cfg, threads=1)
+    assert inp["text"].shape == (1, 3, 10) and inp["proprio_w"].shape == (10, 3)
+    vw = O.to_torch_expert(inp["video"], f64)
+    aw = O.to_torch_expert(inp["action"], f64)
+    ctx = O.episode_condition(cfg, inp, 0, f64)
+    condv, conda = O.condition_cache(cfg, vw, ctx), O.condition_cache(cfg, aw, ctx)
+    cache, z, frames = O.video_prefill(cfg, vw, inp["hist"][0], inp["hist_valid"][0], inp["eps_v"][0],
+                                       cond=condv)
+    t0 = float(O.schedule(cfg.N, 0.0)[0])
+    a = torch.tensor(inp["eps_a"][0], dtype=f64)
+    v_cached = O.action_velocity(cfg, aw, O.read_layers(cfg, cache, None), a, t0,
+                                 int(cache[0][0].shape[0]), conda)
+    valid_frames = [f for f in range(cfg.Fh) if inp["hist_valid"][0][f]]
+    hist_tok = torch.tensor(inp["hist"][0][valid_frames], dtype=f64).reshape(-1, cfg.Cv)
+    vtok = torch.cat([hist_tok, z])
+    sig_f = float(O.schedule(cfg.V, cfg.sigma_star)[-1])
+    vsig = [0.0] * hist_tok.shape[0] + [sig_f] * z.shape[0]
+    fvalid = list(inp["hist_valid"][0]) + [1] * cfg.Ff
+    v_joint, kv = O.joint_mot_step(cfg, vw, aw, vtok, vsig, frames, fvalid, a, t0, ctx=ctx)
+    assert torch.max(torch.abs(v_joint - v_cached)) < 1e-12
+    for (Kc, Vc), (Kj, Vj) in zip(cache, kv):
+        assert torch.max(torch.abs(Kc - Kj)) < 1e-12
+        assert torch.max(torch.abs(Vc - Vj)) < 1e-12
+    # and the condition matters: the chunk moves when the state changes
+    inp2 = dict(inp, state=inp["state"] + 1.0)
+    assert np.max(np.abs(O.run_chunk(cfg, inp)["actions"] - O.run_chunk(cfg, inp2)["actions"])) > 1e-4
