@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define WAM_ABI_VERSION 3
+#define WAM_ABI_VERSION 4
 #define WAM_MAX_FRAMES 256   /* latent frames per episode (history + future) */
 #define WAM_MAX_BATCH 64     /* episodes per call */
 #define WAM_MAX_FUSE 32      /* fused pairs per wam_fuse_interval_kv call */
@@ -83,7 +83,24 @@ typedef struct {
   int Da;     /* action expert width (0: D); its Wqkv is [3 Hh dh][Da], Wo [Da][Hh dh] */
   int Fma;    /* action expert MLP inner width (0: Fm) */
   int rope;   /* 0: no position embedding (C1-C6); 1: rotary option, below */
+  int Tc;     /* condition tokens per episode (Tc - 1 text + 1 proprio); 0: none */
+  int Ct;     /* condition width (the text encoder's output width), multiple of 64 */
+  int S;      /* robot state dims the proprio encoder reads (0: A) */
 } wam_dims;
+
+/* Text/state condition (Tc > 0).  The language instruction enters as text
+ * tokens of width Ct (the text encoder's output, an input here) and the robot
+ * state as one more token of the same width made by a linear layer (the
+ * proprio encoder), appended after the text ("Fast-WAM 精读" section 四.5).
+ * Video and action tokens read this condition sequence through
+ * cross-attention ("Fast-WAM 精读" section 五, step 3): every layer of both
+ * experts gains, after its self-attention,
+ *   X += Attn(RMSNorm(X; gx) Wqx^T ; K_c, V_c) Wox^T,
+ * with K_c, V_c = ctx Wkx^T, ctx Wvx^T per expert layer.  K_c, V_c depend on
+ * nothing that changes across denoising steps: wam_prefill_condition_kv
+ * computes them once per call (text/state KV reuse, Long-WAM Summary section
+ * 4.2) into a wam_kv per expert, which the calls running that expert's
+ * layers read through wam_expert_w.cond.  No rotary positions there. */
 
 /* Rotary option (rope = 1).  The pages say only that rotary position tables
  * are computed once per inference call and reused across the denoising steps
@@ -104,17 +121,27 @@ typedef struct {
   const float* g2;   /* [D] fp32 */
   const void* w1;    /* [Fm][D] */
   const void* w2;    /* [D][Fm] */
+  /* cross-attention to the condition (read only when Tc > 0, else may be NULL) */
+  const float* gx;   /* [D] fp32 */
+  const void* wqx;   /* [Hh dh][D] */
+  const void* wkvx;  /* [2 Hh dh][Ct]: rows 0..Hh dh-1 = Wkx, the rest Wvx */
+  const void* wox;   /* [D][Hh dh] */
 } wam_layer_w;
 
 /* An expert: X = x W_in^T + emb(sigma); layers; v = RMSNorm(X; g_out) W_out^T.
  * emb(sigma) = [cos(t w_i), sin(t w_i)], t = 1000 sigma, w_i = 10000^(-i/(D/2)).
  * C = Cv for the video expert, A for the action expert. */
+struct wam_kv_s;
 typedef struct {
   const void* w_in;            /* [D][C] */
   const float* g_out;          /* [D] fp32 */
   const void* w_out;           /* [C][D] */
   const wam_layer_w* layers;   /* host array of n_layers */
   int n_layers;
+  /* Tc > 0: this expert's condition K/V for the call (n_layers layers, the
+   * call's B episodes, len[b] == Tc), from wam_prefill_condition_kv; NULL
+   * without a condition */
+  const struct wam_kv_s* cond;
 } wam_expert_w;
 
 /* Per-layer K/V cache of B episodes.
@@ -131,7 +158,7 @@ typedef struct {
  *   16g+8..16g+15 keys 32+8g..32+8g+7.  k_scale, v_scale: device
  *   [n_layers][B][Hh][cap/64] fp32, each a power of two; a value is
  *   E4M3(code) * scale of its tile.  NULL for the other dtypes. */
-typedef struct {
+typedef struct wam_kv_s {
   void* k;
   void* v;
   int n_layers, B, Hh, dh, cap, dtype;
@@ -264,17 +291,41 @@ int wam_fuse_interval_kv(const wam_kv* src, int M, const int32_t* start,
 int wam_quantize_kv_fp8(const wam_kv* src, wam_kv* dst, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * wam_prefill_condition_kv -- the text/state condition of a call: per
+ * episode b the condition sequence ctx_b = [text_b ; state_b Wp^T] (Tc rows of
+ * width Ct; the proprio token rounded once to the model dtype), then for every
+ * layer l of each given expert K_c, V_c = ctx_b Wkx^T, ctx_b Wvx^T written to
+ * rows 0..Tc-1 of that expert's condition cache, len[b] = Tc.
+ *   proprio_w  device [Ct][S] dtype      the proprio encoder (S = dims.S or A)
+ *   text       device [B][Tc-1][Ct] dtype
+ *   state      device [B][S] fp32
+ *   video, action   either may be NULL (that side is not computed); the
+ *              other arguments are the experts' weights (cond is not read)
+ *   cond_video, cond_action  wam_kv of dtype dims.dtype, n_layers == L,
+ *              cap >= Tc; NULL where the matching expert is NULL
+ *   ws         wam_condition_workspace_bytes(d, B)
+ * Errors: WAM_E_SHAPE if Tc == 0 or a cache does not fit.
+ * ------------------------------------------------------------------------- */
+size_t wam_condition_workspace_bytes(const wam_dims* d, int B);
+int wam_prefill_condition_kv(const wam_dims* d, const wam_expert_w* video,
+                             const wam_expert_w* action, const void* proprio_w,
+                             const void* text, const float* state, int B, wam_kv* cond_video,
+                             wam_kv* cond_action, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * wam_action_layer -- one action-expert layer on the chunk, in place
  * (forward_action_with_video_cache for one layer): the B*H action queries of
  * episode b attend over [kv layer kv_layer of episode b ; the chunk's own H
  * keys], or over the chunk alone when kv is NULL (SparseMoT action-only
  * layers, Faster-WAM section 3.2).  No mask among action tokens.
  *   x  device [B][H][D] fp32, updated in place.
+ *   cond, cond_layer  with dims.Tc > 0: the action expert's condition cache
+ *      and the layer of it this layer reads (cross-attention); else NULL.
  * ------------------------------------------------------------------------- */
 size_t wam_action_workspace_bytes(const wam_dims* d, int B, const wam_kv* kv);
 int wam_action_layer(const wam_dims* d, const wam_layer_w* w, float* x,
-                     const wam_kv* kv, int kv_layer, int B,
-                     void* ws, size_t ws_bytes, void* stream);
+                     const wam_kv* kv, int kv_layer, const wam_kv* cond, int cond_layer,
+                     int B, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * wam_flow_euler_step -- x <- x + (sigma_next - sigma) * v, elementwise fp32

@@ -73,8 +73,16 @@ int check_dims(const wam_dims* d) {
   if (d->rope != 0 && d->rope != 1) return fail(WAM_E_ARG, "rope must be 0 or 1");
   if (d->Cv < 1 || d->Cv > 64 || d->A < 1 || d->A > 64)
     return fail(WAM_E_SHAPE, "Cv and A must be in [1, 64]");
+  if (d->Tc < 0 || d->Tc > 4096) return fail(WAM_E_SHAPE, "Tc must be in [0, 4096]");
+  if (d->Tc > 0) {
+    if (d->Ct < 64 || d->Ct > 8192 || d->Ct % 64)
+      return fail(WAM_E_SHAPE, "Ct must be a multiple of 64 in [64, 8192]");
+    if (d->S < 0 || d->S > 64) return fail(WAM_E_SHAPE, "S must be in [0, 64]");
+  }
   return WAM_OK;
 }
+
+inline int state_dims(const wam_dims* d) { return d->S ? d->S : d->A; }
 
 // The action expert's shapes: width Da and MLP width Fma in D and Fm (the
 // attention interface Hh x dh is unchanged).
@@ -98,7 +106,39 @@ int check_expert(const wam_dims* d, const wam_expert_w* e, const char* name) {
     if (!aligned16(w.g1) || !aligned16(w.wqkv) || !aligned16(w.wo) || !aligned16(w.g2) ||
         !aligned16(w.w1) || !aligned16(w.w2))
       return fail(WAM_E_ALIGN, "%s layer %d pointer not 16-byte aligned", name, l);
+    if (d->Tc > 0) {
+      if (!w.gx || !w.wqx || !w.wkvx || !w.wox)
+        return fail(WAM_E_ARG, "%s layer %d has a NULL cross-attention pointer", name, l);
+      if (!aligned16(w.gx) || !aligned16(w.wqx) || !aligned16(w.wkvx) || !aligned16(w.wox))
+        return fail(WAM_E_ALIGN, "%s layer %d cross-attention pointer not 16-byte aligned", name, l);
+    }
   }
+  return WAM_OK;
+}
+
+// A condition cache (wam_prefill_condition_kv's output) that L layers of B
+// episodes of this model can read: Tc rows per episode.
+int check_cond_kv(const wam_dims* d, const wam_kv* c, int B, int L, const char* name) {
+  if (!c || !c->k || !c->v || !c->len) return fail(WAM_E_ARG, "%s condition cache missing", name);
+  if (!aligned16(c->k) || !aligned16(c->v))
+    return fail(WAM_E_ALIGN, "%s condition cache not 16-byte aligned", name);
+  if (c->dtype != d->dtype) return fail(WAM_E_DTYPE, "%s condition cache dtype differs", name);
+  if (c->n_layers != L || c->B != B || c->Hh != d->Hh || c->dh != d->dh)
+    return fail(WAM_E_SHAPE, "%s condition cache shape does not match", name);
+  if (c->cap < d->Tc || c->cap % 64)
+    return fail(WAM_E_SHAPE, "%s condition cache cap %d: need a multiple of 64 >= Tc", name, c->cap);
+  return WAM_OK;
+}
+
+// The expert's condition for a call of B episodes (nothing to check without one).
+int check_cond(const wam_dims* d, const wam_expert_w* e, int B, const char* name) {
+  if (d->Tc == 0) return WAM_OK;
+  int st;
+  if ((st = check_cond_kv(d, e->cond, B, e->n_layers, name))) return st;
+  for (int b = 0; b < B; b++)
+    if (e->cond->len[b] != d->Tc)
+      return fail(WAM_E_SHAPE, "%s condition cache len[%d] = %d, Tc is %d", name, b,
+                  e->cond->len[b], d->Tc);
   return WAM_OK;
 }
 
@@ -193,10 +233,82 @@ struct Layer {
 
 int norm_rows(const Layer& c, int odt, const float* g, void* y, int M);
 int video_resid(const Layer& c, int M, int N, int K, const void* A, const void* W);
+int action_resid(const Layer& c, int M, int N, int K, const void* A, const void* W);
+
+// Condition K/V one layer reads (k == nullptr: no condition).  For a video
+// pass they point at one episode's rows, for the action rows at episode 0 of
+// the layer (the kernels step by cap per episode).
+struct CondRef {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int cap = 0;
+};
+
+CondRef cond_ref(const wam_dims* d, const wam_kv* c, int l, int b) {
+  CondRef r;
+  if (d->Tc == 0 || !c) return r;
+  const size_t es = c->dtype == WAM_F32 ? 4 : 2;
+  const size_t ls = (size_t)c->B * c->Hh * c->cap * c->dh * es;
+  const size_t ep = b > 0 ? (size_t)b * c->Hh * c->cap * c->dh * es : 0;
+  r.k = (const char*)c->k + l * ls + ep;
+  r.v = (const char*)c->v + l * ls + ep;
+  r.cap = c->cap;
+  return r;
+}
+
+// Cross-attention of n video rows (one episode) to its condition:
+// X += Attn(RMSNorm(X; gx) Wqx^T ; K_c, V_c) Wox^T.  Every row sees the Tc
+// condition rows: one frame of the table whose key prefix ends at Tc.
+int video_cross(const Layer& c, const wam_layer_w& w, int n, const CondRef& cr) {
+  const wam_dims* d = c.d;
+  const int dt = d->dtype, D = d->D, Dq = d->Hh * d->dh;
+  Bufs& b = *c.b;
+  int st;
+  if ((st = norm_rows(c, dt, w.gx, b.Y, n))) return st;
+  EpiArgs e{};
+  e.q = b.Q;
+  e.D = Dq;
+  e.dh = d->dh;
+  e.rpg = n;
+  e.q_hs = (long long)n * d->dh;
+  e.q_scale = qkv_q_scale(d);
+  HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, Dq, D, b.Y, D, w.wqx, D, e));
+  FrameTab ct;
+  ct.n = 1;
+  ct.P = 1 << 30;
+  ct.kend[0] = d->Tc;
+  HIPCK(attn_prefill(c.s, dt, d->Hh, d->dh, n, 0, ct, b.Q, cr.k, cr.v, cr.cap, b.O, b.pattn,
+                     b.pattn_bytes));
+  return video_resid(c, n, D, Dq, b.O, w.wox);
+}
+
+// The same for the B*H action rows (c.d is the action view: D = its width).
+int action_cross(const Layer& c, const wam_layer_w& w, int B, const CondRef& cr) {
+  const wam_dims* d = c.d;
+  const int dt = d->dtype, D = d->D, Dq = d->Hh * d->dh, H = d->H, M = B * H;
+  Bufs& b = *c.b;
+  int st;
+  if ((st = norm_rows(c, dt, w.gx, b.Y, M))) return st;
+  EpiArgs e{};
+  e.q = b.Q;
+  e.D = Dq;
+  e.dh = d->dh;
+  e.rpg = H;
+  e.q_gs = (long long)d->Hh * H * d->dh;
+  e.q_hs = (long long)H * d->dh;
+  e.q_scale = qkv_q_scale(d);
+  HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, M, Dq, D, b.Y, D, w.wqx, D, e));
+  ActLens cl{};
+  for (int i = 0; i < B; i++) cl.len[i] = d->Tc;
+  // a few condition tiles per (episode, head): one split
+  HIPCK(attn_action(c.s, dt, B, d->Hh, H, d->dh, b.Q, nullptr, nullptr, 0, cr.k, cr.v, cr.cap, cl,
+                    b.O, 1, b.attn, b.attn_bytes));
+  return action_resid(c, M, D, Dq, b.O, w.wox);
+}
 
 // One video layer for rows row0..row0+n-1 of episode cache layer (kl, vl).
 int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const FrameTab& tab,
-                void* kl, void* vl, int cap, bool kv_only) {
+                void* kl, void* vl, int cap, bool kv_only, const CondRef& cr = CondRef()) {
   const wam_dims* d = c.d;
   const int dt = d->dtype, D = d->D;
   Bufs& b = *c.b;
@@ -233,6 +345,7 @@ int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const Fra
     HIPCK(rope_qk(c.s, dt, b.Q, 0, e.q_hs, krows, 0, e.k_hs, 1, n, d->Hh, d->dh, rb));
   HIPCK(attn_prefill(c.s, dt, d->Hh, d->dh, n, row0, tab, b.Q, kl, vl, cap, b.O, b.pattn, b.pattn_bytes));
   if ((st = video_resid(c, n, D, D, b.O, w.wo))) return st;
+  if (cr.k && (st = video_cross(c, w, n, cr))) return st;
   if ((st = norm_rows(c, dt, w.g2, b.Y, n))) return st;
   EpiArgs gl{};
   gl.out = b.Hb;
@@ -296,7 +409,7 @@ int norm_rows(const Layer& c, int odt, const float* g, void* y, int M) {
 // episodes (or NULL).  May leave the W2 product pending (b.pend).
 int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, const void* vc,
                  int cap, const ActLens& lens, const float* ksc = nullptr,
-                 const float* vsc = nullptr) {
+                 const float* vsc = nullptr, const CondRef& cr = CondRef()) {
   const wam_dims* d = c.d;  // the action view: D = the action width
   const int dt = d->dtype, D = d->D, Dq = d->Hh * d->dh, H = d->H, M = B * H;
   Bufs& b = *c.b;
@@ -325,6 +438,7 @@ int action_layer(const Layer& c, const wam_layer_w& w, int B, const void* kc, co
   HIPCK(attn_action(c.s, dt, B, d->Hh, H, d->dh, b.Q, b.Ka, b.Va, H, kc, vc, cap, lens, b.O, 0, b.attn,
                     b.attn_bytes, ksc, vsc));
   if ((st = action_resid(c, M, D, Dq, b.O, w.wo))) return st;
+  if (cr.k && (st = action_cross(c, w, B, cr))) return st;
   if ((st = norm_rows(c, dt, w.g2, b.Y, M))) return st;
   EpiArgs gl{};
   gl.out = b.Hb;
@@ -490,16 +604,16 @@ int build_tables(const int32_t* frame_block, const uint8_t* hist_valid, int B, i
 // History rows [row0, row0 + n) of one episode at sigma = 0 (emb0), gathered
 // from `hist` by `map`, through the L layers; their K/V go to the cache rows.
 // The last layer computes K/V only.
-int history_rows(const Layer& c, const wam_expert_w* video, const void* hist, const RowMap& map,
-                 const float* emb0, const FrameTab& tab, int row0, int n, char* k, char* v,
-                 size_t ls, int cap) {
+int history_rows(const Layer& c, const wam_expert_w* video, int ep, const void* hist,
+                 const RowMap& map, const float* emb0, const FrameTab& tab, int row0, int n,
+                 char* k, char* v, size_t ls, int cap) {
   const wam_dims* d = c.d;
   Bufs& b = *c.b;
   int st;
   HIPCK(embed(c.s, d->dtype, d->dtype, hist, map, video->w_in, emb0, b.X, n, d->D, d->Cv));
   for (int l = 0; l < d->L; l++)
     if ((st = video_layer(c, video->layers[l], n, row0, tab, k + l * ls, v + l * ls, cap,
-                          l == d->L - 1)))
+                          l == d->L - 1, cond_ref(d, video->cond, l, ep))))
       return st;
   return WAM_OK;
 }
@@ -508,8 +622,8 @@ int history_rows(const Layer& c, const wam_expert_w* video, const void* hist, co
 // video_steps Euler steps of z over sig (embeddings emb_steps[k]) attending
 // to [history ; future], then one caching pass at emb_last; z (fp32) starts
 // as fut_noise_b (dtype).  video_steps == 0: the caching pass of the noise.
-int future_rows(const Layer& c, const wam_expert_w* video, const void* fut_noise_b, float* z,
-                const std::vector<float>& sig, int video_steps, const float* emb_steps,
+int future_rows(const Layer& c, const wam_expert_w* video, int ep, const void* fut_noise_b,
+                float* z, const std::vector<float>& sig, int video_steps, const float* emb_steps,
                 const float* emb_last, const FrameTab& tab, int Th, int Tf, char* k, char* v,
                 size_t ls, int cap) {
   const wam_dims* d = c.d;
@@ -525,7 +639,8 @@ int future_rows(const Layer& c, const wam_expert_w* video, const void* fut_noise
     HIPCK(embed(c.s, WAM_F32, dt, z, zmap, video->w_in, emb_steps + (size_t)s * D, b.X, Tf, D,
                 d->Cv));
     for (int l = 0; l < d->L; l++)
-      if ((st = video_layer(c, video->layers[l], Tf, Th, tab, k + l * ls, v + l * ls, cap, false)))
+      if ((st = video_layer(c, video->layers[l], Tf, Th, tab, k + l * ls, v + l * ls, cap, false,
+                            cond_ref(d, video->cond, l, ep))))
         return st;
     if ((st = flush_pending(c, video->g_out, Tf))) return st;  // X whole for the head
     HIPCK(step_boundary(c.s, dt, b.X, video->g_out, video->w_out, z, sig[s + 1] - sig[s], nullptr,
@@ -534,7 +649,7 @@ int future_rows(const Layer& c, const wam_expert_w* video, const void* fut_noise
   HIPCK(embed(c.s, WAM_F32, dt, z, zmap, video->w_in, emb_last, b.X, Tf, D, d->Cv));
   for (int l = 0; l < d->L; l++)
     if ((st = video_layer(c, video->layers[l], Tf, Th, tab, k + l * ls, v + l * ls, cap,
-                          l == d->L - 1)))
+                          l == d->L - 1, cond_ref(d, video->cond, l, ep))))
       return st;
   return WAM_OK;
 }
@@ -566,7 +681,7 @@ int check_video_call(const wam_dims* d, const wam_expert_w* video, int B, int Fh
   if (!cache) return fail(WAM_E_ARG, "cache is NULL");
   if ((st = check_kv(d, cache, B, "cache"))) return st;
   if (cache->n_layers != d->L) return fail(WAM_E_SHAPE, "cache must hold L layers");
-  return WAM_OK;
+  return check_cond(d, video, B, "video");
 }
 
 int check_future_args(int video_steps, double sigma_star, double shift) {
@@ -639,14 +754,14 @@ int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video, const 
                   d->Cv));
       for (int l = 0; l < d->L; l++)
         if ((st = video_layer(c, video->layers[l], Th + Tf, 0, t.tab[b], kb + l * ls, vb + l * ls,
-                              cache->cap, l == d->L - 1)))
+                              cache->cap, l == d->L - 1, cond_ref(d, video->cond, l, b))))
           return st;
     } else {
-      if (Th > 0 && (st = history_rows(c, video, hist, t.hmap[b], emb_hist, t.tab[b], 0, Th, kb, vb,
-                                        ls, cache->cap)))
+      if (Th > 0 && (st = history_rows(c, video, b, hist, t.hmap[b], emb_hist, t.tab[b], 0, Th, kb,
+                                        vb, ls, cache->cap)))
         return st;
-      if (Ff > 0 && (st = future_rows(c, video, fut_b, z, sig, video_steps, bufs.emb + D, emb_last,
-                                       t.tab[b], Th, Tf, kb, vb, ls, cache->cap)))
+      if (Ff > 0 && (st = future_rows(c, video, b, fut_b, z, sig, video_steps, bufs.emb + D,
+                                       emb_last, t.tab[b], Th, Tf, kb, vb, ls, cache->cap)))
         return st;
     }
     if (Ff > 0 && fut_latents_out)
@@ -711,7 +826,7 @@ int wam_extend_history_cache(const wam_dims* d, const wam_expert_w* video, const
   for (int b = 0; b < B; b++) {
     const int rows = (n_all[b] - n_old[b]) * P;
     if (rows > 0 &&
-        (st = history_rows(c, video, hist_new, map[b], bufs.emb, tab[b], n_old[b] * P, rows,
+        (st = history_rows(c, video, b, hist_new, map[b], bufs.emb, tab[b], n_old[b] * P, rows,
                            (char*)cache->k + b * ep, (char*)cache->v + b * ep, ls, cache->cap)))
       return st;
     cache->len[b] = n_all[b] * P;
@@ -755,7 +870,7 @@ int wam_prefill_future(const wam_dims* d, const wam_expert_w* video, const uint8
   const int Tf = Ff * P;
   for (int b = 0; b < B; b++) {
     const void* fut_b = (const char*)fut_noise + (size_t)b * Tf * d->Cv * esz(dt);
-    if ((st = future_rows(c, video, fut_b, z, sig, video_steps, bufs.emb + D,
+    if ((st = future_rows(c, video, b, fut_b, z, sig, video_steps, bufs.emb + D,
                           bufs.emb + (size_t)(embs.size() - 1) * D, t.tab[b], t.nh[b] * P, Tf,
                           (char*)cache->k + b * ep, (char*)cache->v + b * ep, ls, cache->cap)))
       return st;
@@ -867,7 +982,8 @@ static int check_lens(const wam_kv* kv, int B, ActLens* lens) {
 }
 
 int wam_action_layer(const wam_dims* d, const wam_layer_w* w, float* x, const wam_kv* kv,
-                     int kv_layer, int B, void* ws, size_t ws_bytes, void* stream) {
+                     int kv_layer, const wam_kv* cond, int cond_layer, int B, void* ws,
+                     size_t ws_bytes, void* stream) {
   int st;
   if ((st = check_dims(d))) return st;
   const wam_dims* d_in = d;
@@ -878,6 +994,15 @@ int wam_action_layer(const wam_dims* d, const wam_layer_w* w, float* x, const wa
     return fail(WAM_E_ARG, "layer has a NULL pointer");
   if (!aligned16(x)) return fail(WAM_E_ALIGN, "x not 16-byte aligned");
   if (B < 1 || B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "bad B");
+  if (d->Tc > 0) {
+    if (!w->gx || !w->wqx || !w->wkvx || !w->wox)
+      return fail(WAM_E_ARG, "layer has a NULL cross-attention pointer");
+    if (!cond) return fail(WAM_E_ARG, "Tc > 0 needs the condition cache");
+    if ((st = check_cond_kv(d, cond, B, cond->n_layers, "action"))) return st;
+    if (cond_layer < 0 || cond_layer >= cond->n_layers) return fail(WAM_E_ARG, "cond_layer out of range");
+    for (int i = 0; i < B; i++)
+      if (cond->len[i] != d->Tc) return fail(WAM_E_SHAPE, "condition cache len[%d] != Tc", i);
+  }
   ActLens lens{};
   if (kv) {
     if ((st = check_kv(d, kv, B, "kv", true))) return st;
@@ -897,7 +1022,8 @@ int wam_action_layer(const wam_dims* d, const wam_layer_w* w, float* x, const wa
   const void* vc = kv ? (const char*)kv->v + kv_layer * layer_stride(kv) : nullptr;
   if ((st = action_layer(c, *w, B, kc, vc, kv ? kv->cap : 0, lens,
                          kv ? layer_scales(kv, kv->k_scale, kv_layer) : nullptr,
-                         kv ? layer_scales(kv, kv->v_scale, kv_layer) : nullptr)))
+                         kv ? layer_scales(kv, kv->v_scale, kv_layer) : nullptr,
+                         cond_ref(d, cond, cond_layer, 0))))
     return st;
   if ((st = flush_pending(c, w->g1, B * d->H))) return st;
   HIPCK(hipMemcpyAsync(x, b.X, bytes, hipMemcpyDeviceToDevice, s));
@@ -924,6 +1050,7 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
   d = &dav;  // the action expert's shapes from here on
   if ((st = check_expert(d, action, "action"))) return st;
   if (!read_map || !eps || !actions_out) return fail(WAM_E_ARG, "NULL pointer");
+  if (B >= 1 && B <= WAM_MAX_BATCH && (st = check_cond(d, action, B, "action"))) return st;
   if (!aligned16(eps) || !aligned16(actions_out) || (vhat_out && !aligned16(vhat_out)))
     return fail(WAM_E_ALIGN, "pointer not 16-byte aligned");
   if (B < 1 || B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "bad B");
@@ -964,7 +1091,8 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
       const void* vc = r >= 0 ? (const char*)kv->v + r * ls : nullptr;
       if ((st = action_layer(c, action->layers[l], B, kc, vc, r >= 0 ? kv->cap : 0, lens,
                              r >= 0 ? layer_scales(kv, kv->k_scale, r) : nullptr,
-                             r >= 0 ? layer_scales(kv, kv->v_scale, r) : nullptr)))
+                             r >= 0 ? layer_scales(kv, kv->v_scale, r) : nullptr,
+                             cond_ref(d, action->cond, l, 0))))
         return st;
     }
     const bool last = (k + 1 == N);
@@ -1000,6 +1128,7 @@ int wam_codenoise_chunk(const wam_dims* d, const wam_expert_w* video, const wam_
   if ((st = check_expert(d, video, "video"))) return st;
   if ((st = check_expert(d, action, "action"))) return st;
   if (B < 1 || B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "B must be in [1, %d]", WAM_MAX_BATCH);
+  if ((st = check_cond(d, video, B, "video")) || (st = check_cond(d, action, B, "action"))) return st;
   if (Fh < 0 || Ff < 1 || Fh + Ff > WAM_MAX_FRAMES)
     return fail(WAM_E_SHAPE, "co-denoising needs Ff >= 1 and Fh + Ff <= %d", WAM_MAX_FRAMES);
   if (!fut_noise || !eps || !actions_out || !fut_latents_out || !frame_block)
@@ -1077,7 +1206,8 @@ int wam_codenoise_chunk(const wam_dims* d, const wam_expert_w* video, const wam_
       for (int l = 0; l < d->L; l++) {
         char* kl = (char*)cache->k + l * ls + b * ep;
         char* vl = (char*)cache->v + l * ls + b * ep;
-        if ((st = video_layer(cv, video->layers[l], Tf, Th, tabs[b], kl, vl, cache->cap, false)))
+        if ((st = video_layer(cv, video->layers[l], Tf, Th, tabs[b], kl, vl, cache->cap, false,
+                              cond_ref(d, video->cond, l, b))))
           return st;
       }
       if ((st = flush_pending(cv, video->g_out, Tf))) return st;
@@ -1088,7 +1218,9 @@ int wam_codenoise_chunk(const wam_dims* d, const wam_expert_w* video, const wam_
     for (int l = 0; l < d->L; l++) {
       const void* kc = (const char*)cache->k + l * ls;
       const void* vc = (const char*)cache->v + l * ls;
-      if ((st = action_layer(ca, action->layers[l], B, kc, vc, cache->cap, lens))) return st;
+      if ((st = action_layer(ca, action->layers[l], B, kc, vc, cache->cap, lens, nullptr, nullptr,
+                             cond_ref(d, action->cond, l, 0))))
+        return st;
     }
     const bool last = (k + 1 == N);
     if ((st = flush_pending(ca, action->g_out, M))) return st;
@@ -1098,6 +1230,71 @@ int wam_codenoise_chunk(const wam_dims* d, const wam_expert_w* video, const wam_
                         last ? nullptr : ab.emb + (size_t)(k + 1) * da.D, M, da.D, d->A, true));
   }
   for (int b = 0; b < B; b++) cache->len[b] = lens.len[b];
+  return WAM_OK;
+}
+
+size_t wam_condition_workspace_bytes(const wam_dims* d, int B) {
+  if (check_dims(d) || B < 1 || B > WAM_MAX_BATCH || d->Tc < 1) return 0;
+  return (size_t)B * d->Tc * d->Ct * esz(d->dtype) + 256;
+}
+
+int wam_prefill_condition_kv(const wam_dims* d, const wam_expert_w* video, const wam_expert_w* action,
+                             const void* proprio_w, const void* text, const float* state, int B,
+                             wam_kv* cond_video, wam_kv* cond_action, void* ws, size_t ws_bytes,
+                             void* stream) {
+  int st;
+  if ((st = check_dims(d))) return st;
+  if (d->Tc < 1) return fail(WAM_E_SHAPE, "no condition (Tc = 0)");
+  if (B < 1 || B > WAM_MAX_BATCH) return fail(WAM_E_SHAPE, "bad B");
+  if (!video && !action) return fail(WAM_E_ARG, "no expert given");
+  if (!proprio_w || !state || (d->Tc > 1 && !text)) return fail(WAM_E_ARG, "NULL pointer");
+  if (!aligned16(proprio_w) || !aligned16(state) || (text && !aligned16(text)))
+    return fail(WAM_E_ALIGN, "pointer not 16-byte aligned");
+  const wam_dims dav = action_view(d);
+  if (video) {
+    if ((st = check_expert(d, video, "video"))) return st;
+    if ((st = check_cond_kv(d, cond_video, B, video->n_layers, "video"))) return st;
+  }
+  if (action) {
+    if ((st = check_expert(&dav, action, "action"))) return st;
+    if ((st = check_cond_kv(d, cond_action, B, action->n_layers, "action"))) return st;
+  }
+  if (!ws || !aligned16(ws) || ws_bytes < wam_condition_workspace_bytes(d, B))
+    return fail(WAM_E_WORKSPACE, "workspace missing or too small");
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = d->dtype, Tc = d->Tc, Ct = d->Ct, S = state_dims(d), Dq = d->Hh * d->dh;
+  const size_t es = esz(dt);
+  char* ctx = (char*)ws;  // [B][Tc][Ct]: text rows, then the proprio token
+  if (Tc > 1)
+    HIPCK(hipMemcpy2DAsync(ctx, (size_t)Tc * Ct * es, text, (size_t)(Tc - 1) * Ct * es,
+                           (size_t)(Tc - 1) * Ct * es, B, hipMemcpyDeviceToDevice, s));
+  EpiArgs pe{};
+  pe.out = ctx + (size_t)(Tc - 1) * Ct * es;
+  pe.ldo = Tc * Ct;
+  HIPCK(gemm(s, WAM_F32, dt, dt, EPI_STORE, B, Ct, S, state, S, proprio_w, S, pe));
+  const wam_expert_w* ex[2] = {video, action};
+  wam_kv* cc[2] = {cond_video, cond_action};
+  for (int i = 0; i < 2; i++) {
+    if (!ex[i]) continue;
+    wam_kv* c = cc[i];
+    const size_t ls = layer_stride(c);
+    for (int l = 0; l < ex[i]->n_layers; l++) {
+      EpiArgs e{};
+      e.k = (char*)c->k + l * ls;
+      e.v = (char*)c->v + l * ls;
+      e.D = Dq;
+      e.dh = d->dh;
+      e.rpg = Tc;
+      e.n_begin = Dq;  // the K and V parts of [Q | K | V]
+      e.q_scale = 1.0f;
+      e.k_gs = e.v_gs = (long long)d->Hh * c->cap * d->dh;
+      e.k_hs = (long long)c->cap * d->dh;
+      e.v_hs = (long long)d->dh * c->cap;
+      e.v_ld = c->cap;
+      HIPCK(gemm(s, dt, dt, dt, EPI_QKV, B * Tc, 2 * Dq, Ct, ctx, Ct, ex[i]->layers[l].wkvx, Ct, e));
+    }
+    for (int b = 0; b < B; b++) c->len[b] = Tc;
+  }
   return WAM_OK;
 }
 

@@ -21,8 +21,8 @@ def upload_expert(w: dict, cfg: WamConfig, device="cuda") -> wam.DeviceExpert:
     import torch
     mat = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device).to(_tdt(cfg)).contiguous()
     vec = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
-    layers = [{"g1": vec(l["g1"]), "wqkv": mat(l["wqkv"]), "wo": mat(l["wo"]), "g2": vec(l["g2"]),
-               "w1": mat(l["w1"]), "w2": mat(l["w2"])} for l in w["layers"]]
+    gains = ("g1", "g2", "gx")
+    layers = [{k: (vec(a) if k in gains else mat(a)) for k, a in l.items()} for l in w["layers"]]
     return wam.DeviceExpert(mat(w["w_in"]), vec(w["g_out"]), mat(w["w_out"]), layers)
 
 
@@ -40,7 +40,7 @@ class DeviceChunk:
         self.cfg = cfg
         self.dt = wam.WAM_BF16 if cfg.dtype == "bf16" else wam.WAM_F32
         self.dims = wam.dims(cfg.L, cfg.D, cfg.Hh, cfg.dh, cfg.Fm, cfg.Cv, cfg.A, cfg.H, cfg.P, self.dt,
-                             cfg.Da, cfg.Fma, int(cfg.rope))
+                             cfg.Da, cfg.Fma, int(cfg.rope), cfg.Tc, cfg.Ct, cfg.S)
         tdt = _tdt(cfg)
         self.video = upload_expert(inp["video"], cfg, device)
         self.action = upload_expert(inp["action"], cfg, device)
@@ -58,6 +58,18 @@ class DeviceChunk:
             if cfg.dtype != "bf16" or cfg.joint:
                 raise wam.WamError("the E4M3 cache option is for bf16 IDM / Faster-WAM chunks")
             self.kv8 = wam.DeviceKV(cfg.n_kv, cfg.B, cfg.Hh, cfg.dh, cap, wam.WAM_FP8, device)
+        self.cond_v = self.cond_a = None
+        if cfg.Tc > 0:
+            # the text/state condition: inputs, and one K/V cache per expert
+            self.text = torch.from_numpy(inp["text"]).to(device).to(tdt).contiguous()
+            self.state = torch.from_numpy(inp["state"]).to(device).contiguous()
+            self.proprio_w = torch.from_numpy(inp["proprio_w"]).to(device).to(tdt).contiguous()
+            ccap = (cfg.Tc + 63) // 64 * 64
+            self.cond_v = wam.DeviceKV(cfg.L, cfg.B, cfg.Hh, cfg.dh, ccap, self.dt, device)
+            self.cond_a = wam.DeviceKV(cfg.L, cfg.B, cfg.Hh, cfg.dh, ccap, self.dt, device)
+            self.video.set_cond(self.cond_v)
+            self.action.set_cond(self.cond_a)
+            self.ws_cond = wam.workspace(wam.condition_workspace_bytes(self.dims, cfg.B), device)
         self.z = torch.zeros((cfg.B, cfg.Ff, cfg.P, cfg.Cv), dtype=torch.float32, device=device)
         self.actions = torch.zeros((cfg.B, cfg.H, cfg.A), dtype=torch.float32, device=device)
         self.vhat = torch.zeros((cfg.N, cfg.B, cfg.H, cfg.A), dtype=torch.float32, device=device)
@@ -80,8 +92,16 @@ class DeviceChunk:
             return self.kv8
         return self.fused if self.fused is not None else self.cache
 
+    def condition(self, stream=None):
+        """The condition K/V of both experts, once per call (no-op without one)."""
+        c = self.cfg
+        if c.Tc > 0:
+            wam.prefill_condition_kv(self.dims, self.video, self.action, self.proprio_w, self.text,
+                                     self.state, c.B, self.cond_v, self.cond_a, self.ws_cond, stream)
+
     def prefill(self, stream=None):
         c = self.cfg
+        self.condition(stream)
         if c.joint:
             if c.Fh == 0 or not self.hist_valid.any():
                 self.cache.len[:] = 0   # no observed history: the joint steps see the future alone
@@ -124,6 +144,7 @@ class DeviceChunk:
         ``prefill`` of them, or earlier decisions)."""
         c = self.cfg
         old = c.Fh - new_frames
+        self.condition(stream)   # the state changes at every decision
         self.cache.len[:] = self.hist_valid[:, :old].sum(axis=1) * c.P
         wam.extend_history_cache(self.dims, self.video, self.hist[:, old:].contiguous(), self.hist_valid,
                                  c.B, old, new_frames, c.frame_block[:c.Fh], self.cache, self.ws_extend,
@@ -142,6 +163,7 @@ class DeviceChunk:
         old = c.Fh - new_frames
         self.ws_extend = wam.workspace(wam.prefill_workspace_bytes(self.dims, c.B, new_frames, 0))
         self.ws_future = wam.workspace(wam.prefill_workspace_bytes(self.dims, c.B, 0, c.Ff))
+        self.condition(stream)
         wam.prefill_video_cache(self.dims, self.video, self.hist[:, :old].contiguous(),
                                 self.hist_valid[:, :old], c.B, old, None, 0, c.frame_block[:old], 0,
                                 c.sigma_star, c.shift, self.cache, None, self.ws_prefill, stream)

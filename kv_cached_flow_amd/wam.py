@@ -30,22 +30,26 @@ class WamError(RuntimeError):
 
 class WamDims(C.Structure):
     _fields_ = [(n, C.c_int) for n in ("L", "D", "Hh", "dh", "Fm", "Cv", "A", "H", "P", "dtype", "Da",
-                                        "Fma", "rope")]
+                                        "Fma", "rope", "Tc", "Ct", "S")]
+
+
+LAYER_FIELDS = ("g1", "wqkv", "wo", "g2", "w1", "w2", "gx", "wqx", "wkvx", "wox")
 
 
 class WamLayerW(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in ("g1", "wqkv", "wo", "g2", "w1", "w2")]
-
-
-class WamExpertW(C.Structure):
-    _fields_ = [("w_in", C.c_void_p), ("g_out", C.c_void_p), ("w_out", C.c_void_p),
-                ("layers", C.POINTER(WamLayerW)), ("n_layers", C.c_int)]
+    _fields_ = [(n, C.c_void_p) for n in LAYER_FIELDS]
 
 
 class WamKV(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("n_layers", C.c_int), ("B", C.c_int),
                 ("Hh", C.c_int), ("dh", C.c_int), ("cap", C.c_int), ("dtype", C.c_int),
                 ("len", C.POINTER(C.c_int32)), ("k_scale", C.c_void_p), ("v_scale", C.c_void_p)]
+
+
+class WamExpertW(C.Structure):
+    _fields_ = [("w_in", C.c_void_p), ("g_out", C.c_void_p), ("w_out", C.c_void_p),
+                ("layers", C.POINTER(WamLayerW)), ("n_layers", C.c_int),
+                ("cond", C.POINTER(WamKV))]
 
 
 class WamKernelStat(C.Structure):
@@ -78,8 +82,13 @@ _EXPORTS = {
                                        C.c_int, C.POINTER(WamKV), C.c_void_p]),
     "wam_action_workspace_bytes": (C.c_size_t, [C.POINTER(WamDims), C.c_int, C.POINTER(WamKV)]),
     "wam_action_layer": (C.c_int, [C.POINTER(WamDims), C.POINTER(WamLayerW), C.c_void_p,
-                                   C.POINTER(WamKV), C.c_int, C.c_int, C.c_void_p, C.c_size_t,
-                                   C.c_void_p]),
+                                   C.POINTER(WamKV), C.c_int, C.POINTER(WamKV), C.c_int, C.c_int,
+                                   C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wam_condition_workspace_bytes": (C.c_size_t, [C.POINTER(WamDims), C.c_int]),
+    "wam_prefill_condition_kv": (C.c_int, [C.POINTER(WamDims), C.POINTER(WamExpertW),
+                                           C.POINTER(WamExpertW), C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_int, C.POINTER(WamKV), C.POINTER(WamKV), C.c_void_p,
+                                           C.c_size_t, C.c_void_p]),
     "wam_flow_euler_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_float, C.c_float,
                                       C.c_void_p]),
     "wam_denoise_workspace_bytes": (C.c_size_t, [C.POINTER(WamDims), C.c_int, C.POINTER(WamKV)]),
@@ -171,23 +180,30 @@ def frame_table(frame_block: Sequence[int], valid: Optional[Sequence[int]], Fh: 
 
 
 # ------------------------------------------------------------------ device structs
-def dims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype, Da=0, Fma=0, rope=0) -> WamDims:
+def dims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype, Da=0, Fma=0, rope=0, Tc=0, Ct=0, S=0) -> WamDims:
     """Shapes of a call; Da / Fma: the action expert's width and MLP width (0: D / Fm);
-    rope: 1 for the rotary position option."""
-    return WamDims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype, Da, Fma, rope)
+    rope: 1 for the rotary position option; Tc / Ct / S: the text/state condition
+    (tokens, width, robot-state dims; Tc = 0: none)."""
+    return WamDims(L, D, Hh, dh, Fm, Cv, A, H, P, dtype, Da, Fma, rope, Tc, Ct, S)
 
 
 class DeviceExpert:
-    """An expert's weights as device tensors plus the C struct pointing at them."""
+    """An expert's weights as device tensors plus the C struct pointing at them.
+    ``set_cond`` points the struct at the expert's condition cache of a call."""
 
     def __init__(self, w_in, g_out, w_out, layers: List[dict]):
         self.w_in, self.g_out, self.w_out, self.layers = w_in, g_out, w_out, layers
         n = len(layers)
         self._larr = (WamLayerW * n)()
         for i, lw in enumerate(layers):
-            self._larr[i] = WamLayerW(*[lw[k].data_ptr() for k in ("g1", "wqkv", "wo", "g2", "w1", "w2")])
+            self._larr[i] = WamLayerW(*[lw[k].data_ptr() if k in lw else None for k in LAYER_FIELDS])
         self.c = WamExpertW(w_in.data_ptr(), g_out.data_ptr(), w_out.data_ptr(),
-                            C.cast(self._larr, C.POINTER(WamLayerW)), n)
+                            C.cast(self._larr, C.POINTER(WamLayerW)), n, None)
+        self.cond = None
+
+    def set_cond(self, kv: Optional["DeviceKV"]):
+        self.cond = kv
+        self.c.cond = C.pointer(kv.c) if kv is not None else None
 
     def layer_struct(self, l: int) -> WamLayerW:
         return self._larr[l]
@@ -293,13 +309,31 @@ def action_workspace_bytes(d: WamDims, B: int, kv: Optional[DeviceKV]) -> int:
 
 
 def action_layer(d: WamDims, expert: DeviceExpert, l: int, x, kv: Optional[DeviceKV], kv_layer: int,
-                 B: int, ws=None, stream=None):
+                 B: int, ws=None, stream=None, cond: Optional[DeviceKV] = None, cond_layer: int = 0):
     if ws is None:
         ws = workspace(action_workspace_bytes(d, B, kv))
     lw = expert.layer_struct(l)
     _check(lib().wam_action_layer(C.byref(d), C.byref(lw), _ptr(x),
-                                  C.byref(kv.c) if kv is not None else None, kv_layer, B, _ptr(ws),
-                                  ws.numel(), _stream(stream)), "wam_action_layer")
+                                  C.byref(kv.c) if kv is not None else None, kv_layer,
+                                  C.byref(cond.c) if cond is not None else None, cond_layer, B,
+                                  _ptr(ws), ws.numel(), _stream(stream)), "wam_action_layer")
+
+
+def condition_workspace_bytes(d: WamDims, B: int) -> int:
+    return lib().wam_condition_workspace_bytes(C.byref(d), B)
+
+
+def prefill_condition_kv(d: WamDims, video: Optional[DeviceExpert], action: Optional[DeviceExpert],
+                         proprio_w, text, state, B: int, cond_video: Optional[DeviceKV],
+                         cond_action: Optional[DeviceKV], ws=None, stream=None):
+    if ws is None:
+        ws = workspace(condition_workspace_bytes(d, B))
+    _check(lib().wam_prefill_condition_kv(
+        C.byref(d), C.byref(video.c) if video is not None else None,
+        C.byref(action.c) if action is not None else None, _ptr(proprio_w), _ptr(text), _ptr(state), B,
+        C.byref(cond_video.c) if cond_video is not None else None,
+        C.byref(cond_action.c) if cond_action is not None else None, _ptr(ws), ws.numel(),
+        _stream(stream)), "wam_prefill_condition_kv")
 
 
 def flow_euler_step(x, v, sigma: float, sigma_next: float, stream=None):

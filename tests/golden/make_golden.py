@@ -3,9 +3,10 @@ CPU oracle (and nothing else) on the seeded inputs.
 
     python tests/golden/make_golden.py C1 C2 C3 C4 C5 C6 C1+fp8 C1+sharp C6+fp8
 
-A name may carry options after "+": ``fp8`` (the E4M3 cache option) and
+A name may carry options after "+": ``fp8`` (the E4M3 cache option),
 ``sharp`` (the diagnostic variant with Wq, Wk ~ N(0, 0.06^2): peaked
-attention, score std about 3.7 at width 1024); the file is then
+attention, score std about 3.7 at width 1024) and ``cond`` (the text/state
+condition of ``configs.CONDITION``); the file is then
 ``<config>_<option>.json``.
 
 Each ``<name>.json`` holds the input fingerprint, the final action chunk of
@@ -55,6 +56,8 @@ def main(names):
                 kw["kv_fp8"] = True
             elif o == "sharp":
                 kw["qk_std"] = 0.06
+            elif o == "cond":
+                kw.update(configs.CONDITION)
             else:
                 raise SystemExit(f"unknown option {o}")
         cfg = configs.get(base, **kw)
@@ -88,6 +91,7 @@ def main(names):
             "config": name,
             "kv_fp8": cfg.kv_fp8,
             "qk_std": cfg.qk_std,
+            "Tc": cfg.Tc,
             "seed": cfg.seed,
             "fingerprint": inputs.fingerprint(inp),
             "source": ("oracle/wam_oracle.py " + ("run_codenoise" if cfg.joint else "run_chunk")

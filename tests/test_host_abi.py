@@ -23,11 +23,11 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = wam.lib()
     names = header_functions()
-    assert len(names) == 26
+    assert len(names) == 28
     for n in names:
         assert hasattr(L, n), n
     assert sorted(wam.exported_names()) == names
-    assert wam.abi_version() == 3
+    assert wam.abi_version() == 4
 
 
 def test_status_strings():
@@ -88,9 +88,11 @@ def good_dims(**kw):
 
 
 class FakeExpert:
-    def __init__(self, L, ptr=FAKE):
-        self.larr = (wam.WamLayerW * L)(*[wam.WamLayerW(*([ptr] * 6)) for _ in range(L)])
-        self.c = wam.WamExpertW(ptr, ptr, ptr, C.cast(self.larr, C.POINTER(wam.WamLayerW)), L)
+    def __init__(self, L, ptr=FAKE, cross=False, cond=None):
+        n = 10 if cross else 6   # with the condition's cross-attention weights
+        self.larr = (wam.WamLayerW * L)(*[wam.WamLayerW(*([ptr] * n)) for _ in range(L)])
+        self.c = wam.WamExpertW(ptr, ptr, ptr, C.cast(self.larr, C.POINTER(wam.WamLayerW)), L,
+                                C.pointer(cond) if cond is not None else None)
 
 
 def fake_kv(n_layers=2, B=1, Hh=4, cap=512, dtype=wam.WAM_BF16, lens=None, dh=64):
@@ -425,3 +427,35 @@ def test_python_limits_match_header():
     for name in ("WAM_MAX_FRAMES", "WAM_MAX_BATCH", "WAM_MAX_FUSE", "WAM_MAX_INTERVAL", "WAM_MAX_STEPS"):
         m = re.search(r"#define %s (\d+)" % name, hdr)
         assert m and int(m.group(1)) == getattr(wam, name)
+
+
+# ---------------------------------------------------------------- text/state condition
+def test_condition_validation_errors():
+    L = wam.lib()
+    d = good_dims(Tc=37, Ct=128, S=14)
+    # the condition needs the cross-attention weights and the expert's cache
+    st, msg = call_prefill(d=d, expert=FakeExpert(d.L))
+    assert st == -1 and "cross-attention" in msg
+    st, msg = call_prefill(d=d, expert=FakeExpert(d.L, cross=True))
+    assert st == -1 and "condition cache" in msg
+    bad, _k2 = fake_kv(cap=64, lens=[36])                   # len must be Tc
+    st, msg = call_prefill(d=d, expert=FakeExpert(d.L, cross=True, cond=bad))
+    assert st == -2 and "len" in msg
+    small, _k3 = fake_kv(cap=0, lens=[37])                  # cap below Tc
+    st, msg = call_prefill(d=d, expert=FakeExpert(d.L, cross=True, cond=small))
+    assert st == -2
+    # dims
+    assert L.wam_prefill_condition_kv(C.byref(good_dims(Tc=5, Ct=100)), None, None, FAKE, FAKE,
+                                      FAKE, 1, None, None, FAKE, 1 << 30, None) == -2  # Ct % 64
+    assert L.wam_prefill_condition_kv(C.byref(good_dims()), None, None, FAKE, FAKE, FAKE, 1, None,
+                                      None, FAKE, 1 << 30, None) == -2                  # Tc == 0
+    ex = FakeExpert(d.L, cross=True)
+    assert L.wam_prefill_condition_kv(C.byref(d), None, None, FAKE, FAKE, FAKE, 1, None, None, FAKE,
+                                      1 << 30, None) == -1                              # no expert
+    assert L.wam_prefill_condition_kv(C.byref(d), C.byref(ex.c), None, FAKE, FAKE, FAKE, 1, None,
+                                      None, FAKE, 1 << 30, None) == -1                  # no cache
+    cc, _k4 = fake_kv(cap=64, lens=[0])
+    assert L.wam_prefill_condition_kv(C.byref(d), C.byref(ex.c), None, FAKE, FAKE, FAKE, 1,
+                                      C.byref(cc), None, FAKE, 16, None) == -5          # workspace
+    assert L.wam_condition_workspace_bytes(C.byref(d), 2) >= 2 * 37 * 128 * 2
+    assert L.wam_condition_workspace_bytes(C.byref(good_dims()), 1) == 0
