@@ -356,6 +356,26 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
                       void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * wam_denoise_chunk_noalloc -- wam_denoise_chunk for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments and kernels, but no
+ * workspace argument.  Its scratch is a static device array of
+ * WAM_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on every GPU it
+ * runs on until the process ends; the call allocates nothing and frees
+ * nothing.  Returns WAM_E_WORKSPACE, before enqueuing anything, when the
+ * chunk needs more scratch than that (wam_denoise_workspace_bytes(d, B, kv),
+ * e.g. 4 episodes of 16 heads x 64 or one of 24 heads x 128 fit).  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.  No part
+ * of the scratch needs to start at any value.
+ * ------------------------------------------------------------------------- */
+#define WAM_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define WAM_MAX_DEVICES 64
+int wam_denoise_chunk_noalloc(const wam_dims* d, const wam_expert_w* action, const wam_kv* kv,
+                              const int32_t* read_map, const float* eps, int B, int N,
+                              double shift, float* actions_out, float* vhat_out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * wam_codenoise_chunk -- co-denoising (CoD): the future video latents and the
  * action chunk take N Euler steps together (Long-WAM Summary section 3.2 and
  * Figure 2; the joint call creates and returns both latents, "Fast-WAM 精读"

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1073,9 +1074,9 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
   Arena a(ws);
   Bufs b;
   plan_action(a, d, B, any ? std::max(max_len_of(kv, B), kv->cap) : 0, true, b);
-  std::vector<float> t(N + 1);
-  schedule(N, 0.0, shift, t.data());
-  HIPCK(time_embedding(s, t.data(), N, d->D, b.emb));
+  float t[WAM_MAX_STEPS + 1];  // no host allocation on this path
+  schedule(N, 0.0, shift, t);
+  HIPCK(time_embedding(s, t, N, d->D, b.emb));
   const int M = B * d->H;
   HIPCK(hipMemcpyAsync(actions_out, eps, (size_t)M * d->A * 4, hipMemcpyDeviceToDevice, s));
   Layer c{s, d, &b};
@@ -1103,6 +1104,55 @@ int wam_denoise_chunk(const wam_dims* d, const wam_expert_w* action, const wam_k
                         last ? nullptr : b.emb + (size_t)(k + 1) * d->D, M, d->D, d->A, true));
   }
   return WAM_OK;
+}
+
+// ----------------------------------------------------------------- no allocation
+// Scratch of wam_denoise_chunk_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes `scratch`
+// itself (its host-side name is not the device address): the address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) char scratch[WAM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[WAM_MAX_DEVICES] = {};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WAM_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= WAM_MAX_DEVICES) return fail(WAM_E_ARG, "device %d beyond %d", dev, WAM_MAX_DEVICES);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(WAM_E_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return WAM_OK;
+}
+}  // namespace
+
+int wam_denoise_chunk_noalloc(const wam_dims* d, const wam_expert_w* action, const wam_kv* kv,
+                              const int32_t* read_map, const float* eps, int B, int N, double shift,
+                              float* actions_out, float* vhat_out, void* stream) {
+  int st;
+  if ((st = check_dims(d))) return st;
+  if (!read_map) return fail(WAM_E_ARG, "NULL pointer");
+  bool any = false;
+  for (int l = 0; l < d->L; l++) any |= read_map[l] >= 0;
+  const size_t need = wam_denoise_workspace_bytes(d, B, any ? kv : nullptr);
+  if (need > WAM_NOALLOC_SCRATCH_BYTES)
+    return fail(WAM_E_WORKSPACE,
+                "this chunk needs %zu bytes of scratch; the static scratch holds %zu (use "
+                "wam_denoise_chunk with a workspace)",
+                need, (size_t)WAM_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return wam_denoise_chunk(d, action, kv, read_map, eps, B, N, shift, actions_out, vhat_out, ws,
+                           WAM_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ----------------------------------------------------------------- co-denoising

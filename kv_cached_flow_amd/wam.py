@@ -95,6 +95,9 @@ _EXPORTS = {
     "wam_denoise_chunk": (C.c_int, [C.POINTER(WamDims), C.POINTER(WamExpertW), C.POINTER(WamKV),
                                     C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_double, C.c_void_p,
                                     C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "wam_denoise_chunk_noalloc": (C.c_int, [C.POINTER(WamDims), C.POINTER(WamExpertW), C.POINTER(WamKV),
+                                            C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_double,
+                                            C.c_void_p, C.c_void_p, C.c_void_p]),
     "wam_codenoise_workspace_bytes": (C.c_size_t, [C.POINTER(WamDims), C.c_int, C.c_int, C.POINTER(WamKV)]),
     "wam_codenoise_chunk": (C.c_int, [C.POINTER(WamDims), C.POINTER(WamExpertW), C.POINTER(WamExpertW),
                                       C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p,
@@ -354,6 +357,19 @@ def denoise_chunk(d: WamDims, action: DeviceExpert, kv: Optional[DeviceKV], read
                                    rm.ctypes.data, _ptr(eps), B, N, shift, _ptr(actions_out),
                                    _ptr(vhat_out), _ptr(ws), ws.numel(), _stream(stream)),
            "wam_denoise_chunk")
+
+
+WAM_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def denoise_chunk_noalloc(d: WamDims, action: DeviceExpert, kv: Optional[DeviceKV], read_map, eps,
+                          B: int, N: int, shift: float, actions_out, vhat_out=None, stream=None):
+    """wam_denoise_chunk on the library's static scratch (no workspace, no allocation)."""
+    rm = np.ascontiguousarray(read_map, dtype=np.int32)
+    _check(lib().wam_denoise_chunk_noalloc(C.byref(d), C.byref(action.c),
+                                           C.byref(kv.c) if kv is not None else None, rm.ctypes.data,
+                                           _ptr(eps), B, N, shift, _ptr(actions_out), _ptr(vhat_out),
+                                           _stream(stream)), "wam_denoise_chunk_noalloc")
 
 
 def codenoise_workspace_bytes(d: WamDims, B: int, Ff: int, cache: DeviceKV) -> int:

@@ -23,7 +23,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     L = wam.lib()
     names = header_functions()
-    assert len(names) == 28
+    assert len(names) == 29
     for n in names:
         assert hasattr(L, n), n
     assert sorted(wam.exported_names()) == names
@@ -459,3 +459,18 @@ def test_condition_validation_errors():
                                       C.byref(cc), None, FAKE, 16, None) == -5          # workspace
     assert L.wam_condition_workspace_bytes(C.byref(d), 2) >= 2 * 37 * 128 * 2
     assert L.wam_condition_workspace_bytes(C.byref(good_dims()), 1) == 0
+
+
+def test_noalloc_denoise_rejects_chunks_beyond_its_scratch():
+    # 64 episodes of 16 heads x 128 need far more than the 64 MiB static
+    # scratch: refused on the host, before anything is enqueued
+    L = wam.lib()
+    d = good_dims(D=2048, Hh=16, dh=128)
+    ex = FakeExpert(d.L)
+    kv, _k = fake_kv(B=64, Hh=16, dh=128, cap=4096, lens=[4096] * 64)
+    rm = np.asarray([0, 1], dtype=np.int32)
+    need = L.wam_denoise_workspace_bytes(C.byref(d), 64, C.byref(kv))
+    assert need > wam.WAM_NOALLOC_SCRATCH_BYTES
+    st = L.wam_denoise_chunk_noalloc(C.byref(d), C.byref(ex.c), C.byref(kv), rm.ctypes.data, FAKE, 64,
+                                     4, 1.0, FAKE, None, None)
+    assert st == -5 and "scratch" in L.wam_last_error().decode()
