@@ -136,7 +136,8 @@ def blas_threads() -> list:
         return []
 
 
-def cpu_baseline(cfg_name: str, layers: int, kv_fp8: bool = False, rope: bool = False) -> dict:
+def cpu_baseline(cfg_name: str, layers: int, kv_fp8: bool = False, rope: bool = False,
+                 cond: bool = False) -> dict:
     """The oracle, as it stands, on one episode of the workload with the first
     `layers` layers of each expert; the time is scaled by B and by L / layers
     (the per-layer work of prefill, imagine and the action steps dominates)."""
@@ -152,6 +153,8 @@ def cpu_baseline(cfg_name: str, layers: int, kv_fp8: bool = False, rope: bool = 
         # one interaction layer (the last) reading the fusion of the sampled layers
         kw["fuse"] = ((0, layers),)
         kw["read_map"] = (-1,) * (layers - 1) + (0,)
+    if cond:
+        kw.update(configs.CONDITION)
     cfg = configs.get(cfg_name, kv_fp8=kv_fp8, rope=rope, **kw)
     inp = inputs.generate(cfg)
     t0 = time.perf_counter()
@@ -176,7 +179,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C4")
     ap.add_argument("--cpu-layers", type=int, default=0,
-                    help="layers per expert in the CPU oracle sample (0: 1 for C3-C5, 10 else)")
+                    help="layers per expert in the CPU oracle sample (0: 3 for C3-C5, 10 else)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stream", type=int, default=0, metavar="K",
                     help="streamed history: each timed step is one decision whose last K history "
@@ -187,6 +190,9 @@ def main():
     ap.add_argument("--rope", action="store_true",
                     help="rotary position option: Q and K of both experts rotated by their "
                          "token's index in the joint sequence")
+    ap.add_argument("--cond", action="store_true",
+                    help="text/state condition: 100 text tokens of width 4096 plus one proprio token "
+                         "from 14 state numbers, read by every layer through cross-attention")
     ap.add_argument("--minimal", action="store_true",
                     help="only warmup + timed chunks (for counter collection)")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -215,7 +221,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n * 4}))
         return
-    cfg = configs.get(args.config, kv_fp8=args.kv_fp8, rope=args.rope)
+    cfg = configs.get(args.config, kv_fp8=args.kv_fp8, rope=args.rope,
+                      **(configs.CONDITION if args.cond else {}))
     inp = inputs.generate(cfg)
     dc = DeviceChunk(cfg, inp)
     print(f"[bench] {cfg.name}: inputs resident, warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -313,6 +320,7 @@ def main():
         "config": {"workload": f"{cfg.name}: {WORKLOAD_TEXT.get(cfg.name, '')}"
                                + (", E4M3 K/V read by the action layers" if cfg.kv_fp8 else "")
                                + (", rotary positions on Q and K" if cfg.rope else "")
+                               + (f", text/state condition ({cfg.Tc} tokens of width {cfg.Ct})" if cfg.Tc else "")
                                + (f", streamed: {args.stream} new history frame(s) per decision"
                                   if args.stream else ""),
                    "kv_cache": "e4m3" if cfg.kv_fp8 else ("bf16" if cfg.dtype == "bf16" else "f32"),
@@ -320,7 +328,7 @@ def main():
                    "L": cfg.L, "D": cfg.D, "heads": f"{cfg.Hh}x{cfg.dh}", "kv_tokens": cfg.tokens_valid,
                    "action_steps": cfg.N, "video_steps": cfg.N if cfg.joint else cfg.V,
                    "streamed_new_frames": args.stream,
-                   "joint": cfg.joint, "rope": cfg.rope},
+                   "joint": cfg.joint, "rope": cfg.rope, "condition_tokens": cfg.Tc},
         "roofline": roofline,
         "attn_action_hbm_gbps": kt.get("attn_action", {}).get("achieved"),
         "prefill_attn_mfma_util": kt.get("attn_prefill", {}).get("frac"),
@@ -332,8 +340,8 @@ def main():
     rec["yardsticks"] = yardsticks()
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
-        layers = args.cpu_layers or (1 if cfg.name in ("C3", "C4", "C5") else 10)
-        rec["cpu_baseline"] = cpu_baseline(cfg.name, min(layers, cfg.L), cfg.kv_fp8, cfg.rope)
+        layers = args.cpu_layers or (3 if cfg.name in ("C3", "C4", "C5") else 10)
+        rec["cpu_baseline"] = cpu_baseline(cfg.name, min(layers, cfg.L), cfg.kv_fp8, cfg.rope, cfg.Tc > 0)
     print(json.dumps(rec), flush=True)
 
 
