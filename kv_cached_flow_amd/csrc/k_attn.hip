@@ -256,7 +256,7 @@ template <int DH>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     bf16_t* __restrict__ out, int nq, int row0, int cap, int Hh, FrameTab tab, int nsplit,
-    float* __restrict__ part) {
+    float* __restrict__ part, int n_ep, long long kv_ep) {
   using namespace pf;
   static_assert(DH == 64 || DH == 128, "head dim");
   // A K tile is DH/64 halves of 64 keys x 64 dims (128-byte rows), a V^T
@@ -264,9 +264,16 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   constexpr int NS = DH / 32, ND = DH / 16, TB = KT * DH * 2;
   __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];  // [stage][K | V^T]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int ntq = (nq + QT - 1) / QT;
-  int h, j;
-  prefill_block(blockIdx.x, Hh, ntq * nsplit, &h, &j);
+  const int ntq = (nq + QT - 1) / QT, HE = Hh * n_ep;
+  // (episode, head) pairs are scheduled as HE heads; episode ep's queries,
+  // output rows and cache sit at their own offsets, with the same frame table
+  int hx, j;
+  prefill_block(blockIdx.x, HE, ntq * nsplit, &hx, &j);
+  const int ep = hx / Hh, h = hx - ep * Hh;
+  q += (long long)ep * Hh * nq * DH;
+  kc += ep * kv_ep;
+  vc += ep * kv_ep;
+  out += (long long)ep * nq * Hh * DH;
   const int qt = j / nsplit, sp = j % nsplit;
   const int q0 = qt * QT;
   const int qlast = min(q0 + QT, nq) - 1;
@@ -394,15 +401,15 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   for (int kt = k_lo + KT; kt < k_hi; kt += KT) tile(kt, std::false_type{});
   const int D = Hh * DH;
   if (part != nullptr) {
-    // split partial (log2-domain max m, row sum l, unnormalised O):
-    // m [nsplit][Hh][nq], l [nsplit][Hh][nq], o [nsplit][Hh][nq][DH]
-    const long long plane = (long long)nsplit * Hh * nq;
+    // split partial (log2-domain max m, row sum l, unnormalised O), heads
+    // numbered ep * Hh + h: m [nsplit][HE][nq], l [nsplit][HE][nq], o [nsplit][HE][nq][DH]
+    const long long plane = (long long)nsplit * HE * nq;
 #pragma unroll
     for (int t = 0; t < 2; t++) {
       const float l = acc_rowsum(acc, t);
       const int qi = q0 + w * QW + 16 * t + c16;
       if (qi >= nq) continue;
-      const long long pi = ((long long)sp * Hh + h) * nq + qi;
+      const long long pi = ((long long)sp * HE + hx) * nq + qi;
       if (g == 0) {
         part[pi] = acc.m[t];
         part[plane + pi] = l;
@@ -433,16 +440,17 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
 template <int DH>
 __global__ __launch_bounds__(256) void attn_prefill_merge_kernel(const float* __restrict__ part,
                                                                  int nsplit, int Hh, int nq,
-                                                                 bf16_t* __restrict__ out) {
+                                                                 bf16_t* __restrict__ out, int n_ep) {
   const int wv = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (wv >= nq * Hh) return;
-  const int qi = wv / Hh, h = wv - qi * Hh;
-  const long long plane = (long long)nsplit * Hh * nq;
+  const int HE = Hh * n_ep;
+  if (wv >= nq * HE) return;
+  const int qi = wv / HE, hx = wv - qi * HE, ep = hx / Hh, h = hx - ep * Hh;
+  const long long plane = (long long)nsplit * HE * nq;
   float mv[pf::MAX_SPLIT], lv[pf::MAX_SPLIT], ov[pf::MAX_SPLIT][DH / 64];
 #pragma unroll
   for (int s = 0; s < pf::MAX_SPLIT; s++) {
     if (s < nsplit) {
-      const long long pi = ((long long)s * Hh + h) * nq + qi;
+      const long long pi = ((long long)s * HE + hx) * nq + qi;
       mv[s] = part[pi];
       lv[s] = part[plane + pi];
 #pragma unroll
@@ -467,7 +475,7 @@ __global__ __launch_bounds__(256) void attn_prefill_merge_kernel(const float* __
   }
 #pragma unroll
   for (int r = 0; r < DH / 64; r++)
-    out[(long long)qi * Hh * DH + h * DH + 64 * r + lane] = dev_f2bf(O[r] / L);
+    out[((long long)ep * nq + qi) * Hh * DH + h * DH + 64 * r + lane] = dev_f2bf(O[r] / L);
 }
 
 // fp32: one thread per (query, head)
@@ -477,13 +485,16 @@ __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(const float* __res
                                                               const float* __restrict__ vc,
                                                               float* __restrict__ out, int nq,
                                                               int row0, int cap, int Hh,
-                                                              FrameTab tab, float scale) {
-  const int h = blockIdx.y;
+                                                              FrameTab tab, float scale,
+                                                              long long kv_ep) {
+  const int h = blockIdx.y, ep = blockIdx.z;
   const int qi = blockIdx.x * 64 + threadIdx.x;
   if (qi >= nq) return;
+  q += (long long)ep * Hh * nq * DH;
+  out += (long long)ep * nq * Hh * DH;
   const float* qr = q + ((long long)h * nq + qi) * DH;
-  const float* kh = kc + (long long)h * cap * DH;
-  const float* vh = vc + (long long)h * DH * cap;
+  const float* kh = kc + ep * kv_ep + (long long)h * cap * DH;
+  const float* vh = vc + ep * kv_ep + (long long)h * DH * cap;
   float qv[DH], o[DH];
 #pragma unroll
   for (int d = 0; d < DH; d++) { qv[d] = qr[d]; o[d] = 0.f; }
@@ -558,11 +569,11 @@ static int prefill_splits(int Hh, int dh, int nq, int row0, const FrameTab& tab,
 
 hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int dh, int nq, int row0,
                         const FrameTab& tab, const void* q, const void* kc, const void* vc, int cap,
-                        void* out, float* part, size_t part_bytes) {
-  if (nq <= 0) return hipSuccess;
+                        void* out, float* part, size_t part_bytes, int n_ep, long long kv_ep) {
+  if (nq <= 0 || n_ep <= 0) return hipSuccess;
   if (dh != 64 && dh != 128) return hipErrorInvalidValue;
   const float scale = dh == 64 ? 0.125f : 0.08838834764831845f;  // 1 / sqrt(dh)
-  double pairs = 0.0;  // visible (query, key) pairs
+  double pairs = 0.0;  // visible (query, key) pairs of one episode
   for (int r = row0; r < row0 + nq;) {
     int f = r / tab.P, e = std::min(row0 + nq, (f + 1) * tab.P);
     pairs += (double)(e - r) * tab.kend[f];
@@ -570,45 +581,46 @@ hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int dh, int nq, int row0,
   }
   const int es = dt == WAM_BF16 ? 2 : 4;
   const int kmax = tab.kend[(row0 + nq - 1) / tab.P];
+  const int HE = Hh * n_ep;  // (episode, head) pairs
   if (dt == WAM_BF16) {
-    const int nsplit = part ? prefill_splits(Hh, dh, nq, row0, tab, part_bytes) : 1;
+    const int nsplit = part ? prefill_splits(HE, dh, nq, row0, tab, part_bytes) : 1;
     {
-      TimingScope ts(s, KC_ATTN_PREFILL, (double)Hh * dh * es * (2.0 * nq + 2.0 * kmax),
-                     4.0 * dh * Hh * pairs);
-      dim3 grid(((nq + pf::QT - 1) / pf::QT) * Hh * nsplit);
+      TimingScope ts(s, KC_ATTN_PREFILL, (double)HE * dh * es * (2.0 * nq + 2.0 * kmax),
+                     4.0 * dh * HE * pairs);
+      dim3 grid(((nq + pf::QT - 1) / pf::QT) * HE * nsplit);
       if (dh == 64)
         hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), 0, s, (const bf16_t*)q,
                            (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)out, nq, row0, cap, Hh,
-                           tab, nsplit, nsplit > 1 ? part : nullptr);
+                           tab, nsplit, nsplit > 1 ? part : nullptr, n_ep, kv_ep);
       else
         hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)q,
                            (const bf16_t*)kc, (const bf16_t*)vc, (bf16_t*)out, nq, row0, cap, Hh,
-                           tab, nsplit, nsplit > 1 ? part : nullptr);
+                           tab, nsplit, nsplit > 1 ? part : nullptr, n_ep, kv_ep);
     }
     if (nsplit > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       TimingScope ts(s, KC_ATTN_MERGE,
-                     (double)nsplit * Hh * nq * (dh + 2) * 4 + (double)nq * Hh * dh * es, 0.0);
+                     (double)nsplit * HE * nq * (dh + 2) * 4 + (double)nq * HE * dh * es, 0.0);
       if (dh == 64)
-        hipLaunchKernelGGL(attn_prefill_merge_kernel<64>, dim3((nq * Hh + 3) / 4), dim3(256), 0, s,
-                           (const float*)part, nsplit, Hh, nq, (bf16_t*)out);
+        hipLaunchKernelGGL(attn_prefill_merge_kernel<64>, dim3((nq * HE + 3) / 4), dim3(256), 0, s,
+                           (const float*)part, nsplit, Hh, nq, (bf16_t*)out, n_ep);
       else
-        hipLaunchKernelGGL(attn_prefill_merge_kernel<128>, dim3((nq * Hh + 3) / 4), dim3(256), 0,
-                           s, (const float*)part, nsplit, Hh, nq, (bf16_t*)out);
+        hipLaunchKernelGGL(attn_prefill_merge_kernel<128>, dim3((nq * HE + 3) / 4), dim3(256), 0,
+                           s, (const float*)part, nsplit, Hh, nq, (bf16_t*)out, n_ep);
     }
   } else {
-    TimingScope ts(s, KC_ATTN_PREFILL, (double)Hh * dh * es * (2.0 * nq + 2.0 * kmax),
-                   4.0 * dh * Hh * pairs);
-    dim3 grid((nq + 63) / 64, Hh);
+    TimingScope ts(s, KC_ATTN_PREFILL, (double)HE * dh * es * (2.0 * nq + 2.0 * kmax),
+                   4.0 * dh * HE * pairs);
+    dim3 grid((nq + 63) / 64, Hh, n_ep);
     if (dh == 64)
       hipLaunchKernelGGL(attn_prefill_f32_kernel<64>, grid, dim3(64), 0, s, (const float*)q,
                          (const float*)kc, (const float*)vc, (float*)out, nq, row0, cap, Hh, tab,
-                         scale);
+                         scale, kv_ep);
     else
       hipLaunchKernelGGL(attn_prefill_f32_kernel<128>, grid, dim3(64), 0, s, (const float*)q,
                          (const float*)kc, (const float*)vc, (float*)out, nq, row0, cap, Hh, tab,
-                         scale);
+                         scale, kv_ep);
   }
   return hipGetLastError();
 }

@@ -243,6 +243,7 @@ struct CondRef {
   const void* k = nullptr;
   const void* v = nullptr;
   int cap = 0;
+  long long ep = 0;  // elements from one episode's condition rows to the next
 };
 
 CondRef cond_ref(const wam_dims* d, const wam_kv* c, int l, int b) {
@@ -254,15 +255,17 @@ CondRef cond_ref(const wam_dims* d, const wam_kv* c, int l, int b) {
   r.k = (const char*)c->k + l * ls + ep;
   r.v = (const char*)c->v + l * ls + ep;
   r.cap = c->cap;
+  r.ep = (long long)c->Hh * c->cap * c->dh;
   return r;
 }
 
-// Cross-attention of n video rows (one episode) to its condition:
+// Cross-attention of n video rows (nep episodes of n / nep rows, episode-
+// major, the condition of the first at cr) to their condition:
 // X += Attn(RMSNorm(X; gx) Wqx^T ; K_c, V_c) Wox^T.  Every row sees the Tc
 // condition rows: one frame of the table whose key prefix ends at Tc.
-int video_cross(const Layer& c, const wam_layer_w& w, int n, const CondRef& cr) {
+int video_cross(const Layer& c, const wam_layer_w& w, int n, const CondRef& cr, int nep) {
   const wam_dims* d = c.d;
-  const int dt = d->dtype, D = d->D, Dq = d->Hh * d->dh;
+  const int dt = d->dtype, D = d->D, Dq = d->Hh * d->dh, rpg = n / nep;
   Bufs& b = *c.b;
   int st;
   if ((st = norm_rows(c, dt, w.gx, b.Y, n))) return st;
@@ -270,16 +273,17 @@ int video_cross(const Layer& c, const wam_layer_w& w, int n, const CondRef& cr) 
   e.q = b.Q;
   e.D = Dq;
   e.dh = d->dh;
-  e.rpg = n;
-  e.q_hs = (long long)n * d->dh;
+  e.rpg = rpg;
+  e.q_gs = (long long)d->Hh * rpg * d->dh;
+  e.q_hs = (long long)rpg * d->dh;
   e.q_scale = qkv_q_scale(d);
   HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, Dq, D, b.Y, D, w.wqx, D, e));
   FrameTab ct;
   ct.n = 1;
   ct.P = 1 << 30;
   ct.kend[0] = d->Tc;
-  HIPCK(attn_prefill(c.s, dt, d->Hh, d->dh, n, 0, ct, b.Q, cr.k, cr.v, cr.cap, b.O, b.pattn,
-                     b.pattn_bytes));
+  HIPCK(attn_prefill(c.s, dt, d->Hh, d->dh, rpg, 0, ct, b.Q, cr.k, cr.v, cr.cap, b.O, b.pattn,
+                     b.pattn_bytes, nep, cr.ep));
   return video_resid(c, n, D, Dq, b.O, w.wox);
 }
 
@@ -307,11 +311,14 @@ int action_cross(const Layer& c, const wam_layer_w& w, int B, const CondRef& cr)
   return action_resid(c, M, D, Dq, b.O, w.wox);
 }
 
-// One video layer for rows row0..row0+n-1 of episode cache layer (kl, vl).
+// One video layer for rows row0.. of nep episodes that share a frame table:
+// n rows, episode-major (n / nep per episode), episode e's cache layer at
+// (kl, vl) + e kv_ep elements.
 int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const FrameTab& tab,
-                void* kl, void* vl, int cap, bool kv_only, const CondRef& cr = CondRef()) {
+                void* kl, void* vl, int cap, bool kv_only, const CondRef& cr = CondRef(),
+                int nep = 1, long long kv_ep = 0) {
   const wam_dims* d = c.d;
-  const int dt = d->dtype, D = d->D;
+  const int dt = d->dtype, D = d->D, rpg = n / nep;
   Bufs& b = *c.b;
   int st;
   if ((st = norm_rows(c, dt, w.g1, b.Y, n))) return st;
@@ -321,8 +328,10 @@ int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const Fra
   e.v = vl;
   e.D = D;
   e.dh = d->dh;
-  e.rpg = n;
-  e.q_hs = (long long)n * d->dh;
+  e.rpg = rpg;
+  e.q_gs = (long long)d->Hh * rpg * d->dh;
+  e.q_hs = (long long)rpg * d->dh;
+  e.k_gs = e.v_gs = kv_ep;
   e.k_hs = (long long)cap * d->dh;
   e.v_hs = (long long)d->dh * cap;
   e.k_row0 = row0;
@@ -331,22 +340,23 @@ int video_layer(const Layer& c, const wam_layer_w& w, int n, int row0, const Fra
   e.q_scale = qkv_q_scale(d);
   // rotary option: Q rows and the K rows just cached sit at positions row0 ..
   RopeRows rb{};
-  rb.base[0] = row0;
+  for (int i = 0; i < nep; i++) rb.base[i] = row0;
   void* krows = (char*)kl + (size_t)row0 * d->dh * esz(dt);
   if (kv_only) {
     e.n_begin = D;
     HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, 2 * D, D, b.Y, D,
                (const char*)w.wqkv + (size_t)D * D * esz(dt), D, e));
     if (d->rope)
-      HIPCK(rope_qk(c.s, dt, krows, 0, e.k_hs, nullptr, 0, 0, 1, n, d->Hh, d->dh, rb));
+      HIPCK(rope_qk(c.s, dt, krows, kv_ep, e.k_hs, nullptr, 0, 0, nep, rpg, d->Hh, d->dh, rb));
     return WAM_OK;
   }
   HIPCK(gemm(c.s, dt, dt, dt, EPI_QKV, n, 3 * D, D, b.Y, D, w.wqkv, D, e));
   if (d->rope)
-    HIPCK(rope_qk(c.s, dt, b.Q, 0, e.q_hs, krows, 0, e.k_hs, 1, n, d->Hh, d->dh, rb));
-  HIPCK(attn_prefill(c.s, dt, d->Hh, d->dh, n, row0, tab, b.Q, kl, vl, cap, b.O, b.pattn, b.pattn_bytes));
+    HIPCK(rope_qk(c.s, dt, b.Q, e.q_gs, e.q_hs, krows, kv_ep, e.k_hs, nep, rpg, d->Hh, d->dh, rb));
+  HIPCK(attn_prefill(c.s, dt, d->Hh, d->dh, rpg, row0, tab, b.Q, kl, vl, cap, b.O, b.pattn,
+                     b.pattn_bytes, nep, kv_ep));
   if ((st = video_resid(c, n, D, D, b.O, w.wo))) return st;
-  if (cr.k && (st = video_cross(c, w, n, cr))) return st;
+  if (cr.k && (st = video_cross(c, w, n, cr, nep))) return st;
   if ((st = norm_rows(c, dt, w.g2, b.Y, n))) return st;
   EpiArgs gl{};
   gl.out = b.Hb;
@@ -477,11 +487,13 @@ void plan_action(Arena& a, const wam_dims* d, int B, int max_len, bool with_emb,
   b.pattn_bytes = 0;
 }
 
-void plan_prefill(Arena& a, const wam_dims* d, int Fh, int Ff, Bufs& b, float** z) {
+// Workspace of a video call: rows for one episode's history and future, or
+// for the future rows of nb episodes denoised together.
+void plan_prefill(Arena& a, const wam_dims* d, int nb, int Fh, int Ff, Bufs& b, float** z) {
   const size_t e = esz(d->dtype);
   // history and future rows share one pass when the future is not denoised
-  const size_t T = (size_t)(Fh + Ff) * d->P;
-  const size_t Tf = (size_t)Ff * d->P;
+  const size_t Tf = (size_t)nb * Ff * d->P;
+  const size_t T = std::max<size_t>((size_t)(Fh + Ff) * d->P, Tf);
   b.emb = (float*)a.take((size_t)(WAM_MAX_STEPS + 2) * d->D * 4);
   b.X = (float*)a.take(T * d->D * 4);
   b.Y = a.take(T * d->D * e);
@@ -563,7 +575,7 @@ size_t wam_prefill_workspace_bytes(const wam_dims* d, int B, int Fh, int Ff) {
   Arena a(nullptr);
   Bufs b;
   float* z;
-  plan_prefill(a, d, Fh, Ff, b, &z);
+  plan_prefill(a, d, std::max(B, 1), Fh, Ff, b, &z);
   return a.off + 256;
 }
 
@@ -619,40 +631,53 @@ int history_rows(const Layer& c, const wam_expert_w* video, int ep, const void* 
   return WAM_OK;
 }
 
-// The future rows [Th, Th + Tf) of one episode over its cached history:
-// video_steps Euler steps of z over sig (embeddings emb_steps[k]) attending
-// to [history ; future], then one caching pass at emb_last; z (fp32) starts
-// as fut_noise_b (dtype).  video_steps == 0: the caching pass of the noise.
+// The future rows [Th, Th + Tf) of episodes ep .. ep + nep - 1, which share
+// one frame table, over their cached history: video_steps Euler steps of z
+// over sig (embeddings emb_steps[k]) attending to [history ; future], then
+// one caching pass at emb_last; z (fp32, [nep][Tf][Cv]) starts as
+// fut_noise_b (dtype, the same layout).  video_steps == 0: the caching pass
+// of the noise.  k / v: episode ep's cache, episode ep + i at + i kv_ep elements.
 int future_rows(const Layer& c, const wam_expert_w* video, int ep, const void* fut_noise_b,
                 float* z, const std::vector<float>& sig, int video_steps, const float* emb_steps,
                 const float* emb_last, const FrameTab& tab, int Th, int Tf, char* k, char* v,
-                size_t ls, int cap) {
+                size_t ls, int cap, int nep = 1, long long kv_ep = 0) {
   const wam_dims* d = c.d;
   Bufs& b = *c.b;
-  const int D = d->D, dt = d->dtype;
+  const int D = d->D, dt = d->dtype, n = nep * Tf;
   int st;
   RowMap zmap;
   zmap.n = 1;
-  zmap.P = Tf;
+  zmap.P = n;
   zmap.src[0] = 0;
-  HIPCK(copy_cvt_f32(c.s, dt, fut_noise_b, z, (int64_t)Tf * d->Cv));
+  HIPCK(copy_cvt_f32(c.s, dt, fut_noise_b, z, (int64_t)n * d->Cv));
   for (int s = 0; s < video_steps; s++) {
-    HIPCK(embed(c.s, WAM_F32, dt, z, zmap, video->w_in, emb_steps + (size_t)s * D, b.X, Tf, D,
+    HIPCK(embed(c.s, WAM_F32, dt, z, zmap, video->w_in, emb_steps + (size_t)s * D, b.X, n, D,
                 d->Cv));
     for (int l = 0; l < d->L; l++)
-      if ((st = video_layer(c, video->layers[l], Tf, Th, tab, k + l * ls, v + l * ls, cap, false,
-                            cond_ref(d, video->cond, l, ep))))
+      if ((st = video_layer(c, video->layers[l], n, Th, tab, k + l * ls, v + l * ls, cap, false,
+                            cond_ref(d, video->cond, l, ep), nep, kv_ep)))
         return st;
-    if ((st = flush_pending(c, video->g_out, Tf))) return st;  // X whole for the head
+    if ((st = flush_pending(c, video->g_out, n))) return st;  // X whole for the head
     HIPCK(step_boundary(c.s, dt, b.X, video->g_out, video->w_out, z, sig[s + 1] - sig[s], nullptr,
-                        nullptr, nullptr, Tf, D, d->Cv, true));
+                        nullptr, nullptr, n, D, d->Cv, true));
   }
-  HIPCK(embed(c.s, WAM_F32, dt, z, zmap, video->w_in, emb_last, b.X, Tf, D, d->Cv));
+  HIPCK(embed(c.s, WAM_F32, dt, z, zmap, video->w_in, emb_last, b.X, n, D, d->Cv));
   for (int l = 0; l < d->L; l++)
-    if ((st = video_layer(c, video->layers[l], Tf, Th, tab, k + l * ls, v + l * ls, cap,
-                          l == d->L - 1, cond_ref(d, video->cond, l, ep))))
+    if ((st = video_layer(c, video->layers[l], n, Th, tab, k + l * ls, v + l * ls, cap,
+                          l == d->L - 1, cond_ref(d, video->cond, l, ep), nep, kv_ep)))
       return st;
   return WAM_OK;
+}
+
+// True when every episode of the call has the same compacted frame table
+// (then their future rows can be denoised together).
+bool same_tables(const Tables& t) {
+  for (size_t b = 1; b < t.tab.size(); b++) {
+    if (t.tab[b].n != t.tab[0].n || t.nh[b] != t.nh[0]) return false;
+    for (int i = 0; i < t.tab[0].n; i++)
+      if (t.tab[b].kend[i] != t.tab[0].kend[i]) return false;
+  }
+  return true;
 }
 
 // Time embeddings of a video call into emb: [0 (history), sigma_0 ..
@@ -721,7 +746,7 @@ int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video, const 
   Arena a(ws);
   Bufs bufs;
   float* z;
-  plan_prefill(a, d, Fh, Ff, bufs, &z);
+  plan_prefill(a, d, B, Fh, Ff, bufs, &z);
   std::vector<float> sig, embs;
   video_schedule(video_steps, sigma_star, shift, sig, embs);
   const int D = d->D;
@@ -734,6 +759,8 @@ int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video, const 
   const size_t ep = (size_t)d->Hh * cache->cap * d->dh * esz(dt);  // one episode in a layer
   Layer c{s, d, &bufs};
   const int Tf = Ff * P;
+  // imagined futures of episodes with one frame table go through the layers together
+  const bool together = video_steps > 0 && Ff > 0 && B > 1 && same_tables(t);
   for (int b = 0; b < B; b++) {
     const int Th = t.nh[b] * P;
     char* kb = (char*)cache->k + b * ep;
@@ -761,14 +788,24 @@ int wam_prefill_video_cache(const wam_dims* d, const wam_expert_w* video, const 
       if (Th > 0 && (st = history_rows(c, video, b, hist, t.hmap[b], emb_hist, t.tab[b], 0, Th, kb,
                                         vb, ls, cache->cap)))
         return st;
-      if (Ff > 0 && (st = future_rows(c, video, b, fut_b, z, sig, video_steps, bufs.emb + D,
-                                       emb_last, t.tab[b], Th, Tf, kb, vb, ls, cache->cap)))
+      if (Ff > 0 && !together &&
+          (st = future_rows(c, video, b, fut_b, z, sig, video_steps, bufs.emb + D, emb_last,
+                            t.tab[b], Th, Tf, kb, vb, ls, cache->cap)))
         return st;
     }
-    if (Ff > 0 && fut_latents_out)
+    if (Ff > 0 && fut_latents_out && !together)
       HIPCK(hipMemcpyAsync(fut_latents_out + (size_t)b * Tf * d->Cv, z, (size_t)Tf * d->Cv * 4,
                            hipMemcpyDeviceToDevice, s));
     cache->len[b] = t.tab[b].n * P;
+  }
+  if (together) {
+    if ((st = future_rows(c, video, 0, fut_noise, z, sig, video_steps, bufs.emb + D, emb_last,
+                          t.tab[0], t.nh[0] * P, Tf, (char*)cache->k, (char*)cache->v, ls,
+                          cache->cap, B, (long long)(ep / esz(dt)))))
+      return st;
+    if (fut_latents_out)
+      HIPCK(hipMemcpyAsync(fut_latents_out, z, (size_t)B * Tf * d->Cv * 4, hipMemcpyDeviceToDevice,
+                           s));
   }
   return WAM_OK;
 }
@@ -818,7 +855,7 @@ int wam_extend_history_cache(const wam_dims* d, const wam_expert_w* video, const
   Arena a(ws);
   Bufs bufs;
   float* z;
-  plan_prefill(a, d, Fn, 0, bufs, &z);
+  plan_prefill(a, d, 1, Fn, 0, bufs, &z);
   const float zero = 0.f;
   HIPCK(time_embedding(s, &zero, 1, d->D, bufs.emb));
   const size_t ls = layer_stride(cache);
@@ -860,7 +897,7 @@ int wam_prefill_future(const wam_dims* d, const wam_expert_w* video, const uint8
   Arena a(ws);
   Bufs bufs;
   float* z;
-  plan_prefill(a, d, 0, Ff, bufs, &z);
+  plan_prefill(a, d, B, 0, Ff, bufs, &z);
   std::vector<float> sig, embs;
   video_schedule(video_steps, sigma_star, shift, sig, embs);
   const int D = d->D, dt = d->dtype;
@@ -869,11 +906,24 @@ int wam_prefill_future(const wam_dims* d, const wam_expert_w* video, const uint8
   const size_t ep = (size_t)d->Hh * cache->cap * d->dh * esz(dt);
   Layer c{s, d, &bufs};
   const int Tf = Ff * P;
+  const float* emb_last = bufs.emb + (size_t)(embs.size() - 1) * D;
+  if (video_steps > 0 && B > 1 && same_tables(t)) {
+    // every episode's future through the layers together
+    if ((st = future_rows(c, video, 0, fut_noise, z, sig, video_steps, bufs.emb + D, emb_last,
+                          t.tab[0], t.nh[0] * P, Tf, (char*)cache->k, (char*)cache->v, ls,
+                          cache->cap, B, (long long)(ep / esz(dt)))))
+      return st;
+    if (fut_latents_out)
+      HIPCK(hipMemcpyAsync(fut_latents_out, z, (size_t)B * Tf * d->Cv * 4, hipMemcpyDeviceToDevice,
+                           s));
+    for (int b = 0; b < B; b++) cache->len[b] = t.tab[b].n * P;
+    return WAM_OK;
+  }
   for (int b = 0; b < B; b++) {
     const void* fut_b = (const char*)fut_noise + (size_t)b * Tf * d->Cv * esz(dt);
-    if ((st = future_rows(c, video, b, fut_b, z, sig, video_steps, bufs.emb + D,
-                          bufs.emb + (size_t)(embs.size() - 1) * D, t.tab[b], t.nh[b] * P, Tf,
-                          (char*)cache->k + b * ep, (char*)cache->v + b * ep, ls, cache->cap)))
+    if ((st = future_rows(c, video, b, fut_b, z, sig, video_steps, bufs.emb + D, emb_last,
+                          t.tab[b], t.nh[b] * P, Tf, (char*)cache->k + b * ep,
+                          (char*)cache->v + b * ep, ls, cache->cap)))
       return st;
     if (fut_latents_out)
       HIPCK(hipMemcpyAsync(fut_latents_out + (size_t)b * Tf * d->Cv, z, (size_t)Tf * d->Cv * 4,
@@ -1161,7 +1211,7 @@ size_t wam_codenoise_workspace_bytes(const wam_dims* d, int B, int Ff, const wam
   Arena a(nullptr);
   Bufs vb, ab;
   float* z;
-  plan_prefill(a, d, 0, Ff, vb, &z);
+  plan_prefill(a, d, 1, 0, Ff, vb, &z);
   const wam_dims da = action_view(d);
   plan_action(a, &da, B, cache->cap, true, ab);
   return a.off + 256;
@@ -1223,7 +1273,7 @@ int wam_codenoise_chunk(const wam_dims* d, const wam_expert_w* video, const wam_
   Arena a(ws);
   Bufs vb, ab;
   float* zs;
-  plan_prefill(a, d, 0, Ff, vb, &zs);
+  plan_prefill(a, d, 1, 0, Ff, vb, &zs);
   const wam_dims da = action_view(d);
   plan_action(a, &da, B, cache->cap, true, ab);
   std::vector<float> sv(N + 1), ta(N + 1);

@@ -209,10 +209,13 @@ hipError_t fuse_kv(hipStream_t s, int dt, const void* src, void* dst, long long 
 
 // part / part_bytes: workspace for split partials (bf16 launches with few
 // query tiles split their keys and merge; NULL: never split).
-// dh is 64 or 128.
+// dh is 64 or 128.  n_ep episodes with the same frame table in one launch:
+// episode e's queries at q + e Hh nq dh, its output rows at out + e nq Hh dh,
+// its cache at kc / vc + e kv_ep (elements).
 hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int dh, int nq, int row0,
                         const FrameTab& tab, const void* q, const void* kc, const void* vc, int cap,
-                        void* out, float* part, size_t part_bytes);
+                        void* out, float* part, size_t part_bytes, int n_ep = 1,
+                        long long kv_ep = 0);
 // Partial workspace a prefill of up to max_rows query rows can use.
 size_t attn_prefill_split_bytes(int Hh, int dh, int max_rows);
 
