@@ -20,8 +20,6 @@
 //
 // fp32 variants (one thread per query, plain FMA) serve the fp32 workload.
 #include <algorithm>
-#include <functional>
-#include <vector>
 #include <type_traits>
 
 #include "wam_internal.h"
@@ -536,86 +534,37 @@ static int device_cus() {
 }
 
 size_t attn_prefill_split_bytes(int Hh, int dh, int max_rows) {
-  // a launch splits only below 8 workgroups per CU, so splits x workgroups
-  // stays below 8 per CU x MAX_SPLIT: at most 8 n_cu QT (query, head, split)
-  // partials
+  // a launch splits only below 2 workgroups per CU, so splits x workgroups
+  // stays below 4 per CU: at most 4 n_cu QT (query, head, split) partials
   const long long n = std::min<long long>((long long)pf::MAX_SPLIT * Hh * max_rows,
-                                          8ll * device_cus() * pf::QT);
+                                          4ll * device_cus() * pf::QT);
   return (size_t)n * (dh + 2) * sizeof(float);
 }
 
-// Longest-first placement of a launch's workgroups (key tiles each) on n_cu
-// CUs that share their throughput among the workgroups they hold: the
-// largest per-CU sum, in key tiles.
-static long long prefill_makespan(const std::vector<int>& tiles, int n_cu) {
-  std::vector<long long> load(n_cu, 0);  // a min-heap of per-CU loads
-  for (int t : tiles) {
-    std::pop_heap(load.begin(), load.end(), std::greater<long long>());
-    load.back() += t;
-    std::push_heap(load.begin(), load.end(), std::greater<long long>());
-  }
-  return *std::max_element(load.begin(), load.end());
-}
-
-// Whether S key splits of every query tile are allowed: the partials fit,
-// and for every query tile the first tile of every split holds a key that
-// every query of the tile sees (the tile loop takes a split's first tile as
-// setting the reference max).  Under the block-causal mask a query sees a
-// key prefix, so that holds when the last split starts below the tile's
-// smallest prefix end.
-static bool prefill_split_ok(int S, int Hh, int dh, int nq, int row0, const FrameTab& tab,
-                             size_t part_bytes) {
-  if ((size_t)S * Hh * nq * (dh + 2) * sizeof(float) > part_bytes) return false;
-  const int ntq = (nq + pf::QT - 1) / pf::QT;
-  for (int qt = 0; qt < ntq; qt++) {
-    const int q0 = qt * pf::QT, ql = std::min(q0 + pf::QT, nq) - 1;
-    const int kmin = tab.kend[(row0 + q0) / tab.P], kmax = tab.kend[(row0 + ql) / tab.P];
-    int lo, hi;
-    prefill_split_range(kmax, S - 1, S, &lo, &hi);
-    if ((kmax + pf::KT - 1) / pf::KT < S || lo >= kmin) return false;
-  }
-  return true;
-}
-
-// Key splits of a launch; a split adds a partial write and a merge.
-//  * Below 2 workgroups per CU: enough splits for two per CU (a CU needs two
-//    to keep its SIMDs busy), at most MAX_SPLIT.
-//  * From 2 to 8 per CU: the split count whose longest-first placement of the
-//    workgroups over the CUs ends first, counting 5 % per added split; it
-//    splits where a last round of equal workgroups would leave CUs idle.
-//  * From 8 per CU: no split.
+// Key splits of a launch: enough (query tile, head, split) workgroups for two
+// per CU, at most MAX_SPLIT, and only where, for every query tile, the first
+// tile of every split holds a key that every query of the tile sees (the
+// tile loop takes a split's first tile as setting the reference max).  Under
+// the block-causal mask a query sees a key prefix, so that holds when the
+// last split starts below the tile's smallest prefix end.
 static int prefill_splits(int Hh, int dh, int nq, int row0, const FrameTab& tab, size_t part_bytes) {
   const int ntq = (nq + pf::QT - 1) / pf::QT, n_cu = device_cus();
   const long long g = (long long)ntq * Hh;
-  if (g >= 8ll * n_cu) return 1;
-  if (g < 2ll * n_cu) {
-    int S = (int)std::min<long long>(pf::MAX_SPLIT, (2ll * n_cu + g - 1) / g);
-    while (S > 1 && !prefill_split_ok(S, Hh, dh, nq, row0, tab, part_bytes)) S--;
-    return S;
-  }
-  int best = 1;
-  double best_cost = 0.0;
-  for (int S = 1; S <= pf::MAX_SPLIT; S++) {
-    if (S > 1 && !prefill_split_ok(S, Hh, dh, nq, row0, tab, part_bytes)) break;
-    std::vector<int> tiles;
-    tiles.reserve((size_t)g * S);
-    for (int qt = 0; qt < ntq; qt++) {
-      const int ql = std::min(qt * pf::QT + pf::QT, nq) - 1;
-      const int kmax = tab.kend[(row0 + ql) / tab.P];
-      for (int sp = 0; sp < S; sp++) {
-        int lo, hi;
-        prefill_split_range(kmax, sp, S, &lo, &hi);
-        for (int h = 0; h < Hh; h++) tiles.push_back((hi - lo + pf::KT - 1) / pf::KT);
-      }
+  if (g >= 2ll * n_cu) return 1;
+  int S = (int)std::min<long long>(pf::MAX_SPLIT, (2ll * n_cu + g - 1) / g);
+  for (; S > 1; S--) {
+    if ((size_t)S * Hh * nq * (dh + 2) * sizeof(float) > part_bytes) continue;
+    bool ok = true;
+    for (int qt = 0; qt < ntq && ok; qt++) {
+      const int q0 = qt * pf::QT, ql = std::min(q0 + pf::QT, nq) - 1;
+      const int kmin = tab.kend[(row0 + q0) / tab.P], kmax = tab.kend[(row0 + ql) / tab.P];
+      int lo, hi;
+      prefill_split_range(kmax, S - 1, S, &lo, &hi);
+      ok = (kmax + pf::KT - 1) / pf::KT >= S && lo < kmin;
     }
-    std::sort(tiles.begin(), tiles.end(), std::greater<int>());
-    const double cost = (double)prefill_makespan(tiles, n_cu) * (1.0 + 0.05 * (S - 1));
-    if (S == 1 || cost < best_cost) {
-      best = S;
-      best_cost = cost;
-    }
+    if (ok) break;
   }
-  return best;
+  return S;
 }
 
 hipError_t attn_prefill(hipStream_t s, int dt, int Hh, int dh, int nq, int row0,
