@@ -56,11 +56,12 @@ __device__ inline int perm_key(int sub, int r) {
 // numerator and denominator use the same bf16 probabilities.  Scores are in
 // log2 units (the bf16 queries arrive as Q log2(e) / sqrt(dh), scaled in the
 // projection's fp32 epilogue before their one rounding), and m is the
-// reference max in those units.  The score MFMA starts from -m instead of 0,
-// so it yields s - m directly and p = exp2(s - m) costs one exponential and
-// no FMA.  The reference max is raised only when a score exceeds it by more
-// than 2^8 in probability, so rescaling is rare; P <= 256 stays exact in bf16
-// and the result does not depend on the reference.
+// reference max in those units, a whole number.  The score MFMA starts from
+// -m instead of 0, so it yields s - m directly and p = exp2(s - m) costs one
+// exponential and no FMA.  The reference max is raised, by whole units, only
+// when a score exceeds it by more than 2^8 in probability, so rescaling is
+// rare; P < 512 stays finite in bf16 and the result does not depend on the
+// reference.
 // DH: head dim (64 or 128); o[0 .. DH/16 - 1] hold O^T, o[DH/16] the row sums.
 template <int DH>
 struct WaveAccT {
@@ -131,17 +132,22 @@ __device__ inline void tile_update(WaveAccT<DH>& a, floatx4 (&sacc)[4][2], bool 
     if (first || __any(mx > kLazyLog2)) {
       mx = wave_max16x4(mx);
       const bool need = mx > kLazyLog2;
+      // The reference moves by whole units only: every probability is then
+      // bf16(2^s) scaled by an exact power of two, whatever keys a split or
+      // tile saw first, and rescales and split merges multiply by exact powers
+      // of two, so split plans differ only in fp32 summation order.
+      const float step = floorf(mx);
       float delta;
       if (first) {
-        a.m[t] = mx;
-        delta = mx;
+        a.m[t] = step;
+        delta = step;
       } else {
-        const float mnew = need ? a.m[t] + mx : a.m[t];
+        const float mnew = need ? a.m[t] + step : a.m[t];
         const float alpha = __builtin_amdgcn_exp2f(a.m[t] - mnew);
         a.m[t] = mnew;
 #pragma unroll
         for (int d = 0; d <= ND; d++) a.o[d][t] *= alpha;
-        delta = need ? mx : 0.f;  // rows without a new max keep their reference
+        delta = need ? step : 0.f;  // rows without a new max keep their reference
       }
 #pragma unroll
       for (int sub = 0; sub < 4; sub++)

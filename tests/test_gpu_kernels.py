@@ -292,10 +292,23 @@ def test_attention_action_split_invariance_and_determinism(dh):
         again = _run_action(dt, q, ka, va, 32, K, V, cap, lens, splits)
         assert np.array_equal(outs[splits], again)      # bitwise run-to-run
         assert rel_l2(outs[splits], ref) <= 5e-3
-    # the plans differ only in fp32 summation order before one bf16 rounding each:
-    # their distance is that of two bf16 roundings (rms ~2^-9 relative)
+    # With whole-number reference maxima every probability is bf16(2^s) times
+    # an exact power of two in every plan, and rescales and merges multiply by
+    # exact powers of two: the plans differ in fp32 summation order (and in
+    # the last bit of a score accumulated from another starting offset), then
+    # each output is rounded to bf16 once.  Elementwise: at most one bf16 step
+    # apart wherever the output is not a near-cancellation.
+    base = outs[1].astype(np.float32)
+    step = np.abs(base).view(np.uint32) & np.uint32(0x7F800000)  # 2^e of each output
+    ulp = step.view(np.float32) * np.float32(2.0 ** -7)            # one bf16 step there
+    big = np.abs(base) >= 0.05 * np.sqrt(np.mean(base.astype(np.float64) ** 2))
     for s in (2, 7, 63):
-        assert rel_l2(outs[s], outs[1]) <= 4e-3
+        d = np.abs(outs[s].astype(np.float32) - base)
+        n1 = int(np.count_nonzero(d[big] > ulp[big]))
+        print(f"splits {s}: rel L2 to one split {rel_l2(outs[s], outs[1]):.2e}, "
+              f"equal {np.mean(d == 0):.4f}, beyond one step {n1} of {int(big.sum())}")
+        assert n1 == 0
+        assert rel_l2(outs[s], outs[1]) <= 1e-3
 
 
 # ---------------------------------------------------------------- fusion

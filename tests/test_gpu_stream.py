@@ -72,7 +72,8 @@ def test_streamed_history_equals_one_prefill(dtype, arrivals):
 def test_decisions_over_a_growing_window():
     """Three decisions: each drops the future rows, appends the frame that
     arrived, adds the future and denoises; the last decision's actions and
-    cache match one prefill of the final window (C3's frame shape, 2 layers)."""
+    cache match one prefill of the final window (C3's frame shape, 2 layers)
+    on the GPU and the oracle's chunk over that window."""
     cfg = configs.get("C3", L=2, read_map=(0, 1), Fh=6, Ff=2, frame_block=tuple(range(8)), N=2, V=2)
     print_case("three streamed decisions, 880-token frames")
     inp = inputs.generate(cfg)
@@ -99,3 +100,14 @@ def test_decisions_over_a_growing_window():
         k, _ = gpu_cache_layer(dc, l, 0, T)
         kf, _ = gpu_cache_layer(full, l, 0, T)
         assert rel_l2(k, kf) <= 1e-2
+    # and against the oracle: its streamed history is pinned to one prefill of
+    # the final window, so the last decision must land on the oracle's chunk
+    ref = O.run_chunk(cfg, inp, keep_cache=True)
+    err = rel_l2(to_np(dc.actions), ref["actions"])
+    zerr = rel_l2(to_np(dc.z).reshape(ref["z"].shape), ref["z"])
+    print(f"three decisions against the oracle: rel L2 actions {err:.2e}, future latents {zerr:.2e}")
+    assert err <= 2e-2 and zerr <= 1e-2
+    for l in range(cfg.L):
+        k, v = gpu_cache_layer(dc, l, 0, T)
+        assert rel_l2(k, ref["cache"][0][l][0].numpy()) <= 1e-2
+        assert rel_l2(v, ref["cache"][0][l][1].numpy()) <= 1e-2
