@@ -185,7 +185,10 @@ typedef struct wam_kv_s {
  *     one more pass at sigma_star stores the future K, V;
  *   - video_steps == 0: one pass of the noise at sigma = 1 stores the future
  *     K, V.  Ff == 0: history only.
- * The last layer of a caching pass computes K, V only.
+ * The last layer of a caching pass computes K, V only.  Episodes whose
+ * compacted frame tables are equal take their video steps and caching pass
+ * together (one launch per product for all their future rows); an episode's
+ * results never depend on another episode's inputs.
  *
  *   hist       device [B][Fh][P][Cv] dtype     history / anchor latents
  *   hist_valid host [B][Fh] uint8 or NULL
@@ -193,6 +196,8 @@ typedef struct wam_kv_s {
  *   frame_block host [Fh + Ff] int32, non-decreasing
  *   cache      device k/v per wam_kv; n_layers == L; cache->len (host) is written
  *   fut_latents_out device [B][Ff][P][Cv] fp32 or NULL: z after the video steps
+ *   ws         wam_prefill_workspace_bytes(d, B, Fh, Ff) bytes, 16-byte aligned
+ *              (it holds one episode's history rows or all B episodes' future rows)
  * Errors: WAM_E_SHAPE if a frame table is not monotone, an episode has no
  * token at all, or cap is too small.
  * ------------------------------------------------------------------------- */
