@@ -218,14 +218,15 @@ constexpr int MAX_SPLIT = 4;                  // key splits per (query tile, hea
 }
 
 // Workgroups are dealt round-robin to the 8 XCDs.  Give every XCD whole heads
-// (their K/V then stay in that XCD's L2) and start the longest (latest) query
-// tiles first.  j in [0, nj) numbers the (query tile, key split) units of a
-// head, longest first.
+// and let it work through them one at a time, each head's longest (latest)
+// query tiles first: the workgroups resident on an XCD then stream one head's
+// K/V through its L2.  j in [0, nj) numbers the (query tile, key split) units
+// of a head, longest first.
 __device__ inline void prefill_block(int bid, int Hh, int nj, int* h, int* j) {
   if ((Hh & 7) == 0) {
-    const int x = bid & 7, i = bid >> 3, hpx = Hh >> 3;
-    *h = x + 8 * (i % hpx);
-    *j = nj - 1 - i / hpx;
+    const int x = bid & 7, i = bid >> 3;
+    *h = x + 8 * (i / nj);
+    *j = nj - 1 - i % nj;
   } else {
     *h = bid % Hh;
     *j = nj - 1 - bid / Hh;
