@@ -70,7 +70,6 @@ struct WaveAccT {
   floatx4 o[ND + 1][2];
   float m[2];
 };
-using WaveAcc = WaveAccT<64>;
 
 template <int DH>
 __device__ inline void acc_init(WaveAccT<DH>& a) {
